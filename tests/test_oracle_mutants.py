@@ -1,0 +1,106 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutant is a copy of an oracle module with one plausible slip (a dropped
+term, a wrong sign or index, a transposed operand).  The copy is built from
+the module's source text, swapped in for the pin tests, and at least one pin
+must fail.  The real oracle is never modified.
+"""
+import importlib.util
+import inspect
+import types
+
+import pytest
+
+import oracle.attention as real_attention
+import oracle.metadata as real_metadata
+from tests import test_oracle_attention as TA
+from tests import test_oracle_metadata as TM
+
+ATTENTION_MUTANTS = [
+    ("drop scale", "s = scale * (K @ qvec)", "s = (K @ qvec)"),
+    ("lse without max", "return (w @ V) / l, m + math.log(l)", "return (w @ V) / l, math.log(l)"),
+    ("unnormalised", "return (w @ V) / l, m + math.log(l)", "return (w @ V), m + math.log(l)"),
+    ("transposed page/slot", "pool[page_row[t // page_size], t % page_size]",
+     "pool[page_row[t % page_size], t // page_size]"),
+    ("causal off by one", "max(0, int(L) - (q_per_req - 1 - i))", "max(0, int(L) - (q_per_req - i))"),
+    ("causal reversed", "max(0, int(L) - (q_per_req - 1 - i))", "max(0, int(L) - i)"),
+    ("head map modulo", "g = h // G\n                out[b, i, h]", "g = h % Hkv\n                out[b, i, h]"),
+    ("split floor", "c = -(-n // num_splits) if n else 0", "c = max(1, n // num_splits) if n else 0"),
+    ("split unclipped", "return min(p0 * page_size, L), min(p1 * page_size, L)",
+     "return p0 * page_size, p1 * page_size"),
+    ("merge linear weights", "w = np.exp(l2[r] - m)", "w = l2[r] - m + 1.0"),
+    ("merge lse drops max", "lse[r] = m + math.log(tot)", "lse[r] = math.log(tot)"),
+    ("softmax sign", "w = np.exp(s - m)", "w = np.exp(m - s)"),
+]
+
+METADATA_MUTANTS = [
+    ("no clamp", "cache = [max(L, 0) for L in seq_lens]", "cache = [L for L in seq_lens]"),
+    ("inclusive prefix", "cu_k = [0]\n    for L in cache:\n        cu_k.append(cu_k[-1] + L)",
+     "cu_k = []\n    acc = 0\n    for L in cache:\n        acc += L\n        cu_k.append(acc)\n    cu_k.append(acc)"),
+    ("floor page count", "n = -(-cache[b] // page_size)", "n = cache[b] // page_size"),
+    ("slot column", "col = j * page_size", "col = j"),
+    ("sentinel passthrough", "pt[b, j] = slot // page_size if slot >= 0 else 0", "pt[b, j] = slot // page_size"),
+    ("rpi unchecked", "if r < 0 or r >= R:\n            continue", "if False:\n            continue"),
+    ("strided off by one", "cu_q = [b * int(q_stride) for b in range(B + 1)]",
+     "cu_q = [(b + 1) * int(q_stride) for b in range(B + 1)]"),
+]
+
+
+def _mutant(module, old, new):
+    src = inspect.getsource(module)
+    assert src.count(old) >= 1, f"mutation site not found: {old!r}"
+    src = src.replace(old, new)
+    m = types.ModuleType(module.__name__ + "_mutant")
+    m.__package__ = module.__package__
+    exec(compile(src, module.__name__ + "_mutant", "exec"), m.__dict__)
+    return m
+
+
+def _attention_pins():
+    g = TA._load_attention_golden()
+    pins = [lambda c=c: TA.test_hand_derived_cases(c) for c in g["cases"]]
+    pins += [TA.test_hand_derived_split_case,
+             lambda: TA.test_matches_library_sdpa_on_dense_inputs(False, 1),
+             lambda: TA.test_matches_library_sdpa_on_dense_inputs(True, 4),
+             TA.test_length_one_gives_v0_exactly, TA.test_equal_scores_give_mean_of_v,
+             TA.test_two_tokens_closed_form, TA.test_gqa_equals_mha_with_repeated_kv_heads,
+             TA.test_mtp_query_equals_single_query_decode_on_shorter_cache,
+             lambda: TA.test_split_then_merge_equals_unsplit(4),
+             TA.test_split_ranges_partition_the_tokens]
+    return pins
+
+
+def _metadata_pins():
+    import oracle.metadata as OM
+    pins = [lambda m=m, k=k, e=e: TM.test_hand_built_batch(m, k, e) for (m, k, e) in [
+        (OM.Q_STRIDED, "cu_seqlens_q_strided", {}),
+        (OM.Q_CUMSUM, "cu_seqlens_q_cumsum", {"q_in": "q_lens"}),
+        (OM.Q_PRESET, "cu_seqlens_q_preset", {"q_in": "cu_q_preset"})]]
+    pins += [TM.test_sentinels_never_produce_negative_or_out_of_range_ids]
+    return pins
+
+
+def _some_pin_fails(pins):
+    for p in pins:
+        try:
+            p()
+        except Exception:
+            return True
+    return False
+
+
+def test_real_oracle_passes_every_pin():
+    assert not _some_pin_fails(_attention_pins())
+    assert not _some_pin_fails(_metadata_pins())
+
+
+@pytest.mark.parametrize("name,old,new", ATTENTION_MUTANTS, ids=[m[0] for m in ATTENTION_MUTANTS])
+def test_attention_mutant_is_caught(monkeypatch, name, old, new):
+    monkeypatch.setattr(TA, "OA", _mutant(real_attention, old, new))
+    assert _some_pin_fails(_attention_pins()), f"no pin caught mutant '{name}'"
+
+
+@pytest.mark.parametrize("name,old,new", METADATA_MUTANTS, ids=[m[0] for m in METADATA_MUTANTS])
+def test_metadata_mutant_is_caught(monkeypatch, name, old, new):
+    monkeypatch.setattr(TM, "OM", _mutant(real_metadata, old, new))
+    assert _some_pin_fails(_metadata_pins()), f"no pin caught mutant '{name}'"
