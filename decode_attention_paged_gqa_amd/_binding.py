@@ -1,0 +1,306 @@
+"""ctypes binding of libdecode_attn.so.
+
+Argument marshalling only: these wrappers check tensor devices, dtypes,
+shapes and contiguity, allocate outputs with torch when the caller passes
+none, and hand raw device pointers plus torch's current HIP stream to the C
+entry points of the same names.  Every computation runs in the HIP kernels;
+there is no fallback, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
+
+DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_LAUNCH = 0, 1, 2, 3
+DA_FP32, DA_BF16 = 0, 1
+DA_Q_STRIDED, DA_Q_CUMSUM, DA_Q_PRESET = 0, 1, 2
+DA_MAX_SPLITS = 256
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F32 = ctypes.c_float
+
+_SIGS = {
+    "decode_attn_metadata": [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _I32,
+                             _P, _P, _P, _P, _P],
+    "decode_attn_split": [_P, _I32, _P, _P, _P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I32,
+                          _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
+    "decode_attn_split_int8": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _I32, _I32, _I32,
+                               _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
+    "decode_attn_split_int4": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _I32, _I32, _I32,
+                               _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
+    "decode_attn_merge": [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P],
+    "decode_attn_pick_splits": [_P, _P, _I32, _I32, _I32, _I32, _I32],
+    "decode_attn_gather_kv": [_P, _I64, _I32, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P],
+    "decode_attn_strerror": [_I32],
+    "decode_attn_version": [],
+}
+
+EXPORTS = tuple(_SIGS)
+
+
+class DecodeAttnError(ValueError):
+    """A C entry point returned a non-zero status."""
+
+
+def load(path: Optional[str] = None):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m decode_attention_paged_gqa_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "decode_attn_strerror" else ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != DA_OK:
+        msg = load().decode_attn_strerror(status).decode()
+        raise DecodeAttnError(f"{what}: status {status} ({msg})")
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, has {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+# ------------------------------------------------------------------ metadata
+def decode_attn_metadata(seq_lens, req_pool_indices, req_to_token, page_size, max_pages,
+                         q_mode=DA_Q_STRIDED, q_in=None, q_stride=1, out=None):
+    """cache_seqlens, cu_seqlens_k, cu_seqlens_q, page_table in one launch.
+
+    Returns a dict of int32 tensors (those in ``out`` are reused)."""
+    lib = load()
+    dev = seq_lens.device
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    _need(req_pool_indices, "req_pool_indices", torch.int64, dev, 1)
+    _need(req_to_token, "req_to_token", torch.int32, dev, 2)
+    B = seq_lens.shape[0]
+    if req_pool_indices.shape[0] != B:
+        raise ValueError("req_pool_indices length != batch")
+    if q_in is not None:
+        _need(q_in, "q_in", torch.int32, dev, 1)
+    out = dict(out or {})
+    mk = lambda k, n: out.get(k) if out.get(k) is not None else torch.empty(n, dtype=torch.int32, device=dev)
+    out["cache_seqlens"] = mk("cache_seqlens", (B,))
+    out["cu_seqlens_k"] = mk("cu_seqlens_k", (B + 1,))
+    out["cu_seqlens_q"] = mk("cu_seqlens_q", (B + 1,))
+    out["page_table"] = mk("page_table", (B, max_pages))
+    for k in ("cache_seqlens", "cu_seqlens_k", "cu_seqlens_q", "page_table"):
+        _need(out[k], k, torch.int32, dev)
+    if tuple(out["page_table"].shape) != (B, max_pages):
+        raise ValueError("page_table must be [batch, max_pages]")
+    st = lib.decode_attn_metadata(
+        _ptr(seq_lens), _ptr(req_pool_indices), _ptr(req_to_token), req_to_token.shape[0],
+        req_to_token.shape[1], req_to_token.stride(0), B, page_size, max_pages, q_mode,
+        _ptr(q_in), q_stride, _ptr(out["cache_seqlens"]), _ptr(out["cu_seqlens_k"]),
+        _ptr(out["cu_seqlens_q"]), _ptr(out["page_table"]), _stream(dev))
+    _check(st, "decode_attn_metadata")
+    return out
+
+
+# ------------------------------------------------------------------ stage 1
+def _partials(q, num_splits, o_partial, lse_partial):
+    B, qn, Hq, D = q.shape
+    if o_partial is None:
+        o_partial = torch.empty((B, qn, Hq, num_splits, D), dtype=torch.float32, device=q.device)
+    if lse_partial is None:
+        lse_partial = torch.empty((B, qn, Hq, num_splits), dtype=torch.float32, device=q.device)
+    _need(o_partial, "o_partial", torch.float32, q.device)
+    _need(lse_partial, "lse_partial", torch.float32, q.device)
+    if o_partial.numel() != B * qn * Hq * num_splits * D or lse_partial.numel() != B * qn * Hq * num_splits:
+        raise ValueError("partial buffers are sized for a different num_splits")
+    return o_partial, lse_partial
+
+
+def _q_code(q):
+    if q.dtype == torch.bfloat16:
+        return DA_BF16
+    if q.dtype == torch.float32:
+        return DA_FP32
+    raise TypeError(f"q dtype {q.dtype} unsupported")
+
+
+def _split_common(q, page_table, cache_seqlens, num_pages_dim):
+    _need(q, "q", (torch.bfloat16, torch.float32), ndim=4)
+    dev = q.device
+    _need(page_table, "page_table", torch.int32, dev, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    if page_table.shape[0] != q.shape[0] or cache_seqlens.shape[0] != q.shape[0]:
+        raise ValueError("batch mismatch between q, page_table and cache_seqlens")
+    return dev
+
+
+def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
+                      softmax_scale=None, causal=False, o_partial=None, lse_partial=None):
+    """Stage 1 over a dense bf16 / fp32 cache.  Returns (o_partial, lse_partial)."""
+    lib = load()
+    dev = _split_common(q, page_table, cache_seqlens, None)
+    _need(k_pool, "k_pool", q.dtype, dev, 4)
+    _need(v_pool, "v_pool", q.dtype, dev, 4)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool / v_pool shapes differ")
+    P, S_p, Hkv, D = k_pool.shape
+    B, qn, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("head_dim mismatch")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
+    st = lib.decode_attn_split(
+        _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), page_table.stride(0),
+        page_table.shape[1], _ptr(cache_seqlens), B, qn, Hq, Hkv, D, S_p, P, num_splits, scale,
+        int(bool(causal)), _ptr(o_partial), _ptr(lse_partial), _stream(dev))
+    _check(st, "decode_attn_split")
+    return o_partial, lse_partial
+
+
+def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cache_seqlens,
+                           num_splits, softmax_scale=None, causal=False, o_partial=None,
+                           lse_partial=None):
+    """Stage 1 over an INT8 cache (fp16 scale per token and kv-head)."""
+    lib = load()
+    dev = _split_common(q, page_table, cache_seqlens, None)
+    _need(k_pool, "k_pool", torch.int8, dev, 4)
+    _need(v_pool, "v_pool", torch.int8, dev, 4)
+    _need(k_scale, "k_scale", torch.float16, dev, 3)
+    _need(v_scale, "v_scale", torch.float16, dev, 3)
+    P, S_p, Hkv, D = k_pool.shape
+    if v_pool.shape != k_pool.shape or tuple(k_scale.shape) != (P, S_p, Hkv) or k_scale.shape != v_scale.shape:
+        raise ValueError("int8 pool / scale shapes inconsistent")
+    B, qn, Hq, _ = q.shape
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
+    st = lib.decode_attn_split_int8(
+        _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+        _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens), B, qn,
+        Hq, Hkv, D, S_p, P, num_splits, scale, int(bool(causal)), _ptr(o_partial),
+        _ptr(lse_partial), _stream(dev))
+    _check(st, "decode_attn_split_int8")
+    return o_partial, lse_partial
+
+
+def decode_attn_split_int4(q, k_pool, v_pool, k_scale_zero, v_scale_zero, page_table,
+                           cache_seqlens, num_splits, softmax_scale=None, causal=False,
+                           o_partial=None, lse_partial=None):
+    """Stage 1 over an INT4 cache (fp16 (scale, zero) per 32-group along D)."""
+    lib = load()
+    dev = _split_common(q, page_table, cache_seqlens, None)
+    _need(k_pool, "k_pool", torch.uint8, dev, 4)
+    _need(v_pool, "v_pool", torch.uint8, dev, 4)
+    _need(k_scale_zero, "k_scale_zero", torch.float16, dev, 5)
+    _need(v_scale_zero, "v_scale_zero", torch.float16, dev, 5)
+    P, S_p, Hkv, Dh = k_pool.shape
+    D = 2 * Dh
+    if v_pool.shape != k_pool.shape or tuple(k_scale_zero.shape) != (P, S_p, Hkv, D // 32, 2) \
+            or k_scale_zero.shape != v_scale_zero.shape:
+        raise ValueError("int4 pool / scale-zero shapes inconsistent")
+    B, qn, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("head_dim mismatch")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
+    st = lib.decode_attn_split_int4(
+        _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale_zero), _ptr(v_scale_zero),
+        _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens), B, qn,
+        Hq, Hkv, D, S_p, P, num_splits, scale, int(bool(causal)), _ptr(o_partial),
+        _ptr(lse_partial), _stream(dev))
+    _check(st, "decode_attn_split_int4")
+    return o_partial, lse_partial
+
+
+# ------------------------------------------------------------------ stage 2
+def decode_attn_merge(o_partial, lse_partial, out_dtype=torch.bfloat16, out=None, lse_out=None,
+                      want_lse=False):
+    """LSE merge of the split partials.  Returns out (and lse if requested)."""
+    lib = load()
+    _need(o_partial, "o_partial", torch.float32, ndim=5)
+    dev = o_partial.device
+    _need(lse_partial, "lse_partial", torch.float32, dev, 4)
+    B, qn, Hq, S, D = o_partial.shape
+    if tuple(lse_partial.shape) != (B, qn, Hq, S):
+        raise ValueError("lse_partial shape mismatch")
+    if out is None:
+        out = torch.empty((B, qn, Hq, D), dtype=out_dtype, device=dev)
+    _need(out, "out", (torch.bfloat16, torch.float32), dev)
+    if want_lse and lse_out is None:
+        lse_out = torch.empty((B, qn, Hq), dtype=torch.float32, device=dev)
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, dev)
+    code = DA_BF16 if out.dtype == torch.bfloat16 else DA_FP32
+    st = lib.decode_attn_merge(_ptr(o_partial), _ptr(lse_partial), B, qn, Hq, D, S, _ptr(out),
+                               code, _ptr(lse_out), _stream(dev))
+    _check(st, "decode_attn_merge")
+    return (out, lse_out) if (want_lse or lse_out is not None) else out
+
+
+# ------------------------------------------------------------------ helpers
+def decode_attn_pick_splits(table, batch_keys, bucket_tokens, batch, kv_len) -> int:
+    """Host lookup of num_splits from a [n_batch_keys, n_buckets] table."""
+    lib = load()
+    t = (ctypes.c_int32 * (len(table) * len(table[0])))(*[int(x) for row in table for x in row])
+    k = (ctypes.c_int32 * len(batch_keys))(*[int(x) for x in batch_keys])
+    s = lib.decode_attn_pick_splits(ctypes.cast(t, _P), ctypes.cast(k, _P), len(batch_keys),
+                                    len(table[0]), int(bucket_tokens), int(batch), int(kv_len))
+    if s < 1:
+        _check(-s, "decode_attn_pick_splits")
+    return int(s)
+
+
+def decode_attn_gather_kv(pool, page_table, cache_seqlens, cu_seqlens_k, total_tokens, out=None):
+    """Dense [total_tokens, *pool.shape[2:]] copy of every request's tokens (test hook)."""
+    lib = load()
+    dev = pool.device
+    _need(pool, "pool", None, dev)
+    _need(page_table, "page_table", torch.int32, dev, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev, 1)
+    P, S_p = pool.shape[:2]
+    token_bytes = pool[0, 0].numel() * pool.element_size()
+    if out is None:
+        out = torch.empty((total_tokens,) + tuple(pool.shape[2:]), dtype=pool.dtype, device=dev)
+    _need(out, "out", pool.dtype, dev)
+    st = lib.decode_attn_gather_kv(_ptr(pool), token_bytes, S_p, P, _ptr(page_table),
+                                   page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
+                                   _ptr(cu_seqlens_k), page_table.shape[0], _ptr(out), _stream(dev))
+    _check(st, "decode_attn_gather_kv")
+    return out
+
+
+def decode_attn_version() -> int:
+    return int(load().decode_attn_version())

@@ -1,0 +1,97 @@
+// Stage 2: log-sum-exp merge of the split partials (LightLLM PR #1549,
+// "Covered decode kernels": the second stage of the two-stage decode
+// attention).  For one query row with split results (O_s, lse_s):
+//   m = max_s lse_s, w_s = exp(lse_s - m),
+//   out = sum_s w_s O_s / sum_s w_s,  lse = m + ln(sum_s w_s).
+// A row whose splits are all empty (every lse_s = -inf) yields 0 / -inf.
+//
+// One wave per query row; the reduction over splits stays in registers:
+// every lane owns D/64 output elements and walks all splits itself, the
+// split weights being wave-uniform.
+#include "common.h"
+
+namespace {
+
+constexpr int kWaves = 4;
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restrict__ op,
+                                                           const float* __restrict__ lp,
+                                                           int rows, int S, void* __restrict__ out,
+                                                           float* __restrict__ lse_out) {
+  constexpr int E = D / 64;  // elements per lane
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* l = lp + (long long)row * S;
+  float m = da::kNegInf;
+  for (int s = lane; s < S; s += 64) m = fmaxf(m, l[s]);
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (m != da::kNegInf) {
+    const float* o = op + (long long)row * S * D + lane * E;
+    const float ml = m * da::kLog2e;
+    for (int s = 0; s < S; ++s) {
+      const float w = da::fast_exp2(fmaf(l[s], da::kLog2e, -ml));  // exp(lse_s - m); 0 for -inf
+      wsum += w;
+      if (E == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(o + (long long)s * D);
+        acc[0] = fmaf(w, v.x, acc[0]);
+        acc[E - 1] = fmaf(w, v.y, acc[E - 1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(w, o[(long long)s * D + e], acc[e]);
+      }
+    }
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= inv;
+  }
+  if (OUT_BF16) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(out) + (long long)row * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e] = da::float_to_bf16_rne(acc[e]);
+  } else {
+    float* dst = reinterpret_cast<float*>(out) + (long long)row * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e] = acc[e];
+  }
+  if (lse_out && lane == 0) lse_out[row] = (m == da::kNegInf) ? m : m + logf(wsum);
+}
+
+template <int D, bool B16>
+int32_t launch(const float* op, const float* lp, int rows, int S, void* out, float* lse_out,
+               hipStream_t st) {
+  const int blocks = (rows + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL((merge_kernel<D, B16>), dim3(blocks), dim3(64 * kWaves), 0, st, op, lp, rows,
+                     S, out, lse_out);
+  return da_host::launch_status();
+}
+
+}  // namespace
+
+extern "C" int32_t decode_attn_merge(const float* o_partial, const float* lse_partial,
+                                     int32_t batch, int32_t q_per_req, int32_t num_q_heads,
+                                     int32_t head_dim, int32_t num_splits, void* out,
+                                     int32_t out_dtype, float* lse_out, void* stream) {
+  if (!o_partial || !lse_partial || !out) return DA_ERR_INVALID_ARG;
+  if (batch <= 0 || q_per_req <= 0 || num_q_heads <= 0 || num_splits <= 0 ||
+      num_splits > DA_MAX_SPLITS || q_per_req > DA_MAX_Q_PER_REQ)
+    return DA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return DA_ERR_UNSUPPORTED;
+  if (out_dtype != DA_BF16 && out_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
+  const long long rows_ll = (long long)batch * q_per_req * num_q_heads;
+  if (rows_ll > (1ll << 30)) return DA_ERR_INVALID_ARG;
+  const int rows = (int)rows_ll;
+  hipStream_t st = (hipStream_t)stream;
+  const bool b16 = out_dtype == DA_BF16;
+  if (head_dim == 128)
+    return b16 ? launch<128, true>(o_partial, lse_partial, rows, num_splits, out, lse_out, st)
+               : launch<128, false>(o_partial, lse_partial, rows, num_splits, out, lse_out, st);
+  return b16 ? launch<64, true>(o_partial, lse_partial, rows, num_splits, out, lse_out, st)
+             : launch<64, false>(o_partial, lse_partial, rows, num_splits, out, lse_out, st);
+}

@@ -1,0 +1,105 @@
+// Decode metadata prelude: cache_seqlens, cu_seqlens_k/q and page_table in
+// one launch (SGLang PR #29843 digest, "Implementation breakdown": one
+// program per batch row, three q modes, -1 sentinel guard; its tests cover
+// a zero-padded page-table tail).
+//
+// One 256-thread workgroup per batch row b.  Row b computes its own
+// exclusive prefix over rows [0, b) with a workgroup reduction, so no
+// cross-workgroup scan (and no second launch) is needed; the last row also
+// writes the closing entries cu_*[B].  Prefix sums are formed in 64-bit and
+// stored as int32.
+#include "common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ long long block_sum(long long v, long long* sh) {
+  // wave reduction, then across the 4 waves through LDS
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  return sh[0] + sh[1] + sh[2] + sh[3];
+}
+
+__global__ __launch_bounds__(kThreads) void metadata_kernel(
+    const int32_t* __restrict__ seq_lens, const int64_t* __restrict__ rpi,
+    const int32_t* __restrict__ r2t, long long r2t_rows, long long r2t_cols,
+    long long r2t_stride, int batch, int page_size, int max_pages, int q_mode,
+    const int32_t* __restrict__ q_in, int q_stride, int32_t* __restrict__ cache_seqlens,
+    int32_t* __restrict__ cu_k, int32_t* __restrict__ cu_q, int32_t* __restrict__ page_table) {
+  __shared__ long long sh[4];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+
+  // ---- exclusive prefix of clamped lengths (and of q lengths for cumsum)
+  long long pk = 0, pq = 0;
+  for (int j = tid; j < b; j += kThreads) {
+    pk += max(seq_lens[j], 0);
+    if (q_mode == DA_Q_CUMSUM) pq += max(q_in[j], 0);
+  }
+  pk = block_sum(pk, sh);
+  if (q_mode == DA_Q_CUMSUM) pq = block_sum(pq, sh);
+
+  const int L = max(seq_lens[b], 0);
+  if (tid == 0) {
+    cache_seqlens[b] = L;
+    cu_k[b] = (int32_t)pk;
+    int32_t cq;
+    if (q_mode == DA_Q_STRIDED) cq = (int32_t)((long long)b * q_stride);
+    else if (q_mode == DA_Q_CUMSUM) cq = (int32_t)pq;
+    else cq = q_in[b];
+    cu_q[b] = cq;
+    if (b == batch - 1) {
+      cu_k[batch] = (int32_t)(pk + L);
+      if (q_mode == DA_Q_STRIDED) cu_q[batch] = (int32_t)((long long)batch * q_stride);
+      else if (q_mode == DA_Q_CUMSUM) cu_q[batch] = (int32_t)(pq + max(q_in[b], 0));
+      else cu_q[batch] = q_in[batch];
+    }
+  }
+
+  // ---- page-table row: first slot of every page / page_size, zero tail
+  const long long n = ((long long)L + page_size - 1) / page_size;
+  const long long r = rpi[b];
+  const bool row_ok = r >= 0 && r < r2t_rows;
+  const int32_t* row = r2t + (row_ok ? r : 0) * r2t_stride;
+  int32_t* out = page_table + (long long)b * max_pages;
+  for (int j = tid; j < max_pages; j += kThreads) {
+    int32_t v = 0;
+    const long long col = (long long)j * page_size;
+    if (row_ok && j < n && col < r2t_cols) {
+      const int32_t slot = row[col];
+      v = slot >= 0 ? slot / page_size : 0;
+    }
+    out[j] = v;
+  }
+}
+
+}  // namespace
+
+extern "C" int32_t decode_attn_metadata(const int32_t* seq_lens, const int64_t* req_pool_indices,
+                                        const int32_t* req_to_token, int64_t req_to_token_rows,
+                                        int64_t req_to_token_cols, int64_t req_to_token_stride,
+                                        int32_t batch, int32_t page_size, int32_t max_pages,
+                                        int32_t q_mode, const int32_t* q_in, int32_t q_stride,
+                                        int32_t* cache_seqlens, int32_t* cu_seqlens_k,
+                                        int32_t* cu_seqlens_q, int32_t* page_table, void* stream) {
+  if (!seq_lens || !req_pool_indices || !req_to_token || !cache_seqlens || !cu_seqlens_k ||
+      !cu_seqlens_q || !page_table)
+    return DA_ERR_INVALID_ARG;
+  if (batch <= 0 || page_size <= 0 || max_pages <= 0 || req_to_token_rows <= 0 ||
+      req_to_token_cols <= 0 || req_to_token_stride < req_to_token_cols)
+    return DA_ERR_INVALID_ARG;
+  if (q_mode != DA_Q_STRIDED && q_mode != DA_Q_CUMSUM && q_mode != DA_Q_PRESET)
+    return DA_ERR_INVALID_ARG;
+  if (q_mode != DA_Q_STRIDED && !q_in) return DA_ERR_INVALID_ARG;
+  if (q_mode == DA_Q_STRIDED && q_stride < 0) return DA_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(metadata_kernel, dim3(batch), dim3(kThreads), 0, (hipStream_t)stream,
+                     seq_lens, req_pool_indices, req_to_token, (long long)req_to_token_rows,
+                     (long long)req_to_token_cols, (long long)req_to_token_stride, batch,
+                     page_size, max_pages, q_mode, q_in, q_stride, cache_seqlens, cu_seqlens_k,
+                     cu_seqlens_q, page_table);
+  return da_host::launch_status();
+}

@@ -1,0 +1,464 @@
+// Stage 1 of split-KV decode attention, vector-ALU path (GQA flash decode
+// "stage 1", its INT8 / INT4 KV variants and the num_splits KV-cache decode
+// of LightLLM PR #1549, section "Covered decode kernels").
+//
+// One workgroup (4 waves) per (kv-head g, split s, request b).  The G*q
+// query rows that read kv-head g are all served by that workgroup, so each
+// K/V byte of the split is fetched from HBM exactly once.
+//
+// Lane layout inside a wave: 16 lanes per token row, 4 tokens per step,
+// 4 steps per 16-token tile.  Lane (tl, c) owns elements [c*E, c*E + E) of
+// its token's row (E = D/16), loaded as one contiguous vector, so a wave's
+// load of 4 rows touches whole 64-to-512-byte row segments (coalesced).
+// Tiles of the split are dealt round-robin to the 4 waves; each wave keeps
+// its own online-softmax state (running max m, sum l, output acc) and the
+// four states are combined through LDS at the end.
+//
+// Scores are kept in log2 units: q is pre-multiplied by softmax_scale*log2(e)
+// and exponentials are exp2; the stored LSE is converted back to natural log.
+//
+// Quantised caches: INT8 rows are x = code * s_tok (s_tok folded into the
+// score after the dot product and into p before P*V); INT4 rows are
+// x = (nib - z) * s per 32-group, each lane's E elements lying inside one
+// group, so (nib - z) is formed exactly and s is folded into the lane's
+// partial dot product and into p.
+#include "common.h"
+
+namespace {
+
+enum KvKind { KV_BF16 = 0, KV_F32 = 1, KV_I8 = 2, KV_I4 = 3 };
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+struct SplitArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint16_t* ks;  // int8: [P,S,Hkv]; int4: [P,S,Hkv,D/32,2]
+  const uint16_t* vs;
+  const int32_t* pt;
+  const int32_t* seqlens;
+  float* o;
+  float* lse;
+  int q_bf16;
+  int pt_stride, max_pages;
+  int qn, Hq, Hkv, G, R;
+  int page_size, log2_ps, num_pages, S;
+  float scale_log2;
+  int causal;
+};
+
+template <int BYTES>
+struct Raw {
+  uint32_t w[(BYTES + 3) / 4];
+};
+
+template <int BYTES>
+__device__ __forceinline__ void load_raw(const uint8_t* p, Raw<BYTES>& r) {
+  if constexpr (BYTES == 32) {
+    const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+    r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
+  } else if constexpr (BYTES == 16) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+  } else if constexpr (BYTES == 8) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = a.x; r.w[1] = a.y;
+  } else if constexpr (BYTES == 4) {
+    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else {
+    r.w[0] = *reinterpret_cast<const uint16_t*>(p);
+  }
+}
+
+template <int BYTES>
+__device__ __forceinline__ void zero_raw(Raw<BYTES>& r) {
+#pragma unroll
+  for (int i = 0; i < (BYTES + 3) / 4; ++i) r.w[i] = 0u;
+}
+
+template <int KV, int D>
+struct Kv;
+
+template <int D>
+struct Kv<KV_BF16, D> {
+  static constexpr int E = D / 16;
+  static constexpr int BYTES = E * 2;
+  static constexpr int ROW_BYTES = D * 2;
+  __device__ static void to_float(const Raw<BYTES>& r, float* f) {
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+      f[2 * i] = da::bf16_lo(r.w[i]);
+      f[2 * i + 1] = da::bf16_hi(r.w[i]);
+    }
+  }
+};
+
+template <int D>
+struct Kv<KV_F32, D> {
+  static constexpr int E = D / 16;
+  static constexpr int BYTES = E * 4;
+  static constexpr int ROW_BYTES = D * 4;
+  __device__ static void to_float(const Raw<BYTES>& r, float* f) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) f[i] = __uint_as_float(r.w[i]);
+  }
+};
+
+template <int D>
+struct Kv<KV_I8, D> {
+  static constexpr int E = D / 16;
+  static constexpr int BYTES = E;
+  static constexpr int ROW_BYTES = D;
+  __device__ static void to_float(const Raw<BYTES>& r, float* f) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) f[i] = da::sbyte_to_float(r.w[i / 4], i % 4);
+  }
+};
+
+template <int D>
+struct Kv<KV_I4, D> {
+  static constexpr int E = D / 16;
+  static constexpr int BYTES = E / 2;
+  static constexpr int ROW_BYTES = D / 2;
+  __device__ static void to_float(const Raw<BYTES>& r, float* f) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) f[i] = (float)((r.w[i / 8] >> (4 * (i % 8))) & 15u);
+  }
+};
+
+template <int KV, int D, int RT>
+__global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) {
+  using P = Kv<KV, D>;
+  constexpr int E = P::E;
+  constexpr int NG = D / 32;  // int4 groups per row
+
+  __shared__ float sm_m[kWaves][RT];
+  __shared__ float sm_l[kWaves][RT];
+  __shared__ float sm_acc[kWaves][RT][D];
+
+  const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tl = lane >> 4, c = lane & 15;
+
+  const int ps = a.page_size;
+  const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
+  const int n = (L + ps - 1) >> a.log2_ps;
+  const int cpg = (n + a.S - 1) / a.S;
+  const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
+  const int t0 = p0 * ps, t1 = min(p1 * ps, L);
+
+  // ---- query rows r = i*G + hh (query token i, head g*G + hh), pre-scaled
+  float qf[RT][E];
+  int tend[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    if (r < a.R) {
+      const int i = r / a.G, h = g * a.G + (r % a.G);
+      const long long qoff = (((long long)b * a.qn + i) * a.Hq + h) * D + c * E;
+      if (a.q_bf16) {
+        Raw<E * 2> qr;
+        load_raw<E * 2>(reinterpret_cast<const uint8_t*>(a.q) + qoff * 2, qr);
+        float f[E];
+        Kv<KV_BF16, D>::to_float(qr, f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) qf[r][e] = f[e] * a.scale_log2;
+      } else {
+        const float* qp = reinterpret_cast<const float*>(a.q) + qoff;
+#pragma unroll
+        for (int e = 0; e < E; ++e) qf[r][e] = qp[e] * a.scale_log2;
+      }
+      tend[r] = a.causal ? L - (a.qn - 1 - i) : L;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) qf[r][e] = 0.f;
+      tend[r] = 0;
+    }
+  }
+
+  float m[RT], l[RT], acc[RT][E];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    m[r] = da::kNegInf;
+    l[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[r][e] = 0.f;
+  }
+
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.k);
+  const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.v);
+  const int ntiles = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
+
+  for (int tile = wave; tile < ntiles; tile += kWaves) {
+    const int tb = t0 + (tile << 4);
+    int pid = a.pt[(long long)b * a.pt_stride + (tb >> a.log2_ps)];
+    if ((unsigned)pid >= (unsigned)a.num_pages) pid = 0;
+    const int slot0 = tb & (ps - 1);
+
+    Raw<P::BYTES> kr[4], vr[4];
+    float kscale[4], kzero[4], vscale[4], vzero[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int t = tb + st * 4 + tl;
+      kscale[st] = vscale[st] = 1.f;
+      kzero[st] = vzero[st] = 0.f;
+      if (t < t1) {
+        const long long row = ((long long)pid * ps + slot0 + st * 4 + tl) * a.Hkv + g;
+        load_raw<P::BYTES>(kb + row * P::ROW_BYTES + c * P::BYTES, kr[st]);
+        load_raw<P::BYTES>(vb + row * P::ROW_BYTES + c * P::BYTES, vr[st]);
+        if constexpr (KV == KV_I8) {
+          kscale[st] = da::half_bits_to_float(a.ks[row]);
+          vscale[st] = da::half_bits_to_float(a.vs[row]);
+        } else if constexpr (KV == KV_I4) {
+          const long long sz = (row * NG + (c * E) / 32) * 2;
+          kscale[st] = da::half_bits_to_float(a.ks[sz]);
+          kzero[st] = da::half_bits_to_float(a.ks[sz + 1]);
+          vscale[st] = da::half_bits_to_float(a.vs[sz]);
+          vzero[st] = da::half_bits_to_float(a.vs[sz + 1]);
+        }
+      } else {
+        zero_raw<P::BYTES>(kr[st]);
+        zero_raw<P::BYTES>(vr[st]);
+      }
+    }
+
+    // ---- scores (log2 units); invisible tokens -> -inf
+    float sc[4][RT];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      float kf[E];
+      P::to_float(kr[st], kf);
+      if constexpr (KV == KV_I4) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) kf[e] -= kzero[st];
+      }
+      const int t = tb + st * 4 + tl;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) d = fmaf(qf[r][e], kf[e], d);
+        if constexpr (KV == KV_I4) d *= kscale[st];
+        d += da::xor_shfl<1>(d);
+        d += da::xor_shfl<2>(d);
+        d += da::xor_shfl<4>(d);
+        d += da::xor_shfl<8>(d);
+        if constexpr (KV == KV_I8) d *= kscale[st];
+        sc[st][r] = (t < t1 && t < tend[r]) ? d : da::kNegInf;
+      }
+    }
+
+    // ---- online softmax; the running max is wave-uniform
+    float p[4][RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      float mx = fmaxf(fmaxf(sc[0][r], sc[1][r]), fmaxf(sc[2][r], sc[3][r]));
+      mx = fmaxf(mx, da::xor_shfl<16>(mx));
+      mx = fmaxf(mx, da::xor_shfl<32>(mx));
+      const float mn = fmaxf(m[r], mx);
+      if (mn == da::kNegInf) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) p[st][r] = 0.f;
+        continue;
+      }
+      const float alpha = da::fast_exp2(m[r] - mn);
+      float psum = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        p[st][r] = da::fast_exp2(sc[st][r] - mn);
+        psum += p[st][r];
+      }
+      l[r] = fmaf(l[r], alpha, psum);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[r][e] *= alpha;
+      m[r] = mn;
+    }
+
+    // ---- acc += p * V
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      float vf[E];
+      P::to_float(vr[st], vf);
+      if constexpr (KV == KV_I4) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) vf[e] -= vzero[st];
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        float pr = p[st][r];
+        if constexpr (KV == KV_I8 || KV == KV_I4) pr *= vscale[st];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[r][e] = fmaf(pr, vf[e], acc[r][e]);
+      }
+    }
+  }
+
+  // ---- sum the 4 token lanes of the wave (same running max)
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    l[r] += da::xor_shfl<16>(l[r]);
+    l[r] += da::xor_shfl<32>(l[r]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      acc[r][e] += da::xor_shfl<16>(acc[r][e]);
+      acc[r][e] += da::xor_shfl<32>(acc[r][e]);
+    }
+  }
+  if (tl == 0) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) sm_acc[wave][r][c * E + e] = acc[r][e];
+      if (c == 0) {
+        sm_m[wave][r] = m[r];
+        sm_l[wave][r] = l[r];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- combine the 4 waves and write this split's partial rows
+  for (int idx = threadIdx.x; idx < a.R * D; idx += kThreads) {
+    const int r = idx / D, d = idx - r * D;
+    float M = da::kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][r]);
+    float lsum = 0.f, o = 0.f;
+    if (M != da::kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = da::fast_exp2(sm_m[w][r] - M);
+        lsum = fmaf(sm_l[w][r], f, lsum);
+        o = fmaf(sm_acc[w][r][d], f, o);
+      }
+    }
+    const int i = r / a.G, h = g * a.G + (r % a.G);
+    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.S + s;
+    a.o[orow * D + d] = lsum > 0.f ? o / lsum : 0.f;
+    if (d == 0) a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum)) * da::kLn2 : da::kNegInf;
+  }
+}
+
+template <int KV, int D, int RT>
+int32_t launch_rt(const SplitArgs& a, int batch, hipStream_t st) {
+  hipLaunchKernelGGL((split_fma_kernel<KV, D, RT>), dim3(a.Hkv, a.S, batch), dim3(kThreads), 0,
+                     st, a);
+  return da_host::launch_status();
+}
+
+template <int KV, int D>
+int32_t launch_d(const SplitArgs& a, int batch, hipStream_t st) {
+  const int R = a.R;
+  if (R <= 1) return launch_rt<KV, D, 1>(a, batch, st);
+  if (R <= 2) return launch_rt<KV, D, 2>(a, batch, st);
+  if (R <= 4) return launch_rt<KV, D, 4>(a, batch, st);
+  if (R <= 5) return launch_rt<KV, D, 5>(a, batch, st);
+  if (R <= 8) return launch_rt<KV, D, 8>(a, batch, st);
+  return launch_rt<KV, D, 16>(a, batch, st);
+}
+
+template <int KV>
+int32_t launch_kv(const SplitArgs& a, int D, int batch, hipStream_t st) {
+  return D == 128 ? launch_d<KV, 128>(a, batch, st) : launch_d<KV, 64>(a, batch, st);
+}
+
+int32_t check_common(const void* q, const void* k, const void* v, const int32_t* pt,
+                     int32_t pt_stride, int32_t max_pages, const int32_t* seqlens, int32_t batch,
+                     int32_t qn, int32_t Hq, int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages,
+                     int32_t S, const float* o, const float* lse) {
+  if (!q || !k || !v || !pt || !seqlens || !o || !lse) return DA_ERR_INVALID_ARG;
+  if (batch <= 0 || batch > 65535 || qn <= 0 || qn > DA_MAX_Q_PER_REQ || Hq <= 0 || Hkv <= 0 ||
+      Hq % Hkv != 0 || num_pages <= 0 || max_pages <= 0 || pt_stride < max_pages ||
+      S <= 0 || S > DA_MAX_SPLITS || ps <= 0)
+    return DA_ERR_INVALID_ARG;
+  if ((long long)max_pages * ps > (1ll << 30)) return DA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return DA_ERR_UNSUPPORTED;
+  if (!da_host::is_pow2(ps) || ps < 16 || ps > 256) return DA_ERR_UNSUPPORTED;
+  if ((Hq / Hkv) * qn > DA_MAX_ROWS) return DA_ERR_UNSUPPORTED;
+  return DA_OK;
+}
+
+SplitArgs make_args(const void* q, int q_bf16, const void* k, const void* v, const uint16_t* ks,
+                    const uint16_t* vs, const int32_t* pt, int32_t pt_stride, int32_t max_pages,
+                    const int32_t* seqlens, int32_t qn, int32_t Hq, int32_t Hkv, int32_t ps,
+                    int32_t num_pages, int32_t S, float scale, int32_t causal, float* o,
+                    float* lse) {
+  SplitArgs a;
+  a.q = q; a.k = k; a.v = v; a.ks = ks; a.vs = vs; a.pt = pt; a.seqlens = seqlens;
+  a.o = o; a.lse = lse; a.q_bf16 = q_bf16;
+  a.pt_stride = pt_stride; a.max_pages = max_pages;
+  a.qn = qn; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.R = a.G * qn;
+  a.page_size = ps; a.log2_ps = __builtin_ctz((unsigned)ps); a.num_pages = num_pages; a.S = S;
+  a.scale_log2 = scale * da::kLog2e;
+  a.causal = causal ? 1 : 0;
+  return a;
+}
+
+}  // namespace
+
+extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool,
+                                     const void* v_pool, const int32_t* page_table,
+                                     int32_t page_table_stride, int32_t max_pages,
+                                     const int32_t* cache_seqlens, int32_t batch,
+                                     int32_t q_per_req, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                     int32_t num_pages, int32_t num_splits, float softmax_scale,
+                                     int32_t causal, float* o_partial, float* lse_partial,
+                                     void* stream) {
+  int32_t st = check_common(q, k_pool, v_pool, page_table, page_table_stride, max_pages,
+                            cache_seqlens, batch, q_per_req, num_q_heads, num_kv_heads, head_dim,
+                            page_size, num_pages, num_splits, o_partial, lse_partial);
+  if (st) return st;
+  if (dtype != DA_BF16 && dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
+  const SplitArgs a = make_args(q, dtype == DA_BF16, k_pool, v_pool, nullptr, nullptr, page_table,
+                                page_table_stride, max_pages, cache_seqlens, q_per_req,
+                                num_q_heads, num_kv_heads, page_size, num_pages, num_splits,
+                                softmax_scale, causal, o_partial, lse_partial);
+  hipStream_t s = (hipStream_t)stream;
+  return dtype == DA_BF16 ? launch_kv<KV_BF16>(a, head_dim, batch, s)
+                          : launch_kv<KV_F32>(a, head_dim, batch, s);
+}
+
+extern "C" int32_t decode_attn_split_int8(
+    const void* q, int32_t q_dtype, const int8_t* k_pool, const int8_t* v_pool,
+    const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* page_table,
+    int32_t page_table_stride, int32_t max_pages, const int32_t* cache_seqlens, int32_t batch,
+    int32_t q_per_req, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t page_size, int32_t num_pages, int32_t num_splits, float softmax_scale,
+    int32_t causal, float* o_partial, float* lse_partial, void* stream) {
+  int32_t st = check_common(q, k_pool, v_pool, page_table, page_table_stride, max_pages,
+                            cache_seqlens, batch, q_per_req, num_q_heads, num_kv_heads, head_dim,
+                            page_size, num_pages, num_splits, o_partial, lse_partial);
+  if (st) return st;
+  if (!k_scale || !v_scale) return DA_ERR_INVALID_ARG;
+  if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
+  const SplitArgs a = make_args(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale, v_scale,
+                                page_table, page_table_stride, max_pages, cache_seqlens,
+                                q_per_req, num_q_heads, num_kv_heads, page_size, num_pages,
+                                num_splits, softmax_scale, causal, o_partial, lse_partial);
+  return launch_kv<KV_I8>(a, head_dim, batch, (hipStream_t)stream);
+}
+
+extern "C" int32_t decode_attn_split_int4(
+    const void* q, int32_t q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
+    const uint16_t* k_scale_zero, const uint16_t* v_scale_zero, const int32_t* page_table,
+    int32_t page_table_stride, int32_t max_pages, const int32_t* cache_seqlens, int32_t batch,
+    int32_t q_per_req, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t page_size, int32_t num_pages, int32_t num_splits, float softmax_scale,
+    int32_t causal, float* o_partial, float* lse_partial, void* stream) {
+  int32_t st = check_common(q, k_pool, v_pool, page_table, page_table_stride, max_pages,
+                            cache_seqlens, batch, q_per_req, num_q_heads, num_kv_heads, head_dim,
+                            page_size, num_pages, num_splits, o_partial, lse_partial);
+  if (st) return st;
+  if (!k_scale_zero || !v_scale_zero) return DA_ERR_INVALID_ARG;
+  if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
+  const SplitArgs a = make_args(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale_zero,
+                                v_scale_zero, page_table, page_table_stride, max_pages,
+                                cache_seqlens, q_per_req, num_q_heads, num_kv_heads, page_size,
+                                num_pages, num_splits, softmax_scale, causal, o_partial,
+                                lse_partial);
+  return launch_kv<KV_I4>(a, head_dim, batch, (hipStream_t)stream);
+}

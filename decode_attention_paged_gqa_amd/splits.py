@@ -1,0 +1,79 @@
+"""num_splits per KV-length bucket.
+
+LightLLM PR #1549 ("Covered decode kernels") tunes the split count of the
+KV-cache decode kernel once, at startup, with KV-length run keys grouped into
+buckets; the real request length picks the bucket at run time, an untuned key
+falls back to the nearest tuned one, and nothing is tuned on live requests.
+Here the tuned values live in ``splits_table.json`` (written by
+``bench.py --tune`` on the GPU), keyed by kernel variant, then by batch key,
+then by 4096-token bucket; the lookup itself is the C helper
+``decode_attn_pick_splits``.  Under graph capture, where lengths are not
+known on the host, callers key on the representative length 32768.
+"""
+from __future__ import annotations
+
+import json
+import os
+from dataclasses import dataclass, field
+from typing import Dict, List
+
+from ._binding import decode_attn_pick_splits
+
+TABLE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "splits_table.json")
+REPRESENTATIVE_KV_LEN = 32768
+BUCKET_TOKENS = 4096
+N_BUCKETS = 8
+BATCH_KEYS = (16, 32, 64)
+CANDIDATES = (1, 2, 4, 8, 16, 32)
+
+
+def kernel_key(kv: str, rows: int, head_dim: int, page_size: int) -> str:
+    """Table key of a stage-1 variant: cache format, query rows per kv-head, D, page size."""
+    return f"{kv}_r{rows}_d{head_dim}_p{page_size}"
+
+
+def _heuristic(batch_key: int, bucket: int, num_kv_heads: int = 8, cus: int = 256) -> int:
+    pages = bucket * BUCKET_TOKENS // 64
+    want = max(1, (4 * cus) // max(1, batch_key * num_kv_heads))
+    s = 1
+    while s < want and s * 2 <= min(32, max(1, pages // 4)):
+        s *= 2
+    return s
+
+
+@dataclass
+class SplitTable:
+    bucket_tokens: int = BUCKET_TOKENS
+    batch_keys: List[int] = field(default_factory=lambda: list(BATCH_KEYS))
+    tables: Dict[str, List[List[int]]] = field(default_factory=dict)
+
+    @classmethod
+    def load(cls, path: str = None) -> "SplitTable":
+        path = path or os.environ.get("DECODE_ATTN_SPLITS_TABLE") or TABLE_PATH
+        if not os.path.exists(path):
+            return default_table()
+        with open(path) as f:
+            d = json.load(f)
+        return cls(bucket_tokens=d["bucket_tokens"], batch_keys=list(d["batch_keys"]),
+                   tables={k: [list(r) for r in v] for k, v in d["tables"].items()})
+
+    def save(self, path: str = None):
+        path = path or TABLE_PATH
+        with open(path, "w") as f:
+            json.dump({"bucket_tokens": self.bucket_tokens, "batch_keys": self.batch_keys,
+                       "tables": self.tables}, f, indent=1, sort_keys=True)
+            f.write("\n")
+
+    def table_for(self, key: str) -> List[List[int]]:
+        if key in self.tables:
+            return self.tables[key]
+        return [[_heuristic(b, k + 1) for k in range(N_BUCKETS)] for b in self.batch_keys]
+
+    def pick(self, key: str, batch: int, kv_len: int = REPRESENTATIVE_KV_LEN) -> int:
+        """num_splits for variant ``key`` at this batch size and (max) KV length."""
+        return decode_attn_pick_splits(self.table_for(key), self.batch_keys, self.bucket_tokens,
+                                       batch, kv_len)
+
+
+def default_table() -> SplitTable:
+    return SplitTable()

@@ -1,0 +1,219 @@
+/*
+ * decode_attn.h -- C ABI of libdecode_attn.so: single-step decode attention
+ * over a paged KV cache on AMD MI355X (gfx950).
+ *
+ * The operation.  The decode kernels tuned in LightLLM PR #1549
+ * "feat(autotune): separate general and decode attention warmup" (section
+ * "Covered decode kernels") are a KV-cache decode attention with a
+ * num_splits tunable, a GQA flash-decode stage 1, INT4 / INT8 KV stage-1
+ * kernels and a two-stage MTP attention.  Here that is:
+ *
+ *   metadata : one launch builds cache_seqlens, cu_seqlens_k/q and page_table
+ *              (SGLang PR #29843 digest, "Implementation breakdown").
+ *   split    : stage 1.  For every (request b, kv-head g, split s) the
+ *              softmax-normalised partial output of the G*q query rows that
+ *              share kv-head g over the split's tokens, and its log-sum-exp.
+ *   merge    : stage 2.  Combines the splits of every query row by their LSE.
+ *
+ * Attention is out = softmax(scale * q K^T) V per query head h, with h reading
+ * kv-head h / G (G = Hq / Hkv).  With q_per_req > 1 (MTP verify) and causal
+ * != 0, query i of the request sees cache tokens t < L - (q_per_req - 1 - i).
+ * The LSE values crossing the ABI are natural logarithms.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers unless stated "host".  All memory is
+ *     owned and allocated by the caller; the library never allocates, frees
+ *     or synchronises, and never reads device data on the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Work is enqueued asynchronously on it; every call can be recorded in
+ *     a HIP graph.
+ *   - Arguments are checked on the host first.  On a non-zero return
+ *     nothing has been enqueued, except DA_ERR_LAUNCH (launch failed).
+ *   - Device data is the caller's contract and is not validated (that would
+ *     need a sync).  Kernels still never read outside the buffers whose
+ *     sizes the arguments give: out-of-range page ids read page 0, lengths
+ *     are clamped to [0, max_pages * page_size], negative ids act as 0.
+ *     Results for such rows are unspecified.
+ *
+ * Layouts (row-major, contiguous):
+ *   q            [B, q_per_req, Hq, D]
+ *   k/v pools    [num_pages, page_size, Hkv, D]          (dense: bf16 / fp32, int8)
+ *                [num_pages, page_size, Hkv, D/2] uint8  (int4: element 2j in the
+ *                                                         low nibble of byte j)
+ *   page_table   [B, page_table_stride], first max_pages entries of a row used
+ *   o_partial    [B, q_per_req, Hq, num_splits, D] fp32
+ *   lse_partial  [B, q_per_req, Hq, num_splits]    fp32
+ *   out          [B, q_per_req, Hq, D]  bf16 (RNE) or fp32
+ *   lse_out      [B, q_per_req, Hq]     fp32
+ *
+ * Split partition: n = ceil(L / page_size) pages, c = ceil(n / num_splits)
+ * pages per split; split s covers pages [s*c, min((s+1)*c, n)), clipped to
+ * L tokens.  Splits with no visible token write (0, -inf); every slot of
+ * o_partial / lse_partial is written, so they need no clearing.
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DA_OK 0
+#define DA_ERR_INVALID_ARG 1  /* null pointer, non-positive size, Hq % Hkv, range */
+#define DA_ERR_UNSUPPORTED 2  /* a shape / dtype no kernel is built for          */
+#define DA_ERR_LAUNCH 3       /* hipGetLastError() after the launch               */
+
+/* element types */
+#define DA_FP32 0
+#define DA_BF16 1
+
+/* cu_seqlens_q modes (SGLang PR #29843 digest, "Implementation breakdown":
+   preset / cumsum / strided) */
+#define DA_Q_STRIDED 0 /* cu_q[b] = b * q_stride, b = 0..B                        */
+#define DA_Q_CUMSUM 1  /* cu_q = exclusive prefix of max(q_in[b], 0), q_in [B]     */
+#define DA_Q_PRESET 2  /* cu_q = copy of q_in [B+1]                                */
+
+/* limits of the built kernels */
+#define DA_MAX_SPLITS 256
+#define DA_MAX_Q_PER_REQ 16
+#define DA_MAX_ROWS 16 /* G * q_per_req query rows per kv-head */
+
+/*
+ * Metadata prelude, one launch (SGLang PR #29843 digest, sections
+ * "Features and motivation" and "Implementation breakdown"; the page-table
+ * tail is zero-padded as its tests describe).
+ *
+ *   seq_lens          [batch] int32      KV length of each request (new tokens included)
+ *   req_pool_indices  [batch] int64      row of req_to_token for each request
+ *   req_to_token      [rows, stride] int32 token slot of every logical token;
+ *                      slot = page * page_size + offset
+ *   outputs: cache_seqlens [batch], cu_seqlens_k [batch+1], cu_seqlens_q [batch+1],
+ *            page_table [batch, max_pages] (row stride max_pages), all int32.
+ *
+ *   cache_seqlens[b]  = max(seq_lens[b], 0)
+ *   cu_seqlens_k      = exclusive prefix sum of cache_seqlens (sum must fit int32)
+ *   page_table[b][j]  = req_to_token[rpi[b]][j * page_size] / page_size for
+ *                       j < ceil(cache_seqlens[b] / page_size), else 0.  A negative
+ *                       or >= req_to_token_rows rpi, a column >= req_to_token_cols,
+ *                       or a negative slot gives 0 (-1 sentinel guard).
+ *   q_in: host-invisible device array, required for CUMSUM ([batch]) and PRESET
+ *   ([batch+1]); ignored (may be NULL) for STRIDED.
+ */
+int32_t decode_attn_metadata(const int32_t* seq_lens, const int64_t* req_pool_indices,
+                             const int32_t* req_to_token, int64_t req_to_token_rows,
+                             int64_t req_to_token_cols, int64_t req_to_token_stride,
+                             int32_t batch, int32_t page_size, int32_t max_pages,
+                             int32_t q_mode, const int32_t* q_in, int32_t q_stride,
+                             int32_t* cache_seqlens, int32_t* cu_seqlens_k,
+                             int32_t* cu_seqlens_q, int32_t* page_table, void* stream);
+
+/*
+ * Stage 1 over a dense bf16 or fp32 cache (GQA flash decode "stage 1" and
+ * the num_splits KV-cache decode of LightLLM PR #1549, "Covered decode
+ * kernels").  q and the pools share `dtype` (DA_BF16 or DA_FP32).
+ *
+ *   head_dim in {64, 128}; page_size in {16, 32, 64, 128, 256};
+ *   num_q_heads % num_kv_heads == 0; G * q_per_req <= DA_MAX_ROWS;
+ *   1 <= num_splits <= DA_MAX_SPLITS; 1 <= q_per_req <= DA_MAX_Q_PER_REQ.
+ *   page_table_stride >= max_pages >= 1.  cache_seqlens is the [batch] int32
+ *   array from decode_attn_metadata (or any caller array of KV lengths).
+ */
+int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool, const void* v_pool,
+                          const int32_t* page_table, int32_t page_table_stride, int32_t max_pages,
+                          const int32_t* cache_seqlens, int32_t batch, int32_t q_per_req,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t page_size, int32_t num_pages, int32_t num_splits,
+                          float softmax_scale, int32_t causal, float* o_partial,
+                          float* lse_partial, void* stream);
+
+/*
+ * Stage 1 over an INT8 cache (LightLLM PR #1549, "Covered decode kernels":
+ * INT8 KV flash decode stage 1).  K = k_pool * k_scale, V = v_pool * v_scale
+ * with one fp16 scale per (page, slot, kv-head):
+ *   k_pool, v_pool    [num_pages, page_size, Hkv, D] int8
+ *   k_scale, v_scale  [num_pages, page_size, Hkv] fp16 (raw bits)
+ * q_dtype is DA_BF16 or DA_FP32.  Other arguments as decode_attn_split.
+ */
+int32_t decode_attn_split_int8(const void* q, int32_t q_dtype, const int8_t* k_pool,
+                               const int8_t* v_pool, const uint16_t* k_scale,
+                               const uint16_t* v_scale, const int32_t* page_table,
+                               int32_t page_table_stride, int32_t max_pages,
+                               const int32_t* cache_seqlens, int32_t batch, int32_t q_per_req,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t page_size, int32_t num_pages, int32_t num_splits,
+                               float softmax_scale, int32_t causal, float* o_partial,
+                               float* lse_partial, void* stream);
+
+/*
+ * Stage 1 over an INT4 cache (LightLLM PR #1549, "Covered decode kernels":
+ * INT4 KV flash decode stage 1; with q_per_req > 1 and causal it is the MTP
+ * verify decode of the same page).  Per group of 32 elements along D:
+ * x = (nibble - zero) * scale.
+ *   k_pool, v_pool            [num_pages, page_size, Hkv, D/2] uint8
+ *   k_scale_zero, v_scale_zero [num_pages, page_size, Hkv, D/32, 2] fp16 bits,
+ *                              (scale, zero) pairs
+ * Other arguments as decode_attn_split_int8.
+ */
+int32_t decode_attn_split_int4(const void* q, int32_t q_dtype, const uint8_t* k_pool,
+                               const uint8_t* v_pool, const uint16_t* k_scale_zero,
+                               const uint16_t* v_scale_zero, const int32_t* page_table,
+                               int32_t page_table_stride, int32_t max_pages,
+                               const int32_t* cache_seqlens, int32_t batch, int32_t q_per_req,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t page_size, int32_t num_pages, int32_t num_splits,
+                               float softmax_scale, int32_t causal, float* o_partial,
+                               float* lse_partial, void* stream);
+
+/*
+ * Stage 2: LSE merge (LightLLM PR #1549, "Covered decode kernels": the
+ * stage 2 of the two-stage attention; "Validation": stage-2 inputs are
+ * reused).  For every query row: m = max_s lse_s, w_s = exp(lse_s - m),
+ * out = sum_s w_s O_s / sum_s w_s, lse = m + ln(sum_s w_s); a row whose
+ * splits are all empty gives out 0, lse -inf.
+ *   out_dtype DA_BF16 (round to nearest even) or DA_FP32; lse_out may be NULL.
+ */
+int32_t decode_attn_merge(const float* o_partial, const float* lse_partial, int32_t batch,
+                          int32_t q_per_req, int32_t num_q_heads, int32_t head_dim,
+                          int32_t num_splits, void* out, int32_t out_dtype, float* lse_out,
+                          void* stream);
+
+/*
+ * Host-only: split count for a launch (LightLLM PR #1549: num_splits is the
+ * tuned config of the KV-cache decode kernel; run keys are KV-length
+ * buckets while the real length selects the config at run time).
+ *   table      host [n_batch_keys, n_buckets] int32 split counts
+ *   batch_keys host [n_batch_keys] int32, ascending
+ *   bucket = clamp(ceil(kv_len / bucket_tokens), 1, n_buckets); the batch key
+ *   is the nearest one to `batch` (ties -> the smaller key).
+ * Returns the split count (>= 1), or -DA_ERR_INVALID_ARG.
+ */
+int32_t decode_attn_pick_splits(const int32_t* table, const int32_t* batch_keys,
+                                int32_t n_batch_keys, int32_t n_buckets, int32_t bucket_tokens,
+                                int32_t batch, int32_t kv_len);
+
+/*
+ * Test hook: dense copy of every request's tokens from a paged pool.
+ * out row cu_seqlens_k[b] + t = pool token (page_table[b][t / page_size],
+ * t % page_size) for t < cache_seqlens[b]; each token is `token_bytes`
+ * bytes (a multiple of 4), e.g. Hkv*D*2 for bf16 K, Hkv*2 for int8 scales.
+ */
+int32_t decode_attn_gather_kv(const void* pool, int64_t token_bytes, int32_t page_size,
+                              int32_t num_pages, const int32_t* page_table,
+                              int32_t page_table_stride, int32_t max_pages,
+                              const int32_t* cache_seqlens, const int32_t* cu_seqlens_k,
+                              int32_t batch, void* out, void* stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* decode_attn_strerror(int32_t status);
+
+/* ABI version (major * 100 + minor). */
+int32_t decode_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

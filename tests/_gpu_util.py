@@ -1,0 +1,189 @@
+"""Comparison helpers for the GPU parity tests (test infrastructure).
+
+Gates for floating point, by output type:
+* bf16 outputs: max-abs <= 1e-2 against the fp64 oracle, and rel-L2 <= 1e-3
+  against the fp64 oracle rounded to bf16 (round to nearest even, directly
+  from fp64).  A correctly rounded bf16 result sits ~1.5e-3 rel-L2 from the
+  unrounded fp64 values, so the rel-L2 gate is applied after rounding the
+  oracle the way the output is rounded; the raw figure is still reported.
+* fp32 outputs of fp32 inputs: rel-L2 <= 1e-5 and max-abs <= 1e-5.
+* quantised caches (oracle run on the identically decoded K/V): max-abs <= 1e-2.
+* stage-1 partials (fp32): |dO| <= 2e-5 * (1 + |O|), |d lse| <= 1e-4, and the
+  empty splits (lse = -inf) must coincide exactly.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from decode_attention_paged_gqa_amd import workloads as W
+from oracle import attention as OA
+from oracle import quant as OQ
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def bf16_rne_from_f64(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even); returns float64."""
+    x = np.asarray(x, dtype=np.float64)
+    bits = x.view(np.uint64).copy()
+    finite = np.isfinite(x)
+    lsb = (bits >> np.uint64(45)) & np.uint64(1)
+    rounded = (bits + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)
+    out = np.where(finite, rounded.view(np.float64), x)
+    return out
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a - b))
+
+
+def check_bf16(out: np.ndarray, ref: np.ndarray, label: str):
+    assert np.all(np.isfinite(out)), f"{label}: non-finite output"
+    max_abs = float(np.max(np.abs(out - ref))) if out.size else 0.0
+    r_round = rel_l2(out, bf16_rne_from_f64(ref))
+    r_raw = rel_l2(out, ref)
+    log(f"  {label}: max_abs={max_abs:.3e} relL2(vs bf16(oracle))={r_round:.3e} relL2(raw)={r_raw:.3e}")
+    assert max_abs <= 1e-2, f"{label}: max_abs {max_abs}"
+    assert r_round <= 1e-3, f"{label}: rel-L2 {r_round}"
+    return max_abs, r_round, r_raw
+
+
+def check_fp32(out: np.ndarray, ref: np.ndarray, label: str, tol=1e-5):
+    assert np.all(np.isfinite(out)), f"{label}: non-finite output"
+    max_abs = float(np.max(np.abs(out - ref))) if out.size else 0.0
+    r = rel_l2(out, ref)
+    log(f"  {label}: max_abs={max_abs:.3e} relL2={r:.3e}")
+    assert max_abs <= tol and r <= tol, label
+
+
+def check_quant(out: np.ndarray, ref: np.ndarray, label: str):
+    assert np.all(np.isfinite(out)), f"{label}: non-finite output"
+    max_abs = float(np.max(np.abs(out - ref))) if out.size else 0.0
+    r = rel_l2(out, bf16_rne_from_f64(ref))
+    log(f"  {label}: max_abs={max_abs:.3e} relL2(vs bf16(oracle), reported)={r:.3e}")
+    assert max_abs <= 1e-2, f"{label}: max_abs {max_abs}"
+
+
+def check_lse(lse: np.ndarray, ref: np.ndarray, label: str, tol=1e-4):
+    inf_k = np.isneginf(lse)
+    inf_r = np.isneginf(ref)
+    assert np.array_equal(inf_k, inf_r), f"{label}: -inf pattern differs"
+    fin = ~inf_r
+    d = float(np.max(np.abs(lse[fin] - ref[fin]))) if fin.any() else 0.0
+    log(f"  {label}: max |d lse| = {d:.3e}")
+    assert d <= tol, label
+
+
+def check_partials(o, l, o_ref, l_ref, label):
+    check_lse(l, l_ref, label + " lse_partial")
+    d = np.abs(o - o_ref)
+    bound = 2e-5 * (1.0 + np.abs(o_ref))
+    worst = float(np.max(d - bound)) if d.size else -1
+    log(f"  {label} o_partial: max|d|={float(np.max(d)) if d.size else 0:.3e}")
+    assert worst <= 0, f"{label}: o_partial off by {worst}"
+    assert np.all(o[np.isneginf(l_ref)] == 0.0), f"{label}: empty split not zero"
+
+
+# ---------------------------------------------------------------- oracle inputs
+def host_inputs(batch: W.PagedBatch):
+    """Full host copies (fp64 / raw) of a small batch for the oracle."""
+    w = batch.w
+    d = dict(q=W.host_f64(batch.q), page_table=W.host_int(batch.page_table),
+             seq_lens=W.host_int(batch.seq_lens))
+    if w.kv == W.KV_DENSE:
+        d["k"] = W.host_f64(batch.k_pool)
+        d["v"] = W.host_f64(batch.v_pool)
+    elif w.kv == W.KV_INT8:
+        d["k"] = OQ.dequant_int8(W.host_int(batch.k_pool), W.host_u16(batch.k_scale))
+        d["v"] = OQ.dequant_int8(W.host_int(batch.v_pool), W.host_u16(batch.v_scale))
+    else:
+        d["k"] = OQ.dequant_int4(W.host_int(batch.k_pool), W.host_u16(batch.k_scale))
+        d["v"] = OQ.dequant_int4(W.host_int(batch.v_pool), W.host_u16(batch.v_scale))
+    return d
+
+
+def oracle_full(batch: W.PagedBatch):
+    h = host_inputs(batch)
+    w = batch.w
+    return OA.decode_attention(h["q"], h["k"], h["v"], h["page_table"], h["seq_lens"],
+                               w.page_size, w.softmax_scale, causal=w.causal)
+
+
+def oracle_partials(batch: W.PagedBatch, S: int):
+    h = host_inputs(batch)
+    w = batch.w
+    return OA.split_partials(h["q"], h["k"], h["v"], h["page_table"], h["seq_lens"],
+                             w.page_size, w.softmax_scale, S, causal=w.causal)
+
+
+def oracle_sampled(batch: W.PagedBatch, pairs):
+    """Oracle output for sampled (b, kv-head) pairs of a large batch.
+
+    For each pair, only that request's pages and that kv-head are copied to
+    the host (compact pool, remapped page table); the query heads of the
+    group are evaluated by the oracle.  Returns {(b, g): (out [q, G, D], lse [q, G])}.
+    """
+    w = batch.w
+    G = w.group
+    res = {}
+    pt_all = W.host_int(batch.page_table)
+    L_all = W.host_int(batch.seq_lens)
+    for b, g in pairs:
+        L = int(L_all[b])
+        n = -(-L // w.page_size)
+        pages = torch.from_numpy(pt_all[b, :n].astype(np.int64)).to(batch.k_pool.device)
+        q = W.host_f64(batch.q[b:b + 1, :, g * G:(g + 1) * G])
+        pt = np.arange(n, dtype=np.int64)[None, :] if n else np.zeros((1, 1), dtype=np.int64)
+
+        def take(pool):
+            return pool.index_select(0, pages)[:, :, g:g + 1].contiguous()
+
+        if w.kv == W.KV_DENSE:
+            k = W.host_f64(take(batch.k_pool))
+            v = W.host_f64(take(batch.v_pool))
+        elif w.kv == W.KV_INT8:
+            k = OQ.dequant_int8(W.host_int(take(batch.k_pool)), W.host_u16(take(batch.k_scale)))
+            v = OQ.dequant_int8(W.host_int(take(batch.v_pool)), W.host_u16(take(batch.v_scale)))
+        else:
+            k = OQ.dequant_int4(W.host_int(take(batch.k_pool)), W.host_u16(take(batch.k_scale)))
+            v = OQ.dequant_int4(W.host_int(take(batch.v_pool)), W.host_u16(take(batch.v_scale)))
+        if n == 0:
+            k = np.zeros((1, w.page_size, 1, w.head_dim))
+            v = np.zeros((1, w.page_size, 1, w.head_dim))
+        out, lse = OA.decode_attention(q, k, v, pt, np.array([L]), w.page_size, w.softmax_scale,
+                                       causal=w.causal)
+        res[(b, g)] = (out[0], lse[0])
+    return res
+
+
+# ---------------------------------------------------------------- GPU path
+def run_split(da, batch: W.PagedBatch, S: int):
+    w = batch.w
+    if w.kv == W.KV_DENSE:
+        return da.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, batch.page_table,
+                                    batch.seq_lens, S, w.softmax_scale, w.causal)
+    if w.kv == W.KV_INT8:
+        return da.decode_attn_split_int8(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
+                                         batch.v_scale, batch.page_table, batch.seq_lens, S,
+                                         w.softmax_scale, w.causal)
+    return da.decode_attn_split_int4(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
+                                     batch.v_scale, batch.page_table, batch.seq_lens, S,
+                                     w.softmax_scale, w.causal)
+
+
+def run_decode(da, batch: W.PagedBatch, S: int, out_dtype=torch.bfloat16):
+    o, l = run_split(da, batch, S)
+    out, lse = da.decode_attn_merge(o, l, out_dtype=out_dtype, want_lse=True)
+    return out, lse, o, l
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)

@@ -1,0 +1,149 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and its host-side argument validation and split-count
+lookup behave as documented (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import decode_attention_paged_gqa_amd as da
+from decode_attention_paged_gqa_amd import _binding as B
+from decode_attention_paged_gqa_amd.splits import SplitTable, kernel_key
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decode_attn.h")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails before any launch
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(decode_attn_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libdecode_attn.so not built (run __graft_entry__.build())")
+    return da.load()
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(decode_attn_\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_strerror_and_version(lib):
+    assert lib.decode_attn_strerror(0) == b"ok"
+    assert lib.decode_attn_strerror(1) == b"invalid argument"
+    assert lib.decode_attn_strerror(2) == b"unsupported shape or dtype"
+    assert lib.decode_attn_strerror(3) == b"kernel launch failed"
+    assert lib.decode_attn_strerror(99) == b"unknown status"
+    assert lib.decode_attn_version() == 100
+
+
+def _split_args(**kw):
+    a = dict(q=FAKE, dtype=B.DA_BF16, k=FAKE, v=FAKE, pt=FAKE, pt_stride=8, max_pages=8,
+             seqlens=FAKE, batch=4, qn=1, Hq=32, Hkv=8, D=128, ps=64, num_pages=100, S=4,
+             scale=0.1, causal=0, o=FAKE, lse=FAKE, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("q", "dtype", "k", "v", "pt", "pt_stride", "max_pages", "seqlens",
+                           "batch", "qn", "Hq", "Hkv", "D", "ps", "num_pages", "S", "scale",
+                           "causal", "o", "lse", "stream")]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(batch=0), 1), (dict(Hq=30), 1),
+    (dict(S=0), 1), (dict(S=257), 1), (dict(qn=17), 1), (dict(pt_stride=4), 1),
+    (dict(num_pages=0), 1), (dict(D=96), 2), (dict(ps=48), 2), (dict(ps=8), 2),
+    (dict(dtype=7), 2), (dict(Hq=64, Hkv=2, qn=2), 2),
+])
+def test_split_validation(lib, kw, status):
+    assert lib.decode_attn_split(*_split_args(**kw)) == status
+
+
+def test_int8_int4_validation(lib):
+    base = _split_args()
+    # (q, q_dtype, k, v, k_scale, v_scale, ...) -- null scales are invalid
+    args8 = base[:2] + [FAKE, FAKE, None, FAKE] + base[4:]
+    assert lib.decode_attn_split_int8(*args8) == 1
+    args4 = base[:2] + [FAKE, FAKE, FAKE, None] + base[4:]
+    assert lib.decode_attn_split_int4(*args4) == 1
+    args4 = base[:2] + [FAKE, FAKE, FAKE, FAKE] + base[4:12] + [80] + base[13:]
+    assert lib.decode_attn_split_int4(*args4) == 2
+
+
+def test_merge_and_metadata_and_gather_validation(lib):
+    assert lib.decode_attn_merge(None, FAKE, 1, 1, 8, 128, 4, FAKE, B.DA_BF16, None, None) == 1
+    assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 96, 4, FAKE, B.DA_BF16, None, None) == 2
+    assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 128, 4, FAKE, 5, None, None) == 2
+    assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 128, 0, FAKE, B.DA_BF16, None, None) == 1
+    md = [FAKE, FAKE, FAKE, 4, 64, 64, 2, 16, 4, B.DA_Q_STRIDED, None, 1, FAKE, FAKE, FAKE, FAKE, None]
+    bad = list(md); bad[0] = None
+    assert lib.decode_attn_metadata(*bad) == 1
+    bad = list(md); bad[9] = 7
+    assert lib.decode_attn_metadata(*bad) == 1
+    bad = list(md); bad[9] = B.DA_Q_CUMSUM  # cumsum needs q_in
+    assert lib.decode_attn_metadata(*bad) == 1
+    bad = list(md); bad[5] = 32  # stride < cols
+    assert lib.decode_attn_metadata(*bad) == 1
+    g = [FAKE, 6, 16, 10, FAKE, 4, 4, FAKE, FAKE, 2, FAKE, None]
+    assert lib.decode_attn_gather_kv(*g) == 1  # token_bytes not a multiple of 4
+
+
+def test_pick_splits_buckets_and_nearest_key(lib):
+    table = [[1, 2, 3, 4, 5, 6, 7, 8], [11, 12, 13, 14, 15, 16, 17, 18], [21, 22, 23, 24, 25, 26, 27, 28]]
+    keys = [16, 32, 64]
+    pick = lambda b, L: da.decode_attn_pick_splits(table, keys, 4096, b, L)
+    assert pick(16, 1) == 1
+    assert pick(16, 4096) == 1
+    assert pick(16, 4097) == 2
+    assert pick(16, 32768) == 8
+    assert pick(16, 10 ** 6) == 8        # clamped to the last bucket
+    assert pick(16, 0) == 1 and pick(16, -5) == 1
+    assert pick(64, 8192) == 22
+    assert pick(1, 8192) == 2            # nearest key 16
+    assert pick(24, 8192) == 2           # tie 16 / 32 -> smaller
+    assert pick(25, 8192) == 12
+    assert pick(48, 8192) == 12          # tie 32 / 64 -> smaller
+    assert pick(1000, 8192) == 22
+    with pytest.raises(da.DecodeAttnError):
+        da.decode_attn_pick_splits(table, [32, 16, 64], 4096, 16, 100)   # keys not ascending
+    with pytest.raises(da.DecodeAttnError):
+        da.decode_attn_pick_splits([[0] * 8] * 3, keys, 4096, 16, 100)   # split count 0
+
+
+def test_split_table_roundtrip(tmp_path, lib):
+    t = SplitTable()
+    key = kernel_key("bf16", 5, 128, 64)
+    t.tables[key] = [[1, 2, 4, 4, 8, 8, 16, 16]] * 3
+    p = tmp_path / "t.json"
+    t.save(str(p))
+    t2 = SplitTable.load(str(p))
+    assert t2.tables == t.tables
+    assert t2.pick(key, 64, 32768) == 16
+    assert t2.pick(key, 64, 5000) == 2
+    # untuned variants fall back to a heuristic in range
+    s = t2.pick(kernel_key("int8", 4, 128, 64), 32, 32768)
+    assert 1 <= s <= 32
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    q = torch.zeros(2, 1, 4, 64)
+    kp = torch.zeros(4, 16, 1, 64)
+    pt = torch.zeros(2, 4, dtype=torch.int32)
+    sl = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        da.decode_attn_split(q, kp, kp, pt, sl, 2)

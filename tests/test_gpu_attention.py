@@ -1,0 +1,170 @@
+"""GPU parity of stage 1 (split), stage 2 (merge) and the whole decode
+against the fp64 oracle, on seeded inputs shaped like the pages' workloads.
+
+Small cases are compared element by element (every output, every split
+partial); full-size workloads in the launch configuration the benchmark uses
+are compared on sampled (request, kv-head) pairs the oracle evaluates one by
+one.  Gates are documented in tests/_gpu_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_paged_gqa_amd import workloads as W
+from tests import _gpu_util as U
+
+pytestmark = pytest.mark.gpu
+log = U.log
+
+# ---------------------------------------------------------------- small cases
+TINY = W.TINY_FP32
+TINY_BF16 = W.TINY_FP32.scaled(name="tiny_bf16", dtype="bf16")
+EDGE_LENGTHS = (0, 1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 1000, 2047, 3001, 5)
+RAGGED_SMALL = W.RAGGED_B64.scaled(name="ragged_small_g5", batch=len(EDGE_LENGTHS),
+                                   lengths="list", length_list=EDGE_LENGTHS, pin_max=False)
+BF16_SMALL = W.BF16_B16.scaled(name="bf16_small_g4", batch=4, length=1500)
+D64_P16 = W.RAGGED_B64.scaled(name="d64_p16_g2", batch=5, num_q_heads=8, num_kv_heads=4,
+                              head_dim=64, page_size=16, lengths="list",
+                              length_list=(3, 16, 40, 333, 17), pin_max=False)
+MHA_P32 = W.RAGGED_B64.scaled(name="mha_p32_g1", batch=3, num_q_heads=4, num_kv_heads=4,
+                              page_size=32, lengths="list", length_list=(33, 100, 1), pin_max=False)
+MTP_BF16 = W.BF16_B16.scaled(name="mtp4_bf16_g4", batch=5, q_per_req=4, causal=True,
+                             lengths="list", length_list=(1, 3, 4, 70, 900))
+MTP_BF16_G2Q3 = W.BF16_B16.scaled(name="mtp3_bf16_g2", batch=3, num_q_heads=16, q_per_req=3,
+                                  causal=True, lengths="list", length_list=(2, 66, 500))
+INT8_SMALL = W.INT8_B32.scaled(name="int8_small", batch=5, lengths="list",
+                               length_list=(1, 64, 65, 777, 2000))
+INT4_SMALL = W.INT4_MTP_B64.scaled(name="int4_mtp_small", batch=5, lengths="list",
+                                   length_list=(1, 4, 65, 777, 2000))
+INT4_Q1 = W.INT4_MTP_B64.scaled(name="int4_q1_small", batch=4, q_per_req=1, causal=False,
+                                lengths="list", length_list=(1, 64, 300, 1500))
+
+
+def _check_out(w, out, ref, label):
+    if w.kv != W.KV_DENSE:
+        U.check_quant(out, ref, label)
+    elif w.dtype == "fp32" and out.dtype == np.float64 and label.endswith("fp32"):
+        U.check_fp32(out, ref, label)
+    else:
+        U.check_bf16(out, ref, label)
+
+
+@pytest.mark.parametrize("S", [1, 2, 4])
+def test_tiny_fp32_every_split(gpu, S):
+    log(f"tiny fp32 S={S}")
+    batch = W.make_batch(TINY, device="cuda")
+    o_ref, l_ref = U.oracle_partials(batch, S)
+    out_ref, lse_ref = U.oracle_full(batch)
+    out, lse, o, l = U.run_decode(gpu, batch, S, out_dtype=torch.float32)
+    U.check_partials(U.to_np(o), U.to_np(l), o_ref, l_ref, f"tiny S={S}")
+    U.check_fp32(U.to_np(out), out_ref, f"tiny S={S} out fp32")
+    U.check_lse(U.to_np(lse), lse_ref, f"tiny S={S} lse")
+    out16, _, _, _ = U.run_decode(gpu, batch, S, out_dtype=torch.bfloat16)
+    U.check_bf16(U.to_np(out16), out_ref, f"tiny S={S} out bf16")
+
+
+@pytest.mark.parametrize("w", [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, MHA_P32, MTP_BF16,
+                               MTP_BF16_G2Q3, INT8_SMALL, INT4_SMALL, INT4_Q1],
+                         ids=lambda w: w.name)
+@pytest.mark.parametrize("S", [1, 3, 8, 32])
+def test_small_elementwise(gpu, w, S):
+    log(f"small {w.name} S={S}")
+    batch = W.make_batch(w, device="cuda")
+    o_ref, l_ref = U.oracle_partials(batch, S)
+    out_ref, lse_ref = U.oracle_full(batch)
+    out, lse, o, l = U.run_decode(gpu, batch, S)
+    U.check_partials(U.to_np(o), U.to_np(l), o_ref, l_ref, f"{w.name} S={S}")
+    _check_out(w, U.to_np(out), out_ref, f"{w.name} S={S} out")
+    U.check_lse(U.to_np(lse), lse_ref, f"{w.name} S={S} lse")
+
+
+def test_page_permutation_is_bit_identical(gpu):
+    w = RAGGED_SMALL
+    log("page permutation invariance")
+    batch = W.make_batch(w, device="cuda")
+    out1, lse1, _, _ = U.run_decode(gpu, batch, 4)
+    P = batch.num_pages
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(5)).cuda()
+    k2 = torch.empty_like(batch.k_pool)
+    v2 = torch.empty_like(batch.v_pool)
+    k2[perm] = batch.k_pool
+    v2[perm] = batch.v_pool
+    pt2 = perm[batch.page_table.long()].to(torch.int32)
+    batch.k_pool, batch.v_pool, batch.page_table = k2, v2, pt2
+    out2, lse2, _, _ = U.run_decode(gpu, batch, 4)
+    assert torch.equal(out1, out2)
+    assert torch.equal(lse1, lse2)
+
+
+def test_num_splits_invariance(gpu):
+    w = RAGGED_SMALL
+    log("num_splits invariance")
+    batch = W.make_batch(w, device="cuda")
+    base, _, _, _ = U.run_decode(gpu, batch, 1, out_dtype=torch.float32)
+    for S in (2, 5, 16, 64, 256):
+        out, _, _, _ = U.run_decode(gpu, batch, S, out_dtype=torch.float32)
+        d = (out - base).abs().max().item()
+        log(f"  S={S}: max |out - out(S=1)| = {d:.3e}")
+        assert d <= 1e-5
+
+
+def test_outputs_fully_overwritten(gpu):
+    """Stage 1 writes every partial slot (no clearing needed): poison first."""
+    w = RAGGED_SMALL
+    batch = W.make_batch(w, device="cuda")
+    B, qn, Hq, D = batch.q.shape
+    S = 16
+    o = torch.full((B, qn, Hq, S, D), float("nan"), device="cuda")
+    l = torch.full((B, qn, Hq, S), float("nan"), device="cuda")
+    gpu.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, batch.page_table, batch.seq_lens,
+                          S, w.softmax_scale, False, o_partial=o, lse_partial=l)
+    assert not torch.isnan(o).any() and not torch.isnan(l).any()
+
+
+def test_nan_in_unused_slots_does_not_leak(gpu):
+    """Slots past a request's length (tail of its last page, unused pages) may hold
+    anything; fill them with NaN and check the output is unchanged."""
+    w = RAGGED_SMALL.scaled(pool_pages=200)
+    batch = W.make_batch(w, device="cuda")
+    ref, _, _, _ = U.run_decode(gpu, batch, 4)
+    L = batch.lengths
+    pt = batch.page_table.cpu().numpy()
+    used = torch.zeros(batch.num_pages, w.page_size, dtype=torch.bool)
+    for b in range(len(L)):
+        for t in range(int(L[b])):
+            used[pt[b, t // w.page_size], t % w.page_size] = True
+    mask = (~used).cuda()
+    batch.k_pool[mask] = float("nan")
+    batch.v_pool[mask] = float("nan")
+    out, _, _, _ = U.run_decode(gpu, batch, 4)
+    assert torch.equal(out, ref)
+
+
+# ---------------------------------------------------------------- full sizes
+FULL = [
+    (W.BF16_B16, 8, [(0, 0), (7, 3), (15, 7)]),
+    (W.RAGGED_B64, 16, None),
+    (W.INT8_B32, 8, [(0, 0), (31, 7), (13, 2)]),
+    (W.INT4_MTP_B64, 8, None),
+]
+
+
+@pytest.mark.parametrize("w,S,pairs", FULL, ids=[f[0].name for f in FULL])
+def test_full_size_sampled(gpu, w, S, pairs):
+    log(f"full {w.name} S={S}")
+    batch = W.make_batch(w, device="cuda")
+    out, lse, _, _ = U.run_decode(gpu, batch, S)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    L = batch.lengths
+    if pairs is None:  # the longest and the shortest request, and one in between
+        order = np.argsort(L)
+        pairs = [(int(order[-1]), 0), (int(order[0]), w.num_kv_heads - 1),
+                 (int(order[len(L) // 2]), 3)]
+    res = U.oracle_sampled(batch, pairs)
+    G = w.group
+    for (b, g), (o_ref, l_ref) in res.items():
+        got = U.to_np(out[b, :, g * G:(g + 1) * G])
+        got_l = U.to_np(lse[b, :, g * G:(g + 1) * G])
+        _check_out(w, got, o_ref, f"{w.name} b={b} (L={L[b]}) g={g}")
+        U.check_lse(got_l, l_ref, f"{w.name} b={b} g={g} lse")

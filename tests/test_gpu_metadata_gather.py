@@ -1,0 +1,112 @@
+"""GPU: the metadata prelude and the page gather are bit-exact against the oracle."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_paged_gqa_amd import workloads as W
+from oracle import attention as OA
+from oracle import metadata as OM
+from tests._gpu_util import log
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _i32(x, dev="cuda"):
+    return torch.as_tensor(np.asarray(x), dtype=torch.int32, device=dev)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_metadata_hand_built_batch(gpu, mode):
+    g = json.load(open(os.path.join(GOLDEN, "metadata_hand.json")))
+    log(f"metadata hand batch mode={mode}")
+    q_in = None
+    if mode == 1:
+        q_in = _i32(g["q_lens"])
+    elif mode == 2:
+        q_in = _i32(g["cu_q_preset"])
+    md = gpu.decode_attn_metadata(_i32(g["seq_lens"]),
+                                  torch.tensor(g["req_pool_indices"], dtype=torch.int64, device="cuda"),
+                                  _i32(g["req_to_token"]), g["page_size"], g["max_pages"],
+                                  q_mode=mode, q_in=q_in, q_stride=g["q_stride"])
+    e = g["expect"]
+    key = ["cu_seqlens_q_strided", "cu_seqlens_q_cumsum", "cu_seqlens_q_preset"][mode]
+    assert md["cache_seqlens"].tolist() == e["cache_seqlens"]
+    assert md["cu_seqlens_k"].tolist() == e["cu_seqlens_k"]
+    assert md["page_table"].tolist() == e["page_table"]
+    assert md["cu_seqlens_q"].tolist() == e[key]
+
+
+def _check_md_against_oracle(seq, rpi, r2t, ps, max_pages, mode=0, q_in=None, q_stride=1):
+    ref = OM.metadata(seq, rpi, r2t, ps, max_pages, q_mode=mode, q_in=q_in, q_stride=q_stride)
+    md = gpu_mod.decode_attn_metadata(
+        _i32(seq), torch.as_tensor(np.asarray(rpi), dtype=torch.int64, device="cuda"), _i32(r2t),
+        ps, max_pages, q_mode=mode, q_in=None if q_in is None else _i32(q_in), q_stride=q_stride)
+    for k in ("cache_seqlens", "cu_seqlens_k", "cu_seqlens_q", "page_table"):
+        assert np.array_equal(md[k].cpu().numpy().astype(np.int64), ref[k]), k
+    return md
+
+
+gpu_mod = None
+
+
+@pytest.fixture(autouse=True)
+def _bind(gpu):
+    global gpu_mod
+    gpu_mod = gpu
+
+
+@pytest.mark.parametrize("w", [W.TINY_FP32, W.RAGGED_B64, W.INT4_MTP_B64, W.BF16_B16],
+                         ids=lambda w: w.name)
+def test_metadata_generated_batches(w):
+    rng = np.random.Generator(np.random.PCG64(1000 + w.seed))
+    L = W.draw_lengths(w, rng)
+    pt, r2t, rpi, P = W.build_layout(w, L, rng)
+    log(f"metadata {w.name}: B={len(L)} max_pages={pt.shape[1]}")
+    for mode, q_in in ((0, None), (1, rng.integers(-2, 9, size=len(L))),
+                       (2, np.cumsum(np.r_[0, rng.integers(0, 5, size=len(L))]))):
+        md = _check_md_against_oracle(L, rpi, r2t, w.page_size, pt.shape[1], mode, q_in,
+                                      q_stride=w.q_per_req)
+    assert np.array_equal(md["page_table"].cpu().numpy(), pt)
+
+
+def test_metadata_sentinels_and_wide_rows():
+    rng = np.random.default_rng(11)
+    for B, R, Wd, ps, mp in ((7, 6, 40, 8, 6), (300, 310, 4096, 16, 300), (1, 1, 64, 64, 1)):
+        log(f"metadata sentinels B={B} R={R} W={Wd} ps={ps} max_pages={mp}")
+        r2t = rng.integers(-3, 10 ** 6, size=(R, Wd)).astype(np.int32)
+        seq = rng.integers(-5, mp * ps + 10, size=B)
+        rpi = rng.integers(-2, R + 2, size=B)
+        _check_md_against_oracle(seq, rpi, r2t, ps, mp, 0, None, 2)
+
+
+@pytest.mark.parametrize("w", [W.TINY_FP32, W.BF16_B16.scaled(batch=6, lengths="list",
+                                                              length_list=(1, 63, 64, 65, 700, 0)),
+                               W.INT8_B32.scaled(batch=3, length=333),
+                               W.INT4_MTP_B64.scaled(batch=3, length_lo=100, length_hi=900)],
+                         ids=lambda w: w.name)
+def test_gather_is_bit_exact(w):
+    log(f"gather {w.name}")
+    batch = W.make_batch(w, device="cuda")
+    L = batch.lengths
+    md = gpu_mod.decode_attn_metadata(batch.seq_lens, batch.req_pool_indices, batch.req_to_token,
+                                      w.page_size, batch.max_pages)
+    assert torch.equal(md["page_table"], batch.page_table)
+    total = int(L.sum())
+    pt = batch.page_table.cpu().numpy()
+    pools = [batch.k_pool, batch.v_pool] + [t for t in (batch.k_scale, batch.v_scale) if t is not None]
+    for pool in pools:
+        got = gpu_mod.decode_attn_gather_kv(pool, md["page_table"], md["cache_seqlens"],
+                                            md["cu_seqlens_k"], total).cpu()
+        host = pool.cpu()
+        # compare raw bytes: oracle gather applied to the host copy, request by request
+        raw = host.view(torch.uint8).numpy().reshape(host.shape[0], host.shape[1], -1)
+        off = 0
+        got_raw = got.contiguous().view(torch.uint8).numpy().reshape(total, -1)
+        for b in range(len(L)):
+            want = OA.gather_tokens(raw, pt[b], int(L[b]), w.page_size)
+            assert np.array_equal(got_raw[off:off + L[b]], want), (b, pool.dtype)
+            off += int(L[b])
