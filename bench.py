@@ -85,17 +85,20 @@ def stage1(da, batch, S, o, l):
     from decode_attention_paged_gqa_amd import workloads as W
 
     w = batch.w
+    md = batch.md
     if w.kv == W.KV_DENSE:
-        return da.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, batch.md["page_table"],
-                                    batch.md["cache_seqlens"], S, w.softmax_scale, w.causal, o, l)
+        return da.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, md["page_table"],
+                                    md["cache_seqlens"], S, w.softmax_scale, w.causal, o, l,
+                                    batch_order=md["batch_order"])
     if w.kv == W.KV_INT8:
         return da.decode_attn_split_int8(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
-                                         batch.v_scale, batch.md["page_table"],
-                                         batch.md["cache_seqlens"], S, w.softmax_scale, w.causal,
-                                         o, l)
+                                         batch.v_scale, md["page_table"], md["cache_seqlens"], S,
+                                         w.softmax_scale, w.causal, o, l,
+                                         batch_order=md["batch_order"])
     return da.decode_attn_split_int4(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
-                                     batch.v_scale, batch.md["page_table"],
-                                     batch.md["cache_seqlens"], S, w.softmax_scale, w.causal, o, l)
+                                     batch.v_scale, md["page_table"], md["cache_seqlens"], S,
+                                     w.softmax_scale, w.causal, o, l,
+                                     batch_order=md["batch_order"])
 
 
 def rows_per_kv_head(w):

@@ -32,13 +32,13 @@ _F32 = ctypes.c_float
 
 _SIGS = {
     "decode_attn_metadata": [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _I32,
-                             _P, _P, _P, _P, _P],
-    "decode_attn_split": [_P, _I32, _P, _P, _P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I32,
-                          _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
-    "decode_attn_split_int8": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _I32, _I32, _I32,
-                               _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
-    "decode_attn_split_int4": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _I32, _I32, _I32,
-                               _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
+                             _P, _P, _P, _P, _P, _P],
+    "decode_attn_split": [_P, _I32, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32,
+                          _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
+    "decode_attn_split_int8": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I32,
+                               _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
+    "decode_attn_split_int4": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I32,
+                               _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
     "decode_attn_merge": [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P],
     "decode_attn_pick_splits": [_P, _P, _I32, _I32, _I32, _I32, _I32],
     "decode_attn_gather_kv": [_P, _I64, _I32, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P],
@@ -103,7 +103,7 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None, ndim=None):
 # ------------------------------------------------------------------ metadata
 def decode_attn_metadata(seq_lens, req_pool_indices, req_to_token, page_size, max_pages,
                          q_mode=DA_Q_STRIDED, q_in=None, q_stride=1, out=None):
-    """cache_seqlens, cu_seqlens_k, cu_seqlens_q, page_table in one launch.
+    """cache_seqlens, cu_seqlens_k, cu_seqlens_q, page_table, batch_order in one launch.
 
     Returns a dict of int32 tensors (those in ``out`` are reused)."""
     lib = load()
@@ -122,7 +122,8 @@ def decode_attn_metadata(seq_lens, req_pool_indices, req_to_token, page_size, ma
     out["cu_seqlens_k"] = mk("cu_seqlens_k", (B + 1,))
     out["cu_seqlens_q"] = mk("cu_seqlens_q", (B + 1,))
     out["page_table"] = mk("page_table", (B, max_pages))
-    for k in ("cache_seqlens", "cu_seqlens_k", "cu_seqlens_q", "page_table"):
+    out["batch_order"] = mk("batch_order", (B,))
+    for k in ("cache_seqlens", "cu_seqlens_k", "cu_seqlens_q", "page_table", "batch_order"):
         _need(out[k], k, torch.int32, dev)
     if tuple(out["page_table"].shape) != (B, max_pages):
         raise ValueError("page_table must be [batch, max_pages]")
@@ -130,7 +131,8 @@ def decode_attn_metadata(seq_lens, req_pool_indices, req_to_token, page_size, ma
         _ptr(seq_lens), _ptr(req_pool_indices), _ptr(req_to_token), req_to_token.shape[0],
         req_to_token.shape[1], req_to_token.stride(0), B, page_size, max_pages, q_mode,
         _ptr(q_in), q_stride, _ptr(out["cache_seqlens"]), _ptr(out["cu_seqlens_k"]),
-        _ptr(out["cu_seqlens_q"]), _ptr(out["page_table"]), _stream(dev))
+        _ptr(out["cu_seqlens_q"]), _ptr(out["page_table"]), _ptr(out["batch_order"]),
+        _stream(dev))
     _check(st, "decode_attn_metadata")
     return out
 
@@ -157,21 +159,26 @@ def _q_code(q):
     raise TypeError(f"q dtype {q.dtype} unsupported")
 
 
-def _split_common(q, page_table, cache_seqlens, num_pages_dim):
+def _split_common(q, page_table, cache_seqlens, batch_order):
     _need(q, "q", (torch.bfloat16, torch.float32), ndim=4)
     dev = q.device
     _need(page_table, "page_table", torch.int32, dev, 2)
     _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
     if page_table.shape[0] != q.shape[0] or cache_seqlens.shape[0] != q.shape[0]:
         raise ValueError("batch mismatch between q, page_table and cache_seqlens")
+    if batch_order is not None:
+        _need(batch_order, "batch_order", torch.int32, dev, 1)
+        if batch_order.shape[0] != q.shape[0]:
+            raise ValueError("batch_order length != batch")
     return dev
 
 
 def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
-                      softmax_scale=None, causal=False, o_partial=None, lse_partial=None):
+                      softmax_scale=None, causal=False, o_partial=None, lse_partial=None,
+                      batch_order=None):
     """Stage 1 over a dense bf16 / fp32 cache.  Returns (o_partial, lse_partial)."""
     lib = load()
-    dev = _split_common(q, page_table, cache_seqlens, None)
+    dev = _split_common(q, page_table, cache_seqlens, batch_order)
     _need(k_pool, "k_pool", q.dtype, dev, 4)
     _need(v_pool, "v_pool", q.dtype, dev, 4)
     if k_pool.shape != v_pool.shape:
@@ -184,7 +191,8 @@ def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
     o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
     st = lib.decode_attn_split(
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), page_table.stride(0),
-        page_table.shape[1], _ptr(cache_seqlens), B, qn, Hq, Hkv, D, S_p, P, num_splits, scale,
+        page_table.shape[1], _ptr(cache_seqlens), _ptr(batch_order), B, qn, Hq, Hkv, D, S_p, P,
+        num_splits, scale,
         int(bool(causal)), _ptr(o_partial), _ptr(lse_partial), _stream(dev))
     _check(st, "decode_attn_split")
     return o_partial, lse_partial
@@ -192,10 +200,10 @@ def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
 
 def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cache_seqlens,
                            num_splits, softmax_scale=None, causal=False, o_partial=None,
-                           lse_partial=None):
+                           lse_partial=None, batch_order=None):
     """Stage 1 over an INT8 cache (fp16 scale per token and kv-head)."""
     lib = load()
-    dev = _split_common(q, page_table, cache_seqlens, None)
+    dev = _split_common(q, page_table, cache_seqlens, batch_order)
     _need(k_pool, "k_pool", torch.int8, dev, 4)
     _need(v_pool, "v_pool", torch.int8, dev, 4)
     _need(k_scale, "k_scale", torch.float16, dev, 3)
@@ -208,7 +216,8 @@ def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cach
     o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
     st = lib.decode_attn_split_int8(
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
-        _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens), B, qn,
+        _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
+        _ptr(batch_order), B, qn,
         Hq, Hkv, D, S_p, P, num_splits, scale, int(bool(causal)), _ptr(o_partial),
         _ptr(lse_partial), _stream(dev))
     _check(st, "decode_attn_split_int8")
@@ -217,10 +226,10 @@ def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cach
 
 def decode_attn_split_int4(q, k_pool, v_pool, k_scale_zero, v_scale_zero, page_table,
                            cache_seqlens, num_splits, softmax_scale=None, causal=False,
-                           o_partial=None, lse_partial=None):
+                           o_partial=None, lse_partial=None, batch_order=None):
     """Stage 1 over an INT4 cache (fp16 (scale, zero) per 32-group along D)."""
     lib = load()
-    dev = _split_common(q, page_table, cache_seqlens, None)
+    dev = _split_common(q, page_table, cache_seqlens, batch_order)
     _need(k_pool, "k_pool", torch.uint8, dev, 4)
     _need(v_pool, "v_pool", torch.uint8, dev, 4)
     _need(k_scale_zero, "k_scale_zero", torch.float16, dev, 5)
@@ -237,7 +246,8 @@ def decode_attn_split_int4(q, k_pool, v_pool, k_scale_zero, v_scale_zero, page_t
     o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
     st = lib.decode_attn_split_int4(
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale_zero), _ptr(v_scale_zero),
-        _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens), B, qn,
+        _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
+        _ptr(batch_order), B, qn,
         Hq, Hkv, D, S_p, P, num_splits, scale, int(bool(causal)), _ptr(o_partial),
         _ptr(lse_partial), _stream(dev))
     _check(st, "decode_attn_split_int4")

@@ -7,7 +7,9 @@
 // exclusive prefix over rows [0, b) with a workgroup reduction, so no
 // cross-workgroup scan (and no second launch) is needed; the last row also
 // writes the closing entries cu_*[B].  Prefix sums are formed in 64-bit and
-// stored as int32.
+// stored as int32.  The optional batch order (requests by descending length,
+// ties by index) is built the same way: row b counts the rows that sort
+// before it and stores b at that rank.
 #include "common.h"
 
 namespace {
@@ -29,7 +31,8 @@ __global__ __launch_bounds__(kThreads) void metadata_kernel(
     const int32_t* __restrict__ r2t, long long r2t_rows, long long r2t_cols,
     long long r2t_stride, int batch, int page_size, int max_pages, int q_mode,
     const int32_t* __restrict__ q_in, int q_stride, int32_t* __restrict__ cache_seqlens,
-    int32_t* __restrict__ cu_k, int32_t* __restrict__ cu_q, int32_t* __restrict__ page_table) {
+    int32_t* __restrict__ cu_k, int32_t* __restrict__ cu_q, int32_t* __restrict__ page_table,
+    int32_t* __restrict__ order) {
   __shared__ long long sh[4];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -44,6 +47,15 @@ __global__ __launch_bounds__(kThreads) void metadata_kernel(
   if (q_mode == DA_Q_CUMSUM) pq = block_sum(pq, sh);
 
   const int L = max(seq_lens[b], 0);
+  if (order) {
+    long long rank = 0;
+    for (int j = tid; j < batch; j += kThreads) {
+      const int Lj = max(seq_lens[j], 0);
+      rank += (Lj > L || (Lj == L && j < b)) ? 1 : 0;
+    }
+    rank = block_sum(rank, sh);
+    if (tid == 0) order[rank] = b;
+  }
   if (tid == 0) {
     cache_seqlens[b] = L;
     cu_k[b] = (int32_t)pk;
@@ -85,7 +97,8 @@ extern "C" int32_t decode_attn_metadata(const int32_t* seq_lens, const int64_t* 
                                         int32_t batch, int32_t page_size, int32_t max_pages,
                                         int32_t q_mode, const int32_t* q_in, int32_t q_stride,
                                         int32_t* cache_seqlens, int32_t* cu_seqlens_k,
-                                        int32_t* cu_seqlens_q, int32_t* page_table, void* stream) {
+                                        int32_t* cu_seqlens_q, int32_t* page_table,
+                                        int32_t* batch_order, void* stream) {
   if (!seq_lens || !req_pool_indices || !req_to_token || !cache_seqlens || !cu_seqlens_k ||
       !cu_seqlens_q || !page_table)
     return DA_ERR_INVALID_ARG;
@@ -100,6 +113,6 @@ extern "C" int32_t decode_attn_metadata(const int32_t* seq_lens, const int64_t* 
                      seq_lens, req_pool_indices, req_to_token, (long long)req_to_token_rows,
                      (long long)req_to_token_cols, (long long)req_to_token_stride, batch,
                      page_size, max_pages, q_mode, q_in, q_stride, cache_seqlens, cu_seqlens_k,
-                     cu_seqlens_q, page_table);
+                     cu_seqlens_q, page_table, batch_order);
   return da_host::launch_status();
 }

@@ -39,6 +39,7 @@ struct SplitArgs {
   const uint16_t* vs;
   const int32_t* pt;
   const int32_t* seqlens;
+  const int32_t* order;  // nullable: request served by grid z-index
   float* o;
   float* lse;
   int q_bf16;
@@ -140,7 +141,9 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
   __shared__ float sm_l[kWaves][RT];
   __shared__ float sm_acc[kWaves][RT][D];
 
-  const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, s = blockIdx.y;
+  int b = a.order ? a.order[blockIdx.z] : (int)blockIdx.z;
+  if ((unsigned)b >= gridDim.z) b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane >> 4, c = lane & 15;
 
@@ -383,11 +386,11 @@ int32_t check_common(const void* q, const void* k, const void* v, const int32_t*
 
 SplitArgs make_args(const void* q, int q_bf16, const void* k, const void* v, const uint16_t* ks,
                     const uint16_t* vs, const int32_t* pt, int32_t pt_stride, int32_t max_pages,
-                    const int32_t* seqlens, int32_t qn, int32_t Hq, int32_t Hkv, int32_t ps,
+                    const int32_t* seqlens, const int32_t* order, int32_t qn, int32_t Hq, int32_t Hkv, int32_t ps,
                     int32_t num_pages, int32_t S, float scale, int32_t causal, float* o,
                     float* lse) {
   SplitArgs a;
-  a.q = q; a.k = k; a.v = v; a.ks = ks; a.vs = vs; a.pt = pt; a.seqlens = seqlens;
+  a.q = q; a.k = k; a.v = v; a.ks = ks; a.vs = vs; a.pt = pt; a.seqlens = seqlens; a.order = order;
   a.o = o; a.lse = lse; a.q_bf16 = q_bf16;
   a.pt_stride = pt_stride; a.max_pages = max_pages;
   a.qn = qn; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.R = a.G * qn;
@@ -399,11 +402,18 @@ SplitArgs make_args(const void* q, int q_bf16, const void* k, const void* v, con
 
 }  // namespace
 
+// bf16 stage 1 for G*q <= 5 (split_bf16.hip); -1 when the shape is not covered.
+int32_t da_split_bf16_fast(const void* q, const void* k, const void* v, const int32_t* pt,
+                           int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
+                           const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
+                           int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
+                           float scale, int32_t causal, float* o, float* lse, hipStream_t st);
+
 extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool,
                                      const void* v_pool, const int32_t* page_table,
                                      int32_t page_table_stride, int32_t max_pages,
-                                     const int32_t* cache_seqlens, int32_t batch,
-                                     int32_t q_per_req, int32_t num_q_heads,
+                                     const int32_t* cache_seqlens, const int32_t* batch_order,
+                                     int32_t batch, int32_t q_per_req, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                                      int32_t num_pages, int32_t num_splits, float softmax_scale,
                                      int32_t causal, float* o_partial, float* lse_partial,
@@ -414,19 +424,27 @@ extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k
   if (st) return st;
   if (dtype != DA_BF16 && dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
   const SplitArgs a = make_args(q, dtype == DA_BF16, k_pool, v_pool, nullptr, nullptr, page_table,
-                                page_table_stride, max_pages, cache_seqlens, q_per_req,
+                                page_table_stride, max_pages, cache_seqlens, batch_order, q_per_req,
                                 num_q_heads, num_kv_heads, page_size, num_pages, num_splits,
                                 softmax_scale, causal, o_partial, lse_partial);
   hipStream_t s = (hipStream_t)stream;
-  return dtype == DA_BF16 ? launch_kv<KV_BF16>(a, head_dim, batch, s)
-                          : launch_kv<KV_F32>(a, head_dim, batch, s);
+  if (dtype == DA_BF16) {
+    const int32_t fast = da_split_bf16_fast(q, k_pool, v_pool, page_table, page_table_stride,
+                                            max_pages, cache_seqlens, batch_order, batch, q_per_req,
+                                            num_q_heads, num_kv_heads, head_dim, page_size,
+                                            num_pages, num_splits, softmax_scale, causal,
+                                            o_partial, lse_partial, s);
+    if (fast >= 0) return fast;
+    return launch_kv<KV_BF16>(a, head_dim, batch, s);
+  }
+  return launch_kv<KV_F32>(a, head_dim, batch, s);
 }
 
 extern "C" int32_t decode_attn_split_int8(
     const void* q, int32_t q_dtype, const int8_t* k_pool, const int8_t* v_pool,
     const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* page_table,
-    int32_t page_table_stride, int32_t max_pages, const int32_t* cache_seqlens, int32_t batch,
-    int32_t q_per_req, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t page_table_stride, int32_t max_pages, const int32_t* cache_seqlens,
+    const int32_t* batch_order, int32_t batch, int32_t q_per_req, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t page_size, int32_t num_pages, int32_t num_splits, float softmax_scale,
     int32_t causal, float* o_partial, float* lse_partial, void* stream) {
   int32_t st = check_common(q, k_pool, v_pool, page_table, page_table_stride, max_pages,
@@ -437,7 +455,7 @@ extern "C" int32_t decode_attn_split_int8(
   if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
   const SplitArgs a = make_args(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale, v_scale,
                                 page_table, page_table_stride, max_pages, cache_seqlens,
-                                q_per_req, num_q_heads, num_kv_heads, page_size, num_pages,
+                                batch_order, q_per_req, num_q_heads, num_kv_heads, page_size, num_pages,
                                 num_splits, softmax_scale, causal, o_partial, lse_partial);
   return launch_kv<KV_I8>(a, head_dim, batch, (hipStream_t)stream);
 }
@@ -445,8 +463,8 @@ extern "C" int32_t decode_attn_split_int8(
 extern "C" int32_t decode_attn_split_int4(
     const void* q, int32_t q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
     const uint16_t* k_scale_zero, const uint16_t* v_scale_zero, const int32_t* page_table,
-    int32_t page_table_stride, int32_t max_pages, const int32_t* cache_seqlens, int32_t batch,
-    int32_t q_per_req, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t page_table_stride, int32_t max_pages, const int32_t* cache_seqlens,
+    const int32_t* batch_order, int32_t batch, int32_t q_per_req, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t page_size, int32_t num_pages, int32_t num_splits, float softmax_scale,
     int32_t causal, float* o_partial, float* lse_partial, void* stream) {
   int32_t st = check_common(q, k_pool, v_pool, page_table, page_table_stride, max_pages,
@@ -457,7 +475,7 @@ extern "C" int32_t decode_attn_split_int4(
   if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
   const SplitArgs a = make_args(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale_zero,
                                 v_scale_zero, page_table, page_table_stride, max_pages,
-                                cache_seqlens, q_per_req, num_q_heads, num_kv_heads, page_size,
+                                cache_seqlens, batch_order, q_per_req, num_q_heads, num_kv_heads, page_size,
                                 num_pages, num_splits, softmax_scale, causal, o_partial,
                                 lse_partial);
   return launch_kv<KV_I4>(a, head_dim, batch, (hipStream_t)stream);

@@ -99,8 +99,12 @@ extern "C" {
  *                       j < ceil(cache_seqlens[b] / page_size), else 0.  A negative
  *                       or >= req_to_token_rows rpi, a column >= req_to_token_cols,
  *                       or a negative slot gives 0 (-1 sentinel guard).
- *   q_in: host-invisible device array, required for CUMSUM ([batch]) and PRESET
- *   ([batch+1]); ignored (may be NULL) for STRIDED.
+ *   q_in: device array, required for CUMSUM ([batch]) and PRESET ([batch+1]);
+ *   ignored (may be NULL) for STRIDED.
+ *   batch_order (nullable) [batch] int32: request indices by descending
+ *   cache_seqlens, ties by ascending index.  Passed to the split calls, it
+ *   makes the longest requests' splits start first (scheduling only: results
+ *   do not depend on it).
  */
 int32_t decode_attn_metadata(const int32_t* seq_lens, const int64_t* req_pool_indices,
                              const int32_t* req_to_token, int64_t req_to_token_rows,
@@ -108,7 +112,8 @@ int32_t decode_attn_metadata(const int32_t* seq_lens, const int64_t* req_pool_in
                              int32_t batch, int32_t page_size, int32_t max_pages,
                              int32_t q_mode, const int32_t* q_in, int32_t q_stride,
                              int32_t* cache_seqlens, int32_t* cu_seqlens_k,
-                             int32_t* cu_seqlens_q, int32_t* page_table, void* stream);
+                             int32_t* cu_seqlens_q, int32_t* page_table, int32_t* batch_order,
+                             void* stream);
 
 /*
  * Stage 1 over a dense bf16 or fp32 cache (GQA flash decode "stage 1" and
@@ -120,10 +125,16 @@ int32_t decode_attn_metadata(const int32_t* seq_lens, const int64_t* req_pool_in
  *   1 <= num_splits <= DA_MAX_SPLITS; 1 <= q_per_req <= DA_MAX_Q_PER_REQ.
  *   page_table_stride >= max_pages >= 1.  cache_seqlens is the [batch] int32
  *   array from decode_attn_metadata (or any caller array of KV lengths).
+ *   batch_order (nullable): a permutation of [0, batch) giving the order in
+ *   which requests are scheduled (decode_attn_metadata's batch_order); NULL
+ *   means 0..batch-1.  An entry outside [0, batch) is replaced by the grid
+ *   index; a non-permutation leaves some requests unprocessed (unspecified
+ *   results, never an out-of-bounds access).
  */
 int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool, const void* v_pool,
                           const int32_t* page_table, int32_t page_table_stride, int32_t max_pages,
-                          const int32_t* cache_seqlens, int32_t batch, int32_t q_per_req,
+                          const int32_t* cache_seqlens, const int32_t* batch_order,
+                          int32_t batch, int32_t q_per_req,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t page_size, int32_t num_pages, int32_t num_splits,
                           float softmax_scale, int32_t causal, float* o_partial,
@@ -141,7 +152,8 @@ int32_t decode_attn_split_int8(const void* q, int32_t q_dtype, const int8_t* k_p
                                const int8_t* v_pool, const uint16_t* k_scale,
                                const uint16_t* v_scale, const int32_t* page_table,
                                int32_t page_table_stride, int32_t max_pages,
-                               const int32_t* cache_seqlens, int32_t batch, int32_t q_per_req,
+                               const int32_t* cache_seqlens, const int32_t* batch_order,
+                               int32_t batch, int32_t q_per_req,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                int32_t page_size, int32_t num_pages, int32_t num_splits,
                                float softmax_scale, int32_t causal, float* o_partial,
@@ -161,7 +173,8 @@ int32_t decode_attn_split_int4(const void* q, int32_t q_dtype, const uint8_t* k_
                                const uint8_t* v_pool, const uint16_t* k_scale_zero,
                                const uint16_t* v_scale_zero, const int32_t* page_table,
                                int32_t page_table_stride, int32_t max_pages,
-                               const int32_t* cache_seqlens, int32_t batch, int32_t q_per_req,
+                               const int32_t* cache_seqlens, const int32_t* batch_order,
+                               int32_t batch, int32_t q_per_req,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                int32_t page_size, int32_t num_pages, int32_t num_splits,
                                float softmax_scale, int32_t causal, float* o_partial,

@@ -16,6 +16,8 @@ Readings taken where the page is silent:
   ``j < ceil(cache_seqlens[b] / page_size)``; every other entry (the tail) is 0.
   A negative / out-of-range ``rpi[b]``, a slot column past the table width, or
   a negative slot gives 0 instead of an index.
+* ``batch_order`` (a scheduling aid the pages do not have): request indices
+  sorted by descending ``cache_seqlens``, ties by ascending index.
 All arithmetic is exact integer arithmetic (Python ints).
 """
 from __future__ import annotations
@@ -30,7 +32,7 @@ Q_PRESET = 2
 def metadata(seq_lens, req_pool_indices, req_to_token, page_size, max_pages,
              q_mode=Q_STRIDED, q_in=None, q_stride=1):
     """Returns dict(cache_seqlens [B], cu_seqlens_k [B+1], cu_seqlens_q [B+1],
-    page_table [B, max_pages]) as int64 numpy arrays (values fit int32)."""
+    page_table [B, max_pages], batch_order [B]) as int64 numpy arrays."""
     seq_lens = [int(x) for x in np.asarray(seq_lens).reshape(-1)]
     rpi = [int(x) for x in np.asarray(req_pool_indices).reshape(-1)]
     r2t = np.asarray(req_to_token)
@@ -67,7 +69,10 @@ def metadata(seq_lens, req_pool_indices, req_to_token, page_size, max_pages,
             slot = int(r2t[r, col])
             pt[b, j] = slot // page_size if slot >= 0 else 0
 
+    order = sorted(range(B), key=lambda b: (-cache[b], b))
+
     return dict(
+        batch_order=np.asarray(order, dtype=np.int64),
         cache_seqlens=np.asarray(cache, dtype=np.int64),
         cu_seqlens_k=np.asarray(cu_k, dtype=np.int64),
         cu_seqlens_q=np.asarray(cu_q, dtype=np.int64),

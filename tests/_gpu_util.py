@@ -165,22 +165,23 @@ def oracle_sampled(batch: W.PagedBatch, pairs):
 
 
 # ---------------------------------------------------------------- GPU path
-def run_split(da, batch: W.PagedBatch, S: int):
+def run_split(da, batch: W.PagedBatch, S: int, batch_order=None):
     w = batch.w
     if w.kv == W.KV_DENSE:
         return da.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, batch.page_table,
-                                    batch.seq_lens, S, w.softmax_scale, w.causal)
+                                    batch.seq_lens, S, w.softmax_scale, w.causal,
+                                    batch_order=batch_order)
     if w.kv == W.KV_INT8:
         return da.decode_attn_split_int8(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
                                          batch.v_scale, batch.page_table, batch.seq_lens, S,
-                                         w.softmax_scale, w.causal)
+                                         w.softmax_scale, w.causal, batch_order=batch_order)
     return da.decode_attn_split_int4(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
                                      batch.v_scale, batch.page_table, batch.seq_lens, S,
-                                     w.softmax_scale, w.causal)
+                                     w.softmax_scale, w.causal, batch_order=batch_order)
 
 
-def run_decode(da, batch: W.PagedBatch, S: int, out_dtype=torch.bfloat16):
-    o, l = run_split(da, batch, S)
+def run_decode(da, batch: W.PagedBatch, S: int, out_dtype=torch.bfloat16, batch_order=None):
+    o, l = run_split(da, batch, S, batch_order)
     out, lse = da.decode_attn_merge(o, l, out_dtype=out_dtype, want_lse=True)
     return out, lse, o, l
 

@@ -55,11 +55,11 @@ def test_strerror_and_version(lib):
 
 def _split_args(**kw):
     a = dict(q=FAKE, dtype=B.DA_BF16, k=FAKE, v=FAKE, pt=FAKE, pt_stride=8, max_pages=8,
-             seqlens=FAKE, batch=4, qn=1, Hq=32, Hkv=8, D=128, ps=64, num_pages=100, S=4,
+             seqlens=FAKE, order=None, batch=4, qn=1, Hq=32, Hkv=8, D=128, ps=64, num_pages=100, S=4,
              scale=0.1, causal=0, o=FAKE, lse=FAKE, stream=None)
     a.update(kw)
     return [a[k] for k in ("q", "dtype", "k", "v", "pt", "pt_stride", "max_pages", "seqlens",
-                           "batch", "qn", "Hq", "Hkv", "D", "ps", "num_pages", "S", "scale",
+                           "order", "batch", "qn", "Hq", "Hkv", "D", "ps", "num_pages", "S", "scale",
                            "causal", "o", "lse", "stream")]
 
 
@@ -80,7 +80,7 @@ def test_int8_int4_validation(lib):
     assert lib.decode_attn_split_int8(*args8) == 1
     args4 = base[:2] + [FAKE, FAKE, FAKE, None] + base[4:]
     assert lib.decode_attn_split_int4(*args4) == 1
-    args4 = base[:2] + [FAKE, FAKE, FAKE, FAKE] + base[4:12] + [80] + base[13:]
+    args4 = base[:2] + [FAKE, FAKE, FAKE, FAKE] + base[4:13] + [80] + base[14:]
     assert lib.decode_attn_split_int4(*args4) == 2
 
 
@@ -89,7 +89,8 @@ def test_merge_and_metadata_and_gather_validation(lib):
     assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 96, 4, FAKE, B.DA_BF16, None, None) == 2
     assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 128, 4, FAKE, 5, None, None) == 2
     assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 128, 0, FAKE, B.DA_BF16, None, None) == 1
-    md = [FAKE, FAKE, FAKE, 4, 64, 64, 2, 16, 4, B.DA_Q_STRIDED, None, 1, FAKE, FAKE, FAKE, FAKE, None]
+    md = [FAKE, FAKE, FAKE, 4, 64, 64, 2, 16, 4, B.DA_Q_STRIDED, None, 1, FAKE, FAKE, FAKE, FAKE,
+          None, None]
     bad = list(md); bad[0] = None
     assert lib.decode_attn_metadata(*bad) == 1
     bad = list(md); bad[9] = 7

@@ -96,6 +96,19 @@ def test_page_permutation_is_bit_identical(gpu):
     assert torch.equal(lse1, lse2)
 
 
+def test_batch_order_is_bit_identical(gpu):
+    """Scheduling requests longest-first (the metadata batch order) changes no bit."""
+    for w in (RAGGED_SMALL, INT8_SMALL, INT4_SMALL, MTP_BF16):
+        log(f"batch order {w.name}")
+        batch = W.make_batch(w, device="cuda")
+        md = gpu.decode_attn_metadata(batch.seq_lens, batch.req_pool_indices, batch.req_to_token,
+                                      w.page_size, batch.max_pages)
+        for S in (1, 4):
+            o1, l1 = U.run_split(gpu, batch, S)
+            o2, l2 = U.run_split(gpu, batch, S, batch_order=md["batch_order"])
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_num_splits_invariance(gpu):
     w = RAGGED_SMALL
     log("num_splits invariance")

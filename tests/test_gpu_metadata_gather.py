@@ -38,6 +38,7 @@ def test_metadata_hand_built_batch(gpu, mode):
     assert md["cu_seqlens_k"].tolist() == e["cu_seqlens_k"]
     assert md["page_table"].tolist() == e["page_table"]
     assert md["cu_seqlens_q"].tolist() == e[key]
+    assert md["batch_order"].tolist() == e["batch_order"]
 
 
 def _check_md_against_oracle(seq, rpi, r2t, ps, max_pages, mode=0, q_in=None, q_stride=1):
@@ -45,7 +46,7 @@ def _check_md_against_oracle(seq, rpi, r2t, ps, max_pages, mode=0, q_in=None, q_
     md = gpu_mod.decode_attn_metadata(
         _i32(seq), torch.as_tensor(np.asarray(rpi), dtype=torch.int64, device="cuda"), _i32(r2t),
         ps, max_pages, q_mode=mode, q_in=None if q_in is None else _i32(q_in), q_stride=q_stride)
-    for k in ("cache_seqlens", "cu_seqlens_k", "cu_seqlens_q", "page_table"):
+    for k in ("cache_seqlens", "cu_seqlens_k", "cu_seqlens_q", "page_table", "batch_order"):
         assert np.array_equal(md[k].cpu().numpy().astype(np.int64), ref[k]), k
     return md
 

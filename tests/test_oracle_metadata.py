@@ -31,6 +31,7 @@ def test_hand_built_batch(mode, key, extra):
     assert md["cu_seqlens_k"].tolist() == e["cu_seqlens_k"]
     assert md["page_table"].tolist() == e["page_table"]
     assert md["cu_seqlens_q"].tolist() == e[key]
+    assert md["batch_order"].tolist() == e["batch_order"]
 
 
 @pytest.mark.parametrize("w", [W.TINY_FP32, W.BF16_B16.scaled(batch=5, length=300),
@@ -51,6 +52,13 @@ def test_closed_forms_on_generated_batches(w):
     for b in range(len(L)):
         assert np.all(md["page_table"][b, n[b]:] == 0)
     assert md["cu_seqlens_q"].tolist() == [3 * b for b in range(len(L) + 1)]
+    order = md["batch_order"]
+    assert sorted(order.tolist()) == list(range(len(L)))          # a permutation
+    Ls = L[order]
+    assert np.all(Ls[:-1] >= Ls[1:])                               # non-increasing lengths
+    for a, b in zip(order[:-1], order[1:]):                        # ties keep index order
+        if L[a] == L[b]:
+            assert a < b
 
 
 def test_sentinels_never_produce_negative_or_out_of_range_ids():

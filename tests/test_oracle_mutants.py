@@ -43,6 +43,8 @@ METADATA_MUTANTS = [
     ("rpi unchecked", "if r < 0 or r >= R:\n            continue", "if False:\n            continue"),
     ("strided off by one", "cu_q = [b * int(q_stride) for b in range(B + 1)]",
      "cu_q = [(b + 1) * int(q_stride) for b in range(B + 1)]"),
+    ("order ascending", "key=lambda b: (-cache[b], b)", "key=lambda b: (cache[b], b)"),
+    ("order ties reversed", "key=lambda b: (-cache[b], b)", "key=lambda b: (-cache[b], -b)"),
 ]
 
 
