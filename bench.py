@@ -44,7 +44,14 @@ def parse():
     p.add_argument("--splits", type=int, default=0, help="override num_splits (0 = table)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--tune", action="store_true", help="sweep num_splits per bucket, write the table")
+    p.add_argument("--tune", nargs="?", const="all", default=None,
+                   help="sweep num_splits per bucket and write the table (optionally a comma list "
+                        "of cache formats: bf16,int8,int4)")
+    p.add_argument("--profile-only", action="store_true",
+                   help="for rocprofv3 --pmc runs: one 1 GiB copy (the byte-count reference), "
+                        "then --steps whole steps, no timing")
+    p.add_argument("--rocprof-summary", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="summarise rocprofv3 CSV output into profiles/ (no GPU needed)")
     return p.parse_args()
 
 
@@ -72,12 +79,21 @@ def algorithmic_bytes(w, lengths, out_elem=2):
                 step=kv + q_bytes + out_bytes + 4 * n_pages + 4 * w.batch)
 
 
-def kernel_hash() -> str:
+# source files of the stage-1 kernel each cache format runs on (traffic counters
+# taken on a kernel stay valid only while these files are unchanged)
+KERNEL_SOURCES = {"bf16": ["split_bf16.hip", "common.h"],
+                  "fp32": ["split_fma.hip", "common.h"],
+                  "int8": ["split_int8.hip", "split_fma.hip", "common.h"],
+                  "int4": ["split_mfma.hip", "split_fma.hip", "common.h"]}
+
+
+def kernel_hash(kv="bf16") -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_paged_gqa_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in KERNEL_SOURCES[kv]:
+        path = os.path.join(csrc, f)
+        if os.path.exists(path):
+            h.update(open(path, "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -231,7 +247,7 @@ def make_resident(da, w, torch):
     return batch
 
 
-def tune(da, torch):
+def tune(da, torch, which="all"):
     """Sweep num_splits per KV-length bucket and batch key; write splits_table.json."""
     from decode_attention_paged_gqa_amd import workloads as W
     from decode_attention_paged_gqa_amd.splits import (BATCH_KEYS, BUCKET_TOKENS, CANDIDATES,
@@ -239,36 +255,123 @@ def tune(da, torch):
 
     table = SplitTable.load()
     variants = [W.RAGGED_B64, W.BF16_B16, W.INT8_B32, W.INT4_MTP_B64]
+    if which != "all":
+        keep = set(which.split(","))
+        variants = [v for v in variants if kv_name(v) in keep]
     for base in variants:
         key = kernel_key(kv_name(base), rows_per_kv_head(base), base.head_dim, base.page_size)
         rows = []
         for bk in BATCH_KEYS:
             row = []
             for k in range(1, N_BUCKETS + 1):
-                # representative batch: the bucket's upper length for one request, the
-                # rest log-uniform below it (ragged, like the pages' serving batches)
+                # representative batches: the bucket's upper length for one request, the
+                # rest log-uniform below it (ragged, like the pages' serving batches);
+                # the split count with the least total time over three seeds wins
                 Lmax = k * BUCKET_TOKENS
-                w = base.scaled(batch=bk, lengths="loguniform", length_lo=max(64, Lmax // 32),
-                                length_hi=Lmax, pin_max=True, seed=100 + k)
-                batch = make_resident(da, w, torch)
-                best, best_t = None, None
-                for S in CANDIDATES:
-                    t = time_split_only(da, batch, S, 10, torch)
-                    if best_t is None or t < best_t * 0.97:
-                        best, best_t = S, t
+                tot = {S: 0.0 for S in CANDIDATES}
+                for rep in range(3):
+                    w = base.scaled(batch=bk, lengths="loguniform", length_lo=max(64, Lmax // 32),
+                                    length_hi=Lmax, pin_max=True, seed=100 + 10 * k + rep)
+                    batch = make_resident(da, w, torch)
+                    for S in CANDIDATES:
+                        tot[S] += time_split_only(da, batch, S, 10, torch)
+                    del batch
+                    torch.cuda.empty_cache()
+                best = min(CANDIDATES, key=lambda S: (tot[S], S))
                 row.append(best)
-                print(f"tune {key} B={bk} bucket={k} -> S={best} ({best_t * 1e3:.1f} us)",
-                      flush=True)
-                del batch
-                torch.cuda.empty_cache()
+                print(f"tune {key} B={bk} bucket={k} -> S={best} "
+                      + " ".join(f"{S}:{tot[S] / 3 * 1e3:.1f}" for S in CANDIDATES), flush=True)
             rows.append(row)
         table.tables[key] = rows
     table.save()
     print(json.dumps({"tuned": list(table.tables)}), flush=True)
 
 
+COPY_BYTES = 1 << 30
+
+
+def profile_only(da, w, batch, S, steps, torch):
+    """Dispatches for counter collection: a plain 1 GiB device copy whose byte
+    count is known (it calibrates FETCH_SIZE / WRITE_SIZE), then whole steps."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    B, qn, Hq, D = batch.q.shape
+    o = torch.empty((B, qn, Hq, S, D), dtype=torch.float32, device="cuda")
+    l = torch.empty((B, qn, Hq, S), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, qn, Hq, D), dtype=torch.bfloat16, device="cuda")
+    md_out = dict(batch.md)
+    for _ in range(steps):
+        da.decode_attn_metadata(batch.seq_lens, batch.req_pool_indices, batch.req_to_token,
+                                w.page_size, batch.max_pages, q_stride=w.q_per_req, out=md_out)
+        stage1(da, batch, S, o, l)
+        da.decode_attn_merge(o, l, out=out)
+    torch.cuda.synchronize()
+    ab = algorithmic_bytes(w, batch.lengths)
+    print(json.dumps({"profile_only": w.name, "num_splits": S, "copy_bytes": COPY_BYTES,
+                      "split_algorithmic_bytes": ab["split"], "kernel_hash": kernel_hash(kv_name(w))}),
+          flush=True)
+
+
+def _read_csv(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def rocprof_summary(trace_dir, fetch_dir, write_dir):
+    """Per-kernel stats from the kernel trace, HBM bytes per dispatch from the
+    two counter runs, calibrated by the 1 GiB copy (read 1 GiB, write 1 GiB)."""
+    stats = _read_csv(trace_dir, "kernel_stats.csv")
+    def counters(d, name):
+        rows = _read_csv(d, "counter_collection.csv")
+        per = {}
+        for r in rows:
+            if r.get("Counter_Name") != name:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        return per
+    fetch = counters(fetch_dir, "FETCH_SIZE")
+    write = counters(write_dir, "WRITE_SIZE")
+
+    def by_kernel(per, pat):
+        vals = [v for (d, k), v in sorted(per.items(), key=lambda x: int(x[0][0])) if pat in k]
+        return vals
+    # the reference copy is the largest copyBuffer dispatch (1 GiB read, 1 GiB written)
+    copy_fetch_kib = sorted(by_kernel(fetch, "copyBuffer"))[-1:]
+    copy_write_kib = sorted(by_kernel(write, "copyBuffer"))[-1:]
+    split_fetch = by_kernel(fetch, "split_")
+    split_write = by_kernel(write, "split_")
+    f_scale = (COPY_BYTES / 1024) / max(copy_fetch_kib[-1], 1e-9) if copy_fetch_kib else None
+    w_scale = (COPY_BYTES / 1024) / max(copy_write_kib[-1], 1e-9) if copy_write_kib else None
+    lines = ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                     f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} |")
+    sf = float(np.mean(split_fetch)) * 1024 * f_scale if split_fetch and f_scale else None
+    sw = float(np.mean(split_write)) * 1024 * w_scale if split_write and w_scale else None
+    return "\n".join(lines), dict(copy_fetch_kib=copy_fetch_kib[-1] if copy_fetch_kib else None,
+                                   copy_write_kib=copy_write_kib[-1] if copy_write_kib else None,
+                                   fetch_scale=f_scale, write_scale=w_scale,
+                                   split_fetch_kib=split_fetch, split_write_kib=split_write,
+                                   split_fetch_bytes=sf, split_write_bytes=sw)
+
+
 def main():
     args = parse()
+    if args.rocprof_summary:
+        table, tr = rocprof_summary(*args.rocprof_summary)
+        print(table)
+        print(json.dumps(tr))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the multi-GPU (kv-head / batch / "
               "sequence) sharding is described in DESIGN.md and not launched. Use --gpus 1.",
@@ -282,12 +385,15 @@ def main():
 
     da.load()
     if args.tune:
-        tune(da, torch)
+        tune(da, torch, args.tune)
         return
     w = W.WORKLOADS[args.workload]
     batch = make_resident(da, w, torch)
     key = kernel_key(kv_name(w), rows_per_kv_head(w), w.head_dim, w.page_size)
     S = args.splits or SplitTable.load().pick(key, w.batch, int(batch.lengths.max()))
+    if args.profile_only:
+        profile_only(da, w, batch, S, args.steps, torch)
+        return
     ms, split_ms, merge_ms, meta_ms = time_config(da, batch, S, args.steps, args.warmup, torch)
     ab = algorithmic_bytes(w, batch.lengths)
     value = ab["step"] / (ms * 1e-3) / 1e9
@@ -296,8 +402,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         t = json.load(open(TRAFFIC_FILE))
         ent = t.get(w.name)
-        if ent and ent.get("kernel_hash") == kernel_hash() and ent.get("num_splits") == S:
-            traffic = ent.get("bytes_per_launch")
+        if ent and ent.get("kernel_hash") == kernel_hash(kv_name(w)) and ent.get("num_splits") == S:
+            traffic = ent.get("hbm_bytes_per_launch")
     res = {
         "metric": "decode-attn achieved HBM GB/s (% of peak) + us/call, B=64 KV=32K bf16",
         "value": round(value, 2),

@@ -20,7 +20,7 @@
 //   p.v : fp32 FMA with p kept in fp32
 //
 // Memory pipeline: tiles are fetched with global_load_lds_dwordx4 straight
-// into a per-wave ring of STAGES LDS stages (4 KB each), STAGES - 1 tiles
+// into a per-wave ring of STAGES (= 4) LDS stages (4 KB each), STAGES - 1 tiles
 // ahead of the one being computed, so no VGPRs hold data in flight.  Each
 // lane reads back exactly the 16-byte slots its own loads filled (lane i of
 // a load lands at stage + 16*i), which is conflict-free.  The compiler would
@@ -160,7 +160,7 @@ struct Smem {
 };
 
 template <int D, int RT, int STAGES>
-__global__ __launch_bounds__(kThreads, 3) void split_bf16_kernel(const Bf16Args a) {
+__global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args a) {
   using SM = Smem<D, RT, STAGES>;
   constexpr int CPL = SM::CPL;
   constexpr int NCH = 2 * CPL;  // 16-byte loads per tile (K chunks, then V chunks)
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 3) void split_bf16_kernel(const Bf16Args 
 
 template <int D, int RT>
 int32_t launch(const Bf16Args& a, int batch, hipStream_t st) {
-  hipLaunchKernelGGL((split_bf16_kernel<D, RT, 3>), dim3(a.Hkv, a.S, batch), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((split_bf16_kernel<D, RT, 4>), dim3(a.Hkv, a.S, batch), dim3(kThreads), 0, st, a);
   return da_host::launch_status();
 }
 

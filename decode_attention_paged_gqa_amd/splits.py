@@ -59,10 +59,15 @@ class SplitTable:
 
     def save(self, path: str = None):
         path = path or TABLE_PATH
+        lines = ['{', f' "bucket_tokens": {self.bucket_tokens},',
+                 f' "batch_keys": {json.dumps(self.batch_keys)},', ' "tables": {']
+        keys = sorted(self.tables)
+        for i, k in enumerate(keys):
+            rows = ",\n   ".join(json.dumps(r) for r in self.tables[k])
+            lines.append(f'  "{k}": [\n   {rows}\n  ]' + ("," if i + 1 < len(keys) else ""))
+        lines += [' }', '}']
         with open(path, "w") as f:
-            json.dump({"bucket_tokens": self.bucket_tokens, "batch_keys": self.batch_keys,
-                       "tables": self.tables}, f, indent=1, sort_keys=True)
-            f.write("\n")
+            f.write("\n".join(lines) + "\n")
 
     def table_for(self, key: str) -> List[List[int]]:
         if key in self.tables:
