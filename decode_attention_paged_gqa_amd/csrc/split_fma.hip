@@ -440,6 +440,15 @@ extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k
   return launch_kv<KV_F32>(a, head_dim, batch, s);
 }
 
+// INT4 stage 1 on the matrix cores for 9..16 rows (split_mfma.hip); -1 when
+// the shape is not covered.
+int32_t da_split_int4_mfma(const void* q, int q_bf16, const uint8_t* k, const uint8_t* v,
+                           const uint16_t* ksz, const uint16_t* vsz, const int32_t* pt,
+                           int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
+                           const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
+                           int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
+                           float scale, int32_t causal, float* o, float* lse, hipStream_t st);
+
 extern "C" int32_t decode_attn_split_int8(
     const void* q, int32_t q_dtype, const int8_t* k_pool, const int8_t* v_pool,
     const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* page_table,
@@ -478,5 +487,12 @@ extern "C" int32_t decode_attn_split_int4(
                                 cache_seqlens, batch_order, q_per_req, num_q_heads, num_kv_heads, page_size,
                                 num_pages, num_splits, softmax_scale, causal, o_partial,
                                 lse_partial);
+  const int32_t mf = da_split_int4_mfma(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale_zero,
+                                        v_scale_zero, page_table, page_table_stride, max_pages,
+                                        cache_seqlens, batch_order, batch, q_per_req, num_q_heads,
+                                        num_kv_heads, head_dim, page_size, num_pages, num_splits,
+                                        softmax_scale, causal, o_partial, lse_partial,
+                                        (hipStream_t)stream);
+  if (mf >= 0) return mf;
   return launch_kv<KV_I4>(a, head_dim, batch, (hipStream_t)stream);
 }

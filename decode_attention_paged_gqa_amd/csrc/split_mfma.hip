@@ -1,0 +1,485 @@
+// Stage 1 over an INT4 cache on the matrix cores, for query groups of
+// 9..16 rows per kv-head (G*q, e.g. the MTP verify batches of LightLLM
+// PR #1549 "Covered decode kernels": INT4 KV flash decode stage 1, MTP
+// attention; SGLang #36219 digest code listing: several tokens per request).
+// Same contract as decode_attn_split_int4.
+//
+// One workgroup (4 waves) per (kv-head g, split s, request b); 16-token
+// tiles dealt round-robin to the waves.  Per tile and wave:
+//   S^T[16 tok x 16 rows] = K[16 x 128] . Q^T   4x v_mfma_f32_16x16x32_f16
+//   O^T[128 x 16 rows]   += V^T[128 x 16] . P^T 8x v_mfma_f32_16x16x16_f16
+// Computing S transposed puts each lane's four scores (4 tokens, one row)
+// exactly where the PV product wants its B operand, so P never moves
+// between lanes.  Lane l = 16*lg + lm: QK row (token) lm, PV row (d) lm.
+//
+// Scores are exact up to fp32 rounding: each QK product covers ONE
+// quantisation group (32 elements of D), so the group's (scale, zero) is a
+// per-token constant of that product:
+//   q.k = sum_g s_g * (sum_{d in g} q_d n_d  -  z_g * sum_{d in g} q_d).
+// The codes n (0..15) enter the matrix core as fp16 subnormals with the
+// bit pattern n, i.e. the value n * 2^-24 (exact; the product with an fp16
+// Q element is exact in fp32).  Q is scaled by a power of two per row so its
+// largest element lies in [2^14, 2^15) before the (then exact, for bf16)
+// conversion to fp16; the power of two and 2^24 are folded into the score
+// factor.  The per-group terms are combined in fp32 with the group's s and
+// z, which makes any fp16 zero point exact too.
+//   * QK: MFMA kb is group kb.  Lane (lm, lg) supplies token lm's dword lg
+//     of that group (elements 32*kb + 8*lg + 0..7); k-slots 2x, 2x+1 are
+//     elements x and x+4 of the dword, which nibble masks give directly.
+//   * PV: output block b row m is d = 8*m + b: lane (lm, lg) reads, for its
+//     four tokens 4*lg+j, the dword lm of each row (d = 8*lm .. 8*lm+7),
+//     all in group lm/4.  V^T is dequantised to fp16 as n*s - z*s (one fma
+//     per element pair after the exact n; -z*s rounded once per token), and
+//     P is rounded to fp16 (p <= 2^8 by the lazy rescale below): these two
+//     roundings are the only ones in the product.
+//
+// Memory pipeline as in the bf16 kernel: global_load_lds into a 4-stage
+// per-wave LDS ring (K 1 KB, V 1 KB, the two scale/zero tiles 256 B each
+// per 16 tokens), read back by inline asm after an explicit vmcnt wait.
+// The K and V tiles are stored with their 16-byte chunks rotated by
+// (token / 4) so that the dword reads of both operands (K: one group of
+// token lm; V: dword lm of token 4*lg + j) hit distinct banks.
+//
+// Softmax: one running reference m per query row, uniform over the lanes
+// holding that row; raised lazily when a score exceeds m + 8 (log2 units).
+#include <type_traits>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 4;
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kMaxSplitPages = 512;
+constexpr int kD = 128;
+
+constexpr int kStageK = 0;
+constexpr int kStageV = 1024;
+constexpr int kStageKsz = 2048;
+constexpr int kStageVsz = 2304;
+constexpr int kStageBytes = 2560;
+constexpr int kRingBytes = kWaves * kStages * kStageBytes;           // 40 KB
+constexpr int kEpiBytes = (kWaves * 16 * kD + 2 * kWaves * 16) * 4;  // 33 KB
+constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
+constexpr int kSmemBytes = kMainBytes + kMaxSplitPages * 4;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define DA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+__device__ __forceinline__ uint32_t as_u(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// value held by lane ^ 16, ^ 32
+__device__ __forceinline__ float xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+struct StageData {
+  uint32_t k[4];   // token lm, group kb: dword lg (elements 32*kb + 8*lg + 0..7)
+  uint32_t v[4];   // dword lm of tokens 4*lg + j
+  u32x4 ksz[4];    // (scale, zero) of token 4*lg + i, groups 0..3
+  uint32_t vsz[4]; // (scale, zero) of token 4*lg + j, group lm/4
+};
+
+// All reads of one stage plus the next page id, in one asm block (the
+// compiler would otherwise drain the LDS-DMA queue before them).
+__device__ __forceinline__ int32_t read_stage(const uint32_t (&kaddr)[4], uint32_t vaddr,
+                                              uint32_t kszaddr, uint32_t vszaddr,
+                                              uint32_t pidaddr, StageData& s) {
+  int32_t pid;
+  asm volatile(
+      "ds_read_b32 %0, %17\n\t"
+      "ds_read_b32 %1, %18\n\t"
+      "ds_read_b32 %2, %19\n\t"
+      "ds_read_b32 %3, %20\n\t"
+      "ds_read_b32 %4, %21\n\t"
+      "ds_read_b32 %5, %21 offset:64\n\t"
+      "ds_read_b32 %6, %21 offset:128\n\t"
+      "ds_read_b32 %7, %21 offset:192\n\t"
+      "ds_read_b128 %8, %22\n\t"
+      "ds_read_b128 %9, %22 offset:16\n\t"
+      "ds_read_b128 %10, %22 offset:32\n\t"
+      "ds_read_b128 %11, %22 offset:48\n\t"
+      "ds_read_b32 %12, %23\n\t"
+      "ds_read_b32 %13, %23 offset:16\n\t"
+      "ds_read_b32 %14, %23 offset:32\n\t"
+      "ds_read_b32 %15, %23 offset:48\n\t"
+      "ds_read_b32 %16, %24\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(s.k[0]), "=&v"(s.k[1]), "=&v"(s.k[2]), "=&v"(s.k[3]), "=&v"(s.v[0]),
+        "=&v"(s.v[1]), "=&v"(s.v[2]), "=&v"(s.v[3]), "=&v"(s.ksz[0]), "=&v"(s.ksz[1]),
+        "=&v"(s.ksz[2]), "=&v"(s.ksz[3]), "=&v"(s.vsz[0]), "=&v"(s.vsz[1]), "=&v"(s.vsz[2]),
+        "=&v"(s.vsz[3]), "=&v"(pid)
+      : "v"(kaddr[0]), "v"(kaddr[1]), "v"(kaddr[2]), "v"(kaddr[3]), "v"(vaddr), "v"(kszaddr),
+        "v"(vszaddr), "v"(pidaddr)
+      : "memory");
+  return __builtin_amdgcn_readfirstlane(pid);
+}
+
+__device__ __forceinline__ int32_t lds_read_i32(uint32_t addr) {
+  int32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+struct MfmaArgs {
+  const uint16_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint8_t* ksz;
+  const uint8_t* vsz;
+  const int32_t* pt;
+  const int32_t* seqlens;
+  const int32_t* order;
+  float* o;
+  float* lse;
+  int pt_stride, max_pages;
+  int qn, Hq, Hkv, G, R;
+  int page_size, log2_ps, num_pages, S;
+  float scale_log2;
+  int causal;
+};
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  half2_t h = {(_Float16)a, (_Float16)b};
+  return as_u(h);
+}
+// codes x and x + 4 of dword w (nibble x of each 16-bit half) as the fp16
+// subnormals n * 2^-24
+template <int X>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w) {
+  return (w >> (4 * X)) & 0x000F000Fu;
+}
+__device__ __forceinline__ float h_lo(uint32_t w) { return (float)as_h2(w)[0]; }
+__device__ __forceinline__ float h_hi(uint32_t w) { return (float)as_h2(w)[1]; }
+
+__global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const MfmaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
+
+  const int g = blockIdx.x, s = blockIdx.y;
+  int b = a.order ? a.order[blockIdx.z] : (int)blockIdx.z;
+  if ((unsigned)b >= gridDim.z) b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lm = lane & 15, lg = lane >> 4;
+
+  const int ps = a.page_size;
+  const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
+  const int n = (L + ps - 1) >> a.log2_ps;
+  const int cpg = (n + a.S - 1) / a.S;
+  const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
+  const int t0 = p0 * ps, t1 = min(p1 * ps, L);
+  const int ntiles = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
+  const int nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+
+  {
+    const int32_t* ptrow = a.pt + (long long)b * a.pt_stride;
+    for (int j = threadIdx.x; j < p1 - p0; j += kThreads) {
+      const int pid = ptrow[p0 + j];
+      s_pid[j] = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
+    }
+  }
+
+  // ---- Q^T operand (row lm of this kv-head's 16 query rows): for MFMA kb,
+  // elements 32*kb + 8*lg + e, e = 0..7, scaled by 2^sh and held in fp16
+  uint32_t qv[4][4];  // [kb][register]
+  float qsum[4];      // 2^-24 * sum of the row's scaled fp16 Q over group kb
+  float rowfac;       // score (log2 units) = rowfac * sum_g s_g (dot_g - z_g qsum_g)
+  int tlim;           // tokens t < tlim are visible to this lane's row
+  {
+    const int r = lm;
+    const bool live = r < a.R;
+    const int i = live ? r / a.G : 0, h = g * a.G + (live ? r % a.G : 0);
+    const long long qoff = (((long long)b * a.qn + i) * a.Hq + h) * kD + 8 * lg;
+    float qf[4][8];
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + qoff);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint4 x = qp[4 * kb];  // 8 bf16 at element 32*kb + 8*lg
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qf[kb][2 * e] = live ? da::bf16_lo(w[e]) : 0.f;
+        qf[kb][2 * e + 1] = live ? da::bf16_hi(w[e]) : 0.f;
+      }
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qf[kb][e]));
+    mx = fmaxf(mx, xor16(mx));
+    mx = fmaxf(mx, xor32(mx));
+    int ex = 0;
+    if (mx > 0.f) (void)frexpf(mx, &ex);  // mx < 2^ex
+    const int sh = 15 - ex;               // max |q| * 2^sh in [2^14, 2^15)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qf[kb][e] = (float)(_Float16)ldexpf(qf[kb][e], sh);
+        part += qf[kb][e];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) qv[kb][x] = pack_h2(qf[kb][x], qf[kb][x + 4]);
+      part += xor16(part);
+      part += xor32(part);
+      qsum[kb] = ldexpf(part, -24);
+    }
+    rowfac = ldexpf(a.scale_log2, 24 - sh);
+    tlim = live ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
+  }
+  // tiles below every live row's limit need no masks (rows past R have
+  // tlim 0 and are never written, so they do not bound the unmasked region)
+  int tfull;
+  {
+    int lim_live = lm < a.R ? tlim : t1;
+    for (int o = 1; o < 16; o <<= 1) lim_live = min(lim_live, __shfl_xor(lim_live, o, 64));
+    tfull = __builtin_amdgcn_readfirstlane(lim_live);
+  }
+
+  float4_t acc[8];
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) acc[bb] = {0.f, 0.f, 0.f, 0.f};
+  float m = da::kNegInf, l = 0.f;
+  __syncthreads();
+
+  // ---- addressing
+  const long long rowb = (long long)a.Hkv * (kD / 2);  // bytes between token rows (codes)
+  const long long szb = (long long)a.Hkv * 16;         // bytes between token rows (scale/zero)
+  // DMA lane i fills LDS chunk i (token i/4, position i%4) with the token's
+  // 16-byte group (position - token/4) mod 4
+  const uint32_t voff_kv = (uint32_t)((lane >> 2) * rowb + 16 * (((lane & 3) - (lane >> 4)) & 3));
+  const uint32_t voff_sz = (uint32_t)((lane >> 2) * szb + 4 * (lane & 3));
+  DA_LDS uint8_t* ring = (DA_LDS uint8_t*)smem + wave * (kStages * kStageBytes);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  const uint32_t pid_lds = (uint32_t)(uintptr_t)(DA_LDS void*)s_pid;
+  uint32_t rd_k[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) rd_k[kb] = kStageK + 64 * lm + 16 * ((kb + (lm >> 2)) & 3) + 4 * lg;
+  const uint32_t rd_v = kStageV + 64 * (4 * lg) + 16 * (((lm >> 2) + lg) & 3) + 4 * (lm & 3);
+  const uint32_t rd_ksz = kStageKsz + 64 * lg;
+  const uint32_t rd_vsz = kStageVsz + 16 * (4 * lg) + 4 * (lm >> 2);
+
+  auto tile_base = [&](int j) { return t0 + ((wave + kWaves * j) << 4); };
+  auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - p0); };
+  auto issue = [&](int j, int pid) {
+    const int tb = tile_base(j);
+    const long long row0 = ((long long)pid * ps + (tb & (ps - 1))) * a.Hkv + g;
+    DA_LDS uint8_t* st = ring + (j % kStages) * kStageBytes;
+    __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * (kD / 2) + voff_kv),
+                                     (DA_LDS void*)(st + kStageK), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * (kD / 2) + voff_kv),
+                                     (DA_LDS void*)(st + kStageV), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(a.ksz + row0 * 16 + voff_sz),
+                                     (DA_LDS void*)(st + kStageKsz), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(a.vsz + row0 * 16 + voff_sz),
+                                     (DA_LDS void*)(st + kStageVsz), 4, 0, 0);
+  };
+
+  auto compute = [&](int j, const StageData& sd, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    // ---- per-group dot products of the raw codes: dot[kb][i] =
+    // 2^-24 * sum_{d in group kb} q'_d n_d for token 4*lg + i, row lm
+    float4_t dot[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t w = sd.k[kb];
+      const half2_t k0 = as_h2(code_pair<0>(w)), k1 = as_h2(code_pair<1>(w));
+      const half2_t k2 = as_h2(code_pair<2>(w)), k3 = as_h2(code_pair<3>(w));
+      const half8_t ka = {k0[0], k0[1], k1[0], k1[1], k2[0], k2[1], k3[0], k3[1]};
+      const half2_t q0 = as_h2(qv[kb][0]), q1 = as_h2(qv[kb][1]);
+      const half2_t q2 = as_h2(qv[kb][2]), q3 = as_h2(qv[kb][3]);
+      const half8_t qb = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+      dot[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
+    float4_t st;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t sz[4] = {sd.ksz[i][0], sd.ksz[i][1], sd.ksz[i][2], sd.ksz[i][3]};
+      float acc_s = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        acc_s = fmaf(h_lo(sz[kb]), fmaf(-h_hi(sz[kb]), qsum[kb], dot[kb][i]), acc_s);
+      st[i] = acc_s;
+    }
+    // st[i] = score of token 4*lg + i for row lm
+    const int tb = tile_base(j) + 4 * lg;
+    float z[4];
+    bool need = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = fmaf(st[i], rowfac, -m);
+      if (MASKED && !(tb + i < tlim)) z[i] = da::kNegInf;
+      need |= z[i] > kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      float sabs[4], mx = da::kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sabs[i] = (!MASKED || tb + i < tlim) ? st[i] * rowfac : da::kNegInf;
+        mx = fmaxf(mx, sabs[i]);
+      }
+      mx = fmaxf(mx, xor16(mx));
+      mx = fmaxf(mx, xor32(mx));
+      const float mn = fmaxf(m, mx);
+      const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m - mn);
+      l *= al;
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) acc[bb] *= al;
+      m = mn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - mn;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = da::fast_exp2(z[i]);
+      l += p[i];
+    }
+    half4_t pb = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+
+    // ---- V operand: tokens 4*lg + j, d = 8*lm + block
+    // rows past the split end may hold anything (even NaN scales): give them
+    // code 0, scale 0, zero 0, i.e. the value 0
+    uint32_t vw[4], vsz[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const bool ok = !MASKED || tb + jj < t1;
+      vw[jj] = ok ? sd.v[jj] : 0u;
+      vsz[jj] = ok ? sd.vsz[jj] : 0u;
+    }
+    // per token pair: s and -z*s (fp16, one per token)
+    const half2_t s01 = as_h2(__builtin_amdgcn_perm(vsz[1], vsz[0], 0x05040100u));
+    const half2_t s23 = as_h2(__builtin_amdgcn_perm(vsz[3], vsz[2], 0x05040100u));
+    const half2_t nzs01 = -(as_h2(__builtin_amdgcn_perm(vsz[1], vsz[0], 0x07060302u)) * s01);
+    const half2_t nzs23 = -(as_h2(__builtin_amdgcn_perm(vsz[3], vsz[2], 0x07060302u)) * s23);
+    const half2_t k1024 = {1024, 1024};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      // byte kk of each token's dword: [t0.byte, 0, t1.byte, 0]
+      const uint32_t sel = (uint32_t)kk | 0x0C00u | ((uint32_t)(4 + kk) << 16) | 0x0C000000u;
+      const uint32_t x01 = __builtin_amdgcn_perm(vw[1], vw[0], sel);
+      const uint32_t x23 = __builtin_amdgcn_perm(vw[3], vw[2], sel);
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int bb = 2 * kk + hi;
+        const half2_t n01 = as_h2(((x01 >> (4 * hi)) & 0x000F000Fu) | 0x64006400u) - k1024;
+        const half2_t n23 = as_h2(((x23 >> (4 * hi)) & 0x000F000Fu) | 0x64006400u) - k1024;
+        const half2_t a01 = __builtin_elementwise_fma(n01, s01, nzs01);
+        const half2_t a23 = __builtin_elementwise_fma(n23, s23, nzs23);
+        half4_t va = {a01[0], a01[1], a23[0], a23[1]};
+        acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, acc[bb], 0, 0, 0);
+      }
+    }
+  };
+
+  auto step = [&](int j, StageData& sd) {
+    const int ahead = min(kStages - 2, nmine - 1 - j);
+    if (ahead >= 2) wait_vmcnt<8>();
+    else if (ahead == 1) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    const int jn = min(j + kStages - 1, nmine - 1);
+    const uint32_t base = ring_lds + (j % kStages) * kStageBytes;
+    const uint32_t ka[4] = {base + rd_k[0], base + rd_k[1], base + rd_k[2], base + rd_k[3]};
+    const int pid = read_stage(ka, base + rd_v, base + rd_ksz, base + rd_vsz, pid_addr(jn), sd);
+    if (j + kStages - 1 < nmine) issue(j + kStages - 1, pid);
+  };
+  const int lim = tfull - t0 - 16 * wave - 16;
+  const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * kWaves) + 1);
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u)
+    if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
+  for (int j = 0; j < jfull; ++j) {
+    StageData sd;
+    step(j, sd);
+    compute(j, sd, std::false_type{});
+  }
+  for (int j = jfull; j < nmine; ++j) {
+    StageData sd;
+    step(j, sd);
+    compute(j, sd, std::true_type{});
+  }
+
+  // ---- l is partial over the lane groups; acc and m are already per row
+  l += xor16(l);
+  l += xor32(l);
+  __syncthreads();
+  float* sm_acc = reinterpret_cast<float*>(smem);  // [kWaves][16][kD]
+  float* sm_m = sm_acc + kWaves * 16 * kD;         // [kWaves][16]
+  float* sm_l = sm_m + kWaves * 16;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_acc[(wave * 16 + lm) * kD + 8 * (4 * lg + i) + bb] = acc[bb][i];
+  if (lg == 0) {
+    sm_m[wave * 16 + lm] = m;
+    sm_l[wave * 16 + lm] = l;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < a.R * kD; idx += kThreads) {
+    const int r = idx / kD, d = idx - r * kD;
+    float M = da::kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + r]);
+    float lsum = 0.f, o = 0.f;
+    if (M != da::kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = da::fast_exp2(sm_m[w * 16 + r] - M);
+        lsum = fmaf(sm_l[w * 16 + r], f, lsum);
+        o = fmaf(sm_acc[(w * 16 + r) * kD + d], f, o);
+      }
+    }
+    const int i = r / a.G, h = g * a.G + (r % a.G);
+    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.S + s;
+    a.o[orow * kD + d] = lsum > 0.f ? o / lsum : 0.f;
+    if (d == 0) a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum)) * da::kLn2 : da::kNegInf;
+  }
+}
+
+}  // namespace
+
+// INT4 stage 1 on the matrix cores; -1 when the shape is not covered
+// (the caller then uses the vector-ALU kernel).
+int32_t da_split_int4_mfma(const void* q, int q_bf16, const uint8_t* k, const uint8_t* v,
+                           const uint16_t* ksz, const uint16_t* vsz, const int32_t* pt,
+                           int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
+                           const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
+                           int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
+                           float scale, int32_t causal, float* o, float* lse, hipStream_t st) {
+  const int G = Hq / Hkv, R = G * qn;
+  if (!q_bf16 || D != kD || R < 9 || R > 16) return -1;
+  if ((max_pages + S - 1) / S > kMaxSplitPages) return -1;
+  MfmaArgs a;
+  a.q = (const uint16_t*)q; a.k = k; a.v = v;
+  a.ksz = (const uint8_t*)ksz; a.vsz = (const uint8_t*)vsz;
+  a.pt = pt; a.seqlens = seqlens; a.order = order; a.o = o; a.lse = lse;
+  a.pt_stride = pt_stride; a.max_pages = max_pages;
+  a.qn = qn; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.R = R;
+  a.page_size = ps; a.log2_ps = __builtin_ctz((unsigned)ps); a.num_pages = num_pages; a.S = S;
+  a.scale_log2 = scale * da::kLog2e;
+  a.causal = causal ? 1 : 0;
+  hipLaunchKernelGGL(split_int4_mfma_kernel, dim3(Hkv, S, batch), dim3(kThreads), 0, st, a);
+  return da_host::launch_status();
+}

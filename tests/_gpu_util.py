@@ -10,6 +10,14 @@ Gates for floating point, by output type:
 * quantised caches (oracle run on the identically decoded K/V): max-abs <= 1e-2.
 * stage-1 partials (fp32): |dO| <= 2e-5 * (1 + |O|), |d lse| <= 1e-4, and the
   empty splits (lse = -inf) must coincide exactly.
+* stage-1 partials of the INT4 matrix-core path (query groups of 9..16 rows,
+  D = 128, bf16 Q): the P.V product takes P and the dequantised V in fp16
+  (unit roundoff u = 2^-11).  V is formed as fma(n, s, -fp16(z*s)) and P as
+  fp16(p), so each term p*v carries at most u*(2|v| + |z*s|) (+u^2 terms) of
+  absolute error per unit of p, and since O divides by the exact fp32 sum of
+  p, |dO| <= u * (2 max|v| + max|z*s|) over the request's tokens; the gate
+  adds that (x1.01) to the fp32 one.  Scores are computed exactly from the
+  codes, so the LSE gate stays 1e-4.
 """
 from __future__ import annotations
 
@@ -82,10 +90,13 @@ def check_lse(lse: np.ndarray, ref: np.ndarray, label: str, tol=1e-4):
     assert d <= tol, label
 
 
-def check_partials(o, l, o_ref, l_ref, label):
+def check_partials(o, l, o_ref, l_ref, label, o_extra=None):
+    """o_extra: optional extra absolute bound, broadcastable to o [B, q, Hq, S, D]."""
     check_lse(l, l_ref, label + " lse_partial")
     d = np.abs(o - o_ref)
     bound = 2e-5 * (1.0 + np.abs(o_ref))
+    if o_extra is not None:
+        bound = bound + o_extra
     worst = float(np.max(d - bound)) if d.size else -1
     log(f"  {label} o_partial: max|d|={float(np.max(d)) if d.size else 0:.3e}")
     assert worst <= 0, f"{label}: o_partial off by {worst}"
@@ -162,6 +173,39 @@ def oracle_sampled(batch: W.PagedBatch, pairs):
                                        causal=w.causal)
         res[(b, g)] = (out[0], lse[0])
     return res
+
+
+FP16_U = 2.0 ** -11
+
+
+def uses_int4_matrix_path(w: W.Workload) -> bool:
+    """Whether stage 1 over this INT4 workload runs on the matrix cores."""
+    rows = w.group * w.q_per_req
+    return w.kv == W.KV_INT4 and w.head_dim == 128 and 9 <= rows <= 16 and w.dtype != "fp32"
+
+
+def int4_fp16_o_bound(batch: W.PagedBatch):
+    """Per (request, query head) bound u*(2 max|v| + max|z*s|)*1.01 over the
+    request's visible tokens, shaped [B, 1, Hq, 1, 1] (see the module notes)."""
+    w = batch.w
+    v = OQ.dequant_int4(W.host_int(batch.v_pool), W.host_u16(batch.v_scale))
+    sz = OQ.fp16_bits_to_f64(W.host_u16(batch.v_scale))
+    zs = np.abs(sz[..., 0] * sz[..., 1])  # [P, ps, Hkv, D/32]
+    pt = W.host_int(batch.page_table)
+    L = W.host_int(batch.seq_lens)
+    B, G = len(L), w.group
+    out = np.zeros((B, 1, w.num_q_heads, 1, 1))
+    for b in range(B):
+        n = int(L[b])
+        if n == 0:
+            continue
+        t = np.arange(n)
+        pages, slots = pt[b, t // w.page_size], t % w.page_size
+        vm = np.abs(v[pages, slots]).max(axis=(0, 2))   # [Hkv]
+        zm = zs[pages, slots].max(axis=(0, 2))           # [Hkv]
+        for g in range(w.num_kv_heads):
+            out[b, 0, g * G:(g + 1) * G] = FP16_U * (2 * vm[g] + zm[g]) * 1.01
+    return out
 
 
 # ---------------------------------------------------------------- GPU path

@@ -38,6 +38,10 @@ INT4_SMALL = W.INT4_MTP_B64.scaled(name="int4_mtp_small", batch=5, lengths="list
                                    length_list=(1, 4, 65, 777, 2000))
 INT4_Q1 = W.INT4_MTP_B64.scaled(name="int4_q1_small", batch=4, q_per_req=1, causal=False,
                                 lengths="list", length_list=(1, 64, 300, 1500))
+INT4_R12 = W.INT4_MTP_B64.scaled(name="int4_mtp3_r12_small", batch=4, q_per_req=3,
+                                 lengths="list", length_list=(2, 17, 95, 1234))
+INT4_G8Q2 = W.INT4_MTP_B64.scaled(name="int4_g8_mtp2_small", batch=3, num_q_heads=64, q_per_req=2,
+                                  lengths="list", length_list=(1, 48, 700))
 
 
 def _check_out(w, out, ref, label):
@@ -64,7 +68,7 @@ def test_tiny_fp32_every_split(gpu, S):
 
 
 @pytest.mark.parametrize("w", [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, MHA_P32, MTP_BF16,
-                               MTP_BF16_G2Q3, INT8_SMALL, INT4_SMALL, INT4_Q1],
+                               MTP_BF16_G2Q3, INT8_SMALL, INT4_SMALL, INT4_Q1, INT4_R12, INT4_G8Q2],
                          ids=lambda w: w.name)
 @pytest.mark.parametrize("S", [1, 3, 8, 32])
 def test_small_elementwise(gpu, w, S):
@@ -73,9 +77,31 @@ def test_small_elementwise(gpu, w, S):
     o_ref, l_ref = U.oracle_partials(batch, S)
     out_ref, lse_ref = U.oracle_full(batch)
     out, lse, o, l = U.run_decode(gpu, batch, S)
-    U.check_partials(U.to_np(o), U.to_np(l), o_ref, l_ref, f"{w.name} S={S}")
+    extra = U.int4_fp16_o_bound(batch) if U.uses_int4_matrix_path(w) else None
+    U.check_partials(U.to_np(o), U.to_np(l), o_ref, l_ref, f"{w.name} S={S}", o_extra=extra)
     _check_out(w, U.to_np(out), out_ref, f"{w.name} S={S} out")
     U.check_lse(U.to_np(lse), lse_ref, f"{w.name} S={S} lse")
+
+
+@pytest.mark.parametrize("w", [INT4_SMALL, INT4_Q1, INT4_R12], ids=lambda w: w.name)
+def test_int4_fractional_zero_points(gpu, w):
+    """The zero point is any fp16 value, not only a code: shift every zero by a
+    fraction (different per slot) and compare with the oracle decoding the same
+    bits."""
+    log(f"int4 fractional zeros {w.name}")
+    batch = W.make_batch(w, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    for sc in (batch.k_scale, batch.v_scale):
+        frac = torch.rand(sc[..., 1].shape, generator=gen, device="cuda") * 0.9 + 0.05
+        sc[..., 1] = (sc[..., 1].float() + frac).to(torch.float16)
+    S = 3
+    o_ref, l_ref = U.oracle_partials(batch, S)
+    out_ref, lse_ref = U.oracle_full(batch)
+    out, lse, o, l = U.run_decode(gpu, batch, S)
+    extra = U.int4_fp16_o_bound(batch) if U.uses_int4_matrix_path(w) else None
+    U.check_partials(U.to_np(o), U.to_np(l), o_ref, l_ref, f"{w.name} frac-z", o_extra=extra)
+    U.check_quant(U.to_np(out), out_ref, f"{w.name} frac-z out")
+    U.check_lse(U.to_np(lse), lse_ref, f"{w.name} frac-z lse")
 
 
 def test_page_permutation_is_bit_identical(gpu):
