@@ -45,6 +45,53 @@ __device__ __forceinline__ float xor_shfl(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- stage-1 work units
+// Stage 1 runs one workgroup per (kv-head g, split s, dispatch slot z) on a
+// 1-D grid.  Workgroups reach the chip's 8 XCDs round-robin by linear id,
+// and each XCD has its own L2.  Two orders:
+//  * spread: id = g + Hkv * (s + S * z).  With Hkv a multiple of 8 every
+//    XCD gets one kv-head of every unit, the best balance; used where a
+//    kv-head's rows fill whole cache lines (dense caches).
+//  * grouped: units u = z * S + s are dealt to the XCDs in rounds of 8, in
+//    snake order (round r sends unit 8r + j to XCD j for even r and to XCD
+//    7 - j for odd r, keeping a longest-first order balanced), and a unit's
+//    Hkv heads are that XCD's next Hkv workgroups.  Short rows of
+//    neighbouring kv-heads (4-bit and 8-bit codes, their scales) share cache
+//    lines; this way each such line is brought into one L2, once, by
+//    workgroups that run side by side.
+// Dispatch slots keep their order (longest requests first with a batch order).
+constexpr int kXcds = 8;
+
+struct WorkUnit {
+  int g, s, z;
+};
+
+// false for the padding workgroups of the last round of units
+template <bool GROUPED>
+__device__ __forceinline__ bool stage1_unit(int Hkv, int S, int B, WorkUnit& w) {
+  const int i = (int)blockIdx.x;
+  if (!GROUPED) {
+    const int u = i / Hkv;
+    w.g = i - u * Hkv;
+    w.z = u / S;
+    w.s = u - w.z * S;
+    return true;
+  }
+  const int x = i % kXcds, k = i / kXcds;
+  const int r = k / Hkv;
+  const int u = r * kXcds + ((r & 1) ? kXcds - 1 - x : x);
+  w.g = k - r * Hkv;
+  w.z = u / S;
+  w.s = u - w.z * S;
+  return u < S * B;
+}
+
+// request of dispatch slot z: order[z] when given and in range, else z
+__device__ __forceinline__ int stage1_request(const int32_t* order, int z, int B) {
+  const int b = order ? order[z] : z;
+  return (unsigned)b < (unsigned)B ? b : z;
+}
+
 }  // namespace da
 
 // ---------------------------------------------------------------- host side
@@ -56,5 +103,13 @@ inline int32_t launch_status() {
 }
 
 inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// 1-D grid of stage 1 (see da::stage1_unit); the grouped order pads to
+// whole rounds of 8 units
+inline unsigned stage1_grid(int Hkv, int S, int B, bool grouped) {
+  const long long units = (long long)S * B;
+  if (!grouped) return (unsigned)(units * Hkv);
+  return (unsigned)(da::kXcds * (long long)Hkv * ((units + da::kXcds - 1) / da::kXcds));
+}
 
 }  // namespace da_host

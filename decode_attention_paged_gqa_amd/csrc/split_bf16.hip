@@ -142,6 +142,7 @@ struct Bf16Args {
   int pt_stride, max_pages;
   int qn, Hq, Hkv, G, R;
   int page_size, log2_ps, num_pages, S;
+  int B;  // requests
   float scale_log2;
   int causal;
 };
@@ -169,9 +170,10 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
   __shared__ __attribute__((aligned(16))) uint8_t smem[SM::BYTES];
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + SM::MAIN_BYTES);
 
-  const int g = blockIdx.x, s = blockIdx.y;
-  int b = a.order ? a.order[blockIdx.z] : (int)blockIdx.z;
-  if ((unsigned)b >= gridDim.z) b = blockIdx.z;
+  da::WorkUnit wu;
+  if (!da::stage1_unit<false>(a.Hkv, a.S, a.B, wu)) return;
+  const int g = wu.g, s = wu.s;
+  const int b = da::stage1_request(a.order, wu.z, a.B);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tq = lane >> 3, c = lane & 7;
@@ -421,7 +423,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
 
 template <int D, int RT>
 int32_t launch(const Bf16Args& a, int batch, hipStream_t st) {
-  hipLaunchKernelGGL((split_bf16_kernel<D, RT, 4>), dim3(a.Hkv, a.S, batch), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((split_bf16_kernel<D, RT, 4>), dim3(da_host::stage1_grid(a.Hkv, a.S, batch, false)),
+                     dim3(kThreads), 0, st, a);
   return da_host::launch_status();
 }
 
@@ -444,6 +447,7 @@ int32_t da_split_bf16_fast(const void* q, const void* k, const void* v, const in
   a.pt_stride = pt_stride; a.max_pages = max_pages;
   a.qn = qn; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.R = R;
   a.page_size = ps; a.log2_ps = __builtin_ctz((unsigned)ps); a.num_pages = num_pages; a.S = S;
+  a.B = batch;
   a.scale_log2 = scale * da::kLog2e;
   a.causal = causal ? 1 : 0;
   if (D == 128) {

@@ -46,6 +46,7 @@ struct SplitArgs {
   int pt_stride, max_pages;
   int qn, Hq, Hkv, G, R;
   int page_size, log2_ps, num_pages, S;
+  int B;  // requests
   float scale_log2;
   int causal;
 };
@@ -141,9 +142,10 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
   __shared__ float sm_l[kWaves][RT];
   __shared__ float sm_acc[kWaves][RT][D];
 
-  const int g = blockIdx.x, s = blockIdx.y;
-  int b = a.order ? a.order[blockIdx.z] : (int)blockIdx.z;
-  if ((unsigned)b >= gridDim.z) b = blockIdx.z;
+  da::WorkUnit wu;
+  if (!da::stage1_unit<(KV == KV_I8 || KV == KV_I4)>(a.Hkv, a.S, a.B, wu)) return;
+  const int g = wu.g, s = wu.s;
+  const int b = da::stage1_request(a.order, wu.z, a.B);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane >> 4, c = lane & 15;
 
@@ -346,8 +348,12 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
 }
 
 template <int KV, int D, int RT>
-int32_t launch_rt(const SplitArgs& a, int batch, hipStream_t st) {
-  hipLaunchKernelGGL((split_fma_kernel<KV, D, RT>), dim3(a.Hkv, a.S, batch), dim3(kThreads), 0,
+int32_t launch_rt(const SplitArgs& args, int batch, hipStream_t st) {
+  SplitArgs a = args;
+  a.B = batch;
+  constexpr bool kGrouped = KV == KV_I8 || KV == KV_I4;  // short rows share cache lines
+  hipLaunchKernelGGL((split_fma_kernel<KV, D, RT>),
+                     dim3(da_host::stage1_grid(a.Hkv, a.S, batch, kGrouped)), dim3(kThreads), 0,
                      st, a);
   return da_host::launch_status();
 }
@@ -395,6 +401,7 @@ SplitArgs make_args(const void* q, int q_bf16, const void* k, const void* v, con
   a.pt_stride = pt_stride; a.max_pages = max_pages;
   a.qn = qn; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.R = a.G * qn;
   a.page_size = ps; a.log2_ps = __builtin_ctz((unsigned)ps); a.num_pages = num_pages; a.S = S;
+  a.B = 0;  // set at launch
   a.scale_log2 = scale * da::kLog2e;
   a.causal = causal ? 1 : 0;
   return a;

@@ -154,6 +154,7 @@ struct MfmaArgs {
   int pt_stride, max_pages;
   int qn, Hq, Hkv, G, R;
   int page_size, log2_ps, num_pages, S;
+  int B;  // requests
   float scale_log2;
   int causal;
 };
@@ -175,9 +176,10 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
 
-  const int g = blockIdx.x, s = blockIdx.y;
-  int b = a.order ? a.order[blockIdx.z] : (int)blockIdx.z;
-  if ((unsigned)b >= gridDim.z) b = blockIdx.z;
+  da::WorkUnit wu;
+  if (!da::stage1_unit<true>(a.Hkv, a.S, a.B, wu)) return;
+  const int g = wu.g, s = wu.s;
+  const int b = da::stage1_request(a.order, wu.z, a.B);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lm = lane & 15, lg = lane >> 4;
@@ -480,6 +482,8 @@ int32_t da_split_int4_mfma(const void* q, int q_bf16, const uint8_t* k, const ui
   a.page_size = ps; a.log2_ps = __builtin_ctz((unsigned)ps); a.num_pages = num_pages; a.S = S;
   a.scale_log2 = scale * da::kLog2e;
   a.causal = causal ? 1 : 0;
-  hipLaunchKernelGGL(split_int4_mfma_kernel, dim3(Hkv, S, batch), dim3(kThreads), 0, st, a);
+  a.B = batch;
+  hipLaunchKernelGGL(split_int4_mfma_kernel, dim3(da_host::stage1_grid(Hkv, S, batch, true)), dim3(kThreads),
+                     0, st, a);
   return da_host::launch_status();
 }
