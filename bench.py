@@ -84,7 +84,7 @@ def algorithmic_bytes(w, lengths, out_elem=2):
 KERNEL_SOURCES = {"bf16": ["split_bf16.hip", "common.h"],
                   "fp32": ["split_fma.hip", "common.h"],
                   "int8": ["split_int8.hip", "split_fma.hip", "common.h"],
-                  "int4": ["split_mfma.hip", "split_fma.hip", "common.h"]}
+                  "int4": ["split_int4.hip", "split_fma.hip", "common.h"]}
 
 
 def kernel_hash(kv="bf16") -> str:

@@ -447,10 +447,19 @@ extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k
   return launch_kv<KV_F32>(a, head_dim, batch, s);
 }
 
-// INT4 stage 1 on the matrix cores for 9..16 rows (split_mfma.hip); -1 when
+// INT4 stage 1 on the matrix cores for 9..16 rows (split_int4.hip); -1 when
 // the shape is not covered.
 int32_t da_split_int4_mfma(const void* q, int q_bf16, const uint8_t* k, const uint8_t* v,
                            const uint16_t* ksz, const uint16_t* vsz, const int32_t* pt,
+                           int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
+                           const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
+                           int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
+                           float scale, int32_t causal, float* o, float* lse, hipStream_t st);
+
+// INT8 stage 1 on the matrix cores for D = 128 and bf16 Q (split_int8.hip);
+// -1 when the shape is not covered.
+int32_t da_split_int8_mfma(const void* q, int q_bf16, const int8_t* k, const int8_t* v,
+                           const uint16_t* ks, const uint16_t* vs, const int32_t* pt,
                            int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
                            const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
                            int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
@@ -473,6 +482,12 @@ extern "C" int32_t decode_attn_split_int8(
                                 page_table, page_table_stride, max_pages, cache_seqlens,
                                 batch_order, q_per_req, num_q_heads, num_kv_heads, page_size, num_pages,
                                 num_splits, softmax_scale, causal, o_partial, lse_partial);
+  const int32_t mf = da_split_int8_mfma(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale, v_scale,
+                                        page_table, page_table_stride, max_pages, cache_seqlens,
+                                        batch_order, batch, q_per_req, num_q_heads, num_kv_heads,
+                                        head_dim, page_size, num_pages, num_splits, softmax_scale,
+                                        causal, o_partial, lse_partial, (hipStream_t)stream);
+  if (mf >= 0) return mf;
   return launch_kv<KV_I8>(a, head_dim, batch, (hipStream_t)stream);
 }
 

@@ -30,8 +30,10 @@
 //     four tokens 4*lg+j, the dword lm of each row (d = 8*lm .. 8*lm+7),
 //     all in group lm/4.  V^T is dequantised to fp16 as n*s - z*s (one fma
 //     per element pair after the exact n; -z*s rounded once per token), and
-//     P is rounded to fp16 (p <= 2^8 by the lazy rescale below): these two
-//     roundings are the only ones in the product.
+//     P enters as fp16(p * 2^7) (p <= 2^8 under the lazy rescale below, so
+//     p * 2^7 < 2^15; the factor keeps small weights out of fp16's subnormal
+//     range and cancels against the same factor in l): these two roundings
+//     are the only ones in the product.
 //
 // Memory pipeline as in the bf16 kernel: global_load_lds into a 4-stage
 // per-wave LDS ring (K 1 KB, V 1 KB, the two scale/zero tiles 256 B each
@@ -44,14 +46,17 @@
 // holding that row; raised lazily when a score exceeds m + 8 (log2 units).
 #include <type_traits>
 
-#include "common.h"
+#include "mfma_util.h"
 
 namespace {
+
+using namespace da_mfma;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStages = 4;
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kPScale = 7.0f;  // P (and l) carry a factor 2^7
 constexpr int kMaxSplitPages = 512;
 constexpr int kD = 128;
 
@@ -64,33 +69,6 @@ constexpr int kRingBytes = kWaves * kStages * kStageBytes;           // 40 KB
 constexpr int kEpiBytes = (kWaves * 16 * kD + 2 * kWaves * 16) * 4;  // 33 KB
 constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
 constexpr int kSmemBytes = kMainBytes + kMaxSplitPages * 4;
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-#define DA_LDS __attribute__((address_space(3)))
-
-__device__ __forceinline__ half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
-__device__ __forceinline__ uint32_t as_u(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
-
-// value held by lane ^ 16, ^ 32
-__device__ __forceinline__ float xor16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
-                                            __builtin_bit_cast(uint32_t, x), false, false);
-  return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float xor32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                            __builtin_bit_cast(uint32_t, x), false, false);
-  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 struct StageData {
   uint32_t k[4];   // token lm, group kb: dword lg (elements 32*kb + 8*lg + 0..7)
@@ -134,12 +112,6 @@ __device__ __forceinline__ int32_t read_stage(const uint32_t (&kaddr)[4], uint32
   return __builtin_amdgcn_readfirstlane(pid);
 }
 
-__device__ __forceinline__ int32_t lds_read_i32(uint32_t addr) {
-  int32_t v;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-  return __builtin_amdgcn_readfirstlane(v);
-}
-
 struct MfmaArgs {
   const uint16_t* q;
   const uint8_t* k;
@@ -159,19 +131,12 @@ struct MfmaArgs {
   int causal;
 };
 
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  half2_t h = {(_Float16)a, (_Float16)b};
-  return as_u(h);
-}
 // codes x and x + 4 of dword w (nibble x of each 16-bit half) as the fp16
 // subnormals n * 2^-24
 template <int X>
 __device__ __forceinline__ uint32_t code_pair(uint32_t w) {
   return (w >> (4 * X)) & 0x000F000Fu;
 }
-__device__ __forceinline__ float h_lo(uint32_t w) { return (float)as_h2(w)[0]; }
-__device__ __forceinline__ float h_hi(uint32_t w) { return (float)as_h2(w)[1]; }
-
 __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
@@ -231,9 +196,7 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qf[kb][e]));
     mx = fmaxf(mx, xor16(mx));
     mx = fmaxf(mx, xor32(mx));
-    int ex = 0;
-    if (mx > 0.f) (void)frexpf(mx, &ex);  // mx < 2^ex
-    const int sh = 15 - ex;               // max |q| * 2^sh in [2^14, 2^15)
+    const int sh = q_row_shift(mx);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       float part = 0.f;
@@ -331,9 +294,9 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
     bool need = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = fmaf(st[i], rowfac, -m);
+      z[i] = fmaf(st[i], rowfac, kPScale - m);
       if (MASKED && !(tb + i < tlim)) z[i] = da::kNegInf;
-      need |= z[i] > kRescaleSlack;
+      need |= z[i] > kRescaleSlack + kPScale;
     }
     if (__builtin_amdgcn_ballot_w64(need)) {
       float sabs[4], mx = da::kNegInf;
@@ -351,7 +314,8 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
       for (int bb = 0; bb < 8; ++bb) acc[bb] *= al;
       m = mn;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - mn;
+      for (int i = 0; i < 4; ++i)
+        z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - (mn - kPScale);
     }
     float p[4];
 #pragma unroll
@@ -456,7 +420,8 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
     const int i = r / a.G, h = g * a.G + (r % a.G);
     const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.S + s;
     a.o[orow * kD + d] = lsum > 0.f ? o / lsum : 0.f;
-    if (d == 0) a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum)) * da::kLn2 : da::kNegInf;
+    if (d == 0)
+      a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum) - kPScale) * da::kLn2 : da::kNegInf;
   }
 }
 

@@ -1,0 +1,457 @@
+// Stage 1 over an INT8 cache on the matrix cores (LightLLM PR #1549,
+// "Covered decode kernels": INT8 KV flash decode stage 1), for D = 128, bf16
+// Q and up to 16 query rows per kv-head (G * q).  Same contract as
+// decode_attn_split_int8: K = k_pool * k_scale, V = v_pool * v_scale, one
+// fp16 scale per (page, slot, kv-head).
+//
+// One workgroup (4 waves) per (kv-head g, split s, request b); 16-token tiles
+// dealt round-robin to the waves.  Per tile and wave:
+//   S^T[16 tok x 16 rows] = K[16 x 128] . Q^T     4x v_mfma_f32_16x16x32_f16
+//   O^T[128 x 16 rows]   += V^T[128 x 16] . P^T   8x v_mfma_f32_16x16x16_f16
+// Computing S transposed leaves each lane's four scores (4 tokens, one row)
+// where the PV product wants its B operand.  Lane l = 16*lg + lm.
+//
+// Scores are exact up to fp32 rounding.  A code b (-128..127) enters the QK
+// product as the fp16 subnormal whose bit pattern is b + 128, i.e. the value
+// (b + 128) * 2^-24: an xor with 0x80 per byte and one byte permute per
+// element pair form it.  Q is scaled per row by a power of two (largest
+// element in [2^14, 2^15)) and held in fp16, exact for bf16 values, so the
+// products are exact in fp32.  The offset is taken out with the row's fp32
+// sum of scaled Q, and the token's scale multiplies the result:
+//   q.k = s * 2^-sh * 2^24 * (dot - 2^-24 * 128 * sum_d q'_d).
+// The PV product takes V = fp16(b * s) (b is exact in fp16, one rounding)
+// and P = fp16(p * 2^7) (one rounding; p <= 2^8 under the lazy rescale, so
+// p * 2^7 < 2^15, and the factor keeps small weights out of fp16's
+// subnormal range; it cancels against the same factor in l).
+//   * QK: MFMA kb, lane (lm, lg): token lm, elements 32*lg + 8*kb + 0..7;
+//     the lane reads its 32 contiguous bytes of the row.
+//   * PV: output block bb row m is d = 8*m + bb: lane (lm, lg) reads bytes
+//     8*lm .. 8*lm+7 of each of its four tokens 4*lg + j.
+//
+// Memory pipeline: global_load_lds into a 4-stage per-wave LDS ring (K 2 KB,
+// V 2 KB, scales 256 B per 16 tokens), read back by inline asm after an
+// explicit vmcnt wait.  K and V rows are stored with their eight 16-byte
+// chunks rotated by ((token / 2) mod 8) so that the reads of both operands
+// spread over the LDS banks.  A token's fp16 scale comes in the aligned dword
+// that holds it (in bounds: a scale array holds num_pages * page_size * Hkv
+// entries, an even count) and the parity of its index picks the half.
+//
+// Softmax: one running reference m per query row, uniform over the lanes
+// holding that row; raised lazily when a score exceeds m + 8 (log2 units).
+#include <type_traits>
+
+#include "mfma_util.h"
+
+namespace {
+
+using namespace da_mfma;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 4;
+constexpr float kRescaleSlack = 8.0f;
+constexpr float kPScale = 7.0f;  // P (and l) carry a factor 2^7
+constexpr int kMaxSplitPages = 512;
+constexpr int kD = 128;
+
+constexpr int kStageK = 0;
+constexpr int kStageV = 2048;
+constexpr int kStageSc = 4096;  // dwords: [0, 16) K scales, [16, 32) V scales, rest unused
+constexpr int kStageBytes = 4352;
+constexpr int kRingBytes = kWaves * kStages * kStageBytes;           // 68 KB
+constexpr int kEpiBytes = (kWaves * 16 * kD + 2 * kWaves * 16) * 4;  // 33 KB
+constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
+constexpr int kSmemBytes = kMainBytes + kMaxSplitPages * 4;
+
+// LDS position of 16-byte chunk c of token t's row
+__host__ __device__ constexpr int chunk_pos(int t, int c) { return (c + (t >> 1)) & 7; }
+
+struct StageData {
+  u32x4 k[2];    // token lm: bytes 32*lg .. 32*lg+31
+  u32x2 v[4];    // token 4*lg + j: bytes 8*lm .. 8*lm+7
+  u32x4 ks;      // dwords holding the K scales of tokens 4*lg + i
+  u32x4 vs;      // dwords holding the V scales of tokens 4*lg + j
+};
+
+// All reads of one stage plus the next page id, in one asm block (the
+// compiler would otherwise drain the LDS-DMA queue before them).
+__device__ __forceinline__ int32_t read_stage(uint32_t k0, uint32_t k1, uint32_t v0, uint32_t v2,
+                                              uint32_t sc, uint32_t pidaddr, StageData& s) {
+  int32_t pid;
+  asm volatile(
+      "ds_read_b128 %0, %9\n\t"
+      "ds_read_b128 %1, %10\n\t"
+      "ds_read_b64 %2, %11\n\t"
+      "ds_read_b64 %3, %11 offset:128\n\t"
+      "ds_read_b64 %4, %12\n\t"
+      "ds_read_b64 %5, %12 offset:128\n\t"
+      "ds_read_b128 %6, %13\n\t"
+      "ds_read_b128 %7, %13 offset:64\n\t"
+      "ds_read_b32 %8, %14\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(s.k[0]), "=&v"(s.k[1]), "=&v"(s.v[0]), "=&v"(s.v[1]), "=&v"(s.v[2]),
+        "=&v"(s.v[3]), "=&v"(s.ks), "=&v"(s.vs), "=&v"(pid)
+      : "v"(k0), "v"(k1), "v"(v0), "v"(v2), "v"(sc), "v"(pidaddr)
+      : "memory");
+  return __builtin_amdgcn_readfirstlane(pid);
+}
+
+struct Int8Args {
+  const uint16_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint8_t* ks;
+  const uint8_t* vs;
+  const int32_t* pt;
+  const int32_t* seqlens;
+  const int32_t* order;
+  float* o;
+  float* lse;
+  int pt_stride, max_pages;
+  int qn, Hq, Hkv, G, R;
+  int page_size, log2_ps, num_pages, S;
+  int B;
+  float scale_log2;
+  int causal;
+};
+
+// bytes of a pair of tokens' codes (byte kk of each dword) as fp16 subnormal
+// pair [b0 + 128, b1 + 128] * 2^-24, from dwords already offset by 0x80
+__device__ __forceinline__ uint32_t code_pair_lo(uint32_t w) {
+  return __builtin_amdgcn_perm(w, w, 0x0C010C00u);
+}
+__device__ __forceinline__ uint32_t code_pair_hi(uint32_t w) {
+  return __builtin_amdgcn_perm(w, w, 0x0C030C02u);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
+
+  da::WorkUnit wu;
+  if (!da::stage1_unit<true>(a.Hkv, a.S, a.B, wu)) return;
+  const int g = wu.g, s = wu.s;
+  const int b = da::stage1_request(a.order, wu.z, a.B);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lm = lane & 15, lg = lane >> 4;
+
+  const int ps = a.page_size;
+  const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
+  const int n = (L + ps - 1) >> a.log2_ps;
+  const int cpg = (n + a.S - 1) / a.S;
+  const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
+  const int t0 = p0 * ps, t1 = min(p1 * ps, L);
+  const int ntiles = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
+  const int nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+
+  {
+    const int32_t* ptrow = a.pt + (long long)b * a.pt_stride;
+    for (int j = threadIdx.x; j < p1 - p0; j += kThreads) {
+      const int pid = ptrow[p0 + j];
+      s_pid[j] = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
+    }
+  }
+
+  // ---- Q^T operand: row lm, elements 32*lg + 8*kb + e, scaled by 2^sh, fp16
+  uint32_t qv[4][4];  // [kb][pair]
+  float rowfac;       // score (log2 units) = s * (rowfac * dot - qoff)
+  float qoff;         // rowfac * 128 * 2^-24 * sum of the row's scaled Q
+  int tlim;           // tokens t < tlim are visible to this lane's row
+  {
+    const int r = lm;
+    const bool live = r < a.R;
+    const int i = live ? r / a.G : 0, h = g * a.G + (live ? r % a.G : 0);
+    const long long qoff_el = (((long long)b * a.qn + i) * a.Hq + h) * kD + 32 * lg;
+    float qf[4][8];
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + qoff_el);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint4 x = qp[kb];
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qf[kb][2 * e] = live ? da::bf16_lo(w[e]) : 0.f;
+        qf[kb][2 * e + 1] = live ? da::bf16_hi(w[e]) : 0.f;
+      }
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qf[kb][e]));
+    mx = fmaxf(mx, xor16(mx));
+    mx = fmaxf(mx, xor32(mx));
+    const int sh = q_row_shift(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qf[kb][e] = (float)(_Float16)ldexpf(qf[kb][e], sh);
+        sum += qf[kb][e];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) qv[kb][x] = pack_h2(qf[kb][2 * x], qf[kb][2 * x + 1]);
+    }
+    sum += xor16(sum);
+    sum += xor32(sum);
+    rowfac = ldexpf(a.scale_log2, 24 - sh);
+    qoff = rowfac * ldexpf(sum, -17);  // 128 * 2^-24 = 2^-17
+    tlim = live ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    asm volatile("" : "+v"(qv[kb][0]), "+v"(qv[kb][1]), "+v"(qv[kb][2]), "+v"(qv[kb][3]));
+  // tiles below every live row's limit need no masks (rows past R have
+  // tlim 0 and are never written, so they do not bound the unmasked region)
+  int tfull;
+  {
+    int lim_live = lm < a.R ? tlim : t1;
+    for (int o = 1; o < 16; o <<= 1) lim_live = min(lim_live, __shfl_xor(lim_live, o, 64));
+    tfull = __builtin_amdgcn_readfirstlane(lim_live);
+  }
+
+  float4_t acc[8];
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) acc[bb] = {0.f, 0.f, 0.f, 0.f};
+  float m = da::kNegInf, l = 0.f;
+  __syncthreads();
+
+  // ---- addressing
+  const long long rowb = (long long)a.Hkv * kD;  // bytes between token rows (codes)
+  // DMA lane i of half h fills LDS chunk i of that half: token 8h + i/8,
+  // position i%8, holding the row's chunk (position - token/2) mod 8
+  uint32_t voff_kv[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = 8 * h + (lane >> 3), p = lane & 7;
+    voff_kv[h] = (uint32_t)(t * rowb + 16 * ((p - (t >> 1)) & 7));
+  }
+  // scale DMA: lanes 0..15 K scale of token i, 16..31 V scale of token i-16,
+  // 32..63 repeat lanes 0..31 (their LDS words are not read)
+  const int sc_tok = lane & 15;
+  const uint8_t* sc_base = ((lane >> 4) & 1) ? a.vs : a.ks;
+  DA_LDS uint8_t* ring = (DA_LDS uint8_t*)smem + wave * (kStages * kStageBytes);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  const uint32_t pid_lds = (uint32_t)(uintptr_t)(DA_LDS void*)s_pid;
+  const uint32_t rd_k0 = kStageK + 128 * lm + 16 * chunk_pos(lm, 2 * lg);
+  const uint32_t rd_k1 = kStageK + 128 * lm + 16 * chunk_pos(lm, 2 * lg + 1);
+  const uint32_t rd_v0 = kStageV + 128 * (4 * lg) + 16 * chunk_pos(4 * lg, lm >> 1) + 8 * (lm & 1);
+  const uint32_t rd_v2 =
+      kStageV + 128 * (4 * lg + 2) + 16 * chunk_pos(4 * lg + 2, lm >> 1) + 8 * (lm & 1);
+  const uint32_t rd_sc = kStageSc + 16 * lg;
+
+  auto tile_base = [&](int j) { return t0 + ((wave + kWaves * j) << 4); };
+  auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - p0); };
+  auto issue = [&](int j, int pid) {
+    const long long row = (long long)pid * ps + (tile_base(j) & (ps - 1));  // tile's first slot
+    const long long row0 = row * a.Hkv + g;
+    DA_LDS uint8_t* st = ring + (j % kStages) * kStageBytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * kD + voff_kv[h]),
+                                       (DA_LDS void*)(st + kStageK + 1024 * h), 16, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * kD + voff_kv[h]),
+                                       (DA_LDS void*)(st + kStageV + 1024 * h), 16, 0, 0);
+    const long long e = (row + sc_tok) * a.Hkv + g;  // scale index
+    __builtin_amdgcn_global_load_lds((const void*)(sc_base + ((2 * e) & ~3ll)),
+                                     (DA_LDS void*)(st + kStageSc), 4, 0, 0);
+  };
+
+  // Half of the scale dword holding token 4*lg + i's scale.  Its index is
+  // (row + 4*lg + i) * Hkv + g with row = pid * page_size + a multiple of
+  // 16, an even number, so the parity is that of g + i * Hkv.
+  int sc_shift[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sc_shift[i] = ((g + i * a.Hkv) & 1) << 4;
+
+  auto compute = [&](int j, const StageData& sd, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    // ---- dot[i] = 2^-24 * sum_d q'_d (b_d + 128) for token 4*lg + i, row lm
+    float4_t dot = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint32_t kw[8] = {sd.k[0][0] ^ 0x80808080u, sd.k[0][1] ^ 0x80808080u,
+                              sd.k[0][2] ^ 0x80808080u, sd.k[0][3] ^ 0x80808080u,
+                              sd.k[1][0] ^ 0x80808080u, sd.k[1][1] ^ 0x80808080u,
+                              sd.k[1][2] ^ 0x80808080u, sd.k[1][3] ^ 0x80808080u};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const half2_t c0 = as_h2(code_pair_lo(kw[2 * kb])), c1 = as_h2(code_pair_hi(kw[2 * kb]));
+        const half2_t c2 = as_h2(code_pair_lo(kw[2 * kb + 1]));
+        const half2_t c3 = as_h2(code_pair_hi(kw[2 * kb + 1]));
+        const half8_t ka = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+        const half2_t q0 = as_h2(qv[kb][0]), q1 = as_h2(qv[kb][1]);
+        const half2_t q2 = as_h2(qv[kb][2]), q3 = as_h2(qv[kb][3]);
+        const half8_t qb = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+        dot = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, dot, 0, 0, 0);
+      }
+    }
+    const int tb = tile_base(j) + 4 * lg;
+    uint32_t ksc[4], vsc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ksc[i] = sd.ks[i] >> sc_shift[i];
+      vsc[i] = sd.vs[i] >> sc_shift[i];
+    }
+    float z[4], tq[4];
+    bool need = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tq[i] = fmaf(dot[i], rowfac, -qoff);
+      z[i] = fmaf(h_lo(ksc[i]), tq[i], kPScale - m);
+      if (MASKED && !(tb + i < tlim)) z[i] = da::kNegInf;
+      need |= z[i] > kRescaleSlack + kPScale;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      float sabs[4], mx = da::kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sabs[i] = (!MASKED || tb + i < tlim) ? h_lo(ksc[i]) * tq[i] : da::kNegInf;
+        mx = fmaxf(mx, sabs[i]);
+      }
+      mx = fmaxf(mx, xor16(mx));
+      mx = fmaxf(mx, xor32(mx));
+      const float mn = fmaxf(m, mx);
+      const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m - mn);
+      l *= al;
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) acc[bb] *= al;
+      m = mn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - (mn - kPScale);
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = da::fast_exp2(z[i]);
+      l += p[i];
+    }
+    const half4_t pb = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+
+    // ---- V operand: tokens 4*lg + j, d = 8*lm + block.  Rows past the
+    // split end may hold anything (even NaN scales): code 0, scale 0 there.
+    uint32_t vw[4][2], vs[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const bool ok = !MASKED || tb + jj < t1;
+      vw[jj][0] = ok ? sd.v[jj][0] : 0u;
+      vw[jj][1] = ok ? sd.v[jj][1] : 0u;
+      vs[jj] = ok ? vsc[jj] : 0u;
+    }
+    const half2_t s01 = as_h2(__builtin_amdgcn_perm(vs[1], vs[0], 0x05040100u));
+    const half2_t s23 = as_h2(__builtin_amdgcn_perm(vs[3], vs[2], 0x05040100u));
+    const half2_t k1152 = {1152, 1152};
+#pragma unroll
+    for (int hw = 0; hw < 2; ++hw) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int bb = 4 * hw + kk;
+        // [t0.byte kk, 0, t1.byte kk, 0], then bytes ^ 0x80 and 0x64 above
+        // them: fp16 1024 + (b + 128), exact
+        const uint32_t sel = (uint32_t)kk | 0x0C00u | ((uint32_t)(4 + kk) << 16) | 0x0C000000u;
+        const uint32_t x01 = __builtin_amdgcn_perm(vw[1][hw], vw[0][hw], sel) ^ 0x64806480u;
+        const uint32_t x23 = __builtin_amdgcn_perm(vw[3][hw], vw[2][hw], sel) ^ 0x64806480u;
+        const half2_t a01 = (as_h2(x01) - k1152) * s01;
+        const half2_t a23 = (as_h2(x23) - k1152) * s23;
+        const half4_t va = {a01[0], a01[1], a23[0], a23[1]};
+        acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, acc[bb], 0, 0, 0);
+      }
+    }
+  };
+
+  auto step = [&](int j, StageData& sd) {
+    const int ahead = min(kStages - 2, nmine - 1 - j);
+    if (ahead >= 2) wait_vmcnt<10>();
+    else if (ahead == 1) wait_vmcnt<5>();
+    else wait_vmcnt<0>();
+    const int jn = min(j + kStages - 1, nmine - 1);
+    const uint32_t base = ring_lds + (j % kStages) * kStageBytes;
+    const int pid = read_stage(base + rd_k0, base + rd_k1, base + rd_v0, base + rd_v2,
+                               base + rd_sc, pid_addr(jn), sd);
+    if (j + kStages - 1 < nmine) issue(j + kStages - 1, pid);
+  };
+  const int lim = tfull - t0 - 16 * wave - 16;
+  const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * kWaves) + 1);
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u)
+    if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
+  for (int j = 0; j < jfull; ++j) {
+    StageData sd;
+    step(j, sd);
+    compute(j, sd, std::false_type{});
+  }
+  for (int j = jfull; j < nmine; ++j) {
+    StageData sd;
+    step(j, sd);
+    compute(j, sd, std::true_type{});
+  }
+
+  // ---- l is partial over the lane groups; acc and m are already per row
+  l += xor16(l);
+  l += xor32(l);
+  __syncthreads();
+  float* sm_acc = reinterpret_cast<float*>(smem);  // [kWaves][16][kD]
+  float* sm_m = sm_acc + kWaves * 16 * kD;         // [kWaves][16]
+  float* sm_l = sm_m + kWaves * 16;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_acc[(wave * 16 + lm) * kD + 8 * (4 * lg + i) + bb] = acc[bb][i];
+  if (lg == 0) {
+    sm_m[wave * 16 + lm] = m;
+    sm_l[wave * 16 + lm] = l;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < a.R * kD; idx += kThreads) {
+    const int r = idx / kD, d = idx - r * kD;
+    float M = da::kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + r]);
+    float lsum = 0.f, o = 0.f;
+    if (M != da::kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = da::fast_exp2(sm_m[w * 16 + r] - M);
+        lsum = fmaf(sm_l[w * 16 + r], f, lsum);
+        o = fmaf(sm_acc[(w * 16 + r) * kD + d], f, o);
+      }
+    }
+    const int i = r / a.G, h = g * a.G + (r % a.G);
+    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.S + s;
+    a.o[orow * kD + d] = lsum > 0.f ? o / lsum : 0.f;
+    if (d == 0)
+      a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum) - kPScale) * da::kLn2 : da::kNegInf;
+  }
+}
+
+}  // namespace
+
+// INT8 stage 1 on the matrix cores; -1 when the shape is not covered (the
+// caller then uses the vector-ALU kernel).
+int32_t da_split_int8_mfma(const void* q, int q_bf16, const int8_t* k, const int8_t* v,
+                           const uint16_t* ks, const uint16_t* vs, const int32_t* pt,
+                           int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
+                           const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
+                           int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
+                           float scale, int32_t causal, float* o, float* lse, hipStream_t st) {
+  const int G = Hq / Hkv, R = G * qn;
+  if (!q_bf16 || D != kD || R > 16) return -1;
+  if ((max_pages + S - 1) / S > kMaxSplitPages) return -1;
+  Int8Args a;
+  a.q = (const uint16_t*)q; a.k = (const uint8_t*)k; a.v = (const uint8_t*)v;
+  a.ks = (const uint8_t*)ks; a.vs = (const uint8_t*)vs;
+  a.pt = pt; a.seqlens = seqlens; a.order = order; a.o = o; a.lse = lse;
+  a.pt_stride = pt_stride; a.max_pages = max_pages;
+  a.qn = qn; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.R = R;
+  a.page_size = ps; a.log2_ps = __builtin_ctz((unsigned)ps); a.num_pages = num_pages; a.S = S;
+  a.B = batch;
+  a.scale_log2 = scale * da::kLog2e;
+  a.causal = causal ? 1 : 0;
+  hipLaunchKernelGGL(split_int8_mfma_kernel, dim3(da_host::stage1_grid(Hkv, S, batch, true)),
+                     dim3(kThreads), 0, st, a);
+  return da_host::launch_status();
+}

@@ -10,13 +10,16 @@ Gates for floating point, by output type:
 * quantised caches (oracle run on the identically decoded K/V): max-abs <= 1e-2.
 * stage-1 partials (fp32): |dO| <= 2e-5 * (1 + |O|), |d lse| <= 1e-4, and the
   empty splits (lse = -inf) must coincide exactly.
-* stage-1 partials of the INT4 matrix-core path (query groups of 9..16 rows,
-  D = 128, bf16 Q): the P.V product takes P and the dequantised V in fp16
-  (unit roundoff u = 2^-11).  V is formed as fma(n, s, -fp16(z*s)) and P as
-  fp16(p), so each term p*v carries at most u*(2|v| + |z*s|) (+u^2 terms) of
-  absolute error per unit of p, and since O divides by the exact fp32 sum of
-  p, |dO| <= u * (2 max|v| + max|z*s|) over the request's tokens; the gate
-  adds that (x1.01) to the fp32 one.  Scores are computed exactly from the
+* stage-1 partials of the matrix-core paths (D = 128, bf16 Q; INT4 with
+  9..16 query rows per kv-head, INT8 with up to 16): the P.V product takes P
+  and the dequantised V in fp16 (unit roundoff u = 2^-11).  P enters as
+  fp16(p * 2^7) (one relative rounding, p * 2^7 stays in fp16's normal range
+  down to p = 2^-21); INT8 V as fp16(b * s) (one rounding); INT4 V as
+  fma(n, s, -fp16(z*s)) (at most u*(|v| + |z*s|)).  Each term p*v so carries
+  at most u*(2|v| + |z*s|) (+u^2 terms) of absolute error per unit of p, and
+  since O divides by the exact fp32 sum of p, |dO| <= u * (2 max|v| +
+  max|z*s|) over the request's tokens (z*s = 0 for INT8); the gate adds
+  that (x1.01) to the fp32 one.  Scores are computed exactly from the
   codes, so the LSE gate stays 1e-4.
 """
 from __future__ import annotations
@@ -178,19 +181,27 @@ def oracle_sampled(batch: W.PagedBatch, pairs):
 FP16_U = 2.0 ** -11
 
 
-def uses_int4_matrix_path(w: W.Workload) -> bool:
-    """Whether stage 1 over this INT4 workload runs on the matrix cores."""
+def uses_matrix_path(w: W.Workload) -> bool:
+    """Whether stage 1 over this quantised workload runs on the matrix cores."""
     rows = w.group * w.q_per_req
-    return w.kv == W.KV_INT4 and w.head_dim == 128 and 9 <= rows <= 16 and w.dtype != "fp32"
+    if w.head_dim != 128 or w.dtype == "fp32":
+        return False
+    if w.kv == W.KV_INT4:
+        return 9 <= rows <= 16
+    return w.kv == W.KV_INT8 and rows <= 16
 
 
-def int4_fp16_o_bound(batch: W.PagedBatch):
+def fp16_pv_o_bound(batch: W.PagedBatch):
     """Per (request, query head) bound u*(2 max|v| + max|z*s|)*1.01 over the
     request's visible tokens, shaped [B, 1, Hq, 1, 1] (see the module notes)."""
     w = batch.w
-    v = OQ.dequant_int4(W.host_int(batch.v_pool), W.host_u16(batch.v_scale))
-    sz = OQ.fp16_bits_to_f64(W.host_u16(batch.v_scale))
-    zs = np.abs(sz[..., 0] * sz[..., 1])  # [P, ps, Hkv, D/32]
+    if w.kv == W.KV_INT4:
+        v = OQ.dequant_int4(W.host_int(batch.v_pool), W.host_u16(batch.v_scale))
+        sz = OQ.fp16_bits_to_f64(W.host_u16(batch.v_scale))
+        zs = np.abs(sz[..., 0] * sz[..., 1])  # [P, ps, Hkv, D/32]
+    else:
+        v = OQ.dequant_int8(W.host_int(batch.v_pool), W.host_u16(batch.v_scale))
+        zs = np.zeros(v.shape[:3] + (1,))
     pt = W.host_int(batch.page_table)
     L = W.host_int(batch.seq_lens)
     B, G = len(L), w.group

@@ -34,6 +34,16 @@ MTP_BF16_G2Q3 = W.BF16_B16.scaled(name="mtp3_bf16_g2", batch=3, num_q_heads=16, 
                                   causal=True, lengths="list", length_list=(2, 66, 500))
 INT8_SMALL = W.INT8_B32.scaled(name="int8_small", batch=5, lengths="list",
                                length_list=(1, 64, 65, 777, 2000))
+INT8_MTP = W.INT8_B32.scaled(name="int8_mtp2_r8_small", batch=4, q_per_req=2, causal=True,
+                             lengths="list", length_list=(2, 33, 500, 1500))
+INT8_G8Q2 = W.INT8_B32.scaled(name="int8_g8_mtp2_r16_small", batch=3, num_q_heads=64, q_per_req=2,
+                              causal=True, lengths="list", length_list=(1, 80, 900))
+INT8_ODD_HKV = W.INT8_B32.scaled(name="int8_hkv3_g2_small", batch=4, num_q_heads=6,
+                                 num_kv_heads=3, lengths="list", length_list=(5, 64, 129, 1100))
+INT8_FP32Q = W.INT8_B32.scaled(name="int8_fp32q_small", batch=3, dtype="fp32", lengths="list",
+                               length_list=(1, 100, 700))
+INT8_D64 = W.INT8_B32.scaled(name="int8_d64_small", batch=3, head_dim=64, lengths="list",
+                             length_list=(7, 64, 1000))
 INT4_SMALL = W.INT4_MTP_B64.scaled(name="int4_mtp_small", batch=5, lengths="list",
                                    length_list=(1, 4, 65, 777, 2000))
 INT4_Q1 = W.INT4_MTP_B64.scaled(name="int4_q1_small", batch=4, q_per_req=1, causal=False,
@@ -68,7 +78,8 @@ def test_tiny_fp32_every_split(gpu, S):
 
 
 @pytest.mark.parametrize("w", [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, MHA_P32, MTP_BF16,
-                               MTP_BF16_G2Q3, INT8_SMALL, INT4_SMALL, INT4_Q1, INT4_R12, INT4_G8Q2],
+                               MTP_BF16_G2Q3, INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV,
+                               INT8_FP32Q, INT8_D64, INT4_SMALL, INT4_Q1, INT4_R12, INT4_G8Q2],
                          ids=lambda w: w.name)
 @pytest.mark.parametrize("S", [1, 3, 8, 32])
 def test_small_elementwise(gpu, w, S):
@@ -77,7 +88,7 @@ def test_small_elementwise(gpu, w, S):
     o_ref, l_ref = U.oracle_partials(batch, S)
     out_ref, lse_ref = U.oracle_full(batch)
     out, lse, o, l = U.run_decode(gpu, batch, S)
-    extra = U.int4_fp16_o_bound(batch) if U.uses_int4_matrix_path(w) else None
+    extra = U.fp16_pv_o_bound(batch) if U.uses_matrix_path(w) else None
     U.check_partials(U.to_np(o), U.to_np(l), o_ref, l_ref, f"{w.name} S={S}", o_extra=extra)
     _check_out(w, U.to_np(out), out_ref, f"{w.name} S={S} out")
     U.check_lse(U.to_np(lse), lse_ref, f"{w.name} S={S} lse")
@@ -98,7 +109,7 @@ def test_int4_fractional_zero_points(gpu, w):
     o_ref, l_ref = U.oracle_partials(batch, S)
     out_ref, lse_ref = U.oracle_full(batch)
     out, lse, o, l = U.run_decode(gpu, batch, S)
-    extra = U.int4_fp16_o_bound(batch) if U.uses_int4_matrix_path(w) else None
+    extra = U.fp16_pv_o_bound(batch) if U.uses_matrix_path(w) else None
     U.check_partials(U.to_np(o), U.to_np(l), o_ref, l_ref, f"{w.name} frac-z", o_extra=extra)
     U.check_quant(U.to_np(out), out_ref, f"{w.name} frac-z out")
     U.check_lse(U.to_np(lse), lse_ref, f"{w.name} frac-z lse")
@@ -124,7 +135,7 @@ def test_page_permutation_is_bit_identical(gpu):
 
 def test_batch_order_is_bit_identical(gpu):
     """Scheduling requests longest-first (the metadata batch order) changes no bit."""
-    for w in (RAGGED_SMALL, INT8_SMALL, INT4_SMALL, MTP_BF16):
+    for w in (RAGGED_SMALL, INT8_SMALL, INT8_ODD_HKV, INT4_SMALL, MTP_BF16):
         log(f"batch order {w.name}")
         batch = W.make_batch(w, device="cuda")
         md = gpu.decode_attn_metadata(batch.seq_lens, batch.req_pool_indices, batch.req_to_token,
