@@ -105,16 +105,16 @@ def stage1(da, batch, S, o, l):
     if w.kv == W.KV_DENSE:
         return da.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, md["page_table"],
                                     md["cache_seqlens"], S, w.softmax_scale, w.causal, o, l,
-                                    batch_order=md["batch_order"])
+                                    batch_order=md["batch_order"], kv_layout=w.kv_layout)
     if w.kv == W.KV_INT8:
         return da.decode_attn_split_int8(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
                                          batch.v_scale, md["page_table"], md["cache_seqlens"], S,
                                          w.softmax_scale, w.causal, o, l,
-                                         batch_order=md["batch_order"])
+                                         batch_order=md["batch_order"], kv_layout=w.kv_layout)
     return da.decode_attn_split_int4(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
                                      batch.v_scale, md["page_table"], md["cache_seqlens"], S,
                                      w.softmax_scale, w.causal, o, l,
-                                     batch_order=md["batch_order"])
+                                     batch_order=md["batch_order"], kv_layout=w.kv_layout)
 
 
 def rows_per_kv_head(w):
@@ -206,15 +206,15 @@ def cpu_baseline(batch, seconds):
         n = -(-L // w.page_size)
         pages = torch.from_numpy(pt_all[b, :n].astype(np.int64)).cuda()
         q = W.host_f64(batch.q[b:b + 1])
+        def take(t):  # this request's pages, in the oracle's [P, page, Hkv, ...] order
+            return batch.nhd(t).index_select(0, pages)
+
         if w.kv == W.KV_DENSE:
-            k = W.host_f64(batch.k_pool.index_select(0, pages))
-            v = W.host_f64(batch.v_pool.index_select(0, pages))
-        elif w.kv == W.KV_INT8:
-            k = (W.host_int(batch.k_pool.index_select(0, pages)), W.host_u16(batch.k_scale.index_select(0, pages)))
-            v = (W.host_int(batch.v_pool.index_select(0, pages)), W.host_u16(batch.v_scale.index_select(0, pages)))
+            k = W.host_f64(take(batch.k_pool))
+            v = W.host_f64(take(batch.v_pool))
         else:
-            k = (W.host_int(batch.k_pool.index_select(0, pages)), W.host_u16(batch.k_scale.index_select(0, pages)))
-            v = (W.host_int(batch.v_pool.index_select(0, pages)), W.host_u16(batch.v_scale.index_select(0, pages)))
+            k = (W.host_int(take(batch.k_pool)), W.host_u16(take(batch.k_scale)))
+            v = (W.host_int(take(batch.v_pool)), W.host_u16(take(batch.v_scale)))
         pt = np.arange(n, dtype=np.int64)[None, :]
         t0 = time.perf_counter()
         if w.kv == W.KV_INT8:
@@ -420,7 +420,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "q_per_req": w.q_per_req,
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
-                   "head_dim": w.head_dim, "page_size": w.page_size,
+                   "head_dim": w.head_dim, "page_size": w.page_size, "kv_layout": w.kv_layout,
                    "kv_len_max": int(batch.lengths.max()), "kv_len_mean": float(batch.lengths.mean()),
                    "kv_tokens": int(batch.lengths.sum()), "num_splits": S, "seed": w.seed,
                    "parallelism": "single-gpu"},

@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
 
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_LAUNCH = 0, 1, 2, 3
 DA_FP32, DA_BF16 = 0, 1
+DA_KV_NHD, DA_KV_HND = 0, 1
+KV_LAYOUTS = {"NHD": DA_KV_NHD, "HND": DA_KV_HND}
 DA_Q_STRIDED, DA_Q_CUMSUM, DA_Q_PRESET = 0, 1, 2
 DA_MAX_SPLITS = 256
 
@@ -34,14 +36,15 @@ _SIGS = {
     "decode_attn_metadata": [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _I32,
                              _P, _P, _P, _P, _P, _P],
     "decode_attn_split": [_P, _I32, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32,
-                          _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
+                          _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
     "decode_attn_split_int8": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I32,
-                               _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
+                               _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
     "decode_attn_split_int4": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I32,
-                               _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
+                               _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
     "decode_attn_merge": [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P],
     "decode_attn_pick_splits": [_P, _P, _I32, _I32, _I32, _I32, _I32],
-    "decode_attn_gather_kv": [_P, _I64, _I32, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P],
+    "decode_attn_gather_kv": [_P, _I64, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _I32,
+                              _P, _P],
     "decode_attn_strerror": [_I32],
     "decode_attn_version": [],
 }
@@ -138,6 +141,22 @@ def decode_attn_metadata(seq_lens, req_pool_indices, req_to_token, page_size, ma
 
 
 # ------------------------------------------------------------------ stage 1
+def _layout_code(kv_layout) -> int:
+    if isinstance(kv_layout, str):
+        if kv_layout.upper() not in KV_LAYOUTS:
+            raise ValueError(f"kv_layout must be one of {tuple(KV_LAYOUTS)}")
+        return KV_LAYOUTS[kv_layout.upper()]
+    if int(kv_layout) not in (DA_KV_NHD, DA_KV_HND):
+        raise ValueError("kv_layout must be DA_KV_NHD or DA_KV_HND")
+    return int(kv_layout)
+
+
+def _pool_dims(pool, code):
+    """(num_pages, page_size, Hkv) of a pool [P, ps, Hkv, ...] (NHD) or [P, Hkv, ps, ...] (HND)."""
+    P, a, b = pool.shape[:3]
+    return (P, a, b) if code == DA_KV_NHD else (P, b, a)
+
+
 def _partials(q, num_splits, o_partial, lse_partial):
     B, qn, Hq, D = q.shape
     if o_partial is None:
@@ -175,15 +194,19 @@ def _split_common(q, page_table, cache_seqlens, batch_order):
 
 def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
                       softmax_scale=None, causal=False, o_partial=None, lse_partial=None,
-                      batch_order=None):
-    """Stage 1 over a dense bf16 / fp32 cache.  Returns (o_partial, lse_partial)."""
+                      batch_order=None, kv_layout="NHD"):
+    """Stage 1 over a dense bf16 / fp32 cache.  Returns (o_partial, lse_partial).
+
+    Pools are [P, page_size, Hkv, D] (kv_layout "NHD") or [P, Hkv, page_size, D] ("HND")."""
     lib = load()
     dev = _split_common(q, page_table, cache_seqlens, batch_order)
+    lay = _layout_code(kv_layout)
     _need(k_pool, "k_pool", q.dtype, dev, 4)
     _need(v_pool, "v_pool", q.dtype, dev, 4)
     if k_pool.shape != v_pool.shape:
         raise ValueError("k_pool / v_pool shapes differ")
-    P, S_p, Hkv, D = k_pool.shape
+    P, S_p, Hkv = _pool_dims(k_pool, lay)
+    D = k_pool.shape[3]
     B, qn, Hq, Dq = q.shape
     if Dq != D:
         raise ValueError("head_dim mismatch")
@@ -192,7 +215,7 @@ def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
     st = lib.decode_attn_split(
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), page_table.stride(0),
         page_table.shape[1], _ptr(cache_seqlens), _ptr(batch_order), B, qn, Hq, Hkv, D, S_p, P,
-        num_splits, scale,
+        lay, num_splits, scale,
         int(bool(causal)), _ptr(o_partial), _ptr(lse_partial), _stream(dev))
     _check(st, "decode_attn_split")
     return o_partial, lse_partial
@@ -200,16 +223,22 @@ def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
 
 def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cache_seqlens,
                            num_splits, softmax_scale=None, causal=False, o_partial=None,
-                           lse_partial=None, batch_order=None):
-    """Stage 1 over an INT8 cache (fp16 scale per token and kv-head)."""
+                           lse_partial=None, batch_order=None, kv_layout="NHD"):
+    """Stage 1 over an INT8 cache (fp16 scale per token and kv-head).
+
+    Pools [P, page_size, Hkv, D] with scales [P, page_size, Hkv] ("NHD"), or
+    [P, Hkv, page_size, D] with [P, Hkv, page_size] ("HND")."""
     lib = load()
     dev = _split_common(q, page_table, cache_seqlens, batch_order)
+    lay = _layout_code(kv_layout)
     _need(k_pool, "k_pool", torch.int8, dev, 4)
     _need(v_pool, "v_pool", torch.int8, dev, 4)
     _need(k_scale, "k_scale", torch.float16, dev, 3)
     _need(v_scale, "v_scale", torch.float16, dev, 3)
-    P, S_p, Hkv, D = k_pool.shape
-    if v_pool.shape != k_pool.shape or tuple(k_scale.shape) != (P, S_p, Hkv) or k_scale.shape != v_scale.shape:
+    P, S_p, Hkv = _pool_dims(k_pool, lay)
+    D = k_pool.shape[3]
+    if v_pool.shape != k_pool.shape or tuple(k_scale.shape) != tuple(k_pool.shape[:3]) \
+            or k_scale.shape != v_scale.shape:
         raise ValueError("int8 pool / scale shapes inconsistent")
     B, qn, Hq, _ = q.shape
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
@@ -218,7 +247,7 @@ def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cach
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
         _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
         _ptr(batch_order), B, qn,
-        Hq, Hkv, D, S_p, P, num_splits, scale, int(bool(causal)), _ptr(o_partial),
+        Hq, Hkv, D, S_p, P, lay, num_splits, scale, int(bool(causal)), _ptr(o_partial),
         _ptr(lse_partial), _stream(dev))
     _check(st, "decode_attn_split_int8")
     return o_partial, lse_partial
@@ -226,17 +255,22 @@ def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cach
 
 def decode_attn_split_int4(q, k_pool, v_pool, k_scale_zero, v_scale_zero, page_table,
                            cache_seqlens, num_splits, softmax_scale=None, causal=False,
-                           o_partial=None, lse_partial=None, batch_order=None):
-    """Stage 1 over an INT4 cache (fp16 (scale, zero) per 32-group along D)."""
+                           o_partial=None, lse_partial=None, batch_order=None, kv_layout="NHD"):
+    """Stage 1 over an INT4 cache (fp16 (scale, zero) per 32-group along D).
+
+    Pools [P, page_size, Hkv, D/2] with (scale, zero) [P, page_size, Hkv, D/32, 2]
+    ("NHD"), or the first three dims as [P, Hkv, page_size] ("HND")."""
     lib = load()
     dev = _split_common(q, page_table, cache_seqlens, batch_order)
+    lay = _layout_code(kv_layout)
     _need(k_pool, "k_pool", torch.uint8, dev, 4)
     _need(v_pool, "v_pool", torch.uint8, dev, 4)
     _need(k_scale_zero, "k_scale_zero", torch.float16, dev, 5)
     _need(v_scale_zero, "v_scale_zero", torch.float16, dev, 5)
-    P, S_p, Hkv, Dh = k_pool.shape
-    D = 2 * Dh
-    if v_pool.shape != k_pool.shape or tuple(k_scale_zero.shape) != (P, S_p, Hkv, D // 32, 2) \
+    P, S_p, Hkv = _pool_dims(k_pool, lay)
+    D = 2 * k_pool.shape[3]
+    if v_pool.shape != k_pool.shape or \
+            tuple(k_scale_zero.shape) != tuple(k_pool.shape[:3]) + (D // 32, 2) \
             or k_scale_zero.shape != v_scale_zero.shape:
         raise ValueError("int4 pool / scale-zero shapes inconsistent")
     B, qn, Hq, Dq = q.shape
@@ -248,7 +282,7 @@ def decode_attn_split_int4(q, k_pool, v_pool, k_scale_zero, v_scale_zero, page_t
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale_zero), _ptr(v_scale_zero),
         _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
         _ptr(batch_order), B, qn,
-        Hq, Hkv, D, S_p, P, num_splits, scale, int(bool(causal)), _ptr(o_partial),
+        Hq, Hkv, D, S_p, P, lay, num_splits, scale, int(bool(causal)), _ptr(o_partial),
         _ptr(lse_partial), _stream(dev))
     _check(st, "decode_attn_split_int4")
     return o_partial, lse_partial
@@ -292,20 +326,27 @@ def decode_attn_pick_splits(table, batch_keys, bucket_tokens, batch, kv_len) -> 
     return int(s)
 
 
-def decode_attn_gather_kv(pool, page_table, cache_seqlens, cu_seqlens_k, total_tokens, out=None):
-    """Dense [total_tokens, *pool.shape[2:]] copy of every request's tokens (test hook)."""
+def decode_attn_gather_kv(pool, page_table, cache_seqlens, cu_seqlens_k, total_tokens, out=None,
+                          kv_layout="NHD"):
+    """Dense [total_tokens, Hkv, *row] copy of every request's tokens (test hook).
+
+    pool is [P, page_size, Hkv, *row] ("NHD") or [P, Hkv, page_size, *row] ("HND")."""
     lib = load()
     dev = pool.device
+    lay = _layout_code(kv_layout)
     _need(pool, "pool", None, dev)
     _need(page_table, "page_table", torch.int32, dev, 2)
     _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
     _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev, 1)
-    P, S_p = pool.shape[:2]
-    token_bytes = pool[0, 0].numel() * pool.element_size()
+    if pool.dim() < 3:
+        raise ValueError("pool needs at least [pages, slots, heads] dims")
+    P, S_p, Hkv = _pool_dims(pool, lay)
+    row = tuple(pool.shape[3:])
+    row_bytes = pool[0, 0, 0].numel() * pool.element_size()
     if out is None:
-        out = torch.empty((total_tokens,) + tuple(pool.shape[2:]), dtype=pool.dtype, device=dev)
+        out = torch.empty((total_tokens, Hkv) + row, dtype=pool.dtype, device=dev)
     _need(out, "out", pool.dtype, dev)
-    st = lib.decode_attn_gather_kv(_ptr(pool), token_bytes, S_p, P, _ptr(page_table),
+    st = lib.decode_attn_gather_kv(_ptr(pool), row_bytes, Hkv, lay, S_p, P, _ptr(page_table),
                                    page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
                                    _ptr(cu_seqlens_k), page_table.shape[0], _ptr(out), _stream(dev))
     _check(st, "decode_attn_gather_kv")

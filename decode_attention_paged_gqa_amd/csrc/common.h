@@ -104,6 +104,49 @@ inline int32_t launch_status() {
 
 inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// Rows between consecutive slots and between consecutive kv-heads of a
+// page, for the two pool layouts; a page is page_size * Hkv rows.  Row of
+// (page p, slot t, head g) = p * page_size * Hkv + t * slot + g * head.
+struct KvStrides {
+  int slot, head;
+};
+inline bool kv_strides(int32_t kv_layout, int Hkv, int page_size, KvStrides& st) {
+  if (kv_layout == DA_KV_NHD) {
+    st.slot = Hkv;
+    st.head = 1;
+    return true;
+  }
+  if (kv_layout == DA_KV_HND) {
+    st.slot = 1;
+    st.head = page_size;
+    return true;
+  }
+  return false;
+}
+
+// Everything a stage-1 launch needs, checked by the entry point; the
+// specialised kernels take it whole and return -1 for shapes they do not
+// cover (the entry point then launches the generic kernel).
+struct SplitCall {
+  const void* q;
+  int q_bf16;
+  const void* k;
+  const void* v;
+  const uint16_t* ks;  // scales (int8) or (scale, zero) pairs (int4); null for dense
+  const uint16_t* vs;
+  const int32_t* pt;
+  int pt_stride, max_pages;
+  const int32_t* seqlens;
+  const int32_t* order;
+  int batch, qn, Hq, Hkv, D, ps, num_pages, S;
+  KvStrides kv;
+  float scale;
+  int causal;
+  float* o;
+  float* lse;
+  hipStream_t stream;
+};
+
 // 1-D grid of stage 1 (see da::stage1_unit); the grouped order pads to
 // whole rounds of 8 units
 inline unsigned stage1_grid(int Hkv, int S, int B, bool grouped) {

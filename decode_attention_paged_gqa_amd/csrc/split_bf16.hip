@@ -143,6 +143,7 @@ struct Bf16Args {
   int qn, Hq, Hkv, G, R;
   int page_size, log2_ps, num_pages, S;
   int B;  // requests
+  int slot_stride, head_stride;  // rows (see da_host::KvStrides)
   float scale_log2;
   int causal;
 };
@@ -236,8 +237,10 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
   __syncthreads();  // s_pid visible
 
   // ---- addressing: per-lane byte offsets are fixed; per-tile bases are scalar
-  const long long row_bytes = (long long)a.Hkv * D * 2;  // between token rows
-  const uint32_t voff = (uint32_t)(tq * row_bytes + (g * D + 8 * c) * 2);
+  const long long slot_bytes = (long long)a.slot_stride * D * 2;  // between token slots
+  const uint32_t voff = (uint32_t)(tq * slot_bytes + 8 * c * 2);
+  const long long head_base = (long long)g * a.head_stride * D * 2;
+  const long long page_bytes = (long long)ps * a.Hkv * D * 2;
   DA_LDS uint8_t* ring = (DA_LDS uint8_t*)smem + wave * (STAGES * SM::STAGE_BYTES);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   const uint32_t pid_lds = (uint32_t)(uintptr_t)(DA_LDS void*)s_pid;
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
   auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - p0); };
   auto issue = [&](int j, int pid) {
     const int tb = tile_base(j);
-    const long long base = ((long long)pid * ps + (tb & (ps - 1))) * row_bytes;
+    const long long base = pid * page_bytes + (tb & (ps - 1)) * slot_bytes + head_base;
     DA_LDS uint8_t* st = ring + (j % STAGES) * SM::STAGE_BYTES;
     const uint8_t* kb = a.k + base + voff;
     const uint8_t* vb = a.v + base + voff;
@@ -433,23 +436,23 @@ int32_t launch(const Bf16Args& a, int batch, hipStream_t st) {
 // Called by the split entry point after argument validation; returns -1
 // when this kernel does not cover the shape (the caller then uses the
 // generic kernel).
-int32_t da_split_bf16_fast(const void* q, const void* k, const void* v, const int32_t* pt,
-                           int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
-                           const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
-                           int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
-                           float scale, int32_t causal, float* o, float* lse, hipStream_t st) {
-  const int G = Hq / Hkv, R = G * qn;
+int32_t da_split_bf16_fast(const da_host::SplitCall& c) {
+  const int G = c.Hq / c.Hkv, R = G * c.qn, D = c.D;
   if (R > 5 || (D != 128 && D != 64)) return -1;
-  if ((max_pages + S - 1) / S > kMaxSplitPages) return -1;
+  if ((c.max_pages + c.S - 1) / c.S > kMaxSplitPages) return -1;
   Bf16Args a;
-  a.q = (const uint16_t*)q; a.k = (const uint8_t*)k; a.v = (const uint8_t*)v;
-  a.pt = pt; a.seqlens = seqlens; a.order = order; a.o = o; a.lse = lse;
-  a.pt_stride = pt_stride; a.max_pages = max_pages;
-  a.qn = qn; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.R = R;
-  a.page_size = ps; a.log2_ps = __builtin_ctz((unsigned)ps); a.num_pages = num_pages; a.S = S;
-  a.B = batch;
-  a.scale_log2 = scale * da::kLog2e;
-  a.causal = causal ? 1 : 0;
+  a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
+  a.pt = c.pt; a.seqlens = c.seqlens; a.order = c.order; a.o = c.o; a.lse = c.lse;
+  a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
+  a.qn = c.qn; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = G; a.R = R;
+  a.page_size = c.ps; a.log2_ps = __builtin_ctz((unsigned)c.ps); a.num_pages = c.num_pages;
+  a.S = c.S;
+  a.B = c.batch;
+  a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
+  a.scale_log2 = c.scale * da::kLog2e;
+  a.causal = c.causal;
+  const int batch = c.batch;
+  hipStream_t st = c.stream;
   if (D == 128) {
     switch (R) {
       case 1: return launch<128, 1>(a, batch, st);

@@ -47,6 +47,7 @@ struct SplitArgs {
   int qn, Hq, Hkv, G, R;
   int page_size, log2_ps, num_pages, S;
   int B;  // requests
+  int slot_stride, head_stride;  // rows (see da_host::KvStrides)
   float scale_log2;
   int causal;
 };
@@ -211,7 +212,9 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
       kscale[st] = vscale[st] = 1.f;
       kzero[st] = vzero[st] = 0.f;
       if (t < t1) {
-        const long long row = ((long long)pid * ps + slot0 + st * 4 + tl) * a.Hkv + g;
+        const long long row = (long long)pid * ps * a.Hkv +
+                              (long long)(slot0 + st * 4 + tl) * a.slot_stride +
+                              (long long)g * a.head_stride;
         load_raw<P::BYTES>(kb + row * P::ROW_BYTES + c * P::BYTES, kr[st]);
         load_raw<P::BYTES>(vb + row * P::ROW_BYTES + c * P::BYTES, vr[st]);
         if constexpr (KV == KV_I8) {
@@ -374,47 +377,61 @@ int32_t launch_kv(const SplitArgs& a, int D, int batch, hipStream_t st) {
   return D == 128 ? launch_d<KV, 128>(a, batch, st) : launch_d<KV, 64>(a, batch, st);
 }
 
-int32_t check_common(const void* q, const void* k, const void* v, const int32_t* pt,
-                     int32_t pt_stride, int32_t max_pages, const int32_t* seqlens, int32_t batch,
-                     int32_t qn, int32_t Hq, int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages,
-                     int32_t S, const float* o, const float* lse) {
-  if (!q || !k || !v || !pt || !seqlens || !o || !lse) return DA_ERR_INVALID_ARG;
-  if (batch <= 0 || batch > 65535 || qn <= 0 || qn > DA_MAX_Q_PER_REQ || Hq <= 0 || Hkv <= 0 ||
-      Hq % Hkv != 0 || num_pages <= 0 || max_pages <= 0 || pt_stride < max_pages ||
-      S <= 0 || S > DA_MAX_SPLITS || ps <= 0)
+int32_t check_common(const da_host::SplitCall& c, int32_t kv_layout) {
+  if (!c.q || !c.k || !c.v || !c.pt || !c.seqlens || !c.o || !c.lse) return DA_ERR_INVALID_ARG;
+  if (c.batch <= 0 || c.batch > 65535 || c.qn <= 0 || c.qn > DA_MAX_Q_PER_REQ || c.Hq <= 0 ||
+      c.Hkv <= 0 || c.Hq % c.Hkv != 0 || c.num_pages <= 0 || c.max_pages <= 0 ||
+      c.pt_stride < c.max_pages || c.S <= 0 || c.S > DA_MAX_SPLITS || c.ps <= 0)
     return DA_ERR_INVALID_ARG;
-  if ((long long)max_pages * ps > (1ll << 30)) return DA_ERR_INVALID_ARG;
-  if (D != 64 && D != 128) return DA_ERR_UNSUPPORTED;
-  if (!da_host::is_pow2(ps) || ps < 16 || ps > 256) return DA_ERR_UNSUPPORTED;
-  if ((Hq / Hkv) * qn > DA_MAX_ROWS) return DA_ERR_UNSUPPORTED;
+  if ((long long)c.max_pages * c.ps > (1ll << 30)) return DA_ERR_INVALID_ARG;
+  if (kv_layout != DA_KV_NHD && kv_layout != DA_KV_HND) return DA_ERR_INVALID_ARG;
+  if (c.D != 64 && c.D != 128) return DA_ERR_UNSUPPORTED;
+  if (!da_host::is_pow2(c.ps) || c.ps < 16 || c.ps > 256) return DA_ERR_UNSUPPORTED;
+  if ((c.Hq / c.Hkv) * c.qn > DA_MAX_ROWS) return DA_ERR_UNSUPPORTED;
   return DA_OK;
 }
 
-SplitArgs make_args(const void* q, int q_bf16, const void* k, const void* v, const uint16_t* ks,
-                    const uint16_t* vs, const int32_t* pt, int32_t pt_stride, int32_t max_pages,
-                    const int32_t* seqlens, const int32_t* order, int32_t qn, int32_t Hq, int32_t Hkv, int32_t ps,
-                    int32_t num_pages, int32_t S, float scale, int32_t causal, float* o,
-                    float* lse) {
+da_host::SplitCall make_call(const void* q, int q_bf16, const void* k, const void* v,
+                             const uint16_t* ks, const uint16_t* vs, const int32_t* pt,
+                             int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
+                             const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
+                             int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages,
+                             int32_t kv_layout, int32_t S, float scale, int32_t causal, float* o,
+                             float* lse, void* stream) {
+  da_host::SplitCall c;
+  c.q = q; c.q_bf16 = q_bf16; c.k = k; c.v = v; c.ks = ks; c.vs = vs;
+  c.pt = pt; c.pt_stride = pt_stride; c.max_pages = max_pages;
+  c.seqlens = seqlens; c.order = order;
+  c.batch = batch; c.qn = qn; c.Hq = Hq; c.Hkv = Hkv; c.D = D; c.ps = ps;
+  c.num_pages = num_pages; c.S = S;
+  if (!da_host::kv_strides(kv_layout, Hkv, ps, c.kv)) c.kv = {0, 0};  // rejected by the check
+  c.scale = scale; c.causal = causal ? 1 : 0;
+  c.o = o; c.lse = lse; c.stream = (hipStream_t)stream;
+  return c;
+}
+
+SplitArgs make_args(const da_host::SplitCall& c) {
   SplitArgs a;
-  a.q = q; a.k = k; a.v = v; a.ks = ks; a.vs = vs; a.pt = pt; a.seqlens = seqlens; a.order = order;
-  a.o = o; a.lse = lse; a.q_bf16 = q_bf16;
-  a.pt_stride = pt_stride; a.max_pages = max_pages;
-  a.qn = qn; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.R = a.G * qn;
-  a.page_size = ps; a.log2_ps = __builtin_ctz((unsigned)ps); a.num_pages = num_pages; a.S = S;
+  a.q = c.q; a.k = c.k; a.v = c.v; a.ks = c.ks; a.vs = c.vs; a.pt = c.pt;
+  a.seqlens = c.seqlens; a.order = c.order;
+  a.o = c.o; a.lse = c.lse; a.q_bf16 = c.q_bf16;
+  a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
+  a.qn = c.qn; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = c.Hq / c.Hkv; a.R = a.G * c.qn;
+  a.page_size = c.ps; a.log2_ps = __builtin_ctz((unsigned)c.ps); a.num_pages = c.num_pages;
+  a.S = c.S;
   a.B = 0;  // set at launch
-  a.scale_log2 = scale * da::kLog2e;
-  a.causal = causal ? 1 : 0;
+  a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
+  a.scale_log2 = c.scale * da::kLog2e;
+  a.causal = c.causal;
   return a;
 }
 
 }  // namespace
 
-// bf16 stage 1 for G*q <= 5 (split_bf16.hip); -1 when the shape is not covered.
-int32_t da_split_bf16_fast(const void* q, const void* k, const void* v, const int32_t* pt,
-                           int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
-                           const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
-                           int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
-                           float scale, int32_t causal, float* o, float* lse, hipStream_t st);
+// Specialised stage-1 kernels; each returns -1 when the shape is not covered.
+int32_t da_split_bf16_fast(const da_host::SplitCall& c);  // split_bf16.hip: bf16, G*q <= 5
+int32_t da_split_int8_mfma(const da_host::SplitCall& c);  // split_int8.hip: D 128, bf16 Q
+int32_t da_split_int4_mfma(const da_host::SplitCall& c);  // split_int4.hip: 9..16 rows
 
 extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool,
                                      const void* v_pool, const int32_t* page_table,
@@ -422,99 +439,62 @@ extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k
                                      const int32_t* cache_seqlens, const int32_t* batch_order,
                                      int32_t batch, int32_t q_per_req, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                                     int32_t num_pages, int32_t num_splits, float softmax_scale,
-                                     int32_t causal, float* o_partial, float* lse_partial,
-                                     void* stream) {
-  int32_t st = check_common(q, k_pool, v_pool, page_table, page_table_stride, max_pages,
-                            cache_seqlens, batch, q_per_req, num_q_heads, num_kv_heads, head_dim,
-                            page_size, num_pages, num_splits, o_partial, lse_partial);
-  if (st) return st;
+                                     int32_t num_pages, int32_t kv_layout, int32_t num_splits,
+                                     float softmax_scale, int32_t causal, float* o_partial,
+                                     float* lse_partial, void* stream) {
+  const da_host::SplitCall c =
+      make_call(q, dtype == DA_BF16, k_pool, v_pool, nullptr, nullptr, page_table,
+                page_table_stride, max_pages, cache_seqlens, batch_order, batch, q_per_req,
+                num_q_heads, num_kv_heads, head_dim, page_size, num_pages, kv_layout, num_splits,
+                softmax_scale, causal, o_partial, lse_partial, stream);
+  if (const int32_t st = check_common(c, kv_layout)) return st;
   if (dtype != DA_BF16 && dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
-  const SplitArgs a = make_args(q, dtype == DA_BF16, k_pool, v_pool, nullptr, nullptr, page_table,
-                                page_table_stride, max_pages, cache_seqlens, batch_order, q_per_req,
-                                num_q_heads, num_kv_heads, page_size, num_pages, num_splits,
-                                softmax_scale, causal, o_partial, lse_partial);
-  hipStream_t s = (hipStream_t)stream;
   if (dtype == DA_BF16) {
-    const int32_t fast = da_split_bf16_fast(q, k_pool, v_pool, page_table, page_table_stride,
-                                            max_pages, cache_seqlens, batch_order, batch, q_per_req,
-                                            num_q_heads, num_kv_heads, head_dim, page_size,
-                                            num_pages, num_splits, softmax_scale, causal,
-                                            o_partial, lse_partial, s);
+    const int32_t fast = da_split_bf16_fast(c);
     if (fast >= 0) return fast;
-    return launch_kv<KV_BF16>(a, head_dim, batch, s);
+    return launch_kv<KV_BF16>(make_args(c), head_dim, batch, c.stream);
   }
-  return launch_kv<KV_F32>(a, head_dim, batch, s);
+  return launch_kv<KV_F32>(make_args(c), head_dim, batch, c.stream);
 }
-
-// INT4 stage 1 on the matrix cores for 9..16 rows (split_int4.hip); -1 when
-// the shape is not covered.
-int32_t da_split_int4_mfma(const void* q, int q_bf16, const uint8_t* k, const uint8_t* v,
-                           const uint16_t* ksz, const uint16_t* vsz, const int32_t* pt,
-                           int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
-                           const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
-                           int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
-                           float scale, int32_t causal, float* o, float* lse, hipStream_t st);
-
-// INT8 stage 1 on the matrix cores for D = 128 and bf16 Q (split_int8.hip);
-// -1 when the shape is not covered.
-int32_t da_split_int8_mfma(const void* q, int q_bf16, const int8_t* k, const int8_t* v,
-                           const uint16_t* ks, const uint16_t* vs, const int32_t* pt,
-                           int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
-                           const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
-                           int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
-                           float scale, int32_t causal, float* o, float* lse, hipStream_t st);
 
 extern "C" int32_t decode_attn_split_int8(
     const void* q, int32_t q_dtype, const int8_t* k_pool, const int8_t* v_pool,
     const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* page_table,
     int32_t page_table_stride, int32_t max_pages, const int32_t* cache_seqlens,
-    const int32_t* batch_order, int32_t batch, int32_t q_per_req, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t page_size, int32_t num_pages, int32_t num_splits, float softmax_scale,
-    int32_t causal, float* o_partial, float* lse_partial, void* stream) {
-  int32_t st = check_common(q, k_pool, v_pool, page_table, page_table_stride, max_pages,
-                            cache_seqlens, batch, q_per_req, num_q_heads, num_kv_heads, head_dim,
-                            page_size, num_pages, num_splits, o_partial, lse_partial);
-  if (st) return st;
+    const int32_t* batch_order, int32_t batch, int32_t q_per_req, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
+    int32_t kv_layout, int32_t num_splits, float softmax_scale, int32_t causal,
+    float* o_partial, float* lse_partial, void* stream) {
+  const da_host::SplitCall c =
+      make_call(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale, v_scale, page_table,
+                page_table_stride, max_pages, cache_seqlens, batch_order, batch, q_per_req,
+                num_q_heads, num_kv_heads, head_dim, page_size, num_pages, kv_layout, num_splits,
+                softmax_scale, causal, o_partial, lse_partial, stream);
+  if (const int32_t st = check_common(c, kv_layout)) return st;
   if (!k_scale || !v_scale) return DA_ERR_INVALID_ARG;
   if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
-  const SplitArgs a = make_args(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale, v_scale,
-                                page_table, page_table_stride, max_pages, cache_seqlens,
-                                batch_order, q_per_req, num_q_heads, num_kv_heads, page_size, num_pages,
-                                num_splits, softmax_scale, causal, o_partial, lse_partial);
-  const int32_t mf = da_split_int8_mfma(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale, v_scale,
-                                        page_table, page_table_stride, max_pages, cache_seqlens,
-                                        batch_order, batch, q_per_req, num_q_heads, num_kv_heads,
-                                        head_dim, page_size, num_pages, num_splits, softmax_scale,
-                                        causal, o_partial, lse_partial, (hipStream_t)stream);
+  const int32_t mf = da_split_int8_mfma(c);
   if (mf >= 0) return mf;
-  return launch_kv<KV_I8>(a, head_dim, batch, (hipStream_t)stream);
+  return launch_kv<KV_I8>(make_args(c), head_dim, batch, c.stream);
 }
 
 extern "C" int32_t decode_attn_split_int4(
     const void* q, int32_t q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
     const uint16_t* k_scale_zero, const uint16_t* v_scale_zero, const int32_t* page_table,
     int32_t page_table_stride, int32_t max_pages, const int32_t* cache_seqlens,
-    const int32_t* batch_order, int32_t batch, int32_t q_per_req, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t page_size, int32_t num_pages, int32_t num_splits, float softmax_scale,
-    int32_t causal, float* o_partial, float* lse_partial, void* stream) {
-  int32_t st = check_common(q, k_pool, v_pool, page_table, page_table_stride, max_pages,
-                            cache_seqlens, batch, q_per_req, num_q_heads, num_kv_heads, head_dim,
-                            page_size, num_pages, num_splits, o_partial, lse_partial);
-  if (st) return st;
+    const int32_t* batch_order, int32_t batch, int32_t q_per_req, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
+    int32_t kv_layout, int32_t num_splits, float softmax_scale, int32_t causal,
+    float* o_partial, float* lse_partial, void* stream) {
+  const da_host::SplitCall c =
+      make_call(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale_zero, v_scale_zero, page_table,
+                page_table_stride, max_pages, cache_seqlens, batch_order, batch, q_per_req,
+                num_q_heads, num_kv_heads, head_dim, page_size, num_pages, kv_layout, num_splits,
+                softmax_scale, causal, o_partial, lse_partial, stream);
+  if (const int32_t st = check_common(c, kv_layout)) return st;
   if (!k_scale_zero || !v_scale_zero) return DA_ERR_INVALID_ARG;
   if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
-  const SplitArgs a = make_args(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale_zero,
-                                v_scale_zero, page_table, page_table_stride, max_pages,
-                                cache_seqlens, batch_order, q_per_req, num_q_heads, num_kv_heads, page_size,
-                                num_pages, num_splits, softmax_scale, causal, o_partial,
-                                lse_partial);
-  const int32_t mf = da_split_int4_mfma(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale_zero,
-                                        v_scale_zero, page_table, page_table_stride, max_pages,
-                                        cache_seqlens, batch_order, batch, q_per_req, num_q_heads,
-                                        num_kv_heads, head_dim, page_size, num_pages, num_splits,
-                                        softmax_scale, causal, o_partial, lse_partial,
-                                        (hipStream_t)stream);
+  const int32_t mf = da_split_int4_mfma(c);
   if (mf >= 0) return mf;
-  return launch_kv<KV_I4>(a, head_dim, batch, (hipStream_t)stream);
+  return launch_kv<KV_I4>(make_args(c), head_dim, batch, c.stream);
 }

@@ -25,11 +25,15 @@
 // z, which makes any fp16 zero point exact too.
 //   * QK: MFMA kb is group kb.  Lane (lm, lg) supplies token lm's dword lg
 //     of that group (elements 32*kb + 8*lg + 0..7); k-slots 2x, 2x+1 are
-//     elements x and x+4 of the dword, which nibble masks give directly.
+//     elements x and x+4 of the dword (nibble x of its two halves).  Pairs
+//     0 and 2 are masked into bits 0..3 (n * 2^-24); pairs 1 and 3 are
+//     masked where they lie, bits 4..7 (16 n * 2^-24, still exact), and
+//     their Q elements are divided by 16 instead.
 //   * PV: output block b row m is d = 8*m + b: lane (lm, lg) reads, for its
 //     four tokens 4*lg+j, the dword lm of each row (d = 8*lm .. 8*lm+7),
 //     all in group lm/4.  V^T is dequantised to fp16 as n*s - z*s (one fma
-//     per element pair after the exact n; -z*s rounded once per token), and
+//     per element pair after the exact n; -z*s rounded once per token; a
+//     high nibble is taken in place as 16 n and meets s / 16), and
 //     P enters as fp16(p * 2^7) (p <= 2^8 under the lazy rescale below, so
 //     p * 2^7 < 2^15; the factor keeps small weights out of fp16's subnormal
 //     range and cancels against the same factor in l): these two roundings
@@ -127,16 +131,11 @@ struct MfmaArgs {
   int qn, Hq, Hkv, G, R;
   int page_size, log2_ps, num_pages, S;
   int B;  // requests
+  int slot_stride, head_stride;  // rows (see da_host::KvStrides)
   float scale_log2;
   int causal;
 };
 
-// codes x and x + 4 of dword w (nibble x of each 16-bit half) as the fp16
-// subnormals n * 2^-24
-template <int X>
-__device__ __forceinline__ uint32_t code_pair(uint32_t w) {
-  return (w >> (4 * X)) & 0x000F000Fu;
-}
 __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
@@ -206,7 +205,11 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
         part += qf[kb][e];
       }
 #pragma unroll
-      for (int x = 0; x < 4; ++x) qv[kb][x] = pack_h2(qf[kb][x], qf[kb][x + 4]);
+      for (int x = 0; x < 4; ++x) {
+        // pairs 1 and 3 meet codes that sit 4 bits up (16 n), see the K operand
+        const float f = (x & 1) ? 0.0625f : 1.f;
+        qv[kb][x] = pack_h2(qf[kb][x] * f, qf[kb][x + 4] * f);
+      }
       part += xor16(part);
       part += xor32(part);
       qsum[kb] = ldexpf(part, -24);
@@ -227,11 +230,15 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) acc[bb] = {0.f, 0.f, 0.f, 0.f};
   float m = da::kNegInf, l = 0.f;
+  // fp16 exponent bits of 1024 in both halves, kept in a register so that
+  // mask-and-or is one instruction
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));
   __syncthreads();
 
   // ---- addressing
-  const long long rowb = (long long)a.Hkv * (kD / 2);  // bytes between token rows (codes)
-  const long long szb = (long long)a.Hkv * 16;         // bytes between token rows (scale/zero)
+  const long long rowb = (long long)a.slot_stride * (kD / 2);  // bytes between slots (codes)
+  const long long szb = (long long)a.slot_stride * 16;         // (scale/zero)
   // DMA lane i fills LDS chunk i (token i/4, position i%4) with the token's
   // 16-byte group (position - token/4) mod 4
   const uint32_t voff_kv = (uint32_t)((lane >> 2) * rowb + 16 * (((lane & 3) - (lane >> 4)) & 3));
@@ -250,7 +257,8 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
   auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - p0); };
   auto issue = [&](int j, int pid) {
     const int tb = tile_base(j);
-    const long long row0 = ((long long)pid * ps + (tb & (ps - 1))) * a.Hkv + g;
+    const long long row0 = (long long)pid * ps * a.Hkv + (long long)(tb & (ps - 1)) * a.slot_stride +
+                           (long long)g * a.head_stride;
     DA_LDS uint8_t* st = ring + (j % kStages) * kStageBytes;
     __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * (kD / 2) + voff_kv),
                                      (DA_LDS void*)(st + kStageK), 16, 0, 0);
@@ -269,9 +277,11 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
     float4_t dot[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const uint32_t w = sd.k[kb];
-      const half2_t k0 = as_h2(code_pair<0>(w)), k1 = as_h2(code_pair<1>(w));
-      const half2_t k2 = as_h2(code_pair<2>(w)), k3 = as_h2(code_pair<3>(w));
+      // elements (x, x+4) are nibble x of the dword's two halves; pairs 1
+      // and 3 are masked in place (16 n * 2^-24, exact), their Q is / 16
+      const uint32_t w = sd.k[kb], wh = w >> 8;
+      const half2_t k0 = as_h2(w & 0x000F000Fu), k1 = as_h2(w & 0x00F000F0u);
+      const half2_t k2 = as_h2(wh & 0x000F000Fu), k3 = as_h2(wh & 0x00F000F0u);
       const half8_t ka = {k0[0], k0[1], k1[0], k1[1], k2[0], k2[1], k3[0], k3[1]};
       const half2_t q0 = as_h2(qv[kb][0]), q1 = as_h2(qv[kb][1]);
       const half2_t q2 = as_h2(qv[kb][2]), q3 = as_h2(qv[kb][3]);
@@ -340,6 +350,8 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
     const half2_t s23 = as_h2(__builtin_amdgcn_perm(vsz[3], vsz[2], 0x05040100u));
     const half2_t nzs01 = -(as_h2(__builtin_amdgcn_perm(vsz[1], vsz[0], 0x07060302u)) * s01);
     const half2_t nzs23 = -(as_h2(__builtin_amdgcn_perm(vsz[3], vsz[2], 0x07060302u)) * s23);
+    // high nibbles are taken in place as 16 n: their scale is s / 16
+    const half2_t s01h = s01 * half2_t{0.0625, 0.0625}, s23h = s23 * half2_t{0.0625, 0.0625};
     const half2_t k1024 = {1024, 1024};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -350,10 +362,12 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) {
         const int bb = 2 * kk + hi;
-        const half2_t n01 = as_h2(((x01 >> (4 * hi)) & 0x000F000Fu) | 0x64006400u) - k1024;
-        const half2_t n23 = as_h2(((x23 >> (4 * hi)) & 0x000F000Fu) | 0x64006400u) - k1024;
-        const half2_t a01 = __builtin_elementwise_fma(n01, s01, nzs01);
-        const half2_t a23 = __builtin_elementwise_fma(n23, s23, nzs23);
+        // fp16 1024 + n (low nibble) or 1024 + 16 n (high nibble), exact
+        const uint32_t mask = hi ? 0x00F000F0u : 0x000F000Fu;
+        const half2_t n01 = as_h2((x01 & mask) | magic) - k1024;
+        const half2_t n23 = as_h2((x23 & mask) | magic) - k1024;
+        const half2_t a01 = __builtin_elementwise_fma(n01, hi ? s01h : s01, nzs01);
+        const half2_t a23 = __builtin_elementwise_fma(n23, hi ? s23h : s23, nzs23);
         half4_t va = {a01[0], a01[1], a23[0], a23[1]};
         acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, acc[bb], 0, 0, 0);
       }
@@ -429,26 +443,23 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
 
 // INT4 stage 1 on the matrix cores; -1 when the shape is not covered
 // (the caller then uses the vector-ALU kernel).
-int32_t da_split_int4_mfma(const void* q, int q_bf16, const uint8_t* k, const uint8_t* v,
-                           const uint16_t* ksz, const uint16_t* vsz, const int32_t* pt,
-                           int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
-                           const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
-                           int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
-                           float scale, int32_t causal, float* o, float* lse, hipStream_t st) {
-  const int G = Hq / Hkv, R = G * qn;
-  if (!q_bf16 || D != kD || R < 9 || R > 16) return -1;
-  if ((max_pages + S - 1) / S > kMaxSplitPages) return -1;
+int32_t da_split_int4_mfma(const da_host::SplitCall& c) {
+  const int G = c.Hq / c.Hkv, R = G * c.qn;
+  if (!c.q_bf16 || c.D != kD || R < 9 || R > 16) return -1;
+  if ((c.max_pages + c.S - 1) / c.S > kMaxSplitPages) return -1;
   MfmaArgs a;
-  a.q = (const uint16_t*)q; a.k = k; a.v = v;
-  a.ksz = (const uint8_t*)ksz; a.vsz = (const uint8_t*)vsz;
-  a.pt = pt; a.seqlens = seqlens; a.order = order; a.o = o; a.lse = lse;
-  a.pt_stride = pt_stride; a.max_pages = max_pages;
-  a.qn = qn; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.R = R;
-  a.page_size = ps; a.log2_ps = __builtin_ctz((unsigned)ps); a.num_pages = num_pages; a.S = S;
-  a.scale_log2 = scale * da::kLog2e;
-  a.causal = causal ? 1 : 0;
-  a.B = batch;
-  hipLaunchKernelGGL(split_int4_mfma_kernel, dim3(da_host::stage1_grid(Hkv, S, batch, true)), dim3(kThreads),
-                     0, st, a);
+  a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
+  a.ksz = (const uint8_t*)c.ks; a.vsz = (const uint8_t*)c.vs;
+  a.pt = c.pt; a.seqlens = c.seqlens; a.order = c.order; a.o = c.o; a.lse = c.lse;
+  a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
+  a.qn = c.qn; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = G; a.R = R;
+  a.page_size = c.ps; a.log2_ps = __builtin_ctz((unsigned)c.ps); a.num_pages = c.num_pages;
+  a.S = c.S;
+  a.B = c.batch;
+  a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
+  a.scale_log2 = c.scale * da::kLog2e;
+  a.causal = c.causal;
+  hipLaunchKernelGGL(split_int4_mfma_kernel, dim3(da_host::stage1_grid(c.Hkv, c.S, c.batch, true)),
+                     dim3(kThreads), 0, c.stream, a);
   return da_host::launch_status();
 }

@@ -111,6 +111,7 @@ struct Int8Args {
   int qn, Hq, Hkv, G, R;
   int page_size, log2_ps, num_pages, S;
   int B;
+  int slot_stride, head_stride;  // rows (see da_host::KvStrides)
   float scale_log2;
   int causal;
 };
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
   __syncthreads();
 
   // ---- addressing
-  const long long rowb = (long long)a.Hkv * kD;  // bytes between token rows (codes)
+  const long long rowb = (long long)a.slot_stride * kD;  // bytes between slots (codes)
   // DMA lane i of half h fills LDS chunk i of that half: token 8h + i/8,
   // position i%8, holding the row's chunk (position - token/2) mod 8
   uint32_t voff_kv[2];
@@ -244,9 +245,11 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 
   auto tile_base = [&](int j) { return t0 + ((wave + kWaves * j) << 4); };
   auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - p0); };
+  const long long head_row = (long long)g * a.head_stride;
   auto issue = [&](int j, int pid) {
-    const long long row = (long long)pid * ps + (tile_base(j) & (ps - 1));  // tile's first slot
-    const long long row0 = row * a.Hkv + g;
+    // row of the tile's first slot
+    const long long row0 = (long long)pid * ps * a.Hkv +
+                           (long long)(tile_base(j) & (ps - 1)) * a.slot_stride + head_row;
     DA_LDS uint8_t* st = ring + (j % kStages) * kStageBytes;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -256,17 +259,18 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     for (int h = 0; h < 2; ++h)
       __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * kD + voff_kv[h]),
                                        (DA_LDS void*)(st + kStageV + 1024 * h), 16, 0, 0);
-    const long long e = (row + sc_tok) * a.Hkv + g;  // scale index
+    const long long e = row0 + (long long)sc_tok * a.slot_stride;  // scale index
     __builtin_amdgcn_global_load_lds((const void*)(sc_base + ((2 * e) & ~3ll)),
                                      (DA_LDS void*)(st + kStageSc), 4, 0, 0);
   };
 
   // Half of the scale dword holding token 4*lg + i's scale.  Its index is
-  // (row + 4*lg + i) * Hkv + g with row = pid * page_size + a multiple of
-  // 16, an even number, so the parity is that of g + i * Hkv.
+  // pid * page_size * Hkv + (slot0 + 4*lg + i) * slot_stride + g * head_stride
+  // with page_size even and slot0 a multiple of 16, so its parity is that
+  // of i * slot_stride + g * head_stride.
   int sc_shift[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sc_shift[i] = ((g + i * a.Hkv) & 1) << 4;
+  for (int i = 0; i < 4; ++i) sc_shift[i] = ((i * a.slot_stride + g * a.head_stride) & 1) << 4;
 
   auto compute = [&](int j, const StageData& sd, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
@@ -432,26 +436,24 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 
 // INT8 stage 1 on the matrix cores; -1 when the shape is not covered (the
 // caller then uses the vector-ALU kernel).
-int32_t da_split_int8_mfma(const void* q, int q_bf16, const int8_t* k, const int8_t* v,
-                           const uint16_t* ks, const uint16_t* vs, const int32_t* pt,
-                           int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
-                           const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
-                           int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages, int32_t S,
-                           float scale, int32_t causal, float* o, float* lse, hipStream_t st) {
-  const int G = Hq / Hkv, R = G * qn;
-  if (!q_bf16 || D != kD || R > 16) return -1;
-  if ((max_pages + S - 1) / S > kMaxSplitPages) return -1;
+int32_t da_split_int8_mfma(const da_host::SplitCall& c) {
+  const int G = c.Hq / c.Hkv, R = G * c.qn;
+  if (!c.q_bf16 || c.D != kD || R > 16) return -1;
+  if ((c.max_pages + c.S - 1) / c.S > kMaxSplitPages) return -1;
   Int8Args a;
-  a.q = (const uint16_t*)q; a.k = (const uint8_t*)k; a.v = (const uint8_t*)v;
-  a.ks = (const uint8_t*)ks; a.vs = (const uint8_t*)vs;
-  a.pt = pt; a.seqlens = seqlens; a.order = order; a.o = o; a.lse = lse;
-  a.pt_stride = pt_stride; a.max_pages = max_pages;
-  a.qn = qn; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.R = R;
-  a.page_size = ps; a.log2_ps = __builtin_ctz((unsigned)ps); a.num_pages = num_pages; a.S = S;
-  a.B = batch;
-  a.scale_log2 = scale * da::kLog2e;
-  a.causal = causal ? 1 : 0;
-  hipLaunchKernelGGL(split_int8_mfma_kernel, dim3(da_host::stage1_grid(Hkv, S, batch, true)),
-                     dim3(kThreads), 0, st, a);
+  a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
+  a.ks = (const uint8_t*)c.ks; a.vs = (const uint8_t*)c.vs;
+  a.pt = c.pt; a.seqlens = c.seqlens; a.order = c.order; a.o = c.o; a.lse = c.lse;
+  a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
+  a.qn = c.qn; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = G; a.R = R;
+  a.page_size = c.ps; a.log2_ps = __builtin_ctz((unsigned)c.ps); a.num_pages = c.num_pages;
+  a.S = c.S;
+  a.B = c.batch;
+  a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
+  a.scale_log2 = c.scale * da::kLog2e;
+  a.causal = c.causal;
+  hipLaunchKernelGGL(split_int8_mfma_kernel,
+                     dim3(da_host::stage1_grid(c.Hkv, c.S, c.batch, true)), dim3(kThreads), 0,
+                     c.stream, a);
   return da_host::launch_status();
 }

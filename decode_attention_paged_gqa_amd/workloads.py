@@ -61,6 +61,7 @@ class Workload:
     pool_pages: int = 0            # 0 => exactly the pages needed
     seed: int = 0
     splits: tuple = (1,)
+    kv_layout: str = "NHD"         # "NHD" [P, page, Hkv, row] | "HND" [P, Hkv, page, row]
 
     @property
     def group(self) -> int:
@@ -84,23 +85,23 @@ TINY_FP32 = Workload(
 BF16_B16 = Workload(
     name="bf16_b16_hq32_hkv8_d128_p64_L8192", batch=16, num_q_heads=32, num_kv_heads=8,
     head_dim=128, page_size=64, lengths="fixed", length=8192, seed=2,
-    splits=(1, 2, 4, 8, 16, 32))
+    splits=(1, 2, 4, 8, 16, 32), kv_layout="HND")
 RAGGED_B64 = Workload(
     name="ragged_bf16_b64_hq40_hkv8_d128_p64_L1k-32k", batch=64, num_q_heads=40,
     num_kv_heads=8, head_dim=128, page_size=64, lengths="loguniform", length_lo=1024,
-    length_hi=32768, pin_max=True, seed=3, splits=(1, 2, 4, 8, 16, 32))
+    length_hi=32768, pin_max=True, seed=3, splits=(1, 2, 4, 8, 16, 32), kv_layout="HND")
 UNIFORM_B64 = RAGGED_B64.scaled(
     name="bf16_b64_hq40_hkv8_d128_p64_L32768", lengths="fixed", length=32768,
     pin_max=False)
 INT8_B32 = Workload(
     name="int8kv_b32_hq32_hkv8_d128_p64_L32768", batch=32, num_q_heads=32, num_kv_heads=8,
     head_dim=128, page_size=64, kv=KV_INT8, lengths="fixed", length=32768, seed=4,
-    splits=(1, 2, 4, 8, 16, 32))
+    splits=(1, 2, 4, 8, 16, 32), kv_layout="HND")
 INT4_MTP_B64 = Workload(
     name="int4kv_mtp4_b64_hq32_hkv8_d128_p64_L8k-32k", batch=64, num_q_heads=32,
     num_kv_heads=8, head_dim=128, page_size=64, q_per_req=4, causal=True, kv=KV_INT4,
     lengths="uniform", length_lo=8192, length_hi=32768, seed=5,
-    splits=(1, 2, 4, 8, 16, 32))
+    splits=(1, 2, 4, 8, 16, 32), kv_layout="HND")
 
 WORKLOADS = {w.name: w for w in (TINY_FP32, BF16_B16, RAGGED_B64, UNIFORM_B64,
                                  INT8_B32, INT4_MTP_B64)}
@@ -137,10 +138,18 @@ class PagedBatch:
     page_table: torch.Tensor        # [B, max_pages] int32 physical page ids (0-padded)
     q: torch.Tensor                 # [B, q, Hq, D] bf16 / fp32
     k_pool: torch.Tensor            # dense [P,S,Hkv,D]; int8 [P,S,Hkv,D]; int4 u8 [P,S,Hkv,D/2]
-    v_pool: torch.Tensor
+    v_pool: torch.Tensor            # (the first three dims [P,Hkv,S] when w.kv_layout is "HND")
     k_scale: Optional[torch.Tensor] = None  # int8: fp16 [P,S,Hkv]; int4: fp16 [P,S,Hkv,D/32,2]
     v_scale: Optional[torch.Tensor] = None
     lengths: np.ndarray = field(default=None)
+
+    @property
+    def kv_layout(self) -> str:
+        return self.w.kv_layout
+
+    def nhd(self, t: torch.Tensor) -> torch.Tensor:
+        """View of a pool or scale tensor of this batch in NHD order (dims 1, 2 swapped back)."""
+        return t if self.w.kv_layout == "NHD" else t.transpose(1, 2)
 
     @property
     def num_pages(self) -> int:
@@ -261,6 +270,12 @@ def make_batch(w: Workload, device="cpu", seed: Optional[int] = None,
         v_pool, v_scale = quantize_int4(normal().to(torch.bfloat16))
     else:
         raise ValueError(w.kv)
+    if w.kv_layout == "HND":  # same values, head-major within each page
+        k_pool, v_pool = to_hnd(k_pool), to_hnd(v_pool)
+        if k_scale is not None:
+            k_scale, v_scale = to_hnd(k_scale), to_hnd(v_scale)
+    elif w.kv_layout != "NHD":
+        raise ValueError(w.kv_layout)
     return PagedBatch(
         w=w,
         seq_lens=torch.from_numpy(L.astype(np.int32)).to(device),
@@ -270,6 +285,11 @@ def make_batch(w: Workload, device="cpu", seed: Optional[int] = None,
         q=q, k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale,
         lengths=L,
     )
+
+
+def to_hnd(t: torch.Tensor) -> torch.Tensor:
+    """[P, page, Hkv, ...] -> contiguous [P, Hkv, page, ...]."""
+    return t.transpose(1, 2).contiguous()
 
 
 def host_f64(t: torch.Tensor) -> np.ndarray:

@@ -37,9 +37,15 @@
  *
  * Layouts (row-major, contiguous):
  *   q            [B, q_per_req, Hq, D]
- *   k/v pools    [num_pages, page_size, Hkv, D]          (dense: bf16 / fp32, int8)
- *                [num_pages, page_size, Hkv, D/2] uint8  (int4: element 2j in the
- *                                                         low nibble of byte j)
+ *   k/v pools    pages of page_size token slots.  A "row" is the entry of one
+ *                (slot, kv-head): D elements (bf16 / fp32 / int8), or D/2
+ *                bytes of 4-bit codes (element 2j in the low nibble of byte
+ *                j); scale arrays have the same layout with their own rows.
+ *                kv_layout DA_KV_NHD: [num_pages, page_size, Hkv, row]
+ *                kv_layout DA_KV_HND: [num_pages, Hkv, page_size, row]
+ *                (HND keeps a kv-head's rows of a page contiguous, which
+ *                makes the stage-1 reads of short rows -- quantised codes,
+ *                their scales -- long contiguous runs.)
  *   page_table   [B, page_table_stride], first max_pages entries of a row used
  *   o_partial    [B, q_per_req, Hq, num_splits, D] fp32
  *   lse_partial  [B, q_per_req, Hq, num_splits]    fp32
@@ -69,6 +75,10 @@ extern "C" {
 /* element types */
 #define DA_FP32 0
 #define DA_BF16 1
+
+/* KV pool layouts within a page (see "Layouts" above) */
+#define DA_KV_NHD 0 /* [num_pages, page_size, Hkv, row] */
+#define DA_KV_HND 1 /* [num_pages, Hkv, page_size, row] */
 
 /* cu_seqlens_q modes (SGLang PR #29843 digest, "Implementation breakdown":
    preset / cumsum / strided) */
@@ -121,6 +131,7 @@ int32_t decode_attn_metadata(const int32_t* seq_lens, const int64_t* req_pool_in
  * kernels").  q and the pools share `dtype` (DA_BF16 or DA_FP32).
  *
  *   head_dim in {64, 128}; page_size in {16, 32, 64, 128, 256};
+ *   kv_layout DA_KV_NHD or DA_KV_HND (pool layout, see "Layouts");
  *   num_q_heads % num_kv_heads == 0; G * q_per_req <= DA_MAX_ROWS;
  *   1 <= num_splits <= DA_MAX_SPLITS; 1 <= q_per_req <= DA_MAX_Q_PER_REQ.
  *   page_table_stride >= max_pages >= 1.  cache_seqlens is the [batch] int32
@@ -136,8 +147,9 @@ int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool, cons
                           const int32_t* cache_seqlens, const int32_t* batch_order,
                           int32_t batch, int32_t q_per_req,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                          int32_t page_size, int32_t num_pages, int32_t num_splits,
-                          float softmax_scale, int32_t causal, float* o_partial,
+                          int32_t page_size, int32_t num_pages, int32_t kv_layout,
+                          int32_t num_splits, float softmax_scale, int32_t causal,
+                          float* o_partial,
                           float* lse_partial, void* stream);
 
 /*
@@ -155,8 +167,9 @@ int32_t decode_attn_split_int8(const void* q, int32_t q_dtype, const int8_t* k_p
                                const int32_t* cache_seqlens, const int32_t* batch_order,
                                int32_t batch, int32_t q_per_req,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                               int32_t page_size, int32_t num_pages, int32_t num_splits,
-                               float softmax_scale, int32_t causal, float* o_partial,
+                               int32_t page_size, int32_t num_pages, int32_t kv_layout,
+                               int32_t num_splits, float softmax_scale, int32_t causal,
+                               float* o_partial,
                                float* lse_partial, void* stream);
 
 /*
@@ -176,8 +189,9 @@ int32_t decode_attn_split_int4(const void* q, int32_t q_dtype, const uint8_t* k_
                                const int32_t* cache_seqlens, const int32_t* batch_order,
                                int32_t batch, int32_t q_per_req,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                               int32_t page_size, int32_t num_pages, int32_t num_splits,
-                               float softmax_scale, int32_t causal, float* o_partial,
+                               int32_t page_size, int32_t num_pages, int32_t kv_layout,
+                               int32_t num_splits, float softmax_scale, int32_t causal,
+                               float* o_partial,
                                float* lse_partial, void* stream);
 
 /*
@@ -209,15 +223,17 @@ int32_t decode_attn_pick_splits(const int32_t* table, const int32_t* batch_keys,
 
 /*
  * Test hook: dense copy of every request's tokens from a paged pool.
- * out row cu_seqlens_k[b] + t = pool token (page_table[b][t / page_size],
- * t % page_size) for t < cache_seqlens[b]; each token is `token_bytes`
- * bytes (a multiple of 4), e.g. Hkv*D*2 for bf16 K, Hkv*2 for int8 scales.
+ * out [total_tokens, Hkv, row_bytes]: entry (cu_seqlens_k[b] + t, g) = the
+ * pool row of (page page_table[b][t / page_size], slot t % page_size,
+ * kv-head g) for t < cache_seqlens[b], in either kv_layout; row_bytes is
+ * even (e.g. D*2 for bf16 K, 2 for int8 scales, 16 for int4 scale/zero).
  */
-int32_t decode_attn_gather_kv(const void* pool, int64_t token_bytes, int32_t page_size,
-                              int32_t num_pages, const int32_t* page_table,
-                              int32_t page_table_stride, int32_t max_pages,
-                              const int32_t* cache_seqlens, const int32_t* cu_seqlens_k,
-                              int32_t batch, void* out, void* stream);
+int32_t decode_attn_gather_kv(const void* pool, int64_t row_bytes, int32_t num_kv_heads,
+                              int32_t kv_layout, int32_t page_size, int32_t num_pages,
+                              const int32_t* page_table, int32_t page_table_stride,
+                              int32_t max_pages, const int32_t* cache_seqlens,
+                              const int32_t* cu_seqlens_k, int32_t batch, void* out,
+                              void* stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* decode_attn_strerror(int32_t status);

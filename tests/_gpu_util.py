@@ -110,17 +110,18 @@ def check_partials(o, l, o_ref, l_ref, label, o_extra=None):
 def host_inputs(batch: W.PagedBatch):
     """Full host copies (fp64 / raw) of a small batch for the oracle."""
     w = batch.w
+    nhd = batch.nhd  # the oracle reads pools as [P, page, Hkv, ...]
     d = dict(q=W.host_f64(batch.q), page_table=W.host_int(batch.page_table),
              seq_lens=W.host_int(batch.seq_lens))
     if w.kv == W.KV_DENSE:
-        d["k"] = W.host_f64(batch.k_pool)
-        d["v"] = W.host_f64(batch.v_pool)
+        d["k"] = W.host_f64(nhd(batch.k_pool))
+        d["v"] = W.host_f64(nhd(batch.v_pool))
     elif w.kv == W.KV_INT8:
-        d["k"] = OQ.dequant_int8(W.host_int(batch.k_pool), W.host_u16(batch.k_scale))
-        d["v"] = OQ.dequant_int8(W.host_int(batch.v_pool), W.host_u16(batch.v_scale))
+        d["k"] = OQ.dequant_int8(W.host_int(nhd(batch.k_pool)), W.host_u16(nhd(batch.k_scale)))
+        d["v"] = OQ.dequant_int8(W.host_int(nhd(batch.v_pool)), W.host_u16(nhd(batch.v_scale)))
     else:
-        d["k"] = OQ.dequant_int4(W.host_int(batch.k_pool), W.host_u16(batch.k_scale))
-        d["v"] = OQ.dequant_int4(W.host_int(batch.v_pool), W.host_u16(batch.v_scale))
+        d["k"] = OQ.dequant_int4(W.host_int(nhd(batch.k_pool)), W.host_u16(nhd(batch.k_scale)))
+        d["v"] = OQ.dequant_int4(W.host_int(nhd(batch.v_pool)), W.host_u16(nhd(batch.v_scale)))
     return d
 
 
@@ -158,7 +159,7 @@ def oracle_sampled(batch: W.PagedBatch, pairs):
         pt = np.arange(n, dtype=np.int64)[None, :] if n else np.zeros((1, 1), dtype=np.int64)
 
         def take(pool):
-            return pool.index_select(0, pages)[:, :, g:g + 1].contiguous()
+            return batch.nhd(pool).index_select(0, pages)[:, :, g:g + 1].contiguous()
 
         if w.kv == W.KV_DENSE:
             k = W.host_f64(take(batch.k_pool))
@@ -195,12 +196,13 @@ def fp16_pv_o_bound(batch: W.PagedBatch):
     """Per (request, query head) bound u*(2 max|v| + max|z*s|)*1.01 over the
     request's visible tokens, shaped [B, 1, Hq, 1, 1] (see the module notes)."""
     w = batch.w
+    vp, vs = batch.nhd(batch.v_pool), batch.nhd(batch.v_scale)
     if w.kv == W.KV_INT4:
-        v = OQ.dequant_int4(W.host_int(batch.v_pool), W.host_u16(batch.v_scale))
-        sz = OQ.fp16_bits_to_f64(W.host_u16(batch.v_scale))
+        v = OQ.dequant_int4(W.host_int(vp), W.host_u16(vs))
+        sz = OQ.fp16_bits_to_f64(W.host_u16(vs))
         zs = np.abs(sz[..., 0] * sz[..., 1])  # [P, ps, Hkv, D/32]
     else:
-        v = OQ.dequant_int8(W.host_int(batch.v_pool), W.host_u16(batch.v_scale))
+        v = OQ.dequant_int8(W.host_int(vp), W.host_u16(vs))
         zs = np.zeros(v.shape[:3] + (1,))
     pt = W.host_int(batch.page_table)
     L = W.host_int(batch.seq_lens)
@@ -222,17 +224,17 @@ def fp16_pv_o_bound(batch: W.PagedBatch):
 # ---------------------------------------------------------------- GPU path
 def run_split(da, batch: W.PagedBatch, S: int, batch_order=None):
     w = batch.w
+    kw = dict(batch_order=batch_order, kv_layout=w.kv_layout)
     if w.kv == W.KV_DENSE:
         return da.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, batch.page_table,
-                                    batch.seq_lens, S, w.softmax_scale, w.causal,
-                                    batch_order=batch_order)
+                                    batch.seq_lens, S, w.softmax_scale, w.causal, **kw)
     if w.kv == W.KV_INT8:
         return da.decode_attn_split_int8(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
                                          batch.v_scale, batch.page_table, batch.seq_lens, S,
-                                         w.softmax_scale, w.causal, batch_order=batch_order)
+                                         w.softmax_scale, w.causal, **kw)
     return da.decode_attn_split_int4(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
                                      batch.v_scale, batch.page_table, batch.seq_lens, S,
-                                     w.softmax_scale, w.causal, batch_order=batch_order)
+                                     w.softmax_scale, w.causal, **kw)
 
 
 def run_decode(da, batch: W.PagedBatch, S: int, out_dtype=torch.bfloat16, batch_order=None):

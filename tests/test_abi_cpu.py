@@ -50,16 +50,17 @@ def test_strerror_and_version(lib):
     assert lib.decode_attn_strerror(2) == b"unsupported shape or dtype"
     assert lib.decode_attn_strerror(3) == b"kernel launch failed"
     assert lib.decode_attn_strerror(99) == b"unknown status"
-    assert lib.decode_attn_version() == 100
+    assert lib.decode_attn_version() == 200
 
 
 def _split_args(**kw):
     a = dict(q=FAKE, dtype=B.DA_BF16, k=FAKE, v=FAKE, pt=FAKE, pt_stride=8, max_pages=8,
-             seqlens=FAKE, order=None, batch=4, qn=1, Hq=32, Hkv=8, D=128, ps=64, num_pages=100, S=4,
-             scale=0.1, causal=0, o=FAKE, lse=FAKE, stream=None)
+             seqlens=FAKE, order=None, batch=4, qn=1, Hq=32, Hkv=8, D=128, ps=64, num_pages=100,
+             layout=B.DA_KV_NHD, S=4, scale=0.1, causal=0, o=FAKE, lse=FAKE, stream=None)
     a.update(kw)
     return [a[k] for k in ("q", "dtype", "k", "v", "pt", "pt_stride", "max_pages", "seqlens",
-                           "order", "batch", "qn", "Hq", "Hkv", "D", "ps", "num_pages", "S", "scale",
+                           "order", "batch", "qn", "Hq", "Hkv", "D", "ps", "num_pages", "layout",
+                           "S", "scale",
                            "causal", "o", "lse", "stream")]
 
 
@@ -67,7 +68,7 @@ def _split_args(**kw):
     (dict(q=None), 1), (dict(o=None), 1), (dict(batch=0), 1), (dict(Hq=30), 1),
     (dict(S=0), 1), (dict(S=257), 1), (dict(qn=17), 1), (dict(pt_stride=4), 1),
     (dict(num_pages=0), 1), (dict(D=96), 2), (dict(ps=48), 2), (dict(ps=8), 2),
-    (dict(dtype=7), 2), (dict(Hq=64, Hkv=2, qn=2), 2),
+    (dict(dtype=7), 2), (dict(Hq=64, Hkv=2, qn=2), 2), (dict(layout=2), 1), (dict(layout=-1), 1),
 ])
 def test_split_validation(lib, kw, status):
     assert lib.decode_attn_split(*_split_args(**kw)) == status
@@ -99,8 +100,15 @@ def test_merge_and_metadata_and_gather_validation(lib):
     assert lib.decode_attn_metadata(*bad) == 1
     bad = list(md); bad[5] = 32  # stride < cols
     assert lib.decode_attn_metadata(*bad) == 1
-    g = [FAKE, 6, 16, 10, FAKE, 4, 4, FAKE, FAKE, 2, FAKE, None]
-    assert lib.decode_attn_gather_kv(*g) == 1  # token_bytes not a multiple of 4
+    # (pool, row_bytes, Hkv, layout, page_size, num_pages, pt, pt_stride, max_pages, seqlens,
+    #  cu_k, batch, out, stream)
+    g = [FAKE, 6, 2, B.DA_KV_NHD, 16, 10, FAKE, 4, 4, FAKE, FAKE, 2, FAKE, None]
+    bad = list(g); bad[1] = 5
+    assert lib.decode_attn_gather_kv(*bad) == 1  # odd row_bytes
+    bad = list(g); bad[3] = 2
+    assert lib.decode_attn_gather_kv(*bad) == 1  # unknown layout
+    bad = list(g); bad[2] = 0
+    assert lib.decode_attn_gather_kv(*bad) == 1  # no heads
 
 
 def test_pick_splits_buckets_and_nearest_key(lib):

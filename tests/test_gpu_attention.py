@@ -77,10 +77,18 @@ def test_tiny_fp32_every_split(gpu, S):
     U.check_bf16(U.to_np(out16), out_ref, f"tiny S={S} out bf16")
 
 
-@pytest.mark.parametrize("w", [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, MHA_P32, MTP_BF16,
-                               MTP_BF16_G2Q3, INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV,
-                               INT8_FP32Q, INT8_D64, INT4_SMALL, INT4_Q1, INT4_R12, INT4_G8Q2],
-                         ids=lambda w: w.name)
+SMALL = [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, MHA_P32, MTP_BF16, MTP_BF16_G2Q3,
+         INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV, INT8_FP32Q, INT8_D64, INT4_SMALL, INT4_Q1,
+         INT4_R12, INT4_G8Q2]
+
+
+def both_layouts(ws):
+    """Every case in the token-major (NHD) and the head-major (HND) pool layout."""
+    return [w.scaled(name=f"{w.name}_{lay.lower()}", kv_layout=lay) for w in ws
+            for lay in ("NHD", "HND")]
+
+
+@pytest.mark.parametrize("w", both_layouts(SMALL), ids=lambda w: w.name)
 @pytest.mark.parametrize("S", [1, 3, 8, 32])
 def test_small_elementwise(gpu, w, S):
     log(f"small {w.name} S={S}")
@@ -94,7 +102,7 @@ def test_small_elementwise(gpu, w, S):
     U.check_lse(U.to_np(lse), lse_ref, f"{w.name} S={S} lse")
 
 
-@pytest.mark.parametrize("w", [INT4_SMALL, INT4_Q1, INT4_R12], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", both_layouts([INT4_SMALL, INT4_Q1, INT4_R12]), ids=lambda w: w.name)
 def test_int4_fractional_zero_points(gpu, w):
     """The zero point is any fp16 value, not only a code: shift every zero by a
     fraction (different per slot) and compare with the oracle decoding the same
@@ -135,7 +143,7 @@ def test_page_permutation_is_bit_identical(gpu):
 
 def test_batch_order_is_bit_identical(gpu):
     """Scheduling requests longest-first (the metadata batch order) changes no bit."""
-    for w in (RAGGED_SMALL, INT8_SMALL, INT8_ODD_HKV, INT4_SMALL, MTP_BF16):
+    for w in both_layouts([RAGGED_SMALL, INT8_SMALL, INT8_ODD_HKV, INT4_SMALL, MTP_BF16]):
         log(f"batch order {w.name}")
         batch = W.make_batch(w, device="cuda")
         md = gpu.decode_attn_metadata(batch.seq_lens, batch.req_pool_indices, batch.req_to_token,
@@ -167,25 +175,37 @@ def test_outputs_fully_overwritten(gpu):
     o = torch.full((B, qn, Hq, S, D), float("nan"), device="cuda")
     l = torch.full((B, qn, Hq, S), float("nan"), device="cuda")
     gpu.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, batch.page_table, batch.seq_lens,
-                          S, w.softmax_scale, False, o_partial=o, lse_partial=l)
+                          S, w.softmax_scale, False, o_partial=o, lse_partial=l,
+                          kv_layout=w.kv_layout)
     assert not torch.isnan(o).any() and not torch.isnan(l).any()
 
 
-def test_nan_in_unused_slots_does_not_leak(gpu):
+@pytest.mark.parametrize("w", both_layouts([RAGGED_SMALL.scaled(pool_pages=200),
+                                             INT8_SMALL.scaled(pool_pages=80),
+                                             INT4_SMALL.scaled(pool_pages=80)]),
+                         ids=lambda w: w.name)
+def test_nan_in_unused_slots_does_not_leak(gpu, w):
     """Slots past a request's length (tail of its last page, unused pages) may hold
-    anything; fill them with NaN and check the output is unchanged."""
-    w = RAGGED_SMALL.scaled(pool_pages=200)
+    anything: NaN in dense pools, NaN scales and arbitrary codes in quantised ones.
+    Poison them and check the output is bit-identical."""
     batch = W.make_batch(w, device="cuda")
     ref, _, _, _ = U.run_decode(gpu, batch, 4)
     L = batch.lengths
     pt = batch.page_table.cpu().numpy()
     used = torch.zeros(batch.num_pages, w.page_size, dtype=torch.bool)
     for b in range(len(L)):
-        for t in range(int(L[b])):
-            used[pt[b, t // w.page_size], t % w.page_size] = True
-    mask = (~used).cuda()
-    batch.k_pool[mask] = float("nan")
-    batch.v_pool[mask] = float("nan")
+        t = np.arange(int(L[b]))
+        used[pt[b, t // w.page_size], t % w.page_size] = True
+    mask = (~used).cuda()  # [P, page] slots; nhd() views the pools in that order
+    if w.kv == W.KV_DENSE:
+        batch.nhd(batch.k_pool)[mask] = float("nan")
+        batch.nhd(batch.v_pool)[mask] = float("nan")
+    else:
+        for sc in (batch.k_scale, batch.v_scale):
+            batch.nhd(sc)[mask] = float("nan")
+        for pool in (batch.k_pool, batch.v_pool):
+            junk = torch.randint(0, 256, pool.shape, dtype=torch.uint8, device="cuda").view(pool.dtype)
+            batch.nhd(pool)[mask] = batch.nhd(junk)[mask]
     out, _, _, _ = U.run_decode(gpu, batch, 4)
     assert torch.equal(out, ref)
 

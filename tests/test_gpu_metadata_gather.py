@@ -84,10 +84,14 @@ def test_metadata_sentinels_and_wide_rows():
         _check_md_against_oracle(seq, rpi, r2t, ps, mp, 0, None, 2)
 
 
-@pytest.mark.parametrize("w", [W.TINY_FP32, W.BF16_B16.scaled(batch=6, lengths="list",
-                                                              length_list=(1, 63, 64, 65, 700, 0)),
-                               W.INT8_B32.scaled(batch=3, length=333),
-                               W.INT4_MTP_B64.scaled(batch=3, length_lo=100, length_hi=900)],
+_GATHER = [W.TINY_FP32, W.BF16_B16.scaled(batch=6, lengths="list",
+                                          length_list=(1, 63, 64, 65, 700, 0)),
+           W.INT8_B32.scaled(batch=3, length=333),
+           W.INT4_MTP_B64.scaled(batch=3, length_lo=100, length_hi=900)]
+
+
+@pytest.mark.parametrize("w", [w.scaled(name=f"{w.name}_{lay}", kv_layout=lay)
+                               for w in _GATHER for lay in ("NHD", "HND")],
                          ids=lambda w: w.name)
 def test_gather_is_bit_exact(w):
     log(f"gather {w.name}")
@@ -101,8 +105,8 @@ def test_gather_is_bit_exact(w):
     pools = [batch.k_pool, batch.v_pool] + [t for t in (batch.k_scale, batch.v_scale) if t is not None]
     for pool in pools:
         got = gpu_mod.decode_attn_gather_kv(pool, md["page_table"], md["cache_seqlens"],
-                                            md["cu_seqlens_k"], total).cpu()
-        host = pool.cpu()
+                                            md["cu_seqlens_k"], total, kv_layout=w.kv_layout).cpu()
+        host = batch.nhd(pool).contiguous().cpu()  # the oracle reads [P, page, Hkv, ...]
         # compare raw bytes: oracle gather applied to the host copy, request by request
         raw = host.view(torch.uint8).numpy().reshape(host.shape[0], host.shape[1], -1)
         off = 0
