@@ -83,8 +83,8 @@ def algorithmic_bytes(w, lengths, out_elem=2):
 # taken on a kernel stay valid only while these files are unchanged)
 KERNEL_SOURCES = {"bf16": ["split_bf16.hip", "common.h"],
                   "fp32": ["split_fma.hip", "common.h"],
-                  "int8": ["split_int8.hip", "split_fma.hip", "common.h"],
-                  "int4": ["split_int4.hip", "split_fma.hip", "common.h"]}
+                  "int8": ["split_int8.hip", "mfma_util.h", "split_fma.hip", "common.h"],
+                  "int4": ["split_int4.hip", "mfma_util.h", "split_fma.hip", "common.h"]}
 
 
 def kernel_hash(kv="bf16") -> str:
@@ -259,7 +259,8 @@ def tune(da, torch, which="all"):
         keep = set(which.split(","))
         variants = [v for v in variants if kv_name(v) in keep]
     for base in variants:
-        key = kernel_key(kv_name(base), rows_per_kv_head(base), base.head_dim, base.page_size)
+        key = kernel_key(kv_name(base), rows_per_kv_head(base), base.head_dim, base.page_size,
+                         base.kv_layout)
         rows = []
         for bk in BATCH_KEYS:
             row = []
@@ -389,7 +390,7 @@ def main():
         return
     w = W.WORKLOADS[args.workload]
     batch = make_resident(da, w, torch)
-    key = kernel_key(kv_name(w), rows_per_kv_head(w), w.head_dim, w.page_size)
+    key = kernel_key(kv_name(w), rows_per_kv_head(w), w.head_dim, w.page_size, w.kv_layout)
     S = args.splits or SplitTable.load().pick(key, w.batch, int(batch.lengths.max()))
     if args.profile_only:
         profile_only(da, w, batch, S, args.steps, torch)
@@ -401,7 +402,7 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         t = json.load(open(TRAFFIC_FILE))
-        ent = t.get(w.name)
+        ent = t.get(f"{w.name}/{w.kv_layout}")
         if ent and ent.get("kernel_hash") == kernel_hash(kv_name(w)) and ent.get("num_splits") == S:
             traffic = ent.get("hbm_bytes_per_launch")
     res = {

@@ -27,9 +27,10 @@ BATCH_KEYS = (16, 32, 64)
 CANDIDATES = (1, 2, 4, 8, 16, 32)
 
 
-def kernel_key(kv: str, rows: int, head_dim: int, page_size: int) -> str:
-    """Table key of a stage-1 variant: cache format, query rows per kv-head, D, page size."""
-    return f"{kv}_r{rows}_d{head_dim}_p{page_size}"
+def kernel_key(kv: str, rows: int, head_dim: int, page_size: int, kv_layout: str = "NHD") -> str:
+    """Table key of a stage-1 variant: cache format, query rows per kv-head, D, page size,
+    pool layout."""
+    return f"{kv}_r{rows}_d{head_dim}_p{page_size}_{kv_layout.lower()}"
 
 
 def _heuristic(batch_key: int, bucket: int, num_kv_heads: int = 8, cus: int = 256) -> int:

@@ -134,6 +134,7 @@ def test_pick_splits_buckets_and_nearest_key(lib):
 
 
 def test_split_table_roundtrip(tmp_path, lib):
+    assert kernel_key("int4", 16, 128, 64, "HND") == "int4_r16_d128_p64_hnd"
     t = SplitTable()
     key = kernel_key("bf16", 5, 128, 64)
     t.tables[key] = [[1, 2, 4, 4, 8, 8, 16, 16]] * 3
