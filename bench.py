@@ -8,7 +8,11 @@ prelude (cache_seqlens / cu_seqlens_k/q / page_table in one launch), the
 split-count lookup, stage 1 (split) and stage 2 (LSE merge).  Inputs are
 resident in HBM before the timed region.  Prints ONE JSON line.
 
-value      = algorithmic bytes of one step / measured step time (GB/s)
+value      = algorithmic bytes of one step / measured step time (GB/s), the K
+             steps launched eagerly on one stream; the same step captured once
+             in a HIP graph (num_splits fixed at capture) and replayed K times
+             is reported beside it as graph_ms_per_step
+
 roofline   = the stage-1 kernel: algorithmic bytes per launch / its average
              launch time from HIP events on the launch stream, against
              MI355X's 8 TB/s HBM peak.
@@ -97,11 +101,11 @@ def kernel_hash(kv="bf16") -> str:
     return h.hexdigest()[:16]
 
 
-def stage1(da, batch, S, o, l):
+def stage1(da, batch, S, o, l, md=None):
     from decode_attention_paged_gqa_amd import workloads as W
 
     w = batch.w
-    md = batch.md
+    md = batch.md if md is None else md
     if w.kv == W.KV_DENSE:
         return da.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, md["page_table"],
                                     md["cache_seqlens"], S, w.softmax_scale, w.causal, o, l,
@@ -165,6 +169,38 @@ def time_config(da, batch, S, steps, warmup, torch):
     split = np.mean([e[1].elapsed_time(e[2]) for e in evs])
     merge = np.mean([e[2].elapsed_time(e[3]) for e in evs])
     return wall_ms, float(split), float(merge), float(meta)
+
+
+def time_graph(da, batch, S, steps, warmup, torch):
+    """The same step captured once in a HIP graph (S fixed at capture, as the pages
+    deploy their tuned kernels) and replayed; returns ms per replayed step."""
+    w = batch.w
+    B, qn, Hq, D = batch.q.shape
+    o = torch.empty((B, qn, Hq, S, D), dtype=torch.float32, device="cuda")
+    l = torch.empty((B, qn, Hq, S), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, qn, Hq, D), dtype=torch.bfloat16, device="cuda")
+    md_out = {k: torch.empty_like(v) for k, v in batch.md.items()}
+
+    def step():
+        da.decode_attn_metadata(batch.seq_lens, batch.req_pool_indices, batch.req_to_token,
+                                w.page_size, batch.max_pages, q_stride=w.q_per_req, out=md_out)
+        stage1(da, batch, S, o, l, md=md_out)
+        da.decode_attn_merge(o, l, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
 
 def time_split_only(da, batch, S, iters, torch):
@@ -396,6 +432,12 @@ def main():
         profile_only(da, w, batch, S, args.steps, torch)
         return
     ms, split_ms, merge_ms, meta_ms = time_config(da, batch, S, args.steps, args.warmup, torch)
+    # the same step captured once in a HIP graph and replayed (reported beside it)
+    try:
+        graph_ms = time_graph(da, batch, S, args.steps, args.warmup, torch)
+    except Exception as e:
+        print(f"bench.py: graph capture failed ({e})", file=sys.stderr)
+        graph_ms = None
     ab = algorithmic_bytes(w, batch.lengths)
     value = ab["step"] / (ms * 1e-3) / 1e9
     achieved = ab["split"] / (split_ms * 1e-3) / 1e9
@@ -414,6 +456,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "us_per_call": round(ms * 1e3, 2),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
