@@ -199,13 +199,13 @@ def _to_dtype(x: torch.Tensor, dtype: str) -> torch.Tensor:
 def quantize_int8(x: torch.Tensor):
     """Symmetric int8 with one fp16 scale per row of the last dim.
 
-    s = fp16(amax / 127) (1 where amax == 0), code = clamp(rne(x / s), -127, 127).
+    s = fp16(amax / 127) (1 where that is 0), code = clamp(rne(x / s), -127, 127).
     Test-data encoder only.
     """
     xf = x.to(torch.float32)
     amax = xf.abs().amax(dim=-1)
     s = (amax / 127.0).to(torch.float16)
-    s = torch.where(amax == 0, torch.ones_like(s), s)
+    s = torch.where(s == 0, torch.ones_like(s), s)
     code = torch.clamp(torch.round(xf / s.to(torch.float32).unsqueeze(-1)), -127, 127)
     return code.to(torch.int8), s
 
@@ -213,7 +213,7 @@ def quantize_int8(x: torch.Tensor):
 def quantize_int4(x: torch.Tensor, group: int = INT4_GROUP):
     """Asymmetric 4-bit with fp16 (scale, zero) per group of ``group`` along D.
 
-    s = fp16((max - min) / 15) (1 where 0); z = fp16(clamp(rne(-min / s), 0, 15));
+    s = fp16((max - min) / 15) (1 where that is 0); z = fp16(clamp(rne(-min / s), 0, 15));
     nib = clamp(rne(x / s) + z, 0, 15); byte j = nib[2j] | nib[2j+1] << 4.
     Returns (packed uint8 [..., D/2], scale_zero fp16 [..., D/group, 2]).
     Test-data encoder only.
@@ -224,7 +224,7 @@ def quantize_int4(x: torch.Tensor, group: int = INT4_GROUP):
     mn = g.amin(dim=-1)
     mx = g.amax(dim=-1)
     s = ((mx - mn) / 15.0).to(torch.float16)
-    s = torch.where(mx == mn, torch.ones_like(s), s)
+    s = torch.where(s == 0, torch.ones_like(s), s)
     sf = s.to(torch.float32)
     z = torch.clamp(torch.round(-mn / sf), 0, 15).to(torch.float16)
     nib = torch.clamp(torch.round(g / sf.unsqueeze(-1)) + z.to(torch.float32).unsqueeze(-1), 0, 15)

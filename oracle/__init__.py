@@ -9,5 +9,6 @@ Modules:
   attention -- gather, softmax attention, split partials, LSE merge (float64)
   metadata  -- cache_seqlens / cu_seqlens_k / cu_seqlens_q / page_table (exact ints)
   quant     -- fp64 decoders of the INT8 / INT4 KV formats
+  kvcache   -- appending new tokens at their slots, with the INT8 / INT4 encoders
 """
-from . import attention, metadata, quant  # noqa: F401
+from . import attention, kvcache, metadata, quant  # noqa: F401

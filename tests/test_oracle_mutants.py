@@ -12,8 +12,10 @@ import types
 import pytest
 
 import oracle.attention as real_attention
+import oracle.kvcache as real_kvcache
 import oracle.metadata as real_metadata
 from tests import test_oracle_attention as TA
+from tests import test_oracle_kvcache as TK
 from tests import test_oracle_metadata as TM
 
 ATTENTION_MUTANTS = [
@@ -45,6 +47,23 @@ METADATA_MUTANTS = [
      "cu_q = [(b + 1) * int(q_stride) for b in range(B + 1)]"),
     ("order ascending", "key=lambda b: (-cache[b], b)", "key=lambda b: (cache[b], b)"),
     ("order ties reversed", "key=lambda b: (-cache[b], b)", "key=lambda b: (-cache[b], -b)"),
+]
+
+
+KVCACHE_MUTANTS = [
+    ("int8 scale /128", "s = _fp16_scale(amax / _F32(127.0))", "s = _fp16_scale(amax / _F32(128.0))"),
+    ("int8 floor", "q = np.rint(xf / s.astype(_F32)[..., None])", "q = np.floor(xf / s.astype(_F32)[..., None])"),
+    ("no zero-scale guard", "return np.where(s == 0, np.float16(1.0), s)", "return s"),
+    ("int4 scale /16", "s = _fp16_scale((mx - mn) / _F32(15.0))", "s = _fp16_scale((mx - mn) / _F32(16.0))"),
+    ("int4 zero sign", "z = np.clip(np.rint(-mn / sf), 0, 15)", "z = np.clip(np.rint(mn / sf), 0, 15)"),
+    ("int4 zero not added", "np.rint(g / sf[..., None]) + z.astype(_F32)[..., None]",
+     "np.rint(g / sf[..., None])"),
+    ("int4 nibble order", "(nib[..., 0::2] | (nib[..., 1::2] << 4))", "(nib[..., 1::2] | (nib[..., 0::2] << 4))"),
+    ("int4 zero floor", "z = np.clip(np.rint(-mn / sf), 0, 15)", "z = np.clip(np.floor(-mn / sf), 0, 15)"),
+    ("append page/offset swapped", "p, t = int(slot) // page_size, int(slot) % page_size",
+     "t, p = int(slot) // page_size, int(slot) % page_size"),
+    ("append past the pool", "if slot < 0 or slot >= P * page_size:", "if slot < 0:"),
+    ("append sentinel", "if slot < 0 or slot >= P * page_size:", "if slot >= P * page_size:"),
 ]
 
 
@@ -82,6 +101,20 @@ def _metadata_pins():
     return pins
 
 
+def _kvcache_pins():
+    pins = [lambda a=a: TK.test_int8_hand_rows(*a) for a in [
+        ([0.0, 1.0, -1.0, 2.5, 127.0], 1.0, [0, 1, -1, 2, 127]),
+        ([254.0, -3.0, 1.5, -0.5], 2.0, [127, -2, 1, 0]),
+        ([0.0, 0.0, 0.0], 1.0, [0, 0, 0]),
+        ([1e-9, -1e-9], 1.0, [0, 0])]]
+    pins += [TK.test_int4_hand_row_rounding_zero_clamp_and_nibble_order,
+             TK.test_int4_all_equal_groups_decode_exactly, TK.test_int8_roundtrip_within_half_step,
+             TK.test_int4_roundtrip_within_half_step,
+             TK.test_append_writes_only_valid_slots_at_page_and_offset,
+             TK.test_append_quantises_each_row_with_its_encoder]
+    return pins
+
+
 def _some_pin_fails(pins):
     for p in pins:
         try:
@@ -94,6 +127,7 @@ def _some_pin_fails(pins):
 def test_real_oracle_passes_every_pin():
     assert not _some_pin_fails(_attention_pins())
     assert not _some_pin_fails(_metadata_pins())
+    assert not _some_pin_fails(_kvcache_pins())
 
 
 @pytest.mark.parametrize("name,old,new", ATTENTION_MUTANTS, ids=[m[0] for m in ATTENTION_MUTANTS])
@@ -106,3 +140,9 @@ def test_attention_mutant_is_caught(monkeypatch, name, old, new):
 def test_metadata_mutant_is_caught(monkeypatch, name, old, new):
     monkeypatch.setattr(TM, "OM", _mutant(real_metadata, old, new))
     assert _some_pin_fails(_metadata_pins()), f"no pin caught mutant '{name}'"
+
+
+@pytest.mark.parametrize("name,old,new", KVCACHE_MUTANTS, ids=[m[0] for m in KVCACHE_MUTANTS])
+def test_kvcache_mutant_is_caught(monkeypatch, name, old, new):
+    monkeypatch.setattr(TK, "OK", _mutant(real_kvcache, old, new))
+    assert _some_pin_fails(_kvcache_pins()), f"no pin caught mutant '{name}'"
