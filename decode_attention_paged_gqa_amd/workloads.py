@@ -226,7 +226,7 @@ def quantize_int4(x: torch.Tensor, group: int = INT4_GROUP):
     s = ((mx - mn) / 15.0).to(torch.float16)
     s = torch.where(s == 0, torch.ones_like(s), s)
     sf = s.to(torch.float32)
-    z = torch.clamp(torch.round(-mn / sf), 0, 15).to(torch.float16)
+    z = (torch.clamp(torch.round(-mn / sf), 0, 15) + 0.0).to(torch.float16)  # -0 -> +0
     nib = torch.clamp(torch.round(g / sf.unsqueeze(-1)) + z.to(torch.float32).unsqueeze(-1), 0, 15)
     nib = nib.to(torch.uint8).reshape(*xf.shape[:-1], D)
     packed = nib[..., 0::2] | (nib[..., 1::2] << 4)

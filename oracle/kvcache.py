@@ -15,7 +15,8 @@ rounding decision is taken in IEEE fp32, as a kernel would take it):
   bf16 / fp32 input):  s = fp16(max|x| / 127), and s = 1 if that fp16 value
   is 0;  code = clamp(rne(x / s), -127, 127).
 * INT4, per group of 32 along D:  s = fp16((max - min) / 15), and s = 1 if
-  that fp16 value is 0;  z = fp16(clamp(rne(-min / s), 0, 15));
+  that fp16 value is 0;  z = fp16(clamp(rne(-min / s), 0, 15)), an integer
+  code stored as +0 when it is zero (rounding a small positive min gives -0);
   nib = clamp(rne(x / s) + z, 0, 15);  byte j = nib[2j] | nib[2j+1] << 4.
 * dense (bf16 / fp32): the values are stored unchanged.
 * A negative slot, or one at or past ``num_pages * page_size``, writes
@@ -58,7 +59,7 @@ def quantize_int4(x: np.ndarray):
     mx = g.max(axis=-1)
     s = _fp16_scale((mx - mn) / _F32(15.0))
     sf = s.astype(_F32)
-    z = np.clip(np.rint(-mn / sf), 0, 15).astype(np.float16)
+    z = (np.clip(np.rint(-mn / sf), 0, 15) + _F32(0.0)).astype(np.float16)  # -0 -> +0
     nib = np.clip(np.rint(g / sf[..., None]) + z.astype(_F32)[..., None], 0, 15)
     nib = nib.astype(np.uint8).reshape(xf.shape)
     packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)

@@ -60,6 +60,13 @@ def test_int4_hand_row_rounding_zero_clamp_and_nibble_order():
     np.testing.assert_array_equal(s, sz)
 
 
+def test_int4_zero_point_zero_is_stored_as_plus_zero():
+    # min = 0.01, s ~ 0.1993: -min / s = -0.05 rounds to -0 -> the code 0 is stored as +0
+    x = np.linspace(0.01, 3.0, 32, dtype=np.float32)
+    _, sz = OK.quantize_int4(x)
+    assert sz[0, 1].view(np.uint16) == 0
+
+
 def test_int4_all_equal_groups_decode_exactly():
     x, _, _ = _int4_hand_row()
     p, s = OK.quantize_int4(x)

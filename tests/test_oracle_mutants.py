@@ -55,11 +55,12 @@ KVCACHE_MUTANTS = [
     ("int8 floor", "q = np.rint(xf / s.astype(_F32)[..., None])", "q = np.floor(xf / s.astype(_F32)[..., None])"),
     ("no zero-scale guard", "return np.where(s == 0, np.float16(1.0), s)", "return s"),
     ("int4 scale /16", "s = _fp16_scale((mx - mn) / _F32(15.0))", "s = _fp16_scale((mx - mn) / _F32(16.0))"),
-    ("int4 zero sign", "z = np.clip(np.rint(-mn / sf), 0, 15)", "z = np.clip(np.rint(mn / sf), 0, 15)"),
+    ("int4 zero sign", "z = (np.clip(np.rint(-mn / sf), 0, 15)", "z = (np.clip(np.rint(mn / sf), 0, 15)"),
     ("int4 zero not added", "np.rint(g / sf[..., None]) + z.astype(_F32)[..., None]",
      "np.rint(g / sf[..., None])"),
     ("int4 nibble order", "(nib[..., 0::2] | (nib[..., 1::2] << 4))", "(nib[..., 1::2] | (nib[..., 0::2] << 4))"),
-    ("int4 zero floor", "z = np.clip(np.rint(-mn / sf), 0, 15)", "z = np.clip(np.floor(-mn / sf), 0, 15)"),
+    ("int4 zero floor", "z = (np.clip(np.rint(-mn / sf), 0, 15)", "z = (np.clip(np.floor(-mn / sf), 0, 15)"),
+    ("int4 zero keeps -0", "+ _F32(0.0)).astype(np.float16)", ").astype(np.float16)"),
     ("append page/offset swapped", "p, t = int(slot) // page_size, int(slot) % page_size",
      "t, p = int(slot) // page_size, int(slot) % page_size"),
     ("append past the pool", "if slot < 0 or slot >= P * page_size:", "if slot < 0:"),
@@ -108,6 +109,7 @@ def _kvcache_pins():
         ([0.0, 0.0, 0.0], 1.0, [0, 0, 0]),
         ([1e-9, -1e-9], 1.0, [0, 0])]]
     pins += [TK.test_int4_hand_row_rounding_zero_clamp_and_nibble_order,
+             TK.test_int4_zero_point_zero_is_stored_as_plus_zero,
              TK.test_int4_all_equal_groups_decode_exactly, TK.test_int8_roundtrip_within_half_step,
              TK.test_int4_roundtrip_within_half_step,
              TK.test_append_writes_only_valid_slots_at_page_and_offset,
