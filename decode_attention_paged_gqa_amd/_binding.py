@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_LAUNCH = 0, 1, 2, 3
 DA_FP32, DA_BF16 = 0, 1
 DA_KV_NHD, DA_KV_HND = 0, 1
+DA_CACHE_DENSE, DA_CACHE_INT8, DA_CACHE_INT4 = 0, 1, 2
+CACHE_FORMATS = {"dense": DA_CACHE_DENSE, "int8": DA_CACHE_INT8, "int4": DA_CACHE_INT4}
 KV_LAYOUTS = {"NHD": DA_KV_NHD, "HND": DA_KV_HND}
 DA_Q_STRIDED, DA_Q_CUMSUM, DA_Q_PRESET = 0, 1, 2
 DA_MAX_SPLITS = 256
@@ -42,6 +44,8 @@ _SIGS = {
     "decode_attn_split_int4": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I32,
                                _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
     "decode_attn_merge": [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P],
+    "decode_attn_append_kv": [_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32,
+                              _I32, _P],
     "decode_attn_pick_splits": [_P, _P, _I32, _I32, _I32, _I32, _I32],
     "decode_attn_gather_kv": [_P, _I64, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _I32,
                               _P, _P],
@@ -286,6 +290,45 @@ def decode_attn_split_int4(q, k_pool, v_pool, k_scale_zero, v_scale_zero, page_t
         _ptr(lse_partial), _stream(dev))
     _check(st, "decode_attn_split_int4")
     return o_partial, lse_partial
+
+
+# ------------------------------------------------------------------ KV append
+def decode_attn_append_kv(k_new, v_new, out_cache_loc, k_pool, v_pool, k_scale=None,
+                          v_scale=None, cache_format="dense", kv_layout="NHD"):
+    """Write the new tokens' K/V [N, Hkv, D] into the pools at ``out_cache_loc`` (int64
+    token slots), encoding them for "int8" / "int4" caches.  Pools and scales are
+    updated in place, in the layout the split calls read (kv_layout)."""
+    lib = load()
+    _need(k_new, "k_new", (torch.bfloat16, torch.float32), ndim=3)
+    dev = k_new.device
+    _need(v_new, "v_new", k_new.dtype, dev, 3)
+    _need(out_cache_loc, "out_cache_loc", torch.int64, dev, 1)
+    if v_new.shape != k_new.shape or out_cache_loc.shape[0] != k_new.shape[0]:
+        raise ValueError("k_new / v_new / out_cache_loc sizes differ")
+    N, Hkv, D = k_new.shape
+    fmt = CACHE_FORMATS.get(cache_format) if isinstance(cache_format, str) else int(cache_format)
+    if fmt is None:
+        raise ValueError(f"cache_format must be one of {tuple(CACHE_FORMATS)}")
+    lay = _layout_code(kv_layout)
+    pool_dtype = {DA_CACHE_DENSE: k_new.dtype, DA_CACHE_INT8: torch.int8,
+                  DA_CACHE_INT4: torch.uint8}[fmt]
+    row = {DA_CACHE_DENSE: (D,), DA_CACHE_INT8: (D,), DA_CACHE_INT4: (D // 2,)}[fmt]
+    _need(k_pool, "k_pool", pool_dtype, dev, 4)
+    _need(v_pool, "v_pool", pool_dtype, dev, 4)
+    P, S_p, Hp = _pool_dims(k_pool, lay)
+    if v_pool.shape != k_pool.shape or Hp != Hkv or tuple(k_pool.shape[3:]) != row:
+        raise ValueError("pool shape does not match the new rows")
+    if fmt != DA_CACHE_DENSE:
+        nd = 3 if fmt == DA_CACHE_INT8 else 5
+        _need(k_scale, "k_scale", torch.float16, dev, nd)
+        _need(v_scale, "v_scale", torch.float16, dev, nd)
+        want = tuple(k_pool.shape[:3]) + (() if fmt == DA_CACHE_INT8 else (D // 32, 2))
+        if tuple(k_scale.shape) != want or v_scale.shape != k_scale.shape:
+            raise ValueError(f"scale shape must be {want}")
+    st = lib.decode_attn_append_kv(_ptr(k_new), _ptr(v_new), _q_code(k_new), _ptr(out_cache_loc),
+                                   N, Hkv, D, fmt, _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                   _ptr(v_scale), S_p, P, lay, _stream(dev))
+    _check(st, "decode_attn_append_kv")
 
 
 # ------------------------------------------------------------------ stage 2

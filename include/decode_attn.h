@@ -14,6 +14,8 @@
  *              softmax-normalised partial output of the G*q query rows that
  *              share kv-head g over the split's tokens, and its log-sum-exp.
  *   merge    : stage 2.  Combines the splits of every query row by their LSE.
+ *   append   : writes the step's new K/V rows into the pool at their slots,
+ *              encoding them for the INT8 / INT4 caches (the step before).
  *
  * Attention is out = softmax(scale * q K^T) V per query head h, with h reading
  * kv-head h / G (G = Hq / Hkv).  With q_per_req > 1 (MTP verify) and causal
@@ -75,6 +77,11 @@ extern "C" {
 /* element types */
 #define DA_FP32 0
 #define DA_BF16 1
+
+/* cache formats of decode_attn_append_kv */
+#define DA_CACHE_DENSE 0 /* rows stored as given (pool dtype = the new K/V's dtype) */
+#define DA_CACHE_INT8 1  /* int8 codes + one fp16 scale per row                     */
+#define DA_CACHE_INT4 2  /* 4-bit codes + fp16 (scale, zero) per 32-group           */
 
 /* KV pool layouts within a page (see "Layouts" above) */
 #define DA_KV_NHD 0 /* [num_pages, page_size, Hkv, row] */
@@ -193,6 +200,35 @@ int32_t decode_attn_split_int4(const void* q, int32_t q_dtype, const uint8_t* k_
                                int32_t num_splits, float softmax_scale, int32_t causal,
                                float* o_partial,
                                float* lse_partial, void* stream);
+
+/*
+ * KV append with quantise-on-write: writes the new tokens' K and V rows to
+ * their token slots before attention runs (SGLang PR #29843 digest, test
+ * listing: one out_cache_loc slot per new token; LightLLM PR #1549, "Covered
+ * decode kernels": INT8 / INT4 KV caches).
+ *   k_new, v_new   [num_tokens, Hkv, head_dim], new_dtype DA_BF16 or DA_FP32
+ *   out_cache_loc  [num_tokens] int64 token slots; slot = page * page_size +
+ *                  offset.  A negative slot, or one >= num_pages * page_size,
+ *                  writes nothing (the -1 sentinel of padded batches).  Slots
+ *                  are the caller's to keep distinct; with repeats the result
+ *                  is unspecified.
+ *   cache_format   DA_CACHE_DENSE: pools hold new_dtype, rows copied bit for bit;
+ *                  DA_CACHE_INT8: per row s = fp16(max|x| / 127) (1 if that is
+ *                    0), code = clamp(rne(x / s), -127, 127), scale -> k/v_scale;
+ *                  DA_CACHE_INT4: per 32-group s = fp16((max - min) / 15) (1 if
+ *                    0), z = fp16(clamp(rne(-min / s), 0, 15)) (+0 for 0),
+ *                    nibble = clamp(rne(x / s) + z, 0, 15), (s, z) -> k/v_scale.
+ *                  All decisions in IEEE fp32 (the codes are reproducible).
+ *   pools / scales in the layouts of the split calls (kv_layout NHD or HND);
+ *   k_scale, v_scale may be NULL for DA_CACHE_DENSE.
+ *   head_dim in {64, 128}.  num_tokens == 0 enqueues nothing.
+ */
+int32_t decode_attn_append_kv(const void* k_new, const void* v_new, int32_t new_dtype,
+                              const int64_t* out_cache_loc, int32_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t cache_format,
+                              void* k_pool, void* v_pool, uint16_t* k_scale, uint16_t* v_scale,
+                              int32_t page_size, int32_t num_pages, int32_t kv_layout,
+                              void* stream);
 
 /*
  * Stage 2: LSE merge (LightLLM PR #1549, "Covered decode kernels": the

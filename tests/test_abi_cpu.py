@@ -111,6 +111,25 @@ def test_merge_and_metadata_and_gather_validation(lib):
     assert lib.decode_attn_gather_kv(*bad) == 1  # no heads
 
 
+def test_append_validation(lib):
+    # (k_new, v_new, new_dtype, loc, N, Hkv, D, fmt, k_pool, v_pool, k_scale, v_scale,
+    #  page_size, num_pages, layout, stream)
+    a = [FAKE, FAKE, B.DA_BF16, FAKE, 4, 8, 128, B.DA_CACHE_INT8, FAKE, FAKE, FAKE, FAKE, 64, 10,
+         B.DA_KV_HND, None]
+    def bad(i, v):
+        b = list(a); b[i] = v
+        return lib.decode_attn_append_kv(*b)
+    assert bad(4, -1) == 1       # negative token count
+    assert bad(5, 0) == 1        # no heads
+    assert bad(2, 9) == 2        # dtype
+    assert bad(6, 96) == 2       # head_dim
+    assert bad(7, 3) == 1        # cache format
+    assert bad(14, 5) == 1       # layout
+    assert bad(10, None) == 1    # int8 needs scales
+    assert bad(3, None) == 1     # no slots
+    assert bad(4, 0) == 0        # nothing to do: OK, nothing enqueued
+
+
 def test_pick_splits_buckets_and_nearest_key(lib):
     table = [[1, 2, 3, 4, 5, 6, 7, 8], [11, 12, 13, 14, 15, 16, 17, 18], [21, 22, 23, 24, 25, 26, 27, 28]]
     keys = [16, 32, 64]
