@@ -10,5 +10,6 @@ Modules:
   metadata  -- cache_seqlens / cu_seqlens_k / cu_seqlens_q / page_table (exact ints)
   quant     -- fp64 decoders of the INT8 / INT4 KV formats
   kvcache   -- appending new tokens at their slots, with the INT8 / INT4 encoders
+  schedule  -- per-request split counts and the flattened stage-1 work list (exact ints)
 """
-from . import attention, kvcache, metadata, quant  # noqa: F401
+from . import attention, kvcache, metadata, quant, schedule  # noqa: F401

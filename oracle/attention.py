@@ -159,12 +159,14 @@ def split_token_range(L: int, page_size: int, num_splits: int, s: int):
 
 
 def split_partials(q, k_pool, v_pool, page_table, seq_lens, page_size, scale,
-                   num_splits, causal=False):
+                   num_splits, causal=False, split_counts=None):
     """Stage 1: per-split normalised partial outputs and their LSE.
 
     o_partial [B, qn, Hq, S, D] = softmax over the split's visible tokens, V-weighted;
     lse_partial [B, qn, Hq, S]  = log-sum-exp of the split's scaled scores.
-    An empty split (no visible token) gives (0, -inf).
+    An empty split (no visible token) gives (0, -inf).  With ``split_counts``
+    ([B], each <= S), request b is partitioned into ``split_counts[b]`` splits
+    and its slots from ``split_counts[b]`` on stay (0, -inf).
     """
     B, qn, Hq, D = q.shape
     Hkv = k_pool.shape[2]
@@ -176,8 +178,9 @@ def split_partials(q, k_pool, v_pool, page_table, seq_lens, page_size, scale,
         L = max(0, int(seq_lens[b]))
         Kb = gather_tokens(k_pool, page_table[b], L, page_size)
         Vb = gather_tokens(v_pool, page_table[b], L, page_size)
-        for s in range(S):
-            t0, t1 = split_token_range(L, page_size, S, s)
+        Sb = S if split_counts is None else int(split_counts[b])
+        for s in range(Sb):
+            t0, t1 = split_token_range(L, page_size, Sb, s)
             for i in range(qn):
                 n = visible_length(L, qn, i, causal)
                 a, e = t0, min(t1, n)
@@ -189,7 +192,7 @@ def split_partials(q, k_pool, v_pool, page_table, seq_lens, page_size, scale,
     return o, lse
 
 
-def merge(o_partial: np.ndarray, lse_partial: np.ndarray):
+def merge(o_partial: np.ndarray, lse_partial: np.ndarray, split_counts=None):
     """Stage 2: combine split partials by their log-sum-exp.
 
     out = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - max_s lse_s);
@@ -197,20 +200,24 @@ def merge(o_partial: np.ndarray, lse_partial: np.ndarray):
     The pages name the two stages and the reuse of stage-2 inputs (LightLLM
     PR #1549, sections "Covered decode kernels" and "Validation"); this is the
     standard recombination of softmax over a partition of the keys.
+    With ``split_counts`` ([B]; the partials' leading axis is B), the rows of
+    request b combine only their first ``split_counts[b]`` slots.
     """
     S = lse_partial.shape[-1]
     lead = lse_partial.shape[:-1]
     D = o_partial.shape[-1]
     o2 = o_partial.reshape(-1, S, D)
     l2 = lse_partial.reshape(-1, S)
+    rows_per_req = o2.shape[0] // lead[0]
     out = np.zeros((o2.shape[0], D), dtype=np.float64)
     lse = np.full(o2.shape[0], NEG_INF, dtype=np.float64)
     for r in range(o2.shape[0]):
-        m = l2[r].max()
+        n = S if split_counts is None else int(split_counts[r // rows_per_req])
+        m = l2[r, :n].max()
         if m == NEG_INF:
             continue
-        w = np.exp(l2[r] - m)
+        w = np.exp(l2[r, :n] - m)
         tot = w.sum()
-        out[r] = (w @ o2[r]) / tot
+        out[r] = (w @ o2[r, :n]) / tot
         lse[r] = m + math.log(tot)
     return out.reshape(*lead, D), lse.reshape(lead)

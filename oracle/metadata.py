@@ -18,6 +18,14 @@ Readings taken where the page is silent:
   a negative slot gives 0 instead of an index.
 * ``batch_order`` (a scheduling aid the pages do not have): request indices
   sorted by descending ``cache_seqlens``, ties by ascending index.
+* SWA translation (same section: the fused kernel performs it, fed by a
+  full-to-SWA slot mapping the backend prepares): layers with a sliding
+  window keep their K/V in a second pool, and ``full_to_swa[slot]`` is the
+  SWA-pool slot holding the token of full-pool ``slot``.  The SWA page table
+  is built like the full one from the translated first slot of every page:
+  ``swa_page_table[b, j] = full_to_swa[slot] // page_size``.  A guarded full
+  slot (the cases that give 0 above), a slot past the end of the mapping, or
+  a negative mapped slot (a token no longer resident in the SWA pool) gives 0.
 All arithmetic is exact integer arithmetic (Python ints).
 """
 from __future__ import annotations
@@ -29,10 +37,42 @@ Q_CUMSUM = 1
 Q_PRESET = 2
 
 
+def _first_slot(r2t, rpi_b, j, page_size):
+    """Full-pool slot of logical page ``j`` of a request, or None when guarded
+    (invalid pool row, column past the table, negative slot)."""
+    R, W = r2t.shape
+    if rpi_b < 0 or rpi_b >= R:
+        return None
+    col = j * page_size
+    if col >= W:
+        return None
+    slot = int(r2t[rpi_b, col])
+    return slot if slot >= 0 else None
+
+
+def swa_page_table(seq_lens, req_pool_indices, req_to_token, page_size, max_pages, full_to_swa):
+    """[B, max_pages] page table of the SWA pool, through the full-to-SWA slot map."""
+    r2t = np.asarray(req_to_token)
+    f2s = [int(x) for x in np.asarray(full_to_swa).reshape(-1)]
+    rpi = [int(x) for x in np.asarray(req_pool_indices).reshape(-1)]
+    seq = [max(int(x), 0) for x in np.asarray(seq_lens).reshape(-1)]
+    pt = np.zeros((len(seq), max_pages), dtype=np.int64)
+    for b, L in enumerate(seq):
+        n = -(-L // page_size)
+        for j in range(min(n, max_pages)):
+            slot = _first_slot(r2t, rpi[b], j, page_size)
+            if slot is None or slot >= len(f2s):
+                continue
+            swa = f2s[slot]
+            pt[b, j] = swa // page_size if swa >= 0 else 0
+    return pt
+
+
 def metadata(seq_lens, req_pool_indices, req_to_token, page_size, max_pages,
-             q_mode=Q_STRIDED, q_in=None, q_stride=1):
+             q_mode=Q_STRIDED, q_in=None, q_stride=1, full_to_swa=None):
     """Returns dict(cache_seqlens [B], cu_seqlens_k [B+1], cu_seqlens_q [B+1],
-    page_table [B, max_pages], batch_order [B]) as int64 numpy arrays."""
+    page_table [B, max_pages], batch_order [B]) as int64 numpy arrays, plus
+    swa_page_table [B, max_pages] when ``full_to_swa`` is given."""
     seq_lens = [int(x) for x in np.asarray(seq_lens).reshape(-1)]
     rpi = [int(x) for x in np.asarray(req_pool_indices).reshape(-1)]
     r2t = np.asarray(req_to_token)
@@ -71,7 +111,12 @@ def metadata(seq_lens, req_pool_indices, req_to_token, page_size, max_pages,
 
     order = sorted(range(B), key=lambda b: (-cache[b], b))
 
+    extra = {}
+    if full_to_swa is not None:
+        extra["swa_page_table"] = swa_page_table(seq_lens, rpi, r2t, page_size, max_pages,
+                                                 full_to_swa)
     return dict(
+        **extra,
         batch_order=np.asarray(order, dtype=np.int64),
         cache_seqlens=np.asarray(cache, dtype=np.int64),
         cu_seqlens_k=np.asarray(cu_k, dtype=np.int64),

@@ -86,3 +86,73 @@ def test_cumsum_and_preset_modes():
     assert md["cu_seqlens_q"].tolist() == [0, 2, 7]
     md = OM.metadata(seq, [0, 1], r2t, 4, 2, q_mode=OM.Q_PRESET, q_in=np.array([0, 9, 11]))
     assert md["cu_seqlens_q"].tolist() == [0, 9, 11]
+
+
+# ---------------------------------------------------------------- SWA translation
+def _swa_golden():
+    with open(os.path.join(GOLDEN, "metadata_swa_hand.json")) as f:
+        return json.load(f)
+
+
+def test_swa_hand_built_batch():
+    g, s = _golden(), _swa_golden()
+    args = (g["seq_lens"], g["req_pool_indices"], np.array(g["req_to_token"]), g["page_size"],
+            g["max_pages"])
+    md = OM.metadata(*args, full_to_swa=np.array(s["full_to_swa"]))
+    assert md["swa_page_table"].tolist() == s["expect"]["swa_page_table"]
+    assert md["page_table"].tolist() == g["expect"]["page_table"]  # the full table is unchanged
+    cut = OM.swa_page_table(*args, np.array(s["full_to_swa"][:40]))
+    assert cut.tolist() == s["expect"]["swa_page_table_mapping40"]
+
+
+def _generated(w):
+    rng = np.random.Generator(np.random.PCG64(1000 + w.seed))
+    L = W.draw_lengths(w, rng)
+    pt, r2t, rpi, P = W.build_layout(w, L, rng)
+    return L, pt, r2t, rpi, P, rng
+
+
+SWA_CASES = [W.TINY_FP32, W.RAGGED_B64.scaled(batch=9, length_lo=3, length_hi=500)]
+
+
+@pytest.mark.parametrize("w", SWA_CASES, ids=lambda w: w.name)
+def test_swa_identity_mapping_gives_the_full_table(w):
+    L, pt, r2t, rpi, P, _ = _generated(w)
+    ident = np.arange(P * w.page_size)
+    swa = OM.swa_page_table(L, rpi, r2t, w.page_size, pt.shape[1], ident)
+    assert np.array_equal(swa, pt)
+
+
+@pytest.mark.parametrize("w", SWA_CASES, ids=lambda w: w.name)
+def test_swa_page_permutation_and_evictions(w):
+    """A page-aligned SWA pool: full page p lives in SWA page pi(p), or is not
+    resident (-1).  The SWA table must be pi applied to the full table, 0 where
+    the page is evicted and in the tail."""
+    L, pt, r2t, rpi, P, rng = _generated(w)
+    ps = w.page_size
+    pi = rng.permutation(P + 5)[:P]                # SWA pool is a bit larger
+    evicted = rng.random(P) < 0.3
+    f2s = np.empty(P * ps, dtype=np.int64)
+    for p in range(P):
+        f2s[p * ps:(p + 1) * ps] = -1 if evicted[p] else pi[p] * ps + np.arange(ps)
+    swa = OM.swa_page_table(L, rpi, r2t, ps, pt.shape[1], f2s)
+    n = (L + ps - 1) // ps
+    for b in range(len(L)):
+        for j in range(pt.shape[1]):
+            want = 0 if j >= n[b] or evicted[pt[b, j]] else pi[pt[b, j]]
+            assert swa[b, j] == want
+
+
+def test_swa_guards():
+    """Sentinel slots are not looked up (mapping[-1] would be the last entry),
+    slots past the mapping give 0, negative mapped slots give 0."""
+    r2t = np.array([[-1, -1, 8, 9, 4, 5]], dtype=np.int32)  # pages: sentinel, 4, 2
+    f2s = np.array([100, 101, 102, 103, -4, -4, 40, 41, 77])  # slot 4 -> -4, slot 8 -> 77
+    swa = OM.swa_page_table([6], [0], r2t, 2, 4, f2s)
+    assert swa.tolist() == [[0, 77 // 2, 0, 0]]
+    swa = OM.swa_page_table([6], [0], r2t, 2, 4, f2s[:8])       # slot 8 now past the end
+    assert swa.tolist() == [[0, 0, 0, 0]]
+    # the tail past ceil(L / page_size) is 0 even where the row holds valid slots
+    r2t = np.arange(8, dtype=np.int32)[None]
+    swa = OM.swa_page_table([3], [0], r2t, 2, 4, np.arange(8) + 10)
+    assert swa.tolist() == [[5, 6, 0, 0]]

@@ -14,9 +14,11 @@ import pytest
 import oracle.attention as real_attention
 import oracle.kvcache as real_kvcache
 import oracle.metadata as real_metadata
+import oracle.schedule as real_schedule
 from tests import test_oracle_attention as TA
 from tests import test_oracle_kvcache as TK
 from tests import test_oracle_metadata as TM
+from tests import test_oracle_schedule as TS
 
 ATTENTION_MUTANTS = [
     ("drop scale", "s = scale * (K @ qvec)", "s = (K @ qvec)"),
@@ -30,9 +32,12 @@ ATTENTION_MUTANTS = [
     ("split floor", "c = -(-n // num_splits) if n else 0", "c = max(1, n // num_splits) if n else 0"),
     ("split unclipped", "return min(p0 * page_size, L), min(p1 * page_size, L)",
      "return p0 * page_size, p1 * page_size"),
-    ("merge linear weights", "w = np.exp(l2[r] - m)", "w = l2[r] - m + 1.0"),
+    ("merge linear weights", "w = np.exp(l2[r, :n] - m)", "w = l2[r, :n] - m + 1.0"),
     ("merge lse drops max", "lse[r] = m + math.log(tot)", "lse[r] = math.log(tot)"),
     ("softmax sign", "w = np.exp(s - m)", "w = np.exp(m - s)"),
+    ("merge ignores split counts", "n = S if split_counts is None else int(split_counts[r // rows_per_req])",
+     "n = S"),
+    ("split ignores split counts", "Sb = S if split_counts is None else int(split_counts[b])", "Sb = S"),
 ]
 
 METADATA_MUTANTS = [
@@ -47,6 +52,31 @@ METADATA_MUTANTS = [
      "cu_q = [(b + 1) * int(q_stride) for b in range(B + 1)]"),
     ("order ascending", "key=lambda b: (-cache[b], b)", "key=lambda b: (cache[b], b)"),
     ("order ties reversed", "key=lambda b: (-cache[b], b)", "key=lambda b: (-cache[b], -b)"),
+    ("swa untranslated", "swa = f2s[slot]", "swa = slot"),
+    ("swa sentinel looked up", "return slot if slot >= 0 else None", "return slot"),
+    ("swa negative mapped slot kept", "pt[b, j] = swa // page_size if swa >= 0 else 0",
+     "pt[b, j] = swa // page_size"),
+    ("swa mapping unbounded", "if slot is None or slot >= len(f2s):", "if slot is None:"),
+    ("swa no tail", "for j in range(min(n, max_pages)):\n            slot = _first_slot",
+     "for j in range(max_pages):\n            slot = _first_slot"),
+]
+
+SCHEDULE_MUTANTS = [
+    ("bucket floor", "k = min(max(-(-L // bucket_tokens), 1), len(table)) - 1",
+     "k = min(max(L // bucket_tokens, 1), len(table)) - 1"),
+    ("bucket off by one", "k = min(max(-(-L // bucket_tokens), 1), len(table)) - 1",
+     "k = min(max(-(-L // bucket_tokens), 0), len(table) - 1)"),
+    ("no page clamp", "out.append(max(1, min(table[k], n, max_splits)))",
+     "out.append(max(1, min(table[k], max_splits)))"),
+    ("no max clamp", "out.append(max(1, min(table[k], n, max_splits)))",
+     "out.append(max(1, min(table[k], n)))"),
+    ("empty request gets no split", "out.append(max(1, min(table[k], n, max_splits)))",
+     "out.append(max(0, min(table[k], n, max_splits)))"),
+    ("order ascending", "key=lambda b: (-seq[b], b)", "key=lambda b: (seq[b], b)"),
+    ("splits descending", "for s in range(int(split_counts[b])):",
+     "for s in reversed(range(int(split_counts[b]))):"),
+    ("item fields swapped", "items.append(b * ITEM_SHIFT + s)", "items.append(s * ITEM_SHIFT + b)"),
+    ("padding not -1", "items + [-1] * (capacity - len(items))", "items + [0] * (capacity - len(items))"),
 ]
 
 
@@ -88,7 +118,9 @@ def _attention_pins():
              TA.test_two_tokens_closed_form, TA.test_gqa_equals_mha_with_repeated_kv_heads,
              TA.test_mtp_query_equals_single_query_decode_on_shorter_cache,
              lambda: TA.test_split_then_merge_equals_unsplit(4),
-             TA.test_split_ranges_partition_the_tokens]
+             TA.test_split_ranges_partition_the_tokens,
+             lambda: TS.test_per_request_splits_merge_to_the_unsplit_result(False, 1),
+             lambda: TS.test_per_request_splits_merge_to_the_unsplit_result(True, 3)]
     return pins
 
 
@@ -98,8 +130,15 @@ def _metadata_pins():
         (OM.Q_STRIDED, "cu_seqlens_q_strided", {}),
         (OM.Q_CUMSUM, "cu_seqlens_q_cumsum", {"q_in": "q_lens"}),
         (OM.Q_PRESET, "cu_seqlens_q_preset", {"q_in": "cu_q_preset"})]]
-    pins += [TM.test_sentinels_never_produce_negative_or_out_of_range_ids]
+    pins += [TM.test_sentinels_never_produce_negative_or_out_of_range_ids,
+             TM.test_swa_hand_built_batch, TM.test_swa_guards]
+    pins += [lambda w=w: TM.test_swa_page_permutation_and_evictions(w) for w in TM.SWA_CASES]
     return pins
+
+
+def _schedule_pins():
+    return [TS.test_hand_built_schedule, TS.test_capacity_too_small_is_an_error,
+            TS.test_constant_table_is_the_batch_wide_split]
 
 
 def _kvcache_pins():
@@ -130,11 +169,14 @@ def test_real_oracle_passes_every_pin():
     assert not _some_pin_fails(_attention_pins())
     assert not _some_pin_fails(_metadata_pins())
     assert not _some_pin_fails(_kvcache_pins())
+    assert not _some_pin_fails(_schedule_pins())
 
 
 @pytest.mark.parametrize("name,old,new", ATTENTION_MUTANTS, ids=[m[0] for m in ATTENTION_MUTANTS])
 def test_attention_mutant_is_caught(monkeypatch, name, old, new):
-    monkeypatch.setattr(TA, "OA", _mutant(real_attention, old, new))
+    m = _mutant(real_attention, old, new)
+    monkeypatch.setattr(TA, "OA", m)
+    monkeypatch.setattr(TS, "OA", m)
     assert _some_pin_fails(_attention_pins()), f"no pin caught mutant '{name}'"
 
 
@@ -148,3 +190,9 @@ def test_metadata_mutant_is_caught(monkeypatch, name, old, new):
 def test_kvcache_mutant_is_caught(monkeypatch, name, old, new):
     monkeypatch.setattr(TK, "OK", _mutant(real_kvcache, old, new))
     assert _some_pin_fails(_kvcache_pins()), f"no pin caught mutant '{name}'"
+
+
+@pytest.mark.parametrize("name,old,new", SCHEDULE_MUTANTS, ids=[m[0] for m in SCHEDULE_MUTANTS])
+def test_schedule_mutant_is_caught(monkeypatch, name, old, new):
+    monkeypatch.setattr(TS, "OS", _mutant(real_schedule, old, new))
+    assert _some_pin_fails(_schedule_pins()), f"no pin caught mutant '{name}'"
