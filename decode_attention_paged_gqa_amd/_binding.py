@@ -37,13 +37,18 @@ _F32 = ctypes.c_float
 _SIGS = {
     "decode_attn_metadata": [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _I32,
                              _P, _P, _P, _P, _P, _P],
+    "decode_attn_metadata_ex": [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _I32,
+                                _P, _P, _P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _P, _P,
+                                _I32, _P],
     "decode_attn_split": [_P, _I32, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32,
-                          _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
+                          _I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _F32, _I32, _P, _P, _P],
     "decode_attn_split_int8": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I32,
-                               _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
+                               _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _F32,
+                               _I32, _P, _P, _P],
     "decode_attn_split_int4": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I32,
-                               _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P],
-    "decode_attn_merge": [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P],
+                               _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _F32,
+                               _I32, _P, _P, _P],
+    "decode_attn_merge": [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _P, _P],
     "decode_attn_append_kv": [_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32,
                               _I32, _P],
     "decode_attn_pick_splits": [_P, _P, _I32, _I32, _I32, _I32, _I32],
@@ -109,10 +114,18 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None, ndim=None):
 
 # ------------------------------------------------------------------ metadata
 def decode_attn_metadata(seq_lens, req_pool_indices, req_to_token, page_size, max_pages,
-                         q_mode=DA_Q_STRIDED, q_in=None, q_stride=1, out=None):
+                         q_mode=DA_Q_STRIDED, q_in=None, q_stride=1, out=None,
+                         full_to_swa=None, split_table=None, bucket_tokens=4096,
+                         max_splits=None, work_capacity=None):
     """cache_seqlens, cu_seqlens_k, cu_seqlens_q, page_table, batch_order in one launch.
 
-    Returns a dict of int32 tensors (those in ``out`` are reused)."""
+    Options, computed in the same launch (``decode_attn_metadata_ex``):
+    ``full_to_swa`` (int64 [n] slot map) adds "swa_page_table"; ``split_table``
+    (a host list of per-bucket split counts) adds "split_counts" and
+    "work_list" (``work_capacity`` entries, default batch * max_splits), for
+    the split calls' per-request scheduling.  ``max_splits`` defaults to
+    max(split_table).  Returns a dict of int32 tensors (those in ``out`` are
+    reused)."""
     lib = load()
     dev = seq_lens.device
     _need(seq_lens, "seq_lens", torch.int32, dev, 1)
@@ -134,6 +147,10 @@ def decode_attn_metadata(seq_lens, req_pool_indices, req_to_token, page_size, ma
         _need(out[k], k, torch.int32, dev)
     if tuple(out["page_table"].shape) != (B, max_pages):
         raise ValueError("page_table must be [batch, max_pages]")
+    if full_to_swa is not None or split_table is not None:
+        return _metadata_ex(lib, dev, B, seq_lens, req_pool_indices, req_to_token, page_size,
+                            max_pages, q_mode, q_in, q_stride, out, mk, full_to_swa,
+                            split_table, bucket_tokens, max_splits, work_capacity)
     st = lib.decode_attn_metadata(
         _ptr(seq_lens), _ptr(req_pool_indices), _ptr(req_to_token), req_to_token.shape[0],
         req_to_token.shape[1], req_to_token.stride(0), B, page_size, max_pages, q_mode,
@@ -141,6 +158,41 @@ def decode_attn_metadata(seq_lens, req_pool_indices, req_to_token, page_size, ma
         _ptr(out["cu_seqlens_q"]), _ptr(out["page_table"]), _ptr(out["batch_order"]),
         _stream(dev))
     _check(st, "decode_attn_metadata")
+    return out
+
+
+def _metadata_ex(lib, dev, B, seq_lens, rpi, r2t, page_size, max_pages, q_mode, q_in, q_stride,
+                 out, mk, full_to_swa, split_table, bucket_tokens, max_splits, work_capacity):
+    f2s_len = 0
+    if full_to_swa is not None:
+        _need(full_to_swa, "full_to_swa", torch.int64, dev, 1)
+        f2s_len = full_to_swa.shape[0]
+        out["swa_page_table"] = mk("swa_page_table", (B, max_pages))
+        _need(out["swa_page_table"], "swa_page_table", torch.int32, dev)
+        if tuple(out["swa_page_table"].shape) != (B, max_pages):
+            raise ValueError("swa_page_table must be [batch, max_pages]")
+    table_host, nb, smax = None, 0, 0
+    if split_table is not None:
+        vals = [int(x) for x in split_table]
+        nb = len(vals)
+        smax = int(max_splits) if max_splits is not None else max(vals)
+        table_host = (ctypes.c_int32 * nb)(*vals)
+        cap = int(work_capacity) if work_capacity is not None else B * min(smax, max(vals))
+        out["split_counts"] = mk("split_counts", (B,))
+        out["work_list"] = mk("work_list", (cap,))
+        for k in ("split_counts", "work_list"):
+            _need(out[k], k, torch.int32, dev, 1)
+        if out["work_list"].shape[0] != cap or out["split_counts"].shape[0] != B:
+            raise ValueError("split_counts / work_list sized for another batch or capacity")
+    st = lib.decode_attn_metadata_ex(
+        _ptr(seq_lens), _ptr(rpi), _ptr(r2t), r2t.shape[0], r2t.shape[1], r2t.stride(0), B,
+        page_size, max_pages, q_mode, _ptr(q_in), q_stride, _ptr(out["cache_seqlens"]),
+        _ptr(out["cu_seqlens_k"]), _ptr(out["cu_seqlens_q"]), _ptr(out["page_table"]),
+        _ptr(out["batch_order"]), _ptr(full_to_swa), f2s_len, _ptr(out.get("swa_page_table")),
+        table_host, nb, int(bucket_tokens), smax, _ptr(out.get("split_counts")),
+        _ptr(out.get("work_list")), out["work_list"].shape[0] if table_host is not None else 0,
+        _stream(dev))
+    _check(st, "decode_attn_metadata_ex")
     return out
 
 
@@ -182,7 +234,8 @@ def _q_code(q):
     raise TypeError(f"q dtype {q.dtype} unsupported")
 
 
-def _split_common(q, page_table, cache_seqlens, batch_order):
+def _split_common(q, page_table, cache_seqlens, batch_order, split_counts=None,
+                  work_list=None):
     _need(q, "q", (torch.bfloat16, torch.float32), ndim=4)
     dev = q.device
     _need(page_table, "page_table", torch.int32, dev, 2)
@@ -193,17 +246,30 @@ def _split_common(q, page_table, cache_seqlens, batch_order):
         _need(batch_order, "batch_order", torch.int32, dev, 1)
         if batch_order.shape[0] != q.shape[0]:
             raise ValueError("batch_order length != batch")
+    if (work_list is None) != (split_counts is None):
+        raise ValueError("work_list and split_counts go together")
+    if work_list is not None:
+        _need(work_list, "work_list", torch.int32, dev, 1)
+        _need(split_counts, "split_counts", torch.int32, dev, 1)
+        if split_counts.shape[0] != q.shape[0]:
+            raise ValueError("split_counts length != batch")
     return dev
+
+
+def _sched_args(split_counts, work_list):
+    return (_ptr(split_counts), _ptr(work_list), 0 if work_list is None else work_list.shape[0])
 
 
 def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
                       softmax_scale=None, causal=False, o_partial=None, lse_partial=None,
-                      batch_order=None, kv_layout="NHD"):
+                      batch_order=None, kv_layout="NHD", split_counts=None, work_list=None):
     """Stage 1 over a dense bf16 / fp32 cache.  Returns (o_partial, lse_partial).
 
-    Pools are [P, page_size, Hkv, D] (kv_layout "NHD") or [P, Hkv, page_size, D] ("HND")."""
+    Pools are [P, page_size, Hkv, D] (kv_layout "NHD") or [P, Hkv, page_size, D] ("HND").
+    With ``work_list`` / ``split_counts`` (from ``decode_attn_metadata(split_table=...)``)
+    request b has split_counts[b] splits and ``num_splits`` is the slots per row."""
     lib = load()
-    dev = _split_common(q, page_table, cache_seqlens, batch_order)
+    dev = _split_common(q, page_table, cache_seqlens, batch_order, split_counts, work_list)
     lay = _layout_code(kv_layout)
     _need(k_pool, "k_pool", q.dtype, dev, 4)
     _need(v_pool, "v_pool", q.dtype, dev, 4)
@@ -219,7 +285,7 @@ def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
     st = lib.decode_attn_split(
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), page_table.stride(0),
         page_table.shape[1], _ptr(cache_seqlens), _ptr(batch_order), B, qn, Hq, Hkv, D, S_p, P,
-        lay, num_splits, scale,
+        lay, num_splits, *_sched_args(split_counts, work_list), scale,
         int(bool(causal)), _ptr(o_partial), _ptr(lse_partial), _stream(dev))
     _check(st, "decode_attn_split")
     return o_partial, lse_partial
@@ -227,13 +293,14 @@ def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
 
 def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cache_seqlens,
                            num_splits, softmax_scale=None, causal=False, o_partial=None,
-                           lse_partial=None, batch_order=None, kv_layout="NHD"):
+                           lse_partial=None, batch_order=None, kv_layout="NHD",
+                           split_counts=None, work_list=None):
     """Stage 1 over an INT8 cache (fp16 scale per token and kv-head).
 
     Pools [P, page_size, Hkv, D] with scales [P, page_size, Hkv] ("NHD"), or
     [P, Hkv, page_size, D] with [P, Hkv, page_size] ("HND")."""
     lib = load()
-    dev = _split_common(q, page_table, cache_seqlens, batch_order)
+    dev = _split_common(q, page_table, cache_seqlens, batch_order, split_counts, work_list)
     lay = _layout_code(kv_layout)
     _need(k_pool, "k_pool", torch.int8, dev, 4)
     _need(v_pool, "v_pool", torch.int8, dev, 4)
@@ -251,7 +318,8 @@ def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cach
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
         _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
         _ptr(batch_order), B, qn,
-        Hq, Hkv, D, S_p, P, lay, num_splits, scale, int(bool(causal)), _ptr(o_partial),
+        Hq, Hkv, D, S_p, P, lay, num_splits, *_sched_args(split_counts, work_list), scale,
+        int(bool(causal)), _ptr(o_partial),
         _ptr(lse_partial), _stream(dev))
     _check(st, "decode_attn_split_int8")
     return o_partial, lse_partial
@@ -259,13 +327,14 @@ def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cach
 
 def decode_attn_split_int4(q, k_pool, v_pool, k_scale_zero, v_scale_zero, page_table,
                            cache_seqlens, num_splits, softmax_scale=None, causal=False,
-                           o_partial=None, lse_partial=None, batch_order=None, kv_layout="NHD"):
+                           o_partial=None, lse_partial=None, batch_order=None, kv_layout="NHD",
+                           split_counts=None, work_list=None):
     """Stage 1 over an INT4 cache (fp16 (scale, zero) per 32-group along D).
 
     Pools [P, page_size, Hkv, D/2] with (scale, zero) [P, page_size, Hkv, D/32, 2]
     ("NHD"), or the first three dims as [P, Hkv, page_size] ("HND")."""
     lib = load()
-    dev = _split_common(q, page_table, cache_seqlens, batch_order)
+    dev = _split_common(q, page_table, cache_seqlens, batch_order, split_counts, work_list)
     lay = _layout_code(kv_layout)
     _need(k_pool, "k_pool", torch.uint8, dev, 4)
     _need(v_pool, "v_pool", torch.uint8, dev, 4)
@@ -286,7 +355,8 @@ def decode_attn_split_int4(q, k_pool, v_pool, k_scale_zero, v_scale_zero, page_t
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale_zero), _ptr(v_scale_zero),
         _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
         _ptr(batch_order), B, qn,
-        Hq, Hkv, D, S_p, P, lay, num_splits, scale, int(bool(causal)), _ptr(o_partial),
+        Hq, Hkv, D, S_p, P, lay, num_splits, *_sched_args(split_counts, work_list), scale,
+        int(bool(causal)), _ptr(o_partial),
         _ptr(lse_partial), _stream(dev))
     _check(st, "decode_attn_split_int4")
     return o_partial, lse_partial
@@ -333,8 +403,9 @@ def decode_attn_append_kv(k_new, v_new, out_cache_loc, k_pool, v_pool, k_scale=N
 
 # ------------------------------------------------------------------ stage 2
 def decode_attn_merge(o_partial, lse_partial, out_dtype=torch.bfloat16, out=None, lse_out=None,
-                      want_lse=False):
-    """LSE merge of the split partials.  Returns out (and lse if requested)."""
+                      want_lse=False, split_counts=None):
+    """LSE merge of the split partials.  Returns out (and lse if requested).
+    With ``split_counts`` ([B] int32) request b merges only its first split_counts[b] slots."""
     lib = load()
     _need(o_partial, "o_partial", torch.float32, ndim=5)
     dev = o_partial.device
@@ -349,9 +420,13 @@ def decode_attn_merge(o_partial, lse_partial, out_dtype=torch.bfloat16, out=None
         lse_out = torch.empty((B, qn, Hq), dtype=torch.float32, device=dev)
     if lse_out is not None:
         _need(lse_out, "lse_out", torch.float32, dev)
+    if split_counts is not None:
+        _need(split_counts, "split_counts", torch.int32, dev, 1)
+        if split_counts.shape[0] != B:
+            raise ValueError("split_counts length != batch")
     code = DA_BF16 if out.dtype == torch.bfloat16 else DA_FP32
-    st = lib.decode_attn_merge(_ptr(o_partial), _ptr(lse_partial), B, qn, Hq, D, S, _ptr(out),
-                               code, _ptr(lse_out), _stream(dev))
+    st = lib.decode_attn_merge(_ptr(o_partial), _ptr(lse_partial), B, qn, Hq, D, S,
+                               _ptr(split_counts), _ptr(out), code, _ptr(lse_out), _stream(dev))
     _check(st, "decode_attn_merge")
     return (out, lse_out) if (want_lse or lse_out is not None) else out
 

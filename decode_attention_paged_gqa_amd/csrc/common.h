@@ -46,50 +46,75 @@ __device__ __forceinline__ float xor_shfl(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------- stage-1 work units
-// Stage 1 runs one workgroup per (kv-head g, split s, dispatch slot z) on a
-// 1-D grid.  Workgroups reach the chip's 8 XCDs round-robin by linear id,
-// and each XCD has its own L2.  Two orders:
-//  * spread: id = g + Hkv * (s + S * z).  With Hkv a multiple of 8 every
-//    XCD gets one kv-head of every unit, the best balance; used where a
-//    kv-head's rows fill whole cache lines (dense caches).
-//  * grouped: units u = z * S + s are dealt to the XCDs in rounds of 8, in
-//    snake order (round r sends unit 8r + j to XCD j for even r and to XCD
-//    7 - j for odd r, keeping a longest-first order balanced), and a unit's
-//    Hkv heads are that XCD's next Hkv workgroups.  Short rows of
-//    neighbouring kv-heads (4-bit and 8-bit codes, their scales) share cache
-//    lines; this way each such line is brought into one L2, once, by
-//    workgroups that run side by side.
-// Dispatch slots keep their order (longest requests first with a batch order).
+// Stage 1 runs one workgroup per (kv-head g, work unit u) on a 1-D grid.  A
+// unit is one (request, split).  Without a work list, unit u = z * S + s is
+// split s of the request in dispatch slot z (order[z] with a batch order,
+// else z), every request having S splits.  With a work list (built by the
+// metadata prelude from per-request split counts), unit u is the list's
+// entry u = b * 256 + s, request b having counts[b] splits; -1 entries are
+// padding.  Either way the partials keep S slots per query row.
+//
+// Workgroups reach the chip's 8 XCDs round-robin by linear id, and each XCD
+// has its own L2.  Two orders of (g, u):
+//  * spread: id = g + Hkv * u.  With Hkv a multiple of 8 every XCD gets one
+//    kv-head of every unit, the best balance; used where a kv-head's rows
+//    fill whole cache lines (dense caches).
+//  * grouped: units are dealt to the XCDs in rounds of 8, in snake order
+//    (round r sends unit 8r + j to XCD j for even r and to XCD 7 - j for odd
+//    r, keeping a longest-first order balanced), and a unit's Hkv heads are
+//    that XCD's next Hkv workgroups.  Short rows of neighbouring kv-heads
+//    (4-bit and 8-bit codes, their scales) share cache lines; this way each
+//    such line is brought into one L2, once, by workgroups that run side by
+//    side.
+// Units keep their order (longest requests first with a batch order or a
+// work list).
 constexpr int kXcds = 8;
+constexpr int kItemShift = 8;  // work item = b << 8 | s
 
-struct WorkUnit {
-  int g, s, z;
+struct Stage1Sched {
+  const int32_t* order;   // nullable: batch order (no work list)
+  const int32_t* work;    // nullable: work list of `units` entries
+  const int32_t* counts;  // per-request split counts (with a work list)
+  int S;                  // split slots per query row; the split count without a work list
+  int B;                  // requests
+  int units;              // S * B, or the work list's capacity
 };
 
-// false for the padding workgroups of the last round of units
+struct Stage1Item {
+  int g, b, s, S;  // kv-head, request, split, the request's split count
+};
+
+// false for padding workgroups: the last round of the grouped order, -1
+// entries of a work list, and entries that name no valid (request, split)
 template <bool GROUPED>
-__device__ __forceinline__ bool stage1_unit(int Hkv, int S, int B, WorkUnit& w) {
+__device__ __forceinline__ bool stage1_item(const Stage1Sched& sc, int Hkv, Stage1Item& it) {
   const int i = (int)blockIdx.x;
+  int u;
   if (!GROUPED) {
-    const int u = i / Hkv;
-    w.g = i - u * Hkv;
-    w.z = u / S;
-    w.s = u - w.z * S;
+    u = i / Hkv;
+    it.g = i - u * Hkv;
+  } else {
+    const int x = i % kXcds, k = i / kXcds;
+    const int r = k / Hkv;
+    u = r * kXcds + ((r & 1) ? kXcds - 1 - x : x);
+    it.g = k - r * Hkv;
+    if (u >= sc.units) return false;
+  }
+  if (!sc.work) {
+    const int z = u / sc.S;
+    it.s = u - z * sc.S;
+    const int b = sc.order ? sc.order[z] : z;
+    it.b = (unsigned)b < (unsigned)sc.B ? b : z;
+    it.S = sc.S;
     return true;
   }
-  const int x = i % kXcds, k = i / kXcds;
-  const int r = k / Hkv;
-  const int u = r * kXcds + ((r & 1) ? kXcds - 1 - x : x);
-  w.g = k - r * Hkv;
-  w.z = u / S;
-  w.s = u - w.z * S;
-  return u < S * B;
-}
-
-// request of dispatch slot z: order[z] when given and in range, else z
-__device__ __forceinline__ int stage1_request(const int32_t* order, int z, int B) {
-  const int b = order ? order[z] : z;
-  return (unsigned)b < (unsigned)B ? b : z;
+  const int item = sc.work[u];
+  if (item < 0) return false;
+  it.b = item >> kItemShift;
+  it.s = item & ((1 << kItemShift) - 1);
+  if (it.b >= sc.B) return false;
+  it.S = min(max(sc.counts[it.b], 1), sc.S);
+  return it.s < it.S;
 }
 
 }  // namespace da
@@ -138,6 +163,9 @@ struct SplitCall {
   int pt_stride, max_pages;
   const int32_t* seqlens;
   const int32_t* order;
+  const int32_t* work;    // nullable: work list (then counts is required)
+  const int32_t* counts;
+  int units;              // grid units: S * batch, or the work list's capacity
   int batch, qn, Hq, Hkv, D, ps, num_pages, S;
   KvStrides kv;
   float scale;
@@ -145,12 +173,24 @@ struct SplitCall {
   float* o;
   float* lse;
   hipStream_t stream;
+
+  da::Stage1Sched sched() const {
+    da::Stage1Sched sc;
+    sc.order = order; sc.work = work; sc.counts = counts;
+    sc.S = S; sc.B = batch; sc.units = units;
+    return sc;
+  }
 };
 
-// 1-D grid of stage 1 (see da::stage1_unit); the grouped order pads to
-// whole rounds of 8 units
-inline unsigned stage1_grid(int Hkv, int S, int B, bool grouped) {
-  const long long units = (long long)S * B;
+// Largest split of a launch, in pages: ceil(max_pages / S), or max_pages with
+// a work list (a request may have a single split).
+inline int max_split_pages(const SplitCall& c) {
+  return c.work ? c.max_pages : (c.max_pages + c.S - 1) / c.S;
+}
+
+// 1-D grid of stage 1 (see da::stage1_item) over `units` work units; the
+// grouped order pads to whole rounds of 8 units
+inline unsigned stage1_grid(int Hkv, long long units, bool grouped) {
   if (!grouped) return (unsigned)(units * Hkv);
   return (unsigned)(da::kXcds * (long long)Hkv * ((units + da::kXcds - 1) / da::kXcds));
 }

@@ -43,4 +43,4 @@ extern "C" const char* decode_attn_strerror(int32_t status) {
   }
 }
 
-extern "C" int32_t decode_attn_version(void) { return 200; }
+extern "C" int32_t decode_attn_version(void) { return 300; }

@@ -7,7 +7,9 @@
 //
 // One wave per query row; the reduction over splits stays in registers:
 // every lane owns D/64 output elements and walks all splits itself, the
-// split weights being wave-uniform.
+// split weights being wave-uniform.  With per-request split counts, the rows
+// of request b combine only their first counts[b] split slots (clamped to
+// [1, S]); the other slots are never read.
 #include "common.h"
 
 namespace {
@@ -17,13 +19,17 @@ constexpr int kWaves = 4;
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restrict__ op,
                                                            const float* __restrict__ lp,
-                                                           int rows, int S, void* __restrict__ out,
+                                                           int rows, int S,
+                                                           const int32_t* __restrict__ counts,
+                                                           int rows_per_req, void* __restrict__ out,
                                                            float* __restrict__ lse_out) {
   constexpr int E = D / 64;  // elements per lane
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
   const float* l = lp + (long long)row * S;
+  const float* o = op + (long long)row * S * D + lane * E;
+  if (counts) S = min(max(counts[row / rows_per_req], 1), S);
   float m = da::kNegInf;
   for (int s = lane; s < S; s += 64) m = fmaxf(m, l[s]);
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -33,7 +39,6 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restr
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   if (m != da::kNegInf) {
-    const float* o = op + (long long)row * S * D + lane * E;
     const float ml = m * da::kLog2e;
     for (int s = 0; s < S; ++s) {
       const float w = da::fast_exp2(fmaf(l[s], da::kLog2e, -ml));  // exp(lse_s - m); 0 for -inf
@@ -64,11 +69,11 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restr
 }
 
 template <int D, bool B16>
-int32_t launch(const float* op, const float* lp, int rows, int S, void* out, float* lse_out,
-               hipStream_t st) {
+int32_t launch(const float* op, const float* lp, int rows, int S, const int32_t* counts,
+               int rows_per_req, void* out, float* lse_out, hipStream_t st) {
   const int blocks = (rows + kWaves - 1) / kWaves;
   hipLaunchKernelGGL((merge_kernel<D, B16>), dim3(blocks), dim3(64 * kWaves), 0, st, op, lp, rows,
-                     S, out, lse_out);
+                     S, counts, rows_per_req, out, lse_out);
   return da_host::launch_status();
 }
 
@@ -76,7 +81,8 @@ int32_t launch(const float* op, const float* lp, int rows, int S, void* out, flo
 
 extern "C" int32_t decode_attn_merge(const float* o_partial, const float* lse_partial,
                                      int32_t batch, int32_t q_per_req, int32_t num_q_heads,
-                                     int32_t head_dim, int32_t num_splits, void* out,
+                                     int32_t head_dim, int32_t num_splits,
+                                     const int32_t* split_counts, void* out,
                                      int32_t out_dtype, float* lse_out, void* stream) {
   if (!o_partial || !lse_partial || !out) return DA_ERR_INVALID_ARG;
   if (batch <= 0 || q_per_req <= 0 || num_q_heads <= 0 || num_splits <= 0 ||
@@ -87,11 +93,13 @@ extern "C" int32_t decode_attn_merge(const float* o_partial, const float* lse_pa
   const long long rows_ll = (long long)batch * q_per_req * num_q_heads;
   if (rows_ll > (1ll << 30)) return DA_ERR_INVALID_ARG;
   const int rows = (int)rows_ll;
+  const int rpr = q_per_req * num_q_heads;
   hipStream_t st = (hipStream_t)stream;
   const bool b16 = out_dtype == DA_BF16;
+  const int32_t* cn = split_counts;
   if (head_dim == 128)
-    return b16 ? launch<128, true>(o_partial, lse_partial, rows, num_splits, out, lse_out, st)
-               : launch<128, false>(o_partial, lse_partial, rows, num_splits, out, lse_out, st);
-  return b16 ? launch<64, true>(o_partial, lse_partial, rows, num_splits, out, lse_out, st)
-             : launch<64, false>(o_partial, lse_partial, rows, num_splits, out, lse_out, st);
+    return b16 ? launch<128, true>(o_partial, lse_partial, rows, num_splits, cn, rpr, out, lse_out, st)
+               : launch<128, false>(o_partial, lse_partial, rows, num_splits, cn, rpr, out, lse_out, st);
+  return b16 ? launch<64, true>(o_partial, lse_partial, rows, num_splits, cn, rpr, out, lse_out, st)
+             : launch<64, false>(o_partial, lse_partial, rows, num_splits, cn, rpr, out, lse_out, st);
 }

@@ -5,8 +5,8 @@
 //
 // Work decomposition: one workgroup (4 waves) per (kv-head g, split s,
 // request b); the split's tokens are cut into 8-token tiles dealt
-// round-robin to the waves.  With a batch order (requests by descending
-// length, from the metadata prelude) the z-index of the grid walks requests
+// round-robin to the waves.  With a batch order or a work list (requests by
+// descending length, from the metadata prelude) the grid walks requests
 // longest first, so the long splits are dispatched before the short ones.
 //
 // Lane layout (D = 128): 8 lanes per token, 8 tokens per wave.  Lane
@@ -136,13 +136,12 @@ struct Bf16Args {
   const uint8_t* v;
   const int32_t* pt;
   const int32_t* seqlens;
-  const int32_t* order;  // nullable: request served by grid z-index
+  da::Stage1Sched sched;  // (request, split) of every workgroup
   float* o;
   float* lse;
   int pt_stride, max_pages;
   int qn, Hq, Hkv, G, R;
-  int page_size, log2_ps, num_pages, S;
-  int B;  // requests
+  int page_size, log2_ps, num_pages;
   int slot_stride, head_stride;  // rows (see da_host::KvStrides)
   float scale_log2;
   int causal;
@@ -171,10 +170,9 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
   __shared__ __attribute__((aligned(16))) uint8_t smem[SM::BYTES];
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + SM::MAIN_BYTES);
 
-  da::WorkUnit wu;
-  if (!da::stage1_unit<false>(a.Hkv, a.S, a.B, wu)) return;
-  const int g = wu.g, s = wu.s;
-  const int b = da::stage1_request(a.order, wu.z, a.B);
+  da::Stage1Item it;
+  if (!da::stage1_item<false>(a.sched, a.Hkv, it)) return;
+  const int g = it.g, s = it.s, b = it.b;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tq = lane >> 3, c = lane & 7;
@@ -182,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
   const int ps = a.page_size;
   const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
   const int n = (L + ps - 1) >> a.log2_ps;
-  const int cpg = (n + a.S - 1) / a.S;
+  const int cpg = (n + it.S - 1) / it.S;
   const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
   const int t0 = p0 * ps, t1 = min(p1 * ps, L);
   const int ntiles = t1 > t0 ? (t1 - t0 + 7) >> 3 : 0;
@@ -418,16 +416,17 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
       }
     }
     const int i = r / a.G, h = g * a.G + (r % a.G);
-    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.S + s;
+    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.sched.S + s;
     a.o[orow * D + d] = lsum > 0.f ? o / lsum : 0.f;
     if (d == 0) a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum)) * da::kLn2 : da::kNegInf;
   }
 }
 
 template <int D, int RT>
-int32_t launch(const Bf16Args& a, int batch, hipStream_t st) {
-  hipLaunchKernelGGL((split_bf16_kernel<D, RT, 4>), dim3(da_host::stage1_grid(a.Hkv, a.S, batch, false)),
-                     dim3(kThreads), 0, st, a);
+int32_t launch(const Bf16Args& a, hipStream_t st) {
+  hipLaunchKernelGGL((split_bf16_kernel<D, RT, 4>),
+                     dim3(da_host::stage1_grid(a.Hkv, a.sched.units, false)), dim3(kThreads), 0, st,
+                     a);
   return da_host::launch_status();
 }
 
@@ -439,32 +438,29 @@ int32_t launch(const Bf16Args& a, int batch, hipStream_t st) {
 int32_t da_split_bf16_fast(const da_host::SplitCall& c) {
   const int G = c.Hq / c.Hkv, R = G * c.qn, D = c.D;
   if (R > 5 || (D != 128 && D != 64)) return -1;
-  if ((c.max_pages + c.S - 1) / c.S > kMaxSplitPages) return -1;
+  if (da_host::max_split_pages(c) > kMaxSplitPages) return -1;
   Bf16Args a;
   a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
-  a.pt = c.pt; a.seqlens = c.seqlens; a.order = c.order; a.o = c.o; a.lse = c.lse;
+  a.pt = c.pt; a.seqlens = c.seqlens; a.sched = c.sched(); a.o = c.o; a.lse = c.lse;
   a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
   a.qn = c.qn; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = G; a.R = R;
   a.page_size = c.ps; a.log2_ps = __builtin_ctz((unsigned)c.ps); a.num_pages = c.num_pages;
-  a.S = c.S;
-  a.B = c.batch;
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  const int batch = c.batch;
   hipStream_t st = c.stream;
   if (D == 128) {
     switch (R) {
-      case 1: return launch<128, 1>(a, batch, st);
-      case 2: return launch<128, 2>(a, batch, st);
-      case 3: case 4: return launch<128, 4>(a, batch, st);
-      default: return launch<128, 5>(a, batch, st);
+      case 1: return launch<128, 1>(a, st);
+      case 2: return launch<128, 2>(a, st);
+      case 3: case 4: return launch<128, 4>(a, st);
+      default: return launch<128, 5>(a, st);
     }
   }
   switch (R) {
-    case 1: return launch<64, 1>(a, batch, st);
-    case 2: return launch<64, 2>(a, batch, st);
-    case 3: case 4: return launch<64, 4>(a, batch, st);
-    default: return launch<64, 5>(a, batch, st);
+    case 1: return launch<64, 1>(a, st);
+    case 2: return launch<64, 2>(a, st);
+    case 3: case 4: return launch<64, 4>(a, st);
+    default: return launch<64, 5>(a, st);
   }
 }

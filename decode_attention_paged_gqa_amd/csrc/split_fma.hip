@@ -39,14 +39,13 @@ struct SplitArgs {
   const uint16_t* vs;
   const int32_t* pt;
   const int32_t* seqlens;
-  const int32_t* order;  // nullable: request served by grid z-index
+  da::Stage1Sched sched;  // (request, split) of every workgroup
   float* o;
   float* lse;
   int q_bf16;
   int pt_stride, max_pages;
   int qn, Hq, Hkv, G, R;
-  int page_size, log2_ps, num_pages, S;
-  int B;  // requests
+  int page_size, log2_ps, num_pages;
   int slot_stride, head_stride;  // rows (see da_host::KvStrides)
   float scale_log2;
   int causal;
@@ -143,17 +142,16 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
   __shared__ float sm_l[kWaves][RT];
   __shared__ float sm_acc[kWaves][RT][D];
 
-  da::WorkUnit wu;
-  if (!da::stage1_unit<(KV == KV_I8 || KV == KV_I4)>(a.Hkv, a.S, a.B, wu)) return;
-  const int g = wu.g, s = wu.s;
-  const int b = da::stage1_request(a.order, wu.z, a.B);
+  da::Stage1Item it;
+  if (!da::stage1_item<(KV == KV_I8 || KV == KV_I4)>(a.sched, a.Hkv, it)) return;
+  const int g = it.g, s = it.s, b = it.b;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane >> 4, c = lane & 15;
 
   const int ps = a.page_size;
   const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
   const int n = (L + ps - 1) >> a.log2_ps;
-  const int cpg = (n + a.S - 1) / a.S;
+  const int cpg = (n + it.S - 1) / it.S;
   const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
   const int t0 = p0 * ps, t1 = min(p1 * ps, L);
 
@@ -344,37 +342,35 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
       }
     }
     const int i = r / a.G, h = g * a.G + (r % a.G);
-    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.S + s;
+    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.sched.S + s;
     a.o[orow * D + d] = lsum > 0.f ? o / lsum : 0.f;
     if (d == 0) a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum)) * da::kLn2 : da::kNegInf;
   }
 }
 
 template <int KV, int D, int RT>
-int32_t launch_rt(const SplitArgs& args, int batch, hipStream_t st) {
-  SplitArgs a = args;
-  a.B = batch;
+int32_t launch_rt(const SplitArgs& a, hipStream_t st) {
   constexpr bool kGrouped = KV == KV_I8 || KV == KV_I4;  // short rows share cache lines
   hipLaunchKernelGGL((split_fma_kernel<KV, D, RT>),
-                     dim3(da_host::stage1_grid(a.Hkv, a.S, batch, kGrouped)), dim3(kThreads), 0,
-                     st, a);
+                     dim3(da_host::stage1_grid(a.Hkv, a.sched.units, kGrouped)), dim3(kThreads),
+                     0, st, a);
   return da_host::launch_status();
 }
 
 template <int KV, int D>
-int32_t launch_d(const SplitArgs& a, int batch, hipStream_t st) {
+int32_t launch_d(const SplitArgs& a, hipStream_t st) {
   const int R = a.R;
-  if (R <= 1) return launch_rt<KV, D, 1>(a, batch, st);
-  if (R <= 2) return launch_rt<KV, D, 2>(a, batch, st);
-  if (R <= 4) return launch_rt<KV, D, 4>(a, batch, st);
-  if (R <= 5) return launch_rt<KV, D, 5>(a, batch, st);
-  if (R <= 8) return launch_rt<KV, D, 8>(a, batch, st);
-  return launch_rt<KV, D, 16>(a, batch, st);
+  if (R <= 1) return launch_rt<KV, D, 1>(a, st);
+  if (R <= 2) return launch_rt<KV, D, 2>(a, st);
+  if (R <= 4) return launch_rt<KV, D, 4>(a, st);
+  if (R <= 5) return launch_rt<KV, D, 5>(a, st);
+  if (R <= 8) return launch_rt<KV, D, 8>(a, st);
+  return launch_rt<KV, D, 16>(a, st);
 }
 
 template <int KV>
-int32_t launch_kv(const SplitArgs& a, int D, int batch, hipStream_t st) {
-  return D == 128 ? launch_d<KV, 128>(a, batch, st) : launch_d<KV, 64>(a, batch, st);
+int32_t launch_kv(const SplitArgs& a, int D, hipStream_t st) {
+  return D == 128 ? launch_d<KV, 128>(a, st) : launch_d<KV, 64>(a, st);
 }
 
 int32_t check_common(const da_host::SplitCall& c, int32_t kv_layout) {
@@ -384,6 +380,9 @@ int32_t check_common(const da_host::SplitCall& c, int32_t kv_layout) {
       c.pt_stride < c.max_pages || c.S <= 0 || c.S > DA_MAX_SPLITS || c.ps <= 0)
     return DA_ERR_INVALID_ARG;
   if ((long long)c.max_pages * c.ps > (1ll << 30)) return DA_ERR_INVALID_ARG;
+  // a work list needs the per-request counts and at most one entry per split slot
+  if (c.work && (!c.counts || c.units <= 0 || (long long)c.units > (long long)c.batch * c.S))
+    return DA_ERR_INVALID_ARG;
   if (kv_layout != DA_KV_NHD && kv_layout != DA_KV_HND) return DA_ERR_INVALID_ARG;
   if (c.D != 64 && c.D != 128) return DA_ERR_UNSUPPORTED;
   if (!da_host::is_pow2(c.ps) || c.ps < 16 || c.ps > 256) return DA_ERR_UNSUPPORTED;
@@ -396,12 +395,15 @@ da_host::SplitCall make_call(const void* q, int q_bf16, const void* k, const voi
                              int32_t pt_stride, int32_t max_pages, const int32_t* seqlens,
                              const int32_t* order, int32_t batch, int32_t qn, int32_t Hq,
                              int32_t Hkv, int32_t D, int32_t ps, int32_t num_pages,
-                             int32_t kv_layout, int32_t S, float scale, int32_t causal, float* o,
-                             float* lse, void* stream) {
+                             int32_t kv_layout, int32_t S, const int32_t* counts,
+                             const int32_t* work, int32_t work_capacity, float scale,
+                             int32_t causal, float* o, float* lse, void* stream) {
   da_host::SplitCall c;
   c.q = q; c.q_bf16 = q_bf16; c.k = k; c.v = v; c.ks = ks; c.vs = vs;
   c.pt = pt; c.pt_stride = pt_stride; c.max_pages = max_pages;
   c.seqlens = seqlens; c.order = order;
+  c.work = work; c.counts = counts;
+  c.units = work ? work_capacity : (int)((long long)S * batch);
   c.batch = batch; c.qn = qn; c.Hq = Hq; c.Hkv = Hkv; c.D = D; c.ps = ps;
   c.num_pages = num_pages; c.S = S;
   if (!da_host::kv_strides(kv_layout, Hkv, ps, c.kv)) c.kv = {0, 0};  // rejected by the check
@@ -413,13 +415,11 @@ da_host::SplitCall make_call(const void* q, int q_bf16, const void* k, const voi
 SplitArgs make_args(const da_host::SplitCall& c) {
   SplitArgs a;
   a.q = c.q; a.k = c.k; a.v = c.v; a.ks = c.ks; a.vs = c.vs; a.pt = c.pt;
-  a.seqlens = c.seqlens; a.order = c.order;
+  a.seqlens = c.seqlens; a.sched = c.sched();
   a.o = c.o; a.lse = c.lse; a.q_bf16 = c.q_bf16;
   a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
   a.qn = c.qn; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = c.Hq / c.Hkv; a.R = a.G * c.qn;
   a.page_size = c.ps; a.log2_ps = __builtin_ctz((unsigned)c.ps); a.num_pages = c.num_pages;
-  a.S = c.S;
-  a.B = 0;  // set at launch
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
@@ -440,21 +440,23 @@ extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k
                                      int32_t batch, int32_t q_per_req, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                                      int32_t num_pages, int32_t kv_layout, int32_t num_splits,
-                                     float softmax_scale, int32_t causal, float* o_partial,
-                                     float* lse_partial, void* stream) {
+                                     const int32_t* split_counts, const int32_t* work_list,
+                                     int32_t work_capacity, float softmax_scale, int32_t causal,
+                                     float* o_partial, float* lse_partial, void* stream) {
   const da_host::SplitCall c =
       make_call(q, dtype == DA_BF16, k_pool, v_pool, nullptr, nullptr, page_table,
                 page_table_stride, max_pages, cache_seqlens, batch_order, batch, q_per_req,
                 num_q_heads, num_kv_heads, head_dim, page_size, num_pages, kv_layout, num_splits,
-                softmax_scale, causal, o_partial, lse_partial, stream);
+                split_counts, work_list, work_capacity, softmax_scale, causal, o_partial,
+                lse_partial, stream);
   if (const int32_t st = check_common(c, kv_layout)) return st;
   if (dtype != DA_BF16 && dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
   if (dtype == DA_BF16) {
     const int32_t fast = da_split_bf16_fast(c);
     if (fast >= 0) return fast;
-    return launch_kv<KV_BF16>(make_args(c), head_dim, batch, c.stream);
+    return launch_kv<KV_BF16>(make_args(c), head_dim, c.stream);
   }
-  return launch_kv<KV_F32>(make_args(c), head_dim, batch, c.stream);
+  return launch_kv<KV_F32>(make_args(c), head_dim, c.stream);
 }
 
 extern "C" int32_t decode_attn_split_int8(
@@ -463,19 +465,21 @@ extern "C" int32_t decode_attn_split_int8(
     int32_t page_table_stride, int32_t max_pages, const int32_t* cache_seqlens,
     const int32_t* batch_order, int32_t batch, int32_t q_per_req, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
-    int32_t kv_layout, int32_t num_splits, float softmax_scale, int32_t causal,
+    int32_t kv_layout, int32_t num_splits, const int32_t* split_counts,
+    const int32_t* work_list, int32_t work_capacity, float softmax_scale, int32_t causal,
     float* o_partial, float* lse_partial, void* stream) {
   const da_host::SplitCall c =
       make_call(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale, v_scale, page_table,
                 page_table_stride, max_pages, cache_seqlens, batch_order, batch, q_per_req,
                 num_q_heads, num_kv_heads, head_dim, page_size, num_pages, kv_layout, num_splits,
-                softmax_scale, causal, o_partial, lse_partial, stream);
+                split_counts, work_list, work_capacity, softmax_scale, causal, o_partial,
+                lse_partial, stream);
   if (const int32_t st = check_common(c, kv_layout)) return st;
   if (!k_scale || !v_scale) return DA_ERR_INVALID_ARG;
   if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
   const int32_t mf = da_split_int8_mfma(c);
   if (mf >= 0) return mf;
-  return launch_kv<KV_I8>(make_args(c), head_dim, batch, c.stream);
+  return launch_kv<KV_I8>(make_args(c), head_dim, c.stream);
 }
 
 extern "C" int32_t decode_attn_split_int4(
@@ -484,17 +488,19 @@ extern "C" int32_t decode_attn_split_int4(
     int32_t page_table_stride, int32_t max_pages, const int32_t* cache_seqlens,
     const int32_t* batch_order, int32_t batch, int32_t q_per_req, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
-    int32_t kv_layout, int32_t num_splits, float softmax_scale, int32_t causal,
+    int32_t kv_layout, int32_t num_splits, const int32_t* split_counts,
+    const int32_t* work_list, int32_t work_capacity, float softmax_scale, int32_t causal,
     float* o_partial, float* lse_partial, void* stream) {
   const da_host::SplitCall c =
       make_call(q, q_dtype == DA_BF16, k_pool, v_pool, k_scale_zero, v_scale_zero, page_table,
                 page_table_stride, max_pages, cache_seqlens, batch_order, batch, q_per_req,
                 num_q_heads, num_kv_heads, head_dim, page_size, num_pages, kv_layout, num_splits,
-                softmax_scale, causal, o_partial, lse_partial, stream);
+                split_counts, work_list, work_capacity, softmax_scale, causal, o_partial,
+                lse_partial, stream);
   if (const int32_t st = check_common(c, kv_layout)) return st;
   if (!k_scale_zero || !v_scale_zero) return DA_ERR_INVALID_ARG;
   if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
   const int32_t mf = da_split_int4_mfma(c);
   if (mf >= 0) return mf;
-  return launch_kv<KV_I4>(make_args(c), head_dim, batch, c.stream);
+  return launch_kv<KV_I4>(make_args(c), head_dim, c.stream);
 }

@@ -124,13 +124,12 @@ struct MfmaArgs {
   const uint8_t* vsz;
   const int32_t* pt;
   const int32_t* seqlens;
-  const int32_t* order;
+  da::Stage1Sched sched;  // (request, split) of every workgroup
   float* o;
   float* lse;
   int pt_stride, max_pages;
   int qn, Hq, Hkv, G, R;
-  int page_size, log2_ps, num_pages, S;
-  int B;  // requests
+  int page_size, log2_ps, num_pages;
   int slot_stride, head_stride;  // rows (see da_host::KvStrides)
   float scale_log2;
   int causal;
@@ -140,10 +139,9 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
 
-  da::WorkUnit wu;
-  if (!da::stage1_unit<true>(a.Hkv, a.S, a.B, wu)) return;
-  const int g = wu.g, s = wu.s;
-  const int b = da::stage1_request(a.order, wu.z, a.B);
+  da::Stage1Item it;
+  if (!da::stage1_item<true>(a.sched, a.Hkv, it)) return;
+  const int g = it.g, s = it.s, b = it.b;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lm = lane & 15, lg = lane >> 4;
@@ -151,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
   const int ps = a.page_size;
   const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
   const int n = (L + ps - 1) >> a.log2_ps;
-  const int cpg = (n + a.S - 1) / a.S;
+  const int cpg = (n + it.S - 1) / it.S;
   const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
   const int t0 = p0 * ps, t1 = min(p1 * ps, L);
   const int ntiles = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
@@ -432,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
       }
     }
     const int i = r / a.G, h = g * a.G + (r % a.G);
-    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.S + s;
+    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.sched.S + s;
     a.o[orow * kD + d] = lsum > 0.f ? o / lsum : 0.f;
     if (d == 0)
       a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum) - kPScale) * da::kLn2 : da::kNegInf;
@@ -446,20 +444,18 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
 int32_t da_split_int4_mfma(const da_host::SplitCall& c) {
   const int G = c.Hq / c.Hkv, R = G * c.qn;
   if (!c.q_bf16 || c.D != kD || R < 9 || R > 16) return -1;
-  if ((c.max_pages + c.S - 1) / c.S > kMaxSplitPages) return -1;
+  if (da_host::max_split_pages(c) > kMaxSplitPages) return -1;
   MfmaArgs a;
   a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
   a.ksz = (const uint8_t*)c.ks; a.vsz = (const uint8_t*)c.vs;
-  a.pt = c.pt; a.seqlens = c.seqlens; a.order = c.order; a.o = c.o; a.lse = c.lse;
+  a.pt = c.pt; a.seqlens = c.seqlens; a.sched = c.sched(); a.o = c.o; a.lse = c.lse;
   a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
   a.qn = c.qn; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = G; a.R = R;
   a.page_size = c.ps; a.log2_ps = __builtin_ctz((unsigned)c.ps); a.num_pages = c.num_pages;
-  a.S = c.S;
-  a.B = c.batch;
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  hipLaunchKernelGGL(split_int4_mfma_kernel, dim3(da_host::stage1_grid(c.Hkv, c.S, c.batch, true)),
+  hipLaunchKernelGGL(split_int4_mfma_kernel, dim3(da_host::stage1_grid(c.Hkv, c.units, true)),
                      dim3(kThreads), 0, c.stream, a);
   return da_host::launch_status();
 }

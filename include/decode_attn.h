@@ -133,6 +133,52 @@ int32_t decode_attn_metadata(const int32_t* seq_lens, const int64_t* req_pool_in
                              void* stream);
 
 /*
+ * decode_attn_metadata plus two options computed in the same launch.
+ *
+ * SWA translation (SGLang PR #29843 digest, "Implementation breakdown": the
+ * fused kernel translates slots through the full-to-SWA mapping the backend
+ * prepares for sliding-window layers, whose K/V live in a second pool):
+ *   full_to_swa      [full_to_swa_len] int64: SWA-pool slot of every
+ *                    full-pool slot, negative for a token not resident there
+ *   swa_page_table   [batch, max_pages] int32 out:
+ *                    full_to_swa[slot] / page_size, slot being the first
+ *                    full-pool slot of logical page j (as for page_table).
+ *                    0 where page_table's guards give 0, where slot >=
+ *                    full_to_swa_len, where the mapped slot is negative, and
+ *                    in the tail.
+ *   Both NULL: no SWA table.
+ *
+ * Per-request split counts (LightLLM PR #1549, "Covered decode kernels":
+ * configurations are tuned over bucketed KV-length keys while each run
+ * picks one from the real request length):
+ *   split_table      HOST [n_buckets] int32 (1..DA_MAX_SPLITS), n_buckets <= 16;
+ *                    copied into the launch, so a captured graph keeps it
+ *   split_counts     [batch] int32 out: S_b = max(1, min(split_table[k],
+ *                    ceil(L_b / page_size), max_splits)) with bucket
+ *                    k = clamp(ceil(L_b / bucket_tokens), 1, n_buckets) - 1
+ *   work_list        [work_capacity] int32 out: one entry b * 256 + s per
+ *                    (request, split s < S_b), requests by descending
+ *                    cache_seqlens (ties by index), splits ascending; -1 after
+ *                    the last entry.  work_capacity >= batch * min(max(split_table),
+ *                    max_splits) (checked), batch < 2^23.
+ *   split_table, split_counts and work_list are all NULL (no schedule) or
+ *   all given.  Pass work_list, split_counts and num_splits = max_splits to
+ *   the split calls and split_counts to decode_attn_merge.
+ */
+int32_t decode_attn_metadata_ex(const int32_t* seq_lens, const int64_t* req_pool_indices,
+                                const int32_t* req_to_token, int64_t req_to_token_rows,
+                                int64_t req_to_token_cols, int64_t req_to_token_stride,
+                                int32_t batch, int32_t page_size, int32_t max_pages,
+                                int32_t q_mode, const int32_t* q_in, int32_t q_stride,
+                                int32_t* cache_seqlens, int32_t* cu_seqlens_k,
+                                int32_t* cu_seqlens_q, int32_t* page_table,
+                                int32_t* batch_order, const int64_t* full_to_swa,
+                                int64_t full_to_swa_len, int32_t* swa_page_table,
+                                const int32_t* split_table, int32_t n_buckets,
+                                int32_t bucket_tokens, int32_t max_splits, int32_t* split_counts,
+                                int32_t* work_list, int32_t work_capacity, void* stream);
+
+/*
  * Stage 1 over a dense bf16 or fp32 cache (GQA flash decode "stage 1" and
  * the num_splits KV-cache decode of LightLLM PR #1549, "Covered decode
  * kernels").  q and the pools share `dtype` (DA_BF16 or DA_FP32).
@@ -148,6 +194,17 @@ int32_t decode_attn_metadata(const int32_t* seq_lens, const int64_t* req_pool_in
  *   means 0..batch-1.  An entry outside [0, batch) is replaced by the grid
  *   index; a non-permutation leaves some requests unprocessed (unspecified
  *   results, never an out-of-bounds access).
+ *   Per-request split counts (work_list != NULL; batch_order is then unused):
+ *   work_list [work_capacity] and split_counts [batch] as written by
+ *   decode_attn_metadata_ex.  Request b is cut into split_counts[b] splits
+ *   (clamped to [1, num_splits]) by the partition rule above, and num_splits
+ *   is only the number of split slots per query row in o_partial /
+ *   lse_partial: slots from split_counts[b] on are not written (pass the
+ *   same split_counts to decode_attn_merge).  Each list entry b * 256 + s
+ *   is one (request, split); entries that are -1, or name no valid request
+ *   or split, are skipped.  1 <= work_capacity <= batch * num_splits.
+ *   With work_list == NULL, split_counts and work_capacity are ignored and
+ *   every request has num_splits splits.
  */
 int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool, const void* v_pool,
                           const int32_t* page_table, int32_t page_table_stride, int32_t max_pages,
@@ -155,9 +212,9 @@ int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool, cons
                           int32_t batch, int32_t q_per_req,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t page_size, int32_t num_pages, int32_t kv_layout,
-                          int32_t num_splits, float softmax_scale, int32_t causal,
-                          float* o_partial,
-                          float* lse_partial, void* stream);
+                          int32_t num_splits, const int32_t* split_counts,
+                          const int32_t* work_list, int32_t work_capacity, float softmax_scale,
+                          int32_t causal, float* o_partial, float* lse_partial, void* stream);
 
 /*
  * Stage 1 over an INT8 cache (LightLLM PR #1549, "Covered decode kernels":
@@ -175,8 +232,9 @@ int32_t decode_attn_split_int8(const void* q, int32_t q_dtype, const int8_t* k_p
                                int32_t batch, int32_t q_per_req,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                int32_t page_size, int32_t num_pages, int32_t kv_layout,
-                               int32_t num_splits, float softmax_scale, int32_t causal,
-                               float* o_partial,
+                               int32_t num_splits, const int32_t* split_counts,
+                               const int32_t* work_list, int32_t work_capacity,
+                               float softmax_scale, int32_t causal, float* o_partial,
                                float* lse_partial, void* stream);
 
 /*
@@ -197,8 +255,9 @@ int32_t decode_attn_split_int4(const void* q, int32_t q_dtype, const uint8_t* k_
                                int32_t batch, int32_t q_per_req,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                int32_t page_size, int32_t num_pages, int32_t kv_layout,
-                               int32_t num_splits, float softmax_scale, int32_t causal,
-                               float* o_partial,
+                               int32_t num_splits, const int32_t* split_counts,
+                               const int32_t* work_list, int32_t work_capacity,
+                               float softmax_scale, int32_t causal, float* o_partial,
                                float* lse_partial, void* stream);
 
 /*
@@ -237,11 +296,14 @@ int32_t decode_attn_append_kv(const void* k_new, const void* v_new, int32_t new_
  * out = sum_s w_s O_s / sum_s w_s, lse = m + ln(sum_s w_s); a row whose
  * splits are all empty gives out 0, lse -inf.
  *   out_dtype DA_BF16 (round to nearest even) or DA_FP32; lse_out may be NULL.
+ *   split_counts (nullable) [batch] int32: the rows of request b combine only
+ *   their first split_counts[b] slots (clamped to [1, num_splits]); the
+ *   other slots are not read.  NULL: all num_splits slots.
  */
 int32_t decode_attn_merge(const float* o_partial, const float* lse_partial, int32_t batch,
                           int32_t q_per_req, int32_t num_q_heads, int32_t head_dim,
-                          int32_t num_splits, void* out, int32_t out_dtype, float* lse_out,
-                          void* stream);
+                          int32_t num_splits, const int32_t* split_counts, void* out,
+                          int32_t out_dtype, float* lse_out, void* stream);
 
 /*
  * Host-only: split count for a launch (LightLLM PR #1549: num_splits is the

@@ -222,9 +222,13 @@ def fp16_pv_o_bound(batch: W.PagedBatch):
 
 
 # ---------------------------------------------------------------- GPU path
-def run_split(da, batch: W.PagedBatch, S: int, batch_order=None):
+def run_split(da, batch: W.PagedBatch, S: int, batch_order=None, sched=None):
+    """Stage 1 with S splits per request, or, with ``sched`` (the metadata dict
+    holding "split_counts" and "work_list"), per-request counts and S slots."""
     w = batch.w
     kw = dict(batch_order=batch_order, kv_layout=w.kv_layout)
+    if sched is not None:
+        kw.update(split_counts=sched["split_counts"], work_list=sched["work_list"])
     if w.kv == W.KV_DENSE:
         return da.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, batch.page_table,
                                     batch.seq_lens, S, w.softmax_scale, w.causal, **kw)
@@ -237,10 +241,39 @@ def run_split(da, batch: W.PagedBatch, S: int, batch_order=None):
                                      w.softmax_scale, w.causal, **kw)
 
 
-def run_decode(da, batch: W.PagedBatch, S: int, out_dtype=torch.bfloat16, batch_order=None):
-    o, l = run_split(da, batch, S, batch_order)
-    out, lse = da.decode_attn_merge(o, l, out_dtype=out_dtype, want_lse=True)
+def run_decode(da, batch: W.PagedBatch, S: int, out_dtype=torch.bfloat16, batch_order=None,
+               sched=None):
+    o, l = run_split(da, batch, S, batch_order, sched)
+    counts = None if sched is None else sched["split_counts"]
+    out, lse = da.decode_attn_merge(o, l, out_dtype=out_dtype, want_lse=True, split_counts=counts)
     return out, lse, o, l
+
+
+def schedule(da, batch: W.PagedBatch, table, bucket_tokens, max_splits, work_capacity=None):
+    """The metadata prelude with a per-request split table (graph-free use)."""
+    w = batch.w
+    return da.decode_attn_metadata(batch.seq_lens, batch.req_pool_indices, batch.req_to_token,
+                                   w.page_size, batch.max_pages, split_table=table,
+                                   bucket_tokens=bucket_tokens, max_splits=max_splits,
+                                   work_capacity=work_capacity)
+
+
+def oracle_partials_per_request(batch: W.PagedBatch, S: int, counts):
+    h = host_inputs(batch)
+    w = batch.w
+    return OA.split_partials(h["q"], h["k"], h["v"], h["page_table"], h["seq_lens"],
+                             w.page_size, w.softmax_scale, S, causal=w.causal,
+                             split_counts=counts)
+
+
+def blank_unused_slots(o: np.ndarray, l: np.ndarray, counts):
+    """Host copies of partials with the slots past each request's count set to
+    (0, -inf), the oracle's value there (stage 1 does not write them)."""
+    o, l = o.copy(), l.copy()
+    for b, c in enumerate(np.asarray(counts).reshape(-1)):
+        o[b, :, :, int(c):] = 0.0
+        l[b, :, :, int(c):] = -np.inf
+    return o, l
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:

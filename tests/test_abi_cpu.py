@@ -50,17 +50,18 @@ def test_strerror_and_version(lib):
     assert lib.decode_attn_strerror(2) == b"unsupported shape or dtype"
     assert lib.decode_attn_strerror(3) == b"kernel launch failed"
     assert lib.decode_attn_strerror(99) == b"unknown status"
-    assert lib.decode_attn_version() == 200
+    assert lib.decode_attn_version() == 300
 
 
 def _split_args(**kw):
     a = dict(q=FAKE, dtype=B.DA_BF16, k=FAKE, v=FAKE, pt=FAKE, pt_stride=8, max_pages=8,
              seqlens=FAKE, order=None, batch=4, qn=1, Hq=32, Hkv=8, D=128, ps=64, num_pages=100,
-             layout=B.DA_KV_NHD, S=4, scale=0.1, causal=0, o=FAKE, lse=FAKE, stream=None)
+             layout=B.DA_KV_NHD, S=4, counts=None, work=None, cap=0, scale=0.1, causal=0,
+             o=FAKE, lse=FAKE, stream=None)
     a.update(kw)
     return [a[k] for k in ("q", "dtype", "k", "v", "pt", "pt_stride", "max_pages", "seqlens",
                            "order", "batch", "qn", "Hq", "Hkv", "D", "ps", "num_pages", "layout",
-                           "S", "scale",
+                           "S", "counts", "work", "cap", "scale",
                            "causal", "o", "lse", "stream")]
 
 
@@ -69,6 +70,9 @@ def _split_args(**kw):
     (dict(S=0), 1), (dict(S=257), 1), (dict(qn=17), 1), (dict(pt_stride=4), 1),
     (dict(num_pages=0), 1), (dict(D=96), 2), (dict(ps=48), 2), (dict(ps=8), 2),
     (dict(dtype=7), 2), (dict(Hq=64, Hkv=2, qn=2), 2), (dict(layout=2), 1), (dict(layout=-1), 1),
+    # work lists: counts required, 1 <= capacity <= batch * S
+    (dict(work=FAKE, cap=8), 1), (dict(work=FAKE, counts=FAKE, cap=0), 1),
+    (dict(work=FAKE, counts=FAKE, cap=17), 1),
 ])
 def test_split_validation(lib, kw, status):
     assert lib.decode_attn_split(*_split_args(**kw)) == status
@@ -83,13 +87,16 @@ def test_int8_int4_validation(lib):
     assert lib.decode_attn_split_int4(*args4) == 1
     args4 = base[:2] + [FAKE, FAKE, FAKE, FAKE] + base[4:13] + [80] + base[14:]
     assert lib.decode_attn_split_int4(*args4) == 2
+    args8 = base[:2] + [FAKE, FAKE, FAKE, FAKE] + _split_args(work=FAKE, cap=4)[4:]
+    assert lib.decode_attn_split_int8(*args8) == 1  # work list without counts
 
 
 def test_merge_and_metadata_and_gather_validation(lib):
-    assert lib.decode_attn_merge(None, FAKE, 1, 1, 8, 128, 4, FAKE, B.DA_BF16, None, None) == 1
-    assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 96, 4, FAKE, B.DA_BF16, None, None) == 2
-    assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 128, 4, FAKE, 5, None, None) == 2
-    assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 128, 0, FAKE, B.DA_BF16, None, None) == 1
+    # (o, lse, batch, q, Hq, D, S, split_counts, out, out_dtype, lse_out, stream)
+    assert lib.decode_attn_merge(None, FAKE, 1, 1, 8, 128, 4, None, FAKE, B.DA_BF16, None, None) == 1
+    assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 96, 4, None, FAKE, B.DA_BF16, None, None) == 2
+    assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 128, 4, FAKE, FAKE, 5, None, None) == 2
+    assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 128, 0, None, FAKE, B.DA_BF16, None, None) == 1
     md = [FAKE, FAKE, FAKE, 4, 64, 64, 2, 16, 4, B.DA_Q_STRIDED, None, 1, FAKE, FAKE, FAKE, FAKE,
           None, None]
     bad = list(md); bad[0] = None
@@ -100,6 +107,25 @@ def test_merge_and_metadata_and_gather_validation(lib):
     assert lib.decode_attn_metadata(*bad) == 1
     bad = list(md); bad[5] = 32  # stride < cols
     assert lib.decode_attn_metadata(*bad) == 1
+    # metadata_ex: (..., batch_order, f2s, f2s_len, swa_pt, table, n_buckets, bucket_tokens,
+    #               max_splits, split_counts, work_list, capacity, stream)
+    table = (ctypes.c_int32 * 3)(1, 4, 8)
+    ex = md[:17] + [None, 0, None, table, 3, 4096, 8, FAKE, FAKE, 16, None]
+    def bad_ex(i, v):
+        b = list(ex); b[i] = v
+        return lib.decode_attn_metadata_ex(*b)
+    assert bad_ex(17, FAKE) == 1                    # mapping without its output table
+    assert bad_ex(19, FAKE) == 1                    # output without a mapping
+    assert bad_ex(25, None) == 1                    # table without a work list
+    assert bad_ex(24, None) == 1                    # ... or without counts
+    assert bad_ex(21, 0) == 1 and bad_ex(21, 17) == 1  # bucket count
+    assert bad_ex(22, 0) == 1                       # bucket width
+    assert bad_ex(23, 0) == 1 and bad_ex(23, 257) == 1  # max_splits
+    assert bad_ex(26, 15) == 1                      # capacity < batch * min(max(table), max_splits)
+    zero = (ctypes.c_int32 * 3)(1, 0, 8)
+    assert bad_ex(20, zero) == 1                    # a table entry out of range
+    b = list(ex); b[17], b[18], b[19] = FAKE, 0, FAKE
+    assert lib.decode_attn_metadata_ex(*b) == 1     # empty mapping
     # (pool, row_bytes, Hkv, layout, page_size, num_pages, pt, pt_stride, max_pages, seqlens,
     #  cu_k, batch, out, stream)
     g = [FAKE, 6, 2, B.DA_KV_NHD, 16, 10, FAKE, 4, 4, FAKE, FAKE, 2, FAKE, None]

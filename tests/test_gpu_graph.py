@@ -6,7 +6,10 @@ graph, "Features and motivation").
 
 Between replays the test changes the inputs in place (shorter KV lengths, new
 queries), runs the same calls eagerly on separate buffers, synchronises, and
-requires every replay to match the eager result bit for bit.  No call in the
+requires every replay to match the eager result bit for bit.  With a
+per-request split table the schedule (split counts, work list) is rebuilt
+on the device at every replay from the new lengths, so the captured graph
+follows them; the table itself is part of the captured launch.  No call in the
 step records a memset (stage 1 overwrites every partial slot), so nothing in
 the graph depends on one.
 """
@@ -33,8 +36,8 @@ CASES = [
 class Step:
     """Buffers and calls of one decode step; every output is caller-owned."""
 
-    def __init__(self, da, batch, S):
-        self.da, self.batch, self.S = da, batch, S
+    def __init__(self, da, batch, S, table=None):
+        self.da, self.batch, self.S, self.table = da, batch, S, table
         w = batch.w
         B, qn, Hq, D = batch.q.shape
         dev = batch.q.device
@@ -43,6 +46,9 @@ class Step:
                    "cu_seqlens_q": torch.empty(B + 1, **i32),
                    "page_table": torch.empty(B, batch.max_pages, **i32),
                    "batch_order": torch.empty(B, **i32)}
+        if table is not None:
+            self.md["split_counts"] = torch.empty(B, **i32)
+            self.md["work_list"] = torch.empty(B * S, **i32)
         self.o = torch.empty((B, qn, Hq, S, D), dtype=torch.float32, device=dev)
         self.l = torch.empty((B, qn, Hq, S), dtype=torch.float32, device=dev)
         self.out = torch.empty((B, qn, Hq, D), dtype=torch.bfloat16, device=dev)
@@ -51,10 +57,16 @@ class Step:
 
     def __call__(self):
         da, b, w, md = self.da, self.batch, self.w, self.md
+        sched = {}
+        if self.table is not None:
+            sched = dict(split_table=self.table, bucket_tokens=512, max_splits=self.S,
+                         work_capacity=md["work_list"].shape[0])
         da.decode_attn_metadata(b.seq_lens, b.req_pool_indices, b.req_to_token, w.page_size,
-                                b.max_pages, q_stride=w.q_per_req, out=md)
+                                b.max_pages, q_stride=w.q_per_req, out=md, **sched)
         kw = dict(o_partial=self.o, lse_partial=self.l, batch_order=md["batch_order"],
                   kv_layout=w.kv_layout)
+        if self.table is not None:
+            kw.update(split_counts=md["split_counts"], work_list=md["work_list"])
         args = (md["page_table"], md["cache_seqlens"], self.S, w.softmax_scale, w.causal)
         if w.kv == W.KV_DENSE:
             da.decode_attn_split(b.q, b.k_pool, b.v_pool, *args, **kw)
@@ -62,16 +74,21 @@ class Step:
             da.decode_attn_split_int8(b.q, b.k_pool, b.v_pool, b.k_scale, b.v_scale, *args, **kw)
         else:
             da.decode_attn_split_int4(b.q, b.k_pool, b.v_pool, b.k_scale, b.v_scale, *args, **kw)
-        da.decode_attn_merge(self.o, self.l, out=self.out, lse_out=self.lse)
+        da.decode_attn_merge(self.o, self.l, out=self.out, lse_out=self.lse,
+                             split_counts=md.get("split_counts"))
 
 
+TABLE = [1, 2, 3, 4, 6, 8, 8, 8]  # per 512-token bucket
+
+
+@pytest.mark.parametrize("table", [None, TABLE], ids=["batch_wide_S", "per_request"])
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
-def test_graph_replay_matches_eager(gpu, w):
-    log(f"graph {w.name}")
+def test_graph_replay_matches_eager(gpu, w, table):
+    log(f"graph {w.name} table={table}")
     batch = W.make_batch(w, device="cuda")
-    S = 4
-    step = Step(gpu, batch, S)
-    ref = Step(gpu, batch, S)  # eager twin on its own buffers
+    S = 4 if table is None else 8
+    step = Step(gpu, batch, S, table)
+    ref = Step(gpu, batch, S, table)  # eager twin on its own buffers
 
     step()  # warm up outside capture
     torch.cuda.synchronize()
@@ -91,7 +108,7 @@ def test_graph_replay_matches_eager(gpu, w):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for k in ("cache_seqlens", "cu_seqlens_k", "cu_seqlens_q", "page_table", "batch_order"):
+        for k in ref.md:
             assert torch.equal(step.md[k], ref.md[k]), (rep, k)
         assert torch.equal(step.out, ref.out), rep
         assert torch.equal(step.lse, ref.lse), rep

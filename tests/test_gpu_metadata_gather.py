@@ -115,3 +115,47 @@ def test_gather_is_bit_exact(w):
             want = OA.gather_tokens(raw, pt[b], int(L[b]), w.page_size)
             assert np.array_equal(got_raw[off:off + L[b]], want), (b, pool.dtype)
             off += int(L[b])
+
+
+# ---------------------------------------------------------------- SWA translation
+def test_swa_hand_built_batch(gpu):
+    g = json.load(open(os.path.join(GOLDEN, "metadata_hand.json")))
+    s = json.load(open(os.path.join(GOLDEN, "metadata_swa_hand.json")))
+    log("metadata SWA hand batch")
+    args = (_i32(g["seq_lens"]), torch.tensor(g["req_pool_indices"], dtype=torch.int64, device="cuda"),
+            _i32(g["req_to_token"]), g["page_size"], g["max_pages"])
+    f2s = torch.tensor(s["full_to_swa"], dtype=torch.int64, device="cuda")
+    md = gpu.decode_attn_metadata(*args, q_stride=g["q_stride"], full_to_swa=f2s)
+    assert md["swa_page_table"].tolist() == s["expect"]["swa_page_table"]
+    assert md["page_table"].tolist() == g["expect"]["page_table"]
+    assert md["cu_seqlens_k"].tolist() == g["expect"]["cu_seqlens_k"]
+    assert md["batch_order"].tolist() == g["expect"]["batch_order"]
+    md = gpu.decode_attn_metadata(*args, q_stride=g["q_stride"], full_to_swa=f2s[:40].contiguous())
+    assert md["swa_page_table"].tolist() == s["expect"]["swa_page_table_mapping40"]
+
+
+@pytest.mark.parametrize("w", [W.TINY_FP32, W.RAGGED_B64.scaled(batch=300, length_lo=1, length_hi=3000),
+                               W.RAGGED_B64], ids=lambda w: w.name)
+def test_swa_generated_bit_exact(w):
+    """A page-aligned SWA pool over a random page permutation with evicted
+    (unmapped) pages and random junk slots; every output bit-exact, and the
+    full-pool outputs unchanged by the option."""
+    rng = np.random.Generator(np.random.PCG64(1000 + w.seed))
+    L = W.draw_lengths(w, rng)
+    pt, r2t, rpi, P = W.build_layout(w, L, rng)
+    ps = w.page_size
+    log(f"metadata SWA {w.name}: B={len(L)} pages={P}")
+    pi = rng.permutation(P + 7)[:P]
+    evicted = rng.random(P) < 0.25
+    f2s = (pi[:, None] * ps + np.arange(ps)[None, :]).astype(np.int64)
+    f2s[evicted] = -1
+    f2s = f2s.reshape(-1)[: P * ps - 3]  # the last page's tail past the mapping
+    ref = OM.metadata(L, rpi, r2t, ps, pt.shape[1], full_to_swa=f2s)
+    dev_args = (_i32(L), torch.as_tensor(rpi, dtype=torch.int64, device="cuda"), _i32(r2t), ps,
+                pt.shape[1])
+    md = gpu_mod.decode_attn_metadata(*dev_args, full_to_swa=torch.as_tensor(f2s, device="cuda"))
+    for k in ("cache_seqlens", "cu_seqlens_k", "cu_seqlens_q", "page_table", "batch_order",
+              "swa_page_table"):
+        assert np.array_equal(md[k].cpu().numpy().astype(np.int64), ref[k]), k
+    plain = gpu_mod.decode_attn_metadata(*dev_args)
+    assert torch.equal(plain["page_table"], md["page_table"])
