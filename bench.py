@@ -1,7 +1,8 @@
 """Decode-attention benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splits S]
-                    [--no-cpu-baseline] [--tune]
+                    [--sched batch|request] [--chunk PAGES] [--no-cpu-baseline]
+                    [--tune [FORMATS]] [--tune-chunks [FORMATS]]
 
 One step is the whole hot path over one synthetic batch: the metadata
 prelude (cache_seqlens / cu_seqlens_k/q / page_table in one launch), the
@@ -16,6 +17,11 @@ value      = algorithmic bytes of one step / measured step time (GB/s), the K
 roofline   = the stage-1 kernel: algorithmic bytes per launch / its average
              launch time from HIP events on the launch stream, against
              MI355X's 8 TB/s HBM peak.
+schedule   = how stage 1 is split: "batch" (one tuned num_splits for every
+             request, the default) or "request" (the metadata prelude picks
+             each request's split count from its own length through a
+             per-bucket table derived from a tuned split size); the other
+             schedule's stage-1 time is reported beside it (alt_schedule).
 Algorithmic bytes: every attended K/V byte once per (request, kv-head)
 (plus quantisation scales), Q, the output, the page-table entries read and
 the lengths.  Split partials are method overhead and are not counted.
@@ -36,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BUCKET_TOKENS = 4096  # KV-length bucket of the split tables
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -46,11 +53,19 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="ragged_bf16_b64_hq40_hkv8_d128_p64_L1k-32k")
     p.add_argument("--splits", type=int, default=0, help="override num_splits (0 = table)")
+    p.add_argument("--sched", choices=("batch", "request"), default="batch",
+                   help="batch-wide num_splits, or per-request counts from the metadata prelude")
+    p.add_argument("--chunk", type=int, default=0,
+                   help="per-request split size in pages (0 = tuned table)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-alt", action="store_true",
+                   help="skip timing the other schedule (keeps a kernel trace to one configuration)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--tune", nargs="?", const="all", default=None,
                    help="sweep num_splits per bucket and write the table (optionally a comma list "
                         "of cache formats: bf16,int8,int4)")
+    p.add_argument("--tune-chunks", nargs="?", const="all", default=None,
+                   help="sweep the per-request split size per batch key and write it to the table")
     p.add_argument("--profile-only", action="store_true",
                    help="for rocprofv3 --pmc runs: one 1 GiB copy (the byte-count reference), "
                         "then --steps whole steps, no timing")
@@ -101,24 +116,78 @@ def kernel_hash(kv="bf16") -> str:
     return h.hexdigest()[:16]
 
 
-def stage1(da, batch, S, o, l, md=None):
+def stage1(da, batch, S, o, l, md=None, sched=False):
+    """Stage 1 of the batch; with ``sched`` the metadata's per-request split
+    counts and work list drive it (S is then the slots per query row)."""
     from decode_attention_paged_gqa_amd import workloads as W
 
     w = batch.w
     md = batch.md if md is None else md
+    kw = dict(kv_layout=w.kv_layout)
+    if sched:
+        kw.update(split_counts=md["split_counts"], work_list=md["work_list"])
+    else:
+        kw.update(batch_order=md["batch_order"])
     if w.kv == W.KV_DENSE:
         return da.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, md["page_table"],
-                                    md["cache_seqlens"], S, w.softmax_scale, w.causal, o, l,
-                                    batch_order=md["batch_order"], kv_layout=w.kv_layout)
+                                    md["cache_seqlens"], S, w.softmax_scale, w.causal, o, l, **kw)
     if w.kv == W.KV_INT8:
         return da.decode_attn_split_int8(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
                                          batch.v_scale, md["page_table"], md["cache_seqlens"], S,
-                                         w.softmax_scale, w.causal, o, l,
-                                         batch_order=md["batch_order"], kv_layout=w.kv_layout)
+                                         w.softmax_scale, w.causal, o, l, **kw)
     return da.decode_attn_split_int4(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
                                      batch.v_scale, md["page_table"], md["cache_seqlens"], S,
-                                     w.softmax_scale, w.causal, o, l,
-                                     batch_order=md["batch_order"], kv_layout=w.kv_layout)
+                                     w.softmax_scale, w.causal, o, l, **kw)
+
+
+class Step:
+    """Caller-owned buffers and the three calls of one whole step.
+
+    table=None: every request has S splits.  table=[per-bucket counts]: the
+    metadata prelude also writes split_counts and the work list, stage 1 and
+    the merge follow them, and S = max(table) slots per query row."""
+
+    def __init__(self, da, batch, torch, S=None, table=None):
+        w = batch.w
+        self.da, self.batch, self.table = da, batch, table
+        self.S = max(table) if table is not None else S
+        B, qn, Hq, D = batch.q.shape
+        self.o = torch.empty((B, qn, Hq, self.S, D), dtype=torch.float32, device="cuda")
+        self.l = torch.empty((B, qn, Hq, self.S), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((B, qn, Hq, D), dtype=torch.bfloat16, device="cuda")
+        self.md = {k: torch.empty_like(v) for k, v in batch.md.items()}
+        self.sched_kw = {}
+        if table is not None:
+            self.md["split_counts"] = torch.empty(B, dtype=torch.int32, device="cuda")
+            self.md["work_list"] = torch.empty(B * self.S, dtype=torch.int32, device="cuda")
+            self.sched_kw = dict(split_table=table, bucket_tokens=BUCKET_TOKENS,
+                                 max_splits=self.S, work_capacity=B * self.S)
+
+    def meta(self):
+        b, w = self.batch, self.batch.w
+        self.da.decode_attn_metadata(b.seq_lens, b.req_pool_indices, b.req_to_token, w.page_size,
+                                     b.max_pages, q_stride=w.q_per_req, out=self.md,
+                                     **self.sched_kw)
+
+    def split(self):
+        stage1(self.da, self.batch, self.S, self.o, self.l, md=self.md,
+               sched=self.table is not None)
+
+    def merge(self):
+        self.da.decode_attn_merge(self.o, self.l, out=self.out,
+                                  split_counts=self.md.get("split_counts"))
+
+    def __call__(self):
+        self.meta()
+        self.split()
+        self.merge()
+
+    def describe(self):
+        if self.table is None:
+            return {"mode": "batch", "num_splits": self.S}
+        items = int(self.md["split_counts"].sum().item())
+        return {"mode": "request", "table": list(self.table), "bucket_tokens": BUCKET_TOKENS,
+                "max_splits": self.S, "work_items": items}
 
 
 def rows_per_kv_head(w):
@@ -131,38 +200,31 @@ def kv_name(w):
     return w.dtype if w.kv == W.KV_DENSE else w.kv
 
 
-def time_config(da, batch, S, steps, warmup, torch):
+def time_config(step, steps, warmup, torch):
     """Times `steps` whole steps; returns (ms_per_step, split_ms_avg, merge_ms_avg, meta_ms_avg)."""
-    w = batch.w
-    B, qn, Hq, D = batch.q.shape
-    o = torch.empty((B, qn, Hq, S, D), dtype=torch.float32, device="cuda")
-    l = torch.empty((B, qn, Hq, S), dtype=torch.float32, device="cuda")
-    out = torch.empty((B, qn, Hq, D), dtype=torch.bfloat16, device="cuda")
-    md_out = dict(batch.md)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def run(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        da.decode_attn_metadata(batch.seq_lens, batch.req_pool_indices, batch.req_to_token,
-                                w.page_size, batch.max_pages, q_stride=w.q_per_req, out=md_out)
+        step.meta()
         if ev is not None:
             ev[1].record(stream)
-        stage1(da, batch, S, o, l)
+        step.split()
         if ev is not None:
             ev[2].record(stream)
-        da.decode_attn_merge(o, l, out=out)
+        step.merge()
         if ev is not None:
             ev[3].record(stream)
 
     for _ in range(warmup):
-        step()
+        run()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(evs[i])
+        run(evs[i])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     meta = np.mean([e[0].elapsed_time(e[1]) for e in evs])
@@ -171,22 +233,9 @@ def time_config(da, batch, S, steps, warmup, torch):
     return wall_ms, float(split), float(merge), float(meta)
 
 
-def time_graph(da, batch, S, steps, warmup, torch):
-    """The same step captured once in a HIP graph (S fixed at capture, as the pages
-    deploy their tuned kernels) and replayed; returns ms per replayed step."""
-    w = batch.w
-    B, qn, Hq, D = batch.q.shape
-    o = torch.empty((B, qn, Hq, S, D), dtype=torch.float32, device="cuda")
-    l = torch.empty((B, qn, Hq, S), dtype=torch.float32, device="cuda")
-    out = torch.empty((B, qn, Hq, D), dtype=torch.bfloat16, device="cuda")
-    md_out = {k: torch.empty_like(v) for k, v in batch.md.items()}
-
-    def step():
-        da.decode_attn_metadata(batch.seq_lens, batch.req_pool_indices, batch.req_to_token,
-                                w.page_size, batch.max_pages, q_stride=w.q_per_req, out=md_out)
-        stage1(da, batch, S, o, l, md=md_out)
-        da.decode_attn_merge(o, l, out=out)
-
+def time_graph(step, steps, warmup, torch):
+    """The same step captured once in a HIP graph (the schedule fixed at capture, as
+    the pages deploy their tuned kernels) and replayed; returns ms per replayed step."""
     step()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -203,16 +252,15 @@ def time_graph(da, batch, S, steps, warmup, torch):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def time_split_only(da, batch, S, iters, torch):
-    B, qn, Hq, D = batch.q.shape
-    o = torch.empty((B, qn, Hq, S, D), dtype=torch.float32, device="cuda")
-    l = torch.empty((B, qn, Hq, S), dtype=torch.float32, device="cuda")
+def time_split_only(step, iters, torch):
+    """Average stage-1 time (ms) over `iters` back-to-back launches."""
+    step.meta()
     for _ in range(3):
-        stage1(da, batch, S, o, l)
+        step.split()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(iters):
-        stage1(da, batch, S, o, l)
+        step.split()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / iters
@@ -311,7 +359,7 @@ def tune(da, torch, which="all"):
                                     length_hi=Lmax, pin_max=True, seed=100 + 10 * k + rep)
                     batch = make_resident(da, w, torch)
                     for S in CANDIDATES:
-                        tot[S] += time_split_only(da, batch, S, 10, torch)
+                        tot[S] += time_split_only(Step(da, batch, torch, S=S), 10, torch)
                     del batch
                     torch.cuda.empty_cache()
                 best = min(CANDIDATES, key=lambda S: (tot[S], S))
@@ -324,10 +372,48 @@ def tune(da, torch, which="all"):
     print(json.dumps({"tuned": list(table.tables)}), flush=True)
 
 
+def tune_chunks(da, torch, which="all"):
+    """Sweep the per-request split size (pages) per batch key over ragged batches
+    whose longest request sits in buckets 2, 4 and 8 (the 32K representative
+    length); write the best size per batch key into splits_table.json."""
+    from decode_attention_paged_gqa_amd import workloads as W
+    from decode_attention_paged_gqa_amd.splits import (BATCH_KEYS, CHUNK_CANDIDATES, SplitTable,
+                                                       kernel_key, per_request_table)
+
+    table = SplitTable.load()
+    variants = [W.RAGGED_B64, W.BF16_B16, W.INT8_B32, W.INT4_MTP_B64]
+    if which != "all":
+        keep = set(which.split(","))
+        variants = [v for v in variants if kv_name(v) in keep]
+    for base in variants:
+        key = kernel_key(kv_name(base), rows_per_kv_head(base), base.head_dim, base.page_size,
+                         base.kv_layout)
+        row = []
+        for bk in BATCH_KEYS:
+            tot = {c: 0.0 for c in CHUNK_CANDIDATES}
+            for k in (2, 4, 8):
+                Lmax = k * BUCKET_TOKENS
+                w = base.scaled(batch=bk, lengths="loguniform", length_lo=max(64, Lmax // 32),
+                                length_hi=Lmax, pin_max=True, seed=200 + k)
+                batch = make_resident(da, w, torch)
+                for c in CHUNK_CANDIDATES:
+                    t = per_request_table(c, w.page_size, BUCKET_TOKENS)
+                    tot[c] += time_split_only(Step(da, batch, torch, table=t), 10, torch)
+                del batch
+                torch.cuda.empty_cache()
+            best = min(CHUNK_CANDIDATES, key=lambda c: (tot[c], -c))
+            row.append(best)
+            print(f"tune-chunks {key} B={bk} -> {best} pages "
+                  + " ".join(f"{c}:{tot[c] * 1e3:.1f}" for c in CHUNK_CANDIDATES), flush=True)
+        table.chunk_pages[key] = row
+    table.save()
+    print(json.dumps({"tuned_chunks": table.chunk_pages}), flush=True)
+
+
 COPY_BYTES = 1 << 30
 
 
-def profile_only(da, w, batch, S, steps, torch):
+def profile_only(step, steps, torch):
     """Dispatches for counter collection: a plain 1 GiB device copy whose byte
     count is known (it calibrates FETCH_SIZE / WRITE_SIZE), then whole steps."""
     src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
@@ -336,19 +422,12 @@ def profile_only(da, w, batch, S, steps, torch):
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    B, qn, Hq, D = batch.q.shape
-    o = torch.empty((B, qn, Hq, S, D), dtype=torch.float32, device="cuda")
-    l = torch.empty((B, qn, Hq, S), dtype=torch.float32, device="cuda")
-    out = torch.empty((B, qn, Hq, D), dtype=torch.bfloat16, device="cuda")
-    md_out = dict(batch.md)
     for _ in range(steps):
-        da.decode_attn_metadata(batch.seq_lens, batch.req_pool_indices, batch.req_to_token,
-                                w.page_size, batch.max_pages, q_stride=w.q_per_req, out=md_out)
-        stage1(da, batch, S, o, l)
-        da.decode_attn_merge(o, l, out=out)
+        step()
     torch.cuda.synchronize()
-    ab = algorithmic_bytes(w, batch.lengths)
-    print(json.dumps({"profile_only": w.name, "num_splits": S, "copy_bytes": COPY_BYTES,
+    w = step.batch.w
+    ab = algorithmic_bytes(w, step.batch.lengths)
+    print(json.dumps({"profile_only": w.name, "schedule": step.describe(), "copy_bytes": COPY_BYTES,
                       "split_algorithmic_bytes": ab["split"], "kernel_hash": kernel_hash(kv_name(w))}),
           flush=True)
 
@@ -418,26 +497,41 @@ def main():
 
     import decode_attention_paged_gqa_amd as da
     from decode_attention_paged_gqa_amd import workloads as W
-    from decode_attention_paged_gqa_amd.splits import SplitTable, kernel_key
+    from decode_attention_paged_gqa_amd.splits import SplitTable, kernel_key, per_request_table
 
     da.load()
-    if args.tune:
-        tune(da, torch, args.tune)
+    if args.tune or args.tune_chunks:
+        if args.tune:
+            tune(da, torch, args.tune)
+        if args.tune_chunks:
+            tune_chunks(da, torch, args.tune_chunks)
         return
     w = W.WORKLOADS[args.workload]
     batch = make_resident(da, w, torch)
     key = kernel_key(kv_name(w), rows_per_kv_head(w), w.head_dim, w.page_size, w.kv_layout)
-    S = args.splits or SplitTable.load().pick(key, w.batch, int(batch.lengths.max()))
+    tables = SplitTable.load()
+    S = args.splits or tables.pick(key, w.batch, int(batch.lengths.max()))
+    chunk = args.chunk or tables.chunk_for(key, w.batch)
+    req_table = per_request_table(chunk, w.page_size, tables.bucket_tokens)
+    batch_step = Step(da, batch, torch, S=S)
+    req_step = Step(da, batch, torch, table=req_table)
+    step, alt = (batch_step, req_step) if args.sched == "batch" else (req_step, batch_step)
     if args.profile_only:
-        profile_only(da, w, batch, S, args.steps, torch)
+        profile_only(step, args.steps, torch)
         return
-    ms, split_ms, merge_ms, meta_ms = time_config(da, batch, S, args.steps, args.warmup, torch)
+    ms, split_ms, merge_ms, meta_ms = time_config(step, args.steps, args.warmup, torch)
     # the same step captured once in a HIP graph and replayed (reported beside it)
     try:
-        graph_ms = time_graph(da, batch, S, args.steps, args.warmup, torch)
+        graph_ms = time_graph(step, args.steps, args.warmup, torch)
     except Exception as e:
         print(f"bench.py: graph capture failed ({e})", file=sys.stderr)
         graph_ms = None
+    alt_split_ms = None if args.no_alt else time_split_only(alt, args.steps, torch)
+    schedule, alt_schedule = step.describe(), alt.describe()
+    if step is req_step:
+        schedule["chunk_pages"] = chunk
+    else:
+        alt_schedule["chunk_pages"] = chunk
     ab = algorithmic_bytes(w, batch.lengths)
     value = ab["step"] / (ms * 1e-3) / 1e9
     achieved = ab["split"] / (split_ms * 1e-3) / 1e9
@@ -445,7 +539,9 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         t = json.load(open(TRAFFIC_FILE))
         ent = t.get(f"{w.name}/{w.kv_layout}")
-        if ent and ent.get("kernel_hash") == kernel_hash(kv_name(w)) and ent.get("num_splits") == S:
+        if ent and ent.get("kernel_hash") == kernel_hash(kv_name(w)) \
+                and ent.get("schedule", {"mode": "batch", "num_splits": ent.get("num_splits")}) \
+                == {k: schedule[k] for k in ("mode", "num_splits") if k in schedule}:
             traffic = ent.get("hbm_bytes_per_launch")
     res = {
         "metric": "decode-attn achieved HBM GB/s (% of peak) + us/call, B=64 KV=32K bf16",
@@ -466,8 +562,12 @@ def main():
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "page_size": w.page_size, "kv_layout": w.kv_layout,
                    "kv_len_max": int(batch.lengths.max()), "kv_len_mean": float(batch.lengths.mean()),
-                   "kv_tokens": int(batch.lengths.sum()), "num_splits": S, "seed": w.seed,
+                   "kv_tokens": int(batch.lengths.sum()), "num_splits": step.S, "seed": w.seed,
                    "parallelism": "single-gpu"},
+        "schedule": schedule,
+        "alt_schedule": None if alt_split_ms is None else dict(
+            alt_schedule, split_us=round(alt_split_ms * 1e3, 2),
+            frac=round(ab["split"] / (alt_split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)),
         "kernels_us": {"metadata": round(meta_ms * 1e3, 2), "split": round(split_ms * 1e3, 2),
                        "merge": round(merge_ms * 1e3, 2)},
         "roofline": {"bound": "hbm", "kernel": "split (stage 1)", "achieved": round(achieved, 2),

@@ -9,6 +9,13 @@ Here the tuned values live in ``splits_table.json`` (written by
 then by 4096-token bucket; the lookup itself is the C helper
 ``decode_attn_pick_splits``.  Under graph capture, where lengths are not
 known on the host, callers key on the representative length 32768.
+
+Per-request split counts (the metadata prelude's schedule option) take a
+per-bucket table too.  It is derived from one tuned number per variant and
+batch key, the target split size in pages: bucket k (1-based) gets
+ceil(k * bucket_pages / chunk_pages) splits, so every request's splits come
+out near that size whatever the batch's length mix, and the device picks
+each request's count from its own length -- also inside a captured graph.
 """
 from __future__ import annotations
 
@@ -25,6 +32,8 @@ BUCKET_TOKENS = 4096
 N_BUCKETS = 8
 BATCH_KEYS = (16, 32, 64)
 CANDIDATES = (1, 2, 4, 8, 16, 32)
+CHUNK_CANDIDATES = (16, 24, 32, 48, 64, 96, 128, 192)
+DEFAULT_CHUNK_PAGES = 64
 
 
 def kernel_key(kv: str, rows: int, head_dim: int, page_size: int, kv_layout: str = "NHD") -> str:
@@ -47,6 +56,7 @@ class SplitTable:
     bucket_tokens: int = BUCKET_TOKENS
     batch_keys: List[int] = field(default_factory=lambda: list(BATCH_KEYS))
     tables: Dict[str, List[List[int]]] = field(default_factory=dict)
+    chunk_pages: Dict[str, List[int]] = field(default_factory=dict)  # per batch key
 
     @classmethod
     def load(cls, path: str = None) -> "SplitTable":
@@ -56,7 +66,8 @@ class SplitTable:
         with open(path) as f:
             d = json.load(f)
         return cls(bucket_tokens=d["bucket_tokens"], batch_keys=list(d["batch_keys"]),
-                   tables={k: [list(r) for r in v] for k, v in d["tables"].items()})
+                   tables={k: [list(r) for r in v] for k, v in d["tables"].items()},
+                   chunk_pages={k: list(v) for k, v in d.get("chunk_pages", {}).items()})
 
     def save(self, path: str = None):
         path = path or TABLE_PATH
@@ -66,7 +77,15 @@ class SplitTable:
         for i, k in enumerate(keys):
             rows = ",\n   ".join(json.dumps(r) for r in self.tables[k])
             lines.append(f'  "{k}": [\n   {rows}\n  ]' + ("," if i + 1 < len(keys) else ""))
-        lines += [' }', '}']
+        lines.append(' },' if self.chunk_pages else ' }')
+        if self.chunk_pages:
+            ck = sorted(self.chunk_pages)
+            lines.append(' "chunk_pages": {')
+            for i, k in enumerate(ck):
+                lines.append(f'  "{k}": {json.dumps(self.chunk_pages[k])}' +
+                             ("," if i + 1 < len(ck) else ""))
+            lines.append(' }')
+        lines.append('}')
         with open(path, "w") as f:
             f.write("\n".join(lines) + "\n")
 
@@ -79,6 +98,24 @@ class SplitTable:
         """num_splits for variant ``key`` at this batch size and (max) KV length."""
         return decode_attn_pick_splits(self.table_for(key), self.batch_keys, self.bucket_tokens,
                                        batch, kv_len)
+
+    def chunk_for(self, key: str, batch: int) -> int:
+        """Tuned split size in pages for per-request counts (nearest batch key)."""
+        row = self.chunk_pages.get(key)
+        if not row:
+            return DEFAULT_CHUNK_PAGES
+        return decode_attn_pick_splits([[c] for c in row], self.batch_keys, 1, batch, 1)
+
+    def request_table(self, key: str, batch: int, page_size: int) -> List[int]:
+        """Per-bucket split counts for the metadata prelude's per-request schedule."""
+        return per_request_table(self.chunk_for(key, batch), page_size, self.bucket_tokens)
+
+
+def per_request_table(chunk_pages: int, page_size: int, bucket_tokens: int = BUCKET_TOKENS,
+                      n_buckets: int = N_BUCKETS) -> List[int]:
+    """Bucket k (1-based) -> ceil(k * bucket_pages / chunk_pages) splits, capped at 256."""
+    per = max(1, bucket_tokens // page_size)
+    return [min(256, max(1, -(-k * per // chunk_pages))) for k in range(1, n_buckets + 1)]
 
 
 def default_table() -> SplitTable:
