@@ -70,7 +70,10 @@ def parse():
                    help="for rocprofv3 --pmc runs: one 1 GiB copy (the byte-count reference), "
                         "then --steps whole steps, no timing")
     p.add_argument("--rocprof-summary", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                   help="summarise rocprofv3 CSV output into profiles/ (no GPU needed)")
+                   help="print per-kernel stats and HBM bytes from rocprofv3 CSV output (no GPU)")
+    p.add_argument("--profile-report", metavar="RUN_PREFIX",
+                   help="write profiles/<kernel>_<workload>.md and update profiles/traffic.json "
+                        "from the rocprofv3 runs RUN_PREFIX_{trace,fetch,write[,sq]} (no GPU)")
     return p.parse_args()
 
 
@@ -481,8 +484,160 @@ def rocprof_summary(trace_dir, fetch_dir, write_dir):
                                    split_fetch_bytes=sf, split_write_bytes=sw)
 
 
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+KERNEL_NAMES = {"bf16": "split_bf16_kernel", "fp32": "split_fma_kernel",
+                "int8": "split_int8_mfma_kernel", "int4": "split_int4_mfma_kernel"}
+
+
+def sq_summary(sq_dir, pat):
+    """MFMA and VALU busy of the kernel matching `pat` (mean over its dispatches):
+    sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE of one XCC x 1024
+    SIMDs), and sum of SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE x 256 CUs)."""
+    rows = _read_csv(sq_dir, "counter_collection.csv")
+    per, grbm = {}, {}
+    for r in rows:
+        if pat not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {})
+        name = r["Counter_Name"]
+        v = float(r["Counter_Value"])
+        if name == "GRBM_GUI_ACTIVE":
+            grbm.setdefault(r["Dispatch_Id"], []).append(v)
+        else:
+            d[name] = d.get(name, 0.0) + v
+    for k, vals in grbm.items():
+        # one row per XCC -> the largest; one row summed over the 8 XCCs -> / 8
+        per[k]["GRBM_GUI_ACTIVE"] = max(vals) if len(vals) > 1 else vals[0] / 8
+    mfma = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] * 1024) for d in per.values()]
+    valu = [d["SQ_ACTIVE_INST_VALU"] / (d["GRBM_GUI_ACTIVE"] * 256) for d in per.values()]
+    return dict(dispatches=len(per), mfma_busy=float(np.mean(mfma)), valu_busy=float(np.mean(valu)),
+                gui_active_cycles=float(np.mean([d["GRBM_GUI_ACTIVE"] for d in per.values()])))
+
+
+def profile_report(prefix):
+    """Summary of the rocprofv3 runs of one workload: writes
+    profiles/<kernel>_<workload>_<layout>.md and its entry in profiles/traffic.json."""
+    import re
+    from decode_attention_paged_gqa_amd import workloads as W
+
+    trace_log = prefix + "_trace.log"
+    line = [ln for ln in open(trace_log) if ln.startswith('{"metric"')][-1]
+    res = json.loads(line)
+    w = W.WORKLOADS[res["config"]["workload"]]
+    wl = w.name
+    kv = kv_name(w)
+    sched = res["schedule"]
+    S = res["config"]["num_splits"]
+    ab = res["roofline"]["algorithmic_bytes_per_launch"]
+    table, tr = rocprof_summary(prefix + "_trace", prefix + "_fetch", prefix + "_write")
+    stats = _read_csv(prefix + "_trace", "kernel_stats.csv")
+    srow = [r for r in stats if KERNEL_NAMES[kv] in r["Name"]][0]
+    avg_us = float(srow["AverageNs"]) / 1e3
+    calls = int(srow["Calls"])
+    kern = re.sub(r"^(void )?\(anonymous namespace\)::", "", srow["Name"]).split("(")[0]
+    fetch, write = tr["split_fetch_bytes"], tr["split_write_bytes"]
+    hbm = fetch + write
+    cfg = res["config"]
+    short = wl.replace("_p64", "")
+    fn = f"profiles/{KERNEL_NAMES[kv]}_{short}_{w.kv_layout.lower()}.md"
+    rel = os.path.relpath(prefix, ROOT)
+    lens = (f"{w.lengths} {w.length}" if w.lengths == "fixed"
+            else f"{w.lengths} in [{w.length_lo}, {w.length_hi}]")
+    wdesc = (f"B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads} (G={w.group}), "
+             f"q_per_req={w.q_per_req}{' causal' if w.causal else ''}, D={w.head_dim}, "
+             f"page_size {w.page_size}, {kv} cache, {w.kv_layout} pool layout; KV lengths {lens}"
+             + (" with one request at the maximum" if w.pin_max else "")
+             + f" (seed {w.seed}): {cfg['kv_tokens']:,} tokens, {ab:,} algorithmic bytes per "
+             f"stage-1 launch")
+    run = f"python3 $R/bench.py --workload {wl} --sched {sched['mode']}"
+    cmds = ["cd /tmp && export TMPDIR=/tmp",
+            f"rocprofv3 --kernel-trace --stats --output-format csv -d $R/{rel}_trace -o run -- "
+            f"{run} --steps 20 --warmup 5 --no-cpu-baseline --no-alt",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/{rel}_fetch -o run -- "
+            f"{run} --profile-only --steps 3",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/{rel}_write -o run -- "
+            f"{run} --profile-only --steps 3"]
+    sq = None
+    if os.path.isdir(prefix + "_sq"):
+        sq = sq_summary(prefix + "_sq", KERNEL_NAMES[kv])
+        cmds.append(f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d $R/{rel}_sq "
+                    f"-o run -- {run} --profile-only --steps 3")
+    cmds.append(f"cd $R && python3 bench.py --profile-report {rel}")
+    rows = "\n".join(f"| {i} | {f:.1f} | {wv:.1f} |" for i, (f, wv) in
+                     enumerate(zip(tr["split_fetch_kib"], tr["split_write_kib"])))
+    partial_bytes = w.batch * w.q_per_req * w.num_q_heads * S * (w.head_dim + 1) * 4
+    sched_txt = (f"num_splits {S} from the tuned split table" if sched["mode"] == "batch" else
+                 f"per-request split counts (table {sched['table']} per {sched['bucket_tokens']}"
+                 f"-token bucket, {sched['work_items']} work items)")
+    units = ""
+    if sq is not None:
+        units = f"""
+## Compute units (`--pmc {' '.join(SQ_COUNTERS)}`, {sq['dispatches']} dispatches)
+
+MFMA busy = sum of SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs / (GRBM_GUI_ACTIVE x 1024),
+GRBM_GUI_ACTIVE being the busy cycles of one XCC (the counter row is the sum over the 8 XCCs):
+**{100 * sq['mfma_busy']:.1f} %**.  VALU busy = sum of SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE x 256 CUs):
+**{100 * sq['valu_busy']:.1f} %**.  (GRBM_GUI_ACTIVE {sq['gui_active_cycles']:,.0f} cycles of one XCC
+per dispatch; counters run with the profiler's serialised dispatches.)
+"""
+    md = f"""# {kern} on {wl} ({w.kv_layout}), {sched['mode']} schedule
+
+Workload: {wdesc}.  MI355X (gfx950), one GPU, rocprofv3 from ROCm 7.2; {sched_txt}.
+`$R` is the repository root.
+
+Commands:
+
+```
+{chr(10).join(cmds)}
+```
+
+## Kernel trace (`--kernel-trace --stats`, {calls} stage-1 calls incl. warmup)
+
+{table}
+
+Stage-1 average {avg_us:.2f} us -> {ab / (avg_us * 1e-6) / 1e9:.1f} GB/s algorithmic
+({ab / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:.1f} % of 8 TB/s).  bench.py's HIP-event average
+over the same run: {res['kernels_us']['split']:.2f} us ({res['roofline']['achieved']:.1f} GB/s).
+
+## HBM traffic (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`, per stage-1 dispatch)
+
+Calibration: a 1 GiB device-to-device copy (`__amd_rocclr_copyBuffer`) reads
+FETCH_SIZE = {tr['copy_fetch_kib']:.1f} KiB and writes WRITE_SIZE = {tr['copy_write_kib']:.1f} KiB,
+so FETCH_SIZE is scaled by {tr['fetch_scale']:.4f} and WRITE_SIZE by {tr['write_scale']:.4f} to give bytes.
+
+| stage-1 dispatch | FETCH_SIZE KiB | WRITE_SIZE KiB |
+|---|---|---|
+{rows}
+
+Mean: {fetch / 1e9:.4f} GB read + {write / 1e6:.2f} MB written = {hbm / 1e9:.4f} GB per launch,
+{hbm / ab:.4f} x the algorithmic bytes (the writes are the fp32 split partials, at most
+{w.batch}*{w.q_per_req}*{w.num_q_heads}*{S}*({w.head_dim}+1)*4 B = {partial_bytes / 1e6:.2f} MB).
+{units}"""
+    with open(os.path.join(ROOT, fn), "w") as f:
+        f.write(md)
+    traffic = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    ent = {"kernel": kern, "kernel_hash": kernel_hash(kv),
+           "schedule": {k: sched[k] for k in ("mode", "num_splits") if k in sched},
+           "num_splits": S, "hbm_bytes_per_launch": int(round(hbm)),
+           "fetch_bytes": int(round(fetch)), "write_bytes": int(round(write)),
+           "fetch_scale": tr["fetch_scale"], "write_scale": tr["write_scale"],
+           "rocprof_avg_us": round(avg_us, 2), "summary": fn}
+    if sq is not None:
+        ent["mfma_busy"] = round(sq["mfma_busy"], 4)
+        ent["valu_busy"] = round(sq["valu_busy"], 4)
+    traffic[f"{wl}/{w.kv_layout}"] = ent
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+    print(fn, f"{avg_us:.1f} us", f"traffic {hbm / ab:.4f}x",
+          "" if sq is None else f"mfma {100 * sq['mfma_busy']:.1f}% valu {100 * sq['valu_busy']:.1f}%")
+
+
 def main():
     args = parse()
+    if args.profile_report:
+        profile_report(os.path.join(ROOT, args.profile_report))
+        return
     if args.rocprof_summary:
         table, tr = rocprof_summary(*args.rocprof_summary)
         print(table)
@@ -536,6 +691,7 @@ def main():
     value = ab["step"] / (ms * 1e-3) / 1e9
     achieved = ab["split"] / (split_ms * 1e-3) / 1e9
     traffic = None
+    counters = {}
     if os.path.exists(TRAFFIC_FILE):
         t = json.load(open(TRAFFIC_FILE))
         ent = t.get(f"{w.name}/{w.kv_layout}")
@@ -543,6 +699,7 @@ def main():
                 and ent.get("schedule", {"mode": "batch", "num_splits": ent.get("num_splits")}) \
                 == {k: schedule[k] for k in ("mode", "num_splits") if k in schedule}:
             traffic = ent.get("hbm_bytes_per_launch")
+            counters = {k: ent[k] for k in ("mfma_busy", "valu_busy") if k in ent}
     res = {
         "metric": "decode-attn achieved HBM GB/s (% of peak) + us/call, B=64 KV=32K bf16",
         "value": round(value, 2),
@@ -572,7 +729,7 @@ def main():
                        "merge": round(merge_ms * 1e3, 2)},
         "roofline": {"bound": "hbm", "kernel": "split (stage 1)", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": ab["split"]},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": ab["split"], **counters},
         "step_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": ab["step"],
     }
