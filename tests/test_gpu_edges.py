@@ -1,0 +1,107 @@
+"""GPU parity at the edges of the supported shapes, element by element against
+the fp64 oracle (gates in tests/_gpu_util.py):
+
+* a split longer than the specialised kernels' page-id tables (1024 pages for
+  bf16, 512 for INT8 / INT4), which hands the launch to the generic kernel;
+* page sizes 128 and 256;
+* 16 query rows per kv-head from 16 MTP tokens of one head (q_per_req = 16);
+* a batch much wider than one workgroup (300 requests), with both schedules.
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_paged_gqa_amd import workloads as W
+from tests import _gpu_util as U
+from tests.test_gpu_attention import _check_out, both_layouts
+
+pytestmark = pytest.mark.gpu
+log = U.log
+
+
+def _run_and_check(gpu, w, S, label):
+    log(f"{label}: {w.name} S={S}")
+    batch = W.make_batch(w, device="cuda")
+    o_ref, l_ref = U.oracle_partials(batch, S)
+    out_ref, lse_ref = U.oracle_full(batch)
+    out, lse, o, l = U.run_decode(gpu, batch, S)
+    extra = U.fp16_pv_o_bound(batch) if U.uses_matrix_path(w) else None
+    U.check_partials(U.to_np(o), U.to_np(l), o_ref, l_ref, f"{w.name} S={S}", o_extra=extra)
+    _check_out(w, U.to_np(out), out_ref, f"{w.name} S={S} out")
+    U.check_lse(U.to_np(lse), lse_ref, f"{w.name} S={S} lse")
+
+
+# one request whose single split spans more pages than the LDS page-id table
+LONG = [
+    W.RAGGED_B64.scaled(name="long_split_bf16_g5_p16", batch=2, page_size=16, lengths="list",
+                        length_list=(16400, 37), pin_max=False),
+    W.INT8_B32.scaled(name="long_split_int8_p16", batch=2, page_size=16, lengths="list",
+                      length_list=(8250, 5)),
+    W.INT4_MTP_B64.scaled(name="long_split_int4_mtp_p16", batch=2, page_size=16, lengths="list",
+                          length_list=(8250, 9)),
+]
+
+
+@pytest.mark.parametrize("w", both_layouts(LONG), ids=lambda w: w.name)
+def test_split_longer_than_the_page_id_table(gpu, w):
+    _run_and_check(gpu, w, 1, "long split")
+
+
+PAGES = [
+    W.RAGGED_B64.scaled(name="ragged_g5_p128", batch=4, page_size=128, lengths="list",
+                        length_list=(1, 127, 129, 3000), pin_max=False),
+    W.RAGGED_B64.scaled(name="ragged_g5_p256", batch=3, page_size=256, lengths="list",
+                        length_list=(255, 257, 2100), pin_max=False),
+    W.INT8_B32.scaled(name="int8_p128", batch=3, page_size=128, lengths="list",
+                      length_list=(5, 128, 1500)),
+    W.INT8_B32.scaled(name="int8_p256", batch=2, page_size=256, lengths="list",
+                      length_list=(300, 1100)),
+    W.INT4_MTP_B64.scaled(name="int4_mtp_p128", batch=3, page_size=128, lengths="list",
+                          length_list=(4, 130, 1400)),
+    W.INT4_MTP_B64.scaled(name="int4_mtp_p256", batch=2, page_size=256, lengths="list",
+                          length_list=(260, 900)),
+]
+
+
+@pytest.mark.parametrize("w", both_layouts(PAGES), ids=lambda w: w.name)
+@pytest.mark.parametrize("S", [1, 3])
+def test_large_pages(gpu, w, S):
+    _run_and_check(gpu, w, S, "large pages")
+
+
+Q16 = [
+    W.BF16_B16.scaled(name="mtp16_bf16_g1", batch=3, num_q_heads=4, num_kv_heads=4, q_per_req=16,
+                      causal=True, lengths="list", length_list=(16, 17, 700)),
+    W.INT8_B32.scaled(name="mtp16_int8_g1", batch=3, num_q_heads=4, num_kv_heads=4, q_per_req=16,
+                      causal=True, lengths="list", length_list=(16, 40, 900)),
+    W.INT4_MTP_B64.scaled(name="mtp16_int4_g1", batch=3, num_q_heads=4, num_kv_heads=4,
+                          q_per_req=16, lengths="list", length_list=(16, 33, 800)),
+]
+
+
+@pytest.mark.parametrize("w", both_layouts(Q16), ids=lambda w: w.name)
+def test_sixteen_query_tokens(gpu, w):
+    _run_and_check(gpu, w, 4, "q_per_req 16")
+
+
+WIDE = W.RAGGED_B64.scaled(name="wide_b300_g5", batch=300, lengths="loguniform", length_lo=1,
+                           length_hi=400, pin_max=True)
+
+
+@pytest.mark.parametrize("w", both_layouts([WIDE]), ids=lambda w: w.name)
+def test_wide_batch_both_schedules(gpu, w):
+    _run_and_check(gpu, w, 2, "wide batch")
+    batch = W.make_batch(w, device="cuda")
+    table = [1, 2, 3, 4]
+    md = U.schedule(gpu, batch, table, 128, 4)
+    out, lse, o, l = U.run_decode(gpu, batch, 4, sched=md)
+    out_ref, lse_ref = U.oracle_full(batch)
+    U.check_bf16(U.to_np(out), out_ref, f"{w.name} per-request out")
+    U.check_lse(U.to_np(lse), lse_ref, f"{w.name} per-request lse")
+    counts = md["split_counts"].cpu().numpy()
+    assert counts.min() >= 1 and counts.max() <= 4
+    o_ref, l_ref = U.oracle_partials_per_request(batch, 4, counts)
+    og, lg = U.blank_unused_slots(U.to_np(o), U.to_np(l), counts)
+    U.check_partials(og, lg, o_ref, l_ref, f"{w.name} per-request")
+    assert torch.isfinite(out.float()).all()
+    assert np.isfinite(lse_ref).sum() == np.isfinite(U.to_np(lse)).sum()
