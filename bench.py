@@ -231,9 +231,12 @@ def time_config(step, steps, warmup, torch):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     meta = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    split = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    splits = [e[1].elapsed_time(e[2]) for e in evs]
     merge = np.mean([e[2].elapsed_time(e[3]) for e in evs])
-    return wall_ms, float(split), float(merge), float(meta)
+    steps_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    pct = {"split_us": [round(float(np.percentile(splits, p)) * 1e3, 2) for p in (10, 50, 90)],
+           "step_us": [round(float(np.percentile(steps_ms, p)) * 1e3, 2) for p in (10, 50, 90)]}
+    return wall_ms, float(np.mean(splits)), float(merge), float(meta), pct
 
 
 def time_graph(step, steps, warmup, torch):
@@ -269,8 +272,22 @@ def time_split_only(step, iters, torch):
     return e0.elapsed_time(e1) / iters
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(batch, seconds):
-    """The fp64 oracle on a bounded sample of the same batch, on the host cores."""
+    """The fp64 oracle on a bounded sample of the same batch, on the host cores.
+
+    Requests are taken in batch order until `seconds` of oracle time are spent;
+    each one's host copy is prepared outside the timer, the oracle is run once
+    warm, then timed three times, and the median counts."""
     import torch
     from decode_attention_paged_gqa_amd import workloads as W
     from oracle import attention as OA
@@ -282,17 +299,16 @@ def cpu_baseline(batch, seconds):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    order = list(range(w.batch))
     done_bytes = 0
     done = []
     elapsed = 0.0
-    G = w.group
     pt_all = batch.page_table.cpu().numpy()
-    for b in order:
+    for b in range(w.batch):
         L = int(batch.lengths[b])
         n = -(-L // w.page_size)
         pages = torch.from_numpy(pt_all[b, :n].astype(np.int64)).cuda()
         q = W.host_f64(batch.q[b:b + 1])
+
         def take(t):  # this request's pages, in the oracle's [P, page, Hkv, ...] order
             return batch.nhd(t).index_select(0, pages)
 
@@ -303,15 +319,23 @@ def cpu_baseline(batch, seconds):
             k = (W.host_int(take(batch.k_pool)), W.host_u16(take(batch.k_scale)))
             v = (W.host_int(take(batch.v_pool)), W.host_u16(take(batch.v_scale)))
         pt = np.arange(n, dtype=np.int64)[None, :]
-        t0 = time.perf_counter()
-        if w.kv == W.KV_INT8:
-            k = OQ.dequant_int8(*k)
-            v = OQ.dequant_int8(*v)
-        elif w.kv == W.KV_INT4:
-            k = OQ.dequant_int4(*k)
-            v = OQ.dequant_int4(*v)
-        OA.decode_attention(q, k, v, pt, np.array([L]), w.page_size, w.softmax_scale, w.causal)
-        elapsed += time.perf_counter() - t0
+
+        def run():
+            kk, vv = k, v
+            if w.kv == W.KV_INT8:
+                kk, vv = OQ.dequant_int8(*k), OQ.dequant_int8(*v)
+            elif w.kv == W.KV_INT4:
+                kk, vv = OQ.dequant_int4(*k), OQ.dequant_int4(*v)
+            OA.decode_attention(q, kk, vv, pt, np.array([L]), w.page_size, w.softmax_scale,
+                                w.causal)
+
+        run()  # warm
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            run()
+            ts.append(time.perf_counter() - t0)
+        elapsed += sorted(ts)[1]
         done.append(b)
         done_bytes += L * w.num_kv_heads * kv_bytes_per_token_head(w)
         if elapsed >= seconds:
@@ -319,9 +343,10 @@ def cpu_baseline(batch, seconds):
     gbs = done_bytes / elapsed / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 oracle over {len(done)} of {w.batch} requests (all heads), "
-                      f"{done_bytes / 1e9:.3f} GB of algorithmic K/V bytes in {elapsed:.1f} s; "
-                      f"host copies prepared outside the timed region",
-            "host_cpus": len(os.sched_getaffinity(0))}
+                      f"{done_bytes / 1e9:.3f} GB of algorithmic K/V bytes in {elapsed:.1f} s "
+                      f"(per request: one warm run, median of three timed runs; host copies "
+                      f"prepared outside the timed region)",
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model()}
 
 
 def make_resident(da, w, torch):
@@ -674,7 +699,7 @@ def main():
     if args.profile_only:
         profile_only(step, args.steps, torch)
         return
-    ms, split_ms, merge_ms, meta_ms = time_config(step, args.steps, args.warmup, torch)
+    ms, split_ms, merge_ms, meta_ms, pct = time_config(step, args.steps, args.warmup, torch)
     # the same step captured once in a HIP graph and replayed (reported beside it)
     try:
         graph_ms = time_graph(step, args.steps, args.warmup, torch)
@@ -727,6 +752,7 @@ def main():
             frac=round(ab["split"] / (alt_split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)),
         "kernels_us": {"metadata": round(meta_ms * 1e3, 2), "split": round(split_ms * 1e3, 2),
                        "merge": round(merge_ms * 1e3, 2)},
+        "percentiles_p10_p50_p90": pct,
         "roofline": {"bound": "hbm", "kernel": "split (stage 1)", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": ab["split"], **counters},
