@@ -211,19 +211,36 @@ def test_nan_in_unused_slots_does_not_leak(gpu, w):
 
 
 # ---------------------------------------------------------------- full sizes
+# The benchmark's launch configuration: its split count comes from the tuned
+# table for the kernel variant, batch size and longest request, as bench.py
+# picks it (None below); a second fixed count covers another split shape.
 FULL = [
-    (W.BF16_B16, 8, [(0, 0), (7, 3), (15, 7)]),
+    (W.BF16_B16, None, [(0, 0), (7, 3), (15, 7)]),
+    (W.RAGGED_B64, None, None),
     (W.RAGGED_B64, 16, None),
-    (W.INT8_B32, 8, [(0, 0), (31, 7), (13, 2)]),
+    (W.UNIFORM_B64, None, [(0, 0), (63, 7), (21, 4)]),
+    (W.INT8_B32, None, [(0, 0), (31, 7), (13, 2)]),
+    (W.INT4_MTP_B64, None, None),
     (W.INT4_MTP_B64, 8, None),
 ]
 
 
-@pytest.mark.parametrize("w,S,pairs", FULL, ids=[f[0].name for f in FULL])
+def bench_splits(w, batch):
+    from decode_attention_paged_gqa_amd.splits import SplitTable, kernel_key
+    kv = w.dtype if w.kv == W.KV_DENSE else w.kv
+    key = kernel_key(kv, w.group * w.q_per_req, w.head_dim, w.page_size, w.kv_layout)
+    return SplitTable.load().pick(key, w.batch, int(batch.lengths.max()))
+
+
+@pytest.mark.parametrize("w,S,pairs", FULL,
+                         ids=[f"{f[0].name}-S{f[1] or 'bench'}" for f in FULL])
 def test_full_size_sampled(gpu, w, S, pairs):
-    log(f"full {w.name} S={S}")
     batch = W.make_batch(w, device="cuda")
-    out, lse, _, _ = U.run_decode(gpu, batch, S)
+    S = S or bench_splits(w, batch)
+    log(f"full {w.name} ({w.kv_layout}) S={S}")
+    out, lse, _, _ = U.run_decode(gpu, batch, S, batch_order=gpu.decode_attn_metadata(
+        batch.seq_lens, batch.req_pool_indices, batch.req_to_token, w.page_size,
+        batch.max_pages, q_stride=w.q_per_req)["batch_order"])
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
     L = batch.lengths
