@@ -15,6 +15,7 @@
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kPrefetch = 8;  // split rows loaded before the weights are known
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restrict__ op,
@@ -30,9 +31,15 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restr
   const float* l = lp + (long long)row * S;
   const float* o = op + (long long)row * S * D + lane * E;
   if (counts) S = min(max(counts[row / rows_per_req], 1), S);
+  // the first kPrefetch split rows are loaded while the max is being found
+  float pre[kPrefetch][E];
+#pragma unroll
+  for (int s = 0; s < kPrefetch; ++s)
+#pragma unroll
+    for (int e = 0; e < E; ++e) pre[s][e] = s < S ? o[(long long)s * D + e] : 0.f;
   float m = da::kNegInf;
   for (int s = lane; s < S; s += 64) m = fmaxf(m, l[s]);
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
 
   float acc[E];
 #pragma unroll
@@ -40,17 +47,21 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restr
   float wsum = 0.f;
   if (m != da::kNegInf) {
     const float ml = m * da::kLog2e;
-    for (int s = 0; s < S; ++s) {
-      const float w = da::fast_exp2(fmaf(l[s], da::kLog2e, -ml));  // exp(lse_s - m); 0 for -inf
-      wsum += w;
-      if (E == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(o + (long long)s * D);
-        acc[0] = fmaf(w, v.x, acc[0]);
-        acc[E - 1] = fmaf(w, v.y, acc[E - 1]);
-      } else {
+    // exp(lse_s - m); 0 for an empty split (lse -inf), whose row holds zeros
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(w, o[(long long)s * D + e], acc[e]);
+    for (int s = 0; s < kPrefetch; ++s) {
+      if (s < S) {
+        const float w = da::fast_exp2(fmaf(l[s], da::kLog2e, -ml));
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(w, pre[s][e], acc[e]);
       }
+    }
+    for (int s = kPrefetch; s < S; ++s) {
+      const float w = da::fast_exp2(fmaf(l[s], da::kLog2e, -ml));
+      wsum += w;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(w, o[(long long)s * D + e], acc[e]);
     }
     const float inv = 1.f / wsum;
 #pragma unroll

@@ -64,32 +64,64 @@ __global__ __launch_bounds__(kThreads) void metadata_kernel(
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
 
-  // ---- exclusive prefix of clamped lengths (and of q lengths for cumsum)
-  long long pk = 0, pq = 0;
-  for (int j = tid; j < b; j += kThreads) {
-    pk += max(seq_lens[j], 0);
-    if (q_mode == DA_Q_CUMSUM) pq += max(q_in[j], 0);
-  }
-  pk = block_sum(pk, sh);
-  if (q_mode == DA_Q_CUMSUM) pq = block_sum(pq, sh);
-
+  // ---- one pass over the batch: exclusive prefixes (lengths, and q lengths
+  // for cumsum), this row's rank in the batch order, and the split counts of
+  // the rows ranked before it.  Every load here is independent of the others,
+  // so the pass costs one memory round trip.
   const int L = max(seq_lens[b], 0);
-  if (order || work) {
-    long long rank = 0, off = 0;
-    for (int j = tid; j < batch; j += kThreads) {
-      const int Lj = max(seq_lens[j], 0);
+  const long long r = rpi[b];
+  const bool ranked = order || work;
+  long long pk = 0, pq = 0, rank = 0, off = 0;
+  for (int j = tid; j < batch; j += kThreads) {
+    const int Lj = max(seq_lens[j], 0);
+    if (j < b) {
+      pk += Lj;
+      if (q_mode == DA_Q_CUMSUM) pq += max(q_in[j], 0);
+    }
+    if (ranked) {
       const bool before = Lj > L || (Lj == L && j < b);
       rank += before ? 1 : 0;
       if (work && before) off += request_splits(table, Lj, page_size);
     }
+  }
+
+  // ---- page-table row: first slot of every page / page_size, zero tail.
+  // Its loads need only L and r, so they go out before the reductions below.
+  {
+    const long long n = ((long long)L + page_size - 1) / page_size;
+    const bool row_ok = r >= 0 && r < r2t_rows;
+    const int32_t* row = r2t + (row_ok ? r : 0) * r2t_stride;
+    int32_t* out = page_table + (long long)b * max_pages;
+    int32_t* swa_out = swa_pt ? swa_pt + (long long)b * max_pages : nullptr;
+    for (int j = tid; j < max_pages; j += kThreads) {
+      int32_t v = 0, w = 0;
+      const long long col = (long long)j * page_size;
+      if (row_ok && j < n && col < r2t_cols) {
+        const int32_t slot = row[col];
+        if (slot >= 0) {
+          v = slot / page_size;
+          if (swa_out && slot < f2s_len) {
+            const long long m = f2s[slot];
+            w = m >= 0 ? (int32_t)(m / page_size) : 0;
+          }
+        }
+      }
+      out[j] = v;
+      if (swa_out) swa_out[j] = w;
+    }
+  }
+
+  pk = block_sum(pk, sh);
+  if (q_mode == DA_Q_CUMSUM) pq = block_sum(pq, sh);
+  if (ranked) {
     rank = block_sum(rank, sh);
     if (order && tid == 0) order[rank] = b;
     if (work) {
       off = block_sum(off, sh);
       const int Sb = request_splits(table, L, page_size);
       if (tid == 0) counts[b] = Sb;
-      for (int s = tid; s < Sb; s += kThreads)
-        if (off + s < capacity) work[off + s] = (b << da::kItemShift) | s;
+      for (int s2 = tid; s2 < Sb; s2 += kThreads)
+        if (off + s2 < capacity) work[off + s2] = (b << da::kItemShift) | s2;
       if (rank == batch - 1)  // the last request in dispatch order closes the list
         for (long long u = off + Sb + tid; u < capacity; u += kThreads) work[u] = -1;
     }
@@ -108,30 +140,6 @@ __global__ __launch_bounds__(kThreads) void metadata_kernel(
       else if (q_mode == DA_Q_CUMSUM) cu_q[batch] = (int32_t)(pq + max(q_in[b], 0));
       else cu_q[batch] = q_in[batch];
     }
-  }
-
-  // ---- page-table row: first slot of every page / page_size, zero tail
-  const long long n = ((long long)L + page_size - 1) / page_size;
-  const long long r = rpi[b];
-  const bool row_ok = r >= 0 && r < r2t_rows;
-  const int32_t* row = r2t + (row_ok ? r : 0) * r2t_stride;
-  int32_t* out = page_table + (long long)b * max_pages;
-  int32_t* swa_out = swa_pt ? swa_pt + (long long)b * max_pages : nullptr;
-  for (int j = tid; j < max_pages; j += kThreads) {
-    int32_t v = 0, w = 0;
-    const long long col = (long long)j * page_size;
-    if (row_ok && j < n && col < r2t_cols) {
-      const int32_t slot = row[col];
-      if (slot >= 0) {
-        v = slot / page_size;
-        if (swa_out && slot < f2s_len) {
-          const long long m = f2s[slot];
-          w = m >= 0 ? (int32_t)(m / page_size) : 0;
-        }
-      }
-    }
-    out[j] = v;
-    if (swa_out) swa_out[j] = w;
   }
 }
 
