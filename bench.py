@@ -59,7 +59,8 @@ def parse():
                    help="per-request split size in pages (0 = tuned table)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-alt", action="store_true",
-                   help="skip timing the other schedule (keeps a kernel trace to one configuration)")
+                   help="skip timing the other schedule and the auxiliary rows (KV append, SWA "
+                        "and schedule metadata), keeping a kernel trace to one configuration")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--tune", nargs="?", const="all", default=None,
                    help="sweep num_splits per bucket and write the table (optionally a comma list "
@@ -256,6 +257,93 @@ def time_graph(step, steps, warmup, torch):
         graph.replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_calls(fn, iters, torch):
+    """Average device time (us) of one call of fn: `iters` calls captured in a
+    HIP graph and replayed, so that host launch cost does not leave the GPU
+    idle between these few-microsecond kernels."""
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(iters):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * iters) * 1e3
+
+
+def aux_timings(da, batch, iters, torch):
+    """The rows around the attention step, timed on the same batch shape:
+    * append: the step's B*q new tokens written (encoded for INT8 / INT4
+      caches) into a scratch pool of the workload's format and layout at
+      distinct random slots -- the benchmarked pools are left untouched;
+    * metadata with SWA translation (a page-permuted SWA pool, a quarter of
+      its pages not resident), and with the per-request split schedule.
+    Bytes are the algorithmic ones: new rows read, codes/scales written."""
+    from decode_attention_paged_gqa_amd import workloads as W
+
+    w = batch.w
+    B, qn, Hq, D = batch.q.shape
+    Hkv, ps = w.num_kv_heads, w.page_size
+    N = B * qn
+    gen = torch.Generator(device="cuda").manual_seed(99)
+    P = max(4 * ((N + ps - 1) // ps), 64)
+    shape = (P, ps, Hkv) if w.kv_layout == "NHD" else (P, Hkv, ps)
+    fmt = "dense" if w.kv == W.KV_DENSE else w.kv
+    new_dtype = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    k_new = torch.randn((N, Hkv, D), generator=gen, device="cuda").to(new_dtype)
+    v_new = torch.randn((N, Hkv, D), generator=gen, device="cuda").to(new_dtype)
+    if fmt == "dense":
+        pools = [torch.empty(shape + (D,), dtype=new_dtype, device="cuda") for _ in range(2)]
+        scales = [None, None]
+        row_out = D * new_dtype.itemsize
+    elif fmt == "int8":
+        pools = [torch.empty(shape + (D,), dtype=torch.int8, device="cuda") for _ in range(2)]
+        scales = [torch.empty(shape, dtype=torch.float16, device="cuda") for _ in range(2)]
+        row_out = D + 2
+    else:
+        pools = [torch.empty(shape + (D // 2,), dtype=torch.uint8, device="cuda") for _ in range(2)]
+        scales = [torch.empty(shape + (D // 32, 2), dtype=torch.float16, device="cuda")
+                  for _ in range(2)]
+        row_out = D // 2 + 4 * (D // 32)
+    loc = torch.randperm(P * ps, generator=gen, device="cuda")[:N].to(torch.int64)
+    us = time_calls(lambda: da.decode_attn_append_kv(k_new, v_new, loc, pools[0], pools[1],
+                                                      scales[0], scales[1], cache_format=fmt,
+                                                      kv_layout=w.kv_layout), iters, torch)
+    append_bytes = 2 * N * Hkv * (D * new_dtype.itemsize + row_out) + 8 * N
+    out = {"append": {"us": round(us, 2), "tokens": N, "format": fmt,
+                      "algorithmic_bytes": append_bytes,
+                      "GB_per_s": round(append_bytes / (us * 1e-6) / 1e9, 1)}}
+
+    slots = int(batch.req_to_token.max().item()) + 1
+    pages = (slots + ps - 1) // ps
+    perm = torch.randperm(pages + 7, generator=gen, device="cuda")[:pages]
+    f2s = (perm[:, None] * ps + torch.arange(ps, device="cuda")[None, :]).to(torch.int64)
+    f2s[torch.rand(pages, generator=gen, device="cuda") < 0.25] = -1
+    f2s = f2s.reshape(-1).contiguous()
+    md = {k: torch.empty_like(v) for k, v in batch.md.items()}
+    md["swa_page_table"] = torch.empty_like(batch.md["page_table"])
+    args = (batch.seq_lens, batch.req_pool_indices, batch.req_to_token, ps, batch.max_pages)
+    out["metadata"] = {"us": round(time_calls(lambda: da.decode_attn_metadata(
+        *args, q_stride=qn, out=md), iters, torch), 2)}
+    out["metadata_swa"] = {"us": round(time_calls(lambda: da.decode_attn_metadata(
+        *args, q_stride=qn, out=md, full_to_swa=f2s), iters, torch), 2)}
+    table = [1, 2, 3, 4, 5, 6, 7, 8]
+    md2 = dict(md, split_counts=torch.empty(B, dtype=torch.int32, device="cuda"),
+               work_list=torch.empty(B * 8, dtype=torch.int32, device="cuda"))
+    out["metadata_schedule"] = {"us": round(time_calls(lambda: da.decode_attn_metadata(
+        *args, q_stride=qn, out=md2, split_table=table, bucket_tokens=BUCKET_TOKENS,
+        max_splits=8), iters, torch), 2)}
+    return out
 
 
 def time_split_only(step, iters, torch):
@@ -707,6 +795,7 @@ def main():
         print(f"bench.py: graph capture failed ({e})", file=sys.stderr)
         graph_ms = None
     alt_split_ms = None if args.no_alt else time_split_only(alt, args.steps, torch)
+    aux = None if args.no_alt else aux_timings(da, batch, args.steps, torch)
     schedule, alt_schedule = step.describe(), alt.describe()
     if step is req_step:
         schedule["chunk_pages"] = chunk
@@ -756,6 +845,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "split (stage 1)", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": ab["split"], **counters},
+        "aux_us": aux,
         "step_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": ab["step"],
     }

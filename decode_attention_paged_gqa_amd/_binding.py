@@ -188,9 +188,12 @@ def _metadata_ex(lib, dev, B, seq_lens, rpi, r2t, page_size, max_pages, q_mode, 
         _ptr(seq_lens), _ptr(rpi), _ptr(r2t), r2t.shape[0], r2t.shape[1], r2t.stride(0), B,
         page_size, max_pages, q_mode, _ptr(q_in), q_stride, _ptr(out["cache_seqlens"]),
         _ptr(out["cu_seqlens_k"]), _ptr(out["cu_seqlens_q"]), _ptr(out["page_table"]),
-        _ptr(out["batch_order"]), _ptr(full_to_swa), f2s_len, _ptr(out.get("swa_page_table")),
-        table_host, nb, int(bucket_tokens), smax, _ptr(out.get("split_counts")),
-        _ptr(out.get("work_list")), out["work_list"].shape[0] if table_host is not None else 0,
+        _ptr(out["batch_order"]), _ptr(full_to_swa), f2s_len,
+        _ptr(out["swa_page_table"]) if full_to_swa is not None else None,
+        table_host, nb, int(bucket_tokens), smax,
+        _ptr(out["split_counts"]) if table_host is not None else None,
+        _ptr(out["work_list"]) if table_host is not None else None,
+        out["work_list"].shape[0] if table_host is not None else 0,
         _stream(dev))
     _check(st, "decode_attn_metadata_ex")
     return out

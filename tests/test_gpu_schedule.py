@@ -92,6 +92,24 @@ def test_schedule_rewrites_a_stale_list(gpu):
     assert torch.equal(md2["split_counts"], md["split_counts"])
 
 
+def test_reused_out_dict_with_other_options(gpu):
+    """An `out` dict that also holds another option's buffers (here the SWA
+    table) passes only the buffers of the options requested."""
+    seq = [5000, 10, 700]
+    ref = _sched_md(gpu, seq, [1, 2, 4], 1024, 8, cap=24)
+    out = dict(ref)
+    out["swa_page_table"] = torch.zeros((3, 4), dtype=torch.int32, device="cuda")
+    md = gpu.decode_attn_metadata(_i32(seq), torch.arange(3, device="cuda"),
+                                  torch.zeros((3, 64), dtype=torch.int32, device="cuda"), 16, 4,
+                                  split_table=[1, 2, 4], bucket_tokens=1024, max_splits=8,
+                                  work_capacity=24, out=out)
+    assert torch.equal(md["work_list"], ref["work_list"])
+    plain = gpu.decode_attn_metadata(_i32(seq), torch.arange(3, device="cuda"),
+                                     torch.zeros((3, 64), dtype=torch.int32, device="cuda"), 16, 4,
+                                     out=out)
+    assert torch.equal(plain["page_table"], ref["page_table"])
+
+
 # ---------------------------------------------------------------- attention
 SMALL_TABLE = [1, 2, 3, 5, 8, 13, 21, 32]
 SMALL_BUCKET = 256
