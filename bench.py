@@ -757,8 +757,8 @@ def main():
         print(json.dumps(tr))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; the multi-GPU (kv-head / batch / "
-              "sequence) sharding is described in DESIGN.md and not launched. Use --gpus 1.",
+        print("bench.py: the path runs on one GPU; sharding it by kv-head, by request or by "
+              "KV sequence is a design note only and nothing here launches it. Use --gpus 1.",
               file=sys.stderr, flush=True)
         sys.exit(2)
     import torch

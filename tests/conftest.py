@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu():
-    """The loaded HIP library on a GPU machine; fails (never skips) when it is missing."""
+    """The loaded HIP library; fails (never skips) when no GPU is visible or the library is missing."""
     import torch
 
     if not torch.cuda.is_available():
