@@ -64,7 +64,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--tune", nargs="?", const="all", default=None,
                    help="sweep num_splits per bucket and write the table (optionally a comma list "
-                        "of cache formats: bf16,int8,int4)")
+                        "of cache formats -- bf16,int8,int4 -- and workload names)")
     p.add_argument("--tune-chunks", nargs="?", const="all", default=None,
                    help="sweep the per-request split size per batch key and write it to the table")
     p.add_argument("--profile-only", action="store_true",
@@ -102,18 +102,29 @@ def algorithmic_bytes(w, lengths, out_elem=2):
                 step=kv + q_bytes + out_bytes + 4 * n_pages + 4 * w.batch)
 
 
-# source files of the stage-1 kernel each cache format runs on (traffic counters
-# taken on a kernel stay valid only while these files are unchanged)
-KERNEL_SOURCES = {"bf16": ["split_bf16.hip", "common.h"],
-                  "fp32": ["split_fma.hip", "common.h"],
-                  "int8": ["split_int8.hip", "mfma_util.h", "split_fma.hip", "common.h"],
-                  "int4": ["split_int4.hip", "mfma_util.h", "split_fma.hip", "common.h"]}
+def stage1_kernel(w):
+    """(kernel name, source files) of the stage-1 kernel a D = 128 workload runs
+    on, as the library dispatches it; traffic counters taken on a kernel stay
+    valid only while its sources are unchanged."""
+    from decode_attention_paged_gqa_amd import workloads as W
+
+    rows = w.group * w.q_per_req
+    bf16_q = w.dtype == "bf16"
+    if w.kv == W.KV_DENSE and bf16_q and rows <= 5:
+        return "split_bf16_kernel", ["split_bf16.hip", "common.h"]
+    if w.kv == W.KV_DENSE and bf16_q and rows <= 16:
+        return "split_bf16_mfma_kernel", ["split_bf16_mfma.hip", "mfma_util.h", "common.h"]
+    if w.kv == W.KV_INT8 and bf16_q and rows <= 16:
+        return "split_int8_mfma_kernel", ["split_int8.hip", "mfma_util.h", "common.h"]
+    if w.kv == W.KV_INT4 and bf16_q and 9 <= rows <= 16:
+        return "split_int4_mfma_kernel", ["split_int4.hip", "mfma_util.h", "common.h"]
+    return "split_fma_kernel", ["split_fma.hip", "common.h"]
 
 
-def kernel_hash(kv="bf16") -> str:
+def kernel_hash(w) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_paged_gqa_amd", "csrc")
-    for f in KERNEL_SOURCES[kv]:
+    for f in stage1_kernel(w)[1]:
         path = os.path.join(csrc, f)
         if os.path.exists(path):
             h.update(open(path, "rb").read())
@@ -447,6 +458,18 @@ def make_resident(da, w, torch):
     return batch
 
 
+def tune_variants(which):
+    """Workloads whose kernel variants a sweep covers: all, or a comma list of
+    cache formats (bf16, int8, int4) and workload names."""
+    from decode_attention_paged_gqa_amd import workloads as W
+
+    variants = [W.RAGGED_B64, W.BF16_B16, W.INT8_B32, W.INT4_MTP_B64, W.BF16_MTP_B64]
+    if which == "all":
+        return variants
+    keep = set(which.split(","))
+    return [v for v in variants if kv_name(v) in keep or v.name in keep]
+
+
 def tune(da, torch, which="all"):
     """Sweep num_splits per KV-length bucket and batch key; write splits_table.json."""
     from decode_attention_paged_gqa_amd import workloads as W
@@ -454,10 +477,7 @@ def tune(da, torch, which="all"):
                                                        N_BUCKETS, SplitTable, kernel_key)
 
     table = SplitTable.load()
-    variants = [W.RAGGED_B64, W.BF16_B16, W.INT8_B32, W.INT4_MTP_B64]
-    if which != "all":
-        keep = set(which.split(","))
-        variants = [v for v in variants if kv_name(v) in keep]
+    variants = tune_variants(which)
     for base in variants:
         key = kernel_key(kv_name(base), rows_per_kv_head(base), base.head_dim, base.page_size,
                          base.kv_layout)
@@ -497,10 +517,7 @@ def tune_chunks(da, torch, which="all"):
                                                        kernel_key, per_request_table)
 
     table = SplitTable.load()
-    variants = [W.RAGGED_B64, W.BF16_B16, W.INT8_B32, W.INT4_MTP_B64]
-    if which != "all":
-        keep = set(which.split(","))
-        variants = [v for v in variants if kv_name(v) in keep]
+    variants = tune_variants(which)
     for base in variants:
         key = kernel_key(kv_name(base), rows_per_kv_head(base), base.head_dim, base.page_size,
                          base.kv_layout)
@@ -544,7 +561,7 @@ def profile_only(step, steps, torch):
     w = step.batch.w
     ab = algorithmic_bytes(w, step.batch.lengths)
     print(json.dumps({"profile_only": w.name, "schedule": step.describe(), "copy_bytes": COPY_BYTES,
-                      "split_algorithmic_bytes": ab["split"], "kernel_hash": kernel_hash(kv_name(w))}),
+                      "split_algorithmic_bytes": ab["split"], "kernel_hash": kernel_hash(w)}),
           flush=True)
 
 
@@ -598,18 +615,16 @@ def rocprof_summary(trace_dir, fetch_dir, write_dir):
 
 
 SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
-KERNEL_NAMES = {"bf16": "split_bf16_kernel", "fp32": "split_fma_kernel",
-                "int8": "split_int8_mfma_kernel", "int4": "split_int4_mfma_kernel"}
 
 
 def sq_summary(sq_dir, pat):
-    """MFMA and VALU busy of the kernel matching `pat` (mean over its dispatches):
+    """MFMA and VALU busy of the kernel named `pat` (mean over its dispatches):
     sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE of one XCC x 1024
     SIMDs), and sum of SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE x 256 CUs)."""
     rows = _read_csv(sq_dir, "counter_collection.csv")
     per, grbm = {}, {}
     for r in rows:
-        if pat not in r["Kernel_Name"]:
+        if pat + "<" not in r["Kernel_Name"] and pat + "(" not in r["Kernel_Name"]:
             continue
         d = per.setdefault(r["Dispatch_Id"], {})
         name = r["Counter_Name"]
@@ -644,7 +659,8 @@ def profile_report(prefix):
     ab = res["roofline"]["algorithmic_bytes_per_launch"]
     table, tr = rocprof_summary(prefix + "_trace", prefix + "_fetch", prefix + "_write")
     stats = _read_csv(prefix + "_trace", "kernel_stats.csv")
-    srow = [r for r in stats if KERNEL_NAMES[kv] in r["Name"]][0]
+    kname = stage1_kernel(w)[0]
+    srow = [r for r in stats if kname + "<" in r["Name"] or kname + "(" in r["Name"]][0]
     avg_us = float(srow["AverageNs"]) / 1e3
     calls = int(srow["Calls"])
     kern = re.sub(r"^(void )?\(anonymous namespace\)::", "", srow["Name"]).split("(")[0]
@@ -652,7 +668,7 @@ def profile_report(prefix):
     hbm = fetch + write
     cfg = res["config"]
     short = wl.replace("_p64", "")
-    fn = f"profiles/{KERNEL_NAMES[kv]}_{short}_{w.kv_layout.lower()}.md"
+    fn = f"profiles/{kname}_{short}_{w.kv_layout.lower()}.md"
     rel = os.path.relpath(prefix, ROOT)
     lens = (f"{w.lengths} {w.length}" if w.lengths == "fixed"
             else f"{w.lengths} in [{w.length_lo}, {w.length_hi}]")
@@ -672,7 +688,7 @@ def profile_report(prefix):
             f"{run} --profile-only --steps 3"]
     sq = None
     if os.path.isdir(prefix + "_sq"):
-        sq = sq_summary(prefix + "_sq", KERNEL_NAMES[kv])
+        sq = sq_summary(prefix + "_sq", kname)
         cmds.append(f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d $R/{rel}_sq "
                     f"-o run -- {run} --profile-only --steps 3")
     cmds.append(f"cd $R && python3 bench.py --profile-report {rel}")
@@ -729,7 +745,7 @@ Mean: {fetch / 1e9:.4f} GB read + {write / 1e6:.2f} MB written = {hbm / 1e9:.4f}
     with open(os.path.join(ROOT, fn), "w") as f:
         f.write(md)
     traffic = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
-    ent = {"kernel": kern, "kernel_hash": kernel_hash(kv),
+    ent = {"kernel": kern, "kernel_hash": kernel_hash(w),
            "schedule": {k: sched[k] for k in ("mode", "num_splits") if k in sched},
            "num_splits": S, "hbm_bytes_per_launch": int(round(hbm)),
            "fetch_bytes": int(round(fetch)), "write_bytes": int(round(write)),
@@ -809,7 +825,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         t = json.load(open(TRAFFIC_FILE))
         ent = t.get(f"{w.name}/{w.kv_layout}")
-        if ent and ent.get("kernel_hash") == kernel_hash(kv_name(w)) \
+        if ent and ent.get("kernel_hash") == kernel_hash(w) \
                 and ent.get("schedule", {"mode": "batch", "num_splits": ent.get("num_splits")}) \
                 == {k: schedule[k] for k in ("mode", "num_splits") if k in schedule}:
             traffic = ent.get("hbm_bytes_per_launch")

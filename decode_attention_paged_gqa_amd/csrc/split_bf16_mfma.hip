@@ -1,0 +1,374 @@
+// Stage 1 over a dense bf16 cache on the matrix cores, for D = 128 and 6..16
+// query rows per kv-head (G * q: the MTP verify batches of LightLLM PR #1549,
+// "Validation", MTP step 3, and the GQA flash decode of "Covered decode
+// kernels" when G * q makes a dense 16-row tile).  Same contract as
+// decode_attn_split.
+//
+// One workgroup (4 waves) per (kv-head g, split s, request b); 16-token tiles
+// dealt round-robin to the waves.  Per tile and wave:
+//   S^T[16 tok x 16 rows] = K[16 x 128] . Q^T       4x v_mfma_f32_16x16x32_bf16
+//   O^T[128 x 16 rows]   += V^T[128 x 16] . P^T    16x v_mfma_f32_16x16x16_bf16
+// S is computed transposed so each lane's four scores (4 tokens, one row)
+// sit where the PV product wants its B operand.  Lane l = 16*lg + lm.
+//
+// Precision: Q, K and V enter as the bf16 values they are, so every product
+// is exact in fp32 and accumulates in fp32.  The weights P are the only
+// values that would need a rounding to enter the matrix core; a single bf16
+// rounding of P would cost ~2e-3 rel-L2 on the output, so P goes in as two
+// bf16 terms, hi = bf16(p) and lo = bf16(p - hi), in two PV products:
+// |p - hi - lo| <= 2^-16 |p|.
+//   * QK: MFMA kb, lane (lm, lg): token lm, elements 32*kb + 8*lg + 0..7,
+//     i.e. 16-byte chunk 4*kb + lg of its row; Q^T likewise for row lm.
+//   * PV: output block bb, row m is d = 8*m + bb: lane (lm, lg) holds chunk
+//     lm (elements 8*lm .. 8*lm+7) of each of its four tokens 4*lg + j, and
+//     one v_perm per token pair picks element bb of each.
+//
+// Memory pipeline: a 16-token tile is 4 KB of K and 4 KB of V per wave.  The
+// per-wave LDS ring has two such stages (two workgroups fit a CU); a stage is
+// read into registers and at once refilled with the tile two ahead, so two
+// tiles are in flight behind the one being computed.  Loads are
+// global_load_lds (16 bytes per lane), read back by inline asm after an
+// explicit vmcnt wait (the compiler would drain the queue before any LDS read
+// it can see).  A row's sixteen 16-byte chunks are stored rotated by the
+// token index within the tile, so both operand reads spread over the LDS
+// banks.
+//
+// Softmax: one running reference m per query row, uniform over the lanes
+// holding that row; raised lazily when a score exceeds m + 8 (log2 units).
+#include <type_traits>
+
+#include "mfma_util.h"
+
+namespace {
+
+using namespace da_mfma;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 2;
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kMaxSplitPages = 512;
+constexpr int kD = 128;
+
+constexpr int kStageK = 0;
+constexpr int kStageV = 4096;
+constexpr int kStageBytes = 8192;
+constexpr int kRingBytes = kWaves * kStages * kStageBytes;           // 64 KB
+constexpr int kEpiBytes = (kWaves * 16 * kD + 2 * kWaves * 16) * 4;  // 33 KB
+constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
+constexpr int kSmemBytes = kMainBytes + kMaxSplitPages * 4;
+
+// LDS position of 16-byte chunk c of tile row t
+__host__ __device__ constexpr int chunk_pos(int t, int c) { return (c + t) & 15; }
+
+struct StageData {
+  u32x4 k[4];  // token lm: chunk 4*kb + lg
+  u32x4 v[4];  // token 4*lg + j: chunk lm
+};
+
+// All reads of one stage plus a page id, in one asm block.
+__device__ __forceinline__ int32_t read_stage(const uint32_t (&ka)[4], const uint32_t (&va)[4],
+                                              uint32_t pidaddr, StageData& s) {
+  int32_t pid;
+  asm volatile(
+      "ds_read_b128 %0, %9\n\t"
+      "ds_read_b128 %1, %10\n\t"
+      "ds_read_b128 %2, %11\n\t"
+      "ds_read_b128 %3, %12\n\t"
+      "ds_read_b128 %4, %13\n\t"
+      "ds_read_b128 %5, %14\n\t"
+      "ds_read_b128 %6, %15\n\t"
+      "ds_read_b128 %7, %16\n\t"
+      "ds_read_b32 %8, %17\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(s.k[0]), "=&v"(s.k[1]), "=&v"(s.k[2]), "=&v"(s.k[3]), "=&v"(s.v[0]),
+        "=&v"(s.v[1]), "=&v"(s.v[2]), "=&v"(s.v[3]), "=&v"(pid)
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
+        "v"(va[3]), "v"(pidaddr)
+      : "memory");
+  return __builtin_amdgcn_readfirstlane(pid);
+}
+
+struct Bf16MfmaArgs {
+  const uint16_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const int32_t* pt;
+  const int32_t* seqlens;
+  da::Stage1Sched sched;  // (request, split) of every workgroup
+  float* o;
+  float* lse;
+  int pt_stride, max_pages;
+  int qn, Hq, Hkv, G, R;
+  int page_size, log2_ps, num_pages;
+  int slot_stride, head_stride;  // rows (see da_host::KvStrides)
+  float scale_log2;
+  int causal;
+};
+
+__device__ __forceinline__ float bf16_to_f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// two fp32 values -> packed bf16 pair (round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)da::float_to_bf16_rne(lo) | ((uint32_t)da::float_to_bf16_rne(hi) << 16);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16MfmaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
+
+  da::Stage1Item it;
+  if (!da::stage1_item<false>(a.sched, a.Hkv, it)) return;
+  const int g = it.g, s = it.s, b = it.b;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lm = lane & 15, lg = lane >> 4;
+
+  const int ps = a.page_size;
+  const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
+  const int n = (L + ps - 1) >> a.log2_ps;
+  const int cpg = (n + it.S - 1) / it.S;
+  const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
+  const int t0 = p0 * ps, t1 = min(p1 * ps, L);
+  const int ntiles = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
+  const int nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+
+  {
+    const int32_t* ptrow = a.pt + (long long)b * a.pt_stride;
+    for (int j = threadIdx.x; j < p1 - p0; j += kThreads) {
+      const int pid = ptrow[p0 + j];
+      s_pid[j] = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
+    }
+  }
+
+  // ---- Q^T operand: row lm, elements 32*kb + 8*lg + e (rows past R: zero)
+  u32x4 qv[4];
+  int tlim;  // tokens t < tlim are visible to this lane's row
+  {
+    const int r = lm;
+    const bool live = r < a.R;
+    const int i = live ? r / a.G : 0, h = g * a.G + (live ? r % a.G : 0);
+    const uint4* qp =
+        reinterpret_cast<const uint4*>(a.q + (((long long)b * a.qn + i) * a.Hq + h) * kD + 8 * lg);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint4 x = qp[4 * kb];
+      qv[kb] = live ? u32x4{x.x, x.y, x.z, x.w} : u32x4{0u, 0u, 0u, 0u};
+    }
+    tlim = live ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
+  }
+  // the query loads are waited for here, not inside the pipeline
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) asm volatile("" : "+v"(qv[kb]));
+  // tiles below every live row's limit need no masks (rows past R have
+  // tlim 0 and are never written, so they do not bound the unmasked region)
+  int tfull;
+  {
+    int lim_live = lm < a.R ? tlim : t1;
+    for (int o = 1; o < 16; o <<= 1) lim_live = min(lim_live, __shfl_xor(lim_live, o, 64));
+    tfull = __builtin_amdgcn_readfirstlane(lim_live);
+  }
+
+  float4_t acc[8];
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) acc[bb] = {0.f, 0.f, 0.f, 0.f};
+  float m = da::kNegInf, l = 0.f;
+  __syncthreads();  // s_pid visible
+
+  // ---- addressing
+  const long long rowb = (long long)a.slot_stride * kD * 2;  // bytes between slots
+  // DMA instruction h, lane i fills LDS chunk i of that 1 KB block: tile row
+  // 4h + i/16, position i%16, holding the row's chunk (position - row) mod 16
+  uint32_t voff[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int t = 4 * h + (lane >> 4), p = lane & 15;
+    voff[h] = (uint32_t)(t * rowb + 16 * ((p - t) & 15));
+  }
+  DA_LDS uint8_t* ring = (DA_LDS uint8_t*)smem + wave * (kStages * kStageBytes);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  const uint32_t pid_lds = (uint32_t)(uintptr_t)(DA_LDS void*)s_pid;
+  uint32_t rd_k[4], rd_v[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    rd_k[x] = kStageK + 256 * lm + 16 * chunk_pos(lm, 4 * x + lg);
+    const int t = 4 * lg + x;
+    rd_v[x] = kStageV + 256 * t + 16 * chunk_pos(t, lm);
+  }
+
+  auto tile_base = [&](int j) { return t0 + ((wave + kWaves * j) << 4); };
+  auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - p0); };
+  const long long head_row = (long long)g * a.head_stride;
+  auto issue = [&](int j, int pid) {
+    const long long row0 = (long long)pid * ps * a.Hkv +
+                           (long long)(tile_base(j) & (ps - 1)) * a.slot_stride + head_row;
+    DA_LDS uint8_t* st = ring + (j % kStages) * kStageBytes;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * (kD * 2) + voff[h]),
+                                       (DA_LDS void*)(st + kStageK + 1024 * h), 16, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * (kD * 2) + voff[h]),
+                                       (DA_LDS void*)(st + kStageV + 1024 * h), 16, 0, 0);
+  };
+
+  auto compute = [&](int j, const StageData& sd, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    // ---- S^T: dot[i] = q . k for token 4*lg + i, row lm
+    float4_t dot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      dot = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, sd.k[kb]),
+                                                    __builtin_bit_cast(bf16x8_t, qv[kb]), dot, 0,
+                                                    0, 0);
+    const int tb = tile_base(j) + 4 * lg;
+    float z[4];
+    bool need = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = fmaf(dot[i], a.scale_log2, -m);
+      if (MASKED && !(tb + i < tlim)) z[i] = da::kNegInf;
+      need |= z[i] > kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      // raise each row's reference to its max over the tile (rare)
+      float sabs[4], mx = da::kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sabs[i] = (!MASKED || tb + i < tlim) ? dot[i] * a.scale_log2 : da::kNegInf;
+        mx = fmaxf(mx, sabs[i]);
+      }
+      mx = fmaxf(mx, xor16(mx));
+      mx = fmaxf(mx, xor32(mx));
+      const float mn = fmaxf(m, mx);
+      const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m - mn);
+      l *= al;
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) acc[bb] *= al;
+      m = mn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - mn;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = da::fast_exp2(z[i]);
+      l += p[i];
+    }
+    // P^T operand in two bf16 terms: hi = bf16(p), lo = bf16(p - hi)
+    const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
+    const uint32_t l01 = pack_bf16(p[0] - bf16_to_f(h01 & 0xffffu), p[1] - bf16_to_f(h01 >> 16));
+    const uint32_t l23 = pack_bf16(p[2] - bf16_to_f(h23 & 0xffffu), p[3] - bf16_to_f(h23 >> 16));
+    const s16x4_t phi = __builtin_bit_cast(s16x4_t, u32x2{h01, h23});
+    const s16x4_t plo = __builtin_bit_cast(s16x4_t, u32x2{l01, l23});
+
+    // ---- V^T operand: tokens 4*lg + jj, d = 8*lm + bb.  Rows past the split
+    // end may hold anything (even NaN): zero there.
+    u32x4 vw[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const bool ok = !MASKED || tb + jj < t1;
+      vw[jj] = ok ? sd.v[jj] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      // element bb of each token's chunk: dword bb/2, half bb%2
+      const uint32_t sel = (bb & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t x01 = __builtin_amdgcn_perm(vw[1][bb >> 1], vw[0][bb >> 1], sel);
+      const uint32_t x23 = __builtin_amdgcn_perm(vw[3][bb >> 1], vw[2][bb >> 1], sel);
+      const s16x4_t va = __builtin_bit_cast(s16x4_t, u32x2{x01, x23});
+      acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[bb], 0, 0, 0);
+      acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[bb], 0, 0, 0);
+    }
+  };
+
+  // ---- pipeline: tile j is read into registers and its stage refilled with
+  // tile j + 2 at once; tiles j+1 and j+2 stay in flight during compute(j)
+  auto step = [&](int j, StageData& sd) {
+    if (j + 1 < nmine) wait_vmcnt<8>();  // tile j+1's 8 loads may stay in flight
+    else wait_vmcnt<0>();
+    const int jn = min(j + kStages, nmine - 1);  // the tile to issue next
+    const uint32_t base = ring_lds + (j % kStages) * kStageBytes;
+    const uint32_t ka[4] = {base + rd_k[0], base + rd_k[1], base + rd_k[2], base + rd_k[3]};
+    const uint32_t va[4] = {base + rd_v[0], base + rd_v[1], base + rd_v[2], base + rd_v[3]};
+    const int pid = read_stage(ka, va, pid_addr(jn), sd);
+    if (j + kStages < nmine) issue(j + kStages, pid);  // into the stage just read
+  };
+  const int lim = tfull - t0 - 16 * wave - 16;
+  const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * kWaves) + 1);
+#pragma unroll
+  for (int u = 0; u < kStages; ++u)
+    if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
+  for (int j = 0; j < jfull; ++j) {
+    StageData sd;
+    step(j, sd);
+    compute(j, sd, std::false_type{});
+  }
+  for (int j = jfull; j < nmine; ++j) {
+    StageData sd;
+    step(j, sd);
+    compute(j, sd, std::true_type{});
+  }
+
+  // ---- l is partial over the lane groups; acc and m are already per row
+  l += xor16(l);
+  l += xor32(l);
+  __syncthreads();  // ring no longer read by any wave; reuse it
+  float* sm_acc = reinterpret_cast<float*>(smem);  // [kWaves][16][kD]
+  float* sm_m = sm_acc + kWaves * 16 * kD;         // [kWaves][16]
+  float* sm_l = sm_m + kWaves * 16;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_acc[(wave * 16 + lm) * kD + 8 * (4 * lg + i) + bb] = acc[bb][i];
+  if (lg == 0) {
+    sm_m[wave * 16 + lm] = m;
+    sm_l[wave * 16 + lm] = l;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < a.R * kD; idx += kThreads) {
+    const int r = idx / kD, d = idx - r * kD;
+    float M = da::kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + r]);
+    float lsum = 0.f, o = 0.f;
+    if (M != da::kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = da::fast_exp2(sm_m[w * 16 + r] - M);
+        lsum = fmaf(sm_l[w * 16 + r], f, lsum);
+        o = fmaf(sm_acc[(w * 16 + r) * kD + d], f, o);
+      }
+    }
+    const int i = r / a.G, h = g * a.G + (r % a.G);
+    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.sched.S + s;
+    a.o[orow * kD + d] = lsum > 0.f ? o / lsum : 0.f;
+    if (d == 0) a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum)) * da::kLn2 : da::kNegInf;
+  }
+}
+
+}  // namespace
+
+// bf16 stage 1 on the matrix cores for 6..16 query rows per kv-head; -1 when
+// the shape is not covered (the caller then uses another kernel).
+int32_t da_split_bf16_mfma(const da_host::SplitCall& c) {
+  const int G = c.Hq / c.Hkv, R = G * c.qn;
+  if (!c.q_bf16 || c.D != kD || R < 6 || R > 16) return -1;
+  if (da_host::max_split_pages(c) > kMaxSplitPages) return -1;
+  Bf16MfmaArgs a;
+  a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
+  a.pt = c.pt; a.seqlens = c.seqlens; a.sched = c.sched(); a.o = c.o; a.lse = c.lse;
+  a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
+  a.qn = c.qn; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = G; a.R = R;
+  a.page_size = c.ps; a.log2_ps = __builtin_ctz((unsigned)c.ps); a.num_pages = c.num_pages;
+  a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
+  a.scale_log2 = c.scale * da::kLog2e;
+  a.causal = c.causal;
+  hipLaunchKernelGGL(split_bf16_mfma_kernel, dim3(da_host::stage1_grid(c.Hkv, c.units, false)),
+                     dim3(kThreads), 0, c.stream, a);
+  return da_host::launch_status();
+}

@@ -430,6 +430,7 @@ SplitArgs make_args(const da_host::SplitCall& c) {
 
 // Specialised stage-1 kernels; each returns -1 when the shape is not covered.
 int32_t da_split_bf16_fast(const da_host::SplitCall& c);  // split_bf16.hip: bf16, G*q <= 5
+int32_t da_split_bf16_mfma(const da_host::SplitCall& c);  // split_bf16_mfma.hip: 6..16 rows
 int32_t da_split_int8_mfma(const da_host::SplitCall& c);  // split_int8.hip: D 128, bf16 Q
 int32_t da_split_int4_mfma(const da_host::SplitCall& c);  // split_int4.hip: 9..16 rows
 
@@ -454,6 +455,8 @@ extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k
   if (dtype == DA_BF16) {
     const int32_t fast = da_split_bf16_fast(c);
     if (fast >= 0) return fast;
+    const int32_t mf = da_split_bf16_mfma(c);
+    if (mf >= 0) return mf;
     return launch_kv<KV_BF16>(make_args(c), head_dim, c.stream);
   }
   return launch_kv<KV_F32>(make_args(c), head_dim, c.stream);

@@ -103,8 +103,12 @@ INT4_MTP_B64 = Workload(
     lengths="uniform", length_lo=8192, length_hi=32768, seed=5,
     splits=(1, 2, 4, 8, 16, 32), kv_layout="HND")
 
+# the INT4-MTP verify shape over a dense bf16 cache (16 query rows per kv-head)
+BF16_MTP_B64 = INT4_MTP_B64.scaled(name="bf16_mtp4_b64_hq32_hkv8_d128_p64_L8k-32k", kv=KV_DENSE,
+                                   seed=6)
+
 WORKLOADS = {w.name: w for w in (TINY_FP32, BF16_B16, RAGGED_B64, UNIFORM_B64,
-                                 INT8_B32, INT4_MTP_B64)}
+                                 INT8_B32, INT4_MTP_B64, BF16_MTP_B64)}
 
 
 def draw_lengths(w: Workload, rng: np.random.Generator) -> np.ndarray:

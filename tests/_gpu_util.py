@@ -183,13 +183,48 @@ FP16_U = 2.0 ** -11
 
 
 def uses_matrix_path(w: W.Workload) -> bool:
-    """Whether stage 1 over this quantised workload runs on the matrix cores."""
+    """Whether stage 1 over this workload runs on the matrix cores (D = 128,
+    bf16 Q): INT4 with 9..16 query rows per kv-head, INT8 with up to 16,
+    a dense bf16 cache with 6..16."""
     rows = w.group * w.q_per_req
     if w.head_dim != 128 or w.dtype == "fp32":
         return False
     if w.kv == W.KV_INT4:
         return 9 <= rows <= 16
-    return w.kv == W.KV_INT8 and rows <= 16
+    if w.kv == W.KV_INT8:
+        return rows <= 16
+    return 6 <= rows <= 16
+
+
+def bf16_split_pv_o_bound(batch: W.PagedBatch):
+    """Per (request, query head) bound on |dO| of the dense bf16 matrix-core
+    path, shaped [B, 1, Hq, 1, 1]: P enters as hi + lo with hi = bf16(p),
+    lo = bf16(p - hi), so |p - hi - lo| <= u^2 |p| with u = 2^-8 (bf16), V is
+    exact, and O divides by the exact fp32 sum of p: |dO| <= 2^-16 max|v|
+    over the request's tokens (x1.01)."""
+    w = batch.w
+    v = W.host_f64(batch.nhd(batch.v_pool))
+    pt = W.host_int(batch.page_table)
+    L = W.host_int(batch.seq_lens)
+    B, G = len(L), w.group
+    out = np.zeros((B, 1, w.num_q_heads, 1, 1))
+    for b in range(B):
+        n = int(L[b])
+        if n == 0:
+            continue
+        t = np.arange(n)
+        vm = np.abs(v[pt[b, t // w.page_size], t % w.page_size]).max(axis=(0, 2))  # [Hkv]
+        for g in range(w.num_kv_heads):
+            out[b, 0, g * G:(g + 1) * G] = 2.0 ** -16 * vm[g] * 1.01
+    return out
+
+
+def matrix_path_o_bound(batch: W.PagedBatch):
+    """The extra |dO| bound of the workload's matrix-core path, or None."""
+    w = batch.w
+    if not uses_matrix_path(w):
+        return None
+    return bf16_split_pv_o_bound(batch) if w.kv == W.KV_DENSE else fp16_pv_o_bound(batch)
 
 
 def fp16_pv_o_bound(batch: W.PagedBatch):

@@ -96,7 +96,7 @@ def test_small_elementwise(gpu, w, S):
     o_ref, l_ref = U.oracle_partials(batch, S)
     out_ref, lse_ref = U.oracle_full(batch)
     out, lse, o, l = U.run_decode(gpu, batch, S)
-    extra = U.fp16_pv_o_bound(batch) if U.uses_matrix_path(w) else None
+    extra = U.matrix_path_o_bound(batch)
     U.check_partials(U.to_np(o), U.to_np(l), o_ref, l_ref, f"{w.name} S={S}", o_extra=extra)
     _check_out(w, U.to_np(out), out_ref, f"{w.name} S={S} out")
     U.check_lse(U.to_np(lse), lse_ref, f"{w.name} S={S} lse")
@@ -117,7 +117,7 @@ def test_int4_fractional_zero_points(gpu, w):
     o_ref, l_ref = U.oracle_partials(batch, S)
     out_ref, lse_ref = U.oracle_full(batch)
     out, lse, o, l = U.run_decode(gpu, batch, S)
-    extra = U.fp16_pv_o_bound(batch) if U.uses_matrix_path(w) else None
+    extra = U.matrix_path_o_bound(batch)
     U.check_partials(U.to_np(o), U.to_np(l), o_ref, l_ref, f"{w.name} frac-z", o_extra=extra)
     U.check_quant(U.to_np(out), out_ref, f"{w.name} frac-z out")
     U.check_lse(U.to_np(lse), lse_ref, f"{w.name} frac-z lse")
@@ -181,6 +181,7 @@ def test_outputs_fully_overwritten(gpu):
 
 
 @pytest.mark.parametrize("w", both_layouts([RAGGED_SMALL.scaled(pool_pages=200),
+                                             MTP_BF16.scaled(pool_pages=80),
                                              INT8_SMALL.scaled(pool_pages=80),
                                              INT4_SMALL.scaled(pool_pages=80)]),
                          ids=lambda w: w.name)
@@ -222,6 +223,7 @@ FULL = [
     (W.INT8_B32, None, [(0, 0), (31, 7), (13, 2)]),
     (W.INT4_MTP_B64, None, None),
     (W.INT4_MTP_B64, 8, None),
+    (W.BF16_MTP_B64, None, None),
 ]
 
 

@@ -2,7 +2,8 @@
 the fp64 oracle (gates in tests/_gpu_util.py):
 
 * a split longer than the specialised kernels' page-id tables (1024 pages for
-  bf16, 512 for INT8 / INT4), which hands the launch to the generic kernel;
+  the bf16 vector kernel, 512 for the matrix-core ones), which hands the
+  launch to the generic kernel;
 * page sizes 128 and 256;
 * 16 query rows per kv-head from 16 MTP tokens of one head (q_per_req = 16);
 * a batch much wider than one workgroup (300 requests), with both schedules.
@@ -25,19 +26,22 @@ def _run_and_check(gpu, w, S, label):
     o_ref, l_ref = U.oracle_partials(batch, S)
     out_ref, lse_ref = U.oracle_full(batch)
     out, lse, o, l = U.run_decode(gpu, batch, S)
-    extra = U.fp16_pv_o_bound(batch) if U.uses_matrix_path(w) else None
+    extra = U.matrix_path_o_bound(batch)
     U.check_partials(U.to_np(o), U.to_np(l), o_ref, l_ref, f"{w.name} S={S}", o_extra=extra)
     _check_out(w, U.to_np(out), out_ref, f"{w.name} S={S} out")
     U.check_lse(U.to_np(lse), lse_ref, f"{w.name} S={S} lse")
 
 
 # one request whose single split spans more pages than the LDS page-id table
+# (1024 pages for the bf16 vector kernel, 512 for the matrix-core kernels)
 LONG = [
     W.RAGGED_B64.scaled(name="long_split_bf16_g5_p16", batch=2, page_size=16, lengths="list",
                         length_list=(16400, 37), pin_max=False),
     W.INT8_B32.scaled(name="long_split_int8_p16", batch=2, page_size=16, lengths="list",
                       length_list=(8250, 5)),
     W.INT4_MTP_B64.scaled(name="long_split_int4_mtp_p16", batch=2, page_size=16, lengths="list",
+                          length_list=(8250, 9)),
+    W.BF16_MTP_B64.scaled(name="long_split_bf16_mtp_p16", batch=2, page_size=16, lengths="list",
                           length_list=(8250, 9)),
 ]
 

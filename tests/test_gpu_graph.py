@@ -30,6 +30,8 @@ CASES = [
                           length_list=(4, 100, 1300, 2500)),
     W.INT4_MTP_B64.scaled(name="graph_int4_mtp_nhd", batch=3, lengths="list",
                           length_list=(9, 400, 1800), kv_layout="NHD"),
+    W.BF16_MTP_B64.scaled(name="graph_bf16_mtp", batch=4, lengths="list",
+                          length_list=(3, 90, 1200, 2600)),
 ]
 
 

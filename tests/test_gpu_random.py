@@ -78,7 +78,7 @@ def test_random_configuration(gpu, w, S, table):
         o_ref, l_ref = U.oracle_partials_per_request(batch, S, counts)
         og, lg = U.blank_unused_slots(U.to_np(o), U.to_np(l), counts)
     out_ref, lse_ref = U.oracle_full(batch)
-    extra = U.fp16_pv_o_bound(batch) if U.uses_matrix_path(w) else None
+    extra = U.matrix_path_o_bound(batch)
     U.check_partials(og, lg, o_ref, l_ref, w.name, o_extra=extra)
     if fp32_out:
         U.check_fp32(U.to_np(out), out_ref, f"{w.name} out fp32")

@@ -132,7 +132,7 @@ def test_per_request_splits_elementwise(gpu, w, smax):
     o_ref, l_ref = U.oracle_partials_per_request(batch, smax, counts)
     out_ref, lse_ref = U.oracle_full(batch)
     og, lg = U.blank_unused_slots(U.to_np(o), U.to_np(l), counts)
-    extra = U.fp16_pv_o_bound(batch) if U.uses_matrix_path(w) else None
+    extra = U.matrix_path_o_bound(batch)
     U.check_partials(og, lg, o_ref, l_ref, f"{w.name} per-request", o_extra=extra)
     if out_dtype == torch.float32:
         U.check_fp32(U.to_np(out), out_ref, f"{w.name} per-request out fp32")
