@@ -109,6 +109,7 @@ def stage1_kernel(w):
     from decode_attention_paged_gqa_amd import workloads as W
 
     rows = w.group * w.q_per_req
+    rows = -(-rows // -(-rows // 16))  # rows per block (blocks of at most 16)
     bf16_q = w.dtype == "bf16"
     if w.kv == W.KV_DENSE and bf16_q and rows <= 5:
         return "split_bf16_kernel", ["split_bf16.hip", "common.h"]

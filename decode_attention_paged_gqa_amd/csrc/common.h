@@ -68,6 +68,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //    side.
 // Units keep their order (longest requests first with a batch order or a
 // work list).
+//
+// Row blocks: a kv-head serves R = G * q_per_req query rows.  A kernel holds
+// at most 16 of them, so R > 16 is cut into nrb = ceil(R / 16) blocks of
+// ceil(R / nrb) rows (the last may be shorter), and each (kv-head, block)
+// pair is a workgroup of its own, as if it were a kv-head: the grid carries
+// Hkv * nrb "heads".  Every block reads the kv-head's pages; the grouped
+// order is then used for every kernel, which puts the nrb blocks of a
+// kv-head on one XCD as consecutive workgroups, so the later blocks find the
+// pages in that XCD's L2.
 constexpr int kXcds = 8;
 constexpr int kItemShift = 8;  // work item = b << 8 | s
 
@@ -78,10 +87,14 @@ struct Stage1Sched {
   int S;                  // split slots per query row; the split count without a work list
   int B;                  // requests
   int units;              // S * B, or the work list's capacity
+  int rows;               // R = G * q_per_req query rows per kv-head
+  int nrb;                // row blocks per kv-head
+  int rb_rows;            // rows per block (the last block may have fewer)
 };
 
 struct Stage1Item {
   int g, b, s, S;  // kv-head, request, split, the request's split count
+  int r0, nr;      // this workgroup's query rows: r0 .. r0 + nr - 1 of the kv-head
 };
 
 // false for padding workgroups: the last round of the grouped order, -1
@@ -89,17 +102,22 @@ struct Stage1Item {
 template <bool GROUPED>
 __device__ __forceinline__ bool stage1_item(const Stage1Sched& sc, int Hkv, Stage1Item& it) {
   const int i = (int)blockIdx.x;
-  int u;
-  if (!GROUPED) {
-    u = i / Hkv;
-    it.g = i - u * Hkv;
+  const int Hv = Hkv * sc.nrb;  // (kv-head, row block) pairs
+  int u, gv;
+  if (!GROUPED && sc.nrb == 1) {
+    u = i / Hv;
+    gv = i - u * Hv;
   } else {
     const int x = i % kXcds, k = i / kXcds;
-    const int r = k / Hkv;
+    const int r = k / Hv;
     u = r * kXcds + ((r & 1) ? kXcds - 1 - x : x);
-    it.g = k - r * Hkv;
+    gv = k - r * Hv;
     if (u >= sc.units) return false;
   }
+  it.g = gv / sc.nrb;
+  it.r0 = (gv - it.g * sc.nrb) * sc.rb_rows;
+  it.nr = min(sc.rb_rows, sc.rows - it.r0);  // >= 1 for every R <= 2^24 (entry check)
+  if (it.nr <= 0) return false;
   if (!sc.work) {
     const int z = u / sc.S;
     it.s = u - z * sc.S;
@@ -167,6 +185,7 @@ struct SplitCall {
   const int32_t* counts;
   int units;              // grid units: S * batch, or the work list's capacity
   int batch, qn, Hq, Hkv, D, ps, num_pages, S;
+  int rows, nrb, rb_rows;  // query rows per kv-head, row blocks, rows per block
   KvStrides kv;
   float scale;
   int causal;
@@ -178,8 +197,13 @@ struct SplitCall {
     da::Stage1Sched sc;
     sc.order = order; sc.work = work; sc.counts = counts;
     sc.S = S; sc.B = batch; sc.units = units;
+    sc.rows = rows; sc.nrb = nrb; sc.rb_rows = rb_rows;
     return sc;
   }
+
+  // grid of the launch for a kernel whose own order is `grouped` (see
+  // da::stage1_item; row blocks always take the grouped order)
+  unsigned grid(bool grouped) const;
 };
 
 // Largest split of a launch, in pages: ceil(max_pages / S), or max_pages with
@@ -190,9 +214,19 @@ inline int max_split_pages(const SplitCall& c) {
 
 // 1-D grid of stage 1 (see da::stage1_item) over `units` work units; the
 // grouped order pads to whole rounds of 8 units
-inline unsigned stage1_grid(int Hkv, long long units, bool grouped) {
-  if (!grouped) return (unsigned)(units * Hkv);
-  return (unsigned)(da::kXcds * (long long)Hkv * ((units + da::kXcds - 1) / da::kXcds));
+inline long long stage1_grid(long long heads, long long units, bool grouped) {
+  if (!grouped) return units * heads;
+  return da::kXcds * heads * ((units + da::kXcds - 1) / da::kXcds);
+}
+
+inline unsigned SplitCall::grid(bool grouped) const {
+  return (unsigned)stage1_grid((long long)Hkv * nrb, units, grouped || nrb > 1);
+}
+
+// Row blocks of R query rows per kv-head (see da::stage1_item).
+inline void row_blocks(int R, int& nrb, int& rb_rows) {
+  nrb = (R + DA_MAX_ROWS - 1) / DA_MAX_ROWS;
+  rb_rows = (R + nrb - 1) / nrb;
 }
 
 }  // namespace da_host

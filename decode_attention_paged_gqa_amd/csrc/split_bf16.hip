@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
 
   da::Stage1Item it;
   if (!da::stage1_item<false>(a.sched, a.Hkv, it)) return;
-  const int g = it.g, s = it.s, b = it.b;
+  const int g = it.g, s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tq = lane >> 3, c = lane & 7;
@@ -195,13 +195,13 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
     }
   }
 
-  // ---- query rows r = i*G + hh; lane keeps its 2*CPL chunks of every row
+  // ---- query rows r0 + r = i*G + hh; lane keeps its 2*CPL chunks of every row
   uint32_t qv[RT][4 * CPL];
   int tlim[RT];
   int tfull = t1;
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const int rr = r < a.R ? r : 0;
+    const int rr = r0 + (r < nr ? r : 0);
     const int i = rr / a.G, h = g * a.G + (rr % a.G);
     const uint16_t* qp = a.q + (((long long)b * a.qn + i) * a.Hq + h) * D + 8 * c;
 #pragma unroll
@@ -211,8 +211,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
       qv[r][4 * cc + 2] = x.z; qv[r][4 * cc + 3] = x.w;
     }
     // visibility limit of the row: split end, and the causal limit of query i
-    tlim[r] = r < a.R ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
-    if (r < a.R) tfull = min(tfull, tlim[r]);
+    tlim[r] = r < nr ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
+    if (r < nr) tfull = min(tfull, tlim[r]);
   }
   // Make the query registers "produced" here, so the compiler waits for the
   // query loads once, before the pipeline, instead of draining the LDS-DMA
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
   __syncthreads();
 
   // ---- combine the partial states and write this split's partial rows
-  for (int idx = threadIdx.x; idx < a.R * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < nr * D; idx += kThreads) {
     const int r = idx / D, d = idx - r * D;
     float M = da::kNegInf;
 #pragma unroll
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
         o = fmaf(ow, f, o);
       }
     }
-    const int i = r / a.G, h = g * a.G + (r % a.G);
+    const int i = (r0 + r) / a.G, h = g * a.G + ((r0 + r) % a.G);
     const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.sched.S + s;
     a.o[orow * D + d] = lsum > 0.f ? o / lsum : 0.f;
     if (d == 0) a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum)) * da::kLn2 : da::kNegInf;
@@ -423,10 +423,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
 }
 
 template <int D, int RT>
-int32_t launch(const Bf16Args& a, hipStream_t st) {
-  hipLaunchKernelGGL((split_bf16_kernel<D, RT, 4>),
-                     dim3(da_host::stage1_grid(a.Hkv, a.sched.units, false)), dim3(kThreads), 0, st,
-                     a);
+int32_t launch(const Bf16Args& a, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((split_bf16_kernel<D, RT, 4>), dim3(grid), dim3(kThreads), 0, st, a);
   return da_host::launch_status();
 }
 
@@ -436,7 +434,7 @@ int32_t launch(const Bf16Args& a, hipStream_t st) {
 // when this kernel does not cover the shape (the caller then uses the
 // generic kernel).
 int32_t da_split_bf16_fast(const da_host::SplitCall& c) {
-  const int G = c.Hq / c.Hkv, R = G * c.qn, D = c.D;
+  const int G = c.Hq / c.Hkv, R = c.rb_rows, D = c.D;  // rows per block
   if (R > 5 || (D != 128 && D != 64)) return -1;
   if (da_host::max_split_pages(c) > kMaxSplitPages) return -1;
   Bf16Args a;
@@ -449,18 +447,19 @@ int32_t da_split_bf16_fast(const da_host::SplitCall& c) {
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
   hipStream_t st = c.stream;
+  const unsigned grid = c.grid(false);
   if (D == 128) {
     switch (R) {
-      case 1: return launch<128, 1>(a, st);
-      case 2: return launch<128, 2>(a, st);
-      case 3: case 4: return launch<128, 4>(a, st);
-      default: return launch<128, 5>(a, st);
+      case 1: return launch<128, 1>(a, grid, st);
+      case 2: return launch<128, 2>(a, grid, st);
+      case 3: case 4: return launch<128, 4>(a, grid, st);
+      default: return launch<128, 5>(a, grid, st);
     }
   }
   switch (R) {
-    case 1: return launch<64, 1>(a, st);
-    case 2: return launch<64, 2>(a, st);
-    case 3: case 4: return launch<64, 4>(a, st);
-    default: return launch<64, 5>(a, st);
+    case 1: return launch<64, 1>(a, grid, st);
+    case 2: return launch<64, 2>(a, grid, st);
+    case 3: case 4: return launch<64, 4>(a, grid, st);
+    default: return launch<64, 5>(a, grid, st);
   }
 }

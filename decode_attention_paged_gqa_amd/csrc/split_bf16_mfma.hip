@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
 
   da::Stage1Item it;
   if (!da::stage1_item<false>(a.sched, a.Hkv, it)) return;
-  const int g = it.g, s = it.s, b = it.b;
+  const int g = it.g, s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lm = lane & 15, lg = lane >> 4;
@@ -148,9 +148,9 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
   u32x4 qv[4];
   int tlim;  // tokens t < tlim are visible to this lane's row
   {
-    const int r = lm;
-    const bool live = r < a.R;
-    const int i = live ? r / a.G : 0, h = g * a.G + (live ? r % a.G : 0);
+    const bool live = lm < nr;
+    const int r = r0 + (live ? lm : 0);  // this lane's query row of the kv-head
+    const int i = r / a.G, h = g * a.G + r % a.G;
     const uint4* qp =
         reinterpret_cast<const uint4*>(a.q + (((long long)b * a.qn + i) * a.Hq + h) * kD + 8 * lg);
 #pragma unroll
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
   // tlim 0 and are never written, so they do not bound the unmasked region)
   int tfull;
   {
-    int lim_live = lm < a.R ? tlim : t1;
+    int lim_live = lm < nr ? tlim : t1;
     for (int o = 1; o < 16; o <<= 1) lim_live = min(lim_live, __shfl_xor(lim_live, o, 64));
     tfull = __builtin_amdgcn_readfirstlane(lim_live);
   }
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
     sm_l[wave * 16 + lm] = l;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < a.R * kD; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < nr * kD; idx += kThreads) {
     const int r = idx / kD, d = idx - r * kD;
     float M = da::kNegInf;
 #pragma unroll
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
         o = fmaf(sm_acc[(w * 16 + r) * kD + d], f, o);
       }
     }
-    const int i = r / a.G, h = g * a.G + (r % a.G);
+    const int i = (r0 + r) / a.G, h = g * a.G + ((r0 + r) % a.G);
     const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.sched.S + s;
     a.o[orow * kD + d] = lsum > 0.f ? o / lsum : 0.f;
     if (d == 0) a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum)) * da::kLn2 : da::kNegInf;
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
 // bf16 stage 1 on the matrix cores for 6..16 query rows per kv-head; -1 when
 // the shape is not covered (the caller then uses another kernel).
 int32_t da_split_bf16_mfma(const da_host::SplitCall& c) {
-  const int G = c.Hq / c.Hkv, R = G * c.qn;
+  const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block
   if (!c.q_bf16 || c.D != kD || R < 6 || R > 16) return -1;
   if (da_host::max_split_pages(c) > kMaxSplitPages) return -1;
   Bf16MfmaArgs a;
@@ -368,7 +368,7 @@ int32_t da_split_bf16_mfma(const da_host::SplitCall& c) {
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  hipLaunchKernelGGL(split_bf16_mfma_kernel, dim3(da_host::stage1_grid(c.Hkv, c.units, false)),
+  hipLaunchKernelGGL(split_bf16_mfma_kernel, dim3(c.grid(false)),
                      dim3(kThreads), 0, c.stream, a);
   return da_host::launch_status();
 }

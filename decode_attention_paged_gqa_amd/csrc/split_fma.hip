@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
 
   da::Stage1Item it;
   if (!da::stage1_item<(KV == KV_I8 || KV == KV_I4)>(a.sched, a.Hkv, it)) return;
-  const int g = it.g, s = it.s, b = it.b;
+  const int g = it.g, s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane >> 4, c = lane & 15;
 
@@ -155,13 +155,13 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
   const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
   const int t0 = p0 * ps, t1 = min(p1 * ps, L);
 
-  // ---- query rows r = i*G + hh (query token i, head g*G + hh), pre-scaled
+  // ---- query rows r0 + r = i*G + hh (query token i, head g*G + hh), pre-scaled
   float qf[RT][E];
   int tend[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    if (r < a.R) {
-      const int i = r / a.G, h = g * a.G + (r % a.G);
+    if (r < nr) {
+      const int i = (r0 + r) / a.G, h = g * a.G + ((r0 + r) % a.G);
       const long long qoff = (((long long)b * a.qn + i) * a.Hq + h) * D + c * E;
       if (a.q_bf16) {
         Raw<E * 2> qr;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
   __syncthreads();
 
   // ---- combine the 4 waves and write this split's partial rows
-  for (int idx = threadIdx.x; idx < a.R * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < nr * D; idx += kThreads) {
     const int r = idx / D, d = idx - r * D;
     float M = da::kNegInf;
 #pragma unroll
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
         o = fmaf(sm_acc[w][r][d], f, o);
       }
     }
-    const int i = r / a.G, h = g * a.G + (r % a.G);
+    const int i = (r0 + r) / a.G, h = g * a.G + ((r0 + r) % a.G);
     const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.sched.S + s;
     a.o[orow * D + d] = lsum > 0.f ? o / lsum : 0.f;
     if (d == 0) a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum)) * da::kLn2 : da::kNegInf;
@@ -349,28 +349,28 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
 }
 
 template <int KV, int D, int RT>
-int32_t launch_rt(const SplitArgs& a, hipStream_t st) {
-  constexpr bool kGrouped = KV == KV_I8 || KV == KV_I4;  // short rows share cache lines
-  hipLaunchKernelGGL((split_fma_kernel<KV, D, RT>),
-                     dim3(da_host::stage1_grid(a.Hkv, a.sched.units, kGrouped)), dim3(kThreads),
-                     0, st, a);
+int32_t launch_rt(const SplitArgs& a, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((split_fma_kernel<KV, D, RT>), dim3(grid), dim3(kThreads), 0, st, a);
   return da_host::launch_status();
 }
 
+// a.R: rows per block (at most DA_MAX_ROWS)
 template <int KV, int D>
-int32_t launch_d(const SplitArgs& a, hipStream_t st) {
+int32_t launch_d(const SplitArgs& a, unsigned grid, hipStream_t st) {
   const int R = a.R;
-  if (R <= 1) return launch_rt<KV, D, 1>(a, st);
-  if (R <= 2) return launch_rt<KV, D, 2>(a, st);
-  if (R <= 4) return launch_rt<KV, D, 4>(a, st);
-  if (R <= 5) return launch_rt<KV, D, 5>(a, st);
-  if (R <= 8) return launch_rt<KV, D, 8>(a, st);
-  return launch_rt<KV, D, 16>(a, st);
+  if (R <= 1) return launch_rt<KV, D, 1>(a, grid, st);
+  if (R <= 2) return launch_rt<KV, D, 2>(a, grid, st);
+  if (R <= 4) return launch_rt<KV, D, 4>(a, grid, st);
+  if (R <= 5) return launch_rt<KV, D, 5>(a, grid, st);
+  if (R <= 8) return launch_rt<KV, D, 8>(a, grid, st);
+  return launch_rt<KV, D, 16>(a, grid, st);
 }
 
 template <int KV>
-int32_t launch_kv(const SplitArgs& a, int D, hipStream_t st) {
-  return D == 128 ? launch_d<KV, 128>(a, st) : launch_d<KV, 64>(a, st);
+int32_t launch_kv(const da_host::SplitCall& c, const SplitArgs& a) {
+  constexpr bool kGrouped = KV == KV_I8 || KV == KV_I4;  // short rows share cache lines
+  const unsigned grid = c.grid(kGrouped);
+  return c.D == 128 ? launch_d<KV, 128>(a, grid, c.stream) : launch_d<KV, 64>(a, grid, c.stream);
 }
 
 int32_t check_common(const da_host::SplitCall& c, int32_t kv_layout) {
@@ -386,7 +386,10 @@ int32_t check_common(const da_host::SplitCall& c, int32_t kv_layout) {
   if (kv_layout != DA_KV_NHD && kv_layout != DA_KV_HND) return DA_ERR_INVALID_ARG;
   if (c.D != 64 && c.D != 128) return DA_ERR_UNSUPPORTED;
   if (!da_host::is_pow2(c.ps) || c.ps < 16 || c.ps > 256) return DA_ERR_UNSUPPORTED;
-  if ((c.Hq / c.Hkv) * c.qn > DA_MAX_ROWS) return DA_ERR_UNSUPPORTED;
+  if (c.Hq / c.Hkv > (1 << 20)) return DA_ERR_INVALID_ARG;
+  // the grouped order (the larger grid) must fit a 1-D launch
+  if (da_host::stage1_grid((long long)c.Hkv * c.nrb, c.units, true) > 0x7fffffffll)
+    return DA_ERR_INVALID_ARG;
   return DA_OK;
 }
 
@@ -406,6 +409,11 @@ da_host::SplitCall make_call(const void* q, int q_bf16, const void* k, const voi
   c.units = work ? work_capacity : (int)((long long)S * batch);
   c.batch = batch; c.qn = qn; c.Hq = Hq; c.Hkv = Hkv; c.D = D; c.ps = ps;
   c.num_pages = num_pages; c.S = S;
+  c.rows = c.nrb = c.rb_rows = 1;
+  if (Hkv > 0 && Hq > 0 && Hq % Hkv == 0 && qn > 0 && qn <= DA_MAX_Q_PER_REQ && Hq / Hkv <= (1 << 20)) {
+    c.rows = (Hq / Hkv) * qn;
+    da_host::row_blocks(c.rows, c.nrb, c.rb_rows);
+  }
   if (!da_host::kv_strides(kv_layout, Hkv, ps, c.kv)) c.kv = {0, 0};  // rejected by the check
   c.scale = scale; c.causal = causal ? 1 : 0;
   c.o = o; c.lse = lse; c.stream = (hipStream_t)stream;
@@ -418,7 +426,7 @@ SplitArgs make_args(const da_host::SplitCall& c) {
   a.seqlens = c.seqlens; a.sched = c.sched();
   a.o = c.o; a.lse = c.lse; a.q_bf16 = c.q_bf16;
   a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
-  a.qn = c.qn; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = c.Hq / c.Hkv; a.R = a.G * c.qn;
+  a.qn = c.qn; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = c.Hq / c.Hkv; a.R = c.rb_rows;
   a.page_size = c.ps; a.log2_ps = __builtin_ctz((unsigned)c.ps); a.num_pages = c.num_pages;
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
@@ -431,6 +439,7 @@ SplitArgs make_args(const da_host::SplitCall& c) {
 // Specialised stage-1 kernels; each returns -1 when the shape is not covered.
 int32_t da_split_bf16_fast(const da_host::SplitCall& c);  // split_bf16.hip: bf16, G*q <= 5
 int32_t da_split_bf16_mfma(const da_host::SplitCall& c);  // split_bf16_mfma.hip: 6..16 rows
+// (rows per block: every kernel takes the rows of one row block, see DA_MAX_ROWS)
 int32_t da_split_int8_mfma(const da_host::SplitCall& c);  // split_int8.hip: D 128, bf16 Q
 int32_t da_split_int4_mfma(const da_host::SplitCall& c);  // split_int4.hip: 9..16 rows
 
@@ -457,9 +466,9 @@ extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k
     if (fast >= 0) return fast;
     const int32_t mf = da_split_bf16_mfma(c);
     if (mf >= 0) return mf;
-    return launch_kv<KV_BF16>(make_args(c), head_dim, c.stream);
+    return launch_kv<KV_BF16>(c, make_args(c));
   }
-  return launch_kv<KV_F32>(make_args(c), head_dim, c.stream);
+  return launch_kv<KV_F32>(c, make_args(c));
 }
 
 extern "C" int32_t decode_attn_split_int8(
@@ -482,7 +491,7 @@ extern "C" int32_t decode_attn_split_int8(
   if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
   const int32_t mf = da_split_int8_mfma(c);
   if (mf >= 0) return mf;
-  return launch_kv<KV_I8>(make_args(c), head_dim, c.stream);
+  return launch_kv<KV_I8>(c, make_args(c));
 }
 
 extern "C" int32_t decode_attn_split_int4(
@@ -505,5 +514,5 @@ extern "C" int32_t decode_attn_split_int4(
   if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
   const int32_t mf = da_split_int4_mfma(c);
   if (mf >= 0) return mf;
-  return launch_kv<KV_I4>(make_args(c), head_dim, c.stream);
+  return launch_kv<KV_I4>(c, make_args(c));
 }

@@ -107,8 +107,13 @@ INT4_MTP_B64 = Workload(
 BF16_MTP_B64 = INT4_MTP_B64.scaled(name="bf16_mtp4_b64_hq32_hkv8_d128_p64_L8k-32k", kv=KV_DENSE,
                                    seed=6)
 
+# MTP verify (4 causal tokens) on the headline's heads (Hq 40, Hkv 8): 20 query
+# rows per kv-head, processed as two row blocks of 10
+BF16_MTP_G5_B64 = INT4_MTP_B64.scaled(name="bf16_mtp4_b64_hq40_hkv8_d128_p64_L8k-32k",
+                                      kv=KV_DENSE, num_q_heads=40, seed=7)
+
 WORKLOADS = {w.name: w for w in (TINY_FP32, BF16_B16, RAGGED_B64, UNIFORM_B64,
-                                 INT8_B32, INT4_MTP_B64, BF16_MTP_B64)}
+                                 INT8_B32, INT4_MTP_B64, BF16_MTP_B64, BF16_MTP_G5_B64)}
 
 
 def draw_lengths(w: Workload, rng: np.random.Generator) -> np.ndarray:

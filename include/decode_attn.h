@@ -96,7 +96,12 @@ extern "C" {
 /* limits of the built kernels */
 #define DA_MAX_SPLITS 256
 #define DA_MAX_Q_PER_REQ 16
-#define DA_MAX_ROWS 16 /* G * q_per_req query rows per kv-head */
+/* Query rows one stage-1 workgroup holds.  A kv-head serves R = G * q_per_req
+ * rows; with R > DA_MAX_ROWS they are processed in ceil(R / DA_MAX_ROWS)
+ * row blocks of ceil(R / blocks) rows, one workgroup each, and every block
+ * reads the kv-head's pages (the blocks of a kv-head run side by side on one
+ * XCD, so the later reads are mostly served by its L2). */
+#define DA_MAX_ROWS 16
 
 /*
  * Metadata prelude, one launch (SGLang PR #29843 digest, sections
@@ -185,8 +190,12 @@ int32_t decode_attn_metadata_ex(const int32_t* seq_lens, const int64_t* req_pool
  *
  *   head_dim in {64, 128}; page_size in {16, 32, 64, 128, 256};
  *   kv_layout DA_KV_NHD or DA_KV_HND (pool layout, see "Layouts");
- *   num_q_heads % num_kv_heads == 0; G * q_per_req <= DA_MAX_ROWS;
- *   1 <= num_splits <= DA_MAX_SPLITS; 1 <= q_per_req <= DA_MAX_Q_PER_REQ.
+ *   num_q_heads % num_kv_heads == 0 (any group G = Hq / Hkv; G * q_per_req
+ *   rows beyond DA_MAX_ROWS run in row blocks, see DA_MAX_ROWS);
+ *   1 <= num_splits <= DA_MAX_SPLITS; 1 <= q_per_req <= DA_MAX_Q_PER_REQ;
+ *   units * num_kv_heads * row blocks < 2^31 workgroups, units being
+ *   batch * num_splits, or work_capacity with a work list (else
+ *   DA_ERR_INVALID_ARG).
  *   page_table_stride >= max_pages >= 1.  cache_seqlens is the [batch] int32
  *   array from decode_attn_metadata (or any caller array of KV lengths).
  *   batch_order (nullable): a permutation of [0, batch) giving the order in

@@ -182,11 +182,19 @@ def oracle_sampled(batch: W.PagedBatch, pairs):
 FP16_U = 2.0 ** -11
 
 
+def rows_per_block(w: W.Workload) -> int:
+    """Query rows one stage-1 workgroup takes: the G*q rows of a kv-head, cut
+    into ceil(G*q / 16) blocks of equal size (the last may be shorter)."""
+    rows = w.group * w.q_per_req
+    nrb = -(-rows // 16)
+    return -(-rows // nrb)
+
+
 def uses_matrix_path(w: W.Workload) -> bool:
     """Whether stage 1 over this workload runs on the matrix cores (D = 128,
-    bf16 Q): INT4 with 9..16 query rows per kv-head, INT8 with up to 16,
-    a dense bf16 cache with 6..16."""
-    rows = w.group * w.q_per_req
+    bf16 Q): INT4 with 9..16 query rows per block, INT8 with up to 16,
+    a dense bf16 cache with 6..16 (rows per block: see rows_per_block)."""
+    rows = rows_per_block(w)
     if w.head_dim != 128 or w.dtype == "fp32":
         return False
     if w.kv == W.KV_INT4:

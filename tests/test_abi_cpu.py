@@ -69,7 +69,9 @@ def _split_args(**kw):
     (dict(q=None), 1), (dict(o=None), 1), (dict(batch=0), 1), (dict(Hq=30), 1),
     (dict(S=0), 1), (dict(S=257), 1), (dict(qn=17), 1), (dict(pt_stride=4), 1),
     (dict(num_pages=0), 1), (dict(D=96), 2), (dict(ps=48), 2), (dict(ps=8), 2),
-    (dict(dtype=7), 2), (dict(Hq=64, Hkv=2, qn=2), 2), (dict(layout=2), 1), (dict(layout=-1), 1),
+    (dict(dtype=7), 2), (dict(Hq=2 ** 21, Hkv=1), 1),
+    # 65535 * 256 units * 8 kv-heads * 32 row blocks: more workgroups than a 1-D grid holds
+    (dict(batch=65535, S=256, Hq=4096, Hkv=8), 1), (dict(layout=2), 1), (dict(layout=-1), 1),
     # work lists: counts required, 1 <= capacity <= batch * S
     (dict(work=FAKE, cap=8), 1), (dict(work=FAKE, counts=FAKE, cap=0), 1),
     (dict(work=FAKE, counts=FAKE, cap=17), 1),

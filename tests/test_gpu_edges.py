@@ -6,7 +6,9 @@ the fp64 oracle (gates in tests/_gpu_util.py):
   launch to the generic kernel;
 * page sizes 128 and 256;
 * 16 query rows per kv-head from 16 MTP tokens of one head (q_per_req = 16);
-* a batch much wider than one workgroup (300 requests), with both schedules.
+* a batch much wider than one workgroup (300 requests), with both schedules;
+* more than 16 query rows per kv-head (G * q_per_req up to 256), which runs
+  as row blocks of at most 16 rows on every kernel, with both schedules.
 """
 import numpy as np
 import pytest
@@ -109,3 +111,53 @@ def test_wide_batch_both_schedules(gpu, w):
     U.check_partials(og, lg, o_ref, l_ref, f"{w.name} per-request")
     assert torch.isfinite(out.float()).all()
     assert np.isfinite(lse_ref).sum() == np.isfinite(U.to_np(lse)).sum()
+
+
+# G * q_per_req > 16: ceil(R / 16) row blocks of ceil(R / blocks) rows each
+ROW_BLOCKS = [
+    # the headline heads with 4 MTP tokens: 20 rows = 2 x 10 (bf16 matrix cores)
+    W.RAGGED_B64.scaled(name="rows20_bf16_g5_mtp4", batch=3, q_per_req=4, causal=True,
+                        lengths="list", length_list=(4, 700, 1500), pin_max=False),
+    # 32 rows = 2 x 16 (bf16 matrix cores), with an empty request
+    W.BF16_B16.scaled(name="rows32_bf16_g8_mtp4", batch=3, num_q_heads=16, num_kv_heads=2,
+                      q_per_req=4, causal=True, lengths="list", length_list=(0, 130, 1100)),
+    # INT4 20 rows = 2 x 10, INT8 18 rows = 2 x 9 (matrix cores)
+    W.INT4_MTP_B64.scaled(name="rows20_int4_g5_mtp4", batch=3, num_q_heads=40, lengths="list",
+                          length_list=(5, 333, 1200)),
+    W.INT8_B32.scaled(name="rows18_int8_g6_mtp3", batch=2, num_q_heads=12, num_kv_heads=2,
+                      q_per_req=3, causal=True, lengths="list", length_list=(77, 900)),
+    # vector-ALU kernel: fp32 18 rows = 2 x 9; bf16 D = 64, 17 rows = 2 x 9
+    W.TINY_FP32.scaled(name="rows18_fp32_g6_mtp3", batch=2, num_q_heads=12, num_kv_heads=2,
+                       q_per_req=3, causal=True, lengths="list", length_list=(50, 600),
+                       pool_pages=0),
+    W.BF16_B16.scaled(name="rows17_bf16_d64_g17", batch=2, num_q_heads=17, num_kv_heads=1,
+                      head_dim=64, page_size=32, lengths="list", length_list=(3, 800)),
+    # one kv-head for 64 query heads: 64 rows = 4 x 16
+    W.BF16_B16.scaled(name="rows64_bf16_mqa", batch=2, num_q_heads=64, num_kv_heads=1,
+                      lengths="list", length_list=(1, 900)),
+    # 16 heads x 16 MTP tokens on one kv-head: 256 rows = 16 x 16
+    W.BF16_B16.scaled(name="rows256_bf16_g16_mtp16", batch=2, num_q_heads=16, num_kv_heads=1,
+                      q_per_req=16, causal=True, lengths="list", length_list=(16, 500)),
+]
+
+
+@pytest.mark.parametrize("w", both_layouts(ROW_BLOCKS), ids=lambda w: w.name)
+@pytest.mark.parametrize("S", [1, 3])
+def test_row_blocks(gpu, w, S):
+    _run_and_check(gpu, w, S, "row blocks")
+
+
+@pytest.mark.parametrize("w", [ROW_BLOCKS[0], ROW_BLOCKS[2]], ids=lambda w: w.name)
+def test_row_blocks_per_request_schedule(gpu, w):
+    log(f"row blocks, per-request schedule: {w.name}")
+    batch = W.make_batch(w, device="cuda")
+    md = U.schedule(gpu, batch, [1, 2, 4], 256, 4)
+    counts = md["split_counts"].cpu().numpy()
+    out, lse, o, l = U.run_decode(gpu, batch, 4, sched=md)
+    o_ref, l_ref = U.oracle_partials_per_request(batch, 4, counts)
+    og, lg = U.blank_unused_slots(U.to_np(o), U.to_np(l), counts)
+    U.check_partials(og, lg, o_ref, l_ref, f"{w.name} per-request",
+                     o_extra=U.matrix_path_o_bound(batch))
+    out_ref, lse_ref = U.oracle_full(batch)
+    _check_out(w, U.to_np(out), out_ref, f"{w.name} per-request out")
+    U.check_lse(U.to_np(lse), lse_ref, f"{w.name} per-request lse")
