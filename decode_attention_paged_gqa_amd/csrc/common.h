@@ -147,6 +147,8 @@ inline int32_t launch_status() {
 
 inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+inline bool aligned(const void* p, unsigned bytes) { return ((uintptr_t)p & (bytes - 1)) == 0; }
+
 // Rows between consecutive slots and between consecutive kv-heads of a
 // page, for the two pool layouts; a page is page_size * Hkv rows.  Row of
 // (page p, slot t, head g) = p * page_size * Hkv + t * slot + g * head.

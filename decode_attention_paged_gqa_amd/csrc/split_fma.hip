@@ -375,6 +375,10 @@ int32_t launch_kv(const da_host::SplitCall& c, const SplitArgs& a) {
 
 int32_t check_common(const da_host::SplitCall& c, int32_t kv_layout) {
   if (!c.q || !c.k || !c.v || !c.pt || !c.seqlens || !c.o || !c.lse) return DA_ERR_INVALID_ARG;
+  // 16-byte vector loads and stores (see "Alignment" in the header)
+  if (!da_host::aligned(c.q, 16) || !da_host::aligned(c.k, 16) || !da_host::aligned(c.v, 16) ||
+      !da_host::aligned(c.o, 16) || !da_host::aligned(c.ks, 4) || !da_host::aligned(c.vs, 4))
+    return DA_ERR_INVALID_ARG;
   if (c.batch <= 0 || c.batch > 65535 || c.qn <= 0 || c.qn > DA_MAX_Q_PER_REQ || c.Hq <= 0 ||
       c.Hkv <= 0 || c.Hq % c.Hkv != 0 || c.num_pages <= 0 || c.max_pages <= 0 ||
       c.pt_stride < c.max_pages || c.S <= 0 || c.S > DA_MAX_SPLITS || c.ps <= 0)

@@ -22,7 +22,10 @@
 // largest element lies in [2^14, 2^15) before the (then exact, for bf16)
 // conversion to fp16; the power of two and 2^24 are folded into the score
 // factor.  The per-group terms are combined in fp32 with the group's s and
-// z, which makes any fp16 zero point exact too.
+// z: the scale terms s_g * dot_g on the vector ALU (one mixed-precision fma
+// each), the zero-point terms -sum_g (s_g z_g) sum_g(q) as one fp32 matrix
+// product [16 tokens x 4 groups] . [4 groups x 16 rows] (s_g z_g is exact in
+// fp32), so any fp16 zero point is taken exactly.
 //   * QK: MFMA kb is group kb.  Lane (lm, lg) supplies token lm's dword lg
 //     of that group (elements 32*kb + 8*lg + 0..7); k-slots 2x, 2x+1 are
 //     elements x and x+4 of the dword (nibble x of its two halves).  Pairs
@@ -79,39 +82,44 @@ struct StageData {
   uint32_t v[4];   // dword lm of tokens 4*lg + j
   u32x4 ksz[4];    // (scale, zero) of token 4*lg + i, groups 0..3
   uint32_t vsz[4]; // (scale, zero) of token 4*lg + j, group lm/4
+  uint32_t kz;     // (scale, zero) of token lm, group lg
 };
 
-// All reads of one stage plus the next page id, in one asm block (the
-// compiler would otherwise drain the LDS-DMA queue before them).
+// All reads of ring stage ST (its byte offset, a constant folded into the
+// instructions' offset fields) plus the next page id, in one asm block (the
+// compiler would otherwise drain the LDS-DMA queue before them).  The
+// address operands are the lanes' fixed positions inside stage 0.
+template <int ST>
 __device__ __forceinline__ int32_t read_stage(const uint32_t (&kaddr)[4], uint32_t vaddr,
                                               uint32_t kszaddr, uint32_t vszaddr,
-                                              uint32_t pidaddr, StageData& s) {
+                                              uint32_t kzaddr, uint32_t pidaddr, StageData& s) {
   int32_t pid;
   asm volatile(
-      "ds_read_b32 %0, %17\n\t"
-      "ds_read_b32 %1, %18\n\t"
-      "ds_read_b32 %2, %19\n\t"
-      "ds_read_b32 %3, %20\n\t"
-      "ds_read_b32 %4, %21\n\t"
-      "ds_read_b32 %5, %21 offset:64\n\t"
-      "ds_read_b32 %6, %21 offset:128\n\t"
-      "ds_read_b32 %7, %21 offset:192\n\t"
-      "ds_read_b128 %8, %22\n\t"
-      "ds_read_b128 %9, %22 offset:16\n\t"
-      "ds_read_b128 %10, %22 offset:32\n\t"
-      "ds_read_b128 %11, %22 offset:48\n\t"
-      "ds_read_b32 %12, %23\n\t"
-      "ds_read_b32 %13, %23 offset:16\n\t"
-      "ds_read_b32 %14, %23 offset:32\n\t"
-      "ds_read_b32 %15, %23 offset:48\n\t"
-      "ds_read_b32 %16, %24\n\t"
+      "ds_read_b32 %0, %18 offset:%27\n\t"
+      "ds_read_b32 %1, %19 offset:%27\n\t"
+      "ds_read_b32 %2, %20 offset:%27\n\t"
+      "ds_read_b32 %3, %21 offset:%27\n\t"
+      "ds_read_b32 %4, %22 offset:%27\n\t"
+      "ds_read_b32 %5, %22 offset:%27+64\n\t"
+      "ds_read_b32 %6, %22 offset:%27+128\n\t"
+      "ds_read_b32 %7, %22 offset:%27+192\n\t"
+      "ds_read_b128 %8, %23 offset:%27\n\t"
+      "ds_read_b128 %9, %23 offset:%27+16\n\t"
+      "ds_read_b128 %10, %23 offset:%27+32\n\t"
+      "ds_read_b128 %11, %23 offset:%27+48\n\t"
+      "ds_read_b32 %12, %24 offset:%27\n\t"
+      "ds_read_b32 %13, %24 offset:%27+16\n\t"
+      "ds_read_b32 %14, %24 offset:%27+32\n\t"
+      "ds_read_b32 %15, %24 offset:%27+48\n\t"
+      "ds_read_b32 %16, %25 offset:%27\n\t"
+      "ds_read_b32 %17, %26\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(s.k[0]), "=&v"(s.k[1]), "=&v"(s.k[2]), "=&v"(s.k[3]), "=&v"(s.v[0]),
         "=&v"(s.v[1]), "=&v"(s.v[2]), "=&v"(s.v[3]), "=&v"(s.ksz[0]), "=&v"(s.ksz[1]),
         "=&v"(s.ksz[2]), "=&v"(s.ksz[3]), "=&v"(s.vsz[0]), "=&v"(s.vsz[1]), "=&v"(s.vsz[2]),
-        "=&v"(s.vsz[3]), "=&v"(pid)
+        "=&v"(s.vsz[3]), "=&v"(s.kz), "=&v"(pid)
       : "v"(kaddr[0]), "v"(kaddr[1]), "v"(kaddr[2]), "v"(kaddr[3]), "v"(vaddr), "v"(kszaddr),
-        "v"(vszaddr), "v"(pidaddr)
+        "v"(vszaddr), "v"(kzaddr), "v"(pidaddr), "i"(ST)
       : "memory");
   return __builtin_amdgcn_readfirstlane(pid);
 }
@@ -168,6 +176,7 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
   uint32_t qv[4][4];  // [kb][register]
   float qsum[4];      // 2^-24 * sum of the row's scaled fp16 Q over group kb
   float rowfac;       // score (log2 units) = rowfac * sum_g s_g (dot_g - z_g qsum_g)
+  float qsum_lg;      // qsum[lg]: operand of the zero-point product (group lg, row lm)
   int tlim;           // tokens t < tlim are visible to this lane's row
   {
     const bool live = lm < nr;
@@ -213,6 +222,9 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
       qsum[kb] = ldexpf(part, -24);
     }
     rowfac = ldexpf(a.scale_log2, 24 - sh);
+    qsum_lg = qsum[0];
+#pragma unroll
+    for (int kb = 1; kb < 4; ++kb) qsum_lg = lg == kb ? qsum[kb] : qsum_lg;
     tlim = live ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
   }
   // tiles below every live row's limit need no masks (rows past R have
@@ -249,6 +261,7 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
   for (int kb = 0; kb < 4; ++kb) rd_k[kb] = kStageK + 64 * lm + 16 * ((kb + (lm >> 2)) & 3) + 4 * lg;
   const uint32_t rd_v = kStageV + 64 * (4 * lg) + 16 * (((lm >> 2) + lg) & 3) + 4 * (lm & 3);
   const uint32_t rd_ksz = kStageKsz + 64 * lg;
+  const uint32_t rd_kz = kStageKsz + 16 * lm + 4 * lg;
   const uint32_t rd_vsz = kStageVsz + 16 * (4 * lg) + 4 * (lm >> 2);
 
   auto tile_base = [&](int j) { return t0 + ((wave + kWaves * j) << 4); };
@@ -270,6 +283,11 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
 
   auto compute = [&](int j, const StageData& sd, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    // ---- zero-point terms: zt[i] = -sum_g s_g z_g qsum_g for token 4*lg + i,
+    // row lm (A: -s z of token lm, group lg; B: qsum of group lg, row lm)
+    const float nsz = -(h_lo(sd.kz) * h_hi(sd.kz));
+    const float4_t zt =
+        __builtin_amdgcn_mfma_f32_16x16x4f32(nsz, qsum_lg, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     // ---- per-group dot products of the raw codes: dot[kb][i] =
     // 2^-24 * sum_{d in group kb} q'_d n_d for token 4*lg + i, row lm
     float4_t dot[4];
@@ -290,10 +308,9 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t sz[4] = {sd.ksz[i][0], sd.ksz[i][1], sd.ksz[i][2], sd.ksz[i][3]};
-      float acc_s = 0.f;
+      float acc_s = zt[i];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        acc_s = fmaf(h_lo(sz[kb]), fmaf(-h_hi(sz[kb]), qsum[kb], dot[kb][i]), acc_s);
+      for (int kb = 0; kb < 4; ++kb) acc_s = fmaf(h_lo(sz[kb]), dot[kb][i], acc_s);
       st[i] = acc_s;
     }
     // st[i] = score of token 4*lg + i for row lm
@@ -372,15 +389,21 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
     }
   };
 
-  auto step = [&](int j, StageData& sd) {
+  // the lanes' read positions inside stage 0; stage j % kStages adds a constant
+  const uint32_t ka[4] = {ring_lds + rd_k[0], ring_lds + rd_k[1], ring_lds + rd_k[2],
+                          ring_lds + rd_k[3]};
+  const uint32_t va = ring_lds + rd_v, ksza = ring_lds + rd_ksz, vsza = ring_lds + rd_vsz,
+                 kza = ring_lds + rd_kz;
+  // wait for tile j, read it (stage offset ST + off bytes), refill its stage
+  auto step = [&](int j, StageData& sd, uint32_t off, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
     const int ahead = min(kStages - 2, nmine - 1 - j);
     if (ahead >= 2) wait_vmcnt<8>();
     else if (ahead == 1) wait_vmcnt<4>();
     else wait_vmcnt<0>();
     const int jn = min(j + kStages - 1, nmine - 1);
-    const uint32_t base = ring_lds + (j % kStages) * kStageBytes;
-    const uint32_t ka[4] = {base + rd_k[0], base + rd_k[1], base + rd_k[2], base + rd_k[3]};
-    const int pid = read_stage(ka, base + rd_v, base + rd_ksz, base + rd_vsz, pid_addr(jn), sd);
+    const uint32_t k4[4] = {ka[0] + off, ka[1] + off, ka[2] + off, ka[3] + off};
+    const int pid = read_stage<ST>(k4, va + off, ksza + off, vsza + off, kza + off, pid_addr(jn), sd);
     if (j + kStages - 1 < nmine) issue(j + kStages - 1, pid);
   };
   const int lim = tfull - t0 - 16 * wave - 16;
@@ -388,14 +411,28 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
 #pragma unroll
   for (int u = 0; u < kStages - 1; ++u)
     if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
-  for (int j = 0; j < jfull; ++j) {
-    StageData sd;
-    step(j, sd);
-    compute(j, sd, std::false_type{});
+  // unmasked tiles, kStages per trip so that each one's stage is a constant
+  static_assert(kStages == 4, "one unrolled trip per ring cycle");
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, kStageBytes>;
+  using C2 = std::integral_constant<int, 2 * kStageBytes>;
+  using C3 = std::integral_constant<int, 3 * kStageBytes>;
+  int j = 0;
+  for (; j + kStages <= jfull; j += kStages) {
+    StageData sd0, sd1, sd2, sd3;
+    step(j, sd0, 0u, C0{});
+    compute(j, sd0, std::false_type{});
+    step(j + 1, sd1, 0u, C1{});
+    compute(j + 1, sd1, std::false_type{});
+    step(j + 2, sd2, 0u, C2{});
+    compute(j + 2, sd2, std::false_type{});
+    step(j + 3, sd3, 0u, C3{});
+    compute(j + 3, sd3, std::false_type{});
   }
-  for (int j = jfull; j < nmine; ++j) {
+  // the rest (fewer than kStages unmasked tiles, then the masked ones)
+  for (; j < nmine; ++j) {
     StageData sd;
-    step(j, sd);
+    step(j, sd, (uint32_t)((j % kStages) * kStageBytes), C0{});
     compute(j, sd, std::true_type{});
   }
 
@@ -415,26 +452,8 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
     sm_l[wave * 16 + lm] = l;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < nr * kD; idx += kThreads) {
-    const int r = idx / kD, d = idx - r * kD;
-    float M = da::kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + r]);
-    float lsum = 0.f, o = 0.f;
-    if (M != da::kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = da::fast_exp2(sm_m[w * 16 + r] - M);
-        lsum = fmaf(sm_l[w * 16 + r], f, lsum);
-        o = fmaf(sm_acc[(w * 16 + r) * kD + d], f, o);
-      }
-    }
-    const int i = (r0 + r) / a.G, h = g * a.G + ((r0 + r) % a.G);
-    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.sched.S + s;
-    a.o[orow * kD + d] = lsum > 0.f ? o / lsum : 0.f;
-    if (d == 0)
-      a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum) - kPScale) * da::kLn2 : da::kNegInf;
-  }
+  write_partials<kWaves>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S, s,
+                         kPScale, a.o, a.lse);
 }
 
 }  // namespace

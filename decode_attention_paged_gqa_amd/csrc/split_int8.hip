@@ -408,26 +408,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     sm_l[wave * 16 + lm] = l;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < nr * kD; idx += kThreads) {
-    const int r = idx / kD, d = idx - r * kD;
-    float M = da::kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + r]);
-    float lsum = 0.f, o = 0.f;
-    if (M != da::kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = da::fast_exp2(sm_m[w * 16 + r] - M);
-        lsum = fmaf(sm_l[w * 16 + r], f, lsum);
-        o = fmaf(sm_acc[(w * 16 + r) * kD + d], f, o);
-      }
-    }
-    const int i = (r0 + r) / a.G, h = g * a.G + ((r0 + r) % a.G);
-    const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.sched.S + s;
-    a.o[orow * kD + d] = lsum > 0.f ? o / lsum : 0.f;
-    if (d == 0)
-      a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum) - kPScale) * da::kLn2 : da::kNegInf;
-  }
+  write_partials<kWaves>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S, s,
+                         kPScale, a.o, a.lse);
 }
 
 }  // namespace

@@ -36,6 +36,11 @@
  *     sizes the arguments give: out-of-range page ids read page 0, lengths
  *     are clamped to [0, max_pages * page_size], negative ids act as 0.
  *     Results for such rows are unspecified.
+ *   - Alignment (checked, DA_ERR_INVALID_ARG): the stage-1 calls need q,
+ *     the K/V pools and o_partial 16-byte aligned, the scale arrays 4-byte
+ *     aligned (16-byte vector accesses).  Allocations from hipMalloc or a
+ *     framework allocator are 256-byte aligned; a view into one keeps the
+ *     alignment when its offset is a multiple of 16 bytes.
  *
  * Layouts (row-major, contiguous):
  *   q            [B, q_per_req, Hq, D]

@@ -70,6 +70,9 @@ def _split_args(**kw):
     (dict(S=0), 1), (dict(S=257), 1), (dict(qn=17), 1), (dict(pt_stride=4), 1),
     (dict(num_pages=0), 1), (dict(D=96), 2), (dict(ps=48), 2), (dict(ps=8), 2),
     (dict(dtype=7), 2), (dict(Hq=2 ** 21, Hkv=1), 1),
+    # 16-byte vector accesses: q, pools and o_partial must be 16-byte aligned
+    (dict(q=ctypes.c_void_p(0x1008)), 1), (dict(k=ctypes.c_void_p(0x1004)), 1),
+    (dict(o=ctypes.c_void_p(0x1008)), 1),
     # 65535 * 256 units * 8 kv-heads * 32 row blocks: more workgroups than a 1-D grid holds
     (dict(batch=65535, S=256, Hq=4096, Hkv=8), 1), (dict(layout=2), 1), (dict(layout=-1), 1),
     # work lists: counts required, 1 <= capacity <= batch * S
