@@ -17,6 +17,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
+# the same library with the device-data contract checks (decode_attn_checks)
+CHECKED_LIB_PATH = os.path.join(_HERE, "libdecode_attn_checked.so")
 
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_LAUNCH = 0, 1, 2, 3
 DA_FP32, DA_BF16 = 0, 1
@@ -26,6 +28,9 @@ CACHE_FORMATS = {"dense": DA_CACHE_DENSE, "int8": DA_CACHE_INT8, "int4": DA_CACH
 KV_LAYOUTS = {"NHD": DA_KV_NHD, "HND": DA_KV_HND}
 DA_Q_STRIDED, DA_Q_CUMSUM, DA_Q_PRESET = 0, 1, 2
 DA_MAX_SPLITS = 256
+# decode_attn_checks flag bits
+DA_CHECK_PAGE_ID, DA_CHECK_SEQLEN, DA_CHECK_ORDER, DA_CHECK_WORK = 0x01, 0x02, 0x04, 0x08
+DA_CHECK_COUNTS, DA_CHECK_REQ_ROW, DA_CHECK_TOO_LONG = 0x10, 0x20, 0x40
 
 _lib = None
 
@@ -54,6 +59,7 @@ _SIGS = {
     "decode_attn_pick_splits": [_P, _P, _I32, _I32, _I32, _I32, _I32],
     "decode_attn_gather_kv": [_P, _I64, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _I32,
                               _P, _P],
+    "decode_attn_checks": [_P, _P, _I32],
     "decode_attn_strerror": [_I32],
     "decode_attn_version": [],
 }
@@ -65,10 +71,11 @@ class DecodeAttnError(ValueError):
     """A C entry point returned a non-zero status."""
 
 
-def load(path: Optional[str] = None):
-    """Load the HIP library (once).  Raises if it has not been built."""
+def load(path: Optional[str] = None, reload: bool = False):
+    """Load the HIP library (once; ``reload`` switches to ``path``, e.g.
+    CHECKED_LIB_PATH).  Raises if it has not been built."""
     global _lib
-    if _lib is not None:
+    if _lib is not None and not reload:
         return _lib
     path = path or LIB_PATH
     if not os.path.exists(path):
@@ -476,3 +483,14 @@ def decode_attn_gather_kv(pool, page_table, cache_seqlens, cu_seqlens_k, total_t
 
 def decode_attn_version() -> int:
     return int(load().decode_attn_version())
+
+
+def decode_attn_checks(reset: bool = False):
+    """(flags, count) of the checked library's contract-check words (see
+    DA_CHECK_*); synchronises the device.  Raises DecodeAttnError with the
+    normal library, which has no checks."""
+    lib = load()
+    flags, count = ctypes.c_uint32(0), ctypes.c_uint64(0)
+    st = lib.decode_attn_checks(ctypes.byref(flags), ctypes.byref(count), 1 if reset else 0)
+    _check(st, "decode_attn_checks")
+    return int(flags.value), int(count.value)

@@ -1,9 +1,12 @@
 """Build libdecode_attn.so in-tree with hipcc for gfx950.
 
-    python -m decode_attention_paged_gqa_amd.build
+    python -m decode_attention_paged_gqa_amd.build [--checked]
 
 Every source under csrc/ is compiled to an object in parallel, then linked
-into ``decode_attention_paged_gqa_amd/libdecode_attn.so``.  Always rebuilds.
+into ``decode_attention_paged_gqa_amd/libdecode_attn.so``.  With --checked
+the same sources are built with -DDA_CHECKED into libdecode_attn_checked.so,
+whose kernels also record violations of the device-data contract
+(decode_attn_checks).  Always rebuilds.
 """
 from __future__ import annotations
 
@@ -19,6 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdecode_attn.so")
+CHECKED_LIB = os.path.join(PKG, "libdecode_attn_checked.so")
 ARCH = "gfx950"
 
 
@@ -43,8 +47,8 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra, build_dir: str) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [hipcc()] + COMMON_FLAGS + list(extra) + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
@@ -54,22 +58,26 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), verbose=True, jobs=None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(extra_flags=(), verbose=True, jobs=None, checked=False) -> str:
+    lib = CHECKED_LIB if checked else LIB
+    build_dir = BUILD + ("_checked" if checked else "")
+    extra = list(extra_flags) + (["-DDA_CHECKED"] if checked else [])
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra_flags), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), srcs))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", flush=True)
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources", flush=True)
+    return lib
 
 
 if __name__ == "__main__":
-    build(sys.argv[1:])
+    args = sys.argv[1:]
+    build([a for a in args if a != "--checked"], checked="--checked" in args)

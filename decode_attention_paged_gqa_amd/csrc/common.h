@@ -45,6 +45,24 @@ __device__ __forceinline__ float xor_shfl(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- contract checks
+// Device data the host cannot see without a sync (page ids, lengths, batch
+// order, work lists, split counts, request rows) is the caller's contract;
+// kernels clamp it to in-bounds values.  A checked build (-DDA_CHECKED) also
+// records every violation in the library's check words chk = [flag bits
+// (DA_CHECK_*), count], read back by decode_attn_checks; an unchecked build
+// compiles the checks away.  Either way the results are the same.
+__device__ __forceinline__ void note(unsigned long long* chk, bool ok, unsigned bit) {
+#ifdef DA_CHECKED
+  if (!ok && chk) {
+    atomicOr(chk, (unsigned long long)bit);
+    atomicAdd(chk + 1, 1ull);
+  }
+#else
+  (void)chk; (void)ok; (void)bit;
+#endif
+}
+
 // ---------------------------------------------------------------- stage-1 work units
 // Stage 1 runs one workgroup per (kv-head g, work unit u) on a 1-D grid.  A
 // unit is one (request, split).  Without a work list, unit u = z * S + s is
@@ -81,6 +99,7 @@ constexpr int kXcds = 8;
 constexpr int kItemShift = 8;  // work item = b << 8 | s
 
 struct Stage1Sched {
+  unsigned long long* checks;  // contract-check words (checked builds; else null)
   const int32_t* order;   // nullable: batch order (no work list)
   const int32_t* work;    // nullable: work list of `units` entries
   const int32_t* counts;  // per-request split counts (with a work list)
@@ -118,10 +137,12 @@ __device__ __forceinline__ bool stage1_item(const Stage1Sched& sc, int Hkv, Stag
   it.r0 = (gv - it.g * sc.nrb) * sc.rb_rows;
   it.nr = min(sc.rb_rows, sc.rows - it.r0);  // >= 1 for every R <= 2^24 (entry check)
   if (it.nr <= 0) return false;
+  const bool first = threadIdx.x == 0;  // one note per workgroup
   if (!sc.work) {
     const int z = u / sc.S;
     it.s = u - z * sc.S;
     const int b = sc.order ? sc.order[z] : z;
+    note(sc.checks, !first || (unsigned)b < (unsigned)sc.B, DA_CHECK_ORDER);
     it.b = (unsigned)b < (unsigned)sc.B ? b : z;
     it.S = sc.S;
     return true;
@@ -130,8 +151,14 @@ __device__ __forceinline__ bool stage1_item(const Stage1Sched& sc, int Hkv, Stag
   if (item < 0) return false;
   it.b = item >> kItemShift;
   it.s = item & ((1 << kItemShift) - 1);
-  if (it.b >= sc.B) return false;
-  it.S = min(max(sc.counts[it.b], 1), sc.S);
+  if (it.b >= sc.B) {
+    note(sc.checks, !first, DA_CHECK_WORK);
+    return false;
+  }
+  const int cnt = sc.counts[it.b];
+  note(sc.checks, !first || (cnt >= 1 && cnt <= sc.S), DA_CHECK_COUNTS);
+  it.S = min(max(cnt, 1), sc.S);
+  note(sc.checks, !first || it.s < it.S, DA_CHECK_WORK);
   return it.s < it.S;
 }
 
@@ -148,6 +175,9 @@ inline int32_t launch_status() {
 inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 inline bool aligned(const void* p, unsigned bytes) { return ((uintptr_t)p & (bytes - 1)) == 0; }
+
+// The current device's contract-check words (checked builds; null otherwise).
+unsigned long long* check_words();
 
 // Rows between consecutive slots and between consecutive kv-heads of a
 // page, for the two pool layouts; a page is page_size * Hkv rows.  Row of
@@ -186,6 +216,7 @@ struct SplitCall {
   const int32_t* work;    // nullable: work list (then counts is required)
   const int32_t* counts;
   int units;              // grid units: S * batch, or the work list's capacity
+  unsigned long long* checks;  // contract-check words (checked builds; else null)
   int batch, qn, Hq, Hkv, D, ps, num_pages, S;
   int rows, nrb, rb_rows;  // query rows per kv-head, row blocks, rows per block
   KvStrides kv;
@@ -197,6 +228,7 @@ struct SplitCall {
 
   da::Stage1Sched sched() const {
     da::Stage1Sched sc;
+    sc.checks = checks;
     sc.order = order; sc.work = work; sc.counts = counts;
     sc.S = S; sc.B = batch; sc.units = units;
     sc.rows = rows; sc.nrb = nrb; sc.rb_rows = rb_rows;

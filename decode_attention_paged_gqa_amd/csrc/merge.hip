@@ -23,14 +23,19 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restr
                                                            int rows, int S,
                                                            const int32_t* __restrict__ counts,
                                                            int rows_per_req, void* __restrict__ out,
-                                                           float* __restrict__ lse_out) {
+                                                           float* __restrict__ lse_out,
+                                                           unsigned long long* checks) {
   constexpr int E = D / 64;  // elements per lane
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
   const float* l = lp + (long long)row * S;
   const float* o = op + (long long)row * S * D + lane * E;
-  if (counts) S = min(max(counts[row / rows_per_req], 1), S);
+  if (counts) {
+    const int cnt = counts[row / rows_per_req];
+    da::note(checks, lane != 0 || (cnt >= 1 && cnt <= S), DA_CHECK_COUNTS);
+    S = min(max(cnt, 1), S);
+  }
   // the first kPrefetch split rows are loaded while the max is being found
   float pre[kPrefetch][E];
 #pragma unroll
@@ -84,7 +89,7 @@ int32_t launch(const float* op, const float* lp, int rows, int S, const int32_t*
                int rows_per_req, void* out, float* lse_out, hipStream_t st) {
   const int blocks = (rows + kWaves - 1) / kWaves;
   hipLaunchKernelGGL((merge_kernel<D, B16>), dim3(blocks), dim3(64 * kWaves), 0, st, op, lp, rows,
-                     S, counts, rows_per_req, out, lse_out);
+                     S, counts, rows_per_req, out, lse_out, da_host::check_words());
   return da_host::launch_status();
 }
 

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void metadata_kernel(
     int32_t* __restrict__ cu_k, int32_t* __restrict__ cu_q, int32_t* __restrict__ page_table,
     int32_t* __restrict__ order, const int64_t* __restrict__ f2s, long long f2s_len,
     int32_t* __restrict__ swa_pt, const SplitTable table, int32_t* __restrict__ counts,
-    int32_t* __restrict__ work, int capacity) {
+    int32_t* __restrict__ work, int capacity, unsigned long long* checks) {
   __shared__ long long sh[4];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -90,6 +90,10 @@ __global__ __launch_bounds__(kThreads) void metadata_kernel(
   {
     const long long n = ((long long)L + page_size - 1) / page_size;
     const bool row_ok = r >= 0 && r < r2t_rows;
+    // a negative row is the sentinel (a request with no slots), a row past
+    // the table is a contract violation; so is a length the table cannot hold
+    da::note(checks, tid != 0 || r < r2t_rows, DA_CHECK_REQ_ROW);
+    da::note(checks, tid != 0 || (n <= max_pages && L <= r2t_cols), DA_CHECK_TOO_LONG);
     const int32_t* row = r2t + (row_ok ? r : 0) * r2t_stride;
     int32_t* out = page_table + (long long)b * max_pages;
     int32_t* swa_out = swa_pt ? swa_pt + (long long)b * max_pages : nullptr;
@@ -195,7 +199,7 @@ extern "C" int32_t decode_attn_metadata_ex(
                      page_size, max_pages, q_mode, q_in, q_stride, cache_seqlens, cu_seqlens_k,
                      cu_seqlens_q, page_table, batch_order, full_to_swa,
                      (long long)full_to_swa_len, swa_page_table, table, split_counts, work_list,
-                     sched ? work_capacity : 0);
+                     sched ? work_capacity : 0, da_host::check_words());
   return da_host::launch_status();
 }
 

@@ -150,6 +150,8 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
 
   const int ps = a.page_size;
   const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
+  da::note(a.sched.checks, threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
+           DA_CHECK_SEQLEN);
   const int n = (L + ps - 1) >> a.log2_ps;
   const int cpg = (n + it.S - 1) / it.S;
   const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
@@ -199,6 +201,7 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
   for (int tile = wave; tile < ntiles; tile += kWaves) {
     const int tb = t0 + (tile << 4);
     int pid = a.pt[(long long)b * a.pt_stride + (tb >> a.log2_ps)];
+    da::note(a.sched.checks, lane != 0 || (unsigned)pid < (unsigned)a.num_pages, DA_CHECK_PAGE_ID);
     if ((unsigned)pid >= (unsigned)a.num_pages) pid = 0;
     const int slot0 = tb & (ps - 1);
 
@@ -410,6 +413,7 @@ da_host::SplitCall make_call(const void* q, int q_bf16, const void* k, const voi
   c.pt = pt; c.pt_stride = pt_stride; c.max_pages = max_pages;
   c.seqlens = seqlens; c.order = order;
   c.work = work; c.counts = counts;
+  c.checks = da_host::check_words();
   c.units = work ? work_capacity : (int)((long long)S * batch);
   c.batch = batch; c.qn = qn; c.Hq = Hq; c.Hkv = Hkv; c.D = D; c.ps = ps;
   c.num_pages = num_pages; c.S = S;

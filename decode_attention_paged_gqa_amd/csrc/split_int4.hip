@@ -156,6 +156,8 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
 
   const int ps = a.page_size;
   const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
+  da::note(a.sched.checks, threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
+           DA_CHECK_SEQLEN);
   const int n = (L + ps - 1) >> a.log2_ps;
   const int cpg = (n + it.S - 1) / it.S;
   const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
@@ -167,6 +169,7 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
     const int32_t* ptrow = a.pt + (long long)b * a.pt_stride;
     for (int j = threadIdx.x; j < p1 - p0; j += kThreads) {
       const int pid = ptrow[p0 + j];
+      da::note(a.sched.checks, (unsigned)pid < (unsigned)a.num_pages, DA_CHECK_PAGE_ID);
       s_pid[j] = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
     }
   }

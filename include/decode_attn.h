@@ -98,6 +98,16 @@ extern "C" {
 #define DA_Q_CUMSUM 1  /* cu_q = exclusive prefix of max(q_in[b], 0), q_in [B]     */
 #define DA_Q_PRESET 2  /* cu_q = copy of q_in [B+1]                                */
 
+/* contract checks of the checked build (bits of decode_attn_checks' flags) */
+#define DA_CHECK_PAGE_ID 0x01u  /* a page id read by stage 1 outside [0, num_pages)        */
+#define DA_CHECK_SEQLEN 0x02u   /* cache_seqlens outside [0, max_pages * page_size] (stage 1) */
+#define DA_CHECK_ORDER 0x04u    /* a batch_order entry outside [0, batch)                    */
+#define DA_CHECK_WORK 0x08u     /* a work-list entry neither -1 nor a valid (request, split)  */
+#define DA_CHECK_COUNTS 0x10u   /* a split_counts entry outside [1, num_splits]               */
+#define DA_CHECK_REQ_ROW 0x20u  /* metadata: req_pool_indices[b] >= req_to_token_rows        */
+#define DA_CHECK_TOO_LONG 0x40u /* metadata: seq_lens[b] needs more than max_pages pages or
+                                   exceeds req_to_token_cols                                 */
+
 /* limits of the built kernels */
 #define DA_MAX_SPLITS 256
 #define DA_MAX_Q_PER_REQ 16
@@ -346,6 +356,24 @@ int32_t decode_attn_gather_kv(const void* pool, int64_t row_bytes, int32_t num_k
                               int32_t max_pages, const int32_t* cache_seqlens,
                               const int32_t* cu_seqlens_k, int32_t batch, void* out,
                               void* stream);
+
+/*
+ * Contract checks (the conventions above leave device data unchecked in the
+ * normal library).  A build compiled with -DDA_CHECKED
+ * (libdecode_attn_checked.so, `python -m decode_attention_paged_gqa_amd.build
+ * --checked`) makes the kernels record every violation of the device-data
+ * contract they meet -- the DA_CHECK_* conditions -- in check words the
+ * library keeps per device, while still clamping the data exactly as the
+ * normal build does (identical results).  Each workgroup that meets a bad
+ * value counts it, so `count` is a number of observations, not of bad
+ * entries.
+ *   flags, count  HOST out (nullable): OR of DA_CHECK_* bits, observations
+ *   reset         != 0: clear the words after reading
+ * Synchronises the current device (hipDeviceSynchronize) before reading.
+ * Returns DA_ERR_UNSUPPORTED in the normal build, DA_ERR_LAUNCH when a HIP
+ * call fails.
+ */
+int32_t decode_attn_checks(uint32_t* flags, uint64_t* count, int32_t reset);
 
 /* Human-readable text for a status code (static storage). */
 const char* decode_attn_strerror(int32_t status);

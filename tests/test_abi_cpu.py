@@ -35,13 +35,31 @@ def test_header_declares_the_binding_exports():
     assert _declared() == sorted(B.EXPORTS)
 
 
-def test_library_exports_every_declared_symbol(lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+@pytest.mark.parametrize("path", [B.LIB_PATH, B.CHECKED_LIB_PATH], ids=["plain", "checked"])
+def test_library_exports_every_declared_symbol(lib, path):
+    if not os.path.exists(path):
+        pytest.fail(f"{path} not built (run __graft_entry__.build())")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(decode_attn_\w+)", out))
     for name in _declared():
         assert name in exported, name
         assert getattr(lib, name) is not None
+
+
+def test_checks_need_the_checked_build(lib):
+    # the plain library has no contract checks: the query says so without touching a device
+    flags, count = ctypes.c_uint32(7), ctypes.c_uint64(7)
+    assert lib.decode_attn_checks(ctypes.byref(flags), ctypes.byref(count), 0) == 2
+    assert (flags.value, count.value) == (7, 7)
+    with pytest.raises(da.DecodeAttnError):
+        da.decode_attn_checks()
+
+
+def test_checked_build_flag_bits_match_the_header():
+    src = open(HEADER).read()
+    bits = {m[0]: int(m[1], 16) for m in re.findall(r"#define (DA_CHECK_\w+) (0x[0-9a-f]+)u", src)}
+    assert bits == {k: getattr(B, k) for k in bits} and len(bits) == 7
 
 
 def test_strerror_and_version(lib):
