@@ -257,9 +257,10 @@ inline unsigned SplitCall::grid(bool grouped) const {
   return (unsigned)stage1_grid((long long)Hkv * nrb, units, grouped || nrb > 1);
 }
 
-// Row blocks of R query rows per kv-head (see da::stage1_item).
-inline void row_blocks(int R, int& nrb, int& rb_rows) {
-  nrb = (R + DA_MAX_ROWS - 1) / DA_MAX_ROWS;
+// Row blocks of R query rows per kv-head, at most max_rows each (see
+// da::stage1_item): ceil(R / max_rows) blocks of equal size but the last.
+inline void row_blocks(int R, int max_rows, int& nrb, int& rb_rows) {
+  nrb = (R + max_rows - 1) / max_rows;
   rb_rows = (R + nrb - 1) / nrb;
 }
 

@@ -56,10 +56,7 @@ constexpr int kD = 128;
 constexpr int kStageK = 0;
 constexpr int kStageV = 4096;
 constexpr int kStageBytes = 8192;
-constexpr int kRingBytes = kWaves * kStages * kStageBytes;           // 64 KB
-constexpr int kEpiBytes = (kWaves * 16 * kD + 2 * kWaves * 16) * 4;  // 33 KB
-constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
-constexpr int kSmemBytes = kMainBytes + kMaxSplitPages * 4;
+constexpr int kRingBytes = kWaves * kStages * kStageBytes;  // 64 KB
 
 // LDS position of 16-byte chunk c of tile row t
 __host__ __device__ constexpr int chunk_pos(int t, int c) { return (c + t) & 15; }
@@ -116,8 +113,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)da::float_to_bf16_rne(lo) | ((uint32_t)da::float_to_bf16_rne(hi) << 16);
 }
 
+// NT row tiles of 16 query rows (NT * 16 rows per workgroup): the K/V
+// operands of a tile are read once and serve every row tile.
+template <int NT>
 __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16MfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  constexpr int ROWS = 16 * NT;
+  constexpr int kEpiBytes = (kWaves * ROWS * kD + 2 * kWaves * ROWS) * 4;
+  constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kMainBytes + kMaxSplitPages * 4];
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
 
   da::Stage1Item it;
@@ -147,38 +150,48 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
     }
   }
 
-  // ---- Q^T operand: row lm, elements 32*kb + 8*lg + e (rows past R: zero)
-  u32x4 qv[4];
-  int tlim;  // tokens t < tlim are visible to this lane's row
-  {
-    const bool live = lm < nr;
-    const int r = r0 + (live ? lm : 0);  // this lane's query row of the kv-head
+  // ---- Q^T operands: row tile rt, row lm, elements 32*kb + 8*lg + e (rows
+  // past the block: zero)
+  u32x4 qv[NT][4];
+  int tlim[NT];  // tokens t < tlim are visible to this lane's row of tile rt
+  int lim_live = t1;
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    const bool live = 16 * rt + lm < nr;
+    const int r = r0 + (live ? 16 * rt + lm : 0);  // this lane's query row of the kv-head
     const int i = r / a.G, h = g * a.G + r % a.G;
     const uint4* qp =
         reinterpret_cast<const uint4*>(a.q + (((long long)b * a.qn + i) * a.Hq + h) * kD + 8 * lg);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const uint4 x = qp[4 * kb];
-      qv[kb] = live ? u32x4{x.x, x.y, x.z, x.w} : u32x4{0u, 0u, 0u, 0u};
+      qv[rt][kb] = live ? u32x4{x.x, x.y, x.z, x.w} : u32x4{0u, 0u, 0u, 0u};
     }
-    tlim = live ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
+    tlim[rt] = live ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
+    if (live) lim_live = min(lim_live, tlim[rt]);
   }
   // the query loads are waited for here, not inside the pipeline
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) asm volatile("" : "+v"(qv[kb]));
-  // tiles below every live row's limit need no masks (rows past R have
-  // tlim 0 and are never written, so they do not bound the unmasked region)
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) asm volatile("" : "+v"(qv[rt][kb]));
+  // tiles below every live row's limit need no masks (rows past the block
+  // have tlim 0 and are never written, so they do not bound the unmasked region)
   int tfull;
   {
-    int lim_live = lm < nr ? tlim : t1;
     for (int o = 1; o < 16; o <<= 1) lim_live = min(lim_live, __shfl_xor(lim_live, o, 64));
     tfull = __builtin_amdgcn_readfirstlane(lim_live);
   }
 
-  float4_t acc[8];
+  float4_t acc[NT][8];
+  float m[NT], l[NT];
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb) acc[bb] = {0.f, 0.f, 0.f, 0.f};
-  float m = da::kNegInf, l = 0.f;
+  for (int rt = 0; rt < NT; ++rt) {
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
+    m[rt] = da::kNegInf;
+    l[rt] = 0.f;
+  }
   __syncthreads();  // s_pid visible
 
   // ---- addressing
@@ -221,53 +234,57 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
 
   auto compute = [&](int j, const StageData& sd, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    // ---- S^T: dot[i] = q . k for token 4*lg + i, row lm
-    float4_t dot = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      dot = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, sd.k[kb]),
-                                                    __builtin_bit_cast(bf16x8_t, qv[kb]), dot, 0,
-                                                    0, 0);
     const int tb = tile_base(j) + 4 * lg;
-    float z[4];
-    bool need = false;
+    s16x4_t phi[NT], plo[NT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = fmaf(dot[i], a.scale_log2, -m);
-      if (MASKED && !(tb + i < tlim)) z[i] = da::kNegInf;
-      need |= z[i] > kRescaleSlack;
-    }
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      // raise each row's reference to its max over the tile (rare)
-      float sabs[4], mx = da::kNegInf;
+    for (int rt = 0; rt < NT; ++rt) {
+      // ---- S^T: dot[i] = q . k for token 4*lg + i, row lm of tile rt
+      float4_t dot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        dot = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, sd.k[kb]),
+                                                      __builtin_bit_cast(bf16x8_t, qv[rt][kb]),
+                                                      dot, 0, 0, 0);
+      float z[4];
+      bool need = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sabs[i] = (!MASKED || tb + i < tlim) ? dot[i] * a.scale_log2 : da::kNegInf;
-        mx = fmaxf(mx, sabs[i]);
+        z[i] = fmaf(dot[i], a.scale_log2, -m[rt]);
+        if (MASKED && !(tb + i < tlim[rt])) z[i] = da::kNegInf;
+        need |= z[i] > kRescaleSlack;
       }
-      mx = fmaxf(mx, xor16(mx));
-      mx = fmaxf(mx, xor32(mx));
-      const float mn = fmaxf(m, mx);
-      const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m - mn);
-      l *= al;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        // raise each row's reference to its max over the tile (rare)
+        float sabs[4], mx = da::kNegInf;
 #pragma unroll
-      for (int bb = 0; bb < 8; ++bb) acc[bb] *= al;
-      m = mn;
+        for (int i = 0; i < 4; ++i) {
+          sabs[i] = (!MASKED || tb + i < tlim[rt]) ? dot[i] * a.scale_log2 : da::kNegInf;
+          mx = fmaxf(mx, sabs[i]);
+        }
+        mx = fmaxf(mx, xor16(mx));
+        mx = fmaxf(mx, xor32(mx));
+        const float mn = fmaxf(m[rt], mx);
+        const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m[rt] - mn);
+        l[rt] *= al;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - mn;
+        for (int bb = 0; bb < 8; ++bb) acc[rt][bb] *= al;
+        m[rt] = mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - mn;
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = da::fast_exp2(z[i]);
+        l[rt] += p[i];
+      }
+      // P^T operand in two bf16 terms: hi = bf16(p), lo = bf16(p - hi)
+      const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
+      const uint32_t l01 = pack_bf16(p[0] - bf16_to_f(h01 & 0xffffu), p[1] - bf16_to_f(h01 >> 16));
+      const uint32_t l23 = pack_bf16(p[2] - bf16_to_f(h23 & 0xffffu), p[3] - bf16_to_f(h23 >> 16));
+      phi[rt] = __builtin_bit_cast(s16x4_t, u32x2{h01, h23});
+      plo[rt] = __builtin_bit_cast(s16x4_t, u32x2{l01, l23});
     }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = da::fast_exp2(z[i]);
-      l += p[i];
-    }
-    // P^T operand in two bf16 terms: hi = bf16(p), lo = bf16(p - hi)
-    const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
-    const uint32_t l01 = pack_bf16(p[0] - bf16_to_f(h01 & 0xffffu), p[1] - bf16_to_f(h01 >> 16));
-    const uint32_t l23 = pack_bf16(p[2] - bf16_to_f(h23 & 0xffffu), p[3] - bf16_to_f(h23 >> 16));
-    const s16x4_t phi = __builtin_bit_cast(s16x4_t, u32x2{h01, h23});
-    const s16x4_t plo = __builtin_bit_cast(s16x4_t, u32x2{l01, l23});
 
     // ---- V^T operand: tokens 4*lg + jj, d = 8*lm + bb.  Rows past the split
     // end may hold anything (even NaN): zero there.
@@ -284,8 +301,11 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
       const uint32_t x01 = __builtin_amdgcn_perm(vw[1][bb >> 1], vw[0][bb >> 1], sel);
       const uint32_t x23 = __builtin_amdgcn_perm(vw[3][bb >> 1], vw[2][bb >> 1], sel);
       const s16x4_t va = __builtin_bit_cast(s16x4_t, u32x2{x01, x23});
-      acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[bb], 0, 0, 0);
-      acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[bb], 0, 0, 0);
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        acc[rt][bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi[rt], acc[rt][bb], 0, 0, 0);
+        acc[rt][bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo[rt], acc[rt][bb], 0, 0, 0);
+      }
     }
   };
 
@@ -318,33 +338,42 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
   }
 
   // ---- l is partial over the lane groups; acc and m are already per row
-  l += xor16(l);
-  l += xor32(l);
   __syncthreads();  // ring no longer read by any wave; reuse it
-  float* sm_acc = reinterpret_cast<float*>(smem);  // [kWaves][16][kD]
-  float* sm_m = sm_acc + kWaves * 16 * kD;         // [kWaves][16]
-  float* sm_l = sm_m + kWaves * 16;
+  float* sm_acc = reinterpret_cast<float*>(smem);  // [kWaves][ROWS][kD]
+  float* sm_m = sm_acc + kWaves * ROWS * kD;       // [kWaves][ROWS]
+  float* sm_l = sm_m + kWaves * ROWS;
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb)
+  for (int rt = 0; rt < NT; ++rt) {
+    l[rt] += xor16(l[rt]);
+    l[rt] += xor32(l[rt]);
+    const int row = wave * ROWS + 16 * rt + lm;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm_acc[(wave * 16 + lm) * kD + 8 * (4 * lg + i) + bb] = acc[bb][i];
-  if (lg == 0) {
-    sm_m[wave * 16 + lm] = m;
-    sm_l[wave * 16 + lm] = l;
+    for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_acc[row * kD + 8 * (4 * lg + i) + bb] = acc[rt][bb][i];
+    if (lg == 0) {
+      sm_m[row] = m[rt];
+      sm_l[row] = l[rt];
+    }
   }
   __syncthreads();
-  write_partials<kWaves>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S, s,
-                         0.f, a.o, a.lse);
+  write_partials<kWaves, ROWS>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S, s,
+                               0.f, a.o, a.lse);
 }
 
 }  // namespace
 
-// bf16 stage 1 on the matrix cores for 6..16 query rows per kv-head; -1 when
-// the shape is not covered (the caller then uses another kernel).
-int32_t da_split_bf16_mfma(const da_host::SplitCall& c) {
+// bf16 stage 1 on the matrix cores for 6..16 query rows per kv-head (one
+// row tile) and for more (two row tiles: blocks of up to 32 rows, so that
+// G * q in 17..32 reads each page once); -1 when the shape is not covered
+// (the caller then uses another kernel).
+int32_t da_split_bf16_mfma(const da_host::SplitCall& call) {
+  if (!call.q_bf16 || call.D != kD) return -1;
+  if (da_host::max_split_pages(call) > kMaxSplitPages) return -1;
+  da_host::SplitCall c = call;
+  if (c.rows > DA_MAX_ROWS) da_host::row_blocks(c.rows, 2 * DA_MAX_ROWS, c.nrb, c.rb_rows);
   const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block
-  if (!c.q_bf16 || c.D != kD || R < 6 || R > 16) return -1;
-  if (da_host::max_split_pages(c) > kMaxSplitPages) return -1;
+  if (R < 6) return -1;
   Bf16MfmaArgs a;
   a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
   a.pt = c.pt; a.seqlens = c.seqlens; a.sched = c.sched(); a.o = c.o; a.lse = c.lse;
@@ -354,7 +383,11 @@ int32_t da_split_bf16_mfma(const da_host::SplitCall& c) {
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  hipLaunchKernelGGL(split_bf16_mfma_kernel, dim3(c.grid(false)),
-                     dim3(kThreads), 0, c.stream, a);
+  if (R <= 16)
+    hipLaunchKernelGGL(split_bf16_mfma_kernel<1>, dim3(c.grid(false)), dim3(kThreads), 0,
+                       c.stream, a);
+  else
+    hipLaunchKernelGGL(split_bf16_mfma_kernel<2>, dim3(c.grid(false)), dim3(kThreads), 0,
+                       c.stream, a);
   return da_host::launch_status();
 }

@@ -420,7 +420,7 @@ da_host::SplitCall make_call(const void* q, int q_bf16, const void* k, const voi
   c.rows = c.nrb = c.rb_rows = 1;
   if (Hkv > 0 && Hq > 0 && Hq % Hkv == 0 && qn > 0 && qn <= DA_MAX_Q_PER_REQ && Hq / Hkv <= (1 << 20)) {
     c.rows = (Hq / Hkv) * qn;
-    da_host::row_blocks(c.rows, c.nrb, c.rb_rows);
+    da_host::row_blocks(c.rows, DA_MAX_ROWS, c.nrb, c.rb_rows);
   }
   if (!da_host::kv_strides(kv_layout, Hkv, ps, c.kv)) c.kv = {0, 0};  // rejected by the check
   c.scale = scale; c.causal = causal ? 1 : 0;

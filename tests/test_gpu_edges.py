@@ -114,11 +114,13 @@ def test_wide_batch_both_schedules(gpu, w):
 
 
 # G * q_per_req > 16: ceil(R / 16) row blocks of ceil(R / blocks) rows each
+# (blocks of up to 32 rows on the dense bf16 matrix-core kernel, which holds
+# two 16-row tiles)
 ROW_BLOCKS = [
-    # the headline heads with 4 MTP tokens: 20 rows = 2 x 10 (bf16 matrix cores)
+    # the headline heads with 4 MTP tokens: 20 rows, one block (bf16 matrix cores, 2 tiles)
     W.RAGGED_B64.scaled(name="rows20_bf16_g5_mtp4", batch=3, q_per_req=4, causal=True,
                         lengths="list", length_list=(4, 700, 1500), pin_max=False),
-    # 32 rows = 2 x 16 (bf16 matrix cores), with an empty request
+    # 32 rows, one block (bf16 matrix cores, 2 tiles), with an empty request
     W.BF16_B16.scaled(name="rows32_bf16_g8_mtp4", batch=3, num_q_heads=16, num_kv_heads=2,
                       q_per_req=4, causal=True, lengths="list", length_list=(0, 130, 1100)),
     # INT4 20 rows = 2 x 10, INT8 18 rows = 2 x 9 (matrix cores)
@@ -132,10 +134,10 @@ ROW_BLOCKS = [
                        pool_pages=0),
     W.BF16_B16.scaled(name="rows17_bf16_d64_g17", batch=2, num_q_heads=17, num_kv_heads=1,
                       head_dim=64, page_size=32, lengths="list", length_list=(3, 800)),
-    # one kv-head for 64 query heads: 64 rows = 4 x 16
+    # one kv-head for 64 query heads: 64 rows = 2 x 32
     W.BF16_B16.scaled(name="rows64_bf16_mqa", batch=2, num_q_heads=64, num_kv_heads=1,
                       lengths="list", length_list=(1, 900)),
-    # 16 heads x 16 MTP tokens on one kv-head: 256 rows = 16 x 16
+    # 16 heads x 16 MTP tokens on one kv-head: 256 rows = 8 x 32
     W.BF16_B16.scaled(name="rows256_bf16_g16_mtp16", batch=2, num_q_heads=16, num_kv_heads=1,
                       q_per_req=16, causal=True, lengths="list", length_list=(16, 500)),
 ]
