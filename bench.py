@@ -464,7 +464,8 @@ def tune_variants(which):
     cache formats (bf16, int8, int4) and workload names."""
     from decode_attention_paged_gqa_amd import workloads as W
 
-    variants = [W.RAGGED_B64, W.BF16_B16, W.INT8_B32, W.INT4_MTP_B64, W.BF16_MTP_B64]
+    variants = [W.RAGGED_B64, W.BF16_B16, W.INT8_B32, W.INT4_MTP_B64, W.BF16_MTP_B64,
+                W.BF16_MTP_G5_B64]
     if which == "all":
         return variants
     keep = set(which.split(","))

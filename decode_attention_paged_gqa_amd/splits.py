@@ -70,7 +70,7 @@ class SplitTable:
                    chunk_pages={k: list(v) for k, v in d.get("chunk_pages", {}).items()})
 
     def save(self, path: str = None):
-        path = path or TABLE_PATH
+        path = path or os.environ.get("DECODE_ATTN_SPLITS_TABLE") or TABLE_PATH
         lines = ['{', f' "bucket_tokens": {self.bucket_tokens},',
                  f' "batch_keys": {json.dumps(self.batch_keys)},', ' "tables": {']
         keys = sorted(self.tables)
