@@ -109,16 +109,16 @@ def stage1_kernel(w):
     from decode_attention_paged_gqa_amd import workloads as W
 
     rows = w.group * w.q_per_req
-    rows = -(-rows // -(-rows // 16))  # rows per block (blocks of at most 16)
     bf16_q = w.dtype == "bf16"
-    if w.kv == W.KV_DENSE and bf16_q and rows <= 5:
-        return "split_bf16_kernel", ["split_bf16.hip", "common.h"]
-    if w.kv == W.KV_DENSE and bf16_q and rows <= 16:
-        return "split_bf16_mfma_kernel", ["split_bf16_mfma.hip", "mfma_util.h", "common.h"]
-    if w.kv == W.KV_INT8 and bf16_q and rows <= 16:
-        return "split_int8_mfma_kernel", ["split_int8.hip", "mfma_util.h", "common.h"]
-    if w.kv == W.KV_INT4 and bf16_q and 9 <= rows <= 16:
-        return "split_int4_mfma_kernel", ["split_int4.hip", "mfma_util.h", "common.h"]
+    if w.head_dim == 128 and bf16_q:
+        if w.kv == W.KV_DENSE and rows <= 5:
+            return "split_bf16_kernel", ["split_bf16.hip", "common.h"]
+        if w.kv == W.KV_DENSE:
+            return "split_bf16_mfma_kernel", ["split_bf16_mfma.hip", "mfma_util.h", "common.h"]
+        if w.kv == W.KV_INT8:
+            return "split_int8_mfma_kernel", ["split_int8.hip", "mfma_util.h", "common.h"]
+        if w.kv == W.KV_INT4 and rows >= 9:
+            return "split_int4_mfma_kernel", ["split_int4.hip", "mfma_util.h", "common.h"]
     return "split_fma_kernel", ["split_fma.hip", "common.h"]
 
 

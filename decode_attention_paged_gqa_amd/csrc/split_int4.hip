@@ -1,5 +1,6 @@
-// Stage 1 over an INT4 cache on the matrix cores, for query groups of
-// 9..16 rows per kv-head (G*q, e.g. the MTP verify batches of LightLLM
+// Stage 1 over an INT4 cache on the matrix cores, for 9 or more query rows
+// per kv-head (G*q, in blocks of up to 32: one or two 16-row tiles per
+// workgroup; e.g. the MTP verify batches of LightLLM
 // PR #1549 "Covered decode kernels": INT4 KV flash decode stage 1, MTP
 // attention; SGLang #36219 digest code listing: several tokens per request).
 // Same contract as decode_attn_split_int4.
@@ -73,9 +74,6 @@ constexpr int kStageKsz = 2048;
 constexpr int kStageVsz = 2304;
 constexpr int kStageBytes = 2560;
 constexpr int kRingBytes = kWaves * kStages * kStageBytes;           // 40 KB
-constexpr int kEpiBytes = (kWaves * 16 * kD + 2 * kWaves * 16) * 4;  // 33 KB
-constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
-constexpr int kSmemBytes = kMainBytes + kMaxSplitPages * 4;
 
 struct StageData {
   uint32_t k[4];   // token lm, group kb: dword lg (elements 32*kb + 8*lg + 0..7)
@@ -143,8 +141,15 @@ struct MfmaArgs {
   int causal;
 };
 
-__global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const MfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+// NT row tiles of 16 query rows (NT * 16 rows per workgroup): the K codes and
+// the dequantised V of a tile are formed once and serve every row tile.
+// One tile fits three workgroups per CU, two tiles two.
+template <int NT>
+__global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_kernel(const MfmaArgs a) {
+  constexpr int ROWS = 16 * NT;
+  constexpr int kEpiBytes = (kWaves * ROWS * kD + 2 * kWaves * ROWS) * 4;
+  constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kMainBytes + kMaxSplitPages * 4];
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
 
   da::Stage1Item it;
@@ -174,16 +179,18 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
     }
   }
 
-  // ---- Q^T operand (row lm of this kv-head's 16 query rows): for MFMA kb,
-  // elements 32*kb + 8*lg + e, e = 0..7, scaled by 2^sh and held in fp16
-  uint32_t qv[4][4];  // [kb][register]
-  float qsum[4];      // 2^-24 * sum of the row's scaled fp16 Q over group kb
-  float rowfac;       // score (log2 units) = rowfac * sum_g s_g (dot_g - z_g qsum_g)
-  float qsum_lg;      // qsum[lg]: operand of the zero-point product (group lg, row lm)
-  int tlim;           // tokens t < tlim are visible to this lane's row
-  {
-    const bool live = lm < nr;
-    const int r = r0 + (live ? lm : 0);  // this lane's query row of the kv-head
+  // ---- Q^T operands (row tile rt, row lm): for MFMA kb, elements
+  // 32*kb + 8*lg + e, e = 0..7, scaled by 2^sh and held in fp16
+  uint32_t qv[NT][4][4];  // [rt][kb][register]
+  float rowfac[NT];       // score (log2 units) = rowfac * sum_g s_g (dot_g - z_g qsum_g)
+  float qsum_lg[NT];      // qsum of group lg: operand of the zero-point product
+  int tlim[NT];           // tokens t < tlim are visible to this lane's row
+  int lim_live = t1;
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    const bool live = 16 * rt + lm < nr;
+    const int r = r0 + (live ? 16 * rt + lm : 0);  // this lane's query row of the kv-head
+    float qsum[4];  // 2^-24 * sum of the row's scaled fp16 Q over group kb
     const int i = r / a.G, h = g * a.G + r % a.G;
     const long long qoff = (((long long)b * a.qn + i) * a.Hq + h) * kD + 8 * lg;
     float qf[4][8];
@@ -218,31 +225,36 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
       for (int x = 0; x < 4; ++x) {
         // pairs 1 and 3 meet codes that sit 4 bits up (16 n), see the K operand
         const float f = (x & 1) ? 0.0625f : 1.f;
-        qv[kb][x] = pack_h2(qf[kb][x] * f, qf[kb][x + 4] * f);
+        qv[rt][kb][x] = pack_h2(qf[kb][x] * f, qf[kb][x + 4] * f);
       }
       part += xor16(part);
       part += xor32(part);
       qsum[kb] = ldexpf(part, -24);
     }
-    rowfac = ldexpf(a.scale_log2, 24 - sh);
-    qsum_lg = qsum[0];
+    rowfac[rt] = ldexpf(a.scale_log2, 24 - sh);
+    qsum_lg[rt] = qsum[0];
 #pragma unroll
-    for (int kb = 1; kb < 4; ++kb) qsum_lg = lg == kb ? qsum[kb] : qsum_lg;
-    tlim = live ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
+    for (int kb = 1; kb < 4; ++kb) qsum_lg[rt] = lg == kb ? qsum[kb] : qsum_lg[rt];
+    tlim[rt] = live ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
+    if (live) lim_live = min(lim_live, tlim[rt]);
   }
-  // tiles below every live row's limit need no masks (rows past R have
-  // tlim 0 and are never written, so they do not bound the unmasked region)
+  // tiles below every live row's limit need no masks (rows past the block
+  // have tlim 0 and are never written, so they do not bound the unmasked region)
   int tfull;
   {
-    int lim_live = lm < nr ? tlim : t1;
     for (int o = 1; o < 16; o <<= 1) lim_live = min(lim_live, __shfl_xor(lim_live, o, 64));
     tfull = __builtin_amdgcn_readfirstlane(lim_live);
   }
 
-  float4_t acc[8];
+  float4_t acc[NT][8];
+  float m[NT], l[NT];
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb) acc[bb] = {0.f, 0.f, 0.f, 0.f};
-  float m = da::kNegInf, l = 0.f;
+  for (int rt = 0; rt < NT; ++rt) {
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
+    m[rt] = da::kNegInf;
+    l[rt] = 0.f;
+  }
   // fp16 exponent bits of 1024 in both halves, kept in a register so that
   // mask-and-or is one instruction
   uint32_t magic = 0x64006400u;
@@ -286,72 +298,83 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
 
   auto compute = [&](int j, const StageData& sd, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    // ---- zero-point terms: zt[i] = -sum_g s_g z_g qsum_g for token 4*lg + i,
-    // row lm (A: -s z of token lm, group lg; B: qsum of group lg, row lm)
-    const float nsz = -(h_lo(sd.kz) * h_hi(sd.kz));
-    const float4_t zt =
-        __builtin_amdgcn_mfma_f32_16x16x4f32(nsz, qsum_lg, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    // ---- per-group dot products of the raw codes: dot[kb][i] =
-    // 2^-24 * sum_{d in group kb} q'_d n_d for token 4*lg + i, row lm
-    float4_t dot[4];
+    // ---- K operands, shared by the row tiles: elements (x, x+4) are nibble x
+    // of the dword's two halves; pairs 1 and 3 are masked in place
+    // (16 n * 2^-24, exact), their Q is / 16
+    half8_t ka[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      // elements (x, x+4) are nibble x of the dword's two halves; pairs 1
-      // and 3 are masked in place (16 n * 2^-24, exact), their Q is / 16
       const uint32_t w = sd.k[kb], wh = w >> 8;
       const half2_t k0 = as_h2(w & 0x000F000Fu), k1 = as_h2(w & 0x00F000F0u);
       const half2_t k2 = as_h2(wh & 0x000F000Fu), k3 = as_h2(wh & 0x00F000F0u);
-      const half8_t ka = {k0[0], k0[1], k1[0], k1[1], k2[0], k2[1], k3[0], k3[1]};
-      const half2_t q0 = as_h2(qv[kb][0]), q1 = as_h2(qv[kb][1]);
-      const half2_t q2 = as_h2(qv[kb][2]), q3 = as_h2(qv[kb][3]);
-      const half8_t qb = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
-      dot[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      ka[kb] = half8_t{k0[0], k0[1], k1[0], k1[1], k2[0], k2[1], k3[0], k3[1]};
     }
-    float4_t st;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t sz[4] = {sd.ksz[i][0], sd.ksz[i][1], sd.ksz[i][2], sd.ksz[i][3]};
-      float acc_s = zt[i];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) acc_s = fmaf(h_lo(sz[kb]), dot[kb][i], acc_s);
-      st[i] = acc_s;
-    }
-    // st[i] = score of token 4*lg + i for row lm
+    // -s z of token lm, group lg: the A operand of the zero-point product
+    const float nsz = -(h_lo(sd.kz) * h_hi(sd.kz));
     const int tb = tile_base(j) + 4 * lg;
-    float z[4];
-    bool need = false;
+    half4_t pb[NT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = fmaf(st[i], rowfac, kPScale - m);
-      if (MASKED && !(tb + i < tlim)) z[i] = da::kNegInf;
-      need |= z[i] > kRescaleSlack + kPScale;
-    }
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      float sabs[4], mx = da::kNegInf;
+    for (int rt = 0; rt < NT; ++rt) {
+      // ---- zero-point terms: zt[i] = -sum_g s_g z_g qsum_g for token 4*lg + i,
+      // row lm of tile rt (B: qsum of group lg, row lm)
+      const float4_t zt = __builtin_amdgcn_mfma_f32_16x16x4f32(nsz, qsum_lg[rt],
+                                                              float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      // ---- per-group dot products of the raw codes: dot[kb][i] =
+      // 2^-24 * sum_{d in group kb} q'_d n_d for token 4*lg + i, row lm
+      float4_t dot[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const half2_t q0 = as_h2(qv[rt][kb][0]), q1 = as_h2(qv[rt][kb][1]);
+        const half2_t q2 = as_h2(qv[rt][kb][2]), q3 = as_h2(qv[rt][kb][3]);
+        const half8_t qb = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+        dot[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[kb], qb, float4_t{0.f, 0.f, 0.f, 0.f},
+                                                         0, 0, 0);
+      }
+      float4_t st;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sabs[i] = (!MASKED || tb + i < tlim) ? st[i] * rowfac : da::kNegInf;
-        mx = fmaxf(mx, sabs[i]);
+        const uint32_t sz[4] = {sd.ksz[i][0], sd.ksz[i][1], sd.ksz[i][2], sd.ksz[i][3]};
+        float acc_s = zt[i];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc_s = fmaf(h_lo(sz[kb]), dot[kb][i], acc_s);
+        st[i] = acc_s;
       }
-      mx = fmaxf(mx, xor16(mx));
-      mx = fmaxf(mx, xor32(mx));
-      const float mn = fmaxf(m, mx);
-      const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m - mn);
-      l *= al;
+      // st[i] = score of token 4*lg + i for row lm
+      float z[4];
+      bool need = false;
 #pragma unroll
-      for (int bb = 0; bb < 8; ++bb) acc[bb] *= al;
-      m = mn;
+      for (int i = 0; i < 4; ++i) {
+        z[i] = fmaf(st[i], rowfac[rt], kPScale - m[rt]);
+        if (MASKED && !(tb + i < tlim[rt])) z[i] = da::kNegInf;
+        need |= z[i] > kRescaleSlack + kPScale;
+      }
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        float sabs[4], mx = da::kNegInf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - (mn - kPScale);
+        for (int i = 0; i < 4; ++i) {
+          sabs[i] = (!MASKED || tb + i < tlim[rt]) ? st[i] * rowfac[rt] : da::kNegInf;
+          mx = fmaxf(mx, sabs[i]);
+        }
+        mx = fmaxf(mx, xor16(mx));
+        mx = fmaxf(mx, xor32(mx));
+        const float mn = fmaxf(m[rt], mx);
+        const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m[rt] - mn);
+        l[rt] *= al;
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) acc[rt][bb] *= al;
+        m[rt] = mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - (mn - kPScale);
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = da::fast_exp2(z[i]);
+        l[rt] += p[i];
+      }
+      pb[rt] = half4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
     }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = da::fast_exp2(z[i]);
-      l += p[i];
-    }
-    half4_t pb = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
 
     // ---- V operand: tokens 4*lg + j, d = 8*lm + block
     // rows past the split end may hold anything (even NaN scales): give them
@@ -387,7 +410,9 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
         const half2_t a01 = __builtin_elementwise_fma(n01, hi ? s01h : s01, nzs01);
         const half2_t a23 = __builtin_elementwise_fma(n23, hi ? s23h : s23, nzs23);
         half4_t va = {a01[0], a01[1], a23[0], a23[1]};
-        acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, acc[bb], 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt)
+          acc[rt][bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[rt], acc[rt][bb], 0, 0, 0);
       }
     }
   };
@@ -440,33 +465,42 @@ __global__ __launch_bounds__(kThreads, 3) void split_int4_mfma_kernel(const Mfma
   }
 
   // ---- l is partial over the lane groups; acc and m are already per row
-  l += xor16(l);
-  l += xor32(l);
   __syncthreads();
-  float* sm_acc = reinterpret_cast<float*>(smem);  // [kWaves][16][kD]
-  float* sm_m = sm_acc + kWaves * 16 * kD;         // [kWaves][16]
-  float* sm_l = sm_m + kWaves * 16;
+  float* sm_acc = reinterpret_cast<float*>(smem);  // [kWaves][ROWS][kD]
+  float* sm_m = sm_acc + kWaves * ROWS * kD;       // [kWaves][ROWS]
+  float* sm_l = sm_m + kWaves * ROWS;
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb)
+  for (int rt = 0; rt < NT; ++rt) {
+    l[rt] += xor16(l[rt]);
+    l[rt] += xor32(l[rt]);
+    const int row = wave * ROWS + 16 * rt + lm;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm_acc[(wave * 16 + lm) * kD + 8 * (4 * lg + i) + bb] = acc[bb][i];
-  if (lg == 0) {
-    sm_m[wave * 16 + lm] = m;
-    sm_l[wave * 16 + lm] = l;
+    for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_acc[row * kD + 8 * (4 * lg + i) + bb] = acc[rt][bb][i];
+    if (lg == 0) {
+      sm_m[row] = m[rt];
+      sm_l[row] = l[rt];
+    }
   }
   __syncthreads();
-  write_partials<kWaves>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S, s,
-                         kPScale, a.o, a.lse);
+  write_partials<kWaves, ROWS>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S, s,
+                               kPScale, a.o, a.lse);
 }
 
 }  // namespace
 
-// INT4 stage 1 on the matrix cores; -1 when the shape is not covered
-// (the caller then uses the vector-ALU kernel).
-int32_t da_split_int4_mfma(const da_host::SplitCall& c) {
+// INT4 stage 1 on the matrix cores, one row tile (9..16 query rows per
+// kv-head) or two (blocks of up to 32 rows, so that G * q in 17..32 forms
+// each tile's operands once); -1 when the shape is not covered (the caller
+// then uses the vector-ALU kernel).
+int32_t da_split_int4_mfma(const da_host::SplitCall& call) {
+  if (!call.q_bf16 || call.D != kD) return -1;
+  if (da_host::max_split_pages(call) > kMaxSplitPages) return -1;
+  da_host::SplitCall c = call;
+  if (c.rows > DA_MAX_ROWS) da_host::row_blocks(c.rows, 2 * DA_MAX_ROWS, c.nrb, c.rb_rows);
   const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block
-  if (!c.q_bf16 || c.D != kD || R < 9 || R > 16) return -1;
-  if (da_host::max_split_pages(c) > kMaxSplitPages) return -1;
+  if (R < 9) return -1;
   MfmaArgs a;
   a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
   a.ksz = (const uint8_t*)c.ks; a.vsz = (const uint8_t*)c.vs;
@@ -477,7 +511,11 @@ int32_t da_split_int4_mfma(const da_host::SplitCall& c) {
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  hipLaunchKernelGGL(split_int4_mfma_kernel, dim3(c.grid(true)),
-                     dim3(kThreads), 0, c.stream, a);
+  if (R <= 16)
+    hipLaunchKernelGGL(split_int4_mfma_kernel<1>, dim3(c.grid(true)), dim3(kThreads), 0,
+                       c.stream, a);
+  else
+    hipLaunchKernelGGL(split_int4_mfma_kernel<2>, dim3(c.grid(true)), dim3(kThreads), 0,
+                       c.stream, a);
   return da_host::launch_status();
 }

@@ -1,6 +1,7 @@
 // Stage 1 over an INT8 cache on the matrix cores (LightLLM PR #1549,
 // "Covered decode kernels": INT8 KV flash decode stage 1), for D = 128, bf16
-// Q and up to 16 query rows per kv-head (G * q).  Same contract as
+// Q and G * q query rows per kv-head in blocks of up to 32 (one or two
+// 16-row tiles per workgroup).  Same contract as
 // decode_attn_split_int8: K = k_pool * k_scale, V = v_pool * v_scale, one
 // fp16 scale per (page, slot, kv-head).
 //
@@ -58,10 +59,7 @@ constexpr int kStageK = 0;
 constexpr int kStageV = 2048;
 constexpr int kStageSc = 4096;  // dwords: [0, 16) K scales, [16, 32) V scales, rest unused
 constexpr int kStageBytes = 4352;
-constexpr int kRingBytes = kWaves * kStages * kStageBytes;           // 68 KB
-constexpr int kEpiBytes = (kWaves * 16 * kD + 2 * kWaves * 16) * 4;  // 33 KB
-constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
-constexpr int kSmemBytes = kMainBytes + kMaxSplitPages * 4;
+constexpr int kRingBytes = kWaves * kStages * kStageBytes;  // 68 KB
 
 // LDS position of 16-byte chunk c of token t's row
 __host__ __device__ constexpr int chunk_pos(int t, int c) { return (c + (t >> 1)) & 7; }
@@ -124,8 +122,14 @@ __device__ __forceinline__ uint32_t code_pair_hi(uint32_t w) {
   return __builtin_amdgcn_perm(w, w, 0x0C030C02u);
 }
 
+// NT row tiles of 16 query rows (NT * 16 rows per workgroup): the K and V
+// operands of a tile are formed once and serve every row tile.
+template <int NT>
 __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  constexpr int ROWS = 16 * NT;
+  constexpr int kEpiBytes = (kWaves * ROWS * kD + 2 * kWaves * ROWS) * 4;
+  constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kMainBytes + kMaxSplitPages * 4];
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
 
   da::Stage1Item it;
@@ -155,14 +159,17 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     }
   }
 
-  // ---- Q^T operand: row lm, elements 32*lg + 8*kb + e, scaled by 2^sh, fp16
-  uint32_t qv[4][4];  // [kb][pair]
-  float rowfac;       // score (log2 units) = s * (rowfac * dot - qoff)
-  float qoff;         // rowfac * 128 * 2^-24 * sum of the row's scaled Q
-  int tlim;           // tokens t < tlim are visible to this lane's row
-  {
-    const bool live = lm < nr;
-    const int r = r0 + (live ? lm : 0);  // this lane's query row of the kv-head
+  // ---- Q^T operands: row tile rt, row lm, elements 32*lg + 8*kb + e, scaled
+  // by 2^sh, fp16
+  uint32_t qv[NT][4][4];  // [rt][kb][pair]
+  float rowfac[NT];       // score (log2 units) = s * (rowfac * dot - qoff)
+  float qoff[NT];         // rowfac * 128 * 2^-24 * sum of the row's scaled Q
+  int tlim[NT];           // tokens t < tlim are visible to this lane's row
+  int lim_live = t1;
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    const bool live = 16 * rt + lm < nr;
+    const int r = r0 + (live ? 16 * rt + lm : 0);  // this lane's query row of the kv-head
     const int i = r / a.G, h = g * a.G + r % a.G;
     const long long qoff_el = (((long long)b * a.qn + i) * a.Hq + h) * kD + 32 * lg;
     float qf[4][8];
@@ -194,30 +201,38 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
         sum += qf[kb][e];
       }
 #pragma unroll
-      for (int x = 0; x < 4; ++x) qv[kb][x] = pack_h2(qf[kb][2 * x], qf[kb][2 * x + 1]);
+      for (int x = 0; x < 4; ++x) qv[rt][kb][x] = pack_h2(qf[kb][2 * x], qf[kb][2 * x + 1]);
     }
     sum += xor16(sum);
     sum += xor32(sum);
-    rowfac = ldexpf(a.scale_log2, 24 - sh);
-    qoff = rowfac * ldexpf(sum, -17);  // 128 * 2^-24 = 2^-17
-    tlim = live ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
+    rowfac[rt] = ldexpf(a.scale_log2, 24 - sh);
+    qoff[rt] = rowfac[rt] * ldexpf(sum, -17);  // 128 * 2^-24 = 2^-17
+    tlim[rt] = live ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
+    if (live) lim_live = min(lim_live, tlim[rt]);
   }
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    asm volatile("" : "+v"(qv[kb][0]), "+v"(qv[kb][1]), "+v"(qv[kb][2]), "+v"(qv[kb][3]));
-  // tiles below every live row's limit need no masks (rows past R have
-  // tlim 0 and are never written, so they do not bound the unmasked region)
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      asm volatile("" : "+v"(qv[rt][kb][0]), "+v"(qv[rt][kb][1]), "+v"(qv[rt][kb][2]),
+                   "+v"(qv[rt][kb][3]));
+  // tiles below every live row's limit need no masks (rows past the block
+  // have tlim 0 and are never written, so they do not bound the unmasked region)
   int tfull;
   {
-    int lim_live = lm < nr ? tlim : t1;
     for (int o = 1; o < 16; o <<= 1) lim_live = min(lim_live, __shfl_xor(lim_live, o, 64));
     tfull = __builtin_amdgcn_readfirstlane(lim_live);
   }
 
-  float4_t acc[8];
+  float4_t acc[NT][8];
+  float m[NT], l[NT];
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb) acc[bb] = {0.f, 0.f, 0.f, 0.f};
-  float m = da::kNegInf, l = 0.f;
+  for (int rt = 0; rt < NT; ++rt) {
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
+    m[rt] = da::kNegInf;
+    l[rt] = 0.f;
+  }
   __syncthreads();
 
   // ---- addressing
@@ -275,8 +290,11 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 
   auto compute = [&](int j, const StageData& sd, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    // ---- dot[i] = 2^-24 * sum_d q'_d (b_d + 128) for token 4*lg + i, row lm
-    float4_t dot = {0.f, 0.f, 0.f, 0.f};
+    // ---- dot[rt][i] = 2^-24 * sum_d q'_d (b_d + 128) for token 4*lg + i, row lm
+    // of tile rt
+    float4_t dot[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) dot[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
     {
       const uint32_t kw[8] = {sd.k[0][0] ^ 0x80808080u, sd.k[0][1] ^ 0x80808080u,
                               sd.k[0][2] ^ 0x80808080u, sd.k[0][3] ^ 0x80808080u,
@@ -288,10 +306,13 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
         const half2_t c2 = as_h2(code_pair_lo(kw[2 * kb + 1]));
         const half2_t c3 = as_h2(code_pair_hi(kw[2 * kb + 1]));
         const half8_t ka = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-        const half2_t q0 = as_h2(qv[kb][0]), q1 = as_h2(qv[kb][1]);
-        const half2_t q2 = as_h2(qv[kb][2]), q3 = as_h2(qv[kb][3]);
-        const half8_t qb = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
-        dot = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, dot, 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          const half2_t q0 = as_h2(qv[rt][kb][0]), q1 = as_h2(qv[rt][kb][1]);
+          const half2_t q2 = as_h2(qv[rt][kb][2]), q3 = as_h2(qv[rt][kb][3]);
+          const half8_t qb = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+          dot[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, dot[rt], 0, 0, 0);
+        }
       }
     }
     const int tb = tile_base(j) + 4 * lg;
@@ -301,41 +322,45 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
       ksc[i] = sd.ks[i] >> sc_shift[i];
       vsc[i] = sd.vs[i] >> sc_shift[i];
     }
-    float z[4], tq[4];
-    bool need = false;
+    half4_t pb[NT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tq[i] = fmaf(dot[i], rowfac, -qoff);
-      z[i] = fmaf(h_lo(ksc[i]), tq[i], kPScale - m);
-      if (MASKED && !(tb + i < tlim)) z[i] = da::kNegInf;
-      need |= z[i] > kRescaleSlack + kPScale;
-    }
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      float sabs[4], mx = da::kNegInf;
+    for (int rt = 0; rt < NT; ++rt) {
+      float z[4], tq[4];
+      bool need = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sabs[i] = (!MASKED || tb + i < tlim) ? h_lo(ksc[i]) * tq[i] : da::kNegInf;
-        mx = fmaxf(mx, sabs[i]);
+        tq[i] = fmaf(dot[rt][i], rowfac[rt], -qoff[rt]);
+        z[i] = fmaf(h_lo(ksc[i]), tq[i], kPScale - m[rt]);
+        if (MASKED && !(tb + i < tlim[rt])) z[i] = da::kNegInf;
+        need |= z[i] > kRescaleSlack + kPScale;
       }
-      mx = fmaxf(mx, xor16(mx));
-      mx = fmaxf(mx, xor32(mx));
-      const float mn = fmaxf(m, mx);
-      const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m - mn);
-      l *= al;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        float sabs[4], mx = da::kNegInf;
 #pragma unroll
-      for (int bb = 0; bb < 8; ++bb) acc[bb] *= al;
-      m = mn;
+        for (int i = 0; i < 4; ++i) {
+          sabs[i] = (!MASKED || tb + i < tlim[rt]) ? h_lo(ksc[i]) * tq[i] : da::kNegInf;
+          mx = fmaxf(mx, sabs[i]);
+        }
+        mx = fmaxf(mx, xor16(mx));
+        mx = fmaxf(mx, xor32(mx));
+        const float mn = fmaxf(m[rt], mx);
+        const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m[rt] - mn);
+        l[rt] *= al;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - (mn - kPScale);
+        for (int bb = 0; bb < 8; ++bb) acc[rt][bb] *= al;
+        m[rt] = mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - (mn - kPScale);
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = da::fast_exp2(z[i]);
+        l[rt] += p[i];
+      }
+      pb[rt] = half4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
     }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = da::fast_exp2(z[i]);
-      l += p[i];
-    }
-    const half4_t pb = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
 
     // ---- V operand: tokens 4*lg + j, d = 8*lm + block.  Rows past the
     // split end may hold anything (even NaN scales): code 0, scale 0 there.
@@ -363,7 +388,9 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
         const half2_t a01 = (as_h2(x01) - k1152) * s01;
         const half2_t a23 = (as_h2(x23) - k1152) * s23;
         const half4_t va = {a01[0], a01[1], a23[0], a23[1]};
-        acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, acc[bb], 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt)
+          acc[rt][bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[rt], acc[rt][bb], 0, 0, 0);
       }
     }
   };
@@ -396,33 +423,41 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
   }
 
   // ---- l is partial over the lane groups; acc and m are already per row
-  l += xor16(l);
-  l += xor32(l);
   __syncthreads();
-  float* sm_acc = reinterpret_cast<float*>(smem);  // [kWaves][16][kD]
-  float* sm_m = sm_acc + kWaves * 16 * kD;         // [kWaves][16]
-  float* sm_l = sm_m + kWaves * 16;
+  float* sm_acc = reinterpret_cast<float*>(smem);  // [kWaves][ROWS][kD]
+  float* sm_m = sm_acc + kWaves * ROWS * kD;       // [kWaves][ROWS]
+  float* sm_l = sm_m + kWaves * ROWS;
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb)
+  for (int rt = 0; rt < NT; ++rt) {
+    l[rt] += xor16(l[rt]);
+    l[rt] += xor32(l[rt]);
+    const int row = wave * ROWS + 16 * rt + lm;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm_acc[(wave * 16 + lm) * kD + 8 * (4 * lg + i) + bb] = acc[bb][i];
-  if (lg == 0) {
-    sm_m[wave * 16 + lm] = m;
-    sm_l[wave * 16 + lm] = l;
+    for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_acc[row * kD + 8 * (4 * lg + i) + bb] = acc[rt][bb][i];
+    if (lg == 0) {
+      sm_m[row] = m[rt];
+      sm_l[row] = l[rt];
+    }
   }
   __syncthreads();
-  write_partials<kWaves>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S, s,
-                         kPScale, a.o, a.lse);
+  write_partials<kWaves, ROWS>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S, s,
+                               kPScale, a.o, a.lse);
 }
 
 }  // namespace
 
-// INT8 stage 1 on the matrix cores; -1 when the shape is not covered (the
-// caller then uses the vector-ALU kernel).
-int32_t da_split_int8_mfma(const da_host::SplitCall& c) {
+// INT8 stage 1 on the matrix cores, one row tile (up to 16 query rows per
+// kv-head) or two (blocks of up to 32 rows, so that G * q in 17..32 forms
+// each tile's operands once); -1 when the shape is not covered (the caller
+// then uses the vector-ALU kernel).
+int32_t da_split_int8_mfma(const da_host::SplitCall& call) {
+  if (!call.q_bf16 || call.D != kD) return -1;
+  if (da_host::max_split_pages(call) > kMaxSplitPages) return -1;
+  da_host::SplitCall c = call;
+  if (c.rows > DA_MAX_ROWS) da_host::row_blocks(c.rows, 2 * DA_MAX_ROWS, c.nrb, c.rb_rows);
   const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block
-  if (!c.q_bf16 || c.D != kD || R > 16) return -1;
-  if (da_host::max_split_pages(c) > kMaxSplitPages) return -1;
   Int8Args a;
   a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
   a.ks = (const uint8_t*)c.ks; a.vs = (const uint8_t*)c.vs;
@@ -433,8 +468,11 @@ int32_t da_split_int8_mfma(const da_host::SplitCall& c) {
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  hipLaunchKernelGGL(split_int8_mfma_kernel,
-                     dim3(c.grid(true)), dim3(kThreads), 0,
-                     c.stream, a);
+  if (R <= 16)
+    hipLaunchKernelGGL(split_int8_mfma_kernel<1>, dim3(c.grid(true)), dim3(kThreads), 0,
+                       c.stream, a);
+  else
+    hipLaunchKernelGGL(split_int8_mfma_kernel<2>, dim3(c.grid(true)), dim3(kThreads), 0,
+                       c.stream, a);
   return da_host::launch_status();
 }

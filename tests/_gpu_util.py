@@ -11,7 +11,7 @@ Gates for floating point, by output type:
 * stage-1 partials (fp32): |dO| <= 2e-5 * (1 + |O|), |d lse| <= 1e-4, and the
   empty splits (lse = -inf) must coincide exactly.
 * stage-1 partials of the matrix-core paths (D = 128, bf16 Q; INT4 with
-  9..16 query rows per kv-head, INT8 with up to 16): the P.V product takes P
+  9 or more query rows per kv-head, INT8 with any): the P.V product takes P
   and the dequantised V in fp16 (unit roundoff u = 2^-11).  P enters as
   fp16(p * 2^7) (one relative rounding, p * 2^7 stays in fp16's normal range
   down to p = 2^-21); INT8 V as fp16(b * s) (one rounding); INT4 V as
@@ -192,16 +192,16 @@ def rows_per_block(w: W.Workload) -> int:
 
 def uses_matrix_path(w: W.Workload) -> bool:
     """Whether stage 1 over this workload runs on the matrix cores (D = 128,
-    bf16 Q): INT4 with 9..16 query rows per block, INT8 with up to 16,
-    a dense bf16 cache with 6..16 (rows per block: see rows_per_block)."""
-    rows = rows_per_block(w)
+    bf16 Q): INT4 with 9 or more query rows per kv-head, INT8 with any, a
+    dense bf16 cache with 6 or more (rows beyond 16 in blocks of up to 32)."""
+    rows = w.group * w.q_per_req
     if w.head_dim != 128 or w.dtype == "fp32":
         return False
     if w.kv == W.KV_INT4:
-        return 9 <= rows <= 16
+        return rows >= 9
     if w.kv == W.KV_INT8:
-        return rows <= 16
-    return 6 <= rows <= 16
+        return True
+    return rows >= 6
 
 
 def bf16_split_pv_o_bound(batch: W.PagedBatch):

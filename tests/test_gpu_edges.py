@@ -8,7 +8,8 @@ the fp64 oracle (gates in tests/_gpu_util.py):
 * 16 query rows per kv-head from 16 MTP tokens of one head (q_per_req = 16);
 * a batch much wider than one workgroup (300 requests), with both schedules;
 * more than 16 query rows per kv-head (G * q_per_req up to 256), which runs
-  as row blocks of at most 16 rows on every kernel, with both schedules.
+  as row blocks (of up to 32 rows, two 16-row tiles, on the matrix-core
+  kernels; of up to 16 on the others), with both schedules.
 """
 import numpy as np
 import pytest
@@ -123,11 +124,16 @@ ROW_BLOCKS = [
     # 32 rows, one block (bf16 matrix cores, 2 tiles), with an empty request
     W.BF16_B16.scaled(name="rows32_bf16_g8_mtp4", batch=3, num_q_heads=16, num_kv_heads=2,
                       q_per_req=4, causal=True, lengths="list", length_list=(0, 130, 1100)),
-    # INT4 20 rows = 2 x 10, INT8 18 rows = 2 x 9 (matrix cores)
+    # INT4 20 rows and INT8 18 rows: one block, two row tiles (matrix cores)
     W.INT4_MTP_B64.scaled(name="rows20_int4_g5_mtp4", batch=3, num_q_heads=40, lengths="list",
                           length_list=(5, 333, 1200)),
     W.INT8_B32.scaled(name="rows18_int8_g6_mtp3", batch=2, num_q_heads=12, num_kv_heads=2,
                       q_per_req=3, causal=True, lengths="list", length_list=(77, 900)),
+    # INT4 32 rows (one full block of two tiles), INT8 64 rows (2 x 32)
+    W.INT4_MTP_B64.scaled(name="rows32_int4_g8_mtp4", batch=2, num_q_heads=16, num_kv_heads=2,
+                          lengths="list", length_list=(40, 1000)),
+    W.INT8_B32.scaled(name="rows64_int8_mqa", batch=2, num_q_heads=64, num_kv_heads=1,
+                      lengths="list", length_list=(3, 700)),
     # vector-ALU kernel: fp32 18 rows = 2 x 9; bf16 D = 64, 17 rows = 2 x 9
     W.TINY_FP32.scaled(name="rows18_fp32_g6_mtp3", batch=2, num_q_heads=12, num_kv_heads=2,
                        q_per_req=3, causal=True, lengths="list", length_list=(50, 600),
