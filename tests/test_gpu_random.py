@@ -4,7 +4,7 @@ tokens (causal or not), ragged lengths with empty requests, split count, and
 the batch-wide or per-request schedule, drawn together so that combinations
 the hand-picked cases do not name are compared against the fp64 oracle too.
 Gates as in tests/_gpu_util.py; every stage-1 slot and every output element
-is checked.
+is checked.  Eight more cases draw 17..64 query rows per kv-head.
 """
 import numpy as np
 import pytest
@@ -56,7 +56,40 @@ def random_case(i):
     return w, S, table
 
 
-CASES = [random_case(i) for i in range(N_CASES)]
+def wide_case(i):
+    """More than 16 query rows per kv-head (row blocks; two row tiles on the
+    matrix-core kernels): G * q in 17..64, every format in turn."""
+    rng = np.random.default_rng(9500 + i)
+    fmt = ["bf16", "int8", "int4", "fp32"][i % 4]
+    kv = {"bf16": W.KV_DENSE, "fp32": W.KV_DENSE, "int8": W.KV_INT8, "int4": W.KV_INT4}[fmt]
+    dtype = "fp32" if fmt == "fp32" else "bf16"
+    D = 128 if fmt != "fp32" else int(rng.choice([64, 128]))
+    qn = int(rng.choice([1, 2, 3, 4, 8]))
+    rows = int(rng.integers(17, 65))
+    G = max(1, rows // qn)
+    Hkv = int(rng.choice([1, 2]))
+    ps = int(rng.choice([16, 64, 128]))
+    causal = bool(qn > 1)
+    B = int(rng.integers(1, 5))
+    L = rng.integers(1, 1500, size=B)
+    L[rng.random(B) < 0.2] = 0
+    L[0] = max(int(L[0]), 1)
+    pages = int(((L + ps - 1) // ps).sum())
+    layout = str(rng.choice(["NHD", "HND"]))
+    S = int(rng.choice([1, 2, 3, 5]))
+    table = None
+    if rng.random() < 0.4:
+        table = sorted(int(x) for x in rng.integers(1, S + 1, size=int(rng.integers(1, 5))))
+    w = W.Workload(name=f"wide{i}_{fmt}_{layout.lower()}_d{D}_p{ps}_hkv{Hkv}_g{G}_q{qn}"
+                        f"_b{B}_s{S}{'_sched' if table else ''}",
+                   batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, page_size=ps,
+                   q_per_req=qn, causal=causal, dtype=dtype, kv=kv, lengths="list",
+                   length_list=tuple(int(x) for x in L), pool_pages=pages + 2, seed=300 + i,
+                   kv_layout=layout)
+    return w, S, table
+
+
+CASES = [random_case(i) for i in range(N_CASES)] + [wide_case(i) for i in range(8)]
 
 
 @pytest.mark.parametrize("w,S,table", CASES, ids=[c[0].name for c in CASES])
