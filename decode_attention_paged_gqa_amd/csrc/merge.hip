@@ -15,7 +15,8 @@
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kPrefetch = 8;  // split rows loaded before the weights are known
+constexpr int kPrefetch = 16;  // split rows loaded before the weights are known
+static_assert(DA_MAX_SPLITS == 256, "four lse registers per lane");
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restrict__ op,
@@ -29,21 +30,30 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restr
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const float* l = lp + (long long)row * S;
-  const float* o = op + (long long)row * S * D + lane * E;
-  if (counts) {
-    const int cnt = counts[row / rows_per_req];
-    da::note(checks, lane != 0 || (cnt >= 1 && cnt <= S), DA_CHECK_COUNTS);
-    S = min(max(cnt, 1), S);
-  }
-  // the first kPrefetch split rows are loaded while the max is being found
+  const int slots = S;  // split slots per row in the buffers
+  const float* l = lp + (long long)row * slots;
+  const float* o = op + (long long)row * slots * D + lane * E;
+  // Every load below stays inside the row's slots and is issued before the
+  // row's split count is known: the first kPrefetch split rows, and the
+  // lse of slot lane + 64 k in lane `lane`.
   float pre[kPrefetch][E];
 #pragma unroll
   for (int s = 0; s < kPrefetch; ++s)
 #pragma unroll
-    for (int e = 0; e < E; ++e) pre[s][e] = s < S ? o[(long long)s * D + e] : 0.f;
+    for (int e = 0; e < E; ++e) pre[s][e] = s < slots ? o[(long long)s * D + e] : 0.f;
+  float lv[DA_MAX_SPLITS / 64];
+#pragma unroll
+  for (int k = 0; k < DA_MAX_SPLITS / 64; ++k)
+    lv[k] = 64 * k + lane < slots ? l[64 * k + lane] : da::kNegInf;
+  if (counts) {
+    const int cnt = counts[row / rows_per_req];
+    da::note(checks, lane != 0 || (cnt >= 1 && cnt <= slots), DA_CHECK_COUNTS);
+    S = min(max(cnt, 1), slots);
+  }
   float m = da::kNegInf;
-  for (int s = lane; s < S; s += 64) m = fmaxf(m, l[s]);
+#pragma unroll
+  for (int k = 0; k < DA_MAX_SPLITS / 64; ++k)
+    if (64 * k + lane < S) m = fmaxf(m, lv[k]);
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
 
   float acc[E];
@@ -52,18 +62,23 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restr
   float wsum = 0.f;
   if (m != da::kNegInf) {
     const float ml = m * da::kLog2e;
-    // exp(lse_s - m); 0 for an empty split (lse -inf), whose row holds zeros
+    // exp(lse_s - m); 0 for an empty split (lse -inf), whose row holds zeros.
+    // lse_s is read from the lane that loaded it.
 #pragma unroll
     for (int s = 0; s < kPrefetch; ++s) {
       if (s < S) {
-        const float w = da::fast_exp2(fmaf(l[s], da::kLog2e, -ml));
+        const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv[0]), s));
+        const float w = da::fast_exp2(fmaf(ls, da::kLog2e, -ml));
         wsum += w;
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] = fmaf(w, pre[s][e], acc[e]);
       }
     }
     for (int s = kPrefetch; s < S; ++s) {
-      const float w = da::fast_exp2(fmaf(l[s], da::kLog2e, -ml));
+      const int k = s >> 6;
+      const float lk = k == 0 ? lv[0] : k == 1 ? lv[1] : k == 2 ? lv[2] : lv[3];
+      const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lk), s & 63));
+      const float w = da::fast_exp2(fmaf(ls, da::kLog2e, -ml));
       wsum += w;
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = fmaf(w, o[(long long)s * D + e], acc[e]);
@@ -74,8 +89,13 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restr
   }
   if (OUT_BF16) {
     uint16_t* dst = reinterpret_cast<uint16_t*>(out) + (long long)row * D + lane * E;
+    if constexpr (E == 2) {
+      *reinterpret_cast<uint32_t*>(dst) =
+          (uint32_t)da::float_to_bf16_rne(acc[0]) | ((uint32_t)da::float_to_bf16_rne(acc[1]) << 16);
+    } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e) dst[e] = da::float_to_bf16_rne(acc[e]);
+      for (int e = 0; e < E; ++e) dst[e] = da::float_to_bf16_rne(acc[e]);
+    }
   } else {
     float* dst = reinterpret_cast<float*>(out) + (long long)row * D + lane * E;
 #pragma unroll
@@ -101,6 +121,10 @@ extern "C" int32_t decode_attn_merge(const float* o_partial, const float* lse_pa
                                      const int32_t* split_counts, void* out,
                                      int32_t out_dtype, float* lse_out, void* stream) {
   if (!o_partial || !lse_partial || !out) return DA_ERR_INVALID_ARG;
+  // bf16 outputs leave as pairs (4-byte stores); see "Alignment" in the header
+  if (!da_host::aligned(out, 4) || !da_host::aligned(o_partial, 4) ||
+      !da_host::aligned(lse_partial, 4) || !da_host::aligned(lse_out, 4))
+    return DA_ERR_INVALID_ARG;
   if (batch <= 0 || q_per_req <= 0 || num_q_heads <= 0 || num_splits <= 0 ||
       num_splits > DA_MAX_SPLITS || q_per_req > DA_MAX_Q_PER_REQ)
     return DA_ERR_INVALID_ARG;

@@ -38,7 +38,8 @@
  *     Results for such rows are unspecified.
  *   - Alignment (checked, DA_ERR_INVALID_ARG): the stage-1 calls need q,
  *     the K/V pools and o_partial 16-byte aligned, the scale arrays 4-byte
- *     aligned (16-byte vector accesses).  Allocations from hipMalloc or a
+ *     aligned (16-byte vector accesses); the merge needs its arrays 4-byte
+ *     aligned (bf16 outputs are written in pairs).  Allocations from hipMalloc or a
  *     framework allocator are 256-byte aligned; a view into one keeps the
  *     alignment when its offset is a multiple of 16 bytes.
  *

@@ -120,6 +120,9 @@ def test_merge_and_metadata_and_gather_validation(lib):
     assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 96, 4, None, FAKE, B.DA_BF16, None, None) == 2
     assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 128, 4, FAKE, FAKE, 5, None, None) == 2
     assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 128, 0, None, FAKE, B.DA_BF16, None, None) == 1
+    # bf16 outputs are written in pairs: out must be 4-byte aligned
+    odd = ctypes.c_void_p(0x1002)
+    assert lib.decode_attn_merge(FAKE, FAKE, 1, 1, 8, 128, 4, None, odd, B.DA_BF16, None, None) == 1
     md = [FAKE, FAKE, FAKE, 4, 64, 64, 2, 16, 4, B.DA_Q_STRIDED, None, 1, FAKE, FAKE, FAKE, FAKE,
           None, None]
     bad = list(md); bad[0] = None
