@@ -179,7 +179,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
 
   const int ps = a.page_size;
   const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
-  da::note(a.sched.checks, threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
+  da::note(a.sched.checks,
+           threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
            DA_CHECK_SEQLEN);
   const int n = (L + ps - 1) >> a.log2_ps;
   const int cpg = (n + it.S - 1) / it.S;
@@ -256,11 +257,13 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
     const uint8_t* vb = a.v + base + voff;
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc)
-      __builtin_amdgcn_global_load_lds((const void*)(kb + 128 * cc), (DA_LDS void*)(st + cc * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(kb + 128 * cc), (DA_LDS void*)(st + cc * 1024),
+                                       16, 0, da::kStreamPolicy);
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc)
       __builtin_amdgcn_global_load_lds((const void*)(vb + 128 * cc),
-                                       (DA_LDS void*)(st + (CPL + cc) * 1024), 16, 0, 0);
+                                       (DA_LDS void*)(st + (CPL + cc) * 1024), 16, 0,
+                                       da::kStreamPolicy);
   };
 
   auto scores = [&](const u32x4 (&x)[NCH], float (&d)[RT]) {

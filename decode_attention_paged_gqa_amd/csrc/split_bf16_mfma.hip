@@ -132,7 +132,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
 
   const int ps = a.page_size;
   const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
-  da::note(a.sched.checks, threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
+  da::note(a.sched.checks,
+           threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
            DA_CHECK_SEQLEN);
   const int n = (L + ps - 1) >> a.log2_ps;
   const int cpg = (n + it.S - 1) / it.S;
@@ -225,11 +226,13 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
 #pragma unroll
     for (int h = 0; h < 4; ++h)
       __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * (kD * 2) + voff[h]),
-                                       (DA_LDS void*)(st + kStageK + 1024 * h), 16, 0, 0);
+                                       (DA_LDS void*)(st + kStageK + 1024 * h), 16, 0,
+                                       da::kStreamPolicy);
 #pragma unroll
     for (int h = 0; h < 4; ++h)
       __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * (kD * 2) + voff[h]),
-                                       (DA_LDS void*)(st + kStageV + 1024 * h), 16, 0, 0);
+                                       (DA_LDS void*)(st + kStageV + 1024 * h), 16, 0,
+                                       da::kStreamPolicy);
   };
 
   auto compute = [&](int j, const StageData& sd, auto masked_tag) {

@@ -56,23 +56,48 @@ struct Raw {
   uint32_t w[(BYTES + 3) / 4];
 };
 
+// K/V row pieces are read once per launch: non-temporal loads (see
+// da::kStreamPolicy), except 4-bit rows in the token-major layout, whose
+// cache lines neighbouring kv-heads' workgroups share; query rows, shared by
+// a request's splits, are plain loads too.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
 template <int BYTES>
-__device__ __forceinline__ void load_raw(const uint8_t* p, Raw<BYTES>& r) {
-  if constexpr (BYTES == 32) {
-    const uint4 a = reinterpret_cast<const uint4*>(p)[0];
-    const uint4 b = reinterpret_cast<const uint4*>(p)[1];
-    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-    r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
-  } else if constexpr (BYTES == 16) {
+__device__ __forceinline__ void load_q(const uint8_t* p, Raw<BYTES>& r) {
+  if constexpr (BYTES == 16) {
     const uint4 a = *reinterpret_cast<const uint4*>(p);
     r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-  } else if constexpr (BYTES == 8) {
+  } else {
+    static_assert(BYTES == 8, "a lane's query piece is 8 or 16 bytes");
     const uint2 a = *reinterpret_cast<const uint2*>(p);
     r.w[0] = a.x; r.w[1] = a.y;
+  }
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ T ld(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int BYTES, bool NT = true>
+__device__ __forceinline__ void load_raw(const uint8_t* p, Raw<BYTES>& r) {
+  if constexpr (BYTES == 32) {
+    const u32x4_t a = ld<u32x4_t, NT>(reinterpret_cast<const u32x4_t*>(p));
+    const u32x4_t b = ld<u32x4_t, NT>(reinterpret_cast<const u32x4_t*>(p) + 1);
+    r.w[0] = a[0]; r.w[1] = a[1]; r.w[2] = a[2]; r.w[3] = a[3];
+    r.w[4] = b[0]; r.w[5] = b[1]; r.w[6] = b[2]; r.w[7] = b[3];
+  } else if constexpr (BYTES == 16) {
+    const u32x4_t a = ld<u32x4_t, NT>(reinterpret_cast<const u32x4_t*>(p));
+    r.w[0] = a[0]; r.w[1] = a[1]; r.w[2] = a[2]; r.w[3] = a[3];
+  } else if constexpr (BYTES == 8) {
+    const u32x2_t a = ld<u32x2_t, NT>(reinterpret_cast<const u32x2_t*>(p));
+    r.w[0] = a[0]; r.w[1] = a[1];
   } else if constexpr (BYTES == 4) {
-    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    r.w[0] = ld<uint32_t, NT>(reinterpret_cast<const uint32_t*>(p));
   } else {
-    r.w[0] = *reinterpret_cast<const uint16_t*>(p);
+    r.w[0] = ld<uint16_t, NT>(reinterpret_cast<const uint16_t*>(p));
   }
 }
 
@@ -150,7 +175,8 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
 
   const int ps = a.page_size;
   const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
-  da::note(a.sched.checks, threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
+  da::note(a.sched.checks,
+           threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
            DA_CHECK_SEQLEN);
   const int n = (L + ps - 1) >> a.log2_ps;
   const int cpg = (n + it.S - 1) / it.S;
@@ -167,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
       const long long qoff = (((long long)b * a.qn + i) * a.Hq + h) * D + c * E;
       if (a.q_bf16) {
         Raw<E * 2> qr;
-        load_raw<E * 2>(reinterpret_cast<const uint8_t*>(a.q) + qoff * 2, qr);
+        load_q<E * 2>(reinterpret_cast<const uint8_t*>(a.q) + qoff * 2, qr);
         float f[E];
         Kv<KV_BF16, D>::to_float(qr, f);
 #pragma unroll
@@ -216,8 +242,15 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
         const long long row = (long long)pid * ps * a.Hkv +
                               (long long)(slot0 + st * 4 + tl) * a.slot_stride +
                               (long long)g * a.head_stride;
-        load_raw<P::BYTES>(kb + row * P::ROW_BYTES + c * P::BYTES, kr[st]);
-        load_raw<P::BYTES>(vb + row * P::ROW_BYTES + c * P::BYTES, vr[st]);
+        const uint8_t* kp = kb + row * P::ROW_BYTES + c * P::BYTES;
+        const uint8_t* vp = vb + row * P::ROW_BYTES + c * P::BYTES;
+        if (KV != KV_I4 || a.slot_stride == 1) {  // a kv-head's rows contiguous
+          load_raw<P::BYTES, true>(kp, kr[st]);
+          load_raw<P::BYTES, true>(vp, vr[st]);
+        } else {
+          load_raw<P::BYTES, false>(kp, kr[st]);
+          load_raw<P::BYTES, false>(vp, vr[st]);
+        }
         if constexpr (KV == KV_I8) {
           kscale[st] = da::half_bits_to_float(a.ks[row]);
           vscale[st] = da::half_bits_to_float(a.vs[row]);

@@ -143,8 +143,13 @@ struct MfmaArgs {
 
 // NT row tiles of 16 query rows (NT * 16 rows per workgroup): the K codes and
 // the dequantised V of a tile are formed once and serve every row tile.
-// One tile fits three workgroups per CU, two tiles two.
-template <int NT>
+// One tile fits three workgroups per CU, two tiles two.  POLICY: the cache
+// policy of the code and scale streams.  Non-temporal in the head-major
+// layout, where every cache line belongs to one kv-head's workgroup; the
+// default in the token-major one, where a 64-byte code row (and a 16-byte
+// scale row) shares its line with the neighbouring kv-heads' rows, which
+// their workgroups read from L2 moments later.
+template <int NT, int POLICY>
 __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_kernel(const MfmaArgs a) {
   constexpr int ROWS = 16 * NT;
   constexpr int kEpiBytes = (kWaves * ROWS * kD + 2 * kWaves * ROWS) * 4;
@@ -161,7 +166,8 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
 
   const int ps = a.page_size;
   const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
-  da::note(a.sched.checks, threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
+  da::note(a.sched.checks,
+           threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
            DA_CHECK_SEQLEN);
   const int n = (L + ps - 1) >> a.log2_ps;
   const int cpg = (n + it.S - 1) / it.S;
@@ -287,13 +293,13 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
                            (long long)g * a.head_stride;
     DA_LDS uint8_t* st = ring + (j % kStages) * kStageBytes;
     __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * (kD / 2) + voff_kv),
-                                     (DA_LDS void*)(st + kStageK), 16, 0, 0);
+                                     (DA_LDS void*)(st + kStageK), 16, 0, POLICY);
     __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * (kD / 2) + voff_kv),
-                                     (DA_LDS void*)(st + kStageV), 16, 0, 0);
+                                     (DA_LDS void*)(st + kStageV), 16, 0, POLICY);
     __builtin_amdgcn_global_load_lds((const void*)(a.ksz + row0 * 16 + voff_sz),
-                                     (DA_LDS void*)(st + kStageKsz), 4, 0, 0);
+                                     (DA_LDS void*)(st + kStageKsz), 4, 0, POLICY);
     __builtin_amdgcn_global_load_lds((const void*)(a.vsz + row0 * 16 + voff_sz),
-                                     (DA_LDS void*)(st + kStageVsz), 4, 0, 0);
+                                     (DA_LDS void*)(st + kStageVsz), 4, 0, POLICY);
   };
 
   auto compute = [&](int j, const StageData& sd, auto masked_tag) {
@@ -511,11 +517,15 @@ int32_t da_split_int4_mfma(const da_host::SplitCall& call) {
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  if (R <= 16)
-    hipLaunchKernelGGL(split_int4_mfma_kernel<1>, dim3(c.grid(true)), dim3(kThreads), 0,
-                       c.stream, a);
-  else
-    hipLaunchKernelGGL(split_int4_mfma_kernel<2>, dim3(c.grid(true)), dim3(kThreads), 0,
-                       c.stream, a);
+  const bool hnd = c.kv.slot == 1;  // head-major pool layout
+  const dim3 grid(c.grid(true)), block(kThreads);
+  constexpr int kNt = da::kStreamPolicy;
+  if (R <= 16) {
+    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<1, kNt>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((split_int4_mfma_kernel<1, 0>), grid, block, 0, c.stream, a);
+  } else {
+    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<2, kNt>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((split_int4_mfma_kernel<2, 0>), grid, block, 0, c.stream, a);
+  }
   return da_host::launch_status();
 }

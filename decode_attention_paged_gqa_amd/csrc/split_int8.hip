@@ -141,7 +141,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 
   const int ps = a.page_size;
   const int L = min(max(a.seqlens[b], 0), a.max_pages * ps);
-  da::note(a.sched.checks, threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
+  da::note(a.sched.checks,
+           threadIdx.x != 0 || (a.seqlens[b] >= 0 && a.seqlens[b] <= a.max_pages * ps),
            DA_CHECK_SEQLEN);
   const int n = (L + ps - 1) >> a.log2_ps;
   const int cpg = (n + it.S - 1) / it.S;
@@ -270,14 +271,16 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * kD + voff_kv[h]),
-                                       (DA_LDS void*)(st + kStageK + 1024 * h), 16, 0, 0);
+                                       (DA_LDS void*)(st + kStageK + 1024 * h), 16, 0,
+                                       da::kStreamPolicy);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * kD + voff_kv[h]),
-                                       (DA_LDS void*)(st + kStageV + 1024 * h), 16, 0, 0);
+                                       (DA_LDS void*)(st + kStageV + 1024 * h), 16, 0,
+                                       da::kStreamPolicy);
     const long long e = row0 + (long long)sc_tok * a.slot_stride;  // scale index
     __builtin_amdgcn_global_load_lds((const void*)(sc_base + ((2 * e) & ~3ll)),
-                                     (DA_LDS void*)(st + kStageSc), 4, 0, 0);
+                                     (DA_LDS void*)(st + kStageSc), 4, 0, da::kStreamPolicy);
   };
 
   // Half of the scale dword holding token 4*lg + i's scale.  Its index is
