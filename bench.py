@@ -33,6 +33,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -123,12 +124,16 @@ def stage1_kernel(w):
 
 
 def kernel_hash(w) -> str:
+    """Hash of the code (comments and blank space removed) of the kernel's sources."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_paged_gqa_amd", "csrc")
     for f in stage1_kernel(w)[1]:
         path = os.path.join(csrc, f)
         if os.path.exists(path):
-            h.update(open(path, "rb").read())
+            src = open(path).read()
+            src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+            src = re.sub(r"//[^\n]*", " ", src)
+            h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,5 +1,6 @@
-// Stage 1 over a dense bf16 cache on the matrix cores, for D = 128 and 6..16
-// query rows per kv-head (G * q: the MTP verify batches of LightLLM PR #1549,
+// Stage 1 over a dense bf16 cache on the matrix cores, for D = 128 and 6 or
+// more query rows per kv-head, in blocks of one or two 16-row tiles (G * q:
+// the MTP verify batches of LightLLM PR #1549,
 // "Validation", MTP step 3, and the GQA flash decode of "Covered decode
 // kernels" when G * q makes a dense 16-row tile).  Same contract as
 // decode_attn_split.

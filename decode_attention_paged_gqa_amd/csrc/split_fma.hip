@@ -479,10 +479,10 @@ SplitArgs make_args(const da_host::SplitCall& c) {
 
 // Specialised stage-1 kernels; each returns -1 when the shape is not covered.
 int32_t da_split_bf16_fast(const da_host::SplitCall& c);  // split_bf16.hip: bf16, G*q <= 5
-int32_t da_split_bf16_mfma(const da_host::SplitCall& c);  // split_bf16_mfma.hip: 6..16 rows
+int32_t da_split_bf16_mfma(const da_host::SplitCall& c);  // split_bf16_mfma.hip: >= 6 rows
 // (rows per block: every kernel takes the rows of one row block, see DA_MAX_ROWS)
 int32_t da_split_int8_mfma(const da_host::SplitCall& c);  // split_int8.hip: D 128, bf16 Q
-int32_t da_split_int4_mfma(const da_host::SplitCall& c);  // split_int4.hip: 9..16 rows
+int32_t da_split_int4_mfma(const da_host::SplitCall& c);  // split_int4.hip: >= 9 rows
 
 extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool,
                                      const void* v_pool, const int32_t* page_table,
