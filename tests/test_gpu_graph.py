@@ -32,6 +32,11 @@ CASES = [
                           length_list=(9, 400, 1800), kv_layout="NHD"),
     W.BF16_MTP_B64.scaled(name="graph_bf16_mtp", batch=4, lengths="list",
                           length_list=(3, 90, 1200, 2600)),
+    # 20 query rows per kv-head: the matrix-core kernels with two row tiles
+    W.BF16_MTP_G5_B64.scaled(name="graph_bf16_mtp_20rows", batch=3, lengths="list",
+                             length_list=(4, 700, 2100)),
+    W.INT4_MTP_B64.scaled(name="graph_int4_mtp_20rows", batch=3, num_q_heads=40, lengths="list",
+                          length_list=(6, 500, 1900)),
 ]
 
 
