@@ -247,12 +247,6 @@ struct SplitCall {
   unsigned grid(bool grouped) const;
 };
 
-// Largest split of a launch, in pages: ceil(max_pages / S), or max_pages with
-// a work list (a request may have a single split).
-inline int max_split_pages(const SplitCall& c) {
-  return c.work ? c.max_pages : (c.max_pages + c.S - 1) / c.S;
-}
-
 // 1-D grid of stage 1 (see da::stage1_item) over `units` work units; the
 // grouped order pads to whole rounds of 8 units
 inline long long stage1_grid(long long heads, long long units, bool grouped) {

@@ -185,19 +185,23 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
   const int n = (L + ps - 1) >> a.log2_ps;
   const int cpg = (n + it.S - 1) / it.S;
   const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
-  const int t0 = p0 * ps, t1 = min(p1 * ps, L);
-  const int ntiles = t1 > t0 ? (t1 - t0 + 7) >> 3 : 0;
-  const int nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-
-  // ---- this split's page ids -> LDS (out-of-range ids read page 0)
-  {
+  const int t1 = min(p1 * ps, L);  // the split's tokens end here
+  // The split's page ids are staged in LDS kMaxSplitPages at a time: a longer
+  // split runs as consecutive chunks (the pipeline drains at each chunk's end,
+  // the softmax state carries over).  pc, c0, nmine: the current chunk's first
+  // page and first token, and this wave's tile count in it.
+  int pc = p0, c0 = p0 * ps, nmine = 0;
+  auto stage_pids = [&](int pe) {  // page ids of pages pc .. pe - 1 into s_pid
     const int32_t* ptrow = a.pt + (long long)b * a.pt_stride;
-    for (int j = threadIdx.x; j < p1 - p0; j += kThreads) {
-      const int pid = ptrow[p0 + j];
+    for (int j = threadIdx.x; j < pe - pc; j += kThreads) {
+      const int pid = ptrow[pc + j];
       da::note(a.sched.checks, (unsigned)pid < (unsigned)a.num_pages, DA_CHECK_PAGE_ID);
       s_pid[j] = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
     }
-  }
+  };
+  stage_pids(min(p0 + kMaxSplitPages, p1));  // the first chunk's, before the query setup
+
+  // ---- this split's page ids -> LDS (out-of-range ids read page 0)
 
   // ---- query rows r0 + r = i*G + hh; lane keeps its 2*CPL chunks of every row
   uint32_t qv[RT][4 * CPL];
@@ -236,7 +240,6 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[r][e] = 0.f;
   }
-  __syncthreads();  // s_pid visible
 
   // ---- addressing: per-lane byte offsets are fixed; per-tile bases are scalar
   const long long slot_bytes = (long long)a.slot_stride * D * 2;  // between token slots
@@ -247,8 +250,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   const uint32_t pid_lds = (uint32_t)(uintptr_t)(DA_LDS void*)s_pid;
 
-  auto tile_base = [&](int j) { return t0 + ((wave + kWaves * j) << 3); };
-  auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - p0); };
+  auto tile_base = [&](int j) { return c0 + ((wave + kWaves * j) << 3); };
+  auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - pc); };
   auto issue = [&](int j, int pid) {
     const int tb = tile_base(j);
     const long long base = pid * page_bytes + (tb & (ps - 1)) * slot_bytes + head_base;
@@ -351,20 +354,32 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const Bf16Args 
                                         pid_addr(jn), x);
     if (j + STAGES - 1 < nmine) issue(j + STAGES - 1, pid);  // into the stage read last iteration
   };
-  const int lim = tfull - t0 - 8 * wave - 8;
-  const int jfull = lim < 0 ? 0 : min(nmine, lim / (8 * kWaves) + 1);
+  for (; pc < p1; pc += kMaxSplitPages) {
+    const int pe = min(pc + kMaxSplitPages, p1);
+    c0 = pc * ps;
+    const int c1 = min(pe * ps, t1);
+    if (pc != p0) {
+      __syncthreads();  // the previous chunk's page ids are no longer read
+      stage_pids(pe);
+    }
+    __syncthreads();  // s_pid visible
+    const int ntiles = (c1 - c0 + 7) >> 3;
+    nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+    const int lim = tfull - c0 - 8 * wave - 8;
+    const int jfull = lim < 0 ? 0 : min(nmine, lim / (8 * kWaves) + 1);
 #pragma unroll
-  for (int u = 0; u < STAGES - 1; ++u)
-    if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
-  for (int j = 0; j < jfull; ++j) {
-    u32x4 x[NCH];
-    step(j, x);
-    compute(j, x, std::false_type{});
-  }
-  for (int j = jfull; j < nmine; ++j) {
-    u32x4 x[NCH];
-    step(j, x);
-    compute(j, x, std::true_type{});
+    for (int u = 0; u < STAGES - 1; ++u)
+      if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
+    for (int j = 0; j < jfull; ++j) {
+      u32x4 x[NCH];
+      step(j, x);
+      compute(j, x, std::false_type{});
+    }
+    for (int j = jfull; j < nmine; ++j) {
+      u32x4 x[NCH];
+      step(j, x);
+      compute(j, x, std::true_type{});
+    }
   }
 
   // ---- the 8 token groups share m.  Pairs of groups are summed with one DPP
@@ -442,7 +457,6 @@ int32_t launch(const Bf16Args& a, unsigned grid, hipStream_t st) {
 int32_t da_split_bf16_fast(const da_host::SplitCall& c) {
   const int G = c.Hq / c.Hkv, R = c.rb_rows, D = c.D;  // rows per block
   if (R > 5 || (D != 128 && D != 64)) return -1;
-  if (da_host::max_split_pages(c) > kMaxSplitPages) return -1;
   Bf16Args a;
   a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
   a.pt = c.pt; a.seqlens = c.seqlens; a.sched = c.sched(); a.o = c.o; a.lse = c.lse;

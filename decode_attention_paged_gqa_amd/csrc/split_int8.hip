@@ -147,18 +147,22 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
   const int n = (L + ps - 1) >> a.log2_ps;
   const int cpg = (n + it.S - 1) / it.S;
   const int p0 = min(s * cpg, n), p1 = min((s + 1) * cpg, n);
-  const int t0 = p0 * ps, t1 = min(p1 * ps, L);
-  const int ntiles = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
-  const int nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-
-  {
+  const int t1 = min(p1 * ps, L);  // the split's tokens end here
+  // The split's page ids are staged in LDS kMaxSplitPages at a time: a longer
+  // split runs as consecutive chunks (the pipeline drains at each chunk's end,
+  // the softmax state carries over).  pc, c0, nmine: the current chunk's first
+  // page and first token, and this wave's tile count in it.
+  int pc = p0, c0 = p0 * ps, nmine = 0;
+  auto stage_pids = [&](int pe) {  // page ids of pages pc .. pe - 1 into s_pid
     const int32_t* ptrow = a.pt + (long long)b * a.pt_stride;
-    for (int j = threadIdx.x; j < p1 - p0; j += kThreads) {
-      const int pid = ptrow[p0 + j];
+    for (int j = threadIdx.x; j < pe - pc; j += kThreads) {
+      const int pid = ptrow[pc + j];
       da::note(a.sched.checks, (unsigned)pid < (unsigned)a.num_pages, DA_CHECK_PAGE_ID);
       s_pid[j] = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
     }
-  }
+  };
+  stage_pids(min(p0 + kMaxSplitPages, p1));  // the first chunk's, before the query setup
+
 
   // ---- Q^T operands: row tile rt, row lm, elements 32*lg + 8*kb + e, scaled
   // by 2^sh, fp16
@@ -234,7 +238,6 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     m[rt] = da::kNegInf;
     l[rt] = 0.f;
   }
-  __syncthreads();
 
   // ---- addressing
   const long long rowb = (long long)a.slot_stride * kD;  // bytes between slots (codes)
@@ -260,8 +263,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
       kStageV + 128 * (4 * lg + 2) + 16 * chunk_pos(4 * lg + 2, lm >> 1) + 8 * (lm & 1);
   const uint32_t rd_sc = kStageSc + 16 * lg;
 
-  auto tile_base = [&](int j) { return t0 + ((wave + kWaves * j) << 4); };
-  auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - p0); };
+  auto tile_base = [&](int j) { return c0 + ((wave + kWaves * j) << 4); };
+  auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - pc); };
   const long long head_row = (long long)g * a.head_stride;
   auto issue = [&](int j, int pid) {
     // row of the tile's first slot
@@ -409,20 +412,32 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
                                base + rd_sc, pid_addr(jn), sd);
     if (j + kStages - 1 < nmine) issue(j + kStages - 1, pid);
   };
-  const int lim = tfull - t0 - 16 * wave - 16;
-  const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * kWaves) + 1);
+  for (; pc < p1; pc += kMaxSplitPages) {
+    const int pe = min(pc + kMaxSplitPages, p1);
+    c0 = pc * ps;
+    const int c1 = min(pe * ps, t1);
+    if (pc != p0) {
+      __syncthreads();  // the previous chunk's page ids are no longer read
+      stage_pids(pe);
+    }
+    __syncthreads();  // s_pid visible
+    const int ntiles = (c1 - c0 + 15) >> 4;
+    nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+    const int lim = tfull - c0 - 16 * wave - 16;
+    const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * kWaves) + 1);
 #pragma unroll
-  for (int u = 0; u < kStages - 1; ++u)
-    if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
-  for (int j = 0; j < jfull; ++j) {
-    StageData sd;
-    step(j, sd);
-    compute(j, sd, std::false_type{});
-  }
-  for (int j = jfull; j < nmine; ++j) {
-    StageData sd;
-    step(j, sd);
-    compute(j, sd, std::true_type{});
+    for (int u = 0; u < kStages - 1; ++u)
+      if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
+    for (int j = 0; j < jfull; ++j) {
+      StageData sd;
+      step(j, sd);
+      compute(j, sd, std::false_type{});
+    }
+    for (int j = jfull; j < nmine; ++j) {
+      StageData sd;
+      step(j, sd);
+      compute(j, sd, std::true_type{});
+    }
   }
 
   // ---- l is partial over the lane groups; acc and m are already per row
@@ -457,7 +472,6 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 // then uses the vector-ALU kernel).
 int32_t da_split_int8_mfma(const da_host::SplitCall& call) {
   if (!call.q_bf16 || call.D != kD) return -1;
-  if (da_host::max_split_pages(call) > kMaxSplitPages) return -1;
   da_host::SplitCall c = call;
   if (c.rows > DA_MAX_ROWS) da_host::row_blocks(c.rows, 2 * DA_MAX_ROWS, c.nrb, c.rb_rows);
   const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block

@@ -2,8 +2,8 @@
 the fp64 oracle (gates in tests/_gpu_util.py):
 
 * a split longer than the specialised kernels' page-id tables (1024 pages for
-  the bf16 vector kernel, 512 for the matrix-core ones), which hands the
-  launch to the generic kernel;
+  the bf16 vector kernel, 512 for the matrix-core ones), which they take in
+  chunks of page ids;
 * page sizes 128 and 256;
 * 16 query rows per kv-head from 16 MTP tokens of one head (q_per_req = 16);
 * a batch much wider than one workgroup (300 requests), with both schedules;
@@ -36,7 +36,8 @@ def _run_and_check(gpu, w, S, label):
 
 
 # one request whose single split spans more pages than the LDS page-id table
-# (1024 pages for the bf16 vector kernel, 512 for the matrix-core kernels)
+# (1024 pages for the bf16 vector kernel, 512 for the matrix-core kernels):
+# two or three chunks of page ids
 LONG = [
     W.RAGGED_B64.scaled(name="long_split_bf16_g5_p16", batch=2, page_size=16, lengths="list",
                         length_list=(16400, 37), pin_max=False),
