@@ -482,7 +482,7 @@ int32_t da_split_bf16_fast(const da_host::SplitCall& c);  // split_bf16.hip: bf1
 int32_t da_split_bf16_mfma(const da_host::SplitCall& c);  // split_bf16_mfma.hip: >= 6 rows
 // (rows per block: every kernel takes the rows of one row block, see DA_MAX_ROWS)
 int32_t da_split_int8_mfma(const da_host::SplitCall& c);  // split_int8.hip: D 128, bf16 Q
-int32_t da_split_int4_mfma(const da_host::SplitCall& c);  // split_int4.hip: >= 9 rows
+int32_t da_split_int4_mfma(const da_host::SplitCall& c);  // split_int4.hip: D 128, bf16 Q
 
 extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool,
                                      const void* v_pool, const int32_t* page_table,

@@ -1,6 +1,8 @@
-// Stage 1 over an INT4 cache on the matrix cores, for 9 or more query rows
-// per kv-head (G*q, in blocks of up to 32: one or two 16-row tiles per
-// workgroup; e.g. the MTP verify batches of LightLLM
+// Stage 1 over an INT4 cache on the matrix cores, for any number of query
+// rows per kv-head (G*q, in blocks of up to 32: one or two 16-row tiles per
+// workgroup; a partly filled tile still beats the vector ALU, whose 4-bit
+// expansion cannot keep pace with the memory stream; e.g. the MTP verify
+// batches of LightLLM
 // PR #1549 "Covered decode kernels": INT4 KV flash decode stage 1, MTP
 // attention; SGLang #36219 digest code listing: several tokens per request).
 // Same contract as decode_attn_split_int4.
@@ -511,7 +513,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
 
 }  // namespace
 
-// INT4 stage 1 on the matrix cores, one row tile (9..16 query rows per
+// INT4 stage 1 on the matrix cores, one row tile (up to 16 query rows per
 // kv-head) or two (blocks of up to 32 rows, so that G * q in 17..32 forms
 // each tile's operands once); -1 when the shape is not covered (the caller
 // then uses the vector-ALU kernel).
@@ -520,7 +522,6 @@ int32_t da_split_int4_mfma(const da_host::SplitCall& call) {
   da_host::SplitCall c = call;
   if (c.rows > DA_MAX_ROWS) da_host::row_blocks(c.rows, 2 * DA_MAX_ROWS, c.nrb, c.rb_rows);
   const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block
-  if (R < 9) return -1;
   MfmaArgs a;
   a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
   a.ksz = (const uint8_t*)c.ks; a.vsz = (const uint8_t*)c.vs;

@@ -30,7 +30,7 @@ def random_case(i):
     Hkv = int(rng.choice([1, 2, 3, 4, 8]))
     qn = int(rng.choice([1, 1, 2, 3, 4, 4]))
     G = int(rng.integers(1, min(16 // qn, 8) + 1))
-    if fmt == "int4" and (i // 4) % 2 == 0:  # every other INT4 case: the matrix-core kernel
+    if fmt == "int4" and (i // 4) % 2 == 0:  # every other INT4 case: an MTP-verify shape
         dtype, D, qn, G = "bf16", 128, 4, int(rng.choice([3, 4]))  # 12 or 16 rows
     while G * Hkv > 32:
         G -= 1
