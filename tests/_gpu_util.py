@@ -1,13 +1,16 @@
 """Comparison helpers for the GPU parity tests (test infrastructure).
 
 Gates for floating point, by output type:
-* bf16 outputs: max-abs <= 1e-2 against the fp64 oracle, and rel-L2 <= 1e-3
-  against the fp64 oracle rounded to bf16 (round to nearest even, directly
-  from fp64).  A correctly rounded bf16 result sits ~1.5e-3 rel-L2 from the
-  unrounded fp64 values, so the rel-L2 gate is applied after rounding the
-  oracle the way the output is rounded; the raw figure is still reported.
+* bf16 outputs: max-abs <= 1e-2 and rel-L2 <= 1e-3 against the fp64 oracle
+  rounded to bf16 (round to nearest even, directly from fp64), and against
+  the unrounded oracle |out - ref| <= 1e-2 + half a bf16 ulp of ref, element
+  by element.  A correctly rounded bf16 result sits ~1.5e-3 rel-L2 from the
+  unrounded fp64 values, and at |ref| >= 4 up to 2^-6 > 1e-2 from them (no
+  bf16 number is closer), so both gates allow the output format's own
+  representation error and nothing more; the raw figures are reported.
 * fp32 outputs of fp32 inputs: rel-L2 <= 1e-5 and max-abs <= 1e-5.
-* quantised caches (oracle run on the identically decoded K/V): max-abs <= 1e-2.
+* quantised caches (oracle run on the identically decoded K/V, bf16 output):
+  max-abs <= 1e-2 on top of half a bf16 ulp of each value.
 * stage-1 partials (fp32): |dO| <= 2e-5 * (1 + |O|), |d lse| <= 1e-4, and the
   empty splits (lse = -inf) must coincide exactly.
 * stage-1 partials of the matrix-core paths (D = 128, bf16 Q; INT4 and INT8
@@ -56,13 +59,26 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a - b))
 
 
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half the spacing of bfloat16 numbers (8 significant bits) in the
+    binade of each |x|: the largest error of rounding x to bf16 (0 at x = 0)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, np.ldexp(1.0, (e - 8).astype(np.int64)), 0.0)
+
+
 def check_bf16(out: np.ndarray, ref: np.ndarray, label: str):
     assert np.all(np.isfinite(out)), f"{label}: non-finite output"
+    rounded = bf16_rne_from_f64(ref)
     max_abs = float(np.max(np.abs(out - ref))) if out.size else 0.0
-    r_round = rel_l2(out, bf16_rne_from_f64(ref))
+    max_abs_r = float(np.max(np.abs(out - rounded))) if out.size else 0.0
+    excess = float(np.max(np.abs(out - ref) - bf16_half_ulp(ref))) if out.size else 0.0
+    r_round = rel_l2(out, rounded)
     r_raw = rel_l2(out, ref)
-    log(f"  {label}: max_abs={max_abs:.3e} relL2(vs bf16(oracle))={r_round:.3e} relL2(raw)={r_raw:.3e}")
-    assert max_abs <= 1e-2, f"{label}: max_abs {max_abs}"
+    log(f"  {label}: max_abs={max_abs:.3e} (vs bf16(oracle) {max_abs_r:.3e}, beyond half an ulp "
+        f"{excess:.3e}) relL2(vs bf16(oracle))={r_round:.3e} relL2(raw)={r_raw:.3e}")
+    assert max_abs_r <= 1e-2, f"{label}: max_abs vs bf16(oracle) {max_abs_r}"
+    assert excess <= 1e-2, f"{label}: max_abs {max_abs} exceeds 1e-2 + half a bf16 ulp"
     assert r_round <= 1e-3, f"{label}: rel-L2 {r_round}"
     return max_abs, r_round, r_raw
 
@@ -76,11 +92,16 @@ def check_fp32(out: np.ndarray, ref: np.ndarray, label: str, tol=1e-5):
 
 
 def check_quant(out: np.ndarray, ref: np.ndarray, label: str):
+    """bf16 output over a quantised cache: max-abs <= 1e-2 against the oracle on
+    the identically decoded K/V, on top of half a bf16 ulp of each value (the
+    output format's own representation error, as for check_bf16)."""
     assert np.all(np.isfinite(out)), f"{label}: non-finite output"
     max_abs = float(np.max(np.abs(out - ref))) if out.size else 0.0
+    excess = float(np.max(np.abs(out - ref) - bf16_half_ulp(ref))) if out.size else 0.0
     r = rel_l2(out, bf16_rne_from_f64(ref))
-    log(f"  {label}: max_abs={max_abs:.3e} relL2(vs bf16(oracle), reported)={r:.3e}")
-    assert max_abs <= 1e-2, f"{label}: max_abs {max_abs}"
+    log(f"  {label}: max_abs={max_abs:.3e} (beyond half an ulp {excess:.3e}) "
+        f"relL2(vs bf16(oracle), reported)={r:.3e}")
+    assert excess <= 1e-2, f"{label}: max_abs {max_abs} exceeds 1e-2 + half a bf16 ulp"
 
 
 def check_lse(lse: np.ndarray, ref: np.ndarray, label: str, tol=1e-4):
