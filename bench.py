@@ -104,18 +104,18 @@ def algorithmic_bytes(w, lengths, out_elem=2):
 
 
 def stage1_kernel(w):
-    """(kernel name, source files) of the stage-1 kernel a D = 128 workload runs
-    on, as the library dispatches it; traffic counters taken on a kernel stay
+    """(kernel name, source files) of the stage-1 kernel a workload runs on,
+    as the library dispatches it; traffic counters taken on a kernel stay
     valid only while its sources are unchanged."""
     from decode_attention_paged_gqa_amd import workloads as W
 
     rows = w.group * w.q_per_req
     bf16_q = w.dtype == "bf16"
-    if w.head_dim == 128 and bf16_q:
-        if w.kv == W.KV_DENSE and rows <= 5:
+    if bf16_q and w.kv == W.KV_DENSE:
+        if rows <= 5:
             return "split_bf16_kernel", ["split_bf16.hip", "common.h"]
-        if w.kv == W.KV_DENSE:
-            return "split_bf16_mfma_kernel", ["split_bf16_mfma.hip", "mfma_util.h", "common.h"]
+        return "split_bf16_mfma_kernel", ["split_bf16_mfma.hip", "mfma_util.h", "common.h"]
+    if w.head_dim == 128 and bf16_q:
         if w.kv == W.KV_INT8:
             return "split_int8_mfma_kernel", ["split_int8.hip", "mfma_util.h", "common.h"]
         if w.kv == W.KV_INT4:

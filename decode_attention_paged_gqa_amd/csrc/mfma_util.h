@@ -56,23 +56,26 @@ __device__ __forceinline__ int q_row_shift(float row_absmax) {
   return 15 - ex;
 }
 
-// End of a matrix-core stage-1 workgroup (256 threads, D = 128): combine
-// the per-wave states of its query rows, sm_acc [waves][ROWS][128] (unscaled
-// output sums), sm_m / sm_l [waves][ROWS] (running reference and weight sum,
-// log2 units), and write the split's partial rows r0 .. r0 + nr - 1 of
-// kv-head g.  Thread t takes rows t / 16 + 16 k and columns 8 * (t % 16) .. + 7,
-// so the per-row terms are formed once per row and the stores are two
-// 16-byte writes.  lse_shift (log2 units) is a constant factor carried in l.
-template <int WAVES, int ROWS = 16>
+// End of a matrix-core stage-1 workgroup (256 threads): combine the per-wave
+// states of its query rows, sm_acc [waves][ROWS][D] (unscaled output sums),
+// sm_m / sm_l [waves][ROWS] (running reference and weight sum, log2 units),
+// and write the split's partial rows r0 .. r0 + nr - 1 of kv-head g.  A row
+// is taken by D / 8 threads of 8 columns each (thread t: row t / (D / 8) +
+// (2048 / D) k, columns 8 * (t % (D / 8)) .. + 7), so the per-row terms are
+// formed once per thread and the stores are two 16-byte writes.  lse_shift
+// (log2 units) is a constant factor carried in l.
+template <int WAVES, int ROWS = 16, int D = 128>
 __device__ __forceinline__ void write_partials(const float* sm_acc, const float* sm_m,
                                                const float* sm_l, int r0, int nr, int G, int g,
                                                int b, int qn, int Hq, int S, int s,
                                                float lse_shift, float* o, float* lse) {
-  constexpr int kD = 128;
-  const int d0 = 8 * (threadIdx.x & 15);
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int kTpr = D / 8;           // threads per row
+  constexpr int kRpp = 256 / kTpr;      // rows per pass
+  const int d0 = 8 * (threadIdx.x & (kTpr - 1));
 #pragma unroll
-  for (int k = 0; k < ROWS / 16; ++k) {
-    const int r = (threadIdx.x >> 4) + 16 * k;
+  for (int k = 0; k < (ROWS + kRpp - 1) / kRpp; ++k) {
+    const int r = threadIdx.x / kTpr + kRpp * k;
     if (r >= nr) return;
     float mw[WAVES], M = da::kNegInf;
 #pragma unroll
@@ -86,7 +89,7 @@ __device__ __forceinline__ void write_partials(const float* sm_acc, const float*
       for (int w = 0; w < WAVES; ++w) {
         const float f = da::fast_exp2(mw[w] - M);
         lsum = fmaf(sm_l[w * ROWS + r], f, lsum);
-        const float4* x = reinterpret_cast<const float4*>(sm_acc + (w * ROWS + r) * kD + d0);
+        const float4* x = reinterpret_cast<const float4*>(sm_acc + (w * ROWS + r) * D + d0);
         const float4 x0 = x[0], x1 = x[1];
         const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
@@ -97,12 +100,27 @@ __device__ __forceinline__ void write_partials(const float* sm_acc, const float*
     for (int e = 0; e < 8; ++e) y[e] = lsum > 0.f ? y[e] / lsum : 0.f;
     const int rr = r0 + r, i = rr / G, h = g * G + rr % G;
     const long long orow = (((long long)b * qn + i) * Hq + h) * S + s;
-    float4* dst = reinterpret_cast<float4*>(o + orow * kD + d0);
+    float4* dst = reinterpret_cast<float4*>(o + orow * D + d0);
     dst[0] = make_float4(y[0], y[1], y[2], y[3]);
     dst[1] = make_float4(y[4], y[5], y[6], y[7]);
     if (d0 == 0)
       lse[orow] = lsum > 0.f ? (M + __log2f(lsum) - lse_shift) * da::kLn2 : da::kNegInf;
   }
+}
+
+// s_waitcnt that leaves `ahead` tiles of LOADS loads each in flight (ahead is
+// wave-uniform, at most MAXA)
+template <int LOADS, int MAXA>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  static_assert(MAXA >= 1 && MAXA <= 3, "pipeline depth");
+  if constexpr (MAXA >= 3) {
+    if (ahead >= 3) { wait_vmcnt<3 * LOADS>(); return; }
+  }
+  if constexpr (MAXA >= 2) {
+    if (ahead >= 2) { wait_vmcnt<2 * LOADS>(); return; }
+  }
+  if (ahead >= 1) { wait_vmcnt<LOADS>(); return; }
+  wait_vmcnt<0>();
 }
 
 }  // namespace da_mfma

@@ -1,5 +1,5 @@
-// Stage 1 over a dense bf16 cache on the matrix cores, for D = 128 and 6 or
-// more query rows per kv-head, in blocks of one or two 16-row tiles (G * q:
+// Stage 1 over a dense bf16 cache on the matrix cores, for D = 128 or 64 and 6
+// or more query rows per kv-head, in blocks of one or two 16-row tiles (G * q:
 // the MTP verify batches of LightLLM PR #1549,
 // "Validation", MTP step 3, and the GQA flash decode of "Covered decode
 // kernels" when G * q makes a dense 16-row tile).  Same contract as
@@ -7,8 +7,8 @@
 //
 // One workgroup (4 waves) per (kv-head g, split s, request b); 16-token tiles
 // dealt round-robin to the waves.  Per tile and wave:
-//   S^T[16 tok x 16 rows] = K[16 x 128] . Q^T       4x v_mfma_f32_16x16x32_bf16
-//   O^T[128 x 16 rows]   += V^T[128 x 16] . P^T    16x v_mfma_f32_16x16x16_bf16
+//   S^T[16 tok x 16 rows] = K[16 x D] . Q^T       D/32 x v_mfma_f32_16x16x32_bf16
+//   O^T[D x 16 rows]     += V^T[D x 16] . P^T     D/8 x v_mfma_f32_16x16x16_bf16
 // S is computed transposed so each lane's four scores (4 tokens, one row)
 // sit where the PV product wants its B operand.  Lane l = 16*lg + lm.
 //
@@ -20,19 +20,21 @@
 // |p - hi - lo| <= 2^-16 |p|.
 //   * QK: MFMA kb, lane (lm, lg): token lm, elements 32*kb + 8*lg + 0..7,
 //     i.e. 16-byte chunk 4*kb + lg of its row; Q^T likewise for row lm.
-//   * PV: output block bb, row m is d = 8*m + bb: lane (lm, lg) holds chunk
-//     lm (elements 8*lm .. 8*lm+7) of each of its four tokens 4*lg + j, and
-//     one v_perm per token pair picks element bb of each.
+//   * PV: output block bb (of D/16), row m is d = (D/16)*m + bb: lane (lm, lg)
+//     holds elements (D/16)*lm .. + D/16 - 1 of each of its four tokens
+//     4*lg + j (a 16-byte chunk at D = 128, half of one at D = 64), and one
+//     v_perm per token pair picks element bb of each.
 //
-// Memory pipeline: a 16-token tile is 4 KB of K and 4 KB of V per wave.  The
-// per-wave LDS ring has two such stages (two workgroups fit a CU); a stage is
-// read into registers and at once refilled with the tile two ahead, so two
-// tiles are in flight behind the one being computed.  Loads are
+// Memory pipeline: a 16-token tile is 32*D bytes of K and as many of V per
+// wave.  The per-wave LDS ring holds 16 KB of such stages (two at D = 128,
+// four at D = 64; two workgroups fit a CU); a stage is read into registers and
+// at once refilled with the tile that many ahead, so the same number of bytes
+// is in flight behind the tile being computed at either D.  Loads are
 // global_load_lds (16 bytes per lane), read back by inline asm after an
 // explicit vmcnt wait (the compiler would drain the queue before any LDS read
-// it can see).  A row's sixteen 16-byte chunks are stored rotated by the
-// token index within the tile, so both operand reads spread over the LDS
-// banks.
+// it can see).  A row's 16-byte chunks are stored rotated by the token index
+// within the tile (by half of it at D = 64, where two rows share a bank
+// sweep), so both operand reads spread over the LDS banks.
 //
 // Softmax: one running reference m per query row, uniform over the lanes
 // holding that row; raised lazily when a score exceeds m + 8 (log2 units).
@@ -49,27 +51,60 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = 2;
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kMaxSplitPages = 512;
-constexpr int kD = 128;
 
-constexpr int kStageK = 0;
-constexpr int kStageV = 4096;
-constexpr int kStageBytes = 8192;
-constexpr int kRingBytes = kWaves * kStages * kStageBytes;  // 64 KB
-
-// LDS position of 16-byte chunk c of tile row t
-__host__ __device__ constexpr int chunk_pos(int t, int c) { return (c + t) & 15; }
-
-struct StageData {
-  u32x4 k[4];  // token lm: chunk 4*kb + lg
-  u32x4 v[4];  // token 4*lg + j: chunk lm
+// Per-head-dim geometry of a tile and of the LDS ring.
+template <int D>
+struct Geo {
+  static_assert(D == 64 || D == 128, "head dim");
+  static constexpr int kChunks = D / 8;        // 16-byte chunks per K/V row
+  static constexpr int kKb = D / 32;           // QK products per row tile
+  static constexpr int kBlocks = D / 16;       // PV output blocks of 16 d-rows
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kStageK = 0;
+  static constexpr int kStageV = 16 * kRowBytes;
+  static constexpr int kStageBytes = 32 * kRowBytes;
+  static constexpr int kStages = 16384 / kStageBytes;  // per wave: 16 KB
+  static constexpr int kDma = D / 32;          // 1 KB DMA instructions per tensor and tile
+  static constexpr int kLoads = 2 * kDma;      // per tile
+  static constexpr int kRingBytes = kWaves * kStages * kStageBytes;  // 64 KB
+  // LDS position of 16-byte chunk c of tile row t
+  __host__ __device__ static constexpr int chunk_pos(int t, int c) {
+    return (c + (D == 128 ? t : t >> 1)) & (kChunks - 1);
+  }
 };
 
-// All reads of one stage plus a page id, in one asm block.
+template <int D>
+struct StageData {
+  using VT = std::conditional_t<D == 128, u32x4, u32x2>;
+  u32x4 k[Geo<D>::kKb];  // token lm: chunk 4*kb + lg
+  VT v[4];               // token 4*lg + j: elements (D/16)*lm .. + D/16 - 1
+};
+
+// All reads of one stage plus a page id, in one asm block.  At D = 64, token
+// 4*lg + 2x + 1 sits one 128-byte row after token 4*lg + 2x, at the same
+// rotation (va[x] addresses the even one).
+__device__ __forceinline__ int32_t read_stage(const uint32_t (&ka)[2], const uint32_t (&va)[2],
+                                              uint32_t pidaddr, StageData<64>& s) {
+  int32_t pid;
+  asm volatile(
+      "ds_read_b128 %0, %7\n\t"
+      "ds_read_b128 %1, %8\n\t"
+      "ds_read_b64 %2, %9\n\t"
+      "ds_read_b64 %3, %9 offset:128\n\t"
+      "ds_read_b64 %4, %10\n\t"
+      "ds_read_b64 %5, %10 offset:128\n\t"
+      "ds_read_b32 %6, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(s.k[0]), "=&v"(s.k[1]), "=&v"(s.v[0]), "=&v"(s.v[1]), "=&v"(s.v[2]),
+        "=&v"(s.v[3]), "=&v"(pid)
+      : "v"(ka[0]), "v"(ka[1]), "v"(va[0]), "v"(va[1]), "v"(pidaddr)
+      : "memory");
+  return __builtin_amdgcn_readfirstlane(pid);
+}
 __device__ __forceinline__ int32_t read_stage(const uint32_t (&ka)[4], const uint32_t (&va)[4],
-                                              uint32_t pidaddr, StageData& s) {
+                                              uint32_t pidaddr, StageData<128>& s) {
   int32_t pid;
   asm volatile(
       "ds_read_b128 %0, %9\n\t"
@@ -116,8 +151,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 // NT row tiles of 16 query rows (NT * 16 rows per workgroup): the K/V
 // operands of a tile are read once and serve every row tile.
-template <int NT>
+template <int D, int NT>
 __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16MfmaArgs a) {
+  using Gm = Geo<D>;
+  constexpr int kD = D, kKb = Gm::kKb, kBlocks = Gm::kBlocks, kStages = Gm::kStages;
+  constexpr int kStageK = Gm::kStageK, kStageV = Gm::kStageV, kStageBytes = Gm::kStageBytes;
+  constexpr int kRingBytes = Gm::kRingBytes;
   constexpr int ROWS = 16 * NT;
   constexpr int kEpiBytes = (kWaves * ROWS * kD + 2 * kWaves * ROWS) * 4;
   constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
@@ -158,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
 
   // ---- Q^T operands: row tile rt, row lm, elements 32*kb + 8*lg + e (rows
   // past the block: zero)
-  u32x4 qv[NT][4];
+  u32x4 qv[NT][kKb];
   int tlim[NT];  // tokens t < tlim are visible to this lane's row of tile rt
   int lim_live = t1;
 #pragma unroll
@@ -169,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
     const uint4* qp =
         reinterpret_cast<const uint4*>(a.q + (((long long)b * a.qn + i) * a.Hq + h) * kD + 8 * lg);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kKb; ++kb) {
       const uint4 x = qp[4 * kb];
       qv[rt][kb] = live ? u32x4{x.x, x.y, x.z, x.w} : u32x4{0u, 0u, 0u, 0u};
     }
@@ -180,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) asm volatile("" : "+v"(qv[rt][kb]));
+    for (int kb = 0; kb < kKb; ++kb) asm volatile("" : "+v"(qv[rt][kb]));
   // tiles below every live row's limit need no masks (rows past the block
   // have tlim 0 and are never written, so they do not bound the unmasked region)
   int tfull;
@@ -189,12 +228,12 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
     tfull = __builtin_amdgcn_readfirstlane(lim_live);
   }
 
-  float4_t acc[NT][8];
+  float4_t acc[NT][kBlocks];
   float m[NT], l[NT];
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
+    for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
     m[rt] = da::kNegInf;
     l[rt] = 0.f;
   }
@@ -202,22 +241,32 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
   // ---- addressing
   const long long rowb = (long long)a.slot_stride * kD * 2;  // bytes between slots
   // DMA instruction h, lane i fills LDS chunk i of that 1 KB block: tile row
-  // 4h + i/16, position i%16, holding the row's chunk (position - row) mod 16
-  uint32_t voff[4];
+  // (64 / chunks) h + i / chunks, position i % chunks, holding the row's
+  // chunk c with chunk_pos(row, c) = position
+  constexpr int kC = Gm::kChunks;
+  uint32_t voff[Gm::kDma];
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int t = 4 * h + (lane >> 4), p = lane & 15;
-    voff[h] = (uint32_t)(t * rowb + 16 * ((p - t) & 15));
+  for (int h = 0; h < Gm::kDma; ++h) {
+    const int t = (64 / kC) * h + lane / kC, p = lane % kC;
+    voff[h] = (uint32_t)(t * rowb + 16 * ((p - Gm::chunk_pos(t, 0)) & (kC - 1)));
   }
   DA_LDS uint8_t* ring = (DA_LDS uint8_t*)smem + wave * (kStages * kStageBytes);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   const uint32_t pid_lds = (uint32_t)(uintptr_t)(DA_LDS void*)s_pid;
-  uint32_t rd_k[4], rd_v[4];
+  constexpr int kRow = Gm::kRowBytes;
+  constexpr int kNv = D == 128 ? 4 : 2;  // V read addresses (D = 64: token pairs)
+  uint32_t rd_k[kKb], rd_v[kNv];
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    rd_k[x] = kStageK + 256 * lm + 16 * chunk_pos(lm, 4 * x + lg);
-    const int t = 4 * lg + x;
-    rd_v[x] = kStageV + 256 * t + 16 * chunk_pos(t, lm);
+  for (int x = 0; x < kKb; ++x) rd_k[x] = kStageK + kRow * lm + 16 * Gm::chunk_pos(lm, 4 * x + lg);
+#pragma unroll
+  for (int x = 0; x < kNv; ++x) {
+    if constexpr (D == 128) {
+      const int t = 4 * lg + x;
+      rd_v[x] = kStageV + kRow * t + 16 * Gm::chunk_pos(t, lm);
+    } else {
+      const int t = 4 * lg + 2 * x;  // elements 4*lm .. 4*lm+3: half lm & 1 of chunk lm / 2
+      rd_v[x] = kStageV + kRow * t + 16 * Gm::chunk_pos(t, lm >> 1) + 8 * (lm & 1);
+    }
   }
 
   auto tile_base = [&](int j) { return c0 + ((wave + kWaves * j) << 4); };
@@ -228,18 +277,18 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
                            (long long)(tile_base(j) & (ps - 1)) * a.slot_stride + head_row;
     DA_LDS uint8_t* st = ring + (j % kStages) * kStageBytes;
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
+    for (int h = 0; h < Gm::kDma; ++h)
       __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * (kD * 2) + voff[h]),
                                        (DA_LDS void*)(st + kStageK + 1024 * h), 16, 0,
                                        da::kStreamPolicy);
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
+    for (int h = 0; h < Gm::kDma; ++h)
       __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * (kD * 2) + voff[h]),
                                        (DA_LDS void*)(st + kStageV + 1024 * h), 16, 0,
                                        da::kStreamPolicy);
   };
 
-  auto compute = [&](int j, const StageData& sd, auto masked_tag) {
+  auto compute = [&](int j, const StageData<D>& sd, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int tb = tile_base(j) + 4 * lg;
     s16x4_t phi[NT], plo[NT];
@@ -248,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
       // ---- S^T: dot[i] = q . k for token 4*lg + i, row lm of tile rt
       float4_t dot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < kKb; ++kb)
         dot = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, sd.k[kb]),
                                                       __builtin_bit_cast(bf16x8_t, qv[rt][kb]),
                                                       dot, 0, 0, 0);
@@ -274,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
         const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m[rt] - mn);
         l[rt] *= al;
 #pragma unroll
-        for (int bb = 0; bb < 8; ++bb) acc[rt][bb] *= al;
+        for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] *= al;
         m[rt] = mn;
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = sabs[i] == da::kNegInf ? da::kNegInf : sabs[i] - mn;
@@ -293,16 +342,17 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
       plo[rt] = __builtin_bit_cast(s16x4_t, u32x2{l01, l23});
     }
 
-    // ---- V^T operand: tokens 4*lg + jj, d = 8*lm + bb.  Rows past the split
-    // end may hold anything (even NaN): zero there.
-    u32x4 vw[4];
+    // ---- V^T operand: tokens 4*lg + jj, d = (D/16)*lm + bb.  Rows past the
+    // split end may hold anything (even NaN): zero there.
+    using VT = typename StageData<D>::VT;
+    VT vw[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const bool ok = !MASKED || tb + jj < t1;
-      vw[jj] = ok ? sd.v[jj] : u32x4{0u, 0u, 0u, 0u};
+      vw[jj] = ok ? sd.v[jj] : VT{};
     }
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
+    for (int bb = 0; bb < kBlocks; ++bb) {
       // element bb of each token's chunk: dword bb/2, half bb%2
       const uint32_t sel = (bb & 1) ? 0x07060302u : 0x05040100u;
       const uint32_t x01 = __builtin_amdgcn_perm(vw[1][bb >> 1], vw[0][bb >> 1], sel);
@@ -317,14 +367,18 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
   };
 
   // ---- pipeline: tile j is read into registers and its stage refilled with
-  // tile j + 2 at once; tiles j+1 and j+2 stay in flight during compute(j)
-  auto step = [&](int j, StageData& sd) {
-    if (j + 1 < nmine) wait_vmcnt<8>();  // tile j+1's 8 loads may stay in flight
-    else wait_vmcnt<0>();
+  // tile j + kStages at once; tiles j+1 .. j+kStages stay in flight during
+  // compute(j)
+  auto step = [&](int j, StageData<D>& sd) {
+    // the tiles after j issued so far may stay in flight
+    wait_tiles_ahead<Gm::kLoads, kStages - 1>(min(kStages - 1, nmine - 1 - j));
     const int jn = min(j + kStages, nmine - 1);  // the tile to issue next
     const uint32_t base = ring_lds + (j % kStages) * kStageBytes;
-    const uint32_t ka[4] = {base + rd_k[0], base + rd_k[1], base + rd_k[2], base + rd_k[3]};
-    const uint32_t va[4] = {base + rd_v[0], base + rd_v[1], base + rd_v[2], base + rd_v[3]};
+    uint32_t ka[kKb], va[kNv];
+#pragma unroll
+    for (int x = 0; x < kKb; ++x) ka[x] = base + rd_k[x];
+#pragma unroll
+    for (int x = 0; x < kNv; ++x) va[x] = base + rd_v[x];
     const int pid = read_stage(ka, va, pid_addr(jn), sd);
     if (j + kStages < nmine) issue(j + kStages, pid);  // into the stage just read
   };
@@ -345,12 +399,12 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
     for (int u = 0; u < kStages; ++u)
       if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
     for (int j = 0; j < jfull; ++j) {
-      StageData sd;
+      StageData<D> sd;
       step(j, sd);
       compute(j, sd, std::false_type{});
     }
     for (int j = jfull; j < nmine; ++j) {
-      StageData sd;
+      StageData<D> sd;
       step(j, sd);
       compute(j, sd, std::true_type{});
     }
@@ -367,27 +421,38 @@ __global__ __launch_bounds__(kThreads, 2) void split_bf16_mfma_kernel(const Bf16
     l[rt] += xor32(l[rt]);
     const int row = wave * ROWS + 16 * rt + lm;
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
+    for (int bb = 0; bb < kBlocks; ++bb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_acc[row * kD + 8 * (4 * lg + i) + bb] = acc[rt][bb][i];
+      for (int i = 0; i < 4; ++i)
+        sm_acc[row * kD + kBlocks * (4 * lg + i) + bb] = acc[rt][bb][i];
     if (lg == 0) {
       sm_m[row] = m[rt];
       sm_l[row] = l[rt];
     }
   }
   __syncthreads();
-  write_partials<kWaves, ROWS>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S, s,
-                               0.f, a.o, a.lse);
+  write_partials<kWaves, ROWS, D>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S,
+                                  s, 0.f, a.o, a.lse);
+}
+
+template <int D>
+void launch(const da_host::SplitCall& c, const Bf16MfmaArgs& a, int R) {
+  if (R <= 16)
+    hipLaunchKernelGGL((split_bf16_mfma_kernel<D, 1>), dim3(c.grid(false)), dim3(kThreads), 0,
+                       c.stream, a);
+  else
+    hipLaunchKernelGGL((split_bf16_mfma_kernel<D, 2>), dim3(c.grid(false)), dim3(kThreads), 0,
+                       c.stream, a);
 }
 
 }  // namespace
 
-// bf16 stage 1 on the matrix cores for 6..16 query rows per kv-head (one
-// row tile) and for more (two row tiles: blocks of up to 32 rows, so that
-// G * q in 17..32 reads each page once); -1 when the shape is not covered
-// (the caller then uses another kernel).
+// bf16 stage 1 on the matrix cores (D = 128 or 64) for 6..16 query rows per
+// kv-head (one row tile) and for more (two row tiles: blocks of up to 32
+// rows, so that G * q in 17..32 reads each page once); -1 when the shape is
+// not covered (the caller then uses another kernel).
 int32_t da_split_bf16_mfma(const da_host::SplitCall& call) {
-  if (!call.q_bf16 || call.D != kD) return -1;
+  if (!call.q_bf16 || (call.D != 128 && call.D != 64)) return -1;
   da_host::SplitCall c = call;
   if (c.rows > DA_MAX_ROWS) da_host::row_blocks(c.rows, 2 * DA_MAX_ROWS, c.nrb, c.rb_rows);
   const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block
@@ -401,11 +466,7 @@ int32_t da_split_bf16_mfma(const da_host::SplitCall& call) {
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  if (R <= 16)
-    hipLaunchKernelGGL(split_bf16_mfma_kernel<1>, dim3(c.grid(false)), dim3(kThreads), 0,
-                       c.stream, a);
-  else
-    hipLaunchKernelGGL(split_bf16_mfma_kernel<2>, dim3(c.grid(false)), dim3(kThreads), 0,
-                       c.stream, a);
+  if (c.D == 128) launch<128>(c, a, R);
+  else launch<64>(c, a, R);
   return da_host::launch_status();
 }

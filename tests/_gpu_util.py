@@ -212,14 +212,15 @@ def rows_per_block(w: W.Workload) -> int:
 
 
 def uses_matrix_path(w: W.Workload) -> bool:
-    """Whether stage 1 over this workload runs on the matrix cores (D = 128,
-    bf16 Q): INT4 and INT8 with any number of query rows per kv-head, a dense
-    bf16 cache with 6 or more (rows beyond 16 in blocks of up to 32)."""
+    """Whether stage 1 over this workload runs on the matrix cores (bf16 Q):
+    INT4 and INT8 (D = 128) with any number of query rows per kv-head, a dense
+    bf16 cache (D = 128 or 64) with 6 or more (rows beyond 16 in blocks of up
+    to 32)."""
     rows = w.group * w.q_per_req
-    if w.head_dim != 128 or w.dtype == "fp32":
+    if w.dtype == "fp32":
         return False
     if w.kv in (W.KV_INT4, W.KV_INT8):
-        return True
+        return w.head_dim == 128
     return rows >= 6
 
 

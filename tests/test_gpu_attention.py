@@ -26,6 +26,18 @@ BF16_SMALL = W.BF16_B16.scaled(name="bf16_small_g4", batch=4, length=1500)
 D64_P16 = W.RAGGED_B64.scaled(name="d64_p16_g2", batch=5, num_q_heads=8, num_kv_heads=4,
                               head_dim=64, page_size=16, lengths="list",
                               length_list=(3, 16, 40, 333, 17), pin_max=False)
+# D = 64 with 6 or more query rows per kv-head: the matrix-core path
+D64_G8 = W.RAGGED_B64.scaled(name="d64_g8_p16", batch=8, num_q_heads=32, num_kv_heads=4,
+                             head_dim=64, page_size=16, lengths="list",
+                             length_list=(0, 1, 15, 16, 17, 63, 65, 2047), pin_max=False)
+D64_MTP = W.BF16_B16.scaled(name="d64_mtp4_g4_r16", batch=5, q_per_req=4, causal=True,
+                            head_dim=64, lengths="list", length_list=(1, 3, 4, 70, 900))
+D64_R20 = W.BF16_B16.scaled(name="d64_mtp4_g5_r20_p32", batch=3, num_q_heads=40, q_per_req=4,
+                            causal=True, head_dim=64, page_size=32, lengths="list",
+                            length_list=(2, 100, 1300))
+D64_G6_P128 = W.BF16_B16.scaled(name="d64_g6_p128", batch=4, num_q_heads=12, num_kv_heads=2,
+                                head_dim=64, page_size=128, lengths="list",
+                                length_list=(127, 128, 129, 3000))
 MHA_P32 = W.RAGGED_B64.scaled(name="mha_p32_g1", batch=3, num_q_heads=4, num_kv_heads=4,
                               page_size=32, lengths="list", length_list=(33, 100, 1), pin_max=False)
 MTP_BF16 = W.BF16_B16.scaled(name="mtp4_bf16_g4", batch=5, q_per_req=4, causal=True,
@@ -77,7 +89,8 @@ def test_tiny_fp32_every_split(gpu, S):
     U.check_bf16(U.to_np(out16), out_ref, f"tiny S={S} out bf16")
 
 
-SMALL = [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, MHA_P32, MTP_BF16, MTP_BF16_G2Q3,
+SMALL = [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, D64_G8, D64_MTP, D64_R20, D64_G6_P128,
+         MHA_P32, MTP_BF16, MTP_BF16_G2Q3,
          INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV, INT8_FP32Q, INT8_D64, INT4_SMALL, INT4_Q1,
          INT4_R12, INT4_G8Q2]
 
