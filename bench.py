@@ -115,9 +115,9 @@ def stage1_kernel(w):
         if rows <= 5:
             return "split_bf16_kernel", ["split_bf16.hip", "common.h"]
         return "split_bf16_mfma_kernel", ["split_bf16_mfma.hip", "mfma_util.h", "common.h"]
+    if bf16_q and w.kv == W.KV_INT8:
+        return "split_int8_mfma_kernel", ["split_int8.hip", "mfma_util.h", "common.h"]
     if w.head_dim == 128 and bf16_q:
-        if w.kv == W.KV_INT8:
-            return "split_int8_mfma_kernel", ["split_int8.hip", "mfma_util.h", "common.h"]
         if w.kv == W.KV_INT4:
             return "split_int4_mfma_kernel", ["split_int4.hip", "mfma_util.h", "common.h"]
     return "split_fma_kernel", ["split_fma.hip", "common.h"]
@@ -222,7 +222,11 @@ def kv_name(w):
 
 
 def time_config(step, steps, warmup, torch):
-    """Times `steps` whole steps; returns (ms_per_step, split_ms_avg, merge_ms_avg, meta_ms_avg)."""
+    """Times `steps` whole steps back to back (host clock, synchronised on both
+    sides); then the same number again with events between the three calls for
+    the per-kernel breakdown and percentiles (an event record between steps
+    costs the stream ~12 us here, so the timed steps carry none).  Returns
+    (ms_per_step, split_ms_avg, merge_ms_avg, meta_ms_avg, percentiles)."""
     stream = torch.cuda.current_stream()
 
     def run(ev=None):
@@ -241,13 +245,16 @@ def time_config(step, steps, warmup, torch):
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         run(evs[i])
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     meta = np.mean([e[0].elapsed_time(e[1]) for e in evs])
     splits = [e[1].elapsed_time(e[2]) for e in evs]
     merge = np.mean([e[2].elapsed_time(e[3]) for e in evs])

@@ -108,19 +108,20 @@ __device__ __forceinline__ void write_partials(const float* sm_acc, const float*
   }
 }
 
-// s_waitcnt that leaves `ahead` tiles of LOADS loads each in flight (ahead is
-// wave-uniform, at most MAXA)
+// s_waitcnt that leaves min(ahead, MAXA) tiles of LOADS loads each in flight
+// (ahead is wave-uniform)
 template <int LOADS, int MAXA>
 __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
-  static_assert(MAXA >= 1 && MAXA <= 3, "pipeline depth");
-  if constexpr (MAXA >= 3) {
-    if (ahead >= 3) { wait_vmcnt<3 * LOADS>(); return; }
+  static_assert(MAXA >= 0 && MAXA * LOADS <= 63, "vmcnt range");
+  if constexpr (MAXA == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= MAXA) {
+      wait_vmcnt<MAXA * LOADS>();
+      return;
+    }
+    wait_tiles_ahead<LOADS, MAXA - 1>(ahead);
   }
-  if constexpr (MAXA >= 2) {
-    if (ahead >= 2) { wait_vmcnt<2 * LOADS>(); return; }
-  }
-  if (ahead >= 1) { wait_vmcnt<LOADS>(); return; }
-  wait_vmcnt<0>();
 }
 
 }  // namespace da_mfma

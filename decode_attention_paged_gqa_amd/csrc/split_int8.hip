@@ -1,14 +1,14 @@
 // Stage 1 over an INT8 cache on the matrix cores (LightLLM PR #1549,
-// "Covered decode kernels": INT8 KV flash decode stage 1), for D = 128, bf16
-// Q and G * q query rows per kv-head in blocks of up to 32 (one or two
+// "Covered decode kernels": INT8 KV flash decode stage 1), for D = 128 or 64,
+// bf16 Q and G * q query rows per kv-head in blocks of up to 32 (one or two
 // 16-row tiles per workgroup).  Same contract as
 // decode_attn_split_int8: K = k_pool * k_scale, V = v_pool * v_scale, one
 // fp16 scale per (page, slot, kv-head).
 //
 // One workgroup (4 waves) per (kv-head g, split s, request b); 16-token tiles
 // dealt round-robin to the waves.  Per tile and wave:
-//   S^T[16 tok x 16 rows] = K[16 x 128] . Q^T     4x v_mfma_f32_16x16x32_f16
-//   O^T[128 x 16 rows]   += V^T[128 x 16] . P^T   8x v_mfma_f32_16x16x16_f16
+//   S^T[16 tok x 16 rows] = K[16 x D] . Q^T     D/32 x v_mfma_f32_16x16x32_f16
+//   O^T[D x 16 rows]     += V^T[D x 16] . P^T   D/16 x v_mfma_f32_16x16x16_f16
 // Computing S transposed leaves each lane's four scores (4 tokens, one row)
 // where the PV product wants its B operand.  Lane l = 16*lg + lm.
 //
@@ -24,16 +24,19 @@
 // and P = fp16(p * 2^7) (one rounding; p <= 2^8 under the lazy rescale, so
 // p * 2^7 < 2^15, and the factor keeps small weights out of fp16's
 // subnormal range; it cancels against the same factor in l).
-//   * QK: MFMA kb, lane (lm, lg): token lm, elements 32*lg + 8*kb + 0..7;
-//     the lane reads its 32 contiguous bytes of the row.
-//   * PV: output block bb row m is d = 8*m + bb: lane (lm, lg) reads bytes
-//     8*lm .. 8*lm+7 of each of its four tokens 4*lg + j.
+//   * QK: MFMA kb, lane (lm, lg): token lm, elements (D/4)*lg + 8*kb + 0..7;
+//     the lane reads its D/4 contiguous bytes of the row.
+//   * PV: output block bb row m is d = (D/16)*m + bb: lane (lm, lg) reads
+//     bytes (D/16)*lm .. + D/16 - 1 of each of its four tokens 4*lg + j.
 //
-// Memory pipeline: global_load_lds into a 4-stage per-wave LDS ring (K 2 KB,
-// V 2 KB, scales 256 B per 16 tokens), read back by inline asm after an
-// explicit vmcnt wait.  K and V rows are stored with their eight 16-byte
-// chunks rotated by ((token / 2) mod 8) so that the reads of both operands
-// spread over the LDS banks.  A token's fp16 scale comes in the aligned dword
+// Memory pipeline: global_load_lds into a per-wave LDS ring of 16-token
+// stages (K 16*D bytes, V as many, scales 256 B; 4 stages at D = 128, 8 at
+// D = 64, so that about as many bytes are in flight), read back by inline
+// asm after an explicit vmcnt wait.  At D = 128 a row's eight 16-byte chunks
+// are rotated by ((token / 2) mod 8), at D = 64 its four by ((token / 4) mod
+// 4), and there row 4*lg + j sits in row slot 4*lg + ((j + lg) mod 4): 64-byte
+// rows 256 bytes apart would put the four lane groups' V reads on the same
+// banks, and the rotation spreads the K reads.  A token's fp16 scale comes in the aligned dword
 // that holds it (in bounds: a scale array holds num_pages * page_size * Hkv
 // entries, an even count) and the parity of its index picks the half.
 //
@@ -49,32 +52,80 @@ using namespace da_mfma;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = 4;
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kPScale = 7.0f;  // P (and l) carry a factor 2^7
 constexpr int kMaxSplitPages = 512;
-constexpr int kD = 128;
 
-constexpr int kStageK = 0;
-constexpr int kStageV = 2048;
-constexpr int kStageSc = 4096;  // dwords: [0, 16) K scales, [16, 32) V scales, rest unused
-constexpr int kStageBytes = 4352;
-constexpr int kRingBytes = kWaves * kStages * kStageBytes;  // 68 KB
-
-// LDS position of 16-byte chunk c of token t's row
-__host__ __device__ constexpr int chunk_pos(int t, int c) { return (c + (t >> 1)) & 7; }
-
-struct StageData {
-  u32x4 k[2];    // token lm: bytes 32*lg .. 32*lg+31
-  u32x2 v[4];    // token 4*lg + j: bytes 8*lm .. 8*lm+7
-  u32x4 ks;      // dwords holding the K scales of tokens 4*lg + i
-  u32x4 vs;      // dwords holding the V scales of tokens 4*lg + j
+// Per-head-dim geometry of a tile and of the LDS ring.
+template <int D>
+struct Geo {
+  static_assert(D == 64 || D == 128, "head dim");
+  static constexpr int kChunks = D / 16;     // 16-byte chunks per code row
+  static constexpr int kKb = D / 32;         // QK products per row tile
+  static constexpr int kBlocks = D / 16;     // PV output blocks of 16 d-rows
+  static constexpr int kHw = D / 64;         // V dwords per token and lane
+  static constexpr int kStageK = 0;
+  static constexpr int kStageV = 16 * D;
+  static constexpr int kStageSc = 32 * D;    // dwords: [0, 16) K scales, [16, 32) V scales
+  static constexpr int kStageBytes = 32 * D + 256;
+  static constexpr int kStages = D == 128 ? 4 : 8;
+  static constexpr int kDma = D / 64;        // 1 KB DMA instructions per tensor and tile
+  static constexpr int kLoads = 2 * kDma + 1;  // per tile, with the scales
+  static constexpr int kRingBytes = kWaves * kStages * kStageBytes;  // 68 / 72 KB
+  // rotation of token t's chunks, and the LDS row slot of token t
+  __host__ __device__ static constexpr int rot(int t) { return D == 128 ? t >> 1 : t >> 2; }
+  __host__ __device__ static constexpr int slot(int t) {
+    return D == 128 ? t : (t & ~3) | (((t & 3) + (t >> 2)) & 3);
+  }
+  __host__ __device__ static constexpr int token_of_slot(int r) {
+    return D == 128 ? r : (r & ~3) | (((r & 3) - (r >> 2)) & 3);
+  }
+  // LDS position of 16-byte chunk c of token t's row
+  __host__ __device__ static constexpr int chunk_pos(int t, int c) {
+    return (c + rot(t)) & (kChunks - 1);
+  }
 };
 
+template <int D>
+struct StageData {
+  using VT = std::conditional_t<D == 128, u32x2, uint32_t>;
+  u32x4 k[Geo<D>::kKb / 2];  // token lm: bytes (D/4)*lg .. + D/4 - 1
+  VT v[4];                   // token 4*lg + j: bytes (D/16)*lm .. + D/16 - 1
+  u32x4 ks;                  // dwords holding the K scales of tokens 4*lg + i
+  u32x4 vs;                  // dwords holding the V scales of tokens 4*lg + j
+};
+
+// dword hw of a token's V bytes in a lane
+__device__ __forceinline__ uint32_t vdw(u32x2 v, int hw) { return v[hw]; }
+__device__ __forceinline__ uint32_t vdw(uint32_t v, int) { return v; }
+
 // All reads of one stage plus the next page id, in one asm block (the
-// compiler would otherwise drain the LDS-DMA queue before them).
-__device__ __forceinline__ int32_t read_stage(uint32_t k0, uint32_t k1, uint32_t v0, uint32_t v2,
-                                              uint32_t sc, uint32_t pidaddr, StageData& s) {
+// compiler would otherwise drain the LDS-DMA queue before them).  D = 64:
+// the four V rows sit at lane-dependent slots, so each has its own address.
+__device__ __forceinline__ int32_t read_stage(const uint32_t (&ka)[1], const uint32_t (&va)[4],
+                                              uint32_t sc, uint32_t pidaddr, StageData<64>& s) {
+  int32_t pid;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b32 %1, %9\n\t"
+      "ds_read_b32 %2, %10\n\t"
+      "ds_read_b32 %3, %11\n\t"
+      "ds_read_b32 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %13 offset:64\n\t"
+      "ds_read_b32 %7, %14\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(s.k[0]), "=&v"(s.v[0]), "=&v"(s.v[1]), "=&v"(s.v[2]), "=&v"(s.v[3]),
+        "=&v"(s.ks), "=&v"(s.vs), "=&v"(pid)
+      : "v"(ka[0]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(sc), "v"(pidaddr)
+      : "memory");
+  return __builtin_amdgcn_readfirstlane(pid);
+}
+// D = 128: token 4*lg + 2x + 1 sits one 128-byte row after token 4*lg + 2x,
+// at the same rotation (va[x] addresses the even one).
+__device__ __forceinline__ int32_t read_stage(const uint32_t (&ka)[2], const uint32_t (&va)[2],
+                                              uint32_t sc, uint32_t pidaddr, StageData<128>& s) {
+  const uint32_t k0 = ka[0], k1 = ka[1], v0 = va[0], v2 = va[1];
   int32_t pid;
   asm volatile(
       "ds_read_b128 %0, %9\n\t"
@@ -124,8 +175,12 @@ __device__ __forceinline__ uint32_t code_pair_hi(uint32_t w) {
 
 // NT row tiles of 16 query rows (NT * 16 rows per workgroup): the K and V
 // operands of a tile are formed once and serve every row tile.
-template <int NT>
+template <int D, int NT>
 __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8Args a) {
+  using Gm = Geo<D>;
+  constexpr int kD = D, kKb = Gm::kKb, kBlocks = Gm::kBlocks, kStages = Gm::kStages;
+  constexpr int kStageK = Gm::kStageK, kStageV = Gm::kStageV, kStageSc = Gm::kStageSc;
+  constexpr int kStageBytes = Gm::kStageBytes, kRingBytes = Gm::kRingBytes;
   constexpr int ROWS = 16 * NT;
   constexpr int kEpiBytes = (kWaves * ROWS * kD + 2 * kWaves * ROWS) * 4;
   constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
@@ -164,9 +219,9 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
   stage_pids(min(p0 + kMaxSplitPages, p1));  // the first chunk's, before the query setup
 
 
-  // ---- Q^T operands: row tile rt, row lm, elements 32*lg + 8*kb + e, scaled
-  // by 2^sh, fp16
-  uint32_t qv[NT][4][4];  // [rt][kb][pair]
+  // ---- Q^T operands: row tile rt, row lm, elements (D/4)*lg + 8*kb + e,
+  // scaled by 2^sh, fp16
+  uint32_t qv[NT][kKb][4];  // [rt][kb][pair]
   float rowfac[NT];       // score (log2 units) = s * (rowfac * dot - qoff)
   float qoff[NT];         // rowfac * 128 * 2^-24 * sum of the row's scaled Q
   int tlim[NT];           // tokens t < tlim are visible to this lane's row
@@ -176,11 +231,11 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     const bool live = 16 * rt + lm < nr;
     const int r = r0 + (live ? 16 * rt + lm : 0);  // this lane's query row of the kv-head
     const int i = r / a.G, h = g * a.G + r % a.G;
-    const long long qoff_el = (((long long)b * a.qn + i) * a.Hq + h) * kD + 32 * lg;
-    float qf[4][8];
+    const long long qoff_el = (((long long)b * a.qn + i) * a.Hq + h) * kD + (kD / 4) * lg;
+    float qf[kKb][8];
     const uint4* qp = reinterpret_cast<const uint4*>(a.q + qoff_el);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kKb; ++kb) {
       const uint4 x = qp[kb];
       const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -191,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     }
     float mx = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qf[kb][e]));
     mx = fmaxf(mx, xor16(mx));
@@ -199,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     const int sh = q_row_shift(mx);
     float sum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kKb; ++kb) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         qf[kb][e] = (float)(_Float16)ldexpf(qf[kb][e], sh);
@@ -218,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < kKb; ++kb)
       asm volatile("" : "+v"(qv[rt][kb][0]), "+v"(qv[rt][kb][1]), "+v"(qv[rt][kb][2]),
                    "+v"(qv[rt][kb][3]));
   // tiles below every live row's limit need no masks (rows past the block
@@ -229,25 +284,27 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     tfull = __builtin_amdgcn_readfirstlane(lim_live);
   }
 
-  float4_t acc[NT][8];
+  float4_t acc[NT][kBlocks];
   float m[NT], l[NT];
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
+    for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
     m[rt] = da::kNegInf;
     l[rt] = 0.f;
   }
 
   // ---- addressing
   const long long rowb = (long long)a.slot_stride * kD;  // bytes between slots (codes)
-  // DMA lane i of half h fills LDS chunk i of that half: token 8h + i/8,
-  // position i%8, holding the row's chunk (position - token/2) mod 8
-  uint32_t voff_kv[2];
+  // DMA lane i of 1 KB block h fills LDS chunk i of that block: row slot
+  // (64 / chunks) h + i / chunks, position i % chunks, holding chunk c of the
+  // slot's token with chunk_pos(token, c) = position
+  constexpr int kC = Gm::kChunks;
+  uint32_t voff_kv[Gm::kDma];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int t = 8 * h + (lane >> 3), p = lane & 7;
-    voff_kv[h] = (uint32_t)(t * rowb + 16 * ((p - (t >> 1)) & 7));
+  for (int h = 0; h < Gm::kDma; ++h) {
+    const int t = Gm::token_of_slot((64 / kC) * h + lane / kC), p = lane % kC;
+    voff_kv[h] = (uint32_t)(t * rowb + 16 * ((p - Gm::rot(t)) & (kC - 1)));
   }
   // scale DMA: lanes 0..15 K scale of token i, 16..31 V scale of token i-16,
   // 32..63 repeat lanes 0..31 (their LDS words are not read)
@@ -256,11 +313,21 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
   DA_LDS uint8_t* ring = (DA_LDS uint8_t*)smem + wave * (kStages * kStageBytes);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   const uint32_t pid_lds = (uint32_t)(uintptr_t)(DA_LDS void*)s_pid;
-  const uint32_t rd_k0 = kStageK + 128 * lm + 16 * chunk_pos(lm, 2 * lg);
-  const uint32_t rd_k1 = kStageK + 128 * lm + 16 * chunk_pos(lm, 2 * lg + 1);
-  const uint32_t rd_v0 = kStageV + 128 * (4 * lg) + 16 * chunk_pos(4 * lg, lm >> 1) + 8 * (lm & 1);
-  const uint32_t rd_v2 =
-      kStageV + 128 * (4 * lg + 2) + 16 * chunk_pos(4 * lg + 2, lm >> 1) + 8 * (lm & 1);
+  // K: the lane's D/4 bytes of token lm are chunks (D/64) lg .. + D/64 - 1.
+  // V: bytes (D/16) lm .. of token t are in chunk lm / (16 / (D/16)).
+  constexpr int kRow = D;  // bytes per code row
+  constexpr int kNk = kKb / 2, kNv = D == 128 ? 2 : 4;
+  uint32_t rd_k[kNk], rd_v[kNv];
+#pragma unroll
+  for (int x = 0; x < kNk; ++x)
+    rd_k[x] = kStageK + kRow * Gm::slot(lm) + 16 * Gm::chunk_pos(lm, kNk * lg + x);
+#pragma unroll
+  for (int x = 0; x < kNv; ++x) {
+    constexpr int kVb = D / 16;            // V bytes per token and lane
+    constexpr int kPer = 16 / kVb;         // lanes per chunk
+    const int t = D == 128 ? 4 * lg + 2 * x : 4 * lg + x;
+    rd_v[x] = kStageV + kRow * Gm::slot(t) + 16 * Gm::chunk_pos(t, lm / kPer) + kVb * (lm % kPer);
+  }
   const uint32_t rd_sc = kStageSc + 16 * lg;
 
   auto tile_base = [&](int j) { return c0 + ((wave + kWaves * j) << 4); };
@@ -272,12 +339,12 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
                            (long long)(tile_base(j) & (ps - 1)) * a.slot_stride + head_row;
     DA_LDS uint8_t* st = ring + (j % kStages) * kStageBytes;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < Gm::kDma; ++h)
       __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * kD + voff_kv[h]),
                                        (DA_LDS void*)(st + kStageK + 1024 * h), 16, 0,
                                        da::kStreamPolicy);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < Gm::kDma; ++h)
       __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * kD + voff_kv[h]),
                                        (DA_LDS void*)(st + kStageV + 1024 * h), 16, 0,
                                        da::kStreamPolicy);
@@ -294,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 #pragma unroll
   for (int i = 0; i < 4; ++i) sc_shift[i] = ((i * a.slot_stride + g * a.head_stride) & 1) << 4;
 
-  auto compute = [&](int j, const StageData& sd, auto masked_tag) {
+  auto compute = [&](int j, const StageData<D>& sd, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     // ---- dot[rt][i] = 2^-24 * sum_d q'_d (b_d + 128) for token 4*lg + i, row lm
     // of tile rt
@@ -302,12 +369,11 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) dot[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
     {
-      const uint32_t kw[8] = {sd.k[0][0] ^ 0x80808080u, sd.k[0][1] ^ 0x80808080u,
-                              sd.k[0][2] ^ 0x80808080u, sd.k[0][3] ^ 0x80808080u,
-                              sd.k[1][0] ^ 0x80808080u, sd.k[1][1] ^ 0x80808080u,
-                              sd.k[1][2] ^ 0x80808080u, sd.k[1][3] ^ 0x80808080u};
+      uint32_t kw[2 * kKb];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int x = 0; x < 2 * kKb; ++x) kw[x] = sd.k[x >> 2][x & 3] ^ 0x80808080u;
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb) {
         const half2_t c0 = as_h2(code_pair_lo(kw[2 * kb])), c1 = as_h2(code_pair_hi(kw[2 * kb]));
         const half2_t c2 = as_h2(code_pair_lo(kw[2 * kb + 1]));
         const half2_t c3 = as_h2(code_pair_hi(kw[2 * kb + 1]));
@@ -353,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
         const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m[rt] - mn);
         l[rt] *= al;
 #pragma unroll
-        for (int bb = 0; bb < 8; ++bb) acc[rt][bb] *= al;
+        for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] *= al;
         m[rt] = mn;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -368,21 +434,22 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
       pb[rt] = half4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
     }
 
-    // ---- V operand: tokens 4*lg + j, d = 8*lm + block.  Rows past the
+    // ---- V operand: tokens 4*lg + j, d = (D/16)*lm + block.  Rows past the
     // split end may hold anything (even NaN scales): code 0, scale 0 there.
-    uint32_t vw[4][2], vs[4];
+    constexpr int kHw = Gm::kHw;
+    uint32_t vw[4][kHw], vs[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const bool ok = !MASKED || tb + jj < t1;
-      vw[jj][0] = ok ? sd.v[jj][0] : 0u;
-      vw[jj][1] = ok ? sd.v[jj][1] : 0u;
+#pragma unroll
+      for (int hw = 0; hw < kHw; ++hw) vw[jj][hw] = ok ? vdw(sd.v[jj], hw) : 0u;
       vs[jj] = ok ? vsc[jj] : 0u;
     }
     const half2_t s01 = as_h2(__builtin_amdgcn_perm(vs[1], vs[0], 0x05040100u));
     const half2_t s23 = as_h2(__builtin_amdgcn_perm(vs[3], vs[2], 0x05040100u));
     const half2_t k1152 = {1152, 1152};
 #pragma unroll
-    for (int hw = 0; hw < 2; ++hw) {
+    for (int hw = 0; hw < kHw; ++hw) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int bb = 4 * hw + kk;
@@ -401,15 +468,17 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     }
   };
 
-  auto step = [&](int j, StageData& sd) {
-    const int ahead = min(kStages - 2, nmine - 1 - j);
-    if (ahead >= 2) wait_vmcnt<10>();
-    else if (ahead == 1) wait_vmcnt<5>();
-    else wait_vmcnt<0>();
+  auto step = [&](int j, StageData<D>& sd) {
+    // the tiles after j issued so far may stay in flight
+    wait_tiles_ahead<Gm::kLoads, kStages - 2>(min(kStages - 2, nmine - 1 - j));
     const int jn = min(j + kStages - 1, nmine - 1);
     const uint32_t base = ring_lds + (j % kStages) * kStageBytes;
-    const int pid = read_stage(base + rd_k0, base + rd_k1, base + rd_v0, base + rd_v2,
-                               base + rd_sc, pid_addr(jn), sd);
+    uint32_t ka[kNk], va[kNv];
+#pragma unroll
+    for (int x = 0; x < kNk; ++x) ka[x] = base + rd_k[x];
+#pragma unroll
+    for (int x = 0; x < kNv; ++x) va[x] = base + rd_v[x];
+    const int pid = read_stage(ka, va, base + rd_sc, pid_addr(jn), sd);
     if (j + kStages - 1 < nmine) issue(j + kStages - 1, pid);
   };
   for (; pc < p1; pc += kMaxSplitPages) {
@@ -429,12 +498,12 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     for (int u = 0; u < kStages - 1; ++u)
       if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
     for (int j = 0; j < jfull; ++j) {
-      StageData sd;
+      StageData<D> sd;
       step(j, sd);
       compute(j, sd, std::false_type{});
     }
     for (int j = jfull; j < nmine; ++j) {
-      StageData sd;
+      StageData<D> sd;
       step(j, sd);
       compute(j, sd, std::true_type{});
     }
@@ -451,27 +520,38 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     l[rt] += xor32(l[rt]);
     const int row = wave * ROWS + 16 * rt + lm;
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
+    for (int bb = 0; bb < kBlocks; ++bb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_acc[row * kD + 8 * (4 * lg + i) + bb] = acc[rt][bb][i];
+      for (int i = 0; i < 4; ++i)
+        sm_acc[row * kD + kBlocks * (4 * lg + i) + bb] = acc[rt][bb][i];
     if (lg == 0) {
       sm_m[row] = m[rt];
       sm_l[row] = l[rt];
     }
   }
   __syncthreads();
-  write_partials<kWaves, ROWS>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S, s,
-                               kPScale, a.o, a.lse);
+  write_partials<kWaves, ROWS, D>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S,
+                                  s, kPScale, a.o, a.lse);
+}
+
+template <int D>
+void launch(const da_host::SplitCall& c, const Int8Args& a, int R) {
+  if (R <= 16)
+    hipLaunchKernelGGL((split_int8_mfma_kernel<D, 1>), dim3(c.grid(true)), dim3(kThreads), 0,
+                       c.stream, a);
+  else
+    hipLaunchKernelGGL((split_int8_mfma_kernel<D, 2>), dim3(c.grid(true)), dim3(kThreads), 0,
+                       c.stream, a);
 }
 
 }  // namespace
 
-// INT8 stage 1 on the matrix cores, one row tile (up to 16 query rows per
-// kv-head) or two (blocks of up to 32 rows, so that G * q in 17..32 forms
-// each tile's operands once); -1 when the shape is not covered (the caller
-// then uses the vector-ALU kernel).
+// INT8 stage 1 on the matrix cores (D = 128 or 64), one row tile (up to 16
+// query rows per kv-head) or two (blocks of up to 32 rows, so that G * q in
+// 17..32 forms each tile's operands once); -1 when the shape is not covered
+// (the caller then uses the vector-ALU kernel).
 int32_t da_split_int8_mfma(const da_host::SplitCall& call) {
-  if (!call.q_bf16 || call.D != kD) return -1;
+  if (!call.q_bf16 || (call.D != 128 && call.D != 64)) return -1;
   da_host::SplitCall c = call;
   if (c.rows > DA_MAX_ROWS) da_host::row_blocks(c.rows, 2 * DA_MAX_ROWS, c.nrb, c.rb_rows);
   const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block
@@ -485,11 +565,7 @@ int32_t da_split_int8_mfma(const da_host::SplitCall& call) {
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  if (R <= 16)
-    hipLaunchKernelGGL(split_int8_mfma_kernel<1>, dim3(c.grid(true)), dim3(kThreads), 0,
-                       c.stream, a);
-  else
-    hipLaunchKernelGGL(split_int8_mfma_kernel<2>, dim3(c.grid(true)), dim3(kThreads), 0,
-                       c.stream, a);
+  if (c.D == 128) launch<128>(c, a, R);
+  else launch<64>(c, a, R);
   return da_host::launch_status();
 }

@@ -56,6 +56,12 @@ INT8_FP32Q = W.INT8_B32.scaled(name="int8_fp32q_small", batch=3, dtype="fp32", l
                                length_list=(1, 100, 700))
 INT8_D64 = W.INT8_B32.scaled(name="int8_d64_small", batch=3, head_dim=64, lengths="list",
                              length_list=(7, 64, 1000))
+INT8_D64_MTP = W.INT8_B32.scaled(name="int8_d64_mtp4_r16_p16", batch=4, q_per_req=4, causal=True,
+                                 head_dim=64, page_size=16, lengths="list",
+                                 length_list=(1, 17, 64, 1500))
+INT8_D64_R20 = W.INT8_B32.scaled(name="int8_d64_g5_mtp4_r20_p128", batch=3, num_q_heads=40,
+                                 q_per_req=4, causal=True, head_dim=64, page_size=128,
+                                 lengths="list", length_list=(3, 129, 2100))
 INT4_SMALL = W.INT4_MTP_B64.scaled(name="int4_mtp_small", batch=5, lengths="list",
                                    length_list=(1, 4, 65, 777, 2000))
 INT4_Q1 = W.INT4_MTP_B64.scaled(name="int4_q1_small", batch=4, q_per_req=1, causal=False,
@@ -91,7 +97,8 @@ def test_tiny_fp32_every_split(gpu, S):
 
 SMALL = [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, D64_G8, D64_MTP, D64_R20, D64_G6_P128,
          MHA_P32, MTP_BF16, MTP_BF16_G2Q3,
-         INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV, INT8_FP32Q, INT8_D64, INT4_SMALL, INT4_Q1,
+         INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV, INT8_FP32Q, INT8_D64, INT8_D64_MTP, INT8_D64_R20,
+         INT4_SMALL, INT4_Q1,
          INT4_R12, INT4_G8Q2]
 
 
