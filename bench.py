@@ -117,9 +117,8 @@ def stage1_kernel(w):
         return "split_bf16_mfma_kernel", ["split_bf16_mfma.hip", "mfma_util.h", "common.h"]
     if bf16_q and w.kv == W.KV_INT8:
         return "split_int8_mfma_kernel", ["split_int8.hip", "mfma_util.h", "common.h"]
-    if w.head_dim == 128 and bf16_q:
-        if w.kv == W.KV_INT4:
-            return "split_int4_mfma_kernel", ["split_int4.hip", "mfma_util.h", "common.h"]
+    if bf16_q and w.kv == W.KV_INT4:
+        return "split_int4_mfma_kernel", ["split_int4.hip", "mfma_util.h", "common.h"]
     return "split_fma_kernel", ["split_fma.hip", "common.h"]
 
 

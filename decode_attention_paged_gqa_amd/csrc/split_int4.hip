@@ -1,5 +1,5 @@
-// Stage 1 over an INT4 cache on the matrix cores, for any number of query
-// rows per kv-head (G*q, in blocks of up to 32: one or two 16-row tiles per
+// Stage 1 over an INT4 cache on the matrix cores, for D = 128 or 64 and any
+// number of query rows per kv-head (G*q, in blocks of up to 32: one or two 16-row tiles per
 // workgroup; a partly filled tile still beats the vector ALU, whose 4-bit
 // expansion cannot keep pace with the memory stream; e.g. the MTP verify
 // batches of LightLLM
@@ -9,8 +9,8 @@
 //
 // One workgroup (4 waves) per (kv-head g, split s, request b); 16-token
 // tiles dealt round-robin to the waves.  Per tile and wave:
-//   S^T[16 tok x 16 rows] = K[16 x 128] . Q^T   4x v_mfma_f32_16x16x32_f16
-//   O^T[128 x 16 rows]   += V^T[128 x 16] . P^T 8x v_mfma_f32_16x16x16_f16
+//   S^T[16 tok x 16 rows] = K[16 x D] . Q^T   D/32 x v_mfma_f32_16x16x32_f16
+//   O^T[D x 16 rows]     += V^T[D x 16] . P^T D/16 x v_mfma_f32_16x16x16_f16
 // Computing S transposed puts each lane's four scores (4 tokens, one row)
 // exactly where the PV product wants its B operand, so P never moves
 // between lanes.  Lane l = 16*lg + lm: QK row (token) lm, PV row (d) lm.
@@ -28,16 +28,18 @@
 // z: the scale terms s_g * dot_g on the vector ALU (one mixed-precision fma
 // each), the zero-point terms -sum_g (s_g z_g) sum_g(q) as one fp32 matrix
 // product [16 tokens x 4 groups] . [4 groups x 16 rows] (s_g z_g is exact in
-// fp32), so any fp16 zero point is taken exactly.
+// fp32; at D = 64 groups 2 and 3 are zero), so any fp16 zero point is taken
+// exactly.
 //   * QK: MFMA kb is group kb.  Lane (lm, lg) supplies token lm's dword lg
 //     of that group (elements 32*kb + 8*lg + 0..7); k-slots 2x, 2x+1 are
 //     elements x and x+4 of the dword (nibble x of its two halves).  Pairs
 //     0 and 2 are masked into bits 0..3 (n * 2^-24); pairs 1 and 3 are
 //     masked where they lie, bits 4..7 (16 n * 2^-24, still exact), and
 //     their Q elements are divided by 16 instead.
-//   * PV: output block b row m is d = 8*m + b: lane (lm, lg) reads, for its
-//     four tokens 4*lg+j, the dword lm of each row (d = 8*lm .. 8*lm+7),
-//     all in group lm/4.  V^T is dequantised to fp16 as n*s - z*s (one fma
+//   * PV: output block b row m is d = (D/16)*m + b: lane (lm, lg) reads, for
+//     its four tokens 4*lg+j, elements (D/16)*lm .. + D/16 - 1 of each row
+//     (D = 128: dword lm, in group lm/4; D = 64: half lm%2 of dword lm/2, in
+//     group lm/8).  V^T is dequantised to fp16 as n*s - z*s (one fma
 //     per element pair after the exact n; -z*s rounded once per token; a
 //     high nibble is taken in place as 16 n and meets s / 16), and
 //     P enters as fp16(p * 2^7) (p <= 2^8 under the lazy rescale below, so
@@ -45,12 +47,17 @@
 //     range and cancels against the same factor in l): these two roundings
 //     are the only ones in the product.
 //
-// Memory pipeline as in the bf16 kernel: global_load_lds into a 4-stage
-// per-wave LDS ring (K 1 KB, V 1 KB, the two scale/zero tiles 256 B each
-// per 16 tokens), read back by inline asm after an explicit vmcnt wait.
-// The K and V tiles are stored with their 16-byte chunks rotated by
+// Memory pipeline as in the bf16 kernel: global_load_lds into a per-wave LDS
+// ring, read back by inline asm after an explicit vmcnt wait.  D = 128: 4
+// stages of K 1 KB, V 1 KB and the two scale/zero tiles of 256 B each per 16
+// tokens; the K and V tiles are stored with their 16-byte chunks rotated by
 // (token / 4) so that the dword reads of both operands (K: one group of
-// token lm; V: dword lm of token 4*lg + j) hit distinct banks.
+// token lm; V: dword lm of token 4*lg + j) hit distinct banks.  D = 64: 8
+// stages of K 512 B, V 512 B (one DMA: lanes 0..31 fetch K, 32..63 V) and the
+// scale/zero tiles of 128 B each (one DMA likewise), as many bytes in flight;
+// the 32-byte rows are stored transposed (token t in row slot 4 (t % 4) +
+// t / 4) with their two chunks rotated by ((t / 2) mod 2), which again puts
+// both operand reads on distinct banks.
 //
 // Softmax: one running reference m per query row, uniform over the lanes
 // holding that row; raised lazily when a score exceeds m + 8 (log2 units).
@@ -64,26 +71,87 @@ using namespace da_mfma;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = 4;
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kPScale = 7.0f;  // P (and l) carry a factor 2^7
 constexpr int kMaxSplitPages = 512;
-constexpr int kD = 128;
 
-constexpr int kStageK = 0;
-constexpr int kStageV = 1024;
-constexpr int kStageKsz = 2048;
-constexpr int kStageVsz = 2304;
-constexpr int kStageBytes = 2560;
-constexpr int kRingBytes = kWaves * kStages * kStageBytes;           // 40 KB
+// Per-head-dim geometry of a tile and of the LDS ring.
+template <int D>
+struct Geo {
+  static_assert(D == 64 || D == 128, "head dim");
+  static constexpr int kGroups = D / 32;     // quantisation groups per row
+  static constexpr int kBlocks = D / 16;     // PV output blocks of 16 d-rows
+  static constexpr int kRowBytes = D / 2;    // code bytes per row
+  static constexpr int kSzBytes = 4 * kGroups;  // (scale, zero) bytes per row
+  static constexpr int kStageK = 0;
+  static constexpr int kStageV = 16 * kRowBytes;
+  static constexpr int kStageKsz = 32 * kRowBytes;
+  static constexpr int kStageVsz = kStageKsz + 16 * kSzBytes;
+  static constexpr int kStageBytes = kStageVsz + 16 * kSzBytes;  // 2560 / 1280
+  static constexpr int kStages = D == 128 ? 4 : 8;
+  static constexpr int kLoads = D == 128 ? 4 : 2;  // DMA instructions per tile
+  static constexpr int kRingBytes = kWaves * kStages * kStageBytes;  // 40 KB
+  // row slot of token t in a code tile, and the rotation of its chunks
+  __host__ __device__ static constexpr int slot(int t) {
+    return D == 128 ? t : 4 * (t & 3) + (t >> 2);  // an involution at D = 64
+  }
+  __host__ __device__ static constexpr int rot(int t) { return D == 128 ? t >> 2 : (t >> 1) & 1; }
+};
 
-struct StageData {
+template <int D>
+struct StageData;
+template <>
+struct StageData<128> {
   uint32_t k[4];   // token lm, group kb: dword lg (elements 32*kb + 8*lg + 0..7)
   uint32_t v[4];   // dword lm of tokens 4*lg + j
   u32x4 ksz[4];    // (scale, zero) of token 4*lg + i, groups 0..3
   uint32_t vsz[4]; // (scale, zero) of token 4*lg + j, group lm/4
   uint32_t kz;     // (scale, zero) of token lm, group lg
 };
+template <>
+struct StageData<64> {
+  uint32_t k[2];   // token lm, group kb: dword lg (elements 32*kb + 8*lg + 0..7)
+  uint32_t v[4];   // dword lm/2 of tokens 4*lg + j
+  u32x2 ksz[4];    // (scale, zero) of token 4*lg + i, groups 0..1
+  uint32_t vsz[4]; // (scale, zero) of token 4*lg + j, group lm/8
+  uint32_t kz;     // (scale, zero) of token lm, group lg & 1
+};
+
+// D = 64: all reads of one stage (at a lane-specific address, the stage
+// offset already added) plus the next page id.  V rows of tokens 4*lg + 2x
+// and 4*lg + 2x + 1 sit 128 bytes apart (va[x] addresses the first).
+__device__ __forceinline__ int32_t read_stage64(const uint32_t (&kaddr)[2],
+                                                const uint32_t (&vaddr)[2], uint32_t kszaddr,
+                                                uint32_t vszaddr, uint32_t kzaddr,
+                                                uint32_t pidaddr, StageData<64>& s) {
+  int32_t pid;
+  asm volatile(
+      "ds_read_b32 %0, %16\n\t"
+      "ds_read_b32 %1, %17\n\t"
+      "ds_read_b32 %2, %18\n\t"
+      "ds_read_b32 %3, %18 offset:128\n\t"
+      "ds_read_b32 %4, %19\n\t"
+      "ds_read_b32 %5, %19 offset:128\n\t"
+      "ds_read_b64 %6, %20\n\t"
+      "ds_read_b64 %7, %20 offset:8\n\t"
+      "ds_read_b64 %8, %20 offset:16\n\t"
+      "ds_read_b64 %9, %20 offset:24\n\t"
+      "ds_read_b32 %10, %21\n\t"
+      "ds_read_b32 %11, %21 offset:8\n\t"
+      "ds_read_b32 %12, %21 offset:16\n\t"
+      "ds_read_b32 %13, %21 offset:24\n\t"
+      "ds_read_b32 %14, %22\n\t"
+      "ds_read_b32 %15, %23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(s.k[0]), "=&v"(s.k[1]), "=&v"(s.v[0]), "=&v"(s.v[1]), "=&v"(s.v[2]),
+        "=&v"(s.v[3]), "=&v"(s.ksz[0]), "=&v"(s.ksz[1]), "=&v"(s.ksz[2]), "=&v"(s.ksz[3]),
+        "=&v"(s.vsz[0]), "=&v"(s.vsz[1]), "=&v"(s.vsz[2]), "=&v"(s.vsz[3]), "=&v"(s.kz),
+        "=&v"(pid)
+      : "v"(kaddr[0]), "v"(kaddr[1]), "v"(vaddr[0]), "v"(vaddr[1]), "v"(kszaddr), "v"(vszaddr),
+        "v"(kzaddr), "v"(pidaddr)
+      : "memory");
+  return __builtin_amdgcn_readfirstlane(pid);
+}
 
 // All reads of ring stage ST (its byte offset, a constant folded into the
 // instructions' offset fields) plus the next page id, in one asm block (the
@@ -92,7 +160,8 @@ struct StageData {
 template <int ST>
 __device__ __forceinline__ int32_t read_stage(const uint32_t (&kaddr)[4], uint32_t vaddr,
                                               uint32_t kszaddr, uint32_t vszaddr,
-                                              uint32_t kzaddr, uint32_t pidaddr, StageData& s) {
+                                              uint32_t kzaddr, uint32_t pidaddr,
+                                              StageData<128>& s) {
   int32_t pid;
   asm volatile(
       "ds_read_b32 %0, %18 offset:%27\n\t"
@@ -151,8 +220,13 @@ struct MfmaArgs {
 // default in the token-major one, where a 64-byte code row (and a 16-byte
 // scale row) shares its line with the neighbouring kv-heads' rows, which
 // their workgroups read from L2 moments later.
-template <int NT, int POLICY>
+template <int D, int NT, int POLICY>
 __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_kernel(const MfmaArgs a) {
+  using Gm = Geo<D>;
+  constexpr int kD = D, kGroups = Gm::kGroups, kBlocks = Gm::kBlocks, kStages = Gm::kStages;
+  constexpr int kStageK = Gm::kStageK, kStageV = Gm::kStageV, kStageKsz = Gm::kStageKsz;
+  constexpr int kStageVsz = Gm::kStageVsz, kStageBytes = Gm::kStageBytes;
+  constexpr int kRingBytes = Gm::kRingBytes;
   constexpr int ROWS = 16 * NT;
   constexpr int kEpiBytes = (kWaves * ROWS * kD + 2 * kWaves * ROWS) * 4;
   constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
@@ -193,7 +267,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
 
   // ---- Q^T operands (row tile rt, row lm): for MFMA kb, elements
   // 32*kb + 8*lg + e, e = 0..7, scaled by 2^sh and held in fp16
-  uint32_t qv[NT][4][4];  // [rt][kb][register]
+  uint32_t qv[NT][kGroups][4];  // [rt][kb][register]
   float rowfac[NT];       // score (log2 units) = rowfac * sum_g s_g (dot_g - z_g qsum_g)
   float qsum_lg[NT];      // qsum of group lg: operand of the zero-point product
   int tlim[NT];           // tokens t < tlim are visible to this lane's row
@@ -202,13 +276,13 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   for (int rt = 0; rt < NT; ++rt) {
     const bool live = 16 * rt + lm < nr;
     const int r = r0 + (live ? 16 * rt + lm : 0);  // this lane's query row of the kv-head
-    float qsum[4];  // 2^-24 * sum of the row's scaled fp16 Q over group kb
+    float qsum[kGroups];  // 2^-24 * sum of the row's scaled fp16 Q over group kb
     const int i = r / a.G, h = g * a.G + r % a.G;
     const long long qoff = (((long long)b * a.qn + i) * a.Hq + h) * kD + 8 * lg;
-    float qf[4][8];
+    float qf[kGroups][8];
     const uint4* qp = reinterpret_cast<const uint4*>(a.q + qoff);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kGroups; ++kb) {
       const uint4 x = qp[4 * kb];  // 8 bf16 at element 32*kb + 8*lg
       const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -219,14 +293,14 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     }
     float mx = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < kGroups; ++kb)
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qf[kb][e]));
     mx = fmaxf(mx, xor16(mx));
     mx = fmaxf(mx, xor32(mx));
     const int sh = q_row_shift(mx);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kGroups; ++kb) {
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -246,7 +320,8 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     rowfac[rt] = ldexpf(a.scale_log2, 24 - sh);
     qsum_lg[rt] = qsum[0];
 #pragma unroll
-    for (int kb = 1; kb < 4; ++kb) qsum_lg[rt] = lg == kb ? qsum[kb] : qsum_lg[rt];
+    for (int kb = 1; kb < kGroups; ++kb) qsum_lg[rt] = lg == kb ? qsum[kb] : qsum_lg[rt];
+    if (kGroups < 4 && lg >= kGroups) qsum_lg[rt] = 0.f;  // no such group
     tlim[rt] = live ? min(t1, a.causal ? L - (a.qn - 1 - i) : L) : 0;
     if (live) lim_live = min(lim_live, tlim[rt]);
   }
@@ -258,12 +333,12 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     tfull = __builtin_amdgcn_readfirstlane(lim_live);
   }
 
-  float4_t acc[NT][8];
+  float4_t acc[NT][kBlocks];
   float m[NT], l[NT];
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
+    for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
     m[rt] = da::kNegInf;
     l[rt] = 0.f;
   }
@@ -273,22 +348,57 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   asm volatile("" : "+v"(magic));
 
   // ---- addressing
-  const long long rowb = (long long)a.slot_stride * (kD / 2);  // bytes between slots (codes)
-  const long long szb = (long long)a.slot_stride * 16;         // (scale/zero)
-  // DMA lane i fills LDS chunk i (token i/4, position i%4) with the token's
-  // 16-byte group (position - token/4) mod 4
-  const uint32_t voff_kv = (uint32_t)((lane >> 2) * rowb + 16 * (((lane & 3) - (lane >> 4)) & 3));
-  const uint32_t voff_sz = (uint32_t)((lane >> 2) * szb + 4 * (lane & 3));
+  constexpr int kRow = Gm::kRowBytes, kSz = Gm::kSzBytes;
+  const long long rowb = (long long)a.slot_stride * kRow;  // bytes between slots (codes)
+  const long long szb = (long long)a.slot_stride * kSz;    // (scale/zero)
+  uint32_t voff_kv, voff_sz;
+  const uint8_t* code_base = a.k;  // the tensor this lane's code DMA reads
+  const uint8_t* sz_base = a.ksz;
+  if constexpr (D == 128) {
+    // DMA lane i fills LDS chunk i (token i/4, position i%4) with the token's
+    // 16-byte group (position - token/4) mod 4
+    voff_kv = (uint32_t)((lane >> 2) * rowb + 16 * (((lane & 3) - (lane >> 4)) & 3));
+    voff_sz = (uint32_t)((lane >> 2) * szb + 4 * (lane & 3));
+  } else {
+    // one DMA per tile for the codes: lanes 0..31 fill the K tile, 32..63
+    // the V tile; lane i fills chunk i % 32 of it (row slot r = (i % 32) / 2,
+    // position i % 2) with chunk (position - rot) mod 2 of token slot(r);
+    // likewise one for the (scale, zero) rows, token (i % 32) / 2, group i % 2
+    const int li = lane & 31, r = li >> 1, t = Gm::slot(r);
+    voff_kv = (uint32_t)(t * rowb + 16 * (((li & 1) - Gm::rot(t)) & 1));
+    voff_sz = (uint32_t)((li >> 1) * szb + 4 * (li & 1));
+    if (lane >= 32) {
+      code_base = a.v;
+      sz_base = a.vsz;
+    }
+  }
   DA_LDS uint8_t* ring = (DA_LDS uint8_t*)smem + wave * (kStages * kStageBytes);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   const uint32_t pid_lds = (uint32_t)(uintptr_t)(DA_LDS void*)s_pid;
-  uint32_t rd_k[4];
+  uint32_t rd_k[kGroups];
+  uint32_t rd_v[D == 128 ? 1 : 2];
+  uint32_t rd_ksz, rd_kz, rd_vsz;
+  if constexpr (D == 128) {
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) rd_k[kb] = kStageK + 64 * lm + 16 * ((kb + (lm >> 2)) & 3) + 4 * lg;
-  const uint32_t rd_v = kStageV + 64 * (4 * lg) + 16 * (((lm >> 2) + lg) & 3) + 4 * (lm & 3);
-  const uint32_t rd_ksz = kStageKsz + 64 * lg;
-  const uint32_t rd_kz = kStageKsz + 16 * lm + 4 * lg;
-  const uint32_t rd_vsz = kStageVsz + 16 * (4 * lg) + 4 * (lm >> 2);
+    for (int kb = 0; kb < 4; ++kb) rd_k[kb] = kStageK + 64 * lm + 16 * ((kb + (lm >> 2)) & 3) + 4 * lg;
+    rd_v[0] = kStageV + 64 * (4 * lg) + 16 * (((lm >> 2) + lg) & 3) + 4 * (lm & 3);
+    rd_ksz = kStageKsz + 64 * lg;
+    rd_kz = kStageKsz + 16 * lm + 4 * lg;
+    rd_vsz = kStageVsz + 16 * (4 * lg) + 4 * (lm >> 2);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      rd_k[kb] = kStageK + kRow * Gm::slot(lm) + 16 * ((kb + Gm::rot(lm)) & 1) + 4 * lg;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {  // tokens 4*lg + 2x (+1 at 128 bytes: slot + 4)
+      const int t = 4 * lg + 2 * x;
+      rd_v[x] = kStageV + kRow * Gm::slot(t) + 16 * (((lm >> 3) + Gm::rot(t)) & 1) +
+                4 * ((lm >> 1) & 3);
+    }
+    rd_ksz = kStageKsz + 32 * lg;
+    rd_kz = kStageKsz + 8 * lm + 4 * (lg & 1);
+    rd_vsz = kStageVsz + 32 * lg + 4 * (lm >> 3);
+  }
 
   auto tile_base = [&](int j) { return c0 + ((wave + kWaves * j) << 4); };
   auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - pc); };
@@ -297,31 +407,40 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     const long long row0 = (long long)pid * ps * a.Hkv + (long long)(tb & (ps - 1)) * a.slot_stride +
                            (long long)g * a.head_stride;
     DA_LDS uint8_t* st = ring + (j % kStages) * kStageBytes;
-    __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * (kD / 2) + voff_kv),
-                                     (DA_LDS void*)(st + kStageK), 16, 0, POLICY);
-    __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * (kD / 2) + voff_kv),
-                                     (DA_LDS void*)(st + kStageV), 16, 0, POLICY);
-    __builtin_amdgcn_global_load_lds((const void*)(a.ksz + row0 * 16 + voff_sz),
-                                     (DA_LDS void*)(st + kStageKsz), 4, 0, POLICY);
-    __builtin_amdgcn_global_load_lds((const void*)(a.vsz + row0 * 16 + voff_sz),
-                                     (DA_LDS void*)(st + kStageVsz), 4, 0, POLICY);
+    if constexpr (D == 128) {
+      __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * (kD / 2) + voff_kv),
+                                       (DA_LDS void*)(st + kStageK), 16, 0, POLICY);
+      __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * (kD / 2) + voff_kv),
+                                       (DA_LDS void*)(st + kStageV), 16, 0, POLICY);
+      __builtin_amdgcn_global_load_lds((const void*)(a.ksz + row0 * 16 + voff_sz),
+                                       (DA_LDS void*)(st + kStageKsz), 4, 0, POLICY);
+      __builtin_amdgcn_global_load_lds((const void*)(a.vsz + row0 * 16 + voff_sz),
+                                       (DA_LDS void*)(st + kStageVsz), 4, 0, POLICY);
+    } else {
+      __builtin_amdgcn_global_load_lds((const void*)(code_base + row0 * kRow + voff_kv),
+                                       (DA_LDS void*)(st + kStageK), 16, 0, POLICY);
+      __builtin_amdgcn_global_load_lds((const void*)(sz_base + row0 * kSz + voff_sz),
+                                       (DA_LDS void*)(st + kStageKsz), 4, 0, POLICY);
+    }
   };
 
-  auto compute = [&](int j, const StageData& sd, auto masked_tag) {
+  auto compute = [&](int j, const StageData<D>& sd, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     // ---- K operands, shared by the row tiles: elements (x, x+4) are nibble x
     // of the dword's two halves; pairs 1 and 3 are masked in place
     // (16 n * 2^-24, exact), their Q is / 16
-    half8_t ka[4];
+    half8_t ka[kGroups];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kGroups; ++kb) {
       const uint32_t w = sd.k[kb], wh = w >> 8;
       const half2_t k0 = as_h2(w & 0x000F000Fu), k1 = as_h2(w & 0x00F000F0u);
       const half2_t k2 = as_h2(wh & 0x000F000Fu), k3 = as_h2(wh & 0x00F000F0u);
       ka[kb] = half8_t{k0[0], k0[1], k1[0], k1[1], k2[0], k2[1], k3[0], k3[1]};
     }
     // -s z of token lm, group lg: the A operand of the zero-point product
-    const float nsz = -(h_lo(sd.kz) * h_hi(sd.kz));
+    // (0, as is its B operand qsum_lg, for a group past D)
+    float nsz = -(h_lo(sd.kz) * h_hi(sd.kz));
+    if (kGroups < 4 && lg >= kGroups) nsz = 0.f;
     const int tb = tile_base(j) + 4 * lg;
     half4_t pb[NT];
 #pragma unroll
@@ -332,9 +451,9 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
                                                               float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       // ---- per-group dot products of the raw codes: dot[kb][i] =
       // 2^-24 * sum_{d in group kb} q'_d n_d for token 4*lg + i, row lm
-      float4_t dot[4];
+      float4_t dot[kGroups];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < kGroups; ++kb) {
         const half2_t q0 = as_h2(qv[rt][kb][0]), q1 = as_h2(qv[rt][kb][1]);
         const half2_t q2 = as_h2(qv[rt][kb][2]), q3 = as_h2(qv[rt][kb][3]);
         const half8_t qb = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
@@ -344,10 +463,9 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
       float4_t st;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t sz[4] = {sd.ksz[i][0], sd.ksz[i][1], sd.ksz[i][2], sd.ksz[i][3]};
         float acc_s = zt[i];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc_s = fmaf(h_lo(sz[kb]), dot[kb][i], acc_s);
+        for (int kb = 0; kb < kGroups; ++kb) acc_s = fmaf(h_lo(sd.ksz[i][kb]), dot[kb][i], acc_s);
         st[i] = acc_s;
       }
       // st[i] = score of token 4*lg + i for row lm
@@ -372,7 +490,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
         const float al = mn == da::kNegInf ? 1.f : da::fast_exp2(m[rt] - mn);
         l[rt] *= al;
 #pragma unroll
-        for (int bb = 0; bb < 8; ++bb) acc[rt][bb] *= al;
+        for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] *= al;
         m[rt] = mn;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -387,7 +505,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
       pb[rt] = half4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
     }
 
-    // ---- V operand: tokens 4*lg + j, d = 8*lm + block
+    // ---- V operand: tokens 4*lg + j, d = (D/16)*lm + block
     // rows past the split end may hold anything (even NaN scales): give them
     // code 0, scale 0, zero 0, i.e. the value 0
     uint32_t vw[4], vsz[4];
@@ -406,9 +524,11 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     const half2_t s01h = s01 * half2_t{0.0625, 0.0625}, s23h = s23 * half2_t{0.0625, 0.0625};
     const half2_t k1024 = {1024, 1024};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      // byte kk of each token's dword: [t0.byte, 0, t1.byte, 0]
-      const uint32_t sel = (uint32_t)kk | 0x0C00u | ((uint32_t)(4 + kk) << 16) | 0x0C000000u;
+    for (int kk = 0; kk < kBlocks / 2; ++kk) {
+      // byte kk of each token's dword (D = 64: byte 2 (lm % 2) + kk, the
+      // lane's half): [t0.byte, 0, t1.byte, 0]
+      const uint32_t by = D == 128 ? (uint32_t)kk : (uint32_t)(2 * (lm & 1) + kk);
+      const uint32_t sel = by | 0x0C00u | ((4 + by) << 16) | 0x0C000000u;
       const uint32_t x01 = __builtin_amdgcn_perm(vw[1], vw[0], sel);
       const uint32_t x23 = __builtin_amdgcn_perm(vw[3], vw[2], sel);
 #pragma unroll
@@ -429,20 +549,26 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   };
 
   // the lanes' read positions inside stage 0; stage j % kStages adds a constant
-  const uint32_t ka[4] = {ring_lds + rd_k[0], ring_lds + rd_k[1], ring_lds + rd_k[2],
-                          ring_lds + rd_k[3]};
-  const uint32_t va = ring_lds + rd_v, ksza = ring_lds + rd_ksz, vsza = ring_lds + rd_vsz,
+  uint32_t ka[kGroups];
+#pragma unroll
+  for (int kb = 0; kb < kGroups; ++kb) ka[kb] = ring_lds + rd_k[kb];
+  const uint32_t va = ring_lds + rd_v[0], ksza = ring_lds + rd_ksz, vsza = ring_lds + rd_vsz,
                  kza = ring_lds + rd_kz;
+  const uint32_t va2 = ring_lds + rd_v[D == 128 ? 0 : 1];
   // wait for tile j, read it (stage offset ST + off bytes), refill its stage
-  auto step = [&](int j, StageData& sd, uint32_t off, auto st_tag) {
+  auto step = [&](int j, StageData<D>& sd, uint32_t off, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
-    const int ahead = min(kStages - 2, nmine - 1 - j);
-    if (ahead >= 2) wait_vmcnt<8>();
-    else if (ahead == 1) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
+    // the tiles after j issued so far may stay in flight
+    wait_tiles_ahead<Gm::kLoads, kStages - 2>(min(kStages - 2, nmine - 1 - j));
     const int jn = min(j + kStages - 1, nmine - 1);
-    const uint32_t k4[4] = {ka[0] + off, ka[1] + off, ka[2] + off, ka[3] + off};
-    const int pid = read_stage<ST>(k4, va + off, ksza + off, vsza + off, kza + off, pid_addr(jn), sd);
+    int pid;
+    if constexpr (D == 128) {
+      const uint32_t k4[4] = {ka[0] + off, ka[1] + off, ka[2] + off, ka[3] + off};
+      pid = read_stage<ST>(k4, va + off, ksza + off, vsza + off, kza + off, pid_addr(jn), sd);
+    } else {
+      const uint32_t k2[2] = {ka[0] + off, ka[1] + off}, v2[2] = {va + off, va2 + off};
+      pid = read_stage64(k2, v2, ksza + off, vsza + off, kza + off, pid_addr(jn), sd);
+    }
     if (j + kStages - 1 < nmine) issue(j + kStages - 1, pid);
   };
   for (; pc < p1; pc += kMaxSplitPages) {
@@ -461,27 +587,36 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
 #pragma unroll
     for (int u = 0; u < kStages - 1; ++u)
       if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
-    // unmasked tiles, kStages per trip so that each one's stage is a constant
-    static_assert(kStages == 4, "one unrolled trip per ring cycle");
     using C0 = std::integral_constant<int, 0>;
-    using C1 = std::integral_constant<int, kStageBytes>;
-    using C2 = std::integral_constant<int, 2 * kStageBytes>;
-    using C3 = std::integral_constant<int, 3 * kStageBytes>;
     int j = 0;
-    for (; j + kStages <= jfull; j += kStages) {
-      StageData sd0, sd1, sd2, sd3;
-      step(j, sd0, 0u, C0{});
-      compute(j, sd0, std::false_type{});
-      step(j + 1, sd1, 0u, C1{});
-      compute(j + 1, sd1, std::false_type{});
-      step(j + 2, sd2, 0u, C2{});
-      compute(j + 2, sd2, std::false_type{});
-      step(j + 3, sd3, 0u, C3{});
-      compute(j + 3, sd3, std::false_type{});
+    if constexpr (D == 128) {
+      // unmasked tiles, kStages per trip so that each one's stage is a constant
+      static_assert(kStages == 4, "one unrolled trip per ring cycle");
+      using C1 = std::integral_constant<int, kStageBytes>;
+      using C2 = std::integral_constant<int, 2 * kStageBytes>;
+      using C3 = std::integral_constant<int, 3 * kStageBytes>;
+      for (; j + kStages <= jfull; j += kStages) {
+        StageData<D> sd0, sd1, sd2, sd3;
+        step(j, sd0, 0u, C0{});
+        compute(j, sd0, std::false_type{});
+        step(j + 1, sd1, 0u, C1{});
+        compute(j + 1, sd1, std::false_type{});
+        step(j + 2, sd2, 0u, C2{});
+        compute(j + 2, sd2, std::false_type{});
+        step(j + 3, sd3, 0u, C3{});
+        compute(j + 3, sd3, std::false_type{});
+      }
+    } else {
+      // unmasked tiles one at a time (the stage offset in a register)
+      for (; j < jfull; ++j) {
+        StageData<D> sd;
+        step(j, sd, (uint32_t)((j % kStages) * kStageBytes), C0{});
+        compute(j, sd, std::false_type{});
+      }
     }
-    // the rest (fewer than kStages unmasked tiles, then the masked ones)
+    // the rest (D = 128: fewer than kStages unmasked tiles; then the masked ones)
     for (; j < nmine; ++j) {
-      StageData sd;
+      StageData<D> sd;
       step(j, sd, (uint32_t)((j % kStages) * kStageBytes), C0{});
       compute(j, sd, std::true_type{});
     }
@@ -498,27 +633,42 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     l[rt] += xor32(l[rt]);
     const int row = wave * ROWS + 16 * rt + lm;
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
+    for (int bb = 0; bb < kBlocks; ++bb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_acc[row * kD + 8 * (4 * lg + i) + bb] = acc[rt][bb][i];
+      for (int i = 0; i < 4; ++i)
+        sm_acc[row * kD + kBlocks * (4 * lg + i) + bb] = acc[rt][bb][i];
     if (lg == 0) {
       sm_m[row] = m[rt];
       sm_l[row] = l[rt];
     }
   }
   __syncthreads();
-  write_partials<kWaves, ROWS>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S, s,
-                               kPScale, a.o, a.lse);
+  write_partials<kWaves, ROWS, D>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S,
+                                  s, kPScale, a.o, a.lse);
+}
+
+template <int D>
+void launch(const da_host::SplitCall& c, const MfmaArgs& a, int R) {
+  const bool hnd = c.kv.slot == 1;  // head-major pool layout
+  const dim3 grid(c.grid(true)), block(kThreads);
+  constexpr int kNt = da::kStreamPolicy;
+  if (R <= 16) {
+    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 1, kNt>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((split_int4_mfma_kernel<D, 1, 0>), grid, block, 0, c.stream, a);
+  } else {
+    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 2, kNt>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((split_int4_mfma_kernel<D, 2, 0>), grid, block, 0, c.stream, a);
+  }
 }
 
 }  // namespace
 
-// INT4 stage 1 on the matrix cores, one row tile (up to 16 query rows per
-// kv-head) or two (blocks of up to 32 rows, so that G * q in 17..32 forms
-// each tile's operands once); -1 when the shape is not covered (the caller
-// then uses the vector-ALU kernel).
+// INT4 stage 1 on the matrix cores (D = 128 or 64), one row tile (up to 16
+// query rows per kv-head) or two (blocks of up to 32 rows, so that G * q in
+// 17..32 forms each tile's operands once); -1 when the shape is not covered
+// (the caller then uses the vector-ALU kernel).
 int32_t da_split_int4_mfma(const da_host::SplitCall& call) {
-  if (!call.q_bf16 || call.D != kD) return -1;
+  if (!call.q_bf16 || (call.D != 128 && call.D != 64)) return -1;
   da_host::SplitCall c = call;
   if (c.rows > DA_MAX_ROWS) da_host::row_blocks(c.rows, 2 * DA_MAX_ROWS, c.nrb, c.rb_rows);
   const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block
@@ -532,15 +682,7 @@ int32_t da_split_int4_mfma(const da_host::SplitCall& call) {
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  const bool hnd = c.kv.slot == 1;  // head-major pool layout
-  const dim3 grid(c.grid(true)), block(kThreads);
-  constexpr int kNt = da::kStreamPolicy;
-  if (R <= 16) {
-    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<1, kNt>), grid, block, 0, c.stream, a);
-    else hipLaunchKernelGGL((split_int4_mfma_kernel<1, 0>), grid, block, 0, c.stream, a);
-  } else {
-    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<2, kNt>), grid, block, 0, c.stream, a);
-    else hipLaunchKernelGGL((split_int4_mfma_kernel<2, 0>), grid, block, 0, c.stream, a);
-  }
+  if (c.D == 128) launch<128>(c, a, R);
+  else launch<64>(c, a, R);
   return da_host::launch_status();
 }

@@ -68,6 +68,13 @@ INT4_Q1 = W.INT4_MTP_B64.scaled(name="int4_q1_small", batch=4, q_per_req=1, caus
                                 lengths="list", length_list=(1, 64, 300, 1500))
 INT4_R12 = W.INT4_MTP_B64.scaled(name="int4_mtp3_r12_small", batch=4, q_per_req=3,
                                  lengths="list", length_list=(2, 17, 95, 1234))
+INT4_D64 = W.INT4_MTP_B64.scaled(name="int4_d64_mtp4_r16_p16", batch=4, head_dim=64,
+                                 page_size=16, lengths="list", length_list=(1, 4, 17, 1500))
+INT4_D64_Q1 = W.INT4_MTP_B64.scaled(name="int4_d64_q1_r4", batch=4, head_dim=64, q_per_req=1,
+                                    causal=False, lengths="list", length_list=(1, 64, 300, 2000))
+INT4_D64_R20 = W.INT4_MTP_B64.scaled(name="int4_d64_g5_mtp4_r20_p128", batch=3, num_q_heads=40,
+                                     head_dim=64, page_size=128, lengths="list",
+                                     length_list=(3, 129, 2100))
 INT4_G8Q2 = W.INT4_MTP_B64.scaled(name="int4_g8_mtp2_small", batch=3, num_q_heads=64, q_per_req=2,
                                   lengths="list", length_list=(1, 48, 700))
 
@@ -99,7 +106,7 @@ SMALL = [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, D64_G8, D64_MTP, D64_R20,
          MHA_P32, MTP_BF16, MTP_BF16_G2Q3,
          INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV, INT8_FP32Q, INT8_D64, INT8_D64_MTP, INT8_D64_R20,
          INT4_SMALL, INT4_Q1,
-         INT4_R12, INT4_G8Q2]
+         INT4_R12, INT4_G8Q2, INT4_D64, INT4_D64_Q1, INT4_D64_R20]
 
 
 def both_layouts(ws):
@@ -122,7 +129,8 @@ def test_small_elementwise(gpu, w, S):
     U.check_lse(U.to_np(lse), lse_ref, f"{w.name} S={S} lse")
 
 
-@pytest.mark.parametrize("w", both_layouts([INT4_SMALL, INT4_Q1, INT4_R12]), ids=lambda w: w.name)
+@pytest.mark.parametrize("w", both_layouts([INT4_SMALL, INT4_Q1, INT4_R12, INT4_D64]),
+                         ids=lambda w: w.name)
 def test_int4_fractional_zero_points(gpu, w):
     """The zero point is any fp16 value, not only a code: shift every zero by a
     fraction (different per slot) and compare with the oracle decoding the same

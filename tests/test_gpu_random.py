@@ -63,7 +63,7 @@ def wide_case(i):
     fmt = ["bf16", "int8", "int4", "fp32"][i % 4]
     kv = {"bf16": W.KV_DENSE, "fp32": W.KV_DENSE, "int8": W.KV_INT8, "int4": W.KV_INT4}[fmt]
     dtype = "fp32" if fmt == "fp32" else "bf16"
-    D = 128 if fmt == "int4" else int(rng.choice([64, 128]))
+    D = int(rng.choice([64, 128]))
     qn = int(rng.choice([1, 2, 3, 4, 8]))
     rows = int(rng.integers(17, 65))
     G = max(1, rows // qn)
