@@ -115,9 +115,9 @@ def stage1_kernel(w):
         if rows <= 5:
             return "split_bf16_kernel", ["split_bf16.hip", "common.h"]
         return "split_bf16_mfma_kernel", ["split_bf16_mfma.hip", "mfma_util.h", "common.h"]
-    if bf16_q and w.kv == W.KV_INT8:
+    if w.kv == W.KV_INT8:
         return "split_int8_mfma_kernel", ["split_int8.hip", "mfma_util.h", "common.h"]
-    if bf16_q and w.kv == W.KV_INT4:
+    if w.kv == W.KV_INT4:
         return "split_int4_mfma_kernel", ["split_int4.hip", "mfma_util.h", "common.h"]
     return "split_fma_kernel", ["split_fma.hip", "common.h"]
 

@@ -208,7 +208,8 @@ inline bool kv_strides(int32_t kv_layout, int Hkv, int page_size, KvStrides& st)
 
 // Everything a stage-1 launch needs, checked by the entry point; the
 // specialised kernels take it whole and return -1 for shapes they do not
-// cover (the entry point then launches the generic kernel).
+// cover (the entry point then tries the next one, or reports the call as
+// unsupported).
 struct SplitCall {
   const void* q;
   int q_bf16;

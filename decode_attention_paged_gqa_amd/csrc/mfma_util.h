@@ -46,6 +46,26 @@ __device__ __forceinline__ int32_t lds_read_i32(uint32_t addr) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// Eight consecutive query elements, starting at element e0, as floats; the
+// query is bf16 (F32 false) or fp32 in memory, 16-byte aligned at e0.
+template <bool F32>
+__device__ __forceinline__ void load_q8(const void* q, long long e0, float (&f)[8]) {
+  if constexpr (F32) {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + e0);
+    const float4 x = p[0], y = p[1];
+    f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
+    f[4] = y.x; f[5] = y.y; f[6] = y.z; f[7] = y.w;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) + e0);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = da::bf16_lo(w[e]);
+      f[2 * e + 1] = da::bf16_hi(w[e]);
+    }
+  }
+}
+
 // Power of two that brings a row of Q into fp16 range: with m = max |q|
 // over the row, m * 2^sh lies in [2^14, 2^15), so every bf16 element maps
 // to fp16 exactly unless it sits more than 2^28 below m (then it rounds in

@@ -1,7 +1,7 @@
 // Stage 1 for a dense bf16 cache and small query groups (G*q <= 5): the
 // vector-ALU path of the GQA flash-decode stage 1 (LightLLM PR #1549,
-// "Covered decode kernels").  Same contract as the generic kernel in
-// split_fma.hip; this one is built to stream K/V at HBM speed.
+// "Covered decode kernels").  Same contract as decode_attn_split (entry
+// point in split_fma.hip); built to stream K/V at HBM speed.
 //
 // Work decomposition: one workgroup (4 waves) per (kv-head g, split s,
 // request b); the split's tokens are cut into 8-token tiles dealt
@@ -452,8 +452,8 @@ int32_t launch(const Bf16Args& a, unsigned grid, hipStream_t st) {
 }  // namespace
 
 // Called by the split entry point after argument validation; returns -1
-// when this kernel does not cover the shape (the caller then uses the
-// generic kernel).
+// when this kernel does not cover the shape (more than 5 rows per block:
+// the caller then uses the matrix-core kernel).
 int32_t da_split_bf16_fast(const da_host::SplitCall& c) {
   const int G = c.Hq / c.Hkv, R = c.rb_rows, D = c.D;  // rows per block
   if (R > 5 || (D != 128 && D != 64)) return -1;

@@ -450,7 +450,7 @@ void launch(const da_host::SplitCall& c, const Bf16MfmaArgs& a, int R) {
 // bf16 stage 1 on the matrix cores (D = 128 or 64) for 6..16 query rows per
 // kv-head (one row tile) and for more (two row tiles: blocks of up to 32
 // rows, so that G * q in 17..32 reads each page once); -1 when the shape is
-// not covered (the caller then uses another kernel).
+// not covered (the caller then reports the call as unsupported).
 int32_t da_split_bf16_mfma(const da_host::SplitCall& call) {
   if (!call.q_bf16 || (call.D != 128 && call.D != 64)) return -1;
   da_host::SplitCall c = call;

@@ -1,6 +1,9 @@
-// Stage 1 of split-KV decode attention, vector-ALU path (GQA flash decode
-// "stage 1", its INT8 / INT4 KV variants and the num_splits KV-cache decode
-// of LightLLM PR #1549, section "Covered decode kernels").
+// Stage 1 of split-KV decode attention over an fp32 cache with fp32 Q,
+// vector-ALU path (GQA flash decode "stage 1" and the num_splits KV-cache
+// decode of LightLLM PR #1549, section "Covered decode kernels"), and the
+// C-ABI entry points of stage 1, which validate the call and dispatch every
+// other cache format to its specialised kernel (split_bf16.hip,
+// split_bf16_mfma.hip, split_int8.hip, split_int4.hip).
 //
 // One workgroup (4 waves) per (kv-head g, split s, request b).  The G*q
 // query rows that read kv-head g are all served by that workgroup, so each
@@ -16,33 +19,22 @@
 //
 // Scores are kept in log2 units: q is pre-multiplied by softmax_scale*log2(e)
 // and exponentials are exp2; the stored LSE is converted back to natural log.
-//
-// Quantised caches: INT8 rows are x = code * s_tok (s_tok folded into the
-// score after the dot product and into p before P*V); INT4 rows are
-// x = (nib - z) * s per 32-group, each lane's E elements lying inside one
-// group, so (nib - z) is formed exactly and s is folded into the lane's
-// partial dot product and into p.
 #include "common.h"
 
 namespace {
-
-enum KvKind { KV_BF16 = 0, KV_F32 = 1, KV_I8 = 2, KV_I4 = 3 };
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
 struct SplitArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const uint16_t* ks;  // int8: [P,S,Hkv]; int4: [P,S,Hkv,D/32,2]
-  const uint16_t* vs;
+  const float* q;
+  const uint8_t* k;
+  const uint8_t* v;
   const int32_t* pt;
   const int32_t* seqlens;
   da::Stage1Sched sched;  // (request, split) of every workgroup
   float* o;
   float* lse;
-  int q_bf16;
   int pt_stride, max_pages;
   int qn, Hq, Hkv, G, R;
   int page_size, log2_ps, num_pages;
@@ -51,124 +43,34 @@ struct SplitArgs {
   int causal;
 };
 
-template <int BYTES>
-struct Raw {
-  uint32_t w[(BYTES + 3) / 4];
-};
-
-// K/V row pieces are read once per launch: non-temporal loads (see
-// da::kStreamPolicy), except 4-bit rows in the token-major layout, whose
-// cache lines neighbouring kv-heads' workgroups share; query rows, shared by
-// a request's splits, are plain loads too.
+// A lane's piece of a K or V row: D/16 fp32 values, read once per launch
+// with non-temporal loads (see da::kStreamPolicy).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-template <int BYTES>
-__device__ __forceinline__ void load_q(const uint8_t* p, Raw<BYTES>& r) {
-  if constexpr (BYTES == 16) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p);
-    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-  } else {
-    static_assert(BYTES == 8, "a lane's query piece is 8 or 16 bytes");
-    const uint2 a = *reinterpret_cast<const uint2*>(p);
-    r.w[0] = a.x; r.w[1] = a.y;
+template <int E>
+__device__ __forceinline__ void load_row(const uint8_t* p, float (&f)[E]) {
+  static_assert(E % 4 == 0, "whole 16-byte pieces");
+#pragma unroll
+  for (int i = 0; i < E / 4; ++i) {
+    const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + i);
+    f[4 * i] = __uint_as_float(a[0]);
+    f[4 * i + 1] = __uint_as_float(a[1]);
+    f[4 * i + 2] = __uint_as_float(a[2]);
+    f[4 * i + 3] = __uint_as_float(a[3]);
   }
 }
 
-template <typename T, bool NT>
-__device__ __forceinline__ T ld(const T* p) {
-  if constexpr (NT) return __builtin_nontemporal_load(p);
-  else return *p;
-}
-
-template <int BYTES, bool NT = true>
-__device__ __forceinline__ void load_raw(const uint8_t* p, Raw<BYTES>& r) {
-  if constexpr (BYTES == 32) {
-    const u32x4_t a = ld<u32x4_t, NT>(reinterpret_cast<const u32x4_t*>(p));
-    const u32x4_t b = ld<u32x4_t, NT>(reinterpret_cast<const u32x4_t*>(p) + 1);
-    r.w[0] = a[0]; r.w[1] = a[1]; r.w[2] = a[2]; r.w[3] = a[3];
-    r.w[4] = b[0]; r.w[5] = b[1]; r.w[6] = b[2]; r.w[7] = b[3];
-  } else if constexpr (BYTES == 16) {
-    const u32x4_t a = ld<u32x4_t, NT>(reinterpret_cast<const u32x4_t*>(p));
-    r.w[0] = a[0]; r.w[1] = a[1]; r.w[2] = a[2]; r.w[3] = a[3];
-  } else if constexpr (BYTES == 8) {
-    const u32x2_t a = ld<u32x2_t, NT>(reinterpret_cast<const u32x2_t*>(p));
-    r.w[0] = a[0]; r.w[1] = a[1];
-  } else if constexpr (BYTES == 4) {
-    r.w[0] = ld<uint32_t, NT>(reinterpret_cast<const uint32_t*>(p));
-  } else {
-    r.w[0] = ld<uint16_t, NT>(reinterpret_cast<const uint16_t*>(p));
-  }
-}
-
-template <int BYTES>
-__device__ __forceinline__ void zero_raw(Raw<BYTES>& r) {
-#pragma unroll
-  for (int i = 0; i < (BYTES + 3) / 4; ++i) r.w[i] = 0u;
-}
-
-template <int KV, int D>
-struct Kv;
-
-template <int D>
-struct Kv<KV_BF16, D> {
-  static constexpr int E = D / 16;
-  static constexpr int BYTES = E * 2;
-  static constexpr int ROW_BYTES = D * 2;
-  __device__ static void to_float(const Raw<BYTES>& r, float* f) {
-#pragma unroll
-    for (int i = 0; i < E / 2; ++i) {
-      f[2 * i] = da::bf16_lo(r.w[i]);
-      f[2 * i + 1] = da::bf16_hi(r.w[i]);
-    }
-  }
-};
-
-template <int D>
-struct Kv<KV_F32, D> {
-  static constexpr int E = D / 16;
-  static constexpr int BYTES = E * 4;
-  static constexpr int ROW_BYTES = D * 4;
-  __device__ static void to_float(const Raw<BYTES>& r, float* f) {
-#pragma unroll
-    for (int i = 0; i < E; ++i) f[i] = __uint_as_float(r.w[i]);
-  }
-};
-
-template <int D>
-struct Kv<KV_I8, D> {
-  static constexpr int E = D / 16;
-  static constexpr int BYTES = E;
-  static constexpr int ROW_BYTES = D;
-  __device__ static void to_float(const Raw<BYTES>& r, float* f) {
-#pragma unroll
-    for (int i = 0; i < E; ++i) f[i] = da::sbyte_to_float(r.w[i / 4], i % 4);
-  }
-};
-
-template <int D>
-struct Kv<KV_I4, D> {
-  static constexpr int E = D / 16;
-  static constexpr int BYTES = E / 2;
-  static constexpr int ROW_BYTES = D / 2;
-  __device__ static void to_float(const Raw<BYTES>& r, float* f) {
-#pragma unroll
-    for (int i = 0; i < E; ++i) f[i] = (float)((r.w[i / 8] >> (4 * (i % 8))) & 15u);
-  }
-};
-
-template <int KV, int D, int RT>
+template <int D, int RT>
 __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) {
-  using P = Kv<KV, D>;
-  constexpr int E = P::E;
-  constexpr int NG = D / 32;  // int4 groups per row
+  constexpr int E = D / 16;       // elements per lane
+  constexpr int kRowBytes = 4 * D;
 
   __shared__ float sm_m[kWaves][RT];
   __shared__ float sm_l[kWaves][RT];
   __shared__ float sm_acc[kWaves][RT][D];
 
   da::Stage1Item it;
-  if (!da::stage1_item<(KV == KV_I8 || KV == KV_I4)>(a.sched, a.Hkv, it)) return;
+  if (!da::stage1_item<false>(a.sched, a.Hkv, it)) return;
   const int g = it.g, s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane >> 4, c = lane & 15;
@@ -190,19 +92,9 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
   for (int r = 0; r < RT; ++r) {
     if (r < nr) {
       const int i = (r0 + r) / a.G, h = g * a.G + ((r0 + r) % a.G);
-      const long long qoff = (((long long)b * a.qn + i) * a.Hq + h) * D + c * E;
-      if (a.q_bf16) {
-        Raw<E * 2> qr;
-        load_q<E * 2>(reinterpret_cast<const uint8_t*>(a.q) + qoff * 2, qr);
-        float f[E];
-        Kv<KV_BF16, D>::to_float(qr, f);
+      const float* qp = a.q + (((long long)b * a.qn + i) * a.Hq + h) * D + c * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) qf[r][e] = f[e] * a.scale_log2;
-      } else {
-        const float* qp = reinterpret_cast<const float*>(a.q) + qoff;
-#pragma unroll
-        for (int e = 0; e < E; ++e) qf[r][e] = qp[e] * a.scale_log2;
-      }
+      for (int e = 0; e < E; ++e) qf[r][e] = qp[e] * a.scale_log2;
       tend[r] = a.causal ? L - (a.qn - 1 - i) : L;
     } else {
 #pragma unroll
@@ -220,8 +112,6 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
     for (int e = 0; e < E; ++e) acc[r][e] = 0.f;
   }
 
-  const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.k);
-  const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.v);
   const int ntiles = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
 
   for (int tile = wave; tile < ntiles; tile += kWaves) {
@@ -231,39 +121,20 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
     if ((unsigned)pid >= (unsigned)a.num_pages) pid = 0;
     const int slot0 = tb & (ps - 1);
 
-    Raw<P::BYTES> kr[4], vr[4];
-    float kscale[4], kzero[4], vscale[4], vzero[4];
+    // rows past the split end are not read (their values stay 0)
+    float kf[4][E], vf[4][E];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int t = tb + st * 4 + tl;
-      kscale[st] = vscale[st] = 1.f;
-      kzero[st] = vzero[st] = 0.f;
       if (t < t1) {
         const long long row = (long long)pid * ps * a.Hkv +
                               (long long)(slot0 + st * 4 + tl) * a.slot_stride +
                               (long long)g * a.head_stride;
-        const uint8_t* kp = kb + row * P::ROW_BYTES + c * P::BYTES;
-        const uint8_t* vp = vb + row * P::ROW_BYTES + c * P::BYTES;
-        if (KV != KV_I4 || a.slot_stride == 1) {  // a kv-head's rows contiguous
-          load_raw<P::BYTES, true>(kp, kr[st]);
-          load_raw<P::BYTES, true>(vp, vr[st]);
-        } else {
-          load_raw<P::BYTES, false>(kp, kr[st]);
-          load_raw<P::BYTES, false>(vp, vr[st]);
-        }
-        if constexpr (KV == KV_I8) {
-          kscale[st] = da::half_bits_to_float(a.ks[row]);
-          vscale[st] = da::half_bits_to_float(a.vs[row]);
-        } else if constexpr (KV == KV_I4) {
-          const long long sz = (row * NG + (c * E) / 32) * 2;
-          kscale[st] = da::half_bits_to_float(a.ks[sz]);
-          kzero[st] = da::half_bits_to_float(a.ks[sz + 1]);
-          vscale[st] = da::half_bits_to_float(a.vs[sz]);
-          vzero[st] = da::half_bits_to_float(a.vs[sz + 1]);
-        }
+        load_row<E>(a.k + row * kRowBytes + c * E * 4, kf[st]);
+        load_row<E>(a.v + row * kRowBytes + c * E * 4, vf[st]);
       } else {
-        zero_raw<P::BYTES>(kr[st]);
-        zero_raw<P::BYTES>(vr[st]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) kf[st][e] = vf[st][e] = 0.f;
       }
     }
 
@@ -271,24 +142,16 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
     float sc[4][RT];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      float kf[E];
-      P::to_float(kr[st], kf);
-      if constexpr (KV == KV_I4) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) kf[e] -= kzero[st];
-      }
       const int t = tb + st * 4 + tl;
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) d = fmaf(qf[r][e], kf[e], d);
-        if constexpr (KV == KV_I4) d *= kscale[st];
+        for (int e = 0; e < E; ++e) d = fmaf(qf[r][e], kf[st][e], d);
         d += da::xor_shfl<1>(d);
         d += da::xor_shfl<2>(d);
         d += da::xor_shfl<4>(d);
         d += da::xor_shfl<8>(d);
-        if constexpr (KV == KV_I8) d *= kscale[st];
         sc[st][r] = (t < t1 && t < tend[r]) ? d : da::kNegInf;
       }
     }
@@ -322,18 +185,10 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
     // ---- acc += p * V
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      float vf[E];
-      P::to_float(vr[st], vf);
-      if constexpr (KV == KV_I4) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) vf[e] -= vzero[st];
-      }
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
-        float pr = p[st][r];
-        if constexpr (KV == KV_I8 || KV == KV_I4) pr *= vscale[st];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[r][e] = fmaf(pr, vf[e], acc[r][e]);
+        for (int e = 0; e < E; ++e) acc[r][e] = fmaf(p[st][r], vf[st][e], acc[r][e]);
       }
     }
   }
@@ -384,29 +239,27 @@ __global__ __launch_bounds__(kThreads) void split_fma_kernel(const SplitArgs a) 
   }
 }
 
-template <int KV, int D, int RT>
+template <int D, int RT>
 int32_t launch_rt(const SplitArgs& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((split_fma_kernel<KV, D, RT>), dim3(grid), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((split_fma_kernel<D, RT>), dim3(grid), dim3(kThreads), 0, st, a);
   return da_host::launch_status();
 }
 
 // a.R: rows per block (at most DA_MAX_ROWS)
-template <int KV, int D>
+template <int D>
 int32_t launch_d(const SplitArgs& a, unsigned grid, hipStream_t st) {
   const int R = a.R;
-  if (R <= 1) return launch_rt<KV, D, 1>(a, grid, st);
-  if (R <= 2) return launch_rt<KV, D, 2>(a, grid, st);
-  if (R <= 4) return launch_rt<KV, D, 4>(a, grid, st);
-  if (R <= 5) return launch_rt<KV, D, 5>(a, grid, st);
-  if (R <= 8) return launch_rt<KV, D, 8>(a, grid, st);
-  return launch_rt<KV, D, 16>(a, grid, st);
+  if (R <= 1) return launch_rt<D, 1>(a, grid, st);
+  if (R <= 2) return launch_rt<D, 2>(a, grid, st);
+  if (R <= 4) return launch_rt<D, 4>(a, grid, st);
+  if (R <= 5) return launch_rt<D, 5>(a, grid, st);
+  if (R <= 8) return launch_rt<D, 8>(a, grid, st);
+  return launch_rt<D, 16>(a, grid, st);
 }
 
-template <int KV>
-int32_t launch_kv(const da_host::SplitCall& c, const SplitArgs& a) {
-  constexpr bool kGrouped = KV == KV_I8 || KV == KV_I4;  // short rows share cache lines
-  const unsigned grid = c.grid(kGrouped);
-  return c.D == 128 ? launch_d<KV, 128>(a, grid, c.stream) : launch_d<KV, 64>(a, grid, c.stream);
+int32_t launch_f32(const da_host::SplitCall& c, const SplitArgs& a) {
+  const unsigned grid = c.grid(false);
+  return c.D == 128 ? launch_d<128>(a, grid, c.stream) : launch_d<64>(a, grid, c.stream);
 }
 
 int32_t check_common(const da_host::SplitCall& c, int32_t kv_layout) {
@@ -463,9 +316,9 @@ da_host::SplitCall make_call(const void* q, int q_bf16, const void* k, const voi
 
 SplitArgs make_args(const da_host::SplitCall& c) {
   SplitArgs a;
-  a.q = c.q; a.k = c.k; a.v = c.v; a.ks = c.ks; a.vs = c.vs; a.pt = c.pt;
+  a.q = (const float*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v; a.pt = c.pt;
   a.seqlens = c.seqlens; a.sched = c.sched();
-  a.o = c.o; a.lse = c.lse; a.q_bf16 = c.q_bf16;
+  a.o = c.o; a.lse = c.lse;
   a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
   a.qn = c.qn; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = c.Hq / c.Hkv; a.R = c.rb_rows;
   a.page_size = c.ps; a.log2_ps = __builtin_ctz((unsigned)c.ps); a.num_pages = c.num_pages;
@@ -478,11 +331,13 @@ SplitArgs make_args(const da_host::SplitCall& c) {
 }  // namespace
 
 // Specialised stage-1 kernels; each returns -1 when the shape is not covered.
-int32_t da_split_bf16_fast(const da_host::SplitCall& c);  // split_bf16.hip: bf16, G*q <= 5
+// Between them they cover every call that passes check_common (D = 64 or 128,
+// any number of query rows), so the entry points report a -1 as unsupported.
+int32_t da_split_bf16_fast(const da_host::SplitCall& c);  // split_bf16.hip: <= 5 rows per block
 int32_t da_split_bf16_mfma(const da_host::SplitCall& c);  // split_bf16_mfma.hip: >= 6 rows
 // (rows per block: every kernel takes the rows of one row block, see DA_MAX_ROWS)
-int32_t da_split_int8_mfma(const da_host::SplitCall& c);  // split_int8.hip: D 128, bf16 Q
-int32_t da_split_int4_mfma(const da_host::SplitCall& c);  // split_int4.hip: D 128, bf16 Q
+int32_t da_split_int8_mfma(const da_host::SplitCall& c);  // split_int8.hip: bf16 or fp32 Q
+int32_t da_split_int4_mfma(const da_host::SplitCall& c);  // split_int4.hip: bf16 or fp32 Q
 
 extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool,
                                      const void* v_pool, const int32_t* page_table,
@@ -506,10 +361,9 @@ extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k
     const int32_t fast = da_split_bf16_fast(c);
     if (fast >= 0) return fast;
     const int32_t mf = da_split_bf16_mfma(c);
-    if (mf >= 0) return mf;
-    return launch_kv<KV_BF16>(c, make_args(c));
+    return mf >= 0 ? mf : DA_ERR_UNSUPPORTED;
   }
-  return launch_kv<KV_F32>(c, make_args(c));
+  return launch_f32(c, make_args(c));
 }
 
 extern "C" int32_t decode_attn_split_int8(
@@ -531,8 +385,7 @@ extern "C" int32_t decode_attn_split_int8(
   if (!k_scale || !v_scale) return DA_ERR_INVALID_ARG;
   if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
   const int32_t mf = da_split_int8_mfma(c);
-  if (mf >= 0) return mf;
-  return launch_kv<KV_I8>(c, make_args(c));
+  return mf >= 0 ? mf : DA_ERR_UNSUPPORTED;
 }
 
 extern "C" int32_t decode_attn_split_int4(
@@ -554,6 +407,5 @@ extern "C" int32_t decode_attn_split_int4(
   if (!k_scale_zero || !v_scale_zero) return DA_ERR_INVALID_ARG;
   if (q_dtype != DA_BF16 && q_dtype != DA_FP32) return DA_ERR_UNSUPPORTED;
   const int32_t mf = da_split_int4_mfma(c);
-  if (mf >= 0) return mf;
-  return launch_kv<KV_I4>(c, make_args(c));
+  return mf >= 0 ? mf : DA_ERR_UNSUPPORTED;
 }

@@ -24,7 +24,10 @@
 // Q element is exact in fp32).  Q is scaled by a power of two per row so its
 // largest element lies in [2^14, 2^15) before the (then exact, for bf16)
 // conversion to fp16; the power of two and 2^24 are folded into the score
-// factor.  The per-group terms are combined in fp32 with the group's s and
+// factor.  An fp32 Q is held as two fp16 terms, hi = fp16(q') and lo =
+// fp16(q' - hi) (22 significant bits; hi + lo is exact in fp32), each taken
+// through the group's QK product into the same accumulator, and the group
+// sums of Q add both.  The per-group terms are combined in fp32 with the group's s and
 // z: the scale terms s_g * dot_g on the vector ALU (one mixed-precision fma
 // each), the zero-point terms -sum_g (s_g z_g) sum_g(q) as one fp32 matrix
 // product [16 tokens x 4 groups] . [4 groups x 16 rows] (s_g z_g is exact in
@@ -194,7 +197,7 @@ __device__ __forceinline__ int32_t read_stage(const uint32_t (&kaddr)[4], uint32
 }
 
 struct MfmaArgs {
-  const uint16_t* q;
+  const void* q;  // bf16 or fp32
   const uint8_t* k;
   const uint8_t* v;
   const uint8_t* ksz;
@@ -220,7 +223,7 @@ struct MfmaArgs {
 // default in the token-major one, where a 64-byte code row (and a 16-byte
 // scale row) shares its line with the neighbouring kv-heads' rows, which
 // their workgroups read from L2 moments later.
-template <int D, int NT, int POLICY>
+template <int D, int NT, int POLICY, bool QF>  // QF: fp32 Q
 __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_kernel(const MfmaArgs a) {
   using Gm = Geo<D>;
   constexpr int kD = D, kGroups = Gm::kGroups, kBlocks = Gm::kBlocks, kStages = Gm::kStages;
@@ -268,6 +271,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   // ---- Q^T operands (row tile rt, row lm): for MFMA kb, elements
   // 32*kb + 8*lg + e, e = 0..7, scaled by 2^sh and held in fp16
   uint32_t qv[NT][kGroups][4];  // [rt][kb][register]
+  uint32_t ql[NT][QF ? kGroups : 1][4];  // fp32 Q: the lo terms
   float rowfac[NT];       // score (log2 units) = rowfac * sum_g s_g (dot_g - z_g qsum_g)
   float qsum_lg[NT];      // qsum of group lg: operand of the zero-point product
   int tlim[NT];           // tokens t < tlim are visible to this lane's row
@@ -280,16 +284,11 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     const int i = r / a.G, h = g * a.G + r % a.G;
     const long long qoff = (((long long)b * a.qn + i) * a.Hq + h) * kD + 8 * lg;
     float qf[kGroups][8];
-    const uint4* qp = reinterpret_cast<const uint4*>(a.q + qoff);
 #pragma unroll
     for (int kb = 0; kb < kGroups; ++kb) {
-      const uint4 x = qp[4 * kb];  // 8 bf16 at element 32*kb + 8*lg
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      load_q8<QF>(a.q, qoff + 32 * kb, qf[kb]);  // 8 elements at 32*kb + 8*lg
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qf[kb][2 * e] = live ? da::bf16_lo(w[e]) : 0.f;
-        qf[kb][2 * e + 1] = live ? da::bf16_hi(w[e]) : 0.f;
-      }
+      for (int e = 0; e < 8; ++e) qf[kb][e] = live ? qf[kb][e] : 0.f;
     }
     float mx = 0.f;
 #pragma unroll
@@ -301,17 +300,23 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     const int sh = q_row_shift(mx);
 #pragma unroll
     for (int kb = 0; kb < kGroups; ++kb) {
-      float part = 0.f;
+      float part = 0.f, lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        qf[kb][e] = (float)(_Float16)ldexpf(qf[kb][e], sh);
+        const float y = ldexpf(qf[kb][e], sh);
+        qf[kb][e] = (float)(_Float16)y;
         part += qf[kb][e];
+        if constexpr (QF) {
+          lo[e] = (float)(_Float16)(y - qf[kb][e]);
+          part += lo[e];
+        }
       }
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         // pairs 1 and 3 meet codes that sit 4 bits up (16 n), see the K operand
         const float f = (x & 1) ? 0.0625f : 1.f;
         qv[rt][kb][x] = pack_h2(qf[kb][x] * f, qf[kb][x + 4] * f);
+        if constexpr (QF) ql[rt][kb][x] = pack_h2(lo[x] * f, lo[x + 4] * f);
       }
       part += xor16(part);
       part += xor32(part);
@@ -459,6 +464,12 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
         const half8_t qb = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
         dot[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[kb], qb, float4_t{0.f, 0.f, 0.f, 0.f},
                                                          0, 0, 0);
+        if constexpr (QF) {
+          const half2_t l0 = as_h2(ql[rt][kb][0]), l1 = as_h2(ql[rt][kb][1]);
+          const half2_t l2 = as_h2(ql[rt][kb][2]), l3 = as_h2(ql[rt][kb][3]);
+          const half8_t lb = {l0[0], l0[1], l1[0], l1[1], l2[0], l2[1], l3[0], l3[1]};
+          dot[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[kb], lb, dot[kb], 0, 0, 0);
+        }
       }
       float4_t st;
 #pragma unroll
@@ -647,33 +658,33 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
                                   s, kPScale, a.o, a.lse);
 }
 
-template <int D>
+template <int D, bool QF>
 void launch(const da_host::SplitCall& c, const MfmaArgs& a, int R) {
   const bool hnd = c.kv.slot == 1;  // head-major pool layout
   const dim3 grid(c.grid(true)), block(kThreads);
   constexpr int kNt = da::kStreamPolicy;
   if (R <= 16) {
-    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 1, kNt>), grid, block, 0, c.stream, a);
-    else hipLaunchKernelGGL((split_int4_mfma_kernel<D, 1, 0>), grid, block, 0, c.stream, a);
+    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 1, kNt, QF>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((split_int4_mfma_kernel<D, 1, 0, QF>), grid, block, 0, c.stream, a);
   } else {
-    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 2, kNt>), grid, block, 0, c.stream, a);
-    else hipLaunchKernelGGL((split_int4_mfma_kernel<D, 2, 0>), grid, block, 0, c.stream, a);
+    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 2, kNt, QF>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((split_int4_mfma_kernel<D, 2, 0, QF>), grid, block, 0, c.stream, a);
   }
 }
 
 }  // namespace
 
-// INT4 stage 1 on the matrix cores (D = 128 or 64), one row tile (up to 16
-// query rows per kv-head) or two (blocks of up to 32 rows, so that G * q in
-// 17..32 forms each tile's operands once); -1 when the shape is not covered
-// (the caller then uses the vector-ALU kernel).
+// INT4 stage 1 on the matrix cores (D = 128 or 64, bf16 or fp32 Q), one row
+// tile (up to 16 query rows per kv-head) or two (blocks of up to 32 rows, so
+// that G * q in 17..32 forms each tile's operands once); -1 when the shape is
+// not covered (the caller then reports the call as unsupported).
 int32_t da_split_int4_mfma(const da_host::SplitCall& call) {
-  if (!call.q_bf16 || (call.D != 128 && call.D != 64)) return -1;
+  if (call.D != 128 && call.D != 64) return -1;
   da_host::SplitCall c = call;
   if (c.rows > DA_MAX_ROWS) da_host::row_blocks(c.rows, 2 * DA_MAX_ROWS, c.nrb, c.rb_rows);
   const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block
   MfmaArgs a;
-  a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
+  a.q = c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
   a.ksz = (const uint8_t*)c.ks; a.vsz = (const uint8_t*)c.vs;
   a.pt = c.pt; a.seqlens = c.seqlens; a.sched = c.sched(); a.o = c.o; a.lse = c.lse;
   a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
@@ -682,7 +693,12 @@ int32_t da_split_int4_mfma(const da_host::SplitCall& call) {
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  if (c.D == 128) launch<128>(c, a, R);
-  else launch<64>(c, a, R);
+  if (c.q_bf16) {
+    if (c.D == 128) launch<128, false>(c, a, R);
+    else launch<64, false>(c, a, R);
+  } else {
+    if (c.D == 128) launch<128, true>(c, a, R);
+    else launch<64, true>(c, a, R);
+  }
   return da_host::launch_status();
 }

@@ -1,7 +1,7 @@
 // Stage 1 over an INT8 cache on the matrix cores (LightLLM PR #1549,
 // "Covered decode kernels": INT8 KV flash decode stage 1), for D = 128 or 64,
-// bf16 Q and G * q query rows per kv-head in blocks of up to 32 (one or two
-// 16-row tiles per workgroup).  Same contract as
+// bf16 or fp32 Q and G * q query rows per kv-head in blocks of up to 32 (one
+// or two 16-row tiles per workgroup).  Same contract as
 // decode_attn_split_int8: K = k_pool * k_scale, V = v_pool * v_scale, one
 // fp16 scale per (page, slot, kv-head).
 //
@@ -17,7 +17,9 @@
 // (b + 128) * 2^-24: an xor with 0x80 per byte and one byte permute per
 // element pair form it.  Q is scaled per row by a power of two (largest
 // element in [2^14, 2^15)) and held in fp16, exact for bf16 values, so the
-// products are exact in fp32.  The offset is taken out with the row's fp32
+// products are exact in fp32.  An fp32 Q is held as two fp16 terms, hi =
+// fp16(q') and lo = fp16(q' - hi) (22 significant bits; hi + lo is exact in
+// fp32), each taken through the QK product into the same accumulator.  The offset is taken out with the row's fp32
 // sum of scaled Q, and the token's scale multiplies the result:
 //   q.k = s * 2^-sh * 2^24 * (dot - 2^-24 * 128 * sum_d q'_d).
 // The PV product takes V = fp16(b * s) (b is exact in fp16, one rounding)
@@ -146,7 +148,7 @@ __device__ __forceinline__ int32_t read_stage(const uint32_t (&ka)[2], const uin
 }
 
 struct Int8Args {
-  const uint16_t* q;
+  const void* q;  // bf16 or fp32
   const uint8_t* k;
   const uint8_t* v;
   const uint8_t* ks;
@@ -174,8 +176,8 @@ __device__ __forceinline__ uint32_t code_pair_hi(uint32_t w) {
 }
 
 // NT row tiles of 16 query rows (NT * 16 rows per workgroup): the K and V
-// operands of a tile are formed once and serve every row tile.
-template <int D, int NT>
+// operands of a tile are formed once and serve every row tile.  QF: fp32 Q.
+template <int D, int NT, bool QF>
 __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8Args a) {
   using Gm = Geo<D>;
   constexpr int kD = D, kKb = Gm::kKb, kBlocks = Gm::kBlocks, kStages = Gm::kStages;
@@ -222,6 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
   // ---- Q^T operands: row tile rt, row lm, elements (D/4)*lg + 8*kb + e,
   // scaled by 2^sh, fp16
   uint32_t qv[NT][kKb][4];  // [rt][kb][pair]
+  uint32_t ql[NT][QF ? kKb : 1][4];  // fp32 Q: the lo terms
   float rowfac[NT];       // score (log2 units) = s * (rowfac * dot - qoff)
   float qoff[NT];         // rowfac * 128 * 2^-24 * sum of the row's scaled Q
   int tlim[NT];           // tokens t < tlim are visible to this lane's row
@@ -233,16 +236,11 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     const int i = r / a.G, h = g * a.G + r % a.G;
     const long long qoff_el = (((long long)b * a.qn + i) * a.Hq + h) * kD + (kD / 4) * lg;
     float qf[kKb][8];
-    const uint4* qp = reinterpret_cast<const uint4*>(a.q + qoff_el);
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb) {
-      const uint4 x = qp[kb];
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      load_q8<QF>(a.q, qoff_el + 8 * kb, qf[kb]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qf[kb][2 * e] = live ? da::bf16_lo(w[e]) : 0.f;
-        qf[kb][2 * e + 1] = live ? da::bf16_hi(w[e]) : 0.f;
-      }
+      for (int e = 0; e < 8; ++e) qf[kb][e] = live ? qf[kb][e] : 0.f;
     }
     float mx = 0.f;
 #pragma unroll
@@ -255,13 +253,22 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     float sum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb) {
+      float lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        qf[kb][e] = (float)(_Float16)ldexpf(qf[kb][e], sh);
+        const float x = ldexpf(qf[kb][e], sh);
+        qf[kb][e] = (float)(_Float16)x;
         sum += qf[kb][e];
+        if constexpr (QF) {
+          lo[e] = (float)(_Float16)(x - qf[kb][e]);
+          sum += lo[e];
+        }
       }
 #pragma unroll
-      for (int x = 0; x < 4; ++x) qv[rt][kb][x] = pack_h2(qf[kb][2 * x], qf[kb][2 * x + 1]);
+      for (int x = 0; x < 4; ++x) {
+        qv[rt][kb][x] = pack_h2(qf[kb][2 * x], qf[kb][2 * x + 1]);
+        if constexpr (QF) ql[rt][kb][x] = pack_h2(lo[2 * x], lo[2 * x + 1]);
+      }
     }
     sum += xor16(sum);
     sum += xor32(sum);
@@ -273,9 +280,13 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-    for (int kb = 0; kb < kKb; ++kb)
+    for (int kb = 0; kb < kKb; ++kb) {
       asm volatile("" : "+v"(qv[rt][kb][0]), "+v"(qv[rt][kb][1]), "+v"(qv[rt][kb][2]),
                    "+v"(qv[rt][kb][3]));
+      if constexpr (QF)
+        asm volatile("" : "+v"(ql[rt][kb][0]), "+v"(ql[rt][kb][1]), "+v"(ql[rt][kb][2]),
+                     "+v"(ql[rt][kb][3]));
+    }
   // tiles below every live row's limit need no masks (rows past the block
   // have tlim 0 and are never written, so they do not bound the unmasked region)
   int tfull;
@@ -384,6 +395,12 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
           const half2_t q2 = as_h2(qv[rt][kb][2]), q3 = as_h2(qv[rt][kb][3]);
           const half8_t qb = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
           dot[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, dot[rt], 0, 0, 0);
+          if constexpr (QF) {
+            const half2_t l0 = as_h2(ql[rt][kb][0]), l1 = as_h2(ql[rt][kb][1]);
+            const half2_t l2 = as_h2(ql[rt][kb][2]), l3 = as_h2(ql[rt][kb][3]);
+            const half8_t lb = {l0[0], l0[1], l1[0], l1[1], l2[0], l2[1], l3[0], l3[1]};
+            dot[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, lb, dot[rt], 0, 0, 0);
+          }
         }
       }
     }
@@ -534,29 +551,29 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
                                   s, kPScale, a.o, a.lse);
 }
 
-template <int D>
+template <int D, bool QF>
 void launch(const da_host::SplitCall& c, const Int8Args& a, int R) {
   if (R <= 16)
-    hipLaunchKernelGGL((split_int8_mfma_kernel<D, 1>), dim3(c.grid(true)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((split_int8_mfma_kernel<D, 1, QF>), dim3(c.grid(true)), dim3(kThreads), 0,
                        c.stream, a);
   else
-    hipLaunchKernelGGL((split_int8_mfma_kernel<D, 2>), dim3(c.grid(true)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((split_int8_mfma_kernel<D, 2, QF>), dim3(c.grid(true)), dim3(kThreads), 0,
                        c.stream, a);
 }
 
 }  // namespace
 
-// INT8 stage 1 on the matrix cores (D = 128 or 64), one row tile (up to 16
-// query rows per kv-head) or two (blocks of up to 32 rows, so that G * q in
-// 17..32 forms each tile's operands once); -1 when the shape is not covered
-// (the caller then uses the vector-ALU kernel).
+// INT8 stage 1 on the matrix cores (D = 128 or 64, bf16 or fp32 Q), one row
+// tile (up to 16 query rows per kv-head) or two (blocks of up to 32 rows, so
+// that G * q in 17..32 forms each tile's operands once); -1 when the shape is
+// not covered (the caller then reports the call as unsupported).
 int32_t da_split_int8_mfma(const da_host::SplitCall& call) {
-  if (!call.q_bf16 || (call.D != 128 && call.D != 64)) return -1;
+  if (call.D != 128 && call.D != 64) return -1;
   da_host::SplitCall c = call;
   if (c.rows > DA_MAX_ROWS) da_host::row_blocks(c.rows, 2 * DA_MAX_ROWS, c.nrb, c.rb_rows);
   const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block
   Int8Args a;
-  a.q = (const uint16_t*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
+  a.q = c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
   a.ks = (const uint8_t*)c.ks; a.vs = (const uint8_t*)c.vs;
   a.pt = c.pt; a.seqlens = c.seqlens; a.sched = c.sched(); a.o = c.o; a.lse = c.lse;
   a.pt_stride = c.pt_stride; a.max_pages = c.max_pages;
@@ -565,7 +582,12 @@ int32_t da_split_int8_mfma(const da_host::SplitCall& call) {
   a.slot_stride = c.kv.slot; a.head_stride = c.kv.head;
   a.scale_log2 = c.scale * da::kLog2e;
   a.causal = c.causal;
-  if (c.D == 128) launch<128>(c, a, R);
-  else launch<64>(c, a, R);
+  if (c.q_bf16) {
+    if (c.D == 128) launch<128, false>(c, a, R);
+    else launch<64, false>(c, a, R);
+  } else {
+    if (c.D == 128) launch<128, true>(c, a, R);
+    else launch<64, true>(c, a, R);
+  }
   return da_host::launch_status();
 }

@@ -13,8 +13,9 @@ Gates for floating point, by output type:
   max-abs <= 1e-2 on top of half a bf16 ulp of each value.
 * stage-1 partials (fp32): |dO| <= 2e-5 * (1 + |O|), |d lse| <= 1e-4, and the
   empty splits (lse = -inf) must coincide exactly.
-* stage-1 partials of the matrix-core paths (bf16 Q; INT4 and INT8 with any
-  number of query rows per kv-head): the P.V product takes P
+* stage-1 partials of the matrix-core paths (INT4 and INT8 with any number
+  of query rows per kv-head; bf16 Q exact in fp16, fp32 Q as hi + lo fp16
+  terms, 22 bits, whose 2^-22 relative residue is far inside these gates): the P.V product takes P
   and the dequantised V in fp16 (unit roundoff u = 2^-11).  P enters as
   fp16(p * 2^7) (one relative rounding, p * 2^7 stays in fp16's normal range
   down to p = 2^-21); INT8 V as fp16(b * s) (one rounding); INT4 V as
@@ -212,14 +213,15 @@ def rows_per_block(w: W.Workload) -> int:
 
 
 def uses_matrix_path(w: W.Workload) -> bool:
-    """Whether stage 1 over this workload runs on the matrix cores (bf16 Q,
-    D = 128 or 64): INT4 and INT8 with any number of query rows per kv-head, a
-    dense bf16 cache with 6 or more (rows beyond 16 in blocks of up to 32)."""
+    """Whether stage 1 over this workload runs on the matrix cores (D = 128 or
+    64): INT4 and INT8 (bf16 or fp32 Q) with any number of query rows per
+    kv-head, a dense bf16 cache with 6 or more (rows beyond 16 in blocks of up
+    to 32)."""
     rows = w.group * w.q_per_req
-    if w.dtype == "fp32":
-        return False
     if w.kv in (W.KV_INT4, W.KV_INT8):
         return True
+    if w.dtype == "fp32":
+        return False
     return rows >= 6
 
 

@@ -54,6 +54,10 @@ INT8_ODD_HKV = W.INT8_B32.scaled(name="int8_hkv3_g2_small", batch=4, num_q_heads
                                  num_kv_heads=3, lengths="list", length_list=(5, 64, 129, 1100))
 INT8_FP32Q = W.INT8_B32.scaled(name="int8_fp32q_small", batch=3, dtype="fp32", lengths="list",
                                length_list=(1, 100, 700))
+INT8_FP32Q_MTP = W.INT8_B32.scaled(name="int8_fp32q_mtp4_r16", batch=3, dtype="fp32", q_per_req=4,
+                                   causal=True, lengths="list", length_list=(2, 65, 1200))
+INT8_FP32Q_D64 = W.INT8_B32.scaled(name="int8_fp32q_d64_r4", batch=3, dtype="fp32", head_dim=64,
+                                   lengths="list", length_list=(1, 300, 900))
 INT8_D64 = W.INT8_B32.scaled(name="int8_d64_small", batch=3, head_dim=64, lengths="list",
                              length_list=(7, 64, 1000))
 INT8_D64_MTP = W.INT8_B32.scaled(name="int8_d64_mtp4_r16_p16", batch=4, q_per_req=4, causal=True,
@@ -75,6 +79,13 @@ INT4_D64_Q1 = W.INT4_MTP_B64.scaled(name="int4_d64_q1_r4", batch=4, head_dim=64,
 INT4_D64_R20 = W.INT4_MTP_B64.scaled(name="int4_d64_g5_mtp4_r20_p128", batch=3, num_q_heads=40,
                                      head_dim=64, page_size=128, lengths="list",
                                      length_list=(3, 129, 2100))
+INT4_FP32Q = W.INT4_MTP_B64.scaled(name="int4_fp32q_mtp4_r16", batch=4, dtype="fp32",
+                                   lengths="list", length_list=(1, 5, 129, 1400))
+INT4_FP32Q_Q1 = W.INT4_MTP_B64.scaled(name="int4_fp32q_q1_r4", batch=3, dtype="fp32", q_per_req=1,
+                                      causal=False, lengths="list", length_list=(7, 64, 800))
+INT4_FP32Q_D64 = W.INT4_MTP_B64.scaled(name="int4_fp32q_d64_r16_p32", batch=3, dtype="fp32",
+                                       head_dim=64, page_size=32, lengths="list",
+                                       length_list=(3, 100, 1000))
 INT4_G8Q2 = W.INT4_MTP_B64.scaled(name="int4_g8_mtp2_small", batch=3, num_q_heads=64, q_per_req=2,
                                   lengths="list", length_list=(1, 48, 700))
 
@@ -106,7 +117,8 @@ SMALL = [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, D64_G8, D64_MTP, D64_R20,
          MHA_P32, MTP_BF16, MTP_BF16_G2Q3,
          INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV, INT8_FP32Q, INT8_D64, INT8_D64_MTP, INT8_D64_R20,
          INT4_SMALL, INT4_Q1,
-         INT4_R12, INT4_G8Q2, INT4_D64, INT4_D64_Q1, INT4_D64_R20]
+         INT4_R12, INT4_G8Q2, INT4_D64, INT4_D64_Q1, INT4_D64_R20, INT8_FP32Q_MTP, INT8_FP32Q_D64,
+         INT4_FP32Q, INT4_FP32Q_Q1, INT4_FP32Q_D64]
 
 
 def both_layouts(ws):
