@@ -65,6 +65,17 @@ PATHS = [
                           length_list=(4, 300, 900)),                      # INT4 matrix cores
     W.TINY_FP32.scaled(name="chk_fp32", batch=3, lengths="list", length_list=(1, 300, 900),
                        pool_pages=0),                                      # vector-ALU kernel
+    # the head-dim-64 and fp32-query instances of the matrix-core kernels
+    W.BF16_MTP_B64.scaled(name="chk_bf16_mtp_d64", batch=3, head_dim=64, lengths="list",
+                          length_list=(4, 300, 900)),
+    W.INT8_B32.scaled(name="chk_int8_d64", batch=3, head_dim=64, lengths="list",
+                      length_list=(1, 300, 900)),
+    W.INT4_MTP_B64.scaled(name="chk_int4_mtp_d64", batch=3, head_dim=64, lengths="list",
+                          length_list=(4, 300, 900)),
+    W.INT8_B32.scaled(name="chk_int8_fp32q", batch=3, dtype="fp32", lengths="list",
+                      length_list=(1, 300, 900)),
+    W.INT4_MTP_B64.scaled(name="chk_int4_mtp_fp32q", batch=3, dtype="fp32", lengths="list",
+                          length_list=(4, 300, 900)),
 ]
 
 
