@@ -477,6 +477,9 @@ def tune_variants(which):
 
     variants = [W.RAGGED_B64, W.BF16_B16, W.INT8_B32, W.INT4_MTP_B64, W.BF16_MTP_B64,
                 W.BF16_MTP_G5_B64]
+    # the same shapes at head dim 64 (one per stage-1 kernel)
+    variants += [v.scaled(name=v.name.replace("_d128_", "_d64_"), head_dim=64)
+                 for v in (W.RAGGED_B64, W.INT8_B32, W.INT4_MTP_B64, W.BF16_MTP_B64)]
     if which == "all":
         return variants
     keep = set(which.split(","))
