@@ -200,6 +200,23 @@ int32_t decode_attn_metadata_ex(const int32_t* seq_lens, const int64_t* req_pool
                                 int32_t* work_list, int32_t work_capacity, void* stream);
 
 /*
+ * Stage-1 numerics (all paths accumulate in fp32 and keep one running max and
+ * sum per query row; scores are formed in log2 units and exponentials are
+ * exp2):
+ *   - fp32 cache and Q: fp32 throughout.
+ *   - bf16 cache, up to 5 query rows per kv-head: fp32 products of the bf16
+ *     values, weights p in fp32.
+ *   - bf16 cache, 6 or more rows: matrix-core products of the bf16 values
+ *     (exact in fp32); p enters the P.V product as two bf16 terms, hi + lo,
+ *     within 2^-16 |p|.
+ *   - INT8 / INT4 caches: scores exact up to fp32 rounding (codes and Q enter
+ *     the matrix cores exactly; a bf16 Q after a per-row power-of-two scaling,
+ *     an fp32 Q as two fp16 terms of 22 significant bits together); the P.V
+ *     product takes p and the dequantised V in fp16, one rounding each.
+ * Partial outputs are the normalised fp32 rows O_s and their natural-log LSE.
+ */
+
+/*
  * Stage 1 over a dense bf16 or fp32 cache (GQA flash decode "stage 1" and
  * the num_splits KV-cache decode of LightLLM PR #1549, "Covered decode
  * kernels").  q and the pools share `dtype` (DA_BF16 or DA_FP32).
