@@ -1,5 +1,6 @@
-// Stage 1 of split-KV decode attention over an fp32 cache with fp32 Q,
-// vector-ALU path (GQA flash decode "stage 1" and the num_splits KV-cache
+// Stage 1 of split-KV decode attention over an fp32 cache with fp32 Q at
+// D = 64 and one or two query rows per kv-head (the other fp32 shapes go to
+// split_f32_mfma.hip), vector-ALU path (GQA flash decode "stage 1" and the num_splits KV-cache
 // decode of LightLLM PR #1549, section "Covered decode kernels"), and the
 // C-ABI entry points of stage 1, which validate the call and dispatch every
 // other cache format to its specialised kernel (split_bf16.hip,
@@ -245,21 +246,11 @@ int32_t launch_rt(const SplitArgs& a, unsigned grid, hipStream_t st) {
   return da_host::launch_status();
 }
 
-// a.R: rows per block (at most DA_MAX_ROWS)
-template <int D>
-int32_t launch_d(const SplitArgs& a, unsigned grid, hipStream_t st) {
-  const int R = a.R;
-  if (R <= 1) return launch_rt<D, 1>(a, grid, st);
-  if (R <= 2) return launch_rt<D, 2>(a, grid, st);
-  if (R <= 4) return launch_rt<D, 4>(a, grid, st);
-  if (R <= 5) return launch_rt<D, 5>(a, grid, st);
-  if (R <= 8) return launch_rt<D, 8>(a, grid, st);
-  return launch_rt<D, 16>(a, grid, st);
-}
-
+// the shapes the fp32 matrix-core kernel leaves: D = 64, one or two rows
 int32_t launch_f32(const da_host::SplitCall& c, const SplitArgs& a) {
+  if (c.D != 64 || a.R > 2) return DA_ERR_UNSUPPORTED;
   const unsigned grid = c.grid(false);
-  return c.D == 128 ? launch_d<128>(a, grid, c.stream) : launch_d<64>(a, grid, c.stream);
+  return a.R == 1 ? launch_rt<64, 1>(a, grid, c.stream) : launch_rt<64, 2>(a, grid, c.stream);
 }
 
 int32_t check_common(const da_host::SplitCall& c, int32_t kv_layout) {
@@ -338,6 +329,7 @@ int32_t da_split_bf16_mfma(const da_host::SplitCall& c);  // split_bf16_mfma.hip
 // (rows per block: every kernel takes the rows of one row block, see DA_MAX_ROWS)
 int32_t da_split_int8_mfma(const da_host::SplitCall& c);  // split_int8.hip: bf16 or fp32 Q
 int32_t da_split_int4_mfma(const da_host::SplitCall& c);  // split_int4.hip: bf16 or fp32 Q
+int32_t da_split_f32_mfma(const da_host::SplitCall& c);   // split_f32_mfma.hip: fp32, see there
 
 extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k_pool,
                                      const void* v_pool, const int32_t* page_table,
@@ -363,7 +355,8 @@ extern "C" int32_t decode_attn_split(const void* q, int32_t dtype, const void* k
     const int32_t mf = da_split_bf16_mfma(c);
     return mf >= 0 ? mf : DA_ERR_UNSUPPORTED;
   }
-  return launch_f32(c, make_args(c));
+  const int32_t mf = da_split_f32_mfma(c);
+  return mf >= 0 ? mf : launch_f32(c, make_args(c));
 }
 
 extern "C" int32_t decode_attn_split_int8(

@@ -63,8 +63,8 @@ PATHS = [
     W.INT8_B32.scaled(name="chk_int8", batch=3, lengths="list", length_list=(1, 300, 900)),
     W.INT4_MTP_B64.scaled(name="chk_int4_mtp", batch=3, lengths="list",
                           length_list=(4, 300, 900)),                      # INT4 matrix cores
-    W.TINY_FP32.scaled(name="chk_fp32", batch=3, lengths="list", length_list=(1, 300, 900),
-                       pool_pages=0),                                      # vector-ALU kernel
+    W.TINY_FP32.scaled(name="chk_fp32_g2", batch=3, num_q_heads=2, lengths="list",
+                       length_list=(1, 300, 900), pool_pages=0),          # fp32 vector ALU
     # the head-dim-64 and fp32-query instances of the matrix-core kernels
     W.BF16_MTP_B64.scaled(name="chk_bf16_mtp_d64", batch=3, head_dim=64, lengths="list",
                           length_list=(4, 300, 900)),
@@ -76,6 +76,8 @@ PATHS = [
                       length_list=(1, 300, 900)),
     W.INT4_MTP_B64.scaled(name="chk_int4_mtp_fp32q", batch=3, dtype="fp32", lengths="list",
                           length_list=(4, 300, 900)),
+    W.TINY_FP32.scaled(name="chk_fp32_g8", batch=3, num_q_heads=8, num_kv_heads=1,
+                       lengths="list", length_list=(1, 300, 900), pool_pages=0),  # fp32 matrix cores
 ]
 
 
