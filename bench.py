@@ -119,7 +119,7 @@ def stage1_kernel(w):
         return "split_int8_mfma_kernel", ["split_int8.hip", "mfma_util.h", "common.h"]
     if w.kv == W.KV_INT4:
         return "split_int4_mfma_kernel", ["split_int4.hip", "mfma_util.h", "common.h"]
-    if w.head_dim == 128 or rows > 2:  # fp32 cache
+    if rows >= 5:  # fp32 cache
         return "split_f32_mfma_kernel", ["split_f32_mfma.hip", "mfma_util.h", "common.h"]
     return "split_fma_kernel", ["split_fma.hip", "common.h"]
 

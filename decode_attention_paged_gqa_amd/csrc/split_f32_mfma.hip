@@ -1,10 +1,10 @@
 // Stage 1 over a dense fp32 cache with fp32 Q on the matrix cores (the GQA
-// flash decode of LightLLM PR #1549, "Covered decode kernels", at fp32), in
-// blocks of one or two 16-row tiles: every row count at D = 128, 3 or more
-// query rows per kv-head at D = 64.  Same contract as decode_attn_split.  On
-// the vector ALU each query row costs a dot product and a cross-lane sum per
-// token, so fp32 stops being memory-bound there beyond a few rows; the fp32
-// matrix product takes up to 16 rows per tile at one cost.
+// flash decode of LightLLM PR #1549, "Covered decode kernels", at fp32), for
+// 5 or more query rows per kv-head, in blocks of one or two 16-row tiles.
+// Same contract as decode_attn_split.  On the vector ALU each query row costs
+// a dot product and a cross-lane sum per token, so fp32 stops being
+// memory-bound there beyond 4 rows; the fp32 matrix product takes up to 16
+// rows per tile at one cost.
 //
 // One workgroup (4 waves) per (kv-head g, split s, request b); 16-token
 // tiles dealt round-robin to the waves.  Per tile and wave:
@@ -421,17 +421,15 @@ void launch(const da_host::SplitCall& c, const F32MfmaArgs& a, int R) {
 
 }  // namespace
 
-// fp32 stage 1 on the matrix cores: any number of query rows per kv-head at
-// D = 128, 3 or more at D = 64 (one row tile up to 16 rows, two for blocks of
-// up to 32); -1 when the shape is not covered (the caller then uses the
-// vector-ALU kernel, which streams a 64-element row with one or two query
-// rows slightly faster: 84 / 81 % of 8 TB/s against 81 / 78 %).
+// fp32 stage 1 on the matrix cores for 5 or more query rows per kv-head (one
+// row tile up to 16 rows, two for blocks of up to 32); -1 for fewer, which
+// stay on the vector ALU (split_fma.hip).
 int32_t da_split_f32_mfma(const da_host::SplitCall& call) {
   if (call.q_bf16 || (call.D != 128 && call.D != 64)) return -1;
   da_host::SplitCall c = call;
   if (c.rows > DA_MAX_ROWS) da_host::row_blocks(c.rows, 2 * DA_MAX_ROWS, c.nrb, c.rb_rows);
   const int G = c.Hq / c.Hkv, R = c.rb_rows;  // rows per block
-  if (c.D == 64 && R <= 2) return -1;
+  if (R < 5) return -1;
   F32MfmaArgs a;
   a.q = (const float*)c.q; a.k = (const uint8_t*)c.k; a.v = (const uint8_t*)c.v;
   a.pt = c.pt; a.seqlens = c.seqlens; a.sched = c.sched(); a.o = c.o; a.lse = c.lse;

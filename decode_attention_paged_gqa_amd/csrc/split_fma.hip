@@ -1,6 +1,5 @@
-// Stage 1 of split-KV decode attention over an fp32 cache with fp32 Q at
-// D = 64 and one or two query rows per kv-head (the other fp32 shapes go to
-// split_f32_mfma.hip), vector-ALU path (GQA flash decode "stage 1" and the num_splits KV-cache
+// Stage 1 of split-KV decode attention over an fp32 cache with fp32 Q and up
+// to 4 query rows per kv-head (more go to split_f32_mfma.hip), vector-ALU path (GQA flash decode "stage 1" and the num_splits KV-cache
 // decode of LightLLM PR #1549, section "Covered decode kernels"), and the
 // C-ABI entry points of stage 1, which validate the call and dispatch every
 // other cache format to its specialised kernel (split_bf16.hip,
@@ -246,11 +245,18 @@ int32_t launch_rt(const SplitArgs& a, unsigned grid, hipStream_t st) {
   return da_host::launch_status();
 }
 
-// the shapes the fp32 matrix-core kernel leaves: D = 64, one or two rows
+// a.R: rows per block; the fp32 matrix-core kernel takes 5 or more
+template <int D>
+int32_t launch_d(const SplitArgs& a, unsigned grid, hipStream_t st) {
+  if (a.R <= 1) return launch_rt<D, 1>(a, grid, st);
+  if (a.R <= 2) return launch_rt<D, 2>(a, grid, st);
+  return launch_rt<D, 4>(a, grid, st);
+}
+
 int32_t launch_f32(const da_host::SplitCall& c, const SplitArgs& a) {
-  if (c.D != 64 || a.R > 2) return DA_ERR_UNSUPPORTED;
+  if (a.R > 4) return DA_ERR_UNSUPPORTED;
   const unsigned grid = c.grid(false);
-  return a.R == 1 ? launch_rt<64, 1>(a, grid, c.stream) : launch_rt<64, 2>(a, grid, c.stream);
+  return c.D == 128 ? launch_d<128>(a, grid, c.stream) : launch_d<64>(a, grid, c.stream);
 }
 
 int32_t check_common(const da_host::SplitCall& c, int32_t kv_layout) {

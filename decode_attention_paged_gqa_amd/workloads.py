@@ -116,8 +116,10 @@ BF16_MTP_G5_B64 = INT4_MTP_B64.scaled(name="bf16_mtp4_b64_hq40_hkv8_d128_p64_L8k
 INT4_MTP_D64_B64 = INT4_MTP_B64.scaled(name="int4kv_mtp4_b64_hq32_hkv8_d64_p64_L8k-32k",
                                        head_dim=64, seed=8)
 
-# a dense fp32 cache (fp32 Q) at the bf16 B=16 shape, on the fp32 matrix cores
-FP32_B16 = BF16_B16.scaled(name="fp32_b16_hq32_hkv8_d128_p64_L8192", dtype="fp32", seed=9)
+# a dense fp32 cache (fp32 Q), B=16, G=8: 8 query rows per kv-head, on the fp32
+# matrix cores
+FP32_B16 = BF16_B16.scaled(name="fp32_b16_hq64_hkv8_d128_p64_L8192", dtype="fp32",
+                           num_q_heads=64, seed=9)
 
 WORKLOADS = {w.name: w for w in (TINY_FP32, BF16_B16, RAGGED_B64, UNIFORM_B64,
                                  INT8_B32, INT4_MTP_B64, BF16_MTP_B64, BF16_MTP_G5_B64,

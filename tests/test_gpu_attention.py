@@ -38,7 +38,10 @@ D64_R20 = W.BF16_B16.scaled(name="d64_mtp4_g5_r20_p32", batch=3, num_q_heads=40,
 D64_G6_P128 = W.BF16_B16.scaled(name="d64_g6_p128", batch=4, num_q_heads=12, num_kv_heads=2,
                                 head_dim=64, page_size=128, lengths="list",
                                 length_list=(127, 128, 129, 3000))
-# fp32 at D = 64 with one or two query rows per kv-head: the vector-ALU kernel
+# fp32 with up to 4 query rows per kv-head: the vector-ALU kernel
+FP32_G4_D128 = W.TINY_FP32.scaled(name="fp32_g4_d128_p64", batch=4, num_q_heads=8, num_kv_heads=2,
+                                  head_dim=128, page_size=64, lengths="list",
+                                  length_list=(1, 64, 65, 1300), pool_pages=0)
 FP32_G2 = W.TINY_FP32.scaled(name="fp32_g2_d64_p16", batch=6, num_q_heads=4, num_kv_heads=2,
                              lengths="list", length_list=(0, 1, 15, 16, 17, 700), pool_pages=0)
 FP32_G1_NC = W.TINY_FP32.scaled(name="fp32_mha_d64_p64", batch=3, num_q_heads=3, num_kv_heads=3,
@@ -134,7 +137,7 @@ def test_tiny_fp32_every_split(gpu, S):
 
 
 SMALL = [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, D64_G8, D64_MTP, D64_R20, D64_G6_P128,
-         FP32_G2, FP32_G1_NC, FP32_G5, FP32_G8_P16, FP32_MTP, FP32_R20, MHA_P32, MTP_BF16, MTP_BF16_G2Q3,
+         FP32_G2, FP32_G1_NC, FP32_G4_D128, FP32_G5, FP32_G8_P16, FP32_MTP, FP32_R20, MHA_P32, MTP_BF16, MTP_BF16_G2Q3,
          INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV, INT8_FP32Q, INT8_D64, INT8_D64_MTP, INT8_D64_R20,
          INT4_SMALL, INT4_Q1,
          INT4_R12, INT4_G8Q2, INT4_D64, INT4_D64_Q1, INT4_D64_R20, INT8_FP32Q_MTP, INT8_FP32Q_D64,
