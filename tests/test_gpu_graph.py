@@ -37,6 +37,13 @@ CASES = [
                              length_list=(4, 700, 2100)),
     W.INT4_MTP_B64.scaled(name="graph_int4_mtp_20rows", batch=3, num_q_heads=40, lengths="list",
                           length_list=(6, 500, 1900)),
+    # head dim 64, and the fp32 matrix-core kernel
+    W.INT8_B32.scaled(name="graph_int8_d64", batch=3, head_dim=64, lengths="list",
+                      length_list=(5, 900, 2300)),
+    W.BF16_MTP_B64.scaled(name="graph_bf16_mtp_d64", batch=3, head_dim=64, lengths="list",
+                          length_list=(2, 333, 2000)),
+    W.FP32_B16.scaled(name="graph_fp32_8rows", batch=3, lengths="list",
+                      length_list=(7, 640, 1800)),
 ]
 
 
