@@ -482,25 +482,38 @@ def tune_variants(which):
     # the same shapes at head dim 64 (one per stage-1 kernel)
     variants += [v.scaled(name=v.name.replace("_d128_", "_d64_"), head_dim=64)
                  for v in (W.RAGGED_B64, W.INT8_B32, W.INT4_MTP_B64, W.BF16_MTP_B64)]
+    # the bf16 vector kernel over the token-major pool layout
+    variants += [v.scaled(name=v.name + "_nhd", kv_layout="NHD") for v in (W.RAGGED_B64, W.BF16_B16)]
     if which == "all":
         return variants
     keep = set(which.split(","))
     return [v for v in variants if kv_name(v) in keep or v.name in keep]
 
 
-def tune(da, torch, which="all"):
-    """Sweep num_splits per KV-length bucket and batch key; write splits_table.json."""
+def tune(da, torch, which="all", old_keys=None):
+    """Sweep num_splits per KV-length bucket and batch key; write splits_table.json.
+    A variant's row for a batch key of ``old_keys`` (the batch keys the table's
+    rows were tuned for; default: those of the loaded table) is kept (set
+    DECODE_ATTN_RETUNE=1 to sweep every key again)."""
     from decode_attention_paged_gqa_amd import workloads as W
     from decode_attention_paged_gqa_amd.splits import (BATCH_KEYS, BUCKET_TOKENS, CANDIDATES,
                                                        N_BUCKETS, SplitTable, kernel_key)
 
     table = SplitTable.load()
+    old_keys = list(table.batch_keys) if old_keys is None else list(old_keys)
+    retune = os.environ.get("DECODE_ATTN_RETUNE") == "1"
+    table.batch_keys = list(BATCH_KEYS)  # rows of variants not swept here stop matching
     variants = tune_variants(which)
     for base in variants:
         key = kernel_key(kv_name(base), rows_per_kv_head(base), base.head_dim, base.page_size,
                          base.kv_layout)
+        old = table.tables.get(key)
+        old = old if old is not None and len(old) == len(old_keys) else None
         rows = []
         for bk in BATCH_KEYS:
+            if old is not None and bk in old_keys and not retune:
+                rows.append(old[old_keys.index(bk)])
+                continue
             row = []
             for k in range(1, N_BUCKETS + 1):
                 # representative batches: the bucket's upper length for one request, the
@@ -526,21 +539,30 @@ def tune(da, torch, which="all"):
     print(json.dumps({"tuned": list(table.tables)}), flush=True)
 
 
-def tune_chunks(da, torch, which="all"):
+def tune_chunks(da, torch, which="all", old_keys=None):
     """Sweep the per-request split size (pages) per batch key over ragged batches
     whose longest request sits in buckets 2, 4 and 8 (the 32K representative
-    length); write the best size per batch key into splits_table.json."""
+    length); write the best size per batch key into splits_table.json.  Sizes
+    already tuned for a batch key of ``old_keys`` are kept, as in tune()."""
     from decode_attention_paged_gqa_amd import workloads as W
     from decode_attention_paged_gqa_amd.splits import (BATCH_KEYS, CHUNK_CANDIDATES, SplitTable,
                                                        kernel_key, per_request_table)
 
     table = SplitTable.load()
+    old_keys = list(table.batch_keys) if old_keys is None else list(old_keys)
+    retune = os.environ.get("DECODE_ATTN_RETUNE") == "1"
+    table.batch_keys = list(BATCH_KEYS)
     variants = tune_variants(which)
     for base in variants:
         key = kernel_key(kv_name(base), rows_per_kv_head(base), base.head_dim, base.page_size,
                          base.kv_layout)
+        old = table.chunk_pages.get(key)
+        old = old if old is not None and len(old) == len(old_keys) else None
         row = []
         for bk in BATCH_KEYS:
+            if old is not None and bk in old_keys and not retune:
+                row.append(old[old_keys.index(bk)])
+                continue
             tot = {c: 0.0 for c in CHUNK_CANDIDATES}
             for k in (2, 4, 8):
                 Lmax = k * BUCKET_TOKENS
@@ -803,10 +825,12 @@ def main():
 
     da.load()
     if args.tune or args.tune_chunks:
+        from decode_attention_paged_gqa_amd.splits import SplitTable
+        old_keys = SplitTable.load().batch_keys  # what the stored rows were tuned for
         if args.tune:
-            tune(da, torch, args.tune)
+            tune(da, torch, args.tune, old_keys)
         if args.tune_chunks:
-            tune_chunks(da, torch, args.tune_chunks)
+            tune_chunks(da, torch, args.tune_chunks, old_keys)
         return
     w = W.WORKLOADS[args.workload]
     batch = make_resident(da, w, torch)

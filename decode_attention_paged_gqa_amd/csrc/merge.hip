@@ -7,7 +7,8 @@
 //
 // One wave per query row; the reduction over splits stays in registers:
 // every lane owns D/64 output elements and walks all splits itself, the
-// split weights being wave-uniform.  With per-request split counts, the rows
+// split weights being wave-uniform.  Split rows are loaded kPrefetch at a
+// time ahead of their use (the first group before the split count is known).  With per-request split counts, the rows
 // of request b combine only their first counts[b] split slots (clamped to
 // [1, S]); the other slots are never read.
 #include "common.h"
@@ -74,14 +75,28 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(const float* __restr
         for (int e = 0; e < E; ++e) acc[e] = fmaf(w, pre[s][e], acc[e]);
       }
     }
-    for (int s = kPrefetch; s < S; ++s) {
-      const int k = s >> 6;
-      const float lk = k == 0 ? lv[0] : k == 1 ? lv[1] : k == 2 ? lv[2] : lv[3];
-      const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lk), s & 63));
-      const float w = da::fast_exp2(fmaf(ls, da::kLog2e, -ml));
-      wsum += w;
+    // the rest in groups of kPrefetch: a group's rows are all loaded before
+    // any is used, so a row costs a fraction of a memory round trip
+    for (int s0 = kPrefetch; s0 < S; s0 += kPrefetch) {
+      float buf[kPrefetch][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(w, o[(long long)s * D + e], acc[e]);
+      for (int u = 0; u < kPrefetch; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          buf[u][e] = s0 + u < S ? o[(long long)(s0 + u) * D + e] : 0.f;
+#pragma unroll
+      for (int u = 0; u < kPrefetch; ++u) {
+        const int s = s0 + u;
+        if (s < S) {
+          const int k = s >> 6;
+          const float lk = k == 0 ? lv[0] : k == 1 ? lv[1] : k == 2 ? lv[2] : lv[3];
+          const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lk), s & 63));
+          const float w = da::fast_exp2(fmaf(ls, da::kLog2e, -ml));
+          wsum += w;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] = fmaf(w, buf[u][e], acc[e]);
+        }
+      }
     }
     const float inv = 1.f / wsum;
 #pragma unroll

@@ -30,9 +30,9 @@ TABLE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "splits_ta
 REPRESENTATIVE_KV_LEN = 32768
 BUCKET_TOKENS = 4096
 N_BUCKETS = 8
-BATCH_KEYS = (16, 32, 64)
-CANDIDATES = (1, 2, 4, 8, 16, 32)
-CHUNK_CANDIDATES = (16, 24, 32, 48, 64, 96, 128, 192)
+BATCH_KEYS = (1, 4, 16, 32, 64)
+CANDIDATES = (1, 2, 4, 8, 16, 32, 64, 128)
+CHUNK_CANDIDATES = (8, 16, 24, 32, 48, 64, 96, 128, 192)
 DEFAULT_CHUNK_PAGES = 64
 
 
@@ -90,8 +90,11 @@ class SplitTable:
             f.write("\n".join(lines) + "\n")
 
     def table_for(self, key: str) -> List[List[int]]:
-        if key in self.tables:
-            return self.tables[key]
+        """The variant's [batch key][bucket] counts; the heuristic when it is not
+        tuned, or was tuned for another set of batch keys."""
+        rows = self.tables.get(key)
+        if rows is not None and len(rows) == len(self.batch_keys):
+            return rows
         return [[_heuristic(b, k + 1) for k in range(N_BUCKETS)] for b in self.batch_keys]
 
     def pick(self, key: str, batch: int, kv_len: int = REPRESENTATIVE_KV_LEN) -> int:
@@ -102,7 +105,7 @@ class SplitTable:
     def chunk_for(self, key: str, batch: int) -> int:
         """Tuned split size in pages for per-request counts (nearest batch key)."""
         row = self.chunk_pages.get(key)
-        if not row:
+        if not row or len(row) != len(self.batch_keys):
             return DEFAULT_CHUNK_PAGES
         return decode_attn_pick_splits([[c] for c in row], self.batch_keys, 1, batch, 1)
 

@@ -208,7 +208,7 @@ def test_split_table_roundtrip(tmp_path, lib):
     assert kernel_key("int4", 16, 128, 64, "HND") == "int4_r16_d128_p64_hnd"
     t = SplitTable()
     key = kernel_key("bf16", 5, 128, 64)
-    t.tables[key] = [[1, 2, 4, 4, 8, 8, 16, 16]] * 3
+    t.tables[key] = [[1, 2, 4, 4, 8, 8, 16, 16]] * len(t.batch_keys)
     p = tmp_path / "t.json"
     t.save(str(p))
     t2 = SplitTable.load(str(p))
@@ -218,6 +218,12 @@ def test_split_table_roundtrip(tmp_path, lib):
     # untuned variants fall back to a heuristic in range
     s = t2.pick(kernel_key("int8", 4, 128, 64), 32, 32768)
     assert 1 <= s <= 32
+    # rows tuned for another set of batch keys are not read (heuristic / default instead)
+    t2.tables[key] = [[7] * 8] * (len(t2.batch_keys) - 2)
+    t2.chunk_pages[key] = [40] * (len(t2.batch_keys) + 1)
+    assert t2.table_for(key) != t2.tables[key]
+    assert 1 <= t2.pick(key, 64, 32768) <= 32
+    assert t2.chunk_for(key, 64) == 64  # the default split size
 
 
 def test_binding_rejects_host_tensors(lib):
