@@ -98,49 +98,6 @@ def decode_attention(q, k_pool, v_pool, page_table, seq_lens, page_size, scale,
     return out, lse
 
 
-def decode_attention_rows(q, k_pool, v_pool, page_table, seq_lens, page_size, scale,
-                          causal, rows, kv="dense", k_scale=None, v_scale=None):
-    """The same definition evaluated only at ``rows`` = [(b, i, h), ...].
-
-    Used where the whole batch is too large for one CPU run: one request's
-    pages are gathered (and, for ``kv`` = "int8" / "int4", decoded by
-    ``oracle.quant``) once per distinct (b, kv-head).  Dense pools are float64;
-    quantised pools are the raw codes with ``k_scale`` / ``v_scale`` holding
-    the fp16 bit patterns.  Returns (out [len(rows), D], lse [len(rows)]).
-    """
-    from . import quant
-
-    B, qn, Hq, D = q.shape
-    Hkv = k_pool.shape[2]
-    G = Hq // Hkv
-
-    def tokens(pool, sc, g, b, L):
-        x = gather_tokens(pool[:, :, g], page_table[b], L, page_size)
-        if kv == "dense":
-            return x
-        s = gather_tokens(sc[:, :, g], page_table[b], L, page_size)
-        if kv == "int8":
-            return quant.dequant_int8(x, s)
-        if kv == "int4":
-            return quant.dequant_int4(x, s)
-        raise ValueError(kv)
-
-    out = np.zeros((len(rows), D), dtype=np.float64)
-    lse = np.full(len(rows), NEG_INF, dtype=np.float64)
-    cache = {}
-    for r, (b, i, h) in enumerate(rows):
-        g = h // G
-        key = (b, g)
-        if key not in cache:
-            L = max(0, int(seq_lens[b]))
-            cache.clear()
-            cache[key] = (L, tokens(k_pool, k_scale, g, b, L), tokens(v_pool, v_scale, g, b, L))
-        L, Kg, Vg = cache[key]
-        n = visible_length(L, qn, i, causal)
-        out[r], lse[r] = attend(q[b, i, h], Kg[:n], Vg[:n], scale)
-    return out, lse
-
-
 def split_token_range(L: int, page_size: int, num_splits: int, s: int):
     """Token range [t0, t1) handled by split ``s``.
 

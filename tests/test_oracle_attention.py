@@ -235,14 +235,3 @@ def test_page_permutation_invariance_is_exact():
     np.testing.assert_array_equal(out, out2)
     np.testing.assert_array_equal(lse, lse2)
 
-
-def test_rows_variant_matches_full_oracle():
-    rng = np.random.default_rng(9)
-    L = [3, 40, 17]
-    q, kp, vp, pt, _, _ = _dense_problem(rng, 3, 2, 4, 2, 8, 8, L)
-    out, lse = OA.decode_attention(q, kp, vp, pt, np.array(L), 8, 0.5, causal=True)
-    rows = [(b, i, h) for b in range(3) for i in range(2) for h in range(4)]
-    o2, l2 = OA.decode_attention_rows(q, kp, vp, pt, np.array(L), 8, 0.5, True, rows)
-    for r, (b, i, h) in enumerate(rows):
-        assert np.array_equal(o2[r], out[b, i, h])
-        assert l2[r] == lse[b, i, h]

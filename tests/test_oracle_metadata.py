@@ -34,6 +34,32 @@ def test_hand_built_batch(mode, key, extra):
     assert md["batch_order"].tolist() == e["batch_order"]
 
 
+def test_paged_layout_predicate_rejects_broken_layouts():
+    """paged_layout_holds must say False whenever one token slot is not where
+    the page table puts it: a moved slot, two swapped pages, a shifted
+    offset inside a page, or a request row read through the wrong index."""
+    w = W.BF16_B16.scaled(batch=4, length=200)
+    rng = np.random.Generator(np.random.PCG64(1000 + w.seed))
+    L = W.draw_lengths(w, rng)
+    pt, r2t, rpi, P = W.build_layout(w, L, rng)
+    S = w.page_size
+    assert OM.paged_layout_holds(pt, L, rpi, r2t, S)
+    r = r2t.copy()
+    r[rpi[2], 137] += 1  # one slot of request 2 moved by one
+    assert not OM.paged_layout_holds(pt, L, rpi, r, S)
+    p = pt.copy()
+    p[1, [0, 2]] = p[1, [2, 0]]  # two pages of request 1 swapped in the table
+    assert not OM.paged_layout_holds(p, L, rpi, r2t, S)
+    r = r2t.copy()
+    r[rpi[0], :S] = r[rpi[0], :S][::-1]  # offsets inside the first page reversed
+    assert not OM.paged_layout_holds(pt, L, rpi, r, S)
+    assert not OM.paged_layout_holds(pt, L, rpi[::-1].copy(), r2t, S)  # rows crossed
+    # tokens past a request's length do not matter
+    r = r2t.copy()
+    r[rpi[3], int(L[3]):] = -7
+    assert OM.paged_layout_holds(pt, L, rpi, r, S)
+
+
 @pytest.mark.parametrize("w", [W.TINY_FP32, W.BF16_B16.scaled(batch=5, length=300),
                                W.RAGGED_B64.scaled(batch=9, length_lo=3, length_hi=500)],
                          ids=lambda w: w.name)
