@@ -19,6 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
 # the same library with the device-data contract checks (decode_attn_checks)
 CHECKED_LIB_PATH = os.path.join(_HERE, "libdecode_attn_checked.so")
+# the same library with AddressSanitizer on its host code (build.py --asan)
+ASAN_LIB_PATH = os.path.join(_HERE, "libdecode_attn_asan.so")
 
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_LAUNCH = 0, 1, 2, 3
 DA_FP32, DA_BF16 = 0, 1
@@ -73,11 +75,12 @@ class DecodeAttnError(ValueError):
 
 def load(path: Optional[str] = None, reload: bool = False):
     """Load the HIP library (once; ``reload`` switches to ``path``, e.g.
-    CHECKED_LIB_PATH).  Raises if it has not been built."""
+    CHECKED_LIB_PATH).  Without ``path``: $DECODE_ATTN_LIB if set (one of the
+    built variants), else LIB_PATH.  Raises if it has not been built."""
     global _lib
     if _lib is not None and not reload:
         return _lib
-    path = path or LIB_PATH
+    path = path or os.environ.get("DECODE_ATTN_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m decode_attention_paged_gqa_amd.build`")
@@ -104,7 +107,9 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, device=None, ndim=None):
+def _need(t: torch.Tensor, name: str, dtype=None, device=None, ndim=None, shape=None):
+    """Type, dtype, device, rank, exact shape and contiguity of one tensor
+    (that it lives on a GPU is checked last, by _gpu, after every shape)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
@@ -113,10 +118,17 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None, ndim=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, has {t.dim()}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, has {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _gpu(**tensors):
+    """Every named tensor (None skipped) is a GPU tensor."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
 
 
 # ------------------------------------------------------------------ metadata
@@ -141,8 +153,14 @@ def decode_attn_metadata(seq_lens, req_pool_indices, req_to_token, page_size, ma
     B = seq_lens.shape[0]
     if req_pool_indices.shape[0] != B:
         raise ValueError("req_pool_indices length != batch")
+    if q_mode not in (DA_Q_STRIDED, DA_Q_CUMSUM, DA_Q_PRESET):
+        raise ValueError(f"unknown q_mode {q_mode}")
     if q_in is not None:
         _need(q_in, "q_in", torch.int32, dev, 1)
+    # CUMSUM reads q_in[0 .. B-1], PRESET q_in[0 .. B]
+    q_need = {DA_Q_STRIDED: 0, DA_Q_CUMSUM: B, DA_Q_PRESET: B + 1}[q_mode]
+    if q_need and (q_in is None or q_in.shape[0] < q_need):
+        raise ValueError(f"q_in needs at least {q_need} entries for q_mode {q_mode}")
     out = dict(out or {})
     mk = lambda k, n: out.get(k) if out.get(k) is not None else torch.empty(n, dtype=torch.int32, device=dev)
     out["cache_seqlens"] = mk("cache_seqlens", (B,))
@@ -150,14 +168,16 @@ def decode_attn_metadata(seq_lens, req_pool_indices, req_to_token, page_size, ma
     out["cu_seqlens_q"] = mk("cu_seqlens_q", (B + 1,))
     out["page_table"] = mk("page_table", (B, max_pages))
     out["batch_order"] = mk("batch_order", (B,))
-    for k in ("cache_seqlens", "cu_seqlens_k", "cu_seqlens_q", "page_table", "batch_order"):
-        _need(out[k], k, torch.int32, dev)
-    if tuple(out["page_table"].shape) != (B, max_pages):
-        raise ValueError("page_table must be [batch, max_pages]")
+    shapes = {"cache_seqlens": (B,), "cu_seqlens_k": (B + 1,), "cu_seqlens_q": (B + 1,),
+              "page_table": (B, max_pages), "batch_order": (B,)}
+    for k, shp in shapes.items():
+        _need(out[k], k, torch.int32, dev, shape=shp)
     if full_to_swa is not None or split_table is not None:
         return _metadata_ex(lib, dev, B, seq_lens, req_pool_indices, req_to_token, page_size,
                             max_pages, q_mode, q_in, q_stride, out, mk, full_to_swa,
                             split_table, bucket_tokens, max_splits, work_capacity)
+    _gpu(seq_lens=seq_lens, req_pool_indices=req_pool_indices, req_to_token=req_to_token,
+         q_in=q_in, **{k: out[k] for k in shapes})
     st = lib.decode_attn_metadata(
         _ptr(seq_lens), _ptr(req_pool_indices), _ptr(req_to_token), req_to_token.shape[0],
         req_to_token.shape[1], req_to_token.stride(0), B, page_size, max_pages, q_mode,
@@ -175,9 +195,7 @@ def _metadata_ex(lib, dev, B, seq_lens, rpi, r2t, page_size, max_pages, q_mode, 
         _need(full_to_swa, "full_to_swa", torch.int64, dev, 1)
         f2s_len = full_to_swa.shape[0]
         out["swa_page_table"] = mk("swa_page_table", (B, max_pages))
-        _need(out["swa_page_table"], "swa_page_table", torch.int32, dev)
-        if tuple(out["swa_page_table"].shape) != (B, max_pages):
-            raise ValueError("swa_page_table must be [batch, max_pages]")
+        _need(out["swa_page_table"], "swa_page_table", torch.int32, dev, shape=(B, max_pages))
     table_host, nb, smax = None, 0, 0
     if split_table is not None:
         vals = [int(x) for x in split_table]
@@ -191,6 +209,10 @@ def _metadata_ex(lib, dev, B, seq_lens, rpi, r2t, page_size, max_pages, q_mode, 
             _need(out[k], k, torch.int32, dev, 1)
         if out["work_list"].shape[0] != cap or out["split_counts"].shape[0] != B:
             raise ValueError("split_counts / work_list sized for another batch or capacity")
+    _gpu(seq_lens=seq_lens, req_pool_indices=rpi, req_to_token=r2t, q_in=q_in,
+         full_to_swa=full_to_swa, **{k: v for k, v in out.items() if k in (
+             "cache_seqlens", "cu_seqlens_k", "cu_seqlens_q", "page_table", "batch_order",
+             "swa_page_table", "split_counts", "work_list")})
     st = lib.decode_attn_metadata_ex(
         _ptr(seq_lens), _ptr(rpi), _ptr(r2t), r2t.shape[0], r2t.shape[1], r2t.stride(0), B,
         page_size, max_pages, q_mode, _ptr(q_in), q_stride, _ptr(out["cache_seqlens"]),
@@ -229,10 +251,8 @@ def _partials(q, num_splits, o_partial, lse_partial):
         o_partial = torch.empty((B, qn, Hq, num_splits, D), dtype=torch.float32, device=q.device)
     if lse_partial is None:
         lse_partial = torch.empty((B, qn, Hq, num_splits), dtype=torch.float32, device=q.device)
-    _need(o_partial, "o_partial", torch.float32, q.device)
-    _need(lse_partial, "lse_partial", torch.float32, q.device)
-    if o_partial.numel() != B * qn * Hq * num_splits * D or lse_partial.numel() != B * qn * Hq * num_splits:
-        raise ValueError("partial buffers are sized for a different num_splits")
+    _need(o_partial, "o_partial", torch.float32, q.device, shape=(B, qn, Hq, num_splits, D))
+    _need(lse_partial, "lse_partial", torch.float32, q.device, shape=(B, qn, Hq, num_splits))
     return o_partial, lse_partial
 
 
@@ -292,6 +312,9 @@ def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
         raise ValueError("head_dim mismatch")
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
+    _gpu(q=q, k_pool=k_pool, v_pool=v_pool, page_table=page_table, cache_seqlens=cache_seqlens,
+         batch_order=batch_order, split_counts=split_counts, work_list=work_list,
+         o_partial=o_partial, lse_partial=lse_partial)
     st = lib.decode_attn_split(
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), page_table.stride(0),
         page_table.shape[1], _ptr(cache_seqlens), _ptr(batch_order), B, qn, Hq, Hkv, D, S_p, P,
@@ -321,9 +344,15 @@ def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cach
     if v_pool.shape != k_pool.shape or tuple(k_scale.shape) != tuple(k_pool.shape[:3]) \
             or k_scale.shape != v_scale.shape:
         raise ValueError("int8 pool / scale shapes inconsistent")
-    B, qn, Hq, _ = q.shape
+    B, qn, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("head_dim mismatch")
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
+    _gpu(q=q, k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale,
+         page_table=page_table, cache_seqlens=cache_seqlens, batch_order=batch_order,
+         split_counts=split_counts, work_list=work_list, o_partial=o_partial,
+         lse_partial=lse_partial)
     st = lib.decode_attn_split_int8(
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
         _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
@@ -361,6 +390,10 @@ def decode_attn_split_int4(q, k_pool, v_pool, k_scale_zero, v_scale_zero, page_t
         raise ValueError("head_dim mismatch")
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
+    _gpu(q=q, k_pool=k_pool, v_pool=v_pool, k_scale_zero=k_scale_zero,
+         v_scale_zero=v_scale_zero, page_table=page_table, cache_seqlens=cache_seqlens,
+         batch_order=batch_order, split_counts=split_counts, work_list=work_list,
+         o_partial=o_partial, lse_partial=lse_partial)
     st = lib.decode_attn_split_int4(
         _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale_zero), _ptr(v_scale_zero),
         _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
@@ -405,6 +438,8 @@ def decode_attn_append_kv(k_new, v_new, out_cache_loc, k_pool, v_pool, k_scale=N
         want = tuple(k_pool.shape[:3]) + (() if fmt == DA_CACHE_INT8 else (D // 32, 2))
         if tuple(k_scale.shape) != want or v_scale.shape != k_scale.shape:
             raise ValueError(f"scale shape must be {want}")
+    _gpu(k_new=k_new, v_new=v_new, out_cache_loc=out_cache_loc, k_pool=k_pool, v_pool=v_pool,
+         k_scale=k_scale, v_scale=v_scale)
     st = lib.decode_attn_append_kv(_ptr(k_new), _ptr(v_new), _q_code(k_new), _ptr(out_cache_loc),
                                    N, Hkv, D, fmt, _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
                                    _ptr(v_scale), S_p, P, lay, _stream(dev))
@@ -425,15 +460,15 @@ def decode_attn_merge(o_partial, lse_partial, out_dtype=torch.bfloat16, out=None
         raise ValueError("lse_partial shape mismatch")
     if out is None:
         out = torch.empty((B, qn, Hq, D), dtype=out_dtype, device=dev)
-    _need(out, "out", (torch.bfloat16, torch.float32), dev)
+    _need(out, "out", (torch.bfloat16, torch.float32), dev, shape=(B, qn, Hq, D))
     if want_lse and lse_out is None:
         lse_out = torch.empty((B, qn, Hq), dtype=torch.float32, device=dev)
     if lse_out is not None:
-        _need(lse_out, "lse_out", torch.float32, dev)
+        _need(lse_out, "lse_out", torch.float32, dev, shape=(B, qn, Hq))
     if split_counts is not None:
-        _need(split_counts, "split_counts", torch.int32, dev, 1)
-        if split_counts.shape[0] != B:
-            raise ValueError("split_counts length != batch")
+        _need(split_counts, "split_counts", torch.int32, dev, shape=(B,))
+    _gpu(o_partial=o_partial, lse_partial=lse_partial, out=out, lse_out=lse_out,
+         split_counts=split_counts)
     code = DA_BF16 if out.dtype == torch.bfloat16 else DA_FP32
     st = lib.decode_attn_merge(_ptr(o_partial), _ptr(lse_partial), B, qn, Hq, D, S,
                                _ptr(split_counts), _ptr(out), code, _ptr(lse_out), _stream(dev))
@@ -464,8 +499,9 @@ def decode_attn_gather_kv(pool, page_table, cache_seqlens, cu_seqlens_k, total_t
     lay = _layout_code(kv_layout)
     _need(pool, "pool", None, dev)
     _need(page_table, "page_table", torch.int32, dev, 2)
-    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
-    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev, 1)
+    Bt = page_table.shape[0]
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, shape=(Bt,))
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev, shape=(Bt + 1,))
     if pool.dim() < 3:
         raise ValueError("pool needs at least [pages, slots, heads] dims")
     P, S_p, Hkv = _pool_dims(pool, lay)
@@ -473,7 +509,9 @@ def decode_attn_gather_kv(pool, page_table, cache_seqlens, cu_seqlens_k, total_t
     row_bytes = pool[0, 0, 0].numel() * pool.element_size()
     if out is None:
         out = torch.empty((total_tokens, Hkv) + row, dtype=pool.dtype, device=dev)
-    _need(out, "out", pool.dtype, dev)
+    _need(out, "out", pool.dtype, dev, shape=(total_tokens, Hkv) + row)
+    _gpu(pool=pool, page_table=page_table, cache_seqlens=cache_seqlens,
+         cu_seqlens_k=cu_seqlens_k, out=out)
     st = lib.decode_attn_gather_kv(_ptr(pool), row_bytes, Hkv, lay, S_p, P, _ptr(page_table),
                                    page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
                                    _ptr(cu_seqlens_k), page_table.shape[0], _ptr(out), _stream(dev))

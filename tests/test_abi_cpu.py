@@ -101,6 +101,16 @@ def test_split_validation(lib, kw, status):
     assert lib.decode_attn_split(*_split_args(**kw)) == status
 
 
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), float("-inf"), 0.0, -0.125,
+                                   -0.0])
+def test_softmax_scale_must_be_finite_and_positive(lib, scale):
+    base = _split_args(scale=scale)
+    assert lib.decode_attn_split(*base) == 1
+    q8 = base[:2] + [FAKE, FAKE, FAKE, FAKE] + base[4:]
+    assert lib.decode_attn_split_int8(*q8) == 1
+    assert lib.decode_attn_split_int4(*q8) == 1
+
+
 def test_int8_int4_validation(lib):
     base = _split_args()
     # (q, q_dtype, k, v, k_scale, v_scale, ...) -- null scales are invalid
@@ -234,3 +244,60 @@ def test_binding_rejects_host_tensors(lib):
     sl = torch.zeros(2, dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU"):
         da.decode_attn_split(q, kp, kp, pt, sl, 2)
+
+
+def test_binding_checks_shapes_before_any_pointer_is_passed(lib):
+    """Every size the kernels rely on is checked in the binding, so a wrongly
+    sized tensor is a ValueError, never an out-of-bounds device access.  Host
+    tensors are used: the shape checks come before the GPU-residency check,
+    which then rejects the correctly shaped call."""
+    import torch
+    nb, Hq, Hkv, D, P, ps, S = 2, 8, 2, 128, 6, 16, 3
+    pt = torch.zeros(nb, 4, dtype=torch.int32)
+    sl = torch.zeros(nb, dtype=torch.int32)
+    # INT8: q's head dim must be the pool's
+    k8 = torch.zeros(P, ps, Hkv, D, dtype=torch.int8)
+    sc = torch.zeros(P, ps, Hkv, dtype=torch.float16)
+    with pytest.raises(ValueError, match="head_dim"):
+        da.decode_attn_split_int8(torch.zeros(nb, 1, Hq, 64), k8, k8, sc, sc, pt, sl, S)
+    with pytest.raises(ValueError, match="GPU"):
+        da.decode_attn_split_int8(torch.zeros(nb, 1, Hq, D), k8, k8, sc, sc, pt, sl, S)
+    # caller-supplied partials must match (nb, q, Hq, S, D) exactly
+    q = torch.zeros(nb, 1, Hq, D, dtype=torch.bfloat16)
+    kb = torch.zeros(P, ps, Hkv, D, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="o_partial must have shape"):
+        da.decode_attn_split(q, kb, kb, pt, sl, S, o_partial=torch.zeros(nb, 1, Hq, D, S))
+    # merge: out (nb, q, Hq, D), lse_out (nb, q, Hq), split_counts (nb,)
+    o = torch.zeros(nb, 1, Hq, S, D)
+    lse = torch.zeros(nb, 1, Hq, S)
+    with pytest.raises(ValueError, match="out must have shape"):
+        da.decode_attn_merge(o, lse, out=torch.zeros(nb, 1, Hq, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="lse_out must have shape"):
+        da.decode_attn_merge(o, lse, lse_out=torch.zeros(nb * Hq))
+    with pytest.raises(ValueError, match="split_counts must have shape"):
+        da.decode_attn_merge(o, lse, split_counts=torch.ones(nb + 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):
+        da.decode_attn_merge(o, lse, out=torch.zeros(nb, 1, Hq, D), lse_out=torch.zeros(nb, 1, Hq))
+    # metadata: outputs of length nb / nb + 1, and q_in long enough for its mode
+    seq = torch.zeros(nb, dtype=torch.int32)
+    rpi = torch.zeros(nb, dtype=torch.int64)
+    r2t = torch.zeros(nb, 64, dtype=torch.int32)
+    bad_out = {"cu_seqlens_k": torch.zeros(nb, dtype=torch.int32)}
+    with pytest.raises(ValueError, match="cu_seqlens_k must have shape"):
+        da.decode_attn_metadata(seq, rpi, r2t, ps, 4, out=bad_out)
+    with pytest.raises(ValueError, match="batch_order must have shape"):
+        da.decode_attn_metadata(seq, rpi, r2t, ps, 4,
+                                out={"batch_order": torch.zeros(nb + 1, dtype=torch.int32)})
+    with pytest.raises(ValueError, match="q_in needs at least 2"):
+        da.decode_attn_metadata(seq, rpi, r2t, ps, 4, q_mode=B.DA_Q_CUMSUM)
+    with pytest.raises(ValueError, match="q_in needs at least 3"):
+        da.decode_attn_metadata(seq, rpi, r2t, ps, 4, q_mode=B.DA_Q_PRESET,
+                                q_in=torch.zeros(nb, dtype=torch.int32))
+    with pytest.raises(ValueError, match="unknown q_mode"):
+        da.decode_attn_metadata(seq, rpi, r2t, ps, 4, q_mode=5)
+    with pytest.raises(ValueError, match="GPU"):
+        da.decode_attn_metadata(seq, rpi, r2t, ps, 4, q_mode=B.DA_Q_PRESET,
+                                q_in=torch.zeros(nb + 1, dtype=torch.int32))
+    # gather: per-request arrays sized by the page table's batch
+    with pytest.raises(ValueError, match="cu_seqlens_k must have shape"):
+        da.decode_attn_gather_kv(kb, pt, sl, torch.zeros(nb, dtype=torch.int32), 10)
