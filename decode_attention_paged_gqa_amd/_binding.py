@@ -22,7 +22,7 @@ CHECKED_LIB_PATH = os.path.join(_HERE, "libdecode_attn_checked.so")
 # the same library with AddressSanitizer on its host code (build.py --asan)
 ASAN_LIB_PATH = os.path.join(_HERE, "libdecode_attn_asan.so")
 
-DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_LAUNCH = 0, 1, 2, 3
+DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_LAUNCH, DA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 DA_FP32, DA_BF16 = 0, 1
 DA_KV_NHD, DA_KV_HND = 0, 1
 DA_CACHE_DENSE, DA_CACHE_INT8, DA_CACHE_INT4 = 0, 1, 2
@@ -30,6 +30,7 @@ CACHE_FORMATS = {"dense": DA_CACHE_DENSE, "int8": DA_CACHE_INT8, "int4": DA_CACH
 KV_LAYOUTS = {"NHD": DA_KV_NHD, "HND": DA_KV_HND}
 DA_Q_STRIDED, DA_Q_CUMSUM, DA_Q_PRESET = 0, 1, 2
 DA_MAX_SPLITS = 256
+DA_STATIC_SCRATCH_BYTES = 64 << 20  # scratch of decode_attn_decode_static, per GPU
 # decode_attn_checks flag bits
 DA_CHECK_PAGE_ID, DA_CHECK_SEQLEN, DA_CHECK_ORDER, DA_CHECK_WORK = 0x01, 0x02, 0x04, 0x08
 DA_CHECK_COUNTS, DA_CHECK_REQ_ROW, DA_CHECK_TOO_LONG = 0x10, 0x20, 0x40
@@ -55,6 +56,9 @@ _SIGS = {
     "decode_attn_split_int4": [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I32,
                                _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _F32,
                                _I32, _P, _P, _P],
+    "decode_attn_decode_static": [_P, _I32, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32,
+                                  _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32,
+                                  _F32, _I32, _P, _I32, _P, _P],
     "decode_attn_merge": [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _P, _P],
     "decode_attn_append_kv": [_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32,
                               _I32, _P],
@@ -256,6 +260,43 @@ def _partials(q, num_splits, o_partial, lse_partial):
     return o_partial, lse_partial
 
 
+def _pool_geometry(fmt, q, k_pool, v_pool, k_scale, v_scale, lay):
+    """Checks the pools (and scales) of a cache format against each other and
+    against q; returns (num_pages, page_size, Hkv, D)."""
+    dev = q.device
+    if fmt == DA_CACHE_DENSE:
+        _need(k_pool, "k_pool", q.dtype, dev, 4)
+        _need(v_pool, "v_pool", q.dtype, dev, 4)
+        if k_pool.shape != v_pool.shape:
+            raise ValueError("k_pool / v_pool shapes differ")
+        D = k_pool.shape[3]
+    elif fmt == DA_CACHE_INT8:
+        _need(k_pool, "k_pool", torch.int8, dev, 4)
+        _need(v_pool, "v_pool", torch.int8, dev, 4)
+        _need(k_scale, "k_scale", torch.float16, dev, 3)
+        _need(v_scale, "v_scale", torch.float16, dev, 3)
+        D = k_pool.shape[3]
+        if v_pool.shape != k_pool.shape or tuple(k_scale.shape) != tuple(k_pool.shape[:3]) \
+                or k_scale.shape != v_scale.shape:
+            raise ValueError("int8 pool / scale shapes inconsistent")
+    elif fmt == DA_CACHE_INT4:
+        _need(k_pool, "k_pool", torch.uint8, dev, 4)
+        _need(v_pool, "v_pool", torch.uint8, dev, 4)
+        _need(k_scale, "k_scale_zero", torch.float16, dev, 5)
+        _need(v_scale, "v_scale_zero", torch.float16, dev, 5)
+        D = 2 * k_pool.shape[3]
+        if v_pool.shape != k_pool.shape or \
+                tuple(k_scale.shape) != tuple(k_pool.shape[:3]) + (D // 32, 2) \
+                or k_scale.shape != v_scale.shape:
+            raise ValueError("int4 pool / scale-zero shapes inconsistent")
+    else:
+        raise ValueError(f"cache_format must be one of {tuple(CACHE_FORMATS)}")
+    if q.shape[3] != D:
+        raise ValueError("head_dim mismatch")
+    P, S_p, Hkv = _pool_dims(k_pool, lay)
+    return P, S_p, Hkv, D
+
+
 def _q_code(q):
     if q.dtype == torch.bfloat16:
         return DA_BF16
@@ -298,30 +339,9 @@ def decode_attn_split(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
     Pools are [P, page_size, Hkv, D] (kv_layout "NHD") or [P, Hkv, page_size, D] ("HND").
     With ``work_list`` / ``split_counts`` (from ``decode_attn_metadata(split_table=...)``)
     request b has split_counts[b] splits and ``num_splits`` is the slots per row."""
-    lib = load()
-    dev = _split_common(q, page_table, cache_seqlens, batch_order, split_counts, work_list)
-    lay = _layout_code(kv_layout)
-    _need(k_pool, "k_pool", q.dtype, dev, 4)
-    _need(v_pool, "v_pool", q.dtype, dev, 4)
-    if k_pool.shape != v_pool.shape:
-        raise ValueError("k_pool / v_pool shapes differ")
-    P, S_p, Hkv = _pool_dims(k_pool, lay)
-    D = k_pool.shape[3]
-    B, qn, Hq, Dq = q.shape
-    if Dq != D:
-        raise ValueError("head_dim mismatch")
-    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
-    o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
-    _gpu(q=q, k_pool=k_pool, v_pool=v_pool, page_table=page_table, cache_seqlens=cache_seqlens,
-         batch_order=batch_order, split_counts=split_counts, work_list=work_list,
-         o_partial=o_partial, lse_partial=lse_partial)
-    st = lib.decode_attn_split(
-        _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), page_table.stride(0),
-        page_table.shape[1], _ptr(cache_seqlens), _ptr(batch_order), B, qn, Hq, Hkv, D, S_p, P,
-        lay, num_splits, *_sched_args(split_counts, work_list), scale,
-        int(bool(causal)), _ptr(o_partial), _ptr(lse_partial), _stream(dev))
-    _check(st, "decode_attn_split")
-    return o_partial, lse_partial
+    return _split(DA_CACHE_DENSE, "decode_attn_split", q, k_pool, v_pool, None, None,
+                  page_table, cache_seqlens, num_splits, softmax_scale, causal, o_partial,
+                  lse_partial, batch_order, kv_layout, split_counts, work_list)
 
 
 def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cache_seqlens,
@@ -332,36 +352,9 @@ def decode_attn_split_int8(q, k_pool, v_pool, k_scale, v_scale, page_table, cach
 
     Pools [P, page_size, Hkv, D] with scales [P, page_size, Hkv] ("NHD"), or
     [P, Hkv, page_size, D] with [P, Hkv, page_size] ("HND")."""
-    lib = load()
-    dev = _split_common(q, page_table, cache_seqlens, batch_order, split_counts, work_list)
-    lay = _layout_code(kv_layout)
-    _need(k_pool, "k_pool", torch.int8, dev, 4)
-    _need(v_pool, "v_pool", torch.int8, dev, 4)
-    _need(k_scale, "k_scale", torch.float16, dev, 3)
-    _need(v_scale, "v_scale", torch.float16, dev, 3)
-    P, S_p, Hkv = _pool_dims(k_pool, lay)
-    D = k_pool.shape[3]
-    if v_pool.shape != k_pool.shape or tuple(k_scale.shape) != tuple(k_pool.shape[:3]) \
-            or k_scale.shape != v_scale.shape:
-        raise ValueError("int8 pool / scale shapes inconsistent")
-    B, qn, Hq, Dq = q.shape
-    if Dq != D:
-        raise ValueError("head_dim mismatch")
-    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
-    o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
-    _gpu(q=q, k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale,
-         page_table=page_table, cache_seqlens=cache_seqlens, batch_order=batch_order,
-         split_counts=split_counts, work_list=work_list, o_partial=o_partial,
-         lse_partial=lse_partial)
-    st = lib.decode_attn_split_int8(
-        _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
-        _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
-        _ptr(batch_order), B, qn,
-        Hq, Hkv, D, S_p, P, lay, num_splits, *_sched_args(split_counts, work_list), scale,
-        int(bool(causal)), _ptr(o_partial),
-        _ptr(lse_partial), _stream(dev))
-    _check(st, "decode_attn_split_int8")
-    return o_partial, lse_partial
+    return _split(DA_CACHE_INT8, "decode_attn_split_int8", q, k_pool, v_pool, k_scale, v_scale,
+                  page_table, cache_seqlens, num_splits, softmax_scale, causal, o_partial,
+                  lse_partial, batch_order, kv_layout, split_counts, work_list)
 
 
 def decode_attn_split_int4(q, k_pool, v_pool, k_scale_zero, v_scale_zero, page_table,
@@ -372,37 +365,74 @@ def decode_attn_split_int4(q, k_pool, v_pool, k_scale_zero, v_scale_zero, page_t
 
     Pools [P, page_size, Hkv, D/2] with (scale, zero) [P, page_size, Hkv, D/32, 2]
     ("NHD"), or the first three dims as [P, Hkv, page_size] ("HND")."""
+    return _split(DA_CACHE_INT4, "decode_attn_split_int4", q, k_pool, v_pool, k_scale_zero,
+                  v_scale_zero, page_table, cache_seqlens, num_splits, softmax_scale, causal,
+                  o_partial, lse_partial, batch_order, kv_layout, split_counts, work_list)
+
+
+def _split(fmt, name, q, k_pool, v_pool, k_scale, v_scale, page_table, cache_seqlens,
+           num_splits, softmax_scale, causal, o_partial, lse_partial, batch_order, kv_layout,
+           split_counts, work_list):
     lib = load()
     dev = _split_common(q, page_table, cache_seqlens, batch_order, split_counts, work_list)
     lay = _layout_code(kv_layout)
-    _need(k_pool, "k_pool", torch.uint8, dev, 4)
-    _need(v_pool, "v_pool", torch.uint8, dev, 4)
-    _need(k_scale_zero, "k_scale_zero", torch.float16, dev, 5)
-    _need(v_scale_zero, "v_scale_zero", torch.float16, dev, 5)
-    P, S_p, Hkv = _pool_dims(k_pool, lay)
-    D = 2 * k_pool.shape[3]
-    if v_pool.shape != k_pool.shape or \
-            tuple(k_scale_zero.shape) != tuple(k_pool.shape[:3]) + (D // 32, 2) \
-            or k_scale_zero.shape != v_scale_zero.shape:
-        raise ValueError("int4 pool / scale-zero shapes inconsistent")
-    B, qn, Hq, Dq = q.shape
-    if Dq != D:
-        raise ValueError("head_dim mismatch")
+    P, S_p, Hkv, D = _pool_geometry(fmt, q, k_pool, v_pool, k_scale, v_scale, lay)
+    B, qn, Hq, _ = q.shape
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     o_partial, lse_partial = _partials(q, num_splits, o_partial, lse_partial)
-    _gpu(q=q, k_pool=k_pool, v_pool=v_pool, k_scale_zero=k_scale_zero,
-         v_scale_zero=v_scale_zero, page_table=page_table, cache_seqlens=cache_seqlens,
-         batch_order=batch_order, split_counts=split_counts, work_list=work_list,
-         o_partial=o_partial, lse_partial=lse_partial)
-    st = lib.decode_attn_split_int4(
-        _ptr(q), _q_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale_zero), _ptr(v_scale_zero),
-        _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
-        _ptr(batch_order), B, qn,
-        Hq, Hkv, D, S_p, P, lay, num_splits, *_sched_args(split_counts, work_list), scale,
-        int(bool(causal)), _ptr(o_partial),
-        _ptr(lse_partial), _stream(dev))
-    _check(st, "decode_attn_split_int4")
+    _gpu(q=q, k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale,
+         page_table=page_table, cache_seqlens=cache_seqlens, batch_order=batch_order,
+         split_counts=split_counts, work_list=work_list, o_partial=o_partial,
+         lse_partial=lse_partial)
+    pools = (_ptr(k_pool), _ptr(v_pool)) + (() if fmt == DA_CACHE_DENSE else
+                                            (_ptr(k_scale), _ptr(v_scale)))
+    st = getattr(lib, name)(
+        _ptr(q), _q_code(q), *pools, _ptr(page_table), page_table.stride(0),
+        page_table.shape[1], _ptr(cache_seqlens), _ptr(batch_order), B, qn, Hq, Hkv, D, S_p, P,
+        lay, num_splits, *_sched_args(split_counts, work_list), scale, int(bool(causal)),
+        _ptr(o_partial), _ptr(lse_partial), _stream(dev))
+    _check(st, name)
     return o_partial, lse_partial
+
+
+def decode_attn_decode_static(q, k_pool, v_pool, page_table, cache_seqlens, num_splits,
+                              softmax_scale=None, causal=False, k_scale=None, v_scale=None,
+                              cache_format="dense", out=None, out_dtype=torch.bfloat16,
+                              lse_out=None, want_lse=False, batch_order=None, kv_layout="NHD",
+                              split_counts=None, work_list=None):
+    """Stage 1 and the merge in one call, the split partials in the library's
+    per-GPU scratch array (the C call allocates nothing; pass ``out`` to
+    allocate nothing here either).  Same arguments and result as
+    decode_attn_split[_int8|_int4] followed by decode_attn_merge; ``k_scale`` /
+    ``v_scale`` are the quantised formats' scales or (scale, zero) pairs.
+    Returns out (and lse if requested)."""
+    lib = load()
+    fmt = CACHE_FORMATS.get(cache_format) if isinstance(cache_format, str) else int(cache_format)
+    if fmt not in (DA_CACHE_DENSE, DA_CACHE_INT8, DA_CACHE_INT4):
+        raise ValueError(f"cache_format must be one of {tuple(CACHE_FORMATS)}")
+    dev = _split_common(q, page_table, cache_seqlens, batch_order, split_counts, work_list)
+    lay = _layout_code(kv_layout)
+    P, S_p, Hkv, D = _pool_geometry(fmt, q, k_pool, v_pool, k_scale, v_scale, lay)
+    B, qn, Hq, _ = q.shape
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, qn, Hq, D), dtype=out_dtype, device=dev)
+    _need(out, "out", (torch.bfloat16, torch.float32), dev, shape=(B, qn, Hq, D))
+    if want_lse and lse_out is None:
+        lse_out = torch.empty((B, qn, Hq), dtype=torch.float32, device=dev)
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, dev, shape=(B, qn, Hq))
+    _gpu(q=q, k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale,
+         page_table=page_table, cache_seqlens=cache_seqlens, batch_order=batch_order,
+         split_counts=split_counts, work_list=work_list, out=out, lse_out=lse_out)
+    st = lib.decode_attn_decode_static(
+        _ptr(q), _q_code(q), fmt, _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+        _ptr(page_table), page_table.stride(0), page_table.shape[1], _ptr(cache_seqlens),
+        _ptr(batch_order), B, qn, Hq, Hkv, D, S_p, P, lay, num_splits,
+        *_sched_args(split_counts, work_list), scale, int(bool(causal)), _ptr(out),
+        DA_BF16 if out.dtype == torch.bfloat16 else DA_FP32, _ptr(lse_out), _stream(dev))
+    _check(st, "decode_attn_decode_static")
+    return (out, lse_out) if (want_lse or lse_out is not None) else out
 
 
 # ------------------------------------------------------------------ KV append

@@ -39,6 +39,7 @@ extern "C" const char* decode_attn_strerror(int32_t status) {
     case DA_ERR_INVALID_ARG: return "invalid argument";
     case DA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case DA_ERR_LAUNCH: return "kernel launch failed";
+    case DA_ERR_TOO_LARGE: return "partials exceed the static scratch buffer";
     default: return "unknown status";
   }
 }

@@ -24,8 +24,10 @@
  *
  * Conventions for every call:
  *   - Pointers are device pointers unless stated "host".  All memory is
- *     owned and allocated by the caller; the library never allocates, frees
- *     or synchronises, and never reads device data on the host.
+ *     owned and allocated by the caller (the one exception is the scratch
+ *     array of decode_attn_decode_static, which the library holds per GPU);
+ *     the library never allocates, frees or synchronises, and never reads
+ *     device data on the host.
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *     Work is enqueued asynchronously on it; every call can be recorded in
  *     a HIP graph.
@@ -79,6 +81,7 @@ extern "C" {
 #define DA_ERR_INVALID_ARG 1  /* null pointer, non-positive size, Hq % Hkv, range */
 #define DA_ERR_UNSUPPORTED 2  /* a shape / dtype no kernel is built for          */
 #define DA_ERR_LAUNCH 3       /* hipGetLastError() after the launch               */
+#define DA_ERR_TOO_LARGE 4    /* partials beyond DA_STATIC_SCRATCH_BYTES (decode_attn_decode_static) */
 
 /* element types */
 #define DA_FP32 0
@@ -112,6 +115,8 @@ extern "C" {
 /* limits of the built kernels */
 #define DA_MAX_SPLITS 256
 #define DA_MAX_Q_PER_REQ 16
+/* bytes of the per-device scratch array of decode_attn_decode_static */
+#define DA_STATIC_SCRATCH_BYTES (64u << 20)
 /* Query rows one stage-1 workgroup holds.  A kv-head serves R = G * q_per_req
  * rows; with R > DA_MAX_ROWS they are processed in ceil(R / DA_MAX_ROWS)
  * row blocks of ceil(R / blocks) rows, one workgroup each, and every block
@@ -346,6 +351,42 @@ int32_t decode_attn_merge(const float* o_partial, const float* lse_partial, int3
                           int32_t q_per_req, int32_t num_q_heads, int32_t head_dim,
                           int32_t num_splits, const int32_t* split_counts, void* out,
                           int32_t out_dtype, float* lse_out, void* stream);
+
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid
+ * it: stage 1 and the merge in one call, with the split partials in a scratch
+ * array the library keeps on each GPU instead of caller buffers.  The result
+ * is that of decode_attn_split / decode_attn_split_int8 / decode_attn_split_int4
+ * (by cache_format: DA_CACHE_DENSE, _INT8, _INT4; k_scale / v_scale are the
+ * scales or (scale, zero) pairs of the quantised formats, NULL for dense)
+ * followed by decode_attn_merge into out / lse_out, with the same kernels;
+ * every argument means what it means there.  With a work list, the merge
+ * takes split_counts.
+ *   Scratch: DA_STATIC_SCRATCH_BYTES (64 MiB) per GPU, allocated when the
+ *   library is loaded on that GPU and held until the process ends.  The
+ *   partials need 4 * B * q_per_req * Hq * num_splits * (D + 1) bytes (the
+ *   output part rounded up to 256); a call that needs more returns
+ *   DA_ERR_TOO_LARGE and enqueues nothing (e.g. B = 64, Hq = 40, D = 128:
+ *   up to 48 splits; B = 64 with 4 MTP tokens and Hq = 32: up to 15).
+ *   Calls on one GPU share its array, which keeps the last call's partials:
+ *   two calls whose work overlaps on one GPU (different streams, threads or
+ *   a graph replayed beside an eager call) race.  Nothing in it needs
+ *   clearing (stage 1 writes every slot the merge reads).
+ *   No allocation, free or synchronisation; capturable in a HIP graph.
+ */
+int32_t decode_attn_decode_static(const void* q, int32_t q_dtype, int32_t cache_format,
+                                  const void* k_pool, const void* v_pool,
+                                  const uint16_t* k_scale, const uint16_t* v_scale,
+                                  const int32_t* page_table, int32_t page_table_stride,
+                                  int32_t max_pages, const int32_t* cache_seqlens,
+                                  const int32_t* batch_order, int32_t batch, int32_t q_per_req,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t page_size, int32_t num_pages, int32_t kv_layout,
+                                  int32_t num_splits, const int32_t* split_counts,
+                                  const int32_t* work_list, int32_t work_capacity,
+                                  float softmax_scale, int32_t causal, void* out,
+                                  int32_t out_dtype, float* lse_out, void* stream);
 
 /*
  * Host-only: split count for a launch (LightLLM PR #1549: num_splits is the

@@ -67,6 +67,7 @@ def test_strerror_and_version(lib):
     assert lib.decode_attn_strerror(1) == b"invalid argument"
     assert lib.decode_attn_strerror(2) == b"unsupported shape or dtype"
     assert lib.decode_attn_strerror(3) == b"kernel launch failed"
+    assert lib.decode_attn_strerror(4) == b"partials exceed the static scratch buffer"
     assert lib.decode_attn_strerror(99) == b"unknown status"
     assert lib.decode_attn_version() == 300
 
@@ -99,6 +100,19 @@ def _split_args(**kw):
 ])
 def test_split_validation(lib, kw, status):
     assert lib.decode_attn_split(*_split_args(**kw)) == status
+
+
+def test_static_decode_refuses_before_touching_a_device(lib):
+    # (q, q_dtype, format, k, v, ks, vs, pt, pt_stride, max_pages, seqlens, order, batch, q, Hq,
+    #  Hkv, D, ps, P, layout, S, counts, work, cap, scale, causal, out, out_dtype, lse, stream)
+    a = [FAKE, B.DA_BF16, B.DA_CACHE_DENSE, FAKE, FAKE, None, None, FAKE, 8, 8, FAKE, None,
+         64, 1, 40, 8, 128, 64, 100, B.DA_KV_HND, 64, None, None, 0, 0.1, 0, FAKE, B.DA_BF16,
+         None, None]
+    assert lib.decode_attn_decode_static(*a) == 4  # 64 x 40 x 64 split rows: beyond the scratch
+    for i, v, st in ((26, None, 1), (26, ctypes.c_void_p(0x1002), 1), (27, 9, 2), (2, 3, 1),
+                     (12, 0, 1), (20, 0, 1), (28, ctypes.c_void_p(0x1001), 1)):
+        b = list(a); b[i] = v
+        assert lib.decode_attn_decode_static(*b) == st, (i, v)
 
 
 @pytest.mark.parametrize("scale", [float("nan"), float("inf"), float("-inf"), 0.0, -0.125,
