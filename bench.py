@@ -16,7 +16,18 @@ value      = algorithmic bytes of one step / measured step time (GB/s), the K
 
 roofline   = the stage-1 kernel: algorithmic bytes per launch / its average
              launch time from HIP events on the launch stream, against
-             MI355X's 8 TB/s HBM peak.
+             MI355X's 8 TB/s HBM peak.  The timed launches are the stage-1
+             dispatches [warmup + steps, warmup + 2 steps) of the run
+             (roofline.dispatch_window), so a kernel trace of the same command
+             averages exactly those (--profile-report does).
+variants   = the other workloads of the pages' matrix (B=16 at 8K, the
+             uniform 32K batch, INT8 at 32K, INT4 MTP verify), each timed the
+             same way at its tuned split count: stage-1 and whole-step us,
+             algorithmic GB/s and the fraction of 8 TB/s.
+pool copies: a pool smaller than 2 GB is built in several independent
+             copies (same shape, other draws) that consecutive steps rotate
+             through, so that no launch finds its K/V in the 256 MB
+             Infinity Cache left there by the previous one.
 schedule   = how stage 1 is split: "batch" (one tuned num_splits for every
              request, the default) or "request" (the metadata prelude picks
              each request's split count from its own length through a
@@ -63,6 +74,11 @@ def parse():
                    help="skip timing the other schedule and the auxiliary rows (KV append, SWA "
                         "and schedule metadata), keeping a kernel trace to one configuration")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the other workloads' timings (the variants object)")
+    p.add_argument("--pool-copies", type=int, default=0,
+                   help="independent copies of the batch that steps rotate through "
+                        "(0 = enough for 2 GB of K/V)")
     p.add_argument("--tune", nargs="?", const="all", default=None,
                    help="sweep num_splits per bucket and write the table (optionally a comma list "
                         "of cache formats -- bf16,int8,int4 -- and workload names)")
@@ -222,15 +238,19 @@ def kv_name(w):
     return w.dtype if w.kv == W.KV_DENSE else w.kv
 
 
-def time_config(step, steps, warmup, torch):
+def time_config(step_list, steps, warmup, torch):
     """Times `steps` whole steps back to back (host clock, synchronised on both
     sides); then the same number again with events between the three calls for
     the per-kernel breakdown and percentiles (an event record between steps
-    costs the stream ~12 us here, so the timed steps carry none).  Returns
-    (ms_per_step, split_ms_avg, merge_ms_avg, meta_ms_avg, percentiles)."""
+    costs the stream ~12 us here, so the timed steps carry none).  Step i runs
+    on copy i % len(step_list) of the batch.  Returns (ms_per_step,
+    split_ms_avg, merge_ms_avg, meta_ms_avg, percentiles); the stage-1 average
+    is over the launches [warmup + steps, warmup + 2 steps) of the run."""
     stream = torch.cuda.current_stream()
+    n = len(step_list)
 
-    def run(ev=None):
+    def run(i, ev=None):
+        step = step_list[i % n]
         if ev is not None:
             ev[0].record(stream)
         step.meta()
@@ -243,18 +263,18 @@ def time_config(step, steps, warmup, torch):
         if ev is not None:
             ev[3].record(stream)
 
-    for _ in range(warmup):
-        run()
+    for i in range(warmup):
+        run(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        run()
+    for i in range(steps):
+        run(i)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
-        run(evs[i])
+        run(i, evs[i])
     torch.cuda.synchronize()
     meta = np.mean([e[0].elapsed_time(e[1]) for e in evs])
     splits = [e[1].elapsed_time(e[2]) for e in evs]
@@ -462,14 +482,67 @@ def cpu_baseline(batch, seconds):
             "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model()}
 
 
-def make_resident(da, w, torch):
+def make_resident(da, w, torch, seed=None, lengths=None):
     from decode_attention_paged_gqa_amd import workloads as W
 
-    batch = W.make_batch(w, device="cuda")
+    batch = W.make_batch(w, device="cuda", seed=seed, lengths=lengths)
     batch.md = da.decode_attn_metadata(batch.seq_lens, batch.req_pool_indices, batch.req_to_token,
                                        w.page_size, batch.max_pages, q_stride=w.q_per_req)
     torch.cuda.synchronize()
     return batch
+
+
+ROTATE_BYTES = 2 << 30  # K/V footprint the rotated copies add up to at least
+
+
+def pool_bytes(batch) -> int:
+    t = [batch.k_pool, batch.v_pool, batch.k_scale, batch.v_scale]
+    return sum(x.numel() * x.element_size() for x in t if x is not None)
+
+
+def resident_copies(da, w, torch, copies=0):
+    """The batch, plus independent copies (same lengths and shape, other draws
+    and page permutations) until the pools add up to ROTATE_BYTES; ``copies``
+    > 0 fixes the number."""
+    first = make_resident(da, w, torch)
+    n = copies or max(1, -(-ROTATE_BYTES // max(1, pool_bytes(first))))
+    return [first] + [make_resident(da, w, torch, seed=w.seed + 1000 * i, lengths=first.lengths)
+                      for i in range(1, n)]
+
+
+VARIANT_WORKLOADS = ("bf16_b16_hq32_hkv8_d128_p64_L8192", "bf16_b64_hq40_hkv8_d128_p64_L32768",
+                     "int8kv_b32_hq32_hkv8_d128_p64_L32768",
+                     "int4kv_mtp4_b64_hq32_hkv8_d128_p64_L8k-32k")
+
+
+def variant_timings(da, torch, steps, warmup):
+    """The pages' other decode shapes, each at its tuned split count and timed
+    as the main line is (HIP events per call; pools under 2 GB rotated)."""
+    from decode_attention_paged_gqa_amd import workloads as W
+    from decode_attention_paged_gqa_amd.splits import SplitTable, kernel_key
+
+    tables = SplitTable.load()
+    out = {}
+    for name in VARIANT_WORKLOADS:
+        w = W.WORKLOADS[name]
+        batches = resident_copies(da, w, torch)
+        key = kernel_key(kv_name(w), rows_per_kv_head(w), w.head_dim, w.page_size, w.kv_layout)
+        S = tables.pick(key, w.batch, int(batches[0].lengths.max()))
+        step_list = [Step(da, b, torch, S=S) for b in batches]
+        ms, split_ms, merge_ms, meta_ms, _ = time_config(step_list, steps, warmup, torch)
+        ab = algorithmic_bytes(w, batches[0].lengths)
+        gbs = ab["split"] / (split_ms * 1e-3) / 1e9
+        out[name] = {"kernel": stage1_kernel(w)[0], "kv": kv_name(w), "batch": w.batch,
+                     "q_per_req": w.q_per_req, "num_q_heads": w.num_q_heads,
+                     "kv_tokens": int(batches[0].lengths.sum()), "num_splits": S,
+                     "pool_copies": len(batches), "split_us": round(split_ms * 1e3, 2),
+                     "step_us": round(ms * 1e3, 2), "split_GBps": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "step_frac": round(ab["step"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": ab["split"]}
+        del step_list, batches
+        torch.cuda.empty_cache()
+    return out
 
 
 def tune_variants(which):
@@ -586,18 +659,20 @@ def tune_chunks(da, torch, which="all", old_keys=None):
 COPY_BYTES = 1 << 30
 
 
-def profile_only(step, steps, torch):
+def profile_only(step_list, steps, torch):
     """Dispatches for counter collection: a plain 1 GiB device copy whose byte
-    count is known (it calibrates FETCH_SIZE / WRITE_SIZE), then whole steps."""
+    count is known (it calibrates FETCH_SIZE / WRITE_SIZE), then whole steps
+    (rotating over the batch copies)."""
     src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    for _ in range(steps):
-        step()
+    for i in range(steps):
+        step_list[i % len(step_list)]()
     torch.cuda.synchronize()
+    step = step_list[0]
     w = step.batch.w
     ab = algorithmic_bytes(w, step.batch.lengths)
     print(json.dumps({"profile_only": w.name, "schedule": step.describe(), "copy_bytes": COPY_BYTES,
@@ -654,6 +729,18 @@ def rocprof_summary(trace_dir, fetch_dir, write_dir):
                                    split_fetch_bytes=sf, split_write_bytes=sw)
 
 
+def window_us(trace_dir, kname, window):
+    """Mean duration (us) of dispatches [first, first + count) of kernel `kname`
+    in a rocprofv3 kernel trace, in launch order, and the number averaged."""
+    rows = [r for r in _read_csv(trace_dir, "kernel_trace.csv")
+            if kname + "<" in r["Kernel_Name"] or kname + "(" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    first, count = window
+    sel = rows[first:first + count]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel]
+    return (float(np.mean(durs)) if durs else float("nan")), len(durs), len(rows)
+
+
 SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 
 
@@ -701,8 +788,11 @@ def profile_report(prefix):
     stats = _read_csv(prefix + "_trace", "kernel_stats.csv")
     kname = stage1_kernel(w)[0]
     srow = [r for r in stats if kname + "<" in r["Name"] or kname + "(" in r["Name"]][0]
-    avg_us = float(srow["AverageNs"]) / 1e3
+    all_avg_us = float(srow["AverageNs"]) / 1e3
     calls = int(srow["Calls"])
+    # the launches the bench line's roofline was timed on (HIP events), from the trace
+    window = res["roofline"].get("dispatch_window")
+    avg_us, n_win, n_all = window_us(prefix + "_trace", kname, window)
     kern = re.sub(r"^(void )?\(anonymous namespace\)::", "", srow["Name"]).split("(")[0]
     fetch, write = tr["split_fetch_bytes"], tr["split_write_bytes"]
     hbm = fetch + write
@@ -721,7 +811,7 @@ def profile_report(prefix):
     run = f"python3 $R/bench.py --workload {wl} --sched {sched['mode']}"
     cmds = ["cd /tmp && export TMPDIR=/tmp",
             f"rocprofv3 --kernel-trace --stats --output-format csv -d $R/{rel}_trace -o run -- "
-            f"{run} --steps 20 --warmup 5 --no-cpu-baseline --no-alt",
+            f"{run} --steps 20 --warmup 5 --no-cpu-baseline --no-alt --no-variants",
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/{rel}_fetch -o run -- "
             f"{run} --profile-only --steps 3",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/{rel}_write -o run -- "
@@ -760,13 +850,17 @@ Commands:
 {chr(10).join(cmds)}
 ```
 
-## Kernel trace (`--kernel-trace --stats`, {calls} stage-1 calls incl. warmup)
+## Kernel trace (`--kernel-trace --stats`, {calls} stage-1 calls in all)
 
 {table}
 
-Stage-1 average {avg_us:.2f} us -> {ab / (avg_us * 1e-6) / 1e9:.1f} GB/s algorithmic
-({ab / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:.1f} % of 8 TB/s).  bench.py's HIP-event average
-over the same run: {res['kernels_us']['split']:.2f} us ({res['roofline']['achieved']:.1f} GB/s).
+The bench line's roofline times stage-1 launches {window[0]} .. {window[0] + window[1] - 1} of the
+run with HIP events (after {window[0]} warm-up and wall-clock launches).  Those {n_win} launches in
+the kernel trace ({n_all} stage-1 dispatches traced): average **{avg_us:.2f} us** ->
+{ab / (avg_us * 1e-6) / 1e9:.1f} GB/s algorithmic, **{ab / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:.1f} %** of 8 TB/s.
+bench.py's HIP-event average over the same launches: {res['kernels_us']['split']:.2f} us
+({res['roofline']['achieved']:.1f} GB/s, {100 * res['roofline']['frac']:.1f} %).  The average over all
+{calls} calls in the stats table (warm-up, graph replays included) is {all_avg_us:.2f} us.
 
 ## HBM traffic (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`, per stage-1 dispatch)
 
@@ -790,7 +884,8 @@ Mean: {fetch / 1e9:.4f} GB read + {write / 1e6:.2f} MB written = {hbm / 1e9:.4f}
            "num_splits": S, "hbm_bytes_per_launch": int(round(hbm)),
            "fetch_bytes": int(round(fetch)), "write_bytes": int(round(write)),
            "fetch_scale": tr["fetch_scale"], "write_scale": tr["write_scale"],
-           "rocprof_avg_us": round(avg_us, 2), "summary": fn}
+           "rocprof_avg_us": round(avg_us, 2), "rocprof_all_calls_avg_us": round(all_avg_us, 2),
+           "summary": fn}
     if sq is not None:
         ent["mfma_busy"] = round(sq["mfma_busy"], 4)
         ent["valu_busy"] = round(sq["valu_busy"], 4)
@@ -798,7 +893,8 @@ Mean: {fetch / 1e9:.4f} GB read + {write / 1e6:.2f} MB written = {hbm / 1e9:.4f}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(traffic, f, indent=1)
         f.write("\n")
-    print(fn, f"{avg_us:.1f} us", f"traffic {hbm / ab:.4f}x",
+    print(fn, f"{avg_us:.1f} us (window; HIP events {res['kernels_us']['split']:.1f} us)",
+          f"traffic {hbm / ab:.4f}x",
           "" if sq is None else f"mfma {100 * sq['mfma_busy']:.1f}% valu {100 * sq['valu_busy']:.1f}%")
 
 
@@ -833,19 +929,24 @@ def main():
             tune_chunks(da, torch, args.tune_chunks, old_keys)
         return
     w = W.WORKLOADS[args.workload]
-    batch = make_resident(da, w, torch)
+    batches = resident_copies(da, w, torch, args.pool_copies)
+    batch = batches[0]
     key = kernel_key(kv_name(w), rows_per_kv_head(w), w.head_dim, w.page_size, w.kv_layout)
     tables = SplitTable.load()
     S = args.splits or tables.pick(key, w.batch, int(batch.lengths.max()))
     chunk = args.chunk or tables.chunk_for(key, w.batch)
     req_table = per_request_table(chunk, w.page_size, tables.bucket_tokens)
-    batch_step = Step(da, batch, torch, S=S)
-    req_step = Step(da, batch, torch, table=req_table)
-    step, alt = (batch_step, req_step) if args.sched == "batch" else (req_step, batch_step)
+    if args.sched == "batch":
+        steps_main = [Step(da, b, torch, S=S) for b in batches]
+        alt = Step(da, batch, torch, table=req_table)
+    else:
+        steps_main = [Step(da, b, torch, table=req_table) for b in batches]
+        alt = Step(da, batch, torch, S=S)
+    step = steps_main[0]
     if args.profile_only:
-        profile_only(step, args.steps, torch)
+        profile_only(steps_main, args.steps, torch)
         return
-    ms, split_ms, merge_ms, meta_ms, pct = time_config(step, args.steps, args.warmup, torch)
+    ms, split_ms, merge_ms, meta_ms, pct = time_config(steps_main, args.steps, args.warmup, torch)
     # the same step captured once in a HIP graph and replayed (reported beside it)
     try:
         graph_ms = time_graph(step, args.steps, args.warmup, torch)
@@ -855,7 +956,7 @@ def main():
     alt_split_ms = None if args.no_alt else time_split_only(alt, args.steps, torch)
     aux = None if args.no_alt else aux_timings(da, batch, args.steps, torch)
     schedule, alt_schedule = step.describe(), alt.describe()
-    if step is req_step:
+    if args.sched == "request":
         schedule["chunk_pages"] = chunk
     else:
         alt_schedule["chunk_pages"] = chunk
@@ -887,7 +988,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if (w.kv == W.KV_DENSE and w.dtype == "bf16") else kv_name(w),
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "q_per_req": w.q_per_req,
+        "config": {"workload": w.name, "pool_copies": len(batches), "batch": w.batch,
+                   "q_per_req": w.q_per_req,
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "page_size": w.page_size, "kv_layout": w.kv_layout,
                    "kv_len_max": int(batch.lengths.max()), "kv_len_mean": float(batch.lengths.mean()),
@@ -902,11 +1004,15 @@ def main():
         "percentiles_p10_p50_p90": pct,
         "roofline": {"bound": "hbm", "kernel": "split (stage 1)", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": ab["split"], **counters},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": ab["split"],
+                     "dispatch_window": [args.warmup + args.steps, args.steps], **counters},
         "aux_us": aux,
         "step_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": ab["step"],
     }
+    if not args.no_variants:
+        del alt
+        res["variants"] = variant_timings(da, torch, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -83,12 +83,15 @@ __device__ __forceinline__ int q_row_shift(float row_absmax) {
 // is taken by D / 8 threads of 8 columns each (thread t: row t / (D / 8) +
 // (2048 / D) k, columns 8 * (t % (D / 8)) .. + 7), so the per-row terms are
 // formed once per thread and the stores are two 16-byte writes.  lse_shift
-// (log2 units) is a constant factor carried in l.
+// (log2 units) is a constant factor carried in l; the output sums carry
+// 2^-acc_shift times l's factor (an exact power of two, taken out of the sum
+// of weights before the division).
 template <int WAVES, int ROWS = 16, int D = 128>
 __device__ __forceinline__ void write_partials(const float* sm_acc, const float* sm_m,
                                                const float* sm_l, int r0, int nr, int G, int g,
                                                int b, int qn, int Hq, int S, int s,
-                                               float lse_shift, float* o, float* lse) {
+                                               float lse_shift, float* o, float* lse,
+                                               int acc_shift = 0) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int kTpr = D / 8;           // threads per row
   constexpr int kRpp = 256 / kTpr;      // rows per pass
@@ -116,8 +119,9 @@ __device__ __forceinline__ void write_partials(const float* sm_acc, const float*
         for (int e = 0; e < 8; ++e) y[e] = fmaf(xs[e], f, y[e]);
       }
     }
+    const float den = ldexpf(lsum, -acc_shift);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = lsum > 0.f ? y[e] / lsum : 0.f;
+    for (int e = 0; e < 8; ++e) y[e] = lsum > 0.f ? y[e] / den : 0.f;
     const int rr = r0 + r, i = rr / G, h = g * G + rr % G;
     const long long orow = (((long long)b * qn + i) * Hq + h) * S + s;
     float4* dst = reinterpret_cast<float4*>(o + orow * D + d0);

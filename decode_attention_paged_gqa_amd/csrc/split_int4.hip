@@ -235,9 +235,12 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMainBytes + kMaxSplitPages * 4];
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
+  __shared__ int s_redo;         // a wave's V operand left fp16's range
+  __shared__ float s_vmax[kWaves];
 
   da::Stage1Item it;
   if (!da::stage1_item<true>(a.sched, a.Hkv, it)) return;
+  if (threadIdx.x == 0) s_redo = 0;  // ordered before any write by the loop's barriers
   const int g = it.g, s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -340,13 +343,20 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
 
   float4_t acc[NT][kBlocks];
   float m[NT], l[NT];
+  auto reset_state = [&]() {
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
+    for (int rt = 0; rt < NT; ++rt) {
 #pragma unroll
-    for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
-    m[rt] = da::kNegInf;
-    l[rt] = 0.f;
-  }
+      for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
+      m[rt] = da::kNegInf;
+      l[rt] = 0.f;
+    }
+  };
+  reset_state();
+  // V is formed as v * 2^-vexp: 0 on the first pass, raised only when that
+  // pass overflowed fp16 (see the end of the split)
+  int vexp = 0;
+  half2_t vdown = {1, 1};
   // fp16 exponent bits of 1024 in both halves, kept in a register so that
   // mask-and-or is one instruction
   uint32_t magic = 0x64006400u;
@@ -429,8 +439,9 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     }
   };
 
-  auto compute = [&](int j, const StageData<D>& sd, auto masked_tag) {
+  auto compute = [&](int j, const StageData<D>& sd, auto masked_tag, auto scaled_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr bool SCALED = decltype(scaled_tag)::value;  // V scaled by 2^-vexp
     // ---- K operands, shared by the row tiles: elements (x, x+4) are nibble x
     // of the dword's two halves; pairs 1 and 3 are masked in place
     // (16 n * 2^-24, exact), their Q is / 16
@@ -526,9 +537,14 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
       vw[jj] = ok ? sd.v[jj] : 0u;
       vsz[jj] = ok ? sd.vsz[jj] : 0u;
     }
-    // per token pair: s and -z*s (fp16, one per token)
-    const half2_t s01 = as_h2(__builtin_amdgcn_perm(vsz[1], vsz[0], 0x05040100u));
-    const half2_t s23 = as_h2(__builtin_amdgcn_perm(vsz[3], vsz[2], 0x05040100u));
+    // per token pair: s and -z*s (fp16, one per token); on the scaled pass
+    // s * 2^-vexp (exact unless it falls below fp16's normal range)
+    half2_t s01 = as_h2(__builtin_amdgcn_perm(vsz[1], vsz[0], 0x05040100u));
+    half2_t s23 = as_h2(__builtin_amdgcn_perm(vsz[3], vsz[2], 0x05040100u));
+    if constexpr (SCALED) {
+      s01 = s01 * vdown;
+      s23 = s23 * vdown;
+    }
     const half2_t nzs01 = -(as_h2(__builtin_amdgcn_perm(vsz[1], vsz[0], 0x07060302u)) * s01);
     const half2_t nzs23 = -(as_h2(__builtin_amdgcn_perm(vsz[3], vsz[2], 0x07060302u)) * s23);
     // high nibbles are taken in place as 16 n: their scale is s / 16
@@ -582,55 +598,104 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     }
     if (j + kStages - 1 < nmine) issue(j + kStages - 1, pid);
   };
-  for (; pc < p1; pc += kMaxSplitPages) {
-    const int pe = min(pc + kMaxSplitPages, p1);
-    c0 = pc * ps;
-    const int c1 = min(pe * ps, t1);
-    if (pc != p0) {
-      __syncthreads();  // the previous chunk's page ids are no longer read
-      stage_pids(pe);
-    }
-    __syncthreads();  // s_pid visible
-    const int ntiles = (c1 - c0 + 15) >> 4;
-    nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-    const int lim = tfull - c0 - 16 * wave - 16;
-    const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * kWaves) + 1);
-#pragma unroll
-    for (int u = 0; u < kStages - 1; ++u)
-      if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
-    using C0 = std::integral_constant<int, 0>;
-    int j = 0;
-    if constexpr (D == 128) {
-      // unmasked tiles, kStages per trip so that each one's stage is a constant
-      static_assert(kStages == 4, "one unrolled trip per ring cycle");
-      using C1 = std::integral_constant<int, kStageBytes>;
-      using C2 = std::integral_constant<int, 2 * kStageBytes>;
-      using C3 = std::integral_constant<int, 3 * kStageBytes>;
-      for (; j + kStages <= jfull; j += kStages) {
-        StageData<D> sd0, sd1, sd2, sd3;
-        step(j, sd0, 0u, C0{});
-        compute(j, sd0, std::false_type{});
-        step(j + 1, sd1, 0u, C1{});
-        compute(j + 1, sd1, std::false_type{});
-        step(j + 2, sd2, 0u, C2{});
-        compute(j + 2, sd2, std::false_type{});
-        step(j + 3, sd3, 0u, C3{});
-        compute(j + 3, sd3, std::false_type{});
+  auto run_split = [&](auto sc) {
+    for (; pc < p1; pc += kMaxSplitPages) {
+      const int pe = min(pc + kMaxSplitPages, p1);
+      c0 = pc * ps;
+      const int c1 = min(pe * ps, t1);
+      if (pc != p0) {
+        __syncthreads();  // the previous chunk's page ids are no longer read
+        stage_pids(pe);
       }
-    } else {
-      // unmasked tiles one at a time (the stage offset in a register)
-      for (; j < jfull; ++j) {
+      __syncthreads();  // s_pid visible
+      const int ntiles = (c1 - c0 + 15) >> 4;
+      nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+      const int lim = tfull - c0 - 16 * wave - 16;
+      const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * kWaves) + 1);
+  #pragma unroll
+      for (int u = 0; u < kStages - 1; ++u)
+        if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
+      using C0 = std::integral_constant<int, 0>;
+      int j = 0;
+      if constexpr (D == 128) {
+        // unmasked tiles, kStages per trip so that each one's stage is a constant
+        static_assert(kStages == 4, "one unrolled trip per ring cycle");
+        using C1 = std::integral_constant<int, kStageBytes>;
+        using C2 = std::integral_constant<int, 2 * kStageBytes>;
+        using C3 = std::integral_constant<int, 3 * kStageBytes>;
+        for (; j + kStages <= jfull; j += kStages) {
+          StageData<D> sd0, sd1, sd2, sd3;
+          step(j, sd0, 0u, C0{});
+          compute(j, sd0, std::false_type{}, sc);
+          step(j + 1, sd1, 0u, C1{});
+          compute(j + 1, sd1, std::false_type{}, sc);
+          step(j + 2, sd2, 0u, C2{});
+          compute(j + 2, sd2, std::false_type{}, sc);
+          step(j + 3, sd3, 0u, C3{});
+          compute(j + 3, sd3, std::false_type{}, sc);
+        }
+      } else {
+        // unmasked tiles one at a time (the stage offset in a register)
+        for (; j < jfull; ++j) {
+          StageData<D> sd;
+          step(j, sd, (uint32_t)((j % kStages) * kStageBytes), C0{});
+          compute(j, sd, std::false_type{}, sc);
+        }
+      }
+      // the rest (D = 128: fewer than kStages unmasked tiles; then the masked ones)
+      for (; j < nmine; ++j) {
         StageData<D> sd;
         step(j, sd, (uint32_t)((j % kStages) * kStageBytes), C0{});
-        compute(j, sd, std::false_type{});
+        compute(j, sd, std::true_type{}, sc);
       }
     }
-    // the rest (D = 128: fewer than kStages unmasked tiles; then the masked ones)
-    for (; j < nmine; ++j) {
-      StageData<D> sd;
-      step(j, sd, (uint32_t)((j % kStages) * kStageBytes), C0{});
-      compute(j, sd, std::true_type{});
+  };
+  run_split(std::false_type{});
+
+  // ---- An fp16 V operand out of range (scales or zero points so large that
+  // n*s, z*s or the value itself pass 65504) leaves inf or NaN in the output
+  // sums.  Then the split is computed again with V formed as v * 2^-vexp,
+  // vexp the smallest power that brings the bound |s| * (15 + |z|) of every
+  // V group of the split below 2^15 (so n*s, z*s and v all stay in range);
+  // the factor is taken out again when the partials are written.
+  {
+    bool bad = false;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int bb = 0; bb < kBlocks; ++bb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bad |= !(fabsf(acc[rt][bb][i]) <= 3.0e38f);
+    if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) s_redo = 1;
+  }
+  __syncthreads();
+  if (s_redo) {  // uniform over the workgroup
+    float vm = 0.f;
+    const int32_t* ptrow = a.pt + (long long)b * a.pt_stride;
+    for (int t = p0 * ps + (int)threadIdx.x; t < t1; t += kThreads) {
+      const int pid0 = ptrow[t >> a.log2_ps];
+      const int pid = (unsigned)pid0 < (unsigned)a.num_pages ? pid0 : 0;
+      const long long row = (long long)pid * ps * a.Hkv + (long long)(t & (ps - 1)) * a.slot_stride +
+                            (long long)g * a.head_stride;
+      const uint32_t* sz = reinterpret_cast<const uint32_t*>(a.vsz + row * kSz);
+#pragma unroll
+      for (int k = 0; k < kGroups; ++k)
+        vm = fmaxf(vm, fabsf(h_lo(sz[k])) * (15.f + fabsf(h_hi(sz[k]))));
     }
+    for (int o = 32; o > 0; o >>= 1) vm = fmaxf(vm, __shfl_xor(vm, o, 64));
+    if (lane == 0) s_vmax[wave] = vm;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) vm = fmaxf(vm, s_vmax[w]);
+    // |s| < 2^16 and |z| < 2^16, so the bound is below 2^33: vexp <= 18
+    int ex = 33;
+    if (vm <= 3.0e38f) (void)frexpf(vm, &ex);  // vm < 2^ex
+    vexp = __builtin_amdgcn_readfirstlane(min(max(ex - 15, 0), 18));
+    vdown = half2_t{(_Float16)ldexpf(1.f, -vexp), (_Float16)ldexpf(1.f, -vexp)};
+    reset_state();
+    pc = p0;
+    stage_pids(min(p0 + kMaxSplitPages, p1));  // every wave is past its last LDS read
+    run_split(std::true_type{});
   }
 
   // ---- l is partial over the lane groups; acc and m are already per row
@@ -655,7 +720,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   }
   __syncthreads();
   write_partials<kWaves, ROWS, D>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S,
-                                  s, kPScale, a.o, a.lse);
+                                  s, kPScale, a.o, a.lse, vexp);
 }
 
 template <int D, bool QF>

@@ -22,10 +22,14 @@
 // fp32), each taken through the QK product into the same accumulator.  The offset is taken out with the row's fp32
 // sum of scaled Q, and the token's scale multiplies the result:
 //   q.k = s * 2^-sh * 2^24 * (dot - 2^-24 * 128 * sum_d q'_d).
-// The PV product takes V = fp16(b * s) (b is exact in fp16, one rounding)
-// and P = fp16(p * 2^7) (one rounding; p <= 2^8 under the lazy rescale, so
-// p * 2^7 < 2^15, and the factor keeps small weights out of fp16's
-// subnormal range; it cancels against the same factor in l).
+// The PV product takes V' = fp16((b / 2^7) * s) (b / 2^7 is exact in fp16;
+// one rounding) and P = fp16(p * 2^7) (one rounding; p <= 2^8 under the lazy
+// rescale, so p * 2^7 < 2^15, and the factor keeps small weights out of
+// fp16's subnormal range).  The two factors cancel in the product, so the
+// output sums are those of p * v while l carries 2^7.  With |b| <= 127 and
+// any fp16 scale (|s| <= 65504), |V'| <= 127 * 65504 / 2^7 < 65504: V' never
+// overflows, whatever the scales; below |b s| = 2^-7 it is an fp16 subnormal
+// (absolute error <= 2^-25 in V', 2^-18 in v).
 //   * QK: MFMA kb, lane (lm, lg): token lm, elements (D/4)*lg + 8*kb + 0..7;
 //     the lane reads its D/4 contiguous bytes of the row.
 //   * PV: output block bb row m is d = (D/16)*m + bb: lane (lm, lg) reads
@@ -56,6 +60,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kPScale = 7.0f;  // P (and l) carry a factor 2^7
+constexpr int kVShift = 7;       // V' = v / 2^7: the output sums carry 2^-7 against l
 constexpr int kMaxSplitPages = 512;
 
 // Per-head-dim geometry of a tile and of the LDS ring.
@@ -464,19 +469,20 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     }
     const half2_t s01 = as_h2(__builtin_amdgcn_perm(vs[1], vs[0], 0x05040100u));
     const half2_t s23 = as_h2(__builtin_amdgcn_perm(vs[3], vs[2], 0x05040100u));
-    const half2_t k1152 = {1152, 1152};
+    const half2_t k9 = {9, 9};
 #pragma unroll
     for (int hw = 0; hw < kHw; ++hw) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int bb = 4 * hw + kk;
-        // [t0.byte kk, 0, t1.byte kk, 0], then bytes ^ 0x80 and 0x64 above
-        // them: fp16 1024 + (b + 128), exact
+        // [t0.byte kk, 0, t1.byte kk, 0], then bytes ^ 0x80 and 0x48 above
+        // them: the fp16 8 + (b + 128) / 2^7 (ulp 2^-7 in [8, 16)), exact;
+        // minus 9 it is b / 2^7
         const uint32_t sel = (uint32_t)kk | 0x0C00u | ((uint32_t)(4 + kk) << 16) | 0x0C000000u;
-        const uint32_t x01 = __builtin_amdgcn_perm(vw[1][hw], vw[0][hw], sel) ^ 0x64806480u;
-        const uint32_t x23 = __builtin_amdgcn_perm(vw[3][hw], vw[2][hw], sel) ^ 0x64806480u;
-        const half2_t a01 = (as_h2(x01) - k1152) * s01;
-        const half2_t a23 = (as_h2(x23) - k1152) * s23;
+        const uint32_t x01 = __builtin_amdgcn_perm(vw[1][hw], vw[0][hw], sel) ^ 0x48804880u;
+        const uint32_t x23 = __builtin_amdgcn_perm(vw[3][hw], vw[2][hw], sel) ^ 0x48804880u;
+        const half2_t a01 = (as_h2(x01) - k9) * s01;
+        const half2_t a23 = (as_h2(x23) - k9) * s23;
         const half4_t va = {a01[0], a01[1], a23[0], a23[1]};
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
@@ -548,7 +554,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
   }
   __syncthreads();
   write_partials<kWaves, ROWS, D>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S,
-                                  s, kPScale, a.o, a.lse);
+                                  s, kPScale, a.o, a.lse, kVShift);
 }
 
 template <int D, bool QF>

@@ -62,6 +62,7 @@ class Workload:
     seed: int = 0
     splits: tuple = (1,)
     kv_layout: str = "NHD"         # "NHD" [P, page, Hkv, row] | "HND" [P, Hkv, page, row]
+    amp: tuple = (1.0, 1.0, 1.0)   # standard deviations of the Q, K, V draws (before encoding)
 
     @property
     def group(self) -> int:
@@ -267,26 +268,27 @@ def make_batch(w: Workload, device="cpu", seed: Optional[int] = None,
     L = draw_lengths(w, rng) if lengths is None else np.asarray(lengths, dtype=np.int64)
     page_table, r2t, rpi, P = build_layout(w, L, rng)
     B, Hq, Hkv, D, S, qn = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, w.q_per_req
-    q = torch.from_numpy(rng.standard_normal((B, qn, Hq, D)).astype(np.float32))
+    q = torch.from_numpy(rng.standard_normal((B, qn, Hq, D)).astype(np.float32)) * w.amp[0]
     q = _to_dtype(q, "fp32" if w.dtype == "fp32" else "bf16").to(device)
 
     gen = torch.Generator(device=device)
     gen.manual_seed(2000 + seed)
     shape = (P, S, Hkv, D)
 
-    def normal():
-        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    def normal(sd):
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * sd
 
     k_scale = v_scale = None
+    ka, va = w.amp[1], w.amp[2]
     if w.kv == KV_DENSE:
-        k_pool = _to_dtype(normal(), w.dtype)
-        v_pool = _to_dtype(normal(), w.dtype)
+        k_pool = _to_dtype(normal(ka), w.dtype)
+        v_pool = _to_dtype(normal(va), w.dtype)
     elif w.kv == KV_INT8:
-        k_pool, k_scale = quantize_int8(normal().to(torch.bfloat16))
-        v_pool, v_scale = quantize_int8(normal().to(torch.bfloat16))
+        k_pool, k_scale = quantize_int8(normal(ka).to(torch.bfloat16))
+        v_pool, v_scale = quantize_int8(normal(va).to(torch.bfloat16))
     elif w.kv == KV_INT4:
-        k_pool, k_scale = quantize_int4(normal().to(torch.bfloat16))
-        v_pool, v_scale = quantize_int4(normal().to(torch.bfloat16))
+        k_pool, k_scale = quantize_int4(normal(ka).to(torch.bfloat16))
+        v_pool, v_scale = quantize_int4(normal(va).to(torch.bfloat16))
     else:
         raise ValueError(w.kv)
     if w.kv_layout == "HND":  # same values, head-major within each page

@@ -217,8 +217,28 @@ int32_t decode_attn_metadata_ex(const int32_t* seq_lens, const int64_t* req_pool
  *   - INT8 / INT4 caches: scores exact up to fp32 rounding (codes and Q enter
  *     the matrix cores exactly; a bf16 Q after a per-row power-of-two scaling,
  *     an fp32 Q as two fp16 terms of 22 significant bits together); the P.V
- *     product takes p and the dequantised V in fp16, one rounding each.
+ *     product takes p and the dequantised V in fp16, one rounding each (unit
+ *     roundoff u = 2^-11).
  * Partial outputs are the normalised fp32 rows O_s and their natural-log LSE.
+ *
+ * Range of the quantised caches: every finite fp16 scale and zero point.
+ *   - INT8: V enters as fp16((b / 2^7) * s), below 65504 for any scale; per
+ *     partial row |dO| <= u * 2 max|v| + 2^-18 (max over the split's tokens;
+ *     the 2^-18 where b s / 2^7 falls into fp16's subnormal range).
+ *   - INT4: V enters as fma(n, s, -fp16(z s)) in fp16, |dO| <= u * (2 max|v|
+ *     + max|z s|) + 2^-24.  When a split's fp16 operands overflow (|s| (15 +
+ *     |z|) near 65504 or beyond), the kernel detects it and computes that
+ *     split again with s * 2^-e (e the smallest power that brings every
+ *     |s| (15 + |z|) of the split below 2^15), adding at most 2^-22 max |s|
+ *     (15 + |z|); other splits pay nothing.
+ *   - Scores: the fp32 terms of a score add up to M = scale * sum_d |q_d| u_d
+ *     (u_d = |k_d| for dense caches, |s| (|b| + 128) for INT8, |s| (n_d + |z|)
+ *     for INT4) and carry a few units of 2^-24 M; a score error E moves the
+ *     LSE by at most E and a normalised output by at most 2 E max|v|.  With
+ *     unit-scale data (|q|, |v| around 1) this is far inside the outputs' own
+ *     rounding; with peaked inputs (M in the thousands) it reaches ~1e-4 in
+ *     the LSE.  Inputs whose scores overflow fp32 (|scale q.k| > 3e38) are
+ *     out of range.
  */
 
 /*

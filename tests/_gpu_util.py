@@ -18,13 +18,17 @@ Gates for floating point, by output type:
   terms, 22 bits, whose 2^-22 relative residue is far inside these gates): the P.V product takes P
   and the dequantised V in fp16 (unit roundoff u = 2^-11).  P enters as
   fp16(p * 2^7) (one relative rounding, p * 2^7 stays in fp16's normal range
-  down to p = 2^-21); INT8 V as fp16(b * s) (one rounding); INT4 V as
-  fma(n, s, -fp16(z*s)) (at most u*(|v| + |z*s|)).  Each term p*v so carries
-  at most u*(2|v| + |z*s|) (+u^2 terms) of absolute error per unit of p, and
-  since O divides by the exact fp32 sum of p, |dO| <= u * (2 max|v| +
-  max|z*s|) over the request's tokens (z*s = 0 for INT8); the gate adds
-  that (x1.01) to the fp32 one.  Scores are computed exactly from the
-  codes, so the LSE gate stays 1e-4.
+  down to p = 2^-21); INT8 V as fp16((b / 2^7) * s) (one rounding; in fp16's
+  subnormal range an absolute 2^-25, i.e. 2^-18 in v); INT4 V as
+  fma(n, s, -fp16(z*s)) (at most u*(|v| + |z*s|), plus 2^-24 absolute in the
+  subnormal range), or, when that overflows fp16, the same with s * 2^-e for a
+  split-wide e chosen so that |s| (15 + |z|) 2^-e < 2^15, which adds the
+  rounding of s * 2^-e: at most 2^-22 max|s| (15 + |z|).  Each term p*v so
+  carries at most u*(2|v| + |z*s|) (+u^2 terms) of absolute error per unit of
+  p, plus those absolute floors, and since O divides by the exact fp32 sum of
+  p, |dO| <= u * (2 max|v| + max|z*s|) + floor over the request's tokens
+  (z*s = 0 for INT8); the gate adds that (x1.01) to the fp32 one.  Scores are
+  computed exactly from the codes, so the LSE gate stays 1e-4.
 """
 from __future__ import annotations
 
@@ -106,18 +110,21 @@ def check_quant(out: np.ndarray, ref: np.ndarray, label: str):
 
 
 def check_lse(lse: np.ndarray, ref: np.ndarray, label: str, tol=1e-4):
+    """tol: a number, or an array of ref's shape (a bound per value)."""
     inf_k = np.isneginf(lse)
     inf_r = np.isneginf(ref)
     assert np.array_equal(inf_k, inf_r), f"{label}: -inf pattern differs"
     fin = ~inf_r
-    d = float(np.max(np.abs(lse[fin] - ref[fin]))) if fin.any() else 0.0
-    log(f"  {label}: max |d lse| = {d:.3e}")
-    assert d <= tol, label
+    d = np.abs(lse[fin] - ref[fin])
+    t = np.broadcast_to(tol, ref.shape)[fin]
+    log(f"  {label}: max |d lse| = {float(d.max()) if d.size else 0.0:.3e}")
+    assert not d.size or float(np.max(d - t)) <= 0, label
 
 
-def check_partials(o, l, o_ref, l_ref, label, o_extra=None):
-    """o_extra: optional extra absolute bound, broadcastable to o [B, q, Hq, S, D]."""
-    check_lse(l, l_ref, label + " lse_partial")
+def check_partials(o, l, o_ref, l_ref, label, o_extra=None, lse_tol=1e-4):
+    """o_extra: optional extra absolute bound, broadcastable to o [B, q, Hq, S, D];
+    lse_tol: the LSE gate, a number or broadcastable to l [B, q, Hq, S]."""
+    check_lse(l, l_ref, label + " lse_partial", tol=np.broadcast_to(lse_tol, l_ref.shape))
     d = np.abs(o - o_ref)
     bound = 2e-5 * (1.0 + np.abs(o_ref))
     if o_extra is not None:
@@ -147,18 +154,20 @@ def host_inputs(batch: W.PagedBatch):
     return d
 
 
-def oracle_full(batch: W.PagedBatch):
+def oracle_full(batch: W.PagedBatch, scale=None):
     h = host_inputs(batch)
     w = batch.w
     return OA.decode_attention(h["q"], h["k"], h["v"], h["page_table"], h["seq_lens"],
-                               w.page_size, w.softmax_scale, causal=w.causal)
+                               w.page_size, w.softmax_scale if scale is None else scale,
+                               causal=w.causal)
 
 
-def oracle_partials(batch: W.PagedBatch, S: int):
+def oracle_partials(batch: W.PagedBatch, S: int, scale=None):
     h = host_inputs(batch)
     w = batch.w
     return OA.split_partials(h["q"], h["k"], h["v"], h["page_table"], h["seq_lens"],
-                             w.page_size, w.softmax_scale, S, causal=w.causal)
+                             w.page_size, w.softmax_scale if scale is None else scale, S,
+                             causal=w.causal)
 
 
 def oracle_sampled(batch: W.PagedBatch, pairs):
@@ -265,9 +274,12 @@ def fp16_pv_o_bound(batch: W.PagedBatch):
         v = OQ.dequant_int4(W.host_int(vp), W.host_u16(vs))
         sz = OQ.fp16_bits_to_f64(W.host_u16(vs))
         zs = np.abs(sz[..., 0] * sz[..., 1])  # [P, ps, Hkv, D/32]
+        # the rescaled pass: 2^-22 |s| (15 + |z|), and the subnormal floor
+        floor = 2.0 ** -22 * np.abs(sz[..., 0]) * (15.0 + np.abs(sz[..., 1])) + 2.0 ** -24
     else:
         v = OQ.dequant_int8(W.host_int(vp), W.host_u16(vs))
         zs = np.zeros(v.shape[:3] + (1,))
+        floor = np.full(v.shape[:3] + (1,), 2.0 ** -18)
     pt = W.host_int(batch.page_table)
     L = W.host_int(batch.seq_lens)
     B, G = len(L), w.group
@@ -280,34 +292,37 @@ def fp16_pv_o_bound(batch: W.PagedBatch):
         pages, slots = pt[b, t // w.page_size], t % w.page_size
         vm = np.abs(v[pages, slots]).max(axis=(0, 2))   # [Hkv]
         zm = zs[pages, slots].max(axis=(0, 2))           # [Hkv]
+        fm = floor[pages, slots].max(axis=(0, 2))        # [Hkv]
         for g in range(w.num_kv_heads):
-            out[b, 0, g * G:(g + 1) * G] = FP16_U * (2 * vm[g] + zm[g]) * 1.01
+            out[b, 0, g * G:(g + 1) * G] = (FP16_U * (2 * vm[g] + zm[g]) + fm[g]) * 1.01
     return out
 
 
 # ---------------------------------------------------------------- GPU path
-def run_split(da, batch: W.PagedBatch, S: int, batch_order=None, sched=None):
+def run_split(da, batch: W.PagedBatch, S: int, batch_order=None, sched=None, scale=None):
     """Stage 1 with S splits per request, or, with ``sched`` (the metadata dict
-    holding "split_counts" and "work_list"), per-request counts and S slots."""
+    holding "split_counts" and "work_list"), per-request counts and S slots.
+    ``scale``: the softmax scale (default the workload's 1/sqrt(D))."""
     w = batch.w
+    scale = w.softmax_scale if scale is None else scale
     kw = dict(batch_order=batch_order, kv_layout=w.kv_layout)
     if sched is not None:
         kw.update(split_counts=sched["split_counts"], work_list=sched["work_list"])
     if w.kv == W.KV_DENSE:
         return da.decode_attn_split(batch.q, batch.k_pool, batch.v_pool, batch.page_table,
-                                    batch.seq_lens, S, w.softmax_scale, w.causal, **kw)
+                                    batch.seq_lens, S, scale, w.causal, **kw)
     if w.kv == W.KV_INT8:
         return da.decode_attn_split_int8(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
                                          batch.v_scale, batch.page_table, batch.seq_lens, S,
-                                         w.softmax_scale, w.causal, **kw)
+                                         scale, w.causal, **kw)
     return da.decode_attn_split_int4(batch.q, batch.k_pool, batch.v_pool, batch.k_scale,
                                      batch.v_scale, batch.page_table, batch.seq_lens, S,
-                                     w.softmax_scale, w.causal, **kw)
+                                     scale, w.causal, **kw)
 
 
 def run_decode(da, batch: W.PagedBatch, S: int, out_dtype=torch.bfloat16, batch_order=None,
-               sched=None):
-    o, l = run_split(da, batch, S, batch_order, sched)
+               sched=None, scale=None):
+    o, l = run_split(da, batch, S, batch_order, sched, scale)
     counts = None if sched is None else sched["split_counts"]
     out, lse = da.decode_attn_merge(o, l, out_dtype=out_dtype, want_lse=True, split_counts=counts)
     return out, lse, o, l
