@@ -391,6 +391,23 @@ def aux_timings(da, batch, iters, torch):
     return out
 
 
+def time_split_merge(step, iters, torch):
+    """Average time (ms) of stage 1 + merge over `iters` back-to-back pairs (the
+    part of a step that depends on the split count)."""
+    step.meta()
+    for _ in range(3):
+        step.split()
+        step.merge()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        step.split()
+        step.merge()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
 def time_split_only(step, iters, torch):
     """Average stage-1 time (ms) over `iters` back-to-back launches."""
     step.meta()
@@ -575,6 +592,8 @@ def tune(da, torch, which="all", old_keys=None):
     table = SplitTable.load()
     old_keys = list(table.batch_keys) if old_keys is None else list(old_keys)
     retune = os.environ.get("DECODE_ATTN_RETUNE") == "1"
+    # DECODE_ATTN_RETUNE_KEYS=1,4: sweep those batch keys again, keep the other rows
+    only = {int(x) for x in os.environ.get("DECODE_ATTN_RETUNE_KEYS", "").split(",") if x}
     table.batch_keys = list(BATCH_KEYS)  # rows of variants not swept here stop matching
     variants = tune_variants(which)
     for base in variants:
@@ -584,30 +603,42 @@ def tune(da, torch, which="all", old_keys=None):
         old = old if old is not None and len(old) == len(old_keys) else None
         rows = []
         for bk in BATCH_KEYS:
-            if old is not None and bk in old_keys and not retune:
+            if old is not None and bk in old_keys and not retune and bk not in only:
                 rows.append(old[old_keys.index(bk)])
                 continue
             row = []
             for k in range(1, N_BUCKETS + 1):
                 # representative batches: the bucket's upper length for one request, the
-                # rest log-uniform below it (ragged, like the pages' serving batches);
-                # the split count with the least total time over three seeds wins
+                # rest log-uniform below it (ragged, like the pages' serving batches).
+                # Candidates stop at the longest request's page count (more splits
+                # would be empty); each is timed as stage 1 + merge, twice per seed,
+                # and the smallest split count within the measured noise of the
+                # fastest wins
                 Lmax = k * BUCKET_TOKENS
-                tot = {S: 0.0 for S in CANDIDATES}
+                cands = [S for S in CANDIDATES if S <= max(1, -(-Lmax // base.page_size))]
+                tot = {S: 0.0 for S in cands}
+                rel = []  # relative differences between the two timings of one configuration
                 for rep in range(3):
                     w = base.scaled(batch=bk, lengths="loguniform", length_lo=max(64, Lmax // 32),
                                     length_hi=Lmax, pin_max=True, seed=100 + 10 * k + rep)
                     batch = make_resident(da, w, torch)
-                    for S in CANDIDATES:
-                        tot[S] += time_split_only(Step(da, batch, torch, S=S), 10, torch)
+                    for S in cands:
+                        step = Step(da, batch, torch, S=S)
+                        t1 = time_split_merge(step, 10, torch)
+                        t2 = time_split_merge(step, 10, torch)
+                        tot[S] += t1 + t2
+                        rel.append(abs(t1 - t2) / max(min(t1, t2), 1e-9))
                     del batch
                     torch.cuda.empty_cache()
-                best = min(CANDIDATES, key=lambda S: (tot[S], S))
+                fastest = min(tot.values())
+                tol = max(0.01, 2.0 * float(np.median(rel)))
+                best = min(S for S in cands if tot[S] <= fastest * (1.0 + tol))
                 row.append(best)
-                print(f"tune {key} B={bk} bucket={k} -> S={best} "
-                      + " ".join(f"{S}:{tot[S] / 3 * 1e3:.1f}" for S in CANDIDATES), flush=True)
+                print(f"tune {key} B={bk} bucket={k} -> S={best} (noise tol {100 * tol:.1f} %) "
+                      + " ".join(f"{S}:{tot[S] / 6 * 1e3:.1f}" for S in cands), flush=True)
             rows.append(row)
         table.tables[key] = rows
+        table.save()  # after every variant, so a long sweep keeps what it has done
     table.save()
     print(json.dumps({"tuned": list(table.tables)}), flush=True)
 
