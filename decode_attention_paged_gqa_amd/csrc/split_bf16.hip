@@ -1,7 +1,7 @@
 // Stage 1 for a dense bf16 cache and small query groups (G*q <= 5): the
 // vector-ALU path of the GQA flash-decode stage 1 (LightLLM PR #1549,
 // "Covered decode kernels").  Same contract as decode_attn_split (entry
-// point in split_fma.hip); built to stream K/V at HBM speed.
+// point in stage1.cpp); built to stream K/V at HBM speed.
 //
 // Work decomposition: one workgroup (4 waves) per (kv-head g, split s,
 // request b); the split's tokens are cut into 8-token tiles dealt
