@@ -135,3 +135,60 @@ def test_graph_replay_matches_eager(gpu, w, table):
     else:
         U.check_quant(U.to_np(step.out), out_ref, f"{w.name} graph out")
     U.check_lse(U.to_np(step.lse), lse_ref, f"{w.name} graph lse")
+
+
+class StaticStep(Step):
+    """The same step through decode_attn_decode_static: the split partials live
+    in the library's per-GPU scratch array, so the captured graph holds no
+    caller-allocated intermediate at all."""
+
+    def __call__(self):
+        da, b, w, md = self.da, self.batch, self.w, self.md
+        sched = {}
+        if self.table is not None:
+            sched = dict(split_table=self.table, bucket_tokens=512, max_splits=self.S,
+                         work_capacity=md["work_list"].shape[0])
+        da.decode_attn_metadata(b.seq_lens, b.req_pool_indices, b.req_to_token, w.page_size,
+                                b.max_pages, q_stride=w.q_per_req, out=md, **sched)
+        kw = dict(batch_order=md["batch_order"], kv_layout=w.kv_layout, causal=w.causal,
+                  softmax_scale=w.softmax_scale, out=self.out, lse_out=self.lse)
+        if self.table is not None:
+            kw.update(split_counts=md["split_counts"], work_list=md["work_list"])
+        if w.kv != W.KV_DENSE:
+            kw.update(k_scale=b.k_scale, v_scale=b.v_scale,
+                      cache_format="int8" if w.kv == W.KV_INT8 else "int4")
+        da.decode_attn_decode_static(b.q, b.k_pool, b.v_pool, md["page_table"],
+                                     md["cache_seqlens"], self.S, **kw)
+
+
+@pytest.mark.parametrize("table", [None, TABLE], ids=["batch_wide_S", "per_request"])
+@pytest.mark.parametrize("w", CASES[:4], ids=lambda w: w.name)
+def test_static_entry_point_replays_like_split_and_merge(gpu, w, table):
+    """Metadata and decode_attn_decode_static captured in one graph; every
+    replay, after the inputs change, must equal the eager split + merge path
+    (other buffers) bit for bit."""
+    log(f"graph static {w.name} table={table}")
+    batch = W.make_batch(w, device="cuda")
+    S = 4 if table is None else 8
+    step = StaticStep(gpu, batch, S, table)
+    ref = Step(gpu, batch, S, table)
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(23)
+    L0 = batch.seq_lens.clone()
+    for rep in range(4):
+        if rep:
+            cut = torch.randint(0, 3, L0.shape, generator=gen, device="cuda", dtype=torch.int32)
+            batch.seq_lens.copy_(torch.clamp(L0 - cut * 41 * rep, min=0))
+            batch.q.copy_(torch.randn(batch.q.shape, generator=gen, device="cuda").to(batch.q.dtype))
+        ref()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, ref.out), rep
+        assert torch.equal(step.lse, ref.lse), rep
+        log(f"  replay {rep}: static entry point bit-identical to split + merge")
