@@ -38,7 +38,8 @@
 // Memory pipeline: global_load_lds into a per-wave LDS ring of 16-token
 // stages (K 16*D bytes, V as many, scales 256 B; 4 stages at D = 128, 8 at
 // D = 64, so that about as many bytes are in flight), read back by inline
-// asm after an explicit vmcnt wait.  At D = 128 a row's eight 16-byte chunks
+// asm after an explicit vmcnt wait.  Codes stream non-temporal, scales with
+// the default policy (their lines have several readers).  At D = 128 a row's eight 16-byte chunks
 // are rotated by ((token / 2) mod 8), at D = 64 its four by ((token / 4) mod
 // 4), and there row 4*lg + j sits in row slot 4*lg + ((j + lg) mod 4): 64-byte
 // rows 256 bytes apart would put the four lane groups' V reads on the same
@@ -364,9 +365,13 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
       __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * kD + voff_kv[h]),
                                        (DA_LDS void*)(st + kStageV + 1024 * h), 16, 0,
                                        da::kStreamPolicy);
+    // The scales keep the default policy: a 2-byte scale per token puts
+    // several readers on one cache line (head-major: the four waves' tiles;
+    // token-major: the eight kv-heads' workgroups), and a non-temporal read
+    // would evict the line before the next reader comes.
     const long long e = row0 + (long long)sc_tok * a.slot_stride;  // scale index
     __builtin_amdgcn_global_load_lds((const void*)(sc_base + ((2 * e) & ~3ll)),
-                                     (DA_LDS void*)(st + kStageSc), 4, 0, da::kStreamPolicy);
+                                     (DA_LDS void*)(st + kStageSc), 4, 0, 0);
   };
 
   // Half of the scale dword holding token 4*lg + i's scale.  Its index is
