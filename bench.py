@@ -572,8 +572,11 @@ def tune_variants(which):
     # the same shapes at head dim 64 (one per stage-1 kernel)
     variants += [v.scaled(name=v.name.replace("_d128_", "_d64_"), head_dim=64)
                  for v in (W.RAGGED_B64, W.INT8_B32, W.INT4_MTP_B64, W.BF16_MTP_B64)]
-    # the bf16 vector kernel over the token-major pool layout
-    variants += [v.scaled(name=v.name + "_nhd", kv_layout="NHD") for v in (W.RAGGED_B64, W.BF16_B16)]
+    # the token-major pool layout: the bf16 vector kernel, and one shape per
+    # matrix-core kernel (INT4 at both head dims)
+    variants += [v.scaled(name=v.name + "_nhd", kv_layout="NHD")
+                 for v in (W.RAGGED_B64, W.BF16_B16, W.INT8_B32, W.INT4_MTP_B64, W.BF16_MTP_B64,
+                           W.INT4_MTP_D64_B64)]
     if which == "all":
         return variants
     keep = set(which.split(","))
