@@ -64,6 +64,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="ragged_bf16_b64_hq40_hkv8_d128_p64_L1k-32k")
+    p.add_argument("--kv-layout", choices=("HND", "NHD"), default=None,
+                   help="override the workload's pool layout (head-major HND, token-major NHD)")
     p.add_argument("--splits", type=int, default=0, help="override num_splits (0 = table)")
     p.add_argument("--sched", choices=("batch", "request"), default="batch",
                    help="batch-wide num_splits, or per-request counts from the metadata prelude")
@@ -813,6 +815,7 @@ def profile_report(prefix):
     line = [ln for ln in open(trace_log) if ln.startswith('{"metric"')][-1]
     res = json.loads(line)
     w = W.WORKLOADS[res["config"]["workload"]]
+    w = w.scaled(kv_layout=res["config"].get("kv_layout", w.kv_layout))
     wl = w.name
     kv = kv_name(w)
     sched = res["schedule"]
@@ -843,6 +846,8 @@ def profile_report(prefix):
              + f" (seed {w.seed}): {cfg['kv_tokens']:,} tokens, {ab:,} algorithmic bytes per "
              f"stage-1 launch")
     run = f"python3 $R/bench.py --workload {wl} --sched {sched['mode']}"
+    if w.kv_layout != W.WORKLOADS[wl].kv_layout:
+        run += f" --kv-layout {w.kv_layout}"
     cmds = ["cd /tmp && export TMPDIR=/tmp",
             f"rocprofv3 --kernel-trace --stats --output-format csv -d $R/{rel}_trace -o run -- "
             f"{run} --steps 20 --warmup 5 --no-cpu-baseline --no-alt --no-variants",
@@ -963,6 +968,8 @@ def main():
             tune_chunks(da, torch, args.tune_chunks, old_keys)
         return
     w = W.WORKLOADS[args.workload]
+    if args.kv_layout:
+        w = w.scaled(kv_layout=args.kv_layout)
     batches = resident_copies(da, w, torch, args.pool_copies)
     batch = batches[0]
     key = kernel_key(kv_name(w), rows_per_kv_head(w), w.head_dim, w.page_size, w.kv_layout)
