@@ -64,6 +64,11 @@ extern "C" int32_t decode_attn_decode_static(
     return DA_ERR_INVALID_ARG;
   const long long rows = (long long)batch * q_per_req * num_q_heads;
   if (rows > (1ll << 30)) return DA_ERR_INVALID_ARG;
+  // rows * S * (D + 1) floats must fit; tested by division, so that no
+  // product of the (not yet validated) sizes can wrap
+  const unsigned long long per_row = (unsigned long long)num_splits * ((unsigned long long)head_dim + 1);
+  if (per_row > (unsigned long long)DA_STATIC_SCRATCH_BYTES / sizeof(float) / (unsigned long long)rows)
+    return DA_ERR_TOO_LARGE;
   // partials: o [rows, S, D] fp32 from the start, lse [rows, S] fp32 after it
   const size_t o_bytes = align256((size_t)rows * num_splits * head_dim * sizeof(float));
   const size_t lse_bytes = (size_t)rows * num_splits * sizeof(float);

@@ -113,6 +113,15 @@ def test_static_decode_refuses_before_touching_a_device(lib):
                      (12, 0, 1), (20, 0, 1), (28, ctypes.c_void_p(0x1001), 1)):
         b = list(a); b[i] = v
         assert lib.decode_attn_decode_static(*b) == st, (i, v)
+    # sizes whose product would wrap 64 bits (2^30 rows x 2^31 - 1 splits x 2^31 D) are refused
+    # as too large, not sized modulo 2^64
+    b = list(a)
+    b[12], b[13], b[14], b[15], b[16], b[20] = 2 ** 22, 16, 16, 16, 2 ** 31 - 1, 2 ** 31 - 1
+    assert lib.decode_attn_decode_static(*b) == 4
+    b[12], b[20], b[16] = 1, 1, 2 ** 31 - 1  # one row, one split, absurd D: still beyond the scratch
+    b[13] = b[14] = 1
+    b[15] = 1
+    assert lib.decode_attn_decode_static(*b) == 4
 
 
 @pytest.mark.parametrize("scale", [float("nan"), float("inf"), float("-inf"), 0.0, -0.125,
