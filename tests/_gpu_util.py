@@ -32,8 +32,6 @@ Gates for floating point, by output type:
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 import torch
 
@@ -211,14 +209,6 @@ def oracle_sampled(batch: W.PagedBatch, pairs):
 
 
 FP16_U = 2.0 ** -11
-
-
-def rows_per_block(w: W.Workload) -> int:
-    """Query rows one stage-1 workgroup takes: the G*q rows of a kv-head, cut
-    into ceil(G*q / 16) blocks of equal size (the last may be shorter)."""
-    rows = w.group * w.q_per_req
-    nrb = -(-rows // 16)
-    return -(-rows // nrb)
 
 
 def uses_matrix_path(w: W.Workload) -> bool:

@@ -5,7 +5,6 @@ term, a wrong sign or index, a transposed operand).  The copy is built from
 the module's source text, swapped in for the pin tests, and at least one pin
 must fail.  The real oracle is never modified.
 """
-import importlib.util
 import inspect
 import types
 
