@@ -111,6 +111,13 @@ INT4_FP32Q_D64 = W.INT4_MTP_B64.scaled(name="int4_fp32q_d64_r16_p32", batch=3, d
                                        length_list=(3, 100, 1000))
 INT4_G8Q2 = W.INT4_MTP_B64.scaled(name="int4_g8_mtp2_small", batch=3, num_q_heads=64, q_per_req=2,
                                   lengths="list", length_list=(1, 48, 700))
+# odd kv-head counts: token-major pools take the one-head-per-workgroup kernel
+# (kv-head pairs need an even count), D = 128 and 64
+INT4_ODD_HKV = W.INT4_MTP_B64.scaled(name="int4_hkv3_mtp4_r16_small", batch=3, num_q_heads=12,
+                                     num_kv_heads=3, lengths="list", length_list=(2, 70, 1300))
+INT4_D64_MQA = W.INT4_MTP_B64.scaled(name="int4_d64_hkv1_q2_r8", batch=3, num_q_heads=4,
+                                     num_kv_heads=1, head_dim=64, q_per_req=2,
+                                     lengths="list", length_list=(9, 300, 1000))
 
 
 def _check_out(w, out, ref, label):
@@ -141,7 +148,7 @@ SMALL = [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, D64_G8, D64_MTP, D64_R20,
          INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV, INT8_FP32Q, INT8_D64, INT8_D64_MTP, INT8_D64_R20,
          INT4_SMALL, INT4_Q1,
          INT4_R12, INT4_G8Q2, INT4_D64, INT4_D64_Q1, INT4_D64_R20, INT8_FP32Q_MTP, INT8_FP32Q_D64,
-         INT4_FP32Q, INT4_FP32Q_Q1, INT4_FP32Q_D64]
+         INT4_FP32Q, INT4_FP32Q_Q1, INT4_FP32Q_D64, INT4_ODD_HKV, INT4_D64_MQA]
 
 
 def both_layouts(ws):
