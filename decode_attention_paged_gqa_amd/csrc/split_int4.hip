@@ -42,13 +42,16 @@
 //   * PV: output block b row m is d = (D/16)*m + b: lane (lm, lg) reads, for
 //     its four tokens 4*lg+j, elements (D/16)*lm .. + D/16 - 1 of each row
 //     (D = 128: dword lm, in group lm/4; D = 64: half lm%2 of dword lm/2, in
-//     group lm/8).  V^T is dequantised to fp16 as n*s - z*s (one fma
-//     per element pair after the exact n; -z*s rounded once per token; a
-//     high nibble is taken in place as 16 n and meets s / 16), and
+//     group lm/8).  Every d-row of a lane lies in one group, so V = n*s - z*s
+//     splits into two products: V^T operand fp16(n*s), one fma per element
+//     pair on the exact code 1024 + n (fma(1024 + n, s, -1024 s); a high
+//     nibble is taken in place as 1024 + 16 n against s / 16 and -64 s), and
+//     the zero-point term, one product per tile of the tokens' -fp16(z*s)
+//     (the lane's group) with P, accumulated apart and added at the end.
 //     P enters as fp16(p * 2^7) (p <= 2^8 under the lazy rescale below, so
 //     p * 2^7 < 2^15; the factor keeps small weights out of fp16's subnormal
-//     range and cancels against the same factor in l): these two roundings
-//     are the only ones in the product.
+//     range and cancels against the same factor in l): the roundings of
+//     n*s, z*s and P are the only ones in the product.
 //
 // Memory pipeline as in the bf16 kernel: global_load_lds into a per-wave LDS
 // ring, read back by inline asm after an explicit vmcnt wait.  D = 128: 4
@@ -342,12 +345,16 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   }
 
   float4_t acc[NT][kBlocks];
+  // zacc[rt]: -sum_t P_t z_t s_t for the lane's d-rows (one quantisation group
+  // per d-row, the same in every output block); added to acc at the end
+  float4_t zacc[NT];
   float m[NT], l[NT];
   auto reset_state = [&]() {
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
 #pragma unroll
       for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
+      zacc[rt] = {0.f, 0.f, 0.f, 0.f};
       m[rt] = da::kNegInf;
       l[rt] = 0.f;
     }
@@ -513,6 +520,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
         l[rt] *= al;
 #pragma unroll
         for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] *= al;
+        zacc[rt] *= al;
         m[rt] = mn;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -547,9 +555,20 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     }
     const half2_t nzs01 = -(as_h2(__builtin_amdgcn_perm(vsz[1], vsz[0], 0x07060302u)) * s01);
     const half2_t nzs23 = -(as_h2(__builtin_amdgcn_perm(vsz[3], vsz[2], 0x07060302u)) * s23);
-    // high nibbles are taken in place as 16 n: their scale is s / 16
+    // the zero-point term of every d-row of the lane's group: one product
+    {
+      const half4_t za = {nzs01[0], nzs01[1], nzs23[0], nzs23[1]};
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+        zacc[rt] = __builtin_amdgcn_mfma_f32_16x16x16f16(za, pb[rt], zacc[rt], 0, 0, 0);
+    }
+    // n s from the code t = 1024 + n: fma(t, s, -1024 s), one rounding (1024 s
+    // is exact in fp16 while |s| < 64; a larger scale overflows it and the
+    // split takes the scaled pass).  High nibbles are taken in place as
+    // t = 1024 + 16 n against s / 16 and -64 s.
     const half2_t s01h = s01 * half2_t{0.0625, 0.0625}, s23h = s23 * half2_t{0.0625, 0.0625};
-    const half2_t k1024 = {1024, 1024};
+    const half2_t o01 = s01 * half2_t{-1024, -1024}, o23 = s23 * half2_t{-1024, -1024};
+    const half2_t o01h = s01 * half2_t{-64, -64}, o23h = s23 * half2_t{-64, -64};
 #pragma unroll
     for (int kk = 0; kk < kBlocks / 2; ++kk) {
       // byte kk of each token's dword (D = 64: byte 2 (lm % 2) + kk, the
@@ -563,10 +582,10 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
         const int bb = 2 * kk + hi;
         // fp16 1024 + n (low nibble) or 1024 + 16 n (high nibble), exact
         const uint32_t mask = hi ? 0x00F000F0u : 0x000F000Fu;
-        const half2_t n01 = as_h2((x01 & mask) | magic) - k1024;
-        const half2_t n23 = as_h2((x23 & mask) | magic) - k1024;
-        const half2_t a01 = __builtin_elementwise_fma(n01, hi ? s01h : s01, nzs01);
-        const half2_t a23 = __builtin_elementwise_fma(n23, hi ? s23h : s23, nzs23);
+        const half2_t t01 = as_h2((x01 & mask) | magic);
+        const half2_t t23 = as_h2((x23 & mask) | magic);
+        const half2_t a01 = __builtin_elementwise_fma(t01, hi ? s01h : s01, hi ? o01h : o01);
+        const half2_t a23 = __builtin_elementwise_fma(t23, hi ? s23h : s23, hi ? o23h : o23);
         half4_t va = {a01[0], a01[1], a23[0], a23[1]};
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
@@ -649,15 +668,19 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
         compute(j, sd, std::true_type{}, sc);
       }
     }
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] += zacc[rt];
   };
   run_split(std::false_type{});
 
-  // ---- An fp16 V operand out of range (scales or zero points so large that
-  // n*s, z*s or the value itself pass 65504) leaves inf or NaN in the output
-  // sums.  Then the split is computed again with V formed as v * 2^-vexp,
-  // vexp the smallest power that brings the bound |s| * (15 + |z|) of every
-  // V group of the split below 2^15 (so n*s, z*s and v all stay in range);
-  // the factor is taken out again when the partials are written.
+  // ---- An fp16 V operand out of range (a scale of 64 or more, so that 1024 s
+  // overflows, or z*s past 65504) leaves inf or NaN in the output sums.  Then
+  // the split is computed again with V formed as v * 2^-vexp, vexp the
+  // smallest power that brings the bound |s| * max(1024, 15 + |z|) of every
+  // V group of the split below 2^15 (so 1024 s, n*s and z*s all stay in
+  // range); the factor is taken out again when the partials are written.
   {
     bool bad = false;
 #pragma unroll
@@ -680,7 +703,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
       const uint32_t* sz = reinterpret_cast<const uint32_t*>(a.vsz + row * kSz);
 #pragma unroll
       for (int k = 0; k < kGroups; ++k)
-        vm = fmaxf(vm, fabsf(h_lo(sz[k])) * (15.f + fabsf(h_hi(sz[k]))));
+        vm = fmaxf(vm, fabsf(h_lo(sz[k])) * fmaxf(1024.f, 15.f + fabsf(h_hi(sz[k]))));
     }
     for (int o = 32; o > 0; o >>= 1) vm = fmaxf(vm, __shfl_xor(vm, o, 64));
     if (lane == 0) s_vmax[wave] = vm;

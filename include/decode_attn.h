@@ -225,12 +225,13 @@ int32_t decode_attn_metadata_ex(const int32_t* seq_lens, const int64_t* req_pool
  *   - INT8: V enters as fp16((b / 2^7) * s), below 65504 for any scale; per
  *     partial row |dO| <= u * 2 max|v| + 2^-18 (max over the split's tokens;
  *     the 2^-18 where b s / 2^7 falls into fp16's subnormal range).
- *   - INT4: V enters as fma(n, s, -fp16(z s)) in fp16, |dO| <= u * (2 max|v|
- *     + max|z s|) + 2^-24.  When a split's fp16 operands overflow (|s| (15 +
- *     |z|) near 65504 or beyond), the kernel detects it and computes that
+ *   - INT4: V enters as two products, fp16(n s) less fp16(z s) (one rounding
+ *     each, summed apart in fp32), |dO| <= u * (max|v| + max|n s| + max|z s|)
+ *     + 2^-24.  When a split's fp16 operands overflow (|s| of 64 or more, or
+ *     |z s| near 65504 or beyond), the kernel detects it and computes that
  *     split again with s * 2^-e (e the smallest power that brings every
- *     |s| (15 + |z|) of the split below 2^15), adding at most 2^-22 max |s|
- *     (15 + |z|); other splits pay nothing.
+ *     |s| max(1024, 15 + |z|) of the split below 2^15), adding at most
+ *     2^-22 max |s| (15 + |z|); other splits pay nothing.
  *   - Scores: the fp32 terms of a score add up to M = scale * sum_d |q_d| u_d
  *     (u_d = |k_d| for dense caches, |s| (|b| + 128) for INT8, |s| (n_d + |z|)
  *     for INT4) and carry a few units of 2^-24 M; a score error E moves the

@@ -19,16 +19,18 @@ Gates for floating point, by output type:
   and the dequantised V in fp16 (unit roundoff u = 2^-11).  P enters as
   fp16(p * 2^7) (one relative rounding, p * 2^7 stays in fp16's normal range
   down to p = 2^-21); INT8 V as fp16((b / 2^7) * s) (one rounding; in fp16's
-  subnormal range an absolute 2^-25, i.e. 2^-18 in v); INT4 V as
-  fma(n, s, -fp16(z*s)) (at most u*(|v| + |z*s|), plus 2^-24 absolute in the
-  subnormal range), or, when that overflows fp16, the same with s * 2^-e for a
-  split-wide e chosen so that |s| (15 + |z|) 2^-e < 2^15, which adds the
-  rounding of s * 2^-e: at most 2^-22 max|s| (15 + |z|).  Each term p*v so
-  carries at most u*(2|v| + |z*s|) (+u^2 terms) of absolute error per unit of
-  p, plus those absolute floors, and since O divides by the exact fp32 sum of
-  p, |dO| <= u * (2 max|v| + max|z*s|) + floor over the request's tokens
-  (z*s = 0 for INT8); the gate adds that (x1.01) to the fp32 one.  Scores are
-  computed exactly from the codes, so the LSE gate stays 1e-4.
+  subnormal range an absolute 2^-25, i.e. 2^-18 in v); INT4 V as two
+  products, fp16(n*s) (one rounding) less fp16(z*s) (one rounding; the two
+  sums are kept apart in fp32 and subtracted at the end), plus 2^-24 absolute
+  in the subnormal range, or, when an fp16 operand overflows, the same with
+  s * 2^-e for a split-wide e chosen so that |s| max(1024, 15 + |z|) 2^-e <
+  2^15, which adds the rounding of s * 2^-e: at most 2^-22 max|s| (15 + |z|).
+  Each term p*v so carries at most u*(|v| + |n*s| + |z*s|) (+u^2 terms) of
+  absolute error per unit of p (INT8: 2u|v|, i.e. n*s = v and z*s = 0), plus
+  those absolute floors, and since O divides by the exact fp32 sum of p,
+  |dO| <= u * (max|v| + max|n*s| + max|z*s|) + floor over the request's
+  tokens; the gate adds that (x1.01) to the fp32 one.  Scores are computed
+  exactly from the codes, so the LSE gate stays 1e-4.
 """
 from __future__ import annotations
 
@@ -256,19 +258,23 @@ def matrix_path_o_bound(batch: W.PagedBatch):
 
 
 def fp16_pv_o_bound(batch: W.PagedBatch):
-    """Per (request, query head) bound u*(2 max|v| + max|z*s|)*1.01 over the
-    request's visible tokens, shaped [B, 1, Hq, 1, 1] (see the module notes)."""
+    """Per (request, query head) bound u*(max|v| + max|n*s| + max|z*s|)*1.01
+    over the request's visible tokens (INT8: n*s = v, z*s = 0), shaped
+    [B, 1, Hq, 1, 1] (see the module notes)."""
     w = batch.w
     vp, vs = batch.nhd(batch.v_pool), batch.nhd(batch.v_scale)
     if w.kv == W.KV_INT4:
         v = OQ.dequant_int4(W.host_int(vp), W.host_u16(vs))
         sz = OQ.fp16_bits_to_f64(W.host_u16(vs))
-        zs = np.abs(sz[..., 0] * sz[..., 1])  # [P, ps, Hkv, D/32]
+        zsv = sz[..., 0] * sz[..., 1]  # [P, ps, Hkv, D/32]
+        zs = np.abs(zsv)
+        ns = np.abs(v + np.repeat(zsv, 32, axis=-1))  # n*s = v + z*s, exact in fp64
         # the rescaled pass: 2^-22 |s| (15 + |z|), and the subnormal floor
         floor = 2.0 ** -22 * np.abs(sz[..., 0]) * (15.0 + np.abs(sz[..., 1])) + 2.0 ** -24
     else:
         v = OQ.dequant_int8(W.host_int(vp), W.host_u16(vs))
         zs = np.zeros(v.shape[:3] + (1,))
+        ns = np.abs(v)
         floor = np.full(v.shape[:3] + (1,), 2.0 ** -18)
     pt = W.host_int(batch.page_table)
     L = W.host_int(batch.seq_lens)
@@ -281,10 +287,11 @@ def fp16_pv_o_bound(batch: W.PagedBatch):
         t = np.arange(n)
         pages, slots = pt[b, t // w.page_size], t % w.page_size
         vm = np.abs(v[pages, slots]).max(axis=(0, 2))   # [Hkv]
+        nm = ns[pages, slots].max(axis=(0, 2))           # [Hkv]
         zm = zs[pages, slots].max(axis=(0, 2))           # [Hkv]
         fm = floor[pages, slots].max(axis=(0, 2))        # [Hkv]
         for g in range(w.num_kv_heads):
-            out[b, 0, g * G:(g + 1) * G] = (FP16_U * (2 * vm[g] + zm[g]) + fm[g]) * 1.01
+            out[b, 0, g * G:(g + 1) * G] = (FP16_U * (vm[g] + nm[g] + zm[g]) + fm[g]) * 1.01
     return out
 
 
