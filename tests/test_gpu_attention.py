@@ -294,6 +294,12 @@ FULL = [
     (W.INT4_MTP_B64, None, None),
     (W.INT4_MTP_B64, 8, None),
     (W.BF16_MTP_B64, None, None),
+    (W.INT4_MTP_D64_B64, None, None),
+    # the token-major pool layout of the pages, at its own tuned split counts
+    (W.RAGGED_B64.scaled(name=W.RAGGED_B64.name + "_nhd", kv_layout="NHD"), None, None),
+    (W.INT8_B32.scaled(name=W.INT8_B32.name + "_nhd", kv_layout="NHD"), None,
+     [(0, 0), (31, 7), (13, 2)]),
+    (W.INT4_MTP_B64.scaled(name=W.INT4_MTP_B64.name + "_nhd", kv_layout="NHD"), None, None),
 ]
 
 
