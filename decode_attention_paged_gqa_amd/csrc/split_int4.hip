@@ -45,9 +45,10 @@
 //     group lm/8).  Every d-row of a lane lies in one group, so V = n*s - z*s
 //     splits into two products: V^T operand fp16(n*s), one fma per element
 //     pair on the exact code 1024 + n (fma(1024 + n, s, -1024 s); a high
-//     nibble is taken in place as 1024 + 16 n against s / 16 and -64 s), and
-//     the zero-point term, one product per tile of the tokens' -fp16(z*s)
-//     (the lane's group) with P, accumulated apart and added at the end.
+//     nibble is taken in place as 1024 + 16 n, giving fp16(16 n s), and its
+//     output blocks are divided by 16 at the end), and the zero-point term,
+//     one product per tile of the tokens' -fp16(z*s) (the lane's group) with
+//     P, accumulated apart and added at the end.
 //     P enters as fp16(p * 2^7) (p <= 2^8 under the lazy rescale below, so
 //     p * 2^7 < 2^15; the factor keeps small weights out of fp16's subnormal
 //     range and cancels against the same factor in l): the roundings of
@@ -564,11 +565,10 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     }
     // n s from the code t = 1024 + n: fma(t, s, -1024 s), one rounding (1024 s
     // is exact in fp16 while |s| < 64; a larger scale overflows it and the
-    // split takes the scaled pass).  High nibbles are taken in place as
-    // t = 1024 + 16 n against s / 16 and -64 s.
-    const half2_t s01h = s01 * half2_t{0.0625, 0.0625}, s23h = s23 * half2_t{0.0625, 0.0625};
+    // split takes the scaled pass).  A high nibble is taken in place as
+    // t = 1024 + 16 n, which gives 16 n s; its output blocks (odd bb) are
+    // divided by 16 when the pass ends.
     const half2_t o01 = s01 * half2_t{-1024, -1024}, o23 = s23 * half2_t{-1024, -1024};
-    const half2_t o01h = s01 * half2_t{-64, -64}, o23h = s23 * half2_t{-64, -64};
 #pragma unroll
     for (int kk = 0; kk < kBlocks / 2; ++kk) {
       // byte kk of each token's dword (D = 64: byte 2 (lm % 2) + kk, the
@@ -584,8 +584,8 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
         const uint32_t mask = hi ? 0x00F000F0u : 0x000F000Fu;
         const half2_t t01 = as_h2((x01 & mask) | magic);
         const half2_t t23 = as_h2((x23 & mask) | magic);
-        const half2_t a01 = __builtin_elementwise_fma(t01, hi ? s01h : s01, hi ? o01h : o01);
-        const half2_t a23 = __builtin_elementwise_fma(t23, hi ? s23h : s23, hi ? o23h : o23);
+        const half2_t a01 = __builtin_elementwise_fma(t01, s01, o01);
+        const half2_t a23 = __builtin_elementwise_fma(t23, s23, o23);
         half4_t va = {a01[0], a01[1], a23[0], a23[1]};
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
@@ -668,10 +668,12 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
         compute(j, sd, std::true_type{}, sc);
       }
     }
+    // high-nibble blocks carry 16 n s; then the zero-point term
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-      for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] += zacc[rt];
+      for (int bb = 0; bb < kBlocks; ++bb)
+        acc[rt][bb] = (bb & 1 ? acc[rt][bb] * 0.0625f : acc[rt][bb]) + zacc[rt];
   };
   run_split(std::false_type{});
 

@@ -365,3 +365,29 @@ def test_int4_large_zero_points(gpu, D, lay, overflow):
     assert (np.abs(v).max() > 65504) == overflow
     _compare(gpu, batch, 3, w.name + (" s*1000" if overflow else ""), magnitudes=True,
              accumulate=True)
+
+
+@pytest.mark.parametrize("D,lay", [(128, "NHD"), (128, "HND"), (64, "NHD"), (64, "HND")])
+def test_int4_tiny_scales(gpu, D, lay):
+    """K, V encoded from N(0,1) * 1e-4 (scales near 3e-5, fp16 subnormals; Q * 1e4
+    keeps the scores moderate).  The partials must hold the kernel's relative
+    bound alone -- u (max|v| + max|n s| + max|z s|), the subnormal floor, and
+    the score and accumulation terms of the module notes -- with no absolute
+    allowance: at this scale an operand formed from a rounded s / 16 would
+    miss it by two orders of magnitude."""
+    w = _range_workload("int4", D, lay, "bf16", amp=(1e4, 1e-4, 1e-4))
+    log(f"int4 tiny scales {w.name}")
+    batch = W.make_batch(w, device="cuda")
+    sz = OQ.fp16_bits_to_f64(W.host_u16(batch.nhd(batch.v_scale)))
+    assert np.abs(sz[..., 0]).max() < 2.0 ** -14  # every V scale an fp16 subnormal
+    S = 3
+    o_ref, l_ref = U.oracle_partials(batch, S)
+    _, _, o, _ = U.run_decode(gpu, batch, S)
+    M, vmax = _score_terms(batch, w.softmax_scale)
+    E = 2.0 ** -20 * M
+    bound = U.fp16_pv_o_bound(batch) + (2 * E * vmax + 2.0 ** -16 * vmax)[:, None, :, None, None]
+    d = np.abs(U.to_np(o) - o_ref)
+    log(f"  max|dO| {float(d.max()):.3e}, max|O| {float(np.abs(o_ref).max()):.3e}, "
+        f"bound up to {float(bound.max()):.3e}")
+    excess = d - bound
+    assert float(excess.max()) <= 0, f"beyond the relative bound by {float(excess.max()):.3e}"
