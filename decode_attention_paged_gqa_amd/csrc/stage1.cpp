@@ -31,6 +31,9 @@ int32_t check_common(const da_host::SplitCall& c, int32_t kv_layout) {
   if (!(c.scale > 0.f && c.scale <= FLT_MAX)) return DA_ERR_INVALID_ARG;
   if (c.D != 64 && c.D != 128) return DA_ERR_UNSUPPORTED;
   if (!da_host::is_pow2(c.ps) || c.ps < 16 || c.ps > 256) return DA_ERR_UNSUPPORTED;
+  // offsets inside a page are 32-bit in the kernels: a page (page_size slots
+  // of Hkv rows, at most 4 D bytes each) must stay below 2^31 bytes
+  if ((long long)c.ps * c.Hkv * c.D * 4 >= (1ll << 31)) return DA_ERR_UNSUPPORTED;
   if (c.Hq / c.Hkv > (1 << 20)) return DA_ERR_INVALID_ARG;
   // the grouped order (the larger grid) must fit a 1-D launch
   if (da_host::stage1_grid((long long)c.Hkv * c.nrb, c.units, true) > 0x7fffffffll)

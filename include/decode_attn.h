@@ -248,6 +248,9 @@ int32_t decode_attn_metadata_ex(const int32_t* seq_lens, const int64_t* req_pool
  * kernels").  q and the pools share `dtype` (DA_BF16 or DA_FP32).
  *
  *   head_dim in {64, 128}; page_size in {16, 32, 64, 128, 256};
+ *   page_size * num_kv_heads * head_dim * 4 < 2^31 (one page of any cache
+ *   format below 2 GiB: the kernels address inside a page with 32-bit
+ *   offsets; else DA_ERR_UNSUPPORTED; the same for the INT8 / INT4 calls);
  *   kv_layout DA_KV_NHD or DA_KV_HND (pool layout, see "Layouts");
  *   num_q_heads % num_kv_heads == 0 (any group G = Hq / Hkv; G * q_per_req
  *   rows beyond DA_MAX_ROWS run in row blocks, see DA_MAX_ROWS);

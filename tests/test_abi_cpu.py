@@ -89,6 +89,8 @@ def _split_args(**kw):
     (dict(S=0), 1), (dict(S=257), 1), (dict(qn=17), 1), (dict(pt_stride=4), 1),
     (dict(num_pages=0), 1), (dict(D=96), 2), (dict(ps=48), 2), (dict(ps=8), 2),
     (dict(dtype=7), 2), (dict(Hq=2 ** 21, Hkv=1), 1),
+    # one page of 2^31 bytes (64 slots x 2^16 kv-heads x 4 D bytes): beyond 32-bit offsets
+    (dict(Hq=2 ** 16, Hkv=2 ** 16), 2),
     # 16-byte vector accesses: q, pools and o_partial must be 16-byte aligned
     (dict(q=ctypes.c_void_p(0x1008)), 1), (dict(k=ctypes.c_void_p(0x1004)), 1),
     (dict(o=ctypes.c_void_p(0x1008)), 1),
