@@ -22,14 +22,16 @@
 // fp32), each taken through the QK product into the same accumulator.  The offset is taken out with the row's fp32
 // sum of scaled Q, and the token's scale multiplies the result:
 //   q.k = s * 2^-sh * 2^24 * (dot - 2^-24 * 128 * sum_d q'_d).
-// The PV product takes V' = fp16((b / 2^7) * s) (b / 2^7 is exact in fp16;
-// one rounding) and P = fp16(p * 2^7) (one rounding; p <= 2^8 under the lazy
-// rescale, so p * 2^7 < 2^15, and the factor keeps small weights out of
-// fp16's subnormal range).  The two factors cancel in the product, so the
-// output sums are those of p * v while l carries 2^7.  With |b| <= 127 and
-// any fp16 scale (|s| <= 65504), |V'| <= 127 * 65504 / 2^7 < 65504: V' never
-// overflows, whatever the scales; below |b s| = 2^-7 it is an fp16 subnormal
-// (absolute error <= 2^-25 in V', 2^-18 in v).
+// The PV product takes V' = fp16(b * s) (b exact in fp16; one rounding;
+// below |b s| = 2^-14 an fp16 subnormal, absolute error <= 2^-25) and P =
+// fp16(p * 2^7) (one rounding; p <= 2^8 under the lazy rescale, so p * 2^7 <
+// 2^15, and the factor keeps small weights out of fp16's subnormal range);
+// l carries the same 2^7.  Where |b s| passes 65504, V' overflows and the
+// split's sums turn inf or NaN: each wave checks its sums at the end, and the
+// workgroup then computes the split again with V' = fp16((b / 2^7) * s),
+// which stays below 127 * 65504 / 2^7 < 65504 for any fp16 scale (absolute
+// error <= 2^-25 in V', 2^-18 in v, below |b s| = 2^-7), the factor taken out
+// when the partials are written.
 //   * QK: MFMA kb, lane (lm, lg): token lm, elements (D/4)*lg + 8*kb + 0..7;
 //     the lane reads its D/4 contiguous bytes of the row.
 //   * PV: output block bb row m is d = (D/16)*m + bb: lane (lm, lg) reads
@@ -61,7 +63,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kPScale = 7.0f;  // P (and l) carry a factor 2^7
-constexpr int kVShift = 7;       // V' = v / 2^7: the output sums carry 2^-7 against l
+constexpr int kVShift = 7;       // scaled pass: V' = v / 2^7, the output sums carry 2^-7 against l
 constexpr int kMaxSplitPages = 512;
 
 // Per-head-dim geometry of a tile and of the LDS ring.
@@ -194,9 +196,11 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
   constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMainBytes + kMaxSplitPages * 4];
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
+  __shared__ int s_redo;  // a wave's V operand left fp16's range
 
   da::Stage1Item it;
   if (!da::stage1_item<true>(a.sched, a.Hkv, it)) return;
+  if (threadIdx.x == 0) s_redo = 0;  // ordered before any write by the loop's barriers
   const int g = it.g, s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -303,13 +307,16 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 
   float4_t acc[NT][kBlocks];
   float m[NT], l[NT];
+  auto reset_state = [&]() {
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
+    for (int rt = 0; rt < NT; ++rt) {
 #pragma unroll
-    for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
-    m[rt] = da::kNegInf;
-    l[rt] = 0.f;
-  }
+      for (int bb = 0; bb < kBlocks; ++bb) acc[rt][bb] = {0.f, 0.f, 0.f, 0.f};
+      m[rt] = da::kNegInf;
+      l[rt] = 0.f;
+    }
+  };
+  reset_state();
 
   // ---- addressing
   const long long rowb = (long long)a.slot_stride * kD;  // bytes between slots (codes)
@@ -382,8 +389,9 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
 #pragma unroll
   for (int i = 0; i < 4; ++i) sc_shift[i] = ((i * a.slot_stride + g * a.head_stride) & 1) << 4;
 
-  auto compute = [&](int j, const StageData<D>& sd, auto masked_tag) {
+  auto compute = [&](int j, const StageData<D>& sd, auto masked_tag, auto scaled_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr bool SCALED = decltype(scaled_tag)::value;  // V formed as v / 2^7
     // ---- dot[rt][i] = 2^-24 * sum_d q'_d (b_d + 128) for token 4*lg + i, row lm
     // of tile rt
     float4_t dot[NT];
@@ -474,20 +482,24 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     }
     const half2_t s01 = as_h2(__builtin_amdgcn_perm(vs[1], vs[0], 0x05040100u));
     const half2_t s23 = as_h2(__builtin_amdgcn_perm(vs[3], vs[2], 0x05040100u));
-    const half2_t k9 = {9, 9};
+    // the code byte b + 128 in the mantissa of 1024 + (b + 128) (ulp 1), minus
+    // 1152: b exactly, and times s: fp16(b s); on the scaled pass in that of
+    // 8 + (b + 128) / 2^7 (ulp 2^-7), minus 9: b / 2^7, and fp16(b s / 2^7),
+    // which no fp16 scale can overflow
+    constexpr uint32_t kHi = SCALED ? 0x48804880u : 0x64806480u;
+    const half2_t kOff = SCALED ? half2_t{9, 9} : half2_t{1152, 1152};
 #pragma unroll
     for (int hw = 0; hw < kHw; ++hw) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int bb = 4 * hw + kk;
-        // [t0.byte kk, 0, t1.byte kk, 0], then bytes ^ 0x80 and 0x48 above
-        // them: the fp16 8 + (b + 128) / 2^7 (ulp 2^-7 in [8, 16)), exact;
-        // minus 9 it is b / 2^7
+        // [t0.byte kk, 0, t1.byte kk, 0], then bytes ^ 0x80 and the exponent
+        // byte above them
         const uint32_t sel = (uint32_t)kk | 0x0C00u | ((uint32_t)(4 + kk) << 16) | 0x0C000000u;
-        const uint32_t x01 = __builtin_amdgcn_perm(vw[1][hw], vw[0][hw], sel) ^ 0x48804880u;
-        const uint32_t x23 = __builtin_amdgcn_perm(vw[3][hw], vw[2][hw], sel) ^ 0x48804880u;
-        const half2_t a01 = (as_h2(x01) - k9) * s01;
-        const half2_t a23 = (as_h2(x23) - k9) * s23;
+        const uint32_t x01 = __builtin_amdgcn_perm(vw[1][hw], vw[0][hw], sel) ^ kHi;
+        const uint32_t x23 = __builtin_amdgcn_perm(vw[3][hw], vw[2][hw], sel) ^ kHi;
+        const half2_t a01 = (as_h2(x01) - kOff) * s01;
+        const half2_t a23 = (as_h2(x23) - kOff) * s23;
         const half4_t va = {a01[0], a01[1], a23[0], a23[1]};
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
@@ -509,32 +521,59 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
     const int pid = read_stage(ka, va, base + rd_sc, pid_addr(jn), sd);
     if (j + kStages - 1 < nmine) issue(j + kStages - 1, pid);
   };
-  for (; pc < p1; pc += kMaxSplitPages) {
-    const int pe = min(pc + kMaxSplitPages, p1);
-    c0 = pc * ps;
-    const int c1 = min(pe * ps, t1);
-    if (pc != p0) {
-      __syncthreads();  // the previous chunk's page ids are no longer read
-      stage_pids(pe);
-    }
-    __syncthreads();  // s_pid visible
-    const int ntiles = (c1 - c0 + 15) >> 4;
-    nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-    const int lim = tfull - c0 - 16 * wave - 16;
-    const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * kWaves) + 1);
+  auto run_split = [&](auto sc) {
+    for (; pc < p1; pc += kMaxSplitPages) {
+      const int pe = min(pc + kMaxSplitPages, p1);
+      c0 = pc * ps;
+      const int c1 = min(pe * ps, t1);
+      if (pc != p0) {
+        __syncthreads();  // the previous chunk's page ids are no longer read
+        stage_pids(pe);
+      }
+      __syncthreads();  // s_pid visible
+      const int ntiles = (c1 - c0 + 15) >> 4;
+      nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+      const int lim = tfull - c0 - 16 * wave - 16;
+      const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * kWaves) + 1);
 #pragma unroll
-    for (int u = 0; u < kStages - 1; ++u)
-      if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
-    for (int j = 0; j < jfull; ++j) {
-      StageData<D> sd;
-      step(j, sd);
-      compute(j, sd, std::false_type{});
+      for (int u = 0; u < kStages - 1; ++u)
+        if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
+      for (int j = 0; j < jfull; ++j) {
+        StageData<D> sd;
+        step(j, sd);
+        compute(j, sd, std::false_type{}, sc);
+      }
+      for (int j = jfull; j < nmine; ++j) {
+        StageData<D> sd;
+        step(j, sd);
+        compute(j, sd, std::true_type{}, sc);
+      }
     }
-    for (int j = jfull; j < nmine; ++j) {
-      StageData<D> sd;
-      step(j, sd);
-      compute(j, sd, std::true_type{});
-    }
+  };
+  run_split(std::false_type{});
+
+  // ---- V formed as fp16(b s) overflows where |b s| passes 65504, leaving
+  // inf or NaN in the output sums; then the split is computed again with V
+  // formed as fp16(b s / 2^7), which no fp16 scale can overflow, and the
+  // factor is taken out again when the partials are written.
+  int vshift = 0;
+  {
+    bool bad = false;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int bb = 0; bb < kBlocks; ++bb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bad |= !(fabsf(acc[rt][bb][i]) <= 3.0e38f);
+    if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) s_redo = 1;
+  }
+  __syncthreads();
+  if (s_redo) {  // uniform over the workgroup
+    vshift = kVShift;
+    reset_state();
+    pc = p0;
+    stage_pids(min(p0 + kMaxSplitPages, p1));  // every wave is past its last LDS read
+    run_split(std::true_type{});
   }
 
   // ---- l is partial over the lane groups; acc and m are already per row
@@ -559,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_int8_mfma_kernel(const Int8
   }
   __syncthreads();
   write_partials<kWaves, ROWS, D>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S,
-                                  s, kPScale, a.o, a.lse, kVShift);
+                                  s, kPScale, a.o, a.lse, vshift);
 }
 
 template <int D, bool QF>

@@ -222,9 +222,11 @@ int32_t decode_attn_metadata_ex(const int32_t* seq_lens, const int64_t* req_pool
  * Partial outputs are the normalised fp32 rows O_s and their natural-log LSE.
  *
  * Range of the quantised caches: every finite fp16 scale and zero point.
- *   - INT8: V enters as fp16((b / 2^7) * s), below 65504 for any scale; per
- *     partial row |dO| <= u * 2 max|v| + 2^-18 (max over the split's tokens;
- *     the 2^-18 where b s / 2^7 falls into fp16's subnormal range).
+ *   - INT8: V enters as fp16(b s); per partial row |dO| <= u * 2 max|v| +
+ *     2^-25 (max over the split's tokens; the 2^-25 in fp16's subnormal
+ *     range).  When a split's |b s| passes 65504, the kernel detects the
+ *     overflow and computes that split again with fp16((b / 2^7) * s), below
+ *     65504 for any scale, where the floor is 2^-18; other splits pay nothing.
  *   - INT4: V enters as two products, fp16(n s) less fp16(z s) (one rounding
  *     each, summed apart in fp32), |dO| <= u * (max|v| + max|n s| + max|z s|)
  *     + 2^-24.  When a split's fp16 operands overflow (|s| of 64 or more, or

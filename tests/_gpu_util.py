@@ -18,8 +18,10 @@ Gates for floating point, by output type:
   terms, 22 bits, whose 2^-22 relative residue is far inside these gates): the P.V product takes P
   and the dequantised V in fp16 (unit roundoff u = 2^-11).  P enters as
   fp16(p * 2^7) (one relative rounding, p * 2^7 stays in fp16's normal range
-  down to p = 2^-21); INT8 V as fp16((b / 2^7) * s) (one rounding; in fp16's
-  subnormal range an absolute 2^-25, i.e. 2^-18 in v); INT4 V as two
+  down to p = 2^-21); INT8 V as fp16(b * s) (one rounding; in fp16's
+  subnormal range an absolute 2^-25), or, on a split where |b s| passes
+  65504, as fp16((b / 2^7) * s) (an absolute 2^-25 in V', i.e. 2^-18 in v,
+  the floor taken for a request whose max|v| passes 65504); INT4 V as two
   products, fp16(n*s) (one rounding) less fp16(z*s) (one rounding; the two
   sums are kept apart in fp32 and subtracted at the end), plus 2^-24 absolute
   in the subnormal range, or, when an fp16 operand overflows, the same with
@@ -275,7 +277,7 @@ def fp16_pv_o_bound(batch: W.PagedBatch):
         v = OQ.dequant_int8(W.host_int(vp), W.host_u16(vs))
         zs = np.zeros(v.shape[:3] + (1,))
         ns = np.abs(v)
-        floor = np.full(v.shape[:3] + (1,), 2.0 ** -18)
+        floor = np.zeros(v.shape[:3] + (1,))  # set per request below
     pt = W.host_int(batch.page_table)
     L = W.host_int(batch.seq_lens)
     B, G = len(L), w.group
@@ -290,6 +292,8 @@ def fp16_pv_o_bound(batch: W.PagedBatch):
         nm = ns[pages, slots].max(axis=(0, 2))           # [Hkv]
         zm = zs[pages, slots].max(axis=(0, 2))           # [Hkv]
         fm = floor[pages, slots].max(axis=(0, 2))        # [Hkv]
+        if w.kv == W.KV_INT8:  # fp16(b s), or the scaled pass where |v| passes 65504
+            fm = np.where(vm > 65504.0, 2.0 ** -18, 2.0 ** -25)
         for g in range(w.num_kv_heads):
             out[b, 0, g * G:(g + 1) * G] = (FP16_U * (vm[g] + nm[g] + zm[g]) + fm[g]) * 1.01
     return out

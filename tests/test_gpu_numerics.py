@@ -367,19 +367,24 @@ def test_int4_large_zero_points(gpu, D, lay, overflow):
              accumulate=True)
 
 
-@pytest.mark.parametrize("D,lay", [(128, "NHD"), (128, "HND"), (64, "NHD"), (64, "HND")])
-def test_int4_tiny_scales(gpu, D, lay):
-    """K, V encoded from N(0,1) * 1e-4 (scales near 3e-5, fp16 subnormals; Q * 1e4
-    keeps the scores moderate).  The partials must hold the kernel's relative
-    bound alone -- u (max|v| + max|n s| + max|z s|), the subnormal floor, and
-    the score and accumulation terms of the module notes -- with no absolute
-    allowance: at this scale an operand formed from a rounded s / 16 would
-    miss it by two orders of magnitude."""
-    w = _range_workload("int4", D, lay, "bf16", amp=(1e4, 1e-4, 1e-4))
-    log(f"int4 tiny scales {w.name}")
+TINY_CASES = [(kv, d, lay) for kv in ("int8", "int4") for d in (128, 64) for lay in ("NHD", "HND")]
+
+
+@pytest.mark.parametrize("kv,D,lay", TINY_CASES, ids=[f"{a}-d{b}-{c}" for a, b, c in TINY_CASES])
+def test_tiny_scales(gpu, kv, D, lay):
+    """K, V encoded from N(0,1) * 1e-4 (Q * 1e4 keeps the scores moderate):
+    INT8 scales near 3e-6 and INT4 scales near 3e-5, fp16 subnormals.  The
+    partials must hold the kernel's relative bound alone -- u (max|v| +
+    max|n s| + max|z s|), the subnormal floor, and the score and accumulation
+    terms of the module notes -- with no absolute allowance: at this scale an
+    INT4 operand formed from a rounded s / 16, or an INT8 V' formed as
+    fp16(b s / 2^7), would miss it by one to two orders of magnitude."""
+    w = _range_workload(kv, D, lay, "bf16", amp=(1e4, 1e-4, 1e-4))
+    log(f"tiny scales {w.name}")
     batch = W.make_batch(w, device="cuda")
-    sz = OQ.fp16_bits_to_f64(W.host_u16(batch.nhd(batch.v_scale)))
-    assert np.abs(sz[..., 0]).max() < 2.0 ** -14  # every V scale an fp16 subnormal
+    sc = OQ.fp16_bits_to_f64(W.host_u16(batch.nhd(batch.v_scale)))
+    scales = sc[..., 0] if kv == "int4" else sc
+    assert np.abs(scales).max() < 2.0 ** -14  # every V scale an fp16 subnormal
     S = 3
     o_ref, l_ref = U.oracle_partials(batch, S)
     _, _, o, _ = U.run_decode(gpu, batch, S)
