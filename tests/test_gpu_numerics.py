@@ -17,6 +17,9 @@ widened below only by terms derived from the inputs' magnitudes).
   N(0,1) * 1e5 (scales near 3e4, so n*s passes fp16's range and the kernel's
   rescaled pass runs); INT4 zero points shifted by fractions up to +-1e3, with
   and without scales that make z*s pass 65504.
+* Tiny magnitudes: INT8 and INT4 caches encoded from N(0,1) * 1e-4 (every V
+  scale an fp16 subnormal), held to the kernels' relative bound with no
+  absolute allowance.
 
 Gates beyond unit scale.  The standard gates assume unit-scale inputs.  A
 kernel forms each score from fp32 terms whose magnitudes add up to
