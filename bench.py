@@ -844,6 +844,11 @@ def profile_report(prefix):
              + (" with one request at the maximum" if w.pin_max else "")
              + f" (seed {w.seed}): {cfg['kv_tokens']:,} tokens, {ab:,} algorithmic bytes per "
              f"stage-1 launch")
+    copies = int(cfg.get("pool_copies", 1))
+    if copies > 1:
+        wdesc += (f"; consecutive steps rotate over {copies} independent copies of the pools "
+                  f"(K/V and scales under 2 GB otherwise), so no launch finds the previous "
+                  f"one's K/V in the 256 MB Infinity Cache")
     run = f"python3 $R/bench.py --workload {wl} --sched {sched['mode']}"
     if w.kv_layout != W.WORKLOADS[wl].kv_layout:
         run += f" --kv-layout {w.kv_layout}"
