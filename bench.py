@@ -130,7 +130,7 @@ def stage1_kernel(w):
     bf16_q = w.dtype == "bf16"
     if bf16_q and w.kv == W.KV_DENSE:
         if rows <= 5:
-            return "split_bf16_kernel", ["split_bf16.hip", "common.h"]
+            return "split_bf16_kernel", ["split_bf16.hip", "split_vec.h", "common.h"]
         return "split_bf16_mfma_kernel", ["split_bf16_mfma.hip", "mfma_util.h", "common.h"]
     if w.kv == W.KV_INT8:
         return "split_int8_mfma_kernel", ["split_int8.hip", "mfma_util.h", "common.h"]
@@ -138,7 +138,7 @@ def stage1_kernel(w):
         return "split_int4_mfma_kernel", ["split_int4.hip", "mfma_util.h", "common.h"]
     if rows >= 5:  # fp32 cache
         return "split_f32_mfma_kernel", ["split_f32_mfma.hip", "mfma_util.h", "common.h"]
-    return "split_fma_kernel", ["split_fma.hip", "common.h"]
+    return "split_fma_kernel", ["split_fma.hip", "split_vec.h", "common.h"]
 
 
 def kernel_hash(w) -> str:
