@@ -47,6 +47,13 @@ FP32_G2 = W.TINY_FP32.scaled(name="fp32_g2_d64_p16", batch=6, num_q_heads=4, num
 FP32_G1_NC = W.TINY_FP32.scaled(name="fp32_mha_d64_p64", batch=3, num_q_heads=3, num_kv_heads=3,
                                 page_size=64, lengths="list", length_list=(5, 64, 1000),
                                 pool_pages=0)
+FP32_MTP2_G2 = W.TINY_FP32.scaled(name="fp32_mtp2_g2_r4_d128", batch=4, num_q_heads=4,
+                                  num_kv_heads=2, head_dim=128, page_size=64, q_per_req=2,
+                                  causal=True, lengths="list", length_list=(1, 2, 65, 1300),
+                                  pool_pages=0)
+FP32_G3_D64 = W.TINY_FP32.scaled(name="fp32_g3_d64_p32", batch=4, num_q_heads=6, num_kv_heads=2,
+                                 page_size=32, lengths="list", length_list=(7, 32, 33, 900),
+                                 pool_pages=0)
 # the other fp32 shapes: the fp32 matrix-core path
 FP32_G5 = W.TINY_FP32.scaled(name="fp32_g5_d128_p64", batch=3, num_q_heads=10, num_kv_heads=2,
                              head_dim=128, page_size=64, lengths="list",
@@ -144,7 +151,7 @@ def test_tiny_fp32_every_split(gpu, S):
 
 
 SMALL = [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, D64_G8, D64_MTP, D64_R20, D64_G6_P128,
-         FP32_G2, FP32_G1_NC, FP32_G4_D128, FP32_G5, FP32_G8_P16, FP32_MTP, FP32_R20, MHA_P32, MTP_BF16, MTP_BF16_G2Q3,
+         FP32_G2, FP32_G1_NC, FP32_G4_D128, FP32_MTP2_G2, FP32_G3_D64, FP32_G5, FP32_G8_P16, FP32_MTP, FP32_R20, MHA_P32, MTP_BF16, MTP_BF16_G2Q3,
          INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV, INT8_FP32Q, INT8_D64, INT8_D64_MTP, INT8_D64_R20,
          INT4_SMALL, INT4_Q1,
          INT4_R12, INT4_G8Q2, INT4_D64, INT4_D64_Q1, INT4_D64_R20, INT8_FP32Q_MTP, INT8_FP32Q_D64,

@@ -47,6 +47,14 @@ LONG = [
                           length_list=(8250, 9)),
     W.BF16_MTP_B64.scaled(name="long_split_bf16_mtp_p16", batch=2, page_size=16, lengths="list",
                           length_list=(8250, 9)),
+    # fp32: the vector kernel (1024-page table; 2-stage ring at D = 128, 4 at D = 64)
+    # and the matrix-core kernel (512 pages)
+    W.TINY_FP32.scaled(name="long_split_fp32_g4_d128_p16", batch=2, num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, lengths="list", length_list=(16400, 37), pool_pages=0),
+    W.TINY_FP32.scaled(name="long_split_fp32_g2_d64_p16", batch=2, num_q_heads=4, num_kv_heads=2,
+                       lengths="list", length_list=(16400, 37), pool_pages=0),
+    W.TINY_FP32.scaled(name="long_split_fp32_g8_d128_p16", batch=2, num_q_heads=8, num_kv_heads=1,
+                       head_dim=128, lengths="list", length_list=(8250, 9), pool_pages=0),
 ]
 
 
