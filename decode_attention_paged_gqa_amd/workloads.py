@@ -122,9 +122,12 @@ INT4_MTP_D64_B64 = INT4_MTP_B64.scaled(name="int4kv_mtp4_b64_hq32_hkv8_d64_p64_L
 FP32_B16 = BF16_B16.scaled(name="fp32_b16_hq64_hkv8_d128_p64_L8192", dtype="fp32",
                            num_q_heads=64, seed=9)
 
+# the same fp32 cache with G=4: 4 query rows per kv-head, on the vector ALU
+FP32_G4_B16 = BF16_B16.scaled(name="fp32_b16_hq32_hkv8_d128_p64_L8192", dtype="fp32", seed=10)
+
 WORKLOADS = {w.name: w for w in (TINY_FP32, BF16_B16, RAGGED_B64, UNIFORM_B64,
                                  INT8_B32, INT4_MTP_B64, BF16_MTP_B64, BF16_MTP_G5_B64,
-                                 INT4_MTP_D64_B64, FP32_B16)}
+                                 INT4_MTP_D64_B64, FP32_B16, FP32_G4_B16)}
 
 
 def draw_lengths(w: Workload, rng: np.random.Generator) -> np.ndarray:
