@@ -226,9 +226,16 @@ struct MfmaArgs {
 // layout, where every cache line belongs to one kv-head's workgroup; the
 // default in the token-major one, where a 64-byte code row (and a 16-byte
 // scale row) shares its line with the neighbouring kv-heads' rows, which
-// their workgroups read from L2 moments later.
-template <int D, int NT, int POLICY, bool QF>  // QF: fp32 Q
+// their workgroups read from L2 moments later.  HQ: kv-heads per workgroup.
+// HQ = 1: the four waves share one kv-head and take its tiles in turn.  HQ =
+// 4 (token-major pools): wave w takes kv-head HQ*g' + w and every tile of the
+// split, and the waves meet at a barrier before each tile, so they read the
+// same token rows together: the 64-byte code rows of neighbouring kv-heads
+// (one 128-byte line) and half of each 128-byte (scale, zero) line are
+// requested by one CU at once.
+template <int D, int NT, int POLICY, bool QF, int HQ>  // QF: fp32 Q
 __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_kernel(const MfmaArgs a) {
+  static_assert(HQ == 1 || HQ == kWaves, "one kv-head per workgroup or one per wave");
   using Gm = Geo<D>;
   constexpr int kD = D, kGroups = Gm::kGroups, kBlocks = Gm::kBlocks, kStages = Gm::kStages;
   constexpr int kStageK = Gm::kStageK, kStageV = Gm::kStageV, kStageKsz = Gm::kStageKsz;
@@ -243,11 +250,15 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   __shared__ float s_vmax[kWaves];
 
   da::Stage1Item it;
-  if (!da::stage1_item<true>(a.sched, a.Hkv, it)) return;
+  if (!da::stage1_item<true>(a.sched, a.Hkv / HQ, it)) return;
   if (threadIdx.x == 0) s_redo = 0;  // ordered before any write by the loop's barriers
-  const int g = it.g, s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = HQ == 1 ? it.g : HQ * it.g + wave;  // this wave's kv-head
+  const int s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
+  // the wave's tiles: toff, toff + tstep, ... of the split
+  constexpr int tstep = HQ == 1 ? kWaves : 1;
+  const int toff = HQ == 1 ? wave : 0;
   const int lm = lane & 15, lg = lane >> 4;
 
   const int ps = a.page_size;
@@ -423,7 +434,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     rd_vsz = kStageVsz + 32 * lg + 4 * (lm >> 3);
   }
 
-  auto tile_base = [&](int j) { return c0 + ((wave + kWaves * j) << 4); };
+  auto tile_base = [&](int j) { return c0 + ((toff + tstep * j) << 4); };
   auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - pc); };
   auto issue = [&](int j, int pid) {
     const int tb = tile_base(j);
@@ -604,6 +615,10 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   // wait for tile j, read it (stage offset ST + off bytes), refill its stage
   auto step = [&](int j, StageData<D>& sd, uint32_t off, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
+    // HQ > 1: the waves (each its own kv-head, every wave the same number of
+    // tiles) meet before each tile, so their reads of the lines they share
+    // leave the CU together
+    if constexpr (HQ > 1) __builtin_amdgcn_s_barrier();
     // the tiles after j issued so far may stay in flight
     wait_tiles_ahead<Gm::kLoads, kStages - 2>(min(kStages - 2, nmine - 1 - j));
     const int jn = min(j + kStages - 1, nmine - 1);
@@ -628,9 +643,9 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
       }
       __syncthreads();  // s_pid visible
       const int ntiles = (c1 - c0 + 15) >> 4;
-      nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-      const int lim = tfull - c0 - 16 * wave - 16;
-      const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * kWaves) + 1);
+      nmine = ntiles > toff ? (ntiles - toff + tstep - 1) / tstep : 0;
+      const int lim = tfull - c0 - 16 * toff - 16;
+      const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * tstep) + 1);
   #pragma unroll
       for (int u = 0; u < kStages - 1; ++u)
         if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
@@ -697,7 +712,9 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   if (s_redo) {  // uniform over the workgroup
     float vm = 0.f;
     const int32_t* ptrow = a.pt + (long long)b * a.pt_stride;
-    for (int t = p0 * ps + (int)threadIdx.x; t < t1; t += kThreads) {
+    // (HQ = 1: the workgroup's threads over the tokens; else each wave over its kv-head's)
+    for (int t = p0 * ps + (HQ == 1 ? (int)threadIdx.x : lane); t < t1;
+         t += HQ == 1 ? kThreads : 64) {
       const int pid0 = ptrow[t >> a.log2_ps];
       const int pid = (unsigned)pid0 < (unsigned)a.num_pages ? pid0 : 0;
       const long long row = (long long)pid * ps * a.Hkv + (long long)(t & (ps - 1)) * a.slot_stride +
@@ -744,21 +761,36 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
     }
   }
   __syncthreads();
-  write_partials<kWaves, ROWS, D>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S,
-                                  s, kPScale, a.o, a.lse, vexp);
+  if constexpr (HQ == 1) {
+    write_partials<kWaves, ROWS, D>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S,
+                                    s, kPScale, a.o, a.lse, vexp);
+  } else {  // every wave's state is its kv-head's whole split
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      write_partials<1, ROWS, D>(sm_acc + w * ROWS * kD, sm_m + w * ROWS, sm_l + w * ROWS, r0, nr,
+                                 a.G, HQ * it.g + w, b, a.qn, a.Hq, a.sched.S, s, kPScale, a.o,
+                                 a.lse, vexp);
+  }
 }
 
 template <int D, bool QF>
 void launch(const da_host::SplitCall& c, const MfmaArgs& a, int R) {
   const bool hnd = c.kv.slot == 1;  // head-major pool layout
-  const dim3 grid(c.grid(true)), block(kThreads);
+  // token-major pools: four kv-heads per workgroup where they divide evenly
+  const bool quad = !hnd && c.Hkv % kWaves == 0;
+  const dim3 grid(quad ? (unsigned)da_host::stage1_grid((long long)(c.Hkv / kWaves) * c.nrb,
+                                                         c.units, true)
+                       : c.grid(true)),
+      block(kThreads);
   constexpr int kNt = da::kStreamPolicy;
   if (R <= 16) {
-    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 1, kNt, QF>), grid, block, 0, c.stream, a);
-    else hipLaunchKernelGGL((split_int4_mfma_kernel<D, 1, 0, QF>), grid, block, 0, c.stream, a);
+    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 1, kNt, QF, 1>), grid, block, 0, c.stream, a);
+    else if (quad) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 1, 0, QF, kWaves>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((split_int4_mfma_kernel<D, 1, 0, QF, 1>), grid, block, 0, c.stream, a);
   } else {
-    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 2, kNt, QF>), grid, block, 0, c.stream, a);
-    else hipLaunchKernelGGL((split_int4_mfma_kernel<D, 2, 0, QF>), grid, block, 0, c.stream, a);
+    if (hnd) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 2, kNt, QF, 1>), grid, block, 0, c.stream, a);
+    else if (quad) hipLaunchKernelGGL((split_int4_mfma_kernel<D, 2, 0, QF, kWaves>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((split_int4_mfma_kernel<D, 2, 0, QF, 1>), grid, block, 0, c.stream, a);
   }
 }
 
