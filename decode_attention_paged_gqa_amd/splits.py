@@ -42,6 +42,21 @@ def kernel_key(kv: str, rows: int, head_dim: int, page_size: int, kv_layout: str
     return f"{kv}_r{rows}_d{head_dim}_p{page_size}_{kv_layout.lower()}"
 
 
+def heads_per_workgroup(key: str) -> int:
+    """kv-heads one stage-1 workgroup covers for variant ``key`` (with Hkv a
+    multiple of 4): 4 where the kernel takes a token-major pool four kv-heads at
+    a time (INT8 and INT4 at any row count, dense bf16 on the matrix cores,
+    i.e. more than 5 rows, at D = 64), else 1."""
+    kv, rows, d, _page, layout = key.split("_")
+    if layout != "nhd":
+        return 1
+    if kv in ("int8", "int4"):
+        return 4
+    if kv == "bf16" and int(rows[1:]) > 5 and d == "d64":
+        return 4
+    return 1
+
+
 def _heuristic(batch_key: int, bucket: int, num_kv_heads: int = 8, cus: int = 256) -> int:
     pages = bucket * BUCKET_TOKENS // 64
     want = max(1, (4 * cus) // max(1, batch_key * num_kv_heads))
@@ -95,7 +110,8 @@ class SplitTable:
         rows = self.tables.get(key)
         if rows is not None and len(rows) == len(self.batch_keys):
             return rows
-        return [[_heuristic(b, k + 1) for k in range(N_BUCKETS)] for b in self.batch_keys]
+        units = 8 // heads_per_workgroup(key)  # workgroups per request and split (Hkv = 8)
+        return [[_heuristic(b, k + 1, units) for k in range(N_BUCKETS)] for b in self.batch_keys]
 
     def pick(self, key: str, batch: int, kv_len: int = REPRESENTATIVE_KV_LEN) -> int:
         """num_splits for variant ``key`` at this batch size and (max) KV length."""
