@@ -78,6 +78,14 @@ PATHS = [
                           length_list=(4, 300, 900)),
     W.TINY_FP32.scaled(name="chk_fp32_g8", batch=3, num_q_heads=8, num_kv_heads=1,
                        lengths="list", length_list=(1, 300, 900), pool_pages=0),  # fp32 matrix cores
+    # token-major pools: the quantised kernels (and bf16 on the matrix cores at
+    # D = 64) take four kv-heads per workgroup there
+    W.INT8_B32.scaled(name="chk_int8_nhd", batch=3, lengths="list", length_list=(1, 300, 900),
+                      kv_layout="NHD"),
+    W.INT4_MTP_B64.scaled(name="chk_int4_mtp_nhd", batch=3, lengths="list",
+                          length_list=(4, 300, 900), kv_layout="NHD"),
+    W.BF16_MTP_B64.scaled(name="chk_bf16_mtp_d64_nhd", batch=3, head_dim=64, lengths="list",
+                          length_list=(4, 300, 900), kv_layout="NHD"),
 ]
 
 
