@@ -118,13 +118,35 @@ INT4_FP32Q_D64 = W.INT4_MTP_B64.scaled(name="int4_fp32q_d64_r16_p32", batch=3, d
                                        length_list=(3, 100, 1000))
 INT4_G8Q2 = W.INT4_MTP_B64.scaled(name="int4_g8_mtp2_small", batch=3, num_q_heads=64, q_per_req=2,
                                   lengths="list", length_list=(1, 48, 700))
-# odd kv-head counts: token-major pools take the one-head-per-workgroup kernel
-# (kv-head pairs need an even count), D = 128 and 64
+# kv-head counts that are not a multiple of 4: token-major pools take the
+# one-kv-head-per-workgroup kernel (four per workgroup need a multiple of 4),
+# D = 128 and 64
 INT4_ODD_HKV = W.INT4_MTP_B64.scaled(name="int4_hkv3_mtp4_r16_small", batch=3, num_q_heads=12,
                                      num_kv_heads=3, lengths="list", length_list=(2, 70, 1300))
 INT4_D64_MQA = W.INT4_MTP_B64.scaled(name="int4_d64_hkv1_q2_r8", batch=3, num_q_heads=4,
                                      num_kv_heads=1, head_dim=64, q_per_req=2,
                                      lengths="list", length_list=(9, 300, 1000))
+# four kv-heads per workgroup (token-major INT8 / INT4, bf16 matrix cores at
+# D = 64): one group of four (Hkv = 4), three (Hkv = 12), and two row tiles
+# (20 rows) at D = 128
+QUAD = [
+    W.INT4_MTP_B64.scaled(name="int4_hkv4_mtp4_r16", batch=3, num_q_heads=16, num_kv_heads=4,
+                          lengths="list", length_list=(2, 70, 1500)),
+    W.INT4_MTP_B64.scaled(name="int4_hkv12_mtp4_r8", batch=3, num_q_heads=24, num_kv_heads=12,
+                          lengths="list", length_list=(5, 200, 900)),
+    W.INT4_MTP_B64.scaled(name="int4_g5_mtp4_r20", batch=3, num_q_heads=40, lengths="list",
+                          length_list=(3, 129, 1100)),
+    W.INT8_B32.scaled(name="int8_hkv4_g4", batch=3, num_q_heads=16, num_kv_heads=4,
+                      lengths="list", length_list=(1, 65, 1400)),
+    W.INT8_B32.scaled(name="int8_hkv12_g2_mtp2_r4", batch=3, num_q_heads=24, num_kv_heads=12,
+                      q_per_req=2, causal=True, lengths="list", length_list=(2, 300, 800)),
+    W.INT8_B32.scaled(name="int8_g5_mtp4_r20", batch=3, num_q_heads=40, q_per_req=4, causal=True,
+                      lengths="list", length_list=(4, 129, 1100)),
+    W.BF16_MTP_B64.scaled(name="bf16_d64_hkv4_mtp4_r16", batch=3, num_q_heads=16, num_kv_heads=4,
+                          head_dim=64, lengths="list", length_list=(4, 100, 1200)),
+    W.BF16_MTP_B64.scaled(name="bf16_d64_hkv12_mtp2_r8", batch=3, num_q_heads=48, num_kv_heads=12,
+                          head_dim=64, q_per_req=2, lengths="list", length_list=(2, 77, 600)),
+]
 
 
 def _check_out(w, out, ref, label):
@@ -155,7 +177,7 @@ SMALL = [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, D64_G8, D64_MTP, D64_R20,
          INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV, INT8_FP32Q, INT8_D64, INT8_D64_MTP, INT8_D64_R20,
          INT4_SMALL, INT4_Q1,
          INT4_R12, INT4_G8Q2, INT4_D64, INT4_D64_Q1, INT4_D64_R20, INT8_FP32Q_MTP, INT8_FP32Q_D64,
-         INT4_FP32Q, INT4_FP32Q_Q1, INT4_FP32Q_D64, INT4_ODD_HKV, INT4_D64_MQA]
+         INT4_FP32Q, INT4_FP32Q_Q1, INT4_FP32Q_D64, INT4_ODD_HKV, INT4_D64_MQA] + QUAD
 
 
 def both_layouts(ws):
