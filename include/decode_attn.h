@@ -55,7 +55,13 @@
  *                kv_layout DA_KV_HND: [num_pages, Hkv, page_size, row]
  *                (HND keeps a kv-head's rows of a page contiguous, which
  *                makes the stage-1 reads of short rows -- quantised codes,
- *                their scales -- long contiguous runs.)
+ *                their scales -- long contiguous runs.  With NHD and Hkv a
+ *                multiple of 4, the INT8 / INT4 stage-1 kernels, and the bf16
+ *                one for 6 or more rows per kv-head at D = 64, give each of a
+ *                workgroup's four waves its own kv-head, so the lines that
+ *                neighbouring kv-heads share are read together; such calls
+ *                want about four times the num_splits of one kv-head per
+ *                workgroup.)
  *   page_table   [B, page_table_stride], first max_pages entries of a row used
  *   o_partial    [B, q_per_req, Hq, num_splits, D] fp32
  *   lse_partial  [B, q_per_req, Hq, num_splits]    fp32
