@@ -8,17 +8,32 @@
 
 namespace {
 
+// token-major pools take four kv-heads per workgroup at D = 64, where a
+// token's four neighbouring kv-head rows are 512 contiguous bytes (ragged
+// G = 5 batch 246 -> 220 us); at D = 128 it measured slower on the ragged
+// batch (423 -> 442 us), so that head dim keeps one kv-head per workgroup
+template <int D>
+constexpr bool kQuadLayout = D == 64;
+
 // 4 LDS stages of 2*CPL KB per wave: 64 KB of ring at D = 128, so two
 // workgroups share a CU
-template <int D, int RT, int STAGES>
+template <int D, int RT, int STAGES, int HQ>
 __global__ __launch_bounds__(kThreads, 2) void split_bf16_kernel(const VecArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[VecSmem<2, D, RT, STAGES>::BYTES];
-  split_vec_body<false, D, RT, STAGES>(a, smem);
+  split_vec_body<false, D, RT, STAGES, HQ>(a, smem);
 }
 
 template <int D, int RT>
-int32_t launch(const VecArgs& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((split_bf16_kernel<D, RT, 4>), dim3(grid), dim3(kThreads), 0, st, a);
+int32_t launch(const VecArgs& a, const da_host::SplitCall& c, hipStream_t st) {
+  // token-major pools: four kv-heads per workgroup where they divide evenly
+  if (kQuadLayout<D> && c.kv.slot != 1 && c.Hkv % kWaves == 0) {
+    const unsigned grid =
+        (unsigned)da_host::stage1_grid((long long)(c.Hkv / kWaves) * c.nrb, c.units, c.nrb > 1);
+    hipLaunchKernelGGL((split_bf16_kernel<D, RT, 4, kWaves>), dim3(grid), dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((split_bf16_kernel<D, RT, 4, 1>), dim3(c.grid(false)), dim3(kThreads), 0, st,
+                       a);
+  }
   return da_host::launch_status();
 }
 
@@ -32,19 +47,18 @@ int32_t da_split_bf16_fast(const da_host::SplitCall& c) {
   if (!c.q_bf16 || R > 5 || (D != 128 && D != 64)) return -1;
   const VecArgs a = make_vec_args(c);
   hipStream_t st = c.stream;
-  const unsigned grid = c.grid(false);
   if (D == 128) {
     switch (R) {
-      case 1: return launch<128, 1>(a, grid, st);
-      case 2: return launch<128, 2>(a, grid, st);
-      case 3: case 4: return launch<128, 4>(a, grid, st);
-      default: return launch<128, 5>(a, grid, st);
+      case 1: return launch<128, 1>(a, c, st);
+      case 2: return launch<128, 2>(a, c, st);
+      case 3: case 4: return launch<128, 4>(a, c, st);
+      default: return launch<128, 5>(a, c, st);
     }
   }
   switch (R) {
-    case 1: return launch<64, 1>(a, grid, st);
-    case 2: return launch<64, 2>(a, grid, st);
-    case 3: case 4: return launch<64, 4>(a, grid, st);
-    default: return launch<64, 5>(a, grid, st);
+    case 1: return launch<64, 1>(a, c, st);
+    case 2: return launch<64, 2>(a, c, st);
+    case 3: case 4: return launch<64, 4>(a, c, st);
+    default: return launch<64, 5>(a, c, st);
   }
 }

@@ -22,7 +22,7 @@ template <int D, int RT, int STAGES>
 __global__ __launch_bounds__(kThreads, (VecSmem<4, D, RT, STAGES>::BYTES <= 80 * 1024 ? 2 : 1))
 void split_fma_kernel(const VecArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[VecSmem<4, D, RT, STAGES>::BYTES];
-  split_vec_body<true, D, RT, STAGES>(a, smem);
+  split_vec_body<true, D, RT, STAGES, 1>(a, smem);
 }
 
 template <int D, int RT>

@@ -185,8 +185,14 @@ struct VecSmem {
 
 // One workgroup's (kv-head, split, request) over a bf16 (F32 = false) or
 // fp32 cache; smem: the kernel's VecSmem<...>::BYTES of LDS, 16-byte aligned.
-template <bool F32, int D, int RT, int STAGES>
+// HQ: kv-heads per workgroup.  HQ = 1: the four waves share one kv-head and
+// take its tiles in turn.  HQ = 4 (token-major pools): wave w takes kv-head
+// HQ*g' + w and every tile of the split, and the waves meet at a barrier
+// before each tile, so the four kv-heads' neighbouring rows of a token are
+// requested by one CU together.
+template <bool F32, int D, int RT, int STAGES, int HQ>
 __device__ __forceinline__ void split_vec_body(const VecArgs& a, uint8_t* smem) {
+  static_assert(HQ == 1 || HQ == kWaves, "one kv-head per workgroup or one per wave");
   constexpr int EB = F32 ? 4 : 2;
   using SM = VecSmem<EB, D, RT, STAGES>;
   constexpr int CPL = SM::CPL;
@@ -198,10 +204,14 @@ __device__ __forceinline__ void split_vec_body(const VecArgs& a, uint8_t* smem) 
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + SM::MAIN_BYTES);
 
   da::Stage1Item it;
-  if (!da::stage1_item<false>(a.sched, a.Hkv, it)) return;
-  const int g = it.g, s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
+  if (!da::stage1_item<false>(a.sched, a.Hkv / HQ, it)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = HQ == 1 ? it.g : HQ * it.g + wave;  // this wave's kv-head
+  const int s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
+  // the wave's tiles: toff, toff + tstep, ... of the split
+  constexpr int tstep = HQ == 1 ? kWaves : 1;
+  const int toff = HQ == 1 ? wave : 0;
   const int tq = lane >> 3, c = lane & 7;
 
   const int ps = a.page_size;
@@ -276,7 +286,7 @@ __device__ __forceinline__ void split_vec_body(const VecArgs& a, uint8_t* smem) 
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   const uint32_t pid_lds = (uint32_t)(uintptr_t)(DA_LDS void*)s_pid;
 
-  auto tile_base = [&](int j) { return c0 + ((wave + kWaves * j) << 3); };
+  auto tile_base = [&](int j) { return c0 + ((toff + tstep * j) << 3); };
   auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - pc); };
   auto issue = [&](int j, int pid) {
     const int tb = tile_base(j);
@@ -379,6 +389,9 @@ __device__ __forceinline__ void split_vec_body(const VecArgs& a, uint8_t* smem) 
   // without masks; the rest (the split's tail) run masked.  Two loops, so
   // each has a single straight-line body.
   auto step = [&](int j, u32x4 (&x)[NCH]) {
+    // HQ > 1: the waves (each its own kv-head, every wave the same number of
+    // tiles) meet before each tile, so their reads leave the CU together
+    if constexpr (HQ > 1) __builtin_amdgcn_s_barrier();
     // wait for tile j; tiles j+1 .. min(j+STAGES-2, nmine-1) may stay in flight
     const int ahead = min(STAGES - 2, nmine - 1 - j);
     if (ahead >= 2) wait_vmcnt<2 * NCH>();
@@ -399,9 +412,9 @@ __device__ __forceinline__ void split_vec_body(const VecArgs& a, uint8_t* smem) 
     }
     __syncthreads();  // s_pid visible
     const int ntiles = (c1 - c0 + 7) >> 3;
-    nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-    const int lim = tfull - c0 - 8 * wave - 8;
-    const int jfull = lim < 0 ? 0 : min(nmine, lim / (8 * kWaves) + 1);
+    nmine = ntiles > toff ? (ntiles - toff + tstep - 1) / tstep : 0;
+    const int lim = tfull - c0 - 8 * toff - 8;
+    const int jfull = lim < 0 ? 0 : min(nmine, lim / (8 * tstep) + 1);
 #pragma unroll
     for (int u = 0; u < STAGES - 1; ++u)
       if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
@@ -450,16 +463,24 @@ __device__ __forceinline__ void split_vec_body(const VecArgs& a, uint8_t* smem) 
   }
   __syncthreads();
 
-  // ---- combine the partial states and write this split's partial rows
-  for (int idx = threadIdx.x; idx < nr * D; idx += kThreads) {
-    const int r = idx / D, d = idx - r * D;
+  // ---- combine the partial states and write this split's partial rows:
+  // HQ = 1, the four waves' states of the kv-head; else each wave's own (its
+  // kv-head's whole split), wave hw for kv-head HQ*g' + hw
+  constexpr int NW = HQ == 1 ? kWaves : 1;  // waves per kv-head
+  for (int idx = threadIdx.x; idx < HQ * nr * D; idx += kThreads) {
+    int hw = 0, rem = idx;
+    if constexpr (HQ > 1) {
+      hw = idx / (nr * D);
+      rem = idx - hw * (nr * D);
+    }
+    const int r = rem / D, d = rem - r * D;
     float M = da::kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * RT + r]);
+    for (int w = hw; w < hw + NW; ++w) M = fmaxf(M, sm_m[w * RT + r]);
     float lsum = 0.f, o = 0.f;
     if (M != da::kNegInf) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = hw; w < hw + NW; ++w) {
         const float f = da::fast_exp2(sm_m[w * RT + r] - M);
         float lw = 0.f, ow = 0.f;
 #pragma unroll
@@ -471,7 +492,8 @@ __device__ __forceinline__ void split_vec_body(const VecArgs& a, uint8_t* smem) 
         o = fmaf(ow, f, o);
       }
     }
-    const int i = (r0 + r) / a.G, h = g * a.G + ((r0 + r) % a.G);
+    const int gh = HQ == 1 ? g : HQ * it.g + hw;
+    const int i = (r0 + r) / a.G, h = gh * a.G + ((r0 + r) % a.G);
     const long long orow = (((long long)b * a.qn + i) * a.Hq + h) * a.sched.S + s;
     a.o[orow * D + d] = lsum > 0.f ? o / lsum : 0.f;
     if (d == 0) a.lse[orow] = lsum > 0.f ? (M + __log2f(lsum)) * da::kLn2 : da::kNegInf;

@@ -57,7 +57,7 @@
  *                makes the stage-1 reads of short rows -- quantised codes,
  *                their scales -- long contiguous runs.  With NHD and Hkv a
  *                multiple of 4, the INT8 / INT4 stage-1 kernels, and the bf16
- *                one for 6 or more rows per kv-head at D = 64, give each of a
+ *                ones at D = 64, give each of a
  *                workgroup's four waves its own kv-head, so the lines that
  *                neighbouring kv-heads share are read together; such calls
  *                want about four times the num_splits of one kv-head per
