@@ -152,6 +152,14 @@ ROW_BLOCKS = [
     # one kv-head for 64 query heads: 64 rows = 2 x 32
     W.BF16_B16.scaled(name="rows64_bf16_mqa", batch=2, num_q_heads=64, num_kv_heads=1,
                       lengths="list", length_list=(1, 900)),
+    # four kv-heads per workgroup (token-major, Hkv = 4) with two row blocks of 32:
+    # INT8, INT4 and bf16 at D = 64 on the matrix cores, 64 rows each
+    W.INT8_B32.scaled(name="rows64_int8_hkv4_g8_mtp8", batch=2, num_q_heads=32, num_kv_heads=4,
+                      q_per_req=8, causal=True, lengths="list", length_list=(9, 700)),
+    W.INT4_MTP_B64.scaled(name="rows64_int4_hkv4_g4_mtp16", batch=2, num_q_heads=16,
+                          num_kv_heads=4, q_per_req=16, lengths="list", length_list=(17, 600)),
+    W.BF16_B16.scaled(name="rows64_bf16_d64_hkv4_g8_mtp8", batch=2, num_q_heads=32, num_kv_heads=4,
+                      head_dim=64, q_per_req=8, causal=True, lengths="list", length_list=(9, 500)),
     # 16 heads x 16 MTP tokens on one kv-head: 256 rows = 8 x 32
     W.BF16_B16.scaled(name="rows256_bf16_g16_mtp16", batch=2, num_q_heads=16, num_kv_heads=1,
                       q_per_req=16, causal=True, lengths="list", length_list=(16, 500)),
