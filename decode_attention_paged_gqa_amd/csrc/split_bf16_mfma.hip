@@ -6,7 +6,9 @@
 // decode_attn_split.
 //
 // One workgroup (4 waves) per (kv-head g, split s, request b); 16-token tiles
-// dealt round-robin to the waves.  Per tile and wave:
+// dealt round-robin to the waves (token-major pools at D = 64 with Hkv a
+// multiple of 4: one kv-head per wave instead, see HQ below).  Per tile and
+// wave:
 //   S^T[16 tok x 16 rows] = K[16 x D] . Q^T       D/32 x v_mfma_f32_16x16x32_bf16
 //   O^T[D x 16 rows]     += V^T[D x 16] . P^T     D/8 x v_mfma_f32_16x16x16_bf16
 // S is computed transposed so each lane's four scores (4 tokens, one row)

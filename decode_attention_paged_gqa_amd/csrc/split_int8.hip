@@ -6,7 +6,8 @@
 // fp16 scale per (page, slot, kv-head).
 //
 // One workgroup (4 waves) per (kv-head g, split s, request b); 16-token tiles
-// dealt round-robin to the waves.  Per tile and wave:
+// dealt round-robin to the waves (token-major pools with Hkv a multiple of
+// 4: one kv-head per wave instead, see HQ below).  Per tile and wave:
 //   S^T[16 tok x 16 rows] = K[16 x D] . Q^T     D/32 x v_mfma_f32_16x16x32_f16
 //   O^T[D x 16 rows]     += V^T[D x 16] . P^T   D/16 x v_mfma_f32_16x16x16_f16
 // Computing S transposed leaves each lane's four scores (4 tokens, one row)

@@ -6,7 +6,8 @@
 //
 // Work decomposition: one workgroup (4 waves) per (kv-head g, split s,
 // request b); the split's tokens are cut into 8-token tiles dealt
-// round-robin to the waves.  With a batch order or a work list (requests by
+// round-robin to the waves (or, with HQ = 4, one kv-head per wave over every
+// tile: see split_vec_body).  With a batch order or a work list (requests by
 // descending length, from the metadata prelude) the grid walks requests
 // longest first, so the long splits are dispatched before the short ones.
 //
