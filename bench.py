@@ -581,7 +581,10 @@ def tune_variants(which):
     # token-major at head dim 64 where the kernel takes four kv-heads per workgroup
     variants += [v.scaled(name=v.name.replace("_d128_", "_d64_") + "_nhd", head_dim=64,
                           kv_layout="NHD")
-                 for v in (W.INT8_B32, W.BF16_MTP_B64, W.RAGGED_B64, W.BF16_B16)]
+                 for v in (W.INT8_B32, W.BF16_MTP_B64, W.RAGGED_B64, W.BF16_B16, W.FP32_G4_B16,
+                           W.FP32_B16)]
+    # the dense fp32 cache: vector kernel (G = 4) and matrix cores (G = 8)
+    variants += [W.FP32_G4_B16, W.FP32_B16]
     if which == "all":
         return variants
     keep = set(which.split(","))

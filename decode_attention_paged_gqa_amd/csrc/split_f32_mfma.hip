@@ -143,9 +143,15 @@ struct F32MfmaArgs {
 };
 
 // NT row tiles of 16 query rows (NT * 16 rows per workgroup): the K/V
-// operands of a tile are read once and serve every row tile.
-template <int D, int NT>
+// operands of a tile are read once and serve every row tile.  HQ: kv-heads
+// per workgroup.  HQ = 1: the four waves share one kv-head and take its
+// tiles in turn.  HQ = 4 (token-major pools at D = 64): wave w takes kv-head
+// HQ*g' + w and every tile of the split, and the waves meet at a barrier
+// before each tile, so the four kv-heads' neighbouring rows of a token are
+// requested by one CU together.
+template <int D, int NT, int HQ>
 __global__ __launch_bounds__(kThreads, 1) void split_f32_mfma_kernel(const F32MfmaArgs a) {
+  static_assert(HQ == 1 || HQ == kWaves, "one kv-head per workgroup or one per wave");
   using Gm = Geo<D>;
   constexpr int kKq = Gm::kKq, kVc = Gm::kVc, kBlocks = Gm::kBlocks, kStages = Gm::kStages;
   constexpr int kStageK = Gm::kStageK, kStageV = Gm::kStageV, kStageBytes = Gm::kStageBytes;
@@ -157,10 +163,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_f32_mfma_kernel(const F32Mf
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + kMainBytes);
 
   da::Stage1Item it;
-  if (!da::stage1_item<false>(a.sched, a.Hkv, it)) return;
-  const int g = it.g, s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
+  if (!da::stage1_item<false>(a.sched, a.Hkv / HQ, it)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = HQ == 1 ? it.g : HQ * it.g + wave;  // this wave's kv-head
+  const int s = it.s, b = it.b, r0 = it.r0, nr = it.nr;
+  // the wave's tiles: toff, toff + tstep, ... of the split
+  constexpr int tstep = HQ == 1 ? kWaves : 1;
+  const int toff = HQ == 1 ? wave : 0;
   const int lm = lane & 15, lg = lane >> 4;
 
   const int ps = a.page_size;
@@ -255,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_f32_mfma_kernel(const F32Mf
       rd_v[kVc * jj + x] = kStageV + kRow * t + 16 * Gm::chunk_pos(t, kVc * lm + x);
     }
 
-  auto tile_base = [&](int j) { return c0 + ((wave + kWaves * j) << 4); };
+  auto tile_base = [&](int j) { return c0 + ((toff + tstep * j) << 4); };
   auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - pc); };
   const long long head_row = (long long)g * a.head_stride;
   auto issue = [&](int j, int pid) {
@@ -344,6 +354,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_f32_mfma_kernel(const F32Mf
   // tile j + kStages at once; tiles j+1 .. j+kStages stay in flight during
   // compute(j)
   auto step = [&](int j, StageData<D>& sd) {
+    // HQ > 1: the waves (each its own kv-head, every wave the same number of
+    // tiles) meet before each tile, so their reads leave the CU together
+    if constexpr (HQ > 1) __builtin_amdgcn_s_barrier();
     // the tiles after j issued so far may stay in flight
     wait_tiles_ahead<Gm::kLoads, kStages - 1>(min(kStages - 1, nmine - 1 - j));
     const int jn = min(j + kStages, nmine - 1);  // the tile to issue next
@@ -366,9 +379,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_f32_mfma_kernel(const F32Mf
     }
     __syncthreads();  // s_pid visible
     const int ntiles = (c1 - c0 + 15) >> 4;
-    nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-    const int lim = tfull - c0 - 16 * wave - 16;
-    const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * kWaves) + 1);
+    nmine = ntiles > toff ? (ntiles - toff + tstep - 1) / tstep : 0;
+    const int lim = tfull - c0 - 16 * toff - 16;
+    const int jfull = lim < 0 ? 0 : min(nmine, lim / (16 * tstep) + 1);
 #pragma unroll
     for (int u = 0; u < kStages; ++u)
       if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
@@ -405,18 +418,32 @@ __global__ __launch_bounds__(kThreads, 1) void split_f32_mfma_kernel(const F32Mf
     }
   }
   __syncthreads();
-  write_partials<kWaves, ROWS, D>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S,
-                                  s, 0.f, a.o, a.lse);
+  if constexpr (HQ == 1) {
+    write_partials<kWaves, ROWS, D>(sm_acc, sm_m, sm_l, r0, nr, a.G, g, b, a.qn, a.Hq, a.sched.S,
+                                    s, 0.f, a.o, a.lse);
+  } else {  // every wave's state is its kv-head's whole split
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      write_partials<1, ROWS, D>(sm_acc + w * ROWS * D, sm_m + w * ROWS, sm_l + w * ROWS, r0, nr,
+                                 a.G, HQ * it.g + w, b, a.qn, a.Hq, a.sched.S, s, 0.f, a.o, a.lse);
+  }
 }
 
 template <int D>
 void launch(const da_host::SplitCall& c, const F32MfmaArgs& a, int R) {
-  if (R <= 16)
-    hipLaunchKernelGGL((split_f32_mfma_kernel<D, 1>), dim3(c.grid(false)), dim3(kThreads), 0,
-                       c.stream, a);
-  else
-    hipLaunchKernelGGL((split_f32_mfma_kernel<D, 2>), dim3(c.grid(false)), dim3(kThreads), 0,
-                       c.stream, a);
+  // token-major pools at D = 64: four kv-heads per workgroup where they divide evenly
+  const bool quad = D == 64 && c.kv.slot != 1 && c.Hkv % kWaves == 0;
+  const dim3 grid(quad ? (unsigned)da_host::stage1_grid((long long)(c.Hkv / kWaves) * c.nrb,
+                                                         c.units, c.nrb > 1)
+                       : c.grid(false)),
+      block(kThreads);
+  if (R <= 16) {
+    if (quad) hipLaunchKernelGGL((split_f32_mfma_kernel<D, 1, kWaves>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((split_f32_mfma_kernel<D, 1, 1>), grid, block, 0, c.stream, a);
+  } else {
+    if (quad) hipLaunchKernelGGL((split_f32_mfma_kernel<D, 2, kWaves>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((split_f32_mfma_kernel<D, 2, 1>), grid, block, 0, c.stream, a);
+  }
 }
 
 }  // namespace

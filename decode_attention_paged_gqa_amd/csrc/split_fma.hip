@@ -17,26 +17,40 @@ namespace {
 // workgroup per CU (B = 16, 8K tokens: 80-81 % of 8 TB/s against 76-82 %).
 constexpr int FP32_D128_STAGES = 2;
 
+// token-major pools take four kv-heads per workgroup at D = 64 (B = 16, 8K,
+// G = 4: 87.6 -> 85.5 us; G = 1: 89.3 -> 85.8 us); D = 128 rows are 512
+// bytes, and that head dim keeps one kv-head per workgroup
+template <int D>
+constexpr bool kQuadLayout = D == 64;
+
 // two workgroups per CU where their LDS fits (160 KB per CU), else one
-template <int D, int RT, int STAGES>
+template <int D, int RT, int STAGES, int HQ>
 __global__ __launch_bounds__(kThreads, (VecSmem<4, D, RT, STAGES>::BYTES <= 80 * 1024 ? 2 : 1))
 void split_fma_kernel(const VecArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[VecSmem<4, D, RT, STAGES>::BYTES];
-  split_vec_body<true, D, RT, STAGES, 1>(a, smem);
+  split_vec_body<true, D, RT, STAGES, HQ>(a, smem);
 }
 
 template <int D, int RT>
-int32_t launch(const VecArgs& a, unsigned grid, hipStream_t st) {
+int32_t launch(const VecArgs& a, const da_host::SplitCall& c, hipStream_t st) {
   constexpr int STAGES = D == 128 ? FP32_D128_STAGES : 4;
-  hipLaunchKernelGGL((split_fma_kernel<D, RT, STAGES>), dim3(grid), dim3(kThreads), 0, st, a);
+  if (kQuadLayout<D> && c.kv.slot != 1 && c.Hkv % kWaves == 0) {
+    const unsigned grid =
+        (unsigned)da_host::stage1_grid((long long)(c.Hkv / kWaves) * c.nrb, c.units, c.nrb > 1);
+    hipLaunchKernelGGL((split_fma_kernel<D, RT, STAGES, kWaves>), dim3(grid), dim3(kThreads), 0, st,
+                       a);
+  } else {
+    hipLaunchKernelGGL((split_fma_kernel<D, RT, STAGES, 1>), dim3(c.grid(false)), dim3(kThreads), 0,
+                       st, a);
+  }
   return da_host::launch_status();
 }
 
 template <int D>
-int32_t launch_d(const VecArgs& a, unsigned grid, hipStream_t st) {
-  if (a.R <= 1) return launch<D, 1>(a, grid, st);
-  if (a.R <= 2) return launch<D, 2>(a, grid, st);
-  return launch<D, 4>(a, grid, st);
+int32_t launch_d(const VecArgs& a, const da_host::SplitCall& c, hipStream_t st) {
+  if (a.R <= 1) return launch<D, 1>(a, c, st);
+  if (a.R <= 2) return launch<D, 2>(a, c, st);
+  return launch<D, 4>(a, c, st);
 }
 
 }  // namespace
@@ -46,6 +60,5 @@ int32_t launch_d(const VecArgs& a, unsigned grid, hipStream_t st) {
 int32_t da_split_f32_fma(const da_host::SplitCall& c) {
   if (c.q_bf16 || c.rb_rows > 4 || (c.D != 128 && c.D != 64)) return -1;
   const VecArgs a = make_vec_args(c);
-  const unsigned grid = c.grid(false);
-  return c.D == 128 ? launch_d<128>(a, grid, c.stream) : launch_d<64>(a, grid, c.stream);
+  return c.D == 128 ? launch_d<128>(a, c, c.stream) : launch_d<64>(a, c, c.stream);
 }

@@ -45,13 +45,13 @@ def kernel_key(kv: str, rows: int, head_dim: int, page_size: int, kv_layout: str
 def heads_per_workgroup(key: str) -> int:
     """kv-heads one stage-1 workgroup covers for variant ``key`` (with Hkv a
     multiple of 4): 4 where the kernel takes a token-major pool four kv-heads at
-    a time (INT8 and INT4 at any row count, dense bf16 at D = 64), else 1."""
+    a time (INT8 and INT4 at any row count, dense bf16 and fp32 at D = 64), else 1."""
     kv, _rows, d, _page, layout = key.split("_")
     if layout != "nhd":
         return 1
     if kv in ("int8", "int4"):
         return 4
-    if kv == "bf16" and d == "d64":
+    if kv in ("bf16", "fp32") and d == "d64":
         return 4
     return 1
 

@@ -56,8 +56,8 @@
  *                (HND keeps a kv-head's rows of a page contiguous, which
  *                makes the stage-1 reads of short rows -- quantised codes,
  *                their scales -- long contiguous runs.  With NHD and Hkv a
- *                multiple of 4, the INT8 / INT4 stage-1 kernels, and the bf16
- *                ones at D = 64, give each of a
+ *                multiple of 4, the INT8 / INT4 stage-1 kernels, and the dense
+ *                (bf16, fp32) ones at D = 64, give each of a
  *                workgroup's four waves its own kv-head, so the lines that
  *                neighbouring kv-heads share are read together; such calls
  *                want about four times the num_splits of one kv-head per

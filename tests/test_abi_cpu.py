@@ -262,7 +262,8 @@ def test_split_table_roundtrip(tmp_path, lib):
     assert heads_per_workgroup(kernel_key("bf16", 16, 128, 64, "NHD")) == 1
     assert heads_per_workgroup(kernel_key("bf16", 5, 64, 64, "NHD")) == 4
     assert heads_per_workgroup(kernel_key("bf16", 5, 128, 64, "NHD")) == 1
-    assert heads_per_workgroup(kernel_key("fp32", 4, 64, 64, "NHD")) == 1
+    assert heads_per_workgroup(kernel_key("fp32", 4, 64, 64, "NHD")) == 4
+    assert heads_per_workgroup(kernel_key("fp32", 8, 128, 64, "NHD")) == 1
     fresh = SplitTable()
     assert fresh.pick(nhd, 64, 32768) == 4 * fresh.pick(hnd, 64, 32768)
     # rows tuned for another set of batch keys are not read (heuristic / default instead)

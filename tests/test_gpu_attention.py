@@ -126,7 +126,7 @@ INT4_ODD_HKV = W.INT4_MTP_B64.scaled(name="int4_hkv3_mtp4_r16_small", batch=3, n
 INT4_D64_MQA = W.INT4_MTP_B64.scaled(name="int4_d64_hkv1_q2_r8", batch=3, num_q_heads=4,
                                      num_kv_heads=1, head_dim=64, q_per_req=2,
                                      lengths="list", length_list=(9, 300, 1000))
-# four kv-heads per workgroup (token-major INT8 / INT4, bf16 matrix cores at
+# four kv-heads per workgroup (token-major INT8 / INT4, dense bf16 and fp32 at
 # D = 64): one group of four (Hkv = 4), three (Hkv = 12), and two row tiles
 # (20 rows) at D = 128
 QUAD = [
@@ -146,6 +146,13 @@ QUAD = [
                           head_dim=64, lengths="list", length_list=(4, 100, 1200)),
     W.BF16_MTP_B64.scaled(name="bf16_d64_hkv12_mtp2_r8", batch=3, num_q_heads=48, num_kv_heads=12,
                           head_dim=64, q_per_req=2, lengths="list", length_list=(2, 77, 600)),
+    # dense bf16 and fp32 at D = 64 on the vector ALU, fp32 on the matrix cores
+    W.RAGGED_B64.scaled(name="bf16_d64_hkv4_g5", batch=3, num_q_heads=20, num_kv_heads=4,
+                        head_dim=64, lengths="list", length_list=(1, 150, 1300), pin_max=False),
+    W.TINY_FP32.scaled(name="fp32_d64_hkv4_g2", batch=3, num_q_heads=8, num_kv_heads=4,
+                       page_size=64, lengths="list", length_list=(3, 130, 1100), pool_pages=0),
+    W.TINY_FP32.scaled(name="fp32_d64_hkv4_g8", batch=3, num_q_heads=32, num_kv_heads=4,
+                       page_size=64, lengths="list", length_list=(2, 90, 900), pool_pages=0),
 ]
 
 
