@@ -528,21 +528,28 @@ def resident_copies(da, w, torch, copies=0):
                       for i in range(1, n)]
 
 
+# workload names; "@NHD" runs the workload over the token-major pool layout
 VARIANT_WORKLOADS = ("bf16_b16_hq32_hkv8_d128_p64_L8192", "bf16_b64_hq40_hkv8_d128_p64_L32768",
                      "int8kv_b32_hq32_hkv8_d128_p64_L32768",
-                     "int4kv_mtp4_b64_hq32_hkv8_d128_p64_L8k-32k")
+                     "int4kv_mtp4_b64_hq32_hkv8_d128_p64_L8k-32k",
+                     "int8kv_b32_hq32_hkv8_d128_p64_L32768@NHD",
+                     "int4kv_mtp4_b64_hq32_hkv8_d128_p64_L8k-32k@NHD")
 
 
 def variant_timings(da, torch, steps, warmup):
     """The pages' other decode shapes, each at its tuned split count and timed
-    as the main line is (HIP events per call; pools under 2 GB rotated)."""
+    as the main line is (HIP events per call; pools under 2 GB rotated); the
+    quantised ones also over the token-major pool layout."""
     from decode_attention_paged_gqa_amd import workloads as W
     from decode_attention_paged_gqa_amd.splits import SplitTable, kernel_key
 
     tables = SplitTable.load()
     out = {}
-    for name in VARIANT_WORKLOADS:
+    for entry in VARIANT_WORKLOADS:
+        name, _, layout = entry.partition("@")
         w = W.WORKLOADS[name]
+        if layout:
+            w = w.scaled(kv_layout=layout)
         batches = resident_copies(da, w, torch)
         key = kernel_key(kv_name(w), rows_per_kv_head(w), w.head_dim, w.page_size, w.kv_layout)
         S = tables.pick(key, w.batch, int(batches[0].lengths.max()))
@@ -550,14 +557,14 @@ def variant_timings(da, torch, steps, warmup):
         ms, split_ms, merge_ms, meta_ms, _ = time_config(step_list, steps, warmup, torch)
         ab = algorithmic_bytes(w, batches[0].lengths)
         gbs = ab["split"] / (split_ms * 1e-3) / 1e9
-        out[name] = {"kernel": stage1_kernel(w)[0], "kv": kv_name(w), "batch": w.batch,
-                     "q_per_req": w.q_per_req, "num_q_heads": w.num_q_heads,
-                     "kv_tokens": int(batches[0].lengths.sum()), "num_splits": S,
-                     "pool_copies": len(batches), "split_us": round(split_ms * 1e3, 2),
-                     "step_us": round(ms * 1e3, 2), "split_GBps": round(gbs, 1),
-                     "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "step_frac": round(ab["step"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "algorithmic_bytes_per_launch": ab["split"]}
+        out[entry] = {"kernel": stage1_kernel(w)[0], "kv": kv_name(w), "kv_layout": w.kv_layout,
+                      "batch": w.batch, "q_per_req": w.q_per_req, "num_q_heads": w.num_q_heads,
+                      "kv_tokens": int(batches[0].lengths.sum()), "num_splits": S,
+                      "pool_copies": len(batches), "split_us": round(split_ms * 1e3, 2),
+                      "step_us": round(ms * 1e3, 2), "split_GBps": round(gbs, 1),
+                      "frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "step_frac": round(ab["step"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "algorithmic_bytes_per_launch": ab["split"]}
         del step_list, batches
         torch.cuda.empty_cache()
     return out
