@@ -97,9 +97,11 @@ struct Geo {
   static constexpr int kStageKsz = 32 * kRowBytes;
   static constexpr int kStageVsz = kStageKsz + 16 * kSzBytes;
   static constexpr int kStageBytes = kStageVsz + 16 * kSzBytes;  // 2560 / 1280
-  static constexpr int kStages = D == 128 ? 4 : 8;
+  // four tiles per wave in the ring at either head dim (at D = 64 four ran
+  // faster than six or eight, in both pool layouts)
+  static constexpr int kStages = 4;
   static constexpr int kLoads = D == 128 ? 4 : 2;  // DMA instructions per tile
-  static constexpr int kRingBytes = kWaves * kStages * kStageBytes;  // 40 KB
+  static constexpr int kRingBytes = kWaves * kStages * kStageBytes;  // 40 KB / 20 KB
   // row slot of token t in a code tile, and the rotation of its chunks
   __host__ __device__ static constexpr int slot(int t) {
     return D == 128 ? t : 4 * (t & 3) + (t >> 2);  // an involution at D = 64

@@ -258,6 +258,9 @@ def test_split_table_roundtrip(tmp_path, lib):
     from decode_attention_paged_gqa_amd.splits import heads_per_workgroup
     nhd, hnd = kernel_key("int4", 16, 128, 64, "NHD"), kernel_key("int4", 16, 128, 64, "HND")
     assert heads_per_workgroup(nhd) == 4 and heads_per_workgroup(hnd) == 1
+    nhd8, hnd8 = kernel_key("int8", 4, 128, 64, "NHD"), kernel_key("int8", 4, 128, 64, "HND")
+    assert heads_per_workgroup(nhd8) == 4 and heads_per_workgroup(hnd8) == 1
+    assert heads_per_workgroup(kernel_key("int4", 16, 64, 64, "NHD")) == 4
     assert heads_per_workgroup(kernel_key("bf16", 16, 64, 64, "NHD")) == 4
     assert heads_per_workgroup(kernel_key("bf16", 16, 128, 64, "NHD")) == 1
     assert heads_per_workgroup(kernel_key("bf16", 5, 64, 64, "NHD")) == 4
@@ -266,6 +269,7 @@ def test_split_table_roundtrip(tmp_path, lib):
     assert heads_per_workgroup(kernel_key("fp32", 8, 128, 64, "NHD")) == 1
     fresh = SplitTable()
     assert fresh.pick(nhd, 64, 32768) == 4 * fresh.pick(hnd, 64, 32768)
+    assert fresh.pick(nhd8, 64, 32768) == 4 * fresh.pick(hnd8, 64, 32768)
     # rows tuned for another set of batch keys are not read (heuristic / default instead)
     t2.tables[key] = [[7] * 8] * (len(t2.batch_keys) - 2)
     t2.chunk_pages[key] = [40] * (len(t2.batch_keys) + 1)

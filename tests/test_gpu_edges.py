@@ -160,6 +160,10 @@ ROW_BLOCKS = [
                           num_kv_heads=4, q_per_req=16, lengths="list", length_list=(17, 600)),
     W.BF16_B16.scaled(name="rows64_bf16_d64_hkv4_g8_mtp8", batch=2, num_q_heads=32, num_kv_heads=4,
                       head_dim=64, q_per_req=8, causal=True, lengths="list", length_list=(9, 500)),
+    # INT4 at the common Hkv = 8 (two groups of four kv-heads when token-major),
+    # two row blocks of 32
+    W.INT4_MTP_B64.scaled(name="rows64_int4_hkv8_g4_mtp16", batch=2, q_per_req=16,
+                          lengths="list", length_list=(11, 520)),
     # 16 heads x 16 MTP tokens on one kv-head: 256 rows = 8 x 32
     W.BF16_B16.scaled(name="rows256_bf16_g16_mtp16", batch=2, num_q_heads=16, num_kv_heads=1,
                       q_per_req=16, causal=True, lengths="list", length_list=(16, 500)),
