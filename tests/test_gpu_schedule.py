@@ -17,7 +17,7 @@ from decode_attention_paged_gqa_amd import workloads as W
 from oracle import schedule as OS
 from tests import _gpu_util as U
 from tests.test_gpu_attention import (INT4_G8Q2, INT4_SMALL, INT8_MTP, INT8_ODD_HKV, INT8_SMALL,
-                                      MTP_BF16, RAGGED_SMALL, TINY, D64_P16, INT8_FP32Q,
+                                      MTP_BF16, QUAD, RAGGED_SMALL, TINY, D64_P16, INT8_FP32Q,
                                       _check_out, both_layouts)
 
 pytestmark = pytest.mark.gpu
@@ -113,8 +113,14 @@ def test_reused_out_dict_with_other_options(gpu):
 # ---------------------------------------------------------------- attention
 SMALL_TABLE = [1, 2, 3, 5, 8, 13, 21, 32]
 SMALL_BUCKET = 256
+# the kernels that take four kv-heads per workgroup on token-major pools: bf16
+# at D = 64 on the matrix cores, fp32 at D = 64 on the vector ALU and on the
+# matrix cores, INT4 with Hkv = 16
+_QUAD_SCHED = [w for w in QUAD if w.name in ("bf16_d64_hkv4_mtp4_r16", "fp32_d64_hkv4_g2",
+                                             "fp32_d64_hkv4_g8", "int4_hkv16_g2_mtp2_r4")]
+assert len(_QUAD_SCHED) == 4
 SCHED_CASES = both_layouts([RAGGED_SMALL, D64_P16, MTP_BF16, INT8_SMALL, INT8_MTP, INT8_ODD_HKV,
-                            INT8_FP32Q, INT4_SMALL, INT4_G8Q2]) + [TINY]
+                            INT8_FP32Q, INT4_SMALL, INT4_G8Q2] + _QUAD_SCHED) + [TINY]
 
 
 @pytest.mark.parametrize("w", SCHED_CASES, ids=lambda w: w.name)
