@@ -128,30 +128,32 @@ struct StageData<64> {
   uint32_t kz;     // (scale, zero) of token lm, group lg & 1
 };
 
-// D = 64: all reads of one stage (at a lane-specific address, the stage
-// offset already added) plus the next page id.  V rows of tokens 4*lg + 2x
-// and 4*lg + 2x + 1 sit 128 bytes apart (va[x] addresses the first).
+// D = 64: all reads of one stage (at a lane-specific address plus ST, the
+// stage offset or 0 where the address already holds it) plus the next page
+// id.  V rows of tokens 4*lg + 2x and 4*lg + 2x + 1 sit 128 bytes apart
+// (va[x] addresses the first).
+template <int ST>
 __device__ __forceinline__ int32_t read_stage64(const uint32_t (&kaddr)[2],
                                                 const uint32_t (&vaddr)[2], uint32_t kszaddr,
                                                 uint32_t vszaddr, uint32_t kzaddr,
                                                 uint32_t pidaddr, StageData<64>& s) {
   int32_t pid;
   asm volatile(
-      "ds_read_b32 %0, %16\n\t"
-      "ds_read_b32 %1, %17\n\t"
-      "ds_read_b32 %2, %18\n\t"
-      "ds_read_b32 %3, %18 offset:128\n\t"
-      "ds_read_b32 %4, %19\n\t"
-      "ds_read_b32 %5, %19 offset:128\n\t"
-      "ds_read_b64 %6, %20\n\t"
-      "ds_read_b64 %7, %20 offset:8\n\t"
-      "ds_read_b64 %8, %20 offset:16\n\t"
-      "ds_read_b64 %9, %20 offset:24\n\t"
-      "ds_read_b32 %10, %21\n\t"
-      "ds_read_b32 %11, %21 offset:8\n\t"
-      "ds_read_b32 %12, %21 offset:16\n\t"
-      "ds_read_b32 %13, %21 offset:24\n\t"
-      "ds_read_b32 %14, %22\n\t"
+      "ds_read_b32 %0, %16 offset:%24\n\t"
+      "ds_read_b32 %1, %17 offset:%24\n\t"
+      "ds_read_b32 %2, %18 offset:%24\n\t"
+      "ds_read_b32 %3, %18 offset:%24+128\n\t"
+      "ds_read_b32 %4, %19 offset:%24\n\t"
+      "ds_read_b32 %5, %19 offset:%24+128\n\t"
+      "ds_read_b64 %6, %20 offset:%24\n\t"
+      "ds_read_b64 %7, %20 offset:%24+8\n\t"
+      "ds_read_b64 %8, %20 offset:%24+16\n\t"
+      "ds_read_b64 %9, %20 offset:%24+24\n\t"
+      "ds_read_b32 %10, %21 offset:%24\n\t"
+      "ds_read_b32 %11, %21 offset:%24+8\n\t"
+      "ds_read_b32 %12, %21 offset:%24+16\n\t"
+      "ds_read_b32 %13, %21 offset:%24+24\n\t"
+      "ds_read_b32 %14, %22 offset:%24\n\t"
       "ds_read_b32 %15, %23\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(s.k[0]), "=&v"(s.k[1]), "=&v"(s.v[0]), "=&v"(s.v[1]), "=&v"(s.v[2]),
@@ -159,7 +161,7 @@ __device__ __forceinline__ int32_t read_stage64(const uint32_t (&kaddr)[2],
         "=&v"(s.vsz[0]), "=&v"(s.vsz[1]), "=&v"(s.vsz[2]), "=&v"(s.vsz[3]), "=&v"(s.kz),
         "=&v"(pid)
       : "v"(kaddr[0]), "v"(kaddr[1]), "v"(vaddr[0]), "v"(vaddr[1]), "v"(kszaddr), "v"(vszaddr),
-        "v"(kzaddr), "v"(pidaddr)
+        "v"(kzaddr), "v"(pidaddr), "i"(ST)
       : "memory");
   return __builtin_amdgcn_readfirstlane(pid);
 }
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
       pid = read_stage<ST>(k4, va + off, ksza + off, vsza + off, kza + off, pid_addr(jn), sd);
     } else {
       const uint32_t k2[2] = {ka[0] + off, ka[1] + off}, v2[2] = {va + off, va2 + off};
-      pid = read_stage64(k2, v2, ksza + off, vsza + off, kza + off, pid_addr(jn), sd);
+      pid = read_stage64<ST>(k2, v2, ksza + off, vsza + off, kza + off, pid_addr(jn), sd);
     }
     if (j + kStages - 1 < nmine) issue(j + kStages - 1, pid);
   };
@@ -655,7 +657,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
         if (u < nmine) issue(u, lds_read_i32(pid_addr(u)));
       using C0 = std::integral_constant<int, 0>;
       int j = 0;
-      if constexpr (D == 128) {
+      {
         // unmasked tiles, kStages per trip so that each one's stage is a constant
         static_assert(kStages == 4, "one unrolled trip per ring cycle");
         using C1 = std::integral_constant<int, kStageBytes>;
@@ -672,15 +674,8 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
           step(j + 3, sd3, 0u, C3{});
           compute(j + 3, sd3, std::false_type{}, sc);
         }
-      } else {
-        // unmasked tiles one at a time (the stage offset in a register)
-        for (; j < jfull; ++j) {
-          StageData<D> sd;
-          step(j, sd, (uint32_t)((j % kStages) * kStageBytes), C0{});
-          compute(j, sd, std::false_type{}, sc);
-        }
       }
-      // the rest (D = 128: fewer than kStages unmasked tiles; then the masked ones)
+      // the rest (fewer than kStages unmasked tiles; then the masked ones)
       for (; j < nmine; ++j) {
         StageData<D> sd;
         step(j, sd, (uint32_t)((j % kStages) * kStageBytes), C0{});
