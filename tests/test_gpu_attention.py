@@ -128,13 +128,23 @@ INT4_D64_MQA = W.INT4_MTP_B64.scaled(name="int4_d64_hkv1_q2_r8", batch=3, num_q_
                                      lengths="list", length_list=(9, 300, 1000))
 # four kv-heads per workgroup (token-major INT8 / INT4, dense bf16 and fp32 at
 # D = 64): one group of four (Hkv = 4), three (Hkv = 12), and two row tiles
-# (20 rows) at D = 128, and four groups at Hkv = 16 (INT4 at both head dims)
+# (20 rows) at D = 128, and four groups at Hkv = 16 (every such kernel)
 QUAD = [
     W.INT4_MTP_B64.scaled(name="int4_hkv16_g2_mtp2_r4", batch=3, num_q_heads=32, num_kv_heads=16,
                           q_per_req=2, lengths="list", length_list=(1, 260, 1300)),
     W.INT4_MTP_B64.scaled(name="int4_d64_hkv16_g3_r3", batch=2, num_q_heads=48, num_kv_heads=16,
                           head_dim=64, q_per_req=1, causal=False, lengths="list",
                           length_list=(100, 2222)),
+    W.INT8_B32.scaled(name="int8_hkv16_g2", batch=2, num_q_heads=32, num_kv_heads=16,
+                      lengths="list", length_list=(70, 1900)),
+    W.BF16_MTP_B64.scaled(name="bf16_d64_hkv16_g2_mtp4_r8", batch=2, num_q_heads=32,
+                          num_kv_heads=16, head_dim=64, lengths="list", length_list=(5, 1700)),
+    W.RAGGED_B64.scaled(name="bf16_d64_hkv16_g3", batch=2, num_q_heads=48, num_kv_heads=16,
+                        head_dim=64, lengths="list", length_list=(1, 1200), pin_max=False),
+    W.TINY_FP32.scaled(name="fp32_d64_hkv16_g2", batch=2, num_q_heads=32, num_kv_heads=16,
+                       page_size=64, lengths="list", length_list=(33, 700), pool_pages=0),
+    W.TINY_FP32.scaled(name="fp32_d64_hkv16_g8", batch=2, num_q_heads=128, num_kv_heads=16,
+                       page_size=64, lengths="list", length_list=(2, 650), pool_pages=0),
     W.INT4_MTP_B64.scaled(name="int4_hkv4_mtp4_r16", batch=3, num_q_heads=16, num_kv_heads=4,
                           lengths="list", length_list=(2, 70, 1500)),
     W.INT4_MTP_B64.scaled(name="int4_hkv12_mtp4_r8", batch=3, num_q_heads=24, num_kv_heads=12,
