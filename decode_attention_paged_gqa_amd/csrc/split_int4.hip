@@ -61,12 +61,14 @@
 // stages of K 1 KB, V 1 KB and the two scale/zero tiles of 256 B each per 16
 // tokens; the K and V tiles are stored with their 16-byte chunks rotated by
 // (token / 4) so that the dword reads of both operands (K: one group of
-// token lm; V: dword lm of token 4*lg + j) hit distinct banks.  D = 64: 8
+// token lm; V: dword lm of token 4*lg + j) hit distinct banks.  D = 64: 4
 // stages of K 512 B, V 512 B (one DMA: lanes 0..31 fetch K, 32..63 V) and the
-// scale/zero tiles of 128 B each (one DMA likewise), as many bytes in flight;
-// the 32-byte rows are stored transposed (token t in row slot 4 (t % 4) +
-// t / 4) with their two chunks rotated by ((t / 2) mod 2), which again puts
-// both operand reads on distinct banks.
+// scale/zero tiles of 128 B each (one DMA likewise); the 32-byte rows are
+// stored transposed (token t in row slot 4 (t % 4) + t / 4) with their two
+// chunks rotated by ((t / 2) mod 2), which again puts both operand reads on
+// distinct banks.  With four kv-heads per workgroup (token-major pools) the
+// waves fill one ring together instead, each DMA fetching whole token rows
+// of all four heads (see the kernel).
 //
 // Softmax: one running reference m per query row, uniform over the lanes
 // holding that row; raised lazily when a score exceeds m + 8 (log2 units).
@@ -132,7 +134,7 @@ struct StageData<64> {
 // stage offset or 0 where the address already holds it) plus the next page
 // id.  V rows of tokens 4*lg + 2x and 4*lg + 2x + 1 sit 128 bytes apart
 // (va[x] addresses the first).
-template <int ST>
+template <int ST, int SZS = 8>
 __device__ __forceinline__ int32_t read_stage64(const uint32_t (&kaddr)[2],
                                                 const uint32_t (&vaddr)[2], uint32_t kszaddr,
                                                 uint32_t vszaddr, uint32_t kzaddr,
@@ -146,13 +148,13 @@ __device__ __forceinline__ int32_t read_stage64(const uint32_t (&kaddr)[2],
       "ds_read_b32 %4, %19 offset:%24\n\t"
       "ds_read_b32 %5, %19 offset:%24+128\n\t"
       "ds_read_b64 %6, %20 offset:%24\n\t"
-      "ds_read_b64 %7, %20 offset:%24+8\n\t"
-      "ds_read_b64 %8, %20 offset:%24+16\n\t"
-      "ds_read_b64 %9, %20 offset:%24+24\n\t"
+      "ds_read_b64 %7, %20 offset:%24+%25\n\t"
+      "ds_read_b64 %8, %20 offset:%24+2*%25\n\t"
+      "ds_read_b64 %9, %20 offset:%24+3*%25\n\t"
       "ds_read_b32 %10, %21 offset:%24\n\t"
-      "ds_read_b32 %11, %21 offset:%24+8\n\t"
-      "ds_read_b32 %12, %21 offset:%24+16\n\t"
-      "ds_read_b32 %13, %21 offset:%24+24\n\t"
+      "ds_read_b32 %11, %21 offset:%24+%25\n\t"
+      "ds_read_b32 %12, %21 offset:%24+2*%25\n\t"
+      "ds_read_b32 %13, %21 offset:%24+3*%25\n\t"
       "ds_read_b32 %14, %22 offset:%24\n\t"
       "ds_read_b32 %15, %23\n\t"
       "s_waitcnt lgkmcnt(0)"
@@ -161,7 +163,7 @@ __device__ __forceinline__ int32_t read_stage64(const uint32_t (&kaddr)[2],
         "=&v"(s.vsz[0]), "=&v"(s.vsz[1]), "=&v"(s.vsz[2]), "=&v"(s.vsz[3]), "=&v"(s.kz),
         "=&v"(pid)
       : "v"(kaddr[0]), "v"(kaddr[1]), "v"(vaddr[0]), "v"(vaddr[1]), "v"(kszaddr), "v"(vszaddr),
-        "v"(kzaddr), "v"(pidaddr), "i"(ST)
+        "v"(kzaddr), "v"(pidaddr), "i"(ST), "i"(SZS)
       : "memory");
   return __builtin_amdgcn_readfirstlane(pid);
 }
@@ -206,6 +208,46 @@ __device__ __forceinline__ int32_t read_stage(const uint32_t (&kaddr)[4], uint32
   return __builtin_amdgcn_readfirstlane(pid);
 }
 
+// D = 128 with four kv-heads per workgroup sharing each stage (see the
+// kernel): as read_stage, but the four V rows sit at four addresses and a
+// token's (scale, zero) rows are 64 bytes apart.
+template <int ST>
+__device__ __forceinline__ int32_t read_stage_shared(const uint32_t (&kaddr)[4],
+                                                     const uint32_t (&vaddr)[4], uint32_t kszaddr,
+                                                     uint32_t vszaddr, uint32_t kzaddr,
+                                                     uint32_t pidaddr, StageData<128>& s) {
+  int32_t pid;
+  asm volatile(
+      "ds_read_b32 %0, %18 offset:%30\n\t"
+      "ds_read_b32 %1, %19 offset:%30\n\t"
+      "ds_read_b32 %2, %20 offset:%30\n\t"
+      "ds_read_b32 %3, %21 offset:%30\n\t"
+      "ds_read_b32 %4, %22 offset:%30\n\t"
+      "ds_read_b32 %5, %23 offset:%30\n\t"
+      "ds_read_b32 %6, %24 offset:%30\n\t"
+      "ds_read_b32 %7, %25 offset:%30\n\t"
+      "ds_read_b128 %8, %26 offset:%30\n\t"
+      "ds_read_b128 %9, %26 offset:%30+64\n\t"
+      "ds_read_b128 %10, %26 offset:%30+128\n\t"
+      "ds_read_b128 %11, %26 offset:%30+192\n\t"
+      "ds_read_b32 %12, %27 offset:%30\n\t"
+      "ds_read_b32 %13, %27 offset:%30+64\n\t"
+      "ds_read_b32 %14, %27 offset:%30+128\n\t"
+      "ds_read_b32 %15, %27 offset:%30+192\n\t"
+      "ds_read_b32 %16, %28 offset:%30\n\t"
+      "ds_read_b32 %17, %29\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(s.k[0]), "=&v"(s.k[1]), "=&v"(s.k[2]), "=&v"(s.k[3]), "=&v"(s.v[0]),
+        "=&v"(s.v[1]), "=&v"(s.v[2]), "=&v"(s.v[3]), "=&v"(s.ksz[0]), "=&v"(s.ksz[1]),
+        "=&v"(s.ksz[2]), "=&v"(s.ksz[3]), "=&v"(s.vsz[0]), "=&v"(s.vsz[1]), "=&v"(s.vsz[2]),
+        "=&v"(s.vsz[3]), "=&v"(s.kz), "=&v"(pid)
+      : "v"(kaddr[0]), "v"(kaddr[1]), "v"(kaddr[2]), "v"(kaddr[3]), "v"(vaddr[0]), "v"(vaddr[1]),
+        "v"(vaddr[2]), "v"(vaddr[3]), "v"(kszaddr), "v"(vszaddr), "v"(kzaddr), "v"(pidaddr),
+        "i"(ST)
+      : "memory");
+  return __builtin_amdgcn_readfirstlane(pid);
+}
+
 struct MfmaArgs {
   const void* q;  // bf16 or fp32
   const uint8_t* k;
@@ -228,17 +270,21 @@ struct MfmaArgs {
 // NT row tiles of 16 query rows (NT * 16 rows per workgroup): the K codes and
 // the dequantised V of a tile are formed once and serve every row tile.
 // One tile fits three workgroups per CU, two tiles two.  POLICY: the cache
-// policy of the code and scale streams.  Non-temporal in the head-major
-// layout, where every cache line belongs to one kv-head's workgroup; the
-// default in the token-major one, where a 64-byte code row (and a 16-byte
-// scale row) shares its line with the neighbouring kv-heads' rows, which
-// their workgroups read from L2 moments later.  HQ: kv-heads per workgroup.
-// HQ = 1: the four waves share one kv-head and take its tiles in turn.  HQ =
-// 4 (token-major pools): wave w takes kv-head HQ*g' + w and every tile of the
-// split, and the waves meet at a barrier before each tile, so they read the
-// same token rows together: the 64-byte code rows of neighbouring kv-heads
-// (one 128-byte line) and half of each 128-byte (scale, zero) line are
-// requested by one CU at once.
+// policy of the scale stream, and of the code stream with one kv-head per
+// workgroup.  Non-temporal in the head-major layout, where every cache line
+// belongs to one kv-head's workgroup; the default in the token-major one,
+// where a code row (64 or 32 bytes) and a scale row (16 or 8) share their
+// lines with the neighbouring kv-heads' rows, which other waves read moments
+// later.  HQ: kv-heads per workgroup.  HQ = 1: the four waves share one
+// kv-head and take its tiles in turn.  HQ = 4 (token-major pools, kv-heads
+// 4g' .. 4g' + 3): wave w computes kv-head 4g' + w over every tile of the
+// split, and the waves fill one LDS ring together (SHARED): a stage holds
+// the tile of all four heads, wave w fetching its tokens 4w .. 4w + 3, whose
+// four code rows are contiguous, so every code line is requested whole by
+// one instruction and streams non-temporal; the (scale, zero) rows fill half
+// of each line, whose other half the workgroup of the other four kv-heads
+// reads (default policy).  Each wave waits for its own part of a tile, then
+// the waves meet at a barrier before reading it.
 template <int D, int NT, int POLICY, bool QF, int HQ>  // QF: fp32 Q
 __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_kernel(const MfmaArgs a) {
   static_assert(HQ == 1 || HQ == kWaves, "one kv-head per workgroup or one per wave");
@@ -247,6 +293,10 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   constexpr int kStageK = Gm::kStageK, kStageV = Gm::kStageV, kStageKsz = Gm::kStageKsz;
   constexpr int kStageVsz = Gm::kStageVsz, kStageBytes = Gm::kStageBytes;
   constexpr int kRingBytes = Gm::kRingBytes;
+  // four kv-heads per workgroup: the waves fill one ring together (SHARED
+  // below), a stage holding all four heads' tile
+  constexpr bool SHARED = HQ > 1;
+  constexpr int kStageStride = SHARED ? kWaves * kStageBytes : kStageBytes;
   constexpr int ROWS = 16 * NT;
   constexpr int kEpiBytes = (kWaves * ROWS * kD + 2 * kWaves * ROWS) * 4;
   constexpr int kMainBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
@@ -394,7 +444,40 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   uint32_t voff_kv, voff_sz;
   const uint8_t* code_base = a.k;  // the tensor this lane's code DMA reads
   const uint8_t* sz_base = a.ksz;
-  if constexpr (D == 128) {
+  if constexpr (SHARED && D == 64) {
+    // wave w fetches tokens 4w .. 4w + 3 of the tile for all four kv-heads,
+    // whose rows of a token are contiguous (128 code bytes: one line; 32
+    // scale bytes): lanes 0..31 the K codes, 32..63 the V codes, and one DMA
+    // likewise for the (scale, zero) rows.  In LDS wave w's K codes (512 B)
+    // and V codes (512 B) follow each other, a token's four code rows one
+    // 128-byte row, kv-head h of token t in slot (h + t/4) mod 4 with its two
+    // 16-byte groups rotated by (t/2) mod 2; after the four waves' codes, the
+    // waves' K and V (scale, zero) rows (128 B each), a token's four in 32
+    // bytes, kv-head h in slot (h + t/4) mod 4.  DMA lane i fills 16-byte
+    // position i % 8 (codes) or dword i % 8 (scales) of token 4w + (i % 32)/8.
+    const int li = lane & 31, t = 4 * wave + (li >> 3), pos = li & 7;
+    const int hk = ((pos >> 1) - (t >> 2)) & 3, ck = ((pos & 1) - ((t >> 1) & 1)) & 1;
+    voff_kv = (uint32_t)(t * rowb + kRow * hk + 16 * ck);
+    voff_sz = (uint32_t)(t * szb + kSz * hk + 4 * (pos & 1));
+    if (lane >= 32) {
+      code_base = a.v;
+      sz_base = a.vsz;
+    }
+  } else if constexpr (SHARED) {
+    // wave w fetches tokens 4w .. 4w + 3 of the tile for all four kv-heads,
+    // whose rows of a token are contiguous (256 code bytes, 64 scale bytes):
+    // every 128-byte line is requested whole by one instruction.  In LDS a
+    // token's four code rows fill one 256-byte row, kv-head h of token t in
+    // slot (h + t + t/4) mod 4 with its 16-byte groups rotated by t/4; its
+    // four (scale, zero) rows one 64-byte row, kv-head h in slot
+    // (h + t/4) mod 4.  DMA lane i fills 16-byte position i % 16 (codes) or
+    // dword i % 16 (scales) of token 4w + i/16.
+    const int t = 4 * wave + (lane >> 4), pos = lane & 15;
+    const int hk = ((pos >> 2) - t - (t >> 2)) & 3, ck = ((pos & 3) - (t >> 2)) & 3;
+    voff_kv = (uint32_t)(t * rowb + kRow * hk + 16 * ck);
+    const int hs = ((pos >> 2) - (t >> 2)) & 3;
+    voff_sz = (uint32_t)(t * szb + kSz * hs + 4 * (pos & 3));
+  } else if constexpr (D == 128) {
     // DMA lane i fills LDS chunk i (token i/4, position i%4) with the token's
     // 16-byte group (position - token/4) mod 4
     voff_kv = (uint32_t)((lane >> 2) * rowb + 16 * (((lane & 3) - (lane >> 4)) & 3));
@@ -412,13 +495,44 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
       sz_base = a.vsz;
     }
   }
-  DA_LDS uint8_t* ring = (DA_LDS uint8_t*)smem + wave * (kStages * kStageBytes);
+  DA_LDS uint8_t* ring = (DA_LDS uint8_t*)smem + (SHARED ? 0 : wave * (kStages * kStageBytes));
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   const uint32_t pid_lds = (uint32_t)(uintptr_t)(DA_LDS void*)s_pid;
   uint32_t rd_k[kGroups];
-  uint32_t rd_v[D == 128 ? 1 : 2];
+  uint32_t rd_v[SHARED && D == 128 ? 4 : D == 128 ? 1 : 2];
   uint32_t rd_ksz, rd_kz, rd_vsz;
-  if constexpr (D == 128) {
+  // shared stage, D = 128: K 4 KB, V 4 KB, then the two 1 KB (scale, zero)
+  // tiles; D = 64: [K 512 B, V 512 B] per wave, then [K, V (scale, zero) 128
+  // B each] per wave
+  constexpr int kShV = 16 * 4 * kRow, kShKsz = 2 * kShV, kShVsz = kShKsz + 16 * 4 * kSz;
+  constexpr int kSh64Sz = 4 * 1024;
+  if constexpr (SHARED && D == 64) {
+    const int h = wave;  // this wave's kv-head within the workgroup's four
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)  // token lm, group kb, dword lg
+      rd_k[kb] = 1024 * (lm >> 2) + 128 * (lm & 3) + kRow * ((h + (lm >> 2)) & 3) +
+                 16 * ((kb + ((lm >> 1) & 1)) & 1) + 4 * lg;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)  // token 4 lg + 2x (+1 at 128 bytes), dword lm / 2
+      rd_v[x] = 1024 * lg + 512 + 128 * (2 * x) + kRow * ((h + lg) & 3) +
+                16 * (((lm >> 3) + x) & 1) + 4 * ((lm >> 1) & 3);
+    rd_ksz = kSh64Sz + 256 * lg + kSz * ((h + lg) & 3);  // tokens 4 lg + i at 32 i
+    rd_kz = kSh64Sz + 256 * (lm >> 2) + 32 * (lm & 3) + kSz * ((h + (lm >> 2)) & 3) + 4 * (lg & 1);
+    rd_vsz = kSh64Sz + 128 + 256 * lg + kSz * ((h + lg) & 3) + 4 * (lm >> 3);
+  } else if constexpr (SHARED) {
+    const int h = wave;  // this wave's kv-head within the workgroup's four
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      rd_k[kb] = 4 * kRow * lm + kRow * ((h + lm + (lm >> 2)) & 3) + 16 * ((kb + (lm >> 2)) & 3) +
+                 4 * lg;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)  // token 4 lg + jj, dword lm
+      rd_v[jj] = kShV + 4 * kRow * (4 * lg + jj) + kRow * ((h + jj + lg) & 3) +
+                 16 * (((lm >> 2) + lg) & 3) + 4 * (lm & 3);
+    rd_ksz = kShKsz + 4 * kSz * (4 * lg) + kSz * ((h + lg) & 3);
+    rd_kz = kShKsz + 4 * kSz * lm + kSz * ((h + (lm >> 2)) & 3) + 4 * lg;
+    rd_vsz = kShVsz + 4 * kSz * (4 * lg) + kSz * ((h + lg) & 3) + 4 * (lm >> 2);
+  } else if constexpr (D == 128) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) rd_k[kb] = kStageK + 64 * lm + 16 * ((kb + (lm >> 2)) & 3) + 4 * lg;
     rd_v[0] = kStageV + 64 * (4 * lg) + 16 * (((lm >> 2) + lg) & 3) + 4 * (lm & 3);
@@ -442,12 +556,30 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
 
   auto tile_base = [&](int j) { return c0 + ((toff + tstep * j) << 4); };
   auto pid_addr = [&](int j) { return pid_lds + 4 * ((tile_base(j) >> a.log2_ps) - pc); };
+  // shared stage: the workgroup's first kv-head, and this wave's part of it
+  const int g_dma = SHARED ? HQ * it.g : g;
+  const int dst_kv = SHARED ? 1024 * wave : 0,
+            dst_sz = !SHARED ? 0 : D == 128 ? 256 * wave : kSh64Sz + 256 * wave;
   auto issue = [&](int j, int pid) {
     const int tb = tile_base(j);
     const long long row0 = (long long)pid * ps * a.Hkv + (long long)(tb & (ps - 1)) * a.slot_stride +
-                           (long long)g * a.head_stride;
-    DA_LDS uint8_t* st = ring + (j % kStages) * kStageBytes;
-    if constexpr (D == 128) {
+                           (long long)g_dma * a.head_stride;
+    DA_LDS uint8_t* st = ring + (j % kStages) * kStageStride;
+    if constexpr (SHARED && D == 64) {
+      __builtin_amdgcn_global_load_lds((const void*)(code_base + row0 * kRow + voff_kv),
+                                       (DA_LDS void*)(st + dst_kv), 16, 0, da::kStreamPolicy);
+      __builtin_amdgcn_global_load_lds((const void*)(sz_base + row0 * kSz + voff_sz),
+                                       (DA_LDS void*)(st + dst_sz), 4, 0, POLICY);
+    } else if constexpr (SHARED) {
+      __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * (kD / 2) + voff_kv),
+                                       (DA_LDS void*)(st + dst_kv), 16, 0, da::kStreamPolicy);
+      __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * (kD / 2) + voff_kv),
+                                       (DA_LDS void*)(st + kShV + dst_kv), 16, 0, da::kStreamPolicy);
+      __builtin_amdgcn_global_load_lds((const void*)(a.ksz + row0 * 16 + voff_sz),
+                                       (DA_LDS void*)(st + kShKsz + dst_sz), 4, 0, POLICY);
+      __builtin_amdgcn_global_load_lds((const void*)(a.vsz + row0 * 16 + voff_sz),
+                                       (DA_LDS void*)(st + kShVsz + dst_sz), 4, 0, POLICY);
+    } else if constexpr (D == 128) {
       __builtin_amdgcn_global_load_lds((const void*)(a.k + row0 * (kD / 2) + voff_kv),
                                        (DA_LDS void*)(st + kStageK), 16, 0, POLICY);
       __builtin_amdgcn_global_load_lds((const void*)(a.v + row0 * (kD / 2) + voff_kv),
@@ -618,18 +750,32 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
   const uint32_t va = ring_lds + rd_v[0], ksza = ring_lds + rd_ksz, vsza = ring_lds + rd_vsz,
                  kza = ring_lds + rd_kz;
   const uint32_t va2 = ring_lds + rd_v[D == 128 ? 0 : 1];
+  constexpr int kVsh = SHARED && D == 128 ? 4 : 1;
+  uint32_t vsh[kVsh];
+#pragma unroll
+  for (int jj = 0; jj < kVsh; ++jj) vsh[jj] = ring_lds + rd_v[jj];
   // wait for tile j, read it (stage offset ST + off bytes), refill its stage
   auto step = [&](int j, StageData<D>& sd, uint32_t off, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     // HQ > 1: the waves (each its own kv-head, every wave the same number of
     // tiles) meet before each tile, so their reads of the lines they share
     // leave the CU together
-    if constexpr (HQ > 1) __builtin_amdgcn_s_barrier();
+    if constexpr (HQ > 1 && !SHARED) __builtin_amdgcn_s_barrier();
     // the tiles after j issued so far may stay in flight
     wait_tiles_ahead<Gm::kLoads, kStages - 2>(min(kStages - 2, nmine - 1 - j));
+    // shared stage: every wave's part of tile j has landed, and every wave has
+    // read tile j - 1, whose stage the issue below refills
+    if constexpr (SHARED) __builtin_amdgcn_s_barrier();
     const int jn = min(j + kStages - 1, nmine - 1);
     int pid;
-    if constexpr (D == 128) {
+    if constexpr (SHARED && D == 64) {
+      const uint32_t k2[2] = {ka[0] + off, ka[1] + off}, v2[2] = {va + off, va2 + off};
+      pid = read_stage64<ST, 32>(k2, v2, ksza + off, vsza + off, kza + off, pid_addr(jn), sd);
+    } else if constexpr (SHARED) {
+      const uint32_t k4[4] = {ka[0] + off, ka[1] + off, ka[2] + off, ka[3] + off};
+      const uint32_t v4[4] = {vsh[0] + off, vsh[1] + off, vsh[2] + off, vsh[3] + off};
+      pid = read_stage_shared<ST>(k4, v4, ksza + off, vsza + off, kza + off, pid_addr(jn), sd);
+    } else if constexpr (D == 128) {
       const uint32_t k4[4] = {ka[0] + off, ka[1] + off, ka[2] + off, ka[3] + off};
       pid = read_stage<ST>(k4, va + off, ksza + off, vsza + off, kza + off, pid_addr(jn), sd);
     } else {
@@ -660,9 +806,9 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
       {
         // unmasked tiles, kStages per trip so that each one's stage is a constant
         static_assert(kStages == 4, "one unrolled trip per ring cycle");
-        using C1 = std::integral_constant<int, kStageBytes>;
-        using C2 = std::integral_constant<int, 2 * kStageBytes>;
-        using C3 = std::integral_constant<int, 3 * kStageBytes>;
+        using C1 = std::integral_constant<int, kStageStride>;
+        using C2 = std::integral_constant<int, 2 * kStageStride>;
+        using C3 = std::integral_constant<int, 3 * kStageStride>;
         for (; j + kStages <= jfull; j += kStages) {
           StageData<D> sd0, sd1, sd2, sd3;
           step(j, sd0, 0u, C0{});
@@ -678,7 +824,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 3 : 2) void split_int4_mfma_ker
       // the rest (fewer than kStages unmasked tiles; then the masked ones)
       for (; j < nmine; ++j) {
         StageData<D> sd;
-        step(j, sd, (uint32_t)((j % kStages) * kStageBytes), C0{});
+        step(j, sd, (uint32_t)((j % kStages) * kStageStride), C0{});
         compute(j, sd, std::true_type{}, sc);
       }
     }
