@@ -116,6 +116,15 @@ INT4_FP32Q_Q1 = W.INT4_MTP_B64.scaled(name="int4_fp32q_q1_r4", batch=3, dtype="f
 INT4_FP32Q_D64 = W.INT4_MTP_B64.scaled(name="int4_fp32q_d64_r16_p32", batch=3, dtype="fp32",
                                        head_dim=64, page_size=32, lengths="list",
                                        length_list=(3, 100, 1000))
+# fp32 Q over quantised caches with two row tiles per workgroup (17..32 rows)
+INT4_FP32Q_R20 = W.INT4_MTP_B64.scaled(name="int4_fp32q_g5_mtp4_r20", batch=3, dtype="fp32",
+                                       num_q_heads=40, lengths="list", length_list=(3, 130, 1000))
+INT4_FP32Q_D64_R32 = W.INT4_MTP_B64.scaled(name="int4_fp32q_d64_g8_mtp4_r32", batch=3,
+                                           dtype="fp32", num_q_heads=64, head_dim=64,
+                                           lengths="list", length_list=(2, 70, 900))
+INT8_FP32Q_R20 = W.INT8_B32.scaled(name="int8_fp32q_g5_mtp4_r20", batch=3, dtype="fp32",
+                                   num_q_heads=40, q_per_req=4, causal=True, lengths="list",
+                                   length_list=(5, 129, 1000))
 INT4_G8Q2 = W.INT4_MTP_B64.scaled(name="int4_g8_mtp2_small", batch=3, num_q_heads=64, q_per_req=2,
                                   lengths="list", length_list=(1, 48, 700))
 # kv-head counts that are not a multiple of 4: token-major pools take the
@@ -199,7 +208,8 @@ SMALL = [TINY_BF16, RAGGED_SMALL, BF16_SMALL, D64_P16, D64_G8, D64_MTP, D64_R20,
          INT8_SMALL, INT8_MTP, INT8_G8Q2, INT8_ODD_HKV, INT8_FP32Q, INT8_D64, INT8_D64_MTP, INT8_D64_R20,
          INT4_SMALL, INT4_Q1,
          INT4_R12, INT4_G8Q2, INT4_D64, INT4_D64_Q1, INT4_D64_R20, INT8_FP32Q_MTP, INT8_FP32Q_D64,
-         INT4_FP32Q, INT4_FP32Q_Q1, INT4_FP32Q_D64, INT4_ODD_HKV, INT4_D64_MQA] + QUAD
+         INT4_FP32Q, INT4_FP32Q_Q1, INT4_FP32Q_D64, INT4_ODD_HKV, INT4_D64_MQA,
+         INT4_FP32Q_R20, INT4_FP32Q_D64_R32, INT8_FP32Q_R20] + QUAD
 
 
 def both_layouts(ws):
