@@ -4,7 +4,7 @@ tokens (causal or not), ragged lengths with empty requests, split count, and
 the batch-wide or per-request schedule, drawn together so that combinations
 the hand-picked cases do not name are compared against the fp64 oracle too.
 Gates as in tests/_gpu_util.py; every stage-1 slot and every output element
-is checked.  Eight more cases draw 17..64 query rows per kv-head.
+is checked.  N_WIDE more cases draw 17..64 query rows per kv-head.
 """
 import numpy as np
 import pytest
@@ -17,7 +17,8 @@ from tests.test_gpu_attention import _check_out
 pytestmark = pytest.mark.gpu
 log = U.log
 
-N_CASES = 24
+N_CASES = 64
+N_WIDE = 16
 
 
 def random_case(i):
@@ -89,7 +90,7 @@ def wide_case(i):
     return w, S, table
 
 
-CASES = [random_case(i) for i in range(N_CASES)] + [wide_case(i) for i in range(8)]
+CASES = [random_case(i) for i in range(N_CASES)] + [wide_case(i) for i in range(N_WIDE)]
 
 
 @pytest.mark.parametrize("w,S,table", CASES, ids=[c[0].name for c in CASES])
