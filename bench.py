@@ -868,7 +868,8 @@ def profile_report(prefix):
         run += f" --kv-layout {w.kv_layout}"
     cmds = ["cd /tmp && export TMPDIR=/tmp",
             f"rocprofv3 --kernel-trace --stats --output-format csv -d $R/{rel}_trace -o run -- "
-            f"{run} --steps 20 --warmup 5 --no-cpu-baseline --no-alt --no-variants",
+            f"{run} --steps {res['steps']} --warmup {res['warmup']} --no-cpu-baseline --no-alt "
+            f"--no-variants",
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/{rel}_fetch -o run -- "
             f"{run} --profile-only --steps 3",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/{rel}_write -o run -- "
