@@ -42,6 +42,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -239,14 +240,17 @@ def kv_name(w):
     return w.dtype if w.kv == W.KV_DENSE else w.kv
 
 
-def time_config(step_list, steps, warmup, torch):
+def time_config(step_list, steps, warmup, torch, settle_ms=0.0):
     """Times `steps` whole steps back to back (host clock, synchronised on both
     sides); then the same number again with events between the three calls for
     the per-kernel breakdown and percentiles (an event record between steps
     costs the stream ~12 us here, so the timed steps carry none).  Step i runs
     on copy i % len(step_list) of the batch.  Returns (ms_per_step,
     split_ms_avg, merge_ms_avg, meta_ms_avg, percentiles); the stage-1 average
-    is over the launches [warmup + steps, warmup + 2 steps) of the run."""
+    is over the launches [warmup + steps, warmup + 2 steps) of the run.
+    settle_ms > 0 (the variants): after the `warmup` steps, more untimed steps
+    until the warm-up has kept the GPU busy that long, so that short launches
+    are timed once the clocks have settled (10-20 ms after idle)."""
     stream = torch.cuda.current_stream()
     n = len(step_list)
 
@@ -264,9 +268,15 @@ def time_config(step_list, steps, warmup, torch):
         if ev is not None:
             ev[3].record(stream)
 
+    tw = time.perf_counter()
     for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
+    if settle_ms > 0:  # back to back, no synchronisation between the steps
+        per_ms = (time.perf_counter() - tw) * 1e3 / max(warmup, 1)
+        for i in range(int(math.ceil(settle_ms / max(per_ms, 1e-3)))):
+            run(i)
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         run(i)
@@ -536,6 +546,11 @@ VARIANT_WORKLOADS = ("bf16_b16_hq32_hkv8_d128_p64_L8192", "bf16_b64_hq40_hkv8_d1
                      "int4kv_mtp4_b64_hq32_hkv8_d128_p64_L8k-32k@NHD")
 
 
+# untimed warm-up of every variant, at least: the clocks settle 10-20 ms after
+# the GPU leaves idle (building a variant's pools leaves it idle)
+VARIANT_SETTLE_MS = 60.0
+
+
 def variant_timings(da, torch, steps, warmup):
     """The pages' other decode shapes, each at its tuned split count and timed
     as the main line is (HIP events per call; pools under 2 GB rotated); the
@@ -554,7 +569,8 @@ def variant_timings(da, torch, steps, warmup):
         key = kernel_key(kv_name(w), rows_per_kv_head(w), w.head_dim, w.page_size, w.kv_layout)
         S = tables.pick(key, w.batch, int(batches[0].lengths.max()))
         step_list = [Step(da, b, torch, S=S) for b in batches]
-        ms, split_ms, merge_ms, meta_ms, _ = time_config(step_list, steps, warmup, torch)
+        ms, split_ms, merge_ms, meta_ms, _ = time_config(step_list, steps, warmup, torch,
+                                                         settle_ms=VARIANT_SETTLE_MS)
         ab = algorithmic_bytes(w, batches[0].lengths)
         gbs = ab["split"] / (split_ms * 1e-3) / 1e9
         out[entry] = {"kernel": stage1_kernel(w)[0], "kv": kv_name(w), "kv_layout": w.kv_layout,
