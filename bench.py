@@ -419,6 +419,24 @@ def time_split_merge(step, iters, torch):
     return e0.elapsed_time(e1) / iters
 
 
+def settle(step, torch, ms=60.0):
+    """Stage 1 + merge back to back for about `ms` (untimed): building a batch
+    leaves the GPU idle, and its clocks settle 10-20 ms after it is busy again,
+    so candidates timed right away would be timed at other clocks than the
+    later ones."""
+    step.meta()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step.split()
+    step.merge()
+    torch.cuda.synchronize()
+    per_ms = max((time.perf_counter() - t0) * 1e3, 1e-3)
+    for _ in range(int(math.ceil(ms / per_ms))):
+        step.split()
+        step.merge()
+    torch.cuda.synchronize()
+
+
 def time_split_only(step, iters, torch):
     """Average stage-1 time (ms) over `iters` back-to-back launches."""
     step.meta()
@@ -656,6 +674,7 @@ def tune(da, torch, which="all", old_keys=None):
                     w = base.scaled(batch=bk, lengths="loguniform", length_lo=max(64, Lmax // 32),
                                     length_hi=Lmax, pin_max=True, seed=100 + 10 * k + rep)
                     batch = make_resident(da, w, torch)
+                    settle(Step(da, batch, torch, S=cands[len(cands) // 2]), torch)
                     for S in cands:
                         step = Step(da, batch, torch, S=S)
                         t1 = time_split_merge(step, 10, torch)
