@@ -726,6 +726,9 @@ def tune_chunks(da, torch, which="all", old_keys=None):
                 w = base.scaled(batch=bk, lengths="loguniform", length_lo=max(64, Lmax // 32),
                                 length_hi=Lmax, pin_max=True, seed=200 + k)
                 batch = make_resident(da, w, torch)
+                mid = CHUNK_CANDIDATES[len(CHUNK_CANDIDATES) // 2]
+                settle(Step(da, batch, torch,
+                            table=per_request_table(mid, w.page_size, BUCKET_TOKENS)), torch)
                 for c in CHUNK_CANDIDATES:
                     t = per_request_table(c, w.page_size, BUCKET_TOKENS)
                     tot[c] += time_split_only(Step(da, batch, torch, table=t), 10, torch)
